@@ -1,0 +1,226 @@
+"""CPU oracle for the DCNv4 forward spatial aggregation -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It loads ``libdcn4_oracle.so``, built
+from the plain C in ``dcn4_oracle.c`` (gcc, ``-O2 -ffp-contract=off``), and
+shares no code with the HIP library in ``dynamic_sparse_vision_dcn4_amd``.
+
+The arithmetic and the readings of the pages it follows are documented in
+``dcn4_oracle.c``; this module only marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dcn4_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libdcn4_oracle.so")
+
+F32, BF16, F16 = 0, 1, 2
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "f16": F16}
+RAW_NP = {F32: np.float32, BF16: np.uint16, F16: np.uint16}
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (plain IEEE arithmetic, no contraction)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-std=c11", "-Wall", "-shared", "-fPIC", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("N", "H", "W", "C", "G", "kh", "kw", "sh", "sw", "ph", "pw",
+                 "dh", "dw")] + [("offset_scale", ctypes.c_float),
+                                 ("multiscale", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Operator geometry: input [N,H,W,C] channel-last, G groups."""
+    N: int
+    H: int
+    W: int
+    C: int
+    G: int
+    kh: int = 3
+    kw: int = 3
+    sh: int = 1
+    sw: int = 1
+    ph: int = 1
+    pw: int = 1
+    dh: int = 1
+    dw: int = 1
+    offset_scale: float = 1.0
+    multiscale: bool = False
+
+    @property
+    def K(self) -> int:
+        return self.kh * self.kw
+
+    def c_struct(self) -> _Shape:
+        return _Shape(self.N, self.H, self.W, self.C, self.G, self.kh, self.kw,
+                      self.sh, self.sw, self.ph, self.pw, self.dh, self.dw,
+                      float(self.offset_scale), int(bool(self.multiscale)))
+
+
+class Oracle:
+    """ctypes view of one built oracle library (a mutant build can be loaded
+    from another path by the tests that check the pins catch mistakes)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if path == LIB_PATH and not os.path.exists(path):
+            build()
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        sp = ctypes.POINTER(_Shape)
+        lib.dcn4o_check.argtypes = [sp, i32p, i32p]
+        lib.dcn4o_forward_f64.argtypes = [sp, ctypes.c_int, P, P, P, P, P,
+                                          ctypes.c_int64, ctypes.c_int]
+        lib.dcn4o_forward_f32.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P,
+                                          ctypes.c_int64, ctypes.c_int]
+        lib.dcn4o_geometry.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P,
+                                       P, ctypes.c_int64]
+        lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, i64p, i64p]
+        lib.dcn4o_ideal_bytes.argtypes = [sp, ctypes.c_int]
+        lib.dcn4o_ideal_bytes.restype = ctypes.c_int64
+        for f in ("dcn4o_bf16_to_f32", "dcn4o_f16_to_f32"):
+            getattr(lib, f).argtypes = [ctypes.c_uint16]
+            getattr(lib, f).restype = ctypes.c_float
+        for f in ("dcn4o_f32_to_bf16", "dcn4o_f32_to_f16"):
+            getattr(lib, f).argtypes = [ctypes.c_float]
+            getattr(lib, f).restype = ctypes.c_uint16
+        self.lib = lib
+
+    # -- helpers ----------------------------------------------------------
+    @staticmethod
+    def _ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    @staticmethod
+    def _pix(pix):
+        if pix is None:
+            return None, 0
+        pix = np.ascontiguousarray(pix, dtype=np.int64)
+        return pix, pix.size
+
+    def out_size(self, s: Shape):
+        ho, wo = ctypes.c_int32(), ctypes.c_int32()
+        r = self.lib.dcn4o_check(ctypes.byref(s.c_struct()), ctypes.byref(ho),
+                                 ctypes.byref(wo))
+        if r:
+            raise ValueError(f"invalid shape {s}")
+        return ho.value, wo.value
+
+    def _prep(self, s, dtype, x, om, scales):
+        dt = DTYPE_CODES[dtype]
+        raw = RAW_NP[dt]
+        x = None if x is None else np.ascontiguousarray(x, dtype=raw)
+        om = np.ascontiguousarray(om, dtype=raw)
+        if s.multiscale:
+            scales = np.ascontiguousarray(scales, dtype=np.float32)
+            assert scales.size == s.G
+        else:
+            scales = None
+        return dt, x, om, scales
+
+    # -- the oracle ---------------------------------------------------------
+    def forward_f64(self, s: Shape, dtype: str, x, om, scales=None, pix=None,
+                    nthreads: int = 8) -> np.ndarray:
+        """The definition in fp64; returns [N,Ho,Wo,C] (or [npix,C])."""
+        dt, x, om, scales = self._prep(s, dtype, x, om, scales)
+        ho, wo = self.out_size(s)
+        pix, npix = self._pix(pix)
+        shape = (s.N, ho, wo, s.C) if pix is None else (npix, s.C)
+        y = np.empty(shape, np.float64)
+        r = self.lib.dcn4o_forward_f64(ctypes.byref(s.c_struct()), dt,
+                                       self._ptr(x), self._ptr(om),
+                                       self._ptr(scales), self._ptr(y),
+                                       self._ptr(pix), npix, nthreads)
+        if r:
+            raise ValueError("oracle rejected the call")
+        return y
+
+    def forward_f32(self, s: Shape, dtype: str, x, om, scales=None, pix=None,
+                    nthreads: int = 8, want_acc: bool = False):
+        """fp32 evaluation in the fixed order; returns the output in the I/O
+        dtype's raw encoding (and the fp32 accumulators if asked)."""
+        dt, x, om, scales = self._prep(s, dtype, x, om, scales)
+        ho, wo = self.out_size(s)
+        pix, npix = self._pix(pix)
+        shape = (s.N, ho, wo, s.C) if pix is None else (npix, s.C)
+        y = np.empty(shape, RAW_NP[dt])
+        acc = np.empty(shape, np.float32) if want_acc else None
+        r = self.lib.dcn4o_forward_f32(ctypes.byref(s.c_struct()), dt,
+                                       self._ptr(x), self._ptr(om),
+                                       self._ptr(scales), self._ptr(y),
+                                       self._ptr(acc), self._ptr(pix), npix,
+                                       nthreads)
+        if r:
+            raise ValueError("oracle rejected the call")
+        return (y, acc) if want_acc else y
+
+    def geometry(self, s: Shape, dtype: str, om, scales=None, pix=None):
+        """Per (pixel, g, k): dict of inside, y0, x0, lh, lw arrays."""
+        dt, _, om, scales = self._prep(s, dtype, None, om, scales)
+        ho, wo = self.out_size(s)
+        pix, npix = self._pix(pix)
+        npx = s.N * ho * wo if pix is None else npix
+        n = npx * s.G * s.K
+        out = dict(y0=np.empty(n, np.int32), x0=np.empty(n, np.int32),
+                   lh=np.empty(n, np.float32), lw=np.empty(n, np.float32),
+                   inside=np.empty(n, np.uint8))
+        r = self.lib.dcn4o_geometry(ctypes.byref(s.c_struct()), dt,
+                                    self._ptr(om), self._ptr(scales),
+                                    *(self._ptr(out[k]) for k in
+                                      ("y0", "x0", "lh", "lw", "inside")),
+                                    self._ptr(pix), npix)
+        if r:
+            raise ValueError("oracle rejected the call")
+        return out
+
+    def count_terms(self, s: Shape, dtype: str, om, scales=None):
+        dt, _, om, scales = self._prep(s, dtype, None, om, scales)
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        r = self.lib.dcn4o_count_terms(ctypes.byref(s.c_struct()), dt,
+                                       self._ptr(om), self._ptr(scales),
+                                       ctypes.byref(a), ctypes.byref(b))
+        if r:
+            raise ValueError("oracle rejected the call")
+        return a.value, b.value
+
+    def ideal_bytes(self, s: Shape, dtype: str) -> int:
+        return int(self.lib.dcn4o_ideal_bytes(ctypes.byref(s.c_struct()),
+                                              DTYPE_CODES[dtype]))
+
+    # -- codecs -------------------------------------------------------------
+    def bf16_to_f32(self, h: int) -> float:
+        return self.lib.dcn4o_bf16_to_f32(h)
+
+    def f16_to_f32(self, h: int) -> float:
+        return self.lib.dcn4o_f16_to_f32(h)
+
+    def f32_to_bf16(self, f: float) -> int:
+        return self.lib.dcn4o_f32_to_bf16(f)
+
+    def f32_to_f16(self, f: float) -> int:
+        return self.lib.dcn4o_f32_to_f16(f)
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``dcn4_oracle.c`` (built on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

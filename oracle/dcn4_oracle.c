@@ -1,0 +1,417 @@
+/*
+ * dcn4_oracle.c -- plain CPU oracle for the DCNv4 forward spatial aggregation.
+ *
+ * TEST INFRASTRUCTURE ONLY (see dcn4_oracle.h for who may use it and for the
+ * page citations).  Build: gcc -O2 -ffp-contract=off -fopenmp (no fast-math),
+ * so every fp32 operation below is one IEEE operation, rounded to nearest even,
+ * with subnormals kept.
+ *
+ * What is computed, for output pixel (n, yo, xo), group g, channel c = g*D + d:
+ *
+ *   y[n,yo,xo,c] = sum_{k<K} m_{g,k} * bilinear_zero_pad(x[n,:,:,c], py_k, px_k)
+ *
+ * with K = kh*kw points, the weights m unbounded and not normalised
+ * ([DCNv4 digest] section 1), one (offset, weight) set per group shared by its
+ * D = C/G channels ([DCNv4 digest] "方法1"), and the sample location
+ *   standard:    p_k = base + p_grid_k + offset_scale * delta_{g,k}
+ *   multi-scale: p_k = centre + s_g * (grid_k + dir_{g,k})   ([FlowDCN] 3.1)
+ *
+ * Readings taken where the pages are silent or their formulas were lost:
+ *  R1 grid origin: sample row = yo*sh - ph + i*dh + dy, the convolution index
+ *     arithmetic of [CANN Conv2D] 2.1 with padding and dilation added;
+ *  R2 output size: Ho = floor((H + 2ph - dh*(kh-1) - 1)/sh) + 1 (likewise Wo);
+ *  R3 tap order: k = i*kw + j, i along H (rows), j along W;
+ *  R4 offset/weight row of a group: 3K values, first K interleaved pairs
+ *     (dx_k, dy_k) with x along W, then the K weights m_k; groups are stored
+ *     one after another per pixel: om[n,yo,xo,g,3K];
+ *  R5 zero padding: a corner outside [0,H)x[0,W) contributes nothing;
+ *  R6 multi-scale centre: centre = yo*sh - ph + (kh-1)/2, grid_k = i - (kh-1)/2
+ *     (odd kernels, dilation 1, offset_scale 1);
+ *  R7 the offset/weight tensor has the I/O dtype, scales are fp32;
+ *  R8 fp32 evaluation order (dcn4o_forward_f32): position = one fp32 add of
+ *     the exact integer base and fl(offset_scale*delta) (multi-scale: centre +
+ *     fl(s_g * fl(grid + dir))); sample skipped unless -1<py<H and -1<px<W;
+ *     y0=floor(py), lh=py-y0, hh=1-lh (same for x); corner weights hh*hw,
+ *     hh*lw, lh*hw, lh*lw for (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1);
+ *     coefficient fl(m*w); acc = fma(coefficient, value, acc) with k outer,
+ *     corner inner, acc starting at +0; output rounded to the I/O dtype by
+ *     round-to-nearest-even.
+ */
+#include "dcn4_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ codecs */
+
+float dcn4o_bf16_to_f32(uint16_t h) {
+  /* bf16 is the upper half of an IEEE binary32 */
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+float dcn4o_f16_to_f32(uint16_t h) {
+  /* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits */
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24); /* subnormal: f * 2^-14 * 2^-10 */
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+  return (float)(sign ? -v : v);
+}
+
+uint16_t dcn4o_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040); /* stay a quiet NaN */
+  /* round to nearest, ties to even, on the 16 bits that are dropped */
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+uint16_t dcn4o_f32_to_f16(float f) {
+  uint16_t sign = signbit(f) ? 0x8000 : 0;
+  if (isnan(f)) return 0x7e00;
+  double a = fabs((double)f);
+  if (isinf(f) || a >= 65520.0) return sign | 0x7c00; /* overflow -> inf */
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: value = q * 2^-24, q rounded half-to-even; q == 1024
+     * is the smallest normal and is encoded by the same bit pattern. */
+    double q = nearbyint(a * ldexp(1.0, 24));
+    return sign | (uint16_t)q;
+  }
+  int E;
+  frexp(a, &E); /* a = fr * 2^E, fr in [0.5, 1) */
+  int e = E - 1; /* a in [2^e, 2^(e+1)) */
+  double m = nearbyint(ldexp(a, 10 - e)); /* in [1024, 2048] */
+  if (m >= 2048.0) {
+    m = 1024.0;
+    e += 1;
+  }
+  if (e + 15 >= 31) return sign | 0x7c00;
+  return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+static float load_f32(int dtype, const void* buf, int64_t i) {
+  switch (dtype) {
+    case DCN4O_F32: return ((const float*)buf)[i];
+    case DCN4O_BF16: return dcn4o_bf16_to_f32(((const uint16_t*)buf)[i]);
+    default: return dcn4o_f16_to_f32(((const uint16_t*)buf)[i]);
+  }
+}
+
+static void store_io(int dtype, void* buf, int64_t i, float v) {
+  switch (dtype) {
+    case DCN4O_F32: ((float*)buf)[i] = v; break;
+    case DCN4O_BF16: ((uint16_t*)buf)[i] = dcn4o_f32_to_bf16(v); break;
+    default: ((uint16_t*)buf)[i] = dcn4o_f32_to_f16(v); break;
+  }
+}
+
+static int64_t dtype_bytes(int dtype) { return dtype == DCN4O_F32 ? 4 : 2; }
+
+/* ------------------------------------------------------------------ shapes */
+
+int dcn4o_check(const dcn4o_shape* s, int32_t* Ho, int32_t* Wo) {
+  if (!s) return -1;
+  if (s->N < 0 || s->H < 1 || s->W < 1 || s->C < 1 || s->G < 1) return -1;
+  if (s->C % s->G) return -1;
+  if (s->kh < 1 || s->kw < 1 || s->sh < 1 || s->sw < 1) return -1;
+  if (s->ph < 0 || s->pw < 0 || s->dh < 1 || s->dw < 1) return -1;
+  /* keep every integer coordinate below 2^22: exact in fp32, no overflow */
+  if (s->H > (1 << 20) || s->W > (1 << 20)) return -1;
+  if (s->ph > (1 << 20) || s->pw > (1 << 20)) return -1;
+  if (s->sh > (1 << 20) || s->sw > (1 << 20)) return -1;
+  if ((int64_t)s->dh * s->kh > (1 << 20) || (int64_t)s->dw * s->kw > (1 << 20))
+    return -1;
+  if (s->multiscale) {
+    if (!(s->kh & 1) || !(s->kw & 1)) return -1;
+    if (s->dh != 1 || s->dw != 1 || s->offset_scale != 1.0f) return -1;
+  }
+  /* R2: standard convolution output arithmetic */
+  int64_t ho = ((int64_t)s->H + 2 * s->ph - (int64_t)s->dh * (s->kh - 1) - 1);
+  int64_t wo = ((int64_t)s->W + 2 * s->pw - (int64_t)s->dw * (s->kw - 1) - 1);
+  if (ho < 0 || wo < 0) return -1;
+  ho = ho / s->sh + 1;
+  wo = wo / s->sw + 1;
+  if (Ho) *Ho = (int32_t)ho;
+  if (Wo) *Wo = (int32_t)wo;
+  return 0;
+}
+
+int64_t dcn4o_ideal_bytes(const dcn4o_shape* s, int dtype) {
+  int32_t Ho, Wo;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  int64_t K = (int64_t)s->kh * s->kw;
+  int64_t in = (int64_t)s->N * s->H * s->W * s->C;
+  int64_t out = (int64_t)s->N * Ho * Wo * s->C;
+  int64_t om = (int64_t)s->N * Ho * Wo * s->G * 3 * K;
+  int64_t b = (in + out + om) * dtype_bytes(dtype);
+  if (s->multiscale) b += 4 * (int64_t)s->G;
+  return b;
+}
+
+/* ------------------------------------------------------------ the definition
+ * fp64 everywhere.  bilinear_zero_pad() is the textbook bilinear sample of one
+ * channel with zero outside the image (R5): four corner terms, the "factor 4"
+ * of the 36HWC count ([DCNv4 digest] "GPU效率的理论分析").
+ */
+static double bilinear_zero_pad(const dcn4o_shape* s, int dtype, const void* x,
+                                int n, int c, double py, double px) {
+  double y0 = floor(py), x0 = floor(px);
+  double lh = py - y0, lw = px - x0;
+  double v = 0.0;
+  for (int a = 0; a < 2; ++a) {
+    for (int b = 0; b < 2; ++b) {
+      double yy = y0 + a, xx = x0 + b;
+      double w = (a ? lh : 1.0 - lh) * (b ? lw : 1.0 - lw);
+      if (yy >= 0.0 && yy < s->H && xx >= 0.0 && xx < s->W) {
+        int64_t idx = (((int64_t)n * s->H + (int64_t)yy) * s->W + (int64_t)xx) *
+                          s->C + c;
+        v += w * (double)load_f32(dtype, x, idx);
+      }
+    }
+  }
+  return v;
+}
+
+/* sample location of point k=(i,j) of group g at output (yo, xo), fp64 */
+static void location_f64(const dcn4o_shape* s, int yo, int xo, int i, int j,
+                         double dx, double dy, double sg, double* py,
+                         double* px) {
+  if (s->multiscale) {
+    /* [FlowDCN] 3.1: centre + s_g * (grid + direction); R6 */
+    int hy = (s->kh - 1) / 2, hx = (s->kw - 1) / 2;
+    *py = (double)(yo * s->sh - s->ph + hy) + sg * ((double)(i - hy) + dy);
+    *px = (double)(xo * s->sw - s->pw + hx) + sg * ((double)(j - hx) + dx);
+  } else {
+    /* R1: base of tap (i,j) plus the scaled offset */
+    *py = (double)(yo * s->sh - s->ph + i * s->dh) + (double)s->offset_scale * dy;
+    *px = (double)(xo * s->sw - s->pw + j * s->dw) + (double)s->offset_scale * dx;
+  }
+}
+
+static int resolve_pixels(const dcn4o_shape* s, int32_t Ho, int32_t Wo,
+                          const int64_t* pix, int64_t npix, int64_t* count) {
+  int64_t total = (int64_t)s->N * Ho * Wo;
+  if (!pix) {
+    *count = total;
+    return 0;
+  }
+  for (int64_t t = 0; t < npix; ++t)
+    if (pix[t] < 0 || pix[t] >= total) return -1;
+  *count = npix;
+  return 0;
+}
+
+int dcn4o_forward_f64(const dcn4o_shape* s, int dtype, const void* x,
+                      const void* om, const float* scales, double* y,
+                      const int64_t* pix, int64_t npix, int nthreads) {
+  int32_t Ho, Wo;
+  int64_t count;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  if (resolve_pixels(s, Ho, Wo, pix, npix, &count)) return -1;
+  const int K = s->kh * s->kw, G = s->G, C = s->C, D = C / G;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t t = 0; t < count; ++t) {
+    int64_t p = pix ? pix[t] : t; /* flat output pixel (n*Ho+yo)*Wo+xo */
+    int n = (int)(p / ((int64_t)Ho * Wo));
+    int yo = (int)((p / Wo) % Ho);
+    int xo = (int)(p % Wo);
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (p * G + g) * 3 * K; /* R4 */
+      double sg = s->multiscale ? (double)scales[g] : 1.0;
+      for (int d = 0; d < D; ++d) {
+        int c = g * D + d;
+        double acc = 0.0;
+        for (int i = 0; i < s->kh; ++i) {
+          for (int j = 0; j < s->kw; ++j) {
+            int k = i * s->kw + j; /* R3 */
+            double dx = load_f32(dtype, om, row + 2 * k);
+            double dy = load_f32(dtype, om, row + 2 * k + 1);
+            double m = load_f32(dtype, om, row + 2 * K + k);
+            double py, px;
+            location_f64(s, yo, xo, i, j, dx, dy, sg, &py, &px);
+            acc += m * bilinear_zero_pad(s, dtype, x, n, c, py, px);
+          }
+        }
+        y[t * C + c] = acc;
+      }
+    }
+  }
+  return 0;
+}
+
+int dcn4o_count_terms(const dcn4o_shape* s, int dtype, const void* om,
+                      const float* scales, int64_t* corner_terms,
+                      int64_t* inbounds_terms) {
+  int32_t Ho, Wo;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  const int K = s->kh * s->kw, G = s->G, D = s->C / G;
+  int64_t terms = 0, inbounds = 0;
+  /* Walk the sample points of the definition; each point of a group has four
+   * corner terms for each of the group's D channels. */
+  int64_t total = (int64_t)s->N * Ho * Wo;
+  for (int64_t p = 0; p < total; ++p) {
+    int yo = (int)((p / Wo) % Ho), xo = (int)(p % Wo);
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (p * G + g) * 3 * K;
+      double sg = s->multiscale ? (double)scales[g] : 1.0;
+      for (int k = 0; k < K; ++k) {
+        int i = k / s->kw, j = k % s->kw;
+        double dx = load_f32(dtype, om, row + 2 * k);
+        double dy = load_f32(dtype, om, row + 2 * k + 1);
+        double py, px;
+        location_f64(s, yo, xo, i, j, dx, dy, sg, &py, &px);
+        double y0 = floor(py), x0 = floor(px);
+        for (int a = 0; a < 2; ++a)
+          for (int b = 0; b < 2; ++b) {
+            double yy = y0 + a, xx = x0 + b;
+            terms += D;
+            if (yy >= 0.0 && yy < s->H && xx >= 0.0 && xx < s->W) inbounds += D;
+          }
+      }
+    }
+  }
+  if (corner_terms) *corner_terms = terms;
+  if (inbounds_terms) *inbounds_terms = inbounds;
+  return 0;
+}
+
+/* ------------------------------------------------------- the fp32 evaluation
+ * Same sum, every step one fp32 operation in the order R8 fixes.  The
+ * geometry of one sample point is written out once here and used both by the
+ * forward evaluation and by the geometry dump. */
+typedef struct {
+  int inside;
+  int y0, x0;
+  float lh, lw;
+} geom_t;
+
+static geom_t sample_geometry_f32(const dcn4o_shape* s, int yo, int xo, int i,
+                                  int j, float dx, float dy, float sg) {
+  float py, px;
+  if (s->multiscale) {
+    int hy = (s->kh - 1) / 2, hx = (s->kw - 1) / 2;
+    float cy = (float)(yo * s->sh - s->ph + hy);
+    float cx = (float)(xo * s->sw - s->pw + hx);
+    float uy = (float)(i - hy) + dy; /* grid + direction */
+    float ux = (float)(j - hx) + dx;
+    float vy = sg * uy; /* times the group's scale */
+    float vx = sg * ux;
+    py = cy + vy;
+    px = cx + vx;
+  } else {
+    float by = (float)(yo * s->sh - s->ph + i * s->dh); /* exact integer */
+    float bx = (float)(xo * s->sw - s->pw + j * s->dw);
+    float oy = s->offset_scale * dy;
+    float ox = s->offset_scale * dx;
+    py = by + oy;
+    px = bx + ox;
+  }
+  geom_t r = {0, 0, 0, 0.0f, 0.0f};
+  if (!(py > -1.0f && py < (float)s->H && px > -1.0f && px < (float)s->W))
+    return r; /* all four corners are padding (and NaN locations land here) */
+  float fy = floorf(py), fx = floorf(px);
+  r.inside = 1;
+  r.y0 = (int)fy;
+  r.x0 = (int)fx;
+  r.lh = py - fy;
+  r.lw = px - fx;
+  return r;
+}
+
+int dcn4o_forward_f32(const dcn4o_shape* s, int dtype, const void* x,
+                      const void* om, const float* scales, void* y, float* acc_out,
+                      const int64_t* pix, int64_t npix, int nthreads) {
+  int32_t Ho, Wo;
+  int64_t count;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  if (resolve_pixels(s, Ho, Wo, pix, npix, &count)) return -1;
+  const int K = s->kh * s->kw, G = s->G, C = s->C, D = C / G;
+  const int H = s->H, W = s->W;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t t = 0; t < count; ++t) {
+    int64_t p = pix ? pix[t] : t;
+    int n = (int)(p / ((int64_t)Ho * Wo));
+    int yo = (int)((p / Wo) % Ho);
+    int xo = (int)(p % Wo);
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (p * G + g) * 3 * K;
+      float sg = s->multiscale ? scales[g] : 1.0f;
+      for (int d = 0; d < D; ++d) {
+        int c = g * D + d;
+        float acc = 0.0f;
+        for (int i = 0; i < s->kh; ++i) {
+          for (int j = 0; j < s->kw; ++j) {
+            int k = i * s->kw + j;
+            float dx = load_f32(dtype, om, row + 2 * k);
+            float dy = load_f32(dtype, om, row + 2 * k + 1);
+            float m = load_f32(dtype, om, row + 2 * K + k);
+            geom_t q = sample_geometry_f32(s, yo, xo, i, j, dx, dy, sg);
+            if (!q.inside) continue;
+            float hh = 1.0f - q.lh, hw = 1.0f - q.lw;
+            const int cy[4] = {q.y0, q.y0, q.y0 + 1, q.y0 + 1};
+            const int cx[4] = {q.x0, q.x0 + 1, q.x0, q.x0 + 1};
+            const float w[4] = {hh * hw, hh * q.lw, q.lh * hw, q.lh * q.lw};
+            for (int r = 0; r < 4; ++r) {
+              if (cy[r] < 0 || cy[r] >= H || cx[r] < 0 || cx[r] >= W) continue;
+              int64_t idx = (((int64_t)n * H + cy[r]) * W + cx[r]) * C + c;
+              float coef = m * w[r];
+              acc = fmaf(coef, load_f32(dtype, x, idx), acc);
+            }
+          }
+        }
+        if (acc_out) acc_out[t * C + c] = acc;
+        store_io(dtype, y, t * C + c, acc);
+      }
+    }
+  }
+  return 0;
+}
+
+int dcn4o_geometry(const dcn4o_shape* s, int dtype, const void* om,
+                   const float* scales, int32_t* y0, int32_t* x0, float* lh,
+                   float* lw, uint8_t* inside, const int64_t* pix,
+                   int64_t npix) {
+  int32_t Ho, Wo;
+  int64_t count;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  if (resolve_pixels(s, Ho, Wo, pix, npix, &count)) return -1;
+  const int K = s->kh * s->kw, G = s->G;
+  for (int64_t t = 0; t < count; ++t) {
+    int64_t p = pix ? pix[t] : t;
+    int yo = (int)((p / Wo) % Ho), xo = (int)(p % Wo);
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (p * G + g) * 3 * K;
+      float sg = s->multiscale ? scales[g] : 1.0f;
+      for (int k = 0; k < K; ++k) {
+        int i = k / s->kw, j = k % s->kw;
+        float dx = load_f32(dtype, om, row + 2 * k);
+        float dy = load_f32(dtype, om, row + 2 * k + 1);
+        geom_t q = sample_geometry_f32(s, yo, xo, i, j, dx, dy, sg);
+        int64_t e = (t * G + g) * K + k;
+        inside[e] = (uint8_t)q.inside;
+        y0[e] = q.y0;
+        x0[e] = q.x0;
+        lh[e] = q.lh;
+        lw[e] = q.lw;
+      }
+    }
+  }
+  return 0;
+}

@@ -1,0 +1,17 @@
+"""Test configuration: repo root on sys.path and the ``gpu`` marker.
+
+Tests marked ``gpu`` need a real MI355X (gfx950) and the built HIP library;
+everything else runs on the CPU."""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TESTS = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, TESTS):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X GPU and the built HIP library")

@@ -1,0 +1,625 @@
+"""Pins of the CPU oracle: facts fixed by the pages or by mathematics that the
+oracle must reproduce.  Each pin takes an ``oracle.Oracle`` and raises
+AssertionError on a mismatch, so the same pins can be run against deliberately
+broken oracle builds (test_oracle_mutants.py) to show that a plausible mistake
+anywhere in the oracle fails at least one of them.
+
+Pages cited (by title and section):
+  [DCNv4 digest]  CSDN "（论文速读）DCNv4：高效可变形卷积算子"
+  [FlowDCN]       kler.cn "NeurIPS'24 | FlowDCN：基于可变形卷积的任意分辨率图像生成模型"
+  [CANN Conv2D]   intelliparadigm "CANN ops-nn 算子与 Stable Diffusion 的卷积实现"
+
+Inputs are small and mostly dyadic (multiples of powers of two) so that the
+expected values are exact in fp32 and fp64 and equality can be required.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import Shape
+from workloads import from_raw, to_raw
+
+DTYPES = ("f32", "bf16", "f16")
+
+
+# ----------------------------------------------------------------- helpers
+def pack_om(dx, dy, m):
+    """[...,K] offsets x, offsets y, weights -> om [...,3K]: K interleaved
+    (dx, dy) pairs then K weights (the boundary's layout)."""
+    K = m.shape[-1]
+    om = np.empty(m.shape[:-1] + (3 * K,), np.float32)
+    om[..., 0:2 * K:2] = dx
+    om[..., 1:2 * K:2] = dy
+    om[..., 2 * K:] = m
+    return om
+
+
+def dyadic(rng, shape, lo, hi, denom):
+    """uniform multiples of 1/denom in [lo, hi]"""
+    a = rng.integers(int(round(lo * denom)), int(round(hi * denom)) + 1, size=shape)
+    return (a / denom).astype(np.float32)
+
+
+def run(o, s, dtype, x, om, scales=None):
+    """(fp64 definition, fp32 evaluation decoded to float64)"""
+    xr, omr = to_raw(x, dtype), to_raw(om, dtype)
+    y64 = o.forward_f64(s, dtype, xr, omr, scales, nthreads=2)
+    y32 = from_raw(o.forward_f32(s, dtype, xr, omr, scales, nthreads=2),
+                   dtype).astype(np.float64)
+    return y64, y32
+
+
+def exact_equal(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    if got.dtype.kind == "f" or want.dtype.kind == "f":
+        got, want = got.astype(np.float64), want.astype(np.float64)
+    bad = ~((got == want) | (np.isnan(got) & np.isnan(want)))
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} differ; "
+                           f"first got {got[bad][:3]} want {want[bad][:3]}")
+
+
+# Output size of the textbook convolution with padding and dilation
+# ([CANN Conv2D] 2.1 extended), written out here independently of the oracle.
+def conv_out(H, k, s, p, d):
+    return (H + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+# ------------------------------------------------------------------- pins
+def pin_output_size(o):
+    """Output size equals the textbook convolution arithmetic."""
+    cases = [Shape(1, 16, 16, 64, 4), Shape(2, 32, 32, 8, 2, dh=2, dw=2),
+             Shape(1, 9, 7, 4, 1, kh=5, kw=3, sh=2, sw=2, ph=2, pw=0),
+             Shape(1, 5, 5, 2, 2, kh=1, kw=1, ph=0, pw=0)]
+    for s in cases:
+        ho, wo = o.out_size(s)
+        assert (ho, wo) == (conv_out(s.H, s.kh, s.sh, s.ph, s.dh),
+                            conv_out(s.W, s.kw, s.sw, s.pw, s.dw)), s
+    # the wide dilated block keeps padding 1 with dilation 2: 32 -> 30
+    assert o.out_size(Shape(16, 32, 32, 1280, 40, dh=2, dw=2)) == (30, 30)
+
+
+def pin_identity(o):
+    """Zero offsets and a one-hot weight on the centre tap reproduce the input
+    when the padding equals dilation*(k-1)/2 and the stride is 1."""
+    rng = np.random.default_rng(1)
+    for (kh, kw, dh, dw) in [(3, 3, 1, 1), (3, 3, 2, 2), (5, 5, 1, 1),
+                             (3, 5, 1, 2), (1, 1, 1, 1)]:
+        s = Shape(2, 7, 9, 8, 2, kh=kh, kw=kw, ph=dh * (kh - 1) // 2,
+                  pw=dw * (kw - 1) // 2, dh=dh, dw=dw)
+        K = kh * kw
+        ho, wo = o.out_size(s)
+        assert (ho, wo) == (s.H, s.W)
+        x = dyadic(rng, (s.N, s.H, s.W, s.C), -4, 4, 8)
+        z = np.zeros((s.N, ho, wo, s.G, K), np.float32)
+        m = z.copy()
+        m[..., (kh // 2) * kw + kw // 2] = 1.0
+        om = pack_om(z, z, m)
+        for dt in DTYPES:
+            y64, y32 = run(o, s, dt, x, om)
+            exact_equal(y64, x, f"identity f64 {dt} k{kh}x{kw} d{dh},{dw}")
+            exact_equal(y32, x, f"identity f32 {dt} k{kh}x{kw} d{dh},{dw}")
+
+
+def _gather_expected(s, x, dx, dy, m):
+    """y = sum_k m_k * x[row_k, col_k] with integer rows/cols from the
+    convolution index (y*s - p + i*d, [CANN Conv2D] 2.1) plus the offset;
+    zero where the index leaves the image."""
+    N, H, W, C = x.shape
+    ho, wo = conv_out(H, s.kh, s.sh, s.ph, s.dh), conv_out(W, s.kw, s.sw, s.pw, s.dw)
+    D = C // s.G
+    y = np.zeros((N, ho, wo, C), np.float64)
+    for n in range(N):
+        for yo in range(ho):
+            for xo in range(wo):
+                for g in range(s.G):
+                    for i in range(s.kh):
+                        for j in range(s.kw):
+                            k = i * s.kw + j
+                            r = yo * s.sh - s.ph + i * s.dh + s.offset_scale * dy[n, yo, xo, g, k]
+                            c = xo * s.sw - s.pw + j * s.dw + s.offset_scale * dx[n, yo, xo, g, k]
+                            r, c = int(r), int(c)
+                            if 0 <= r < H and 0 <= c < W:
+                                y[n, yo, xo, g * D:(g + 1) * D] += (
+                                    float(m[n, yo, xo, g, k]) *
+                                    x[n, r, c, g * D:(g + 1) * D].astype(np.float64))
+    return y
+
+
+def pin_integer_gather(o):
+    """Integer offsets make every sample land on a pixel: the output is an
+    exact weighted gather of shifted input pixels (zero outside)."""
+    rng = np.random.default_rng(2)
+    shapes = [Shape(2, 6, 7, 6, 3),
+              Shape(1, 9, 8, 4, 2, kh=3, kw=5, sh=2, sw=1, ph=0, pw=2, dh=2, dw=1),
+              Shape(1, 8, 8, 4, 1, kh=2, kw=2, ph=0, pw=1),
+              Shape(1, 7, 6, 4, 2, offset_scale=2.0)]
+    for s in shapes:
+        ho, wo = o.out_size(s)
+        K = s.K
+        dx = rng.integers(-3, 4, (s.N, ho, wo, s.G, K)).astype(np.float32)
+        dy = rng.integers(-3, 4, (s.N, ho, wo, s.G, K)).astype(np.float32)
+        # one-hot taps first, then all taps weighted
+        onehot = np.zeros((s.N, ho, wo, s.G, K), np.float32)
+        idx = rng.integers(0, K, (s.N, ho, wo, s.G))
+        np.put_along_axis(onehot, idx[..., None], 0.5, axis=-1)
+        multi = dyadic(rng, (s.N, ho, wo, s.G, K), -2, 2, 4)
+        x = dyadic(rng, (s.N, s.H, s.W, s.C), -8, 8, 4)
+        for m in (onehot, multi):
+            want = _gather_expected(s, x, dx, dy, m)
+            for dt in DTYPES:
+                y64, y32 = run(o, s, dt, x, pack_om(dx, dy, m))
+                exact_equal(y64, want, f"gather f64 {dt} {s}")
+                exact_equal(y32, from_raw(to_raw(want, dt), dt), f"gather f32 {dt} {s}")
+
+
+def pin_affine_reproduction(o):
+    """Bilinear interpolation reproduces affine functions exactly: with
+    x[.,r,c,ch] = a_ch*r + b_ch*c + e_ch and all four corners inside the
+    image, each sample equals a*py + b*px + e at the sampled location.  This
+    fixes which fraction weights rows and which columns, and the offset order
+    (dx along W, dy along H)."""
+    rng = np.random.default_rng(3)
+    for s in [Shape(1, 12, 13, 4, 2, ph=0, pw=0),
+              Shape(2, 14, 12, 6, 3, kh=3, kw=3, ph=0, pw=0, dh=2, dw=1)]:
+        ho, wo = o.out_size(s)
+        K = s.K
+        rows = np.arange(s.H, dtype=np.float32)[:, None, None]
+        cols = np.arange(s.W, dtype=np.float32)[None, :, None]
+        a = rng.integers(-2, 3, s.C).astype(np.float32)
+        b = rng.integers(-2, 3, s.C).astype(np.float32)
+        a[0], b[0] = 1, 0  # a pure row ramp and
+        a[1], b[1] = 0, 1  # a pure column ramp
+        e = rng.integers(-4, 5, s.C).astype(np.float32)
+        x = np.broadcast_to(a * rows + b * cols + e, (s.N, s.H, s.W, s.C)).copy()
+        # multiples of 1/32 and 1/8 keep every fp32 partial sum exact
+        dx = dyadic(rng, (s.N, ho, wo, s.G, K), -1.5, 1.5, 32)
+        dy = dyadic(rng, (s.N, ho, wo, s.G, K), -1.5, 1.5, 32)
+        m = dyadic(rng, (s.N, ho, wo, s.G, K), -1, 1, 8)
+        D = s.C // s.G
+        want = np.zeros((s.N, ho, wo, s.C), np.float64)
+        for i in range(s.kh):
+            for j in range(s.kw):
+                k = i * s.kw + j
+                py = (np.arange(ho)[None, :, None, None] * s.sh - s.ph + i * s.dh) + dy[..., k]
+                px = (np.arange(wo)[None, None, :, None] * s.sw - s.pw + j * s.dw) + dx[..., k]
+                val = (np.repeat(py, D, -1) * a + np.repeat(px, D, -1) * b + e)
+                want += np.repeat(m[..., k], D, -1) * val
+        # compare where every sample of the pixel is at least 1.5 px inside
+        r0 = 2
+        for dt in ("f32", "bf16"):
+            y64, y32 = run(o, s, dt, x, pack_om(dx, dy, m))
+            sl = (slice(None), slice(r0, ho - r0 - s.dh), slice(r0, wo - r0 - s.dw))
+            exact_equal(y64[sl], want[sl], f"affine f64 {dt}")
+            exact_equal(y32[sl], from_raw(to_raw(want[sl], dt), dt), f"affine f32 {dt}")
+
+
+def _depthwise_bruteforce(x, wk, s):
+    """[CANN Conv2D] 2.1's convolution, per channel (depthwise), with stride,
+    zero padding and dilation; wk[c, i, j]."""
+    N, H, W, C = x.shape
+    ho, wo = conv_out(H, s.kh, s.sh, s.ph, s.dh), conv_out(W, s.kw, s.sw, s.pw, s.dw)
+    y = np.zeros((N, ho, wo, C))
+    for yo in range(ho):
+        for xo in range(wo):
+            for i in range(s.kh):
+                for j in range(s.kw):
+                    r = yo * s.sh - s.ph + i * s.dh
+                    c = xo * s.sw - s.pw + j * s.dw
+                    if 0 <= r < H and 0 <= c < W:
+                        y[:, yo, xo, :] += x[:, r, c, :] * wk[:, i, j]
+    return y
+
+
+def pin_depthwise_conv(o):
+    """Zero offsets and per-group weights that do not vary over pixels turn
+    the operator into a depthwise convolution whose kernel is shared inside
+    each group.  Checked against the textbook loop and torch's conv2d."""
+    import torch
+    rng = np.random.default_rng(4)
+    for s in [Shape(2, 9, 8, 8, 2), Shape(1, 11, 10, 6, 3, kh=3, kw=5, sh=2, sw=1,
+                                          ph=1, pw=2, dh=1, dw=2)]:
+        ho, wo = o.out_size(s)
+        K, D = s.K, s.C // s.G
+        wg = rng.standard_normal((s.G, K)).astype(np.float32) / 3
+        m = np.broadcast_to(wg, (s.N, ho, wo, s.G, K)).copy()
+        z = np.zeros_like(m)
+        x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
+        wk = np.repeat(wg, D, axis=0).reshape(s.C, s.kh, s.kw).astype(np.float64)
+        want = _depthwise_bruteforce(x.astype(np.float64), wk, s)
+        ref = torch.nn.functional.conv2d(
+            torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2),
+            torch.from_numpy(wk)[:, None], stride=(s.sh, s.sw),
+            padding=(s.ph, s.pw), dilation=(s.dh, s.dw), groups=s.C)
+        ref = ref.permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(want, ref, rtol=1e-12, atol=1e-12)
+        y64, y32 = run(o, s, "f32", x, pack_om(z, z, m))
+        scale = np.sqrt(np.mean(want ** 2))
+        assert np.max(np.abs(y64 - want)) <= 1e-12 * scale, "depthwise f64"
+        assert np.max(np.abs(y32 - want)) <= 1e-5 * scale, "depthwise f32"
+
+
+def pin_zero_padding(o):
+    """Samples far outside the image contribute exactly zero; a sample with a
+    single corner inside contributes m * (corner weight) * value."""
+    rng = np.random.default_rng(5)
+    s = Shape(2, 6, 5, 4, 2)
+    ho, wo = o.out_size(s)
+    K = s.K
+    sign = rng.choice([-1.0, 1.0], (s.N, ho, wo, s.G, K)).astype(np.float32)
+    far = 1000.0 * sign
+    m = rng.standard_normal((s.N, ho, wo, s.G, K)).astype(np.float32)
+    x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
+    for dt in DTYPES:
+        y64, y32 = run(o, s, dt, x, pack_om(far, -far, m))
+        exact_equal(y64, 0 * y64, f"far samples f64 {dt}")
+        exact_equal(y32, 0 * y32, f"far samples f32 {dt}")
+    # single-corner samples: output (0,0), tap (0,0) sits at (-1,-1)+(t,u):
+    # only corner (0,0) is inside, weight t*u.  Output (Ho-1,Wo-1), tap (2,2)
+    # sits at (H,W)+(t-1,u-1): only corner (H-1,W-1), weight (1-t)*(1-u).
+    t, u = 0.375, 0.8125
+    dx = np.zeros((s.N, ho, wo, s.G, K), np.float32)
+    dy = np.zeros_like(dx)
+    mm = np.zeros_like(dx)
+    dy[:, 0, 0, :, 0], dx[:, 0, 0, :, 0], mm[:, 0, 0, :, 0] = t, u, 2.0
+    dy[:, -1, -1, :, 8], dx[:, -1, -1, :, 8], mm[:, -1, -1, :, 8] = t - 1, u - 1, -0.5
+    xd = dyadic(rng, (s.N, s.H, s.W, s.C), -4, 4, 8)
+    for dt in ("f32", "bf16"):
+        y64, y32 = run(o, s, dt, xd, pack_om(dx, dy, mm))
+        w0 = 2.0 * t * u * xd[:, 0, 0, :]
+        w1 = -0.5 * (1 - t) * (1 - u) * xd[:, -1, -1, :]
+        exact_equal(y64[:, 0, 0, :], w0, f"corner (0,0) f64 {dt}")
+        exact_equal(y64[:, -1, -1, :], w1, f"corner (H-1,W-1) f64 {dt}")
+        exact_equal(y32[:, 0, 0, :], from_raw(to_raw(w0, dt), dt), f"corner (0,0) f32 {dt}")
+        exact_equal(y32[:, -1, -1, :], from_raw(to_raw(w1, dt), dt), f"corner (H-1,W-1) f32 {dt}")
+        assert not y64[:, 1:-1].any() and not y32[:, 1:-1].any()
+
+
+def pin_partition_of_unity(o):
+    """The four bilinear weights sum to one: a constant input c gives
+    c * sum_k m_k wherever all corners are inside."""
+    rng = np.random.default_rng(6)
+    s = Shape(2, 12, 11, 6, 3, ph=0, pw=0)
+    ho, wo = o.out_size(s)
+    K = s.K
+    cval = dyadic(rng, (s.C,), -3, 3, 4)
+    x = np.broadcast_to(cval, (s.N, s.H, s.W, s.C)).copy()
+    dx = dyadic(rng, (s.N, ho, wo, s.G, K), 0, 0.9375, 16)
+    dy = dyadic(rng, (s.N, ho, wo, s.G, K), 0, 0.9375, 16)
+    m = dyadic(rng, (s.N, ho, wo, s.G, K), -1, 1, 8)
+    want = np.repeat(m.sum(-1), s.C // s.G, -1) * cval
+    for dt in DTYPES:
+        y64, y32 = run(o, s, dt, x, pack_om(dx, dy, m))
+        sl = (slice(None), slice(0, ho - 1), slice(0, wo - 1))
+        exact_equal(y64[sl], want[sl], f"unity f64 {dt}")
+        exact_equal(y32[sl], from_raw(to_raw(want[sl], dt), dt), f"unity f32 {dt}")
+
+
+def pin_linearity(o):
+    """The output is linear in the weights m and in the input x (exact on
+    dyadic data)."""
+    rng = np.random.default_rng(7)
+    s = Shape(1, 8, 9, 8, 2, sh=2, sw=1)
+    ho, wo = o.out_size(s)
+    K = s.K
+    dx = dyadic(rng, (s.N, ho, wo, s.G, K), -2, 2, 16)
+    dy = dyadic(rng, (s.N, ho, wo, s.G, K), -2, 2, 16)
+    m1 = dyadic(rng, (s.N, ho, wo, s.G, K), -1, 1, 16)
+    m2 = dyadic(rng, (s.N, ho, wo, s.G, K), -1, 1, 16)
+    x1 = dyadic(rng, (s.N, s.H, s.W, s.C), -2, 2, 8)
+    x2 = dyadic(rng, (s.N, s.H, s.W, s.C), -2, 2, 8)
+    y = lambda x, m: run(o, s, "f32", x, pack_om(dx, dy, m))
+    a1, b1 = y(x1, m1)
+    a2, b2 = y(x1, m2)
+    a3, b3 = y(x1, 2 * m1 - 0.5 * m2)
+    exact_equal(a3, 2 * a1 - 0.5 * a2, "linear in m f64")
+    exact_equal(b3, 2 * b1 - 0.5 * b2, "linear in m f32")
+    c1, d1 = y(x2, m1)
+    c3, d3 = y(x1 + x2, m1)
+    exact_equal(c3, a1 + c1, "linear in x f64")
+    exact_equal(d3, b1 + d1, "linear in x f32")
+    assert np.abs(a1).max() > 0.5
+
+
+def pin_multiscale(o):
+    """FlowDCN groupwise multi-scale geometry ([FlowDCN] 3.1):
+    (a) s_g = 1 with direction d equals standard mode with offset d;
+    (b) integer s_g with zero direction equals standard mode with dilation s_g
+        and padding p + s_g - 1 (3x3), i.e. the group samples a dilated grid;
+    (c) fractional s_g on an affine input samples at centre + s_g*grid."""
+    rng = np.random.default_rng(8)
+    base = Shape(2, 10, 9, 8, 4, multiscale=True)
+    ho, wo = o.out_size(base)
+    K = base.K
+    D = base.C // base.G
+    x = dyadic(rng, (base.N, base.H, base.W, base.C), -4, 4, 8)
+    dx = dyadic(rng, (base.N, ho, wo, base.G, K), -1, 1, 32)
+    dy = dyadic(rng, (base.N, ho, wo, base.G, K), -1, 1, 32)
+    m = dyadic(rng, (base.N, ho, wo, base.G, K), -1, 1, 8)
+    ones = np.ones(base.G, np.float32)
+    std = Shape(2, 10, 9, 8, 4)
+    for dt in ("f32", "bf16"):
+        a64, a32 = run(o, base, dt, x, pack_om(dx, dy, m), ones)
+        b64, b32 = run(o, std, dt, x, pack_om(dx, dy, m))
+        exact_equal(a64, b64, f"ms s=1 f64 {dt}")
+        exact_equal(a32, b32, f"ms s=1 f32 {dt}")
+    z = np.zeros_like(dx)
+    sg = np.array([1, 2, 3, 2], np.float32)
+    a64, a32 = run(o, base, "f32", x, pack_om(z, z, m), sg)
+    for g in range(base.G):
+        sgi = int(sg[g])
+        st = Shape(2, 10, 9, 8, 4, ph=1 + sgi - 1, pw=1 + sgi - 1, dh=sgi, dw=sgi)
+        b64, b32 = run(o, st, "f32", x, pack_om(z, z, m))
+        sl = (Ellipsis, slice(g * D, (g + 1) * D))
+        exact_equal(a64[sl], b64[sl], f"ms dilated group {g} f64")
+        exact_equal(a32[sl], b32[sl], f"ms dilated group {g} f32")
+    # (c) affine input, fractional scales, sample = centre + s*(grid + dir)
+    s = Shape(1, 16, 16, 4, 2, multiscale=True)
+    ho, wo = o.out_size(s)
+    rows = np.arange(s.H, dtype=np.float32)[:, None, None]
+    cols = np.arange(s.W, dtype=np.float32)[None, :, None]
+    av = np.array([1, 0, 2, -1], np.float32)
+    bv = np.array([0, 1, 1, 2], np.float32)
+    xa = (av * rows + bv * cols)[None]
+    sg = np.array([1.5, 2.25], np.float32)
+    ddx = dyadic(rng, (1, ho, wo, s.G, K), -0.5, 0.5, 16)
+    ddy = dyadic(rng, (1, ho, wo, s.G, K), -0.5, 0.5, 16)
+    mm = dyadic(rng, (1, ho, wo, s.G, K), -1, 1, 4)
+    want = np.zeros((1, ho, wo, s.C))
+    for k in range(K):
+        i, j = divmod(k, 3)
+        py = np.arange(ho)[None, :, None, None] + np.repeat(sg, 2) * (i - 1 + np.repeat(ddy[..., k], 2, -1))
+        px = np.arange(wo)[None, None, :, None] + np.repeat(sg, 2) * (j - 1 + np.repeat(ddx[..., k], 2, -1))
+        want += np.repeat(mm[..., k], 2, -1) * (av * py + bv * px)
+    y64, y32 = run(o, s, "f32", xa, pack_om(ddx, ddy, mm), sg)
+    r = 5  # max reach 2.25*1.5 < 4 px: corners of rows/cols 5..10 are inside
+    sl = (slice(None), slice(r, ho - r), slice(r, wo - r))
+    exact_equal(y64[sl], want[sl], "ms affine f64")
+    exact_equal(y32[sl], want[sl], "ms affine f32")
+
+
+def pin_nonfinite_offsets(o):
+    """A NaN or infinite offset puts the sample nowhere in the image: the
+    output equals the one where that point's weight is zero."""
+    rng = np.random.default_rng(9)
+    s = Shape(1, 6, 6, 4, 2)
+    ho, wo = o.out_size(s)
+    K = s.K
+    dx = dyadic(rng, (1, ho, wo, s.G, K), -1, 1, 16)
+    dy = dyadic(rng, (1, ho, wo, s.G, K), -1, 1, 16)
+    m = dyadic(rng, (1, ho, wo, s.G, K), -1, 1, 8)
+    x = dyadic(rng, (1, s.H, s.W, s.C), -2, 2, 8)
+    dx2, dy2, m0 = dx.copy(), dy.copy(), m.copy()
+    dx2[..., 4] = np.nan
+    dy2[..., 2] = np.inf
+    m0[..., 4] = 0
+    m0[..., 2] = 0
+    for dt in ("f32", "bf16", "f16"):
+        a64, a32 = run(o, s, dt, x, pack_om(dx2, dy2, m))
+        b64, b32 = run(o, s, dt, x, pack_om(dx, dy, m0))
+        exact_equal(a64, b64, f"non-finite offsets f64 {dt}")
+        exact_equal(a32, b32, f"non-finite offsets f32 {dt}")
+
+
+def _cost_model():
+    """The cost-model figures printed on the DCNv4 digest page (golden file)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "dcnv4_cost_model.json")) as f:
+        return json.load(f)
+
+
+def pin_term_count(o):
+    """The definition has 4 bilinear corner terms per sample point and
+    channel: 36*H*W*C per image for 3x3 with H and W kept ([DCNv4 digest],
+    "GPU效率的理论分析")."""
+    cm = _cost_model()
+    f = cm["flops_per_HWC"]
+    assert f == cm["flops_factors"]["spatial_points"] * cm["flops_factors"]["bilinear_corners"]
+    rng = np.random.default_rng(10)
+    for s, want in [(Shape(1, 16, 16, 64, 4), f * 16 * 16 * 64),
+                    (Shape(3, 10, 12, 8, 2), 3 * f * 10 * 12 * 8),
+                    (Shape(1, 9, 9, 4, 1, kh=5, kw=5, ph=2, pw=2), 4 * 25 * 81 * 4)]:
+        ho, wo = o.out_size(s)
+        om = rng.uniform(-3, 3, (s.N, ho, wo, s.G, 3 * s.K)).astype(np.float32)
+        terms, inb = o.count_terms(s, "f32", om)
+        assert terms == want, (terms, want)
+        assert 0 < inb < terms
+
+
+def pin_ideal_bytes(o):
+    """Ideal traffic 2HWC + 27HWG elements for 3x3 ([DCNv4 digest],
+    "GPU效率的理论分析"); about 3.7HWC when G = C/16; the no-cache worst case is
+    36 + 27 + 1 = 64 accesses per output, about 17x the ideal; compute to
+    memory ratios from about 0.6 to 9.7 (figures in the golden file)."""
+    cm = _cost_model()
+    a, b = cm["ideal_elements"]["HWC"], cm["ideal_elements"]["HWG"]
+    s = Shape(1, 16, 16, 64, 4)
+    assert o.ideal_bytes(s, "f32") == 4 * (a * 16 * 16 * 64 + b * 16 * 16 * 4)
+    s = Shape(8, 128, 128, 320, 20)
+    assert o.ideal_bytes(s, "bf16") == 2 * 8 * (a * 128 * 128 * 320 + b * 128 * 128 * 20)
+    assert o.ideal_bytes(s, "bf16") == 309_329_920
+    ratio = a + b / 16
+    assert abs(ratio - cm["ideal_at_G_eq_C_over_16_HWC"]) < 0.02
+    wc = cm["worst_case_accesses_per_output"]
+    assert wc["interpolation_reads"] == cm["flops_per_HWC"]
+    assert wc["offset_weight_reads"] == b
+    assert wc["total"] == wc["interpolation_reads"] + wc["offset_weight_reads"] + wc["writes"]
+    assert abs(wc["total"] / ratio - cm["worst_over_ideal"]) < 0.5
+    lo, hi = cm["compute_to_memory_ratio_range"]
+    assert abs(cm["flops_per_HWC"] / wc["total"] - lo) < 0.05
+    assert abs(cm["flops_per_HWC"] / ratio - hi) < 0.1
+    # Ho != H: input and output counted at their own sizes, fp32 scales added
+    s = Shape(16, 32, 32, 1280, 40, dh=2, dw=2)
+    assert o.ideal_bytes(s, "f16") == 2 * (16 * 32 * 32 * 1280 + 16 * 30 * 30 * 1280
+                                           + 16 * 30 * 30 * 40 * 27)
+    s = Shape(32, 32, 32, 1152, 16, multiscale=True)
+    assert o.ideal_bytes(s, "bf16") == 2 * 32 * (2 * 32 * 32 * 1152 + 27 * 32 * 32 * 16) + 64
+
+
+def _exact_definition(s, x, dx, dy, m, sg=None):
+    """The definition in exact rational arithmetic (tiny shapes only)."""
+    N, H, W, C = x.shape
+    ho, wo = conv_out(H, s.kh, s.sh, s.ph, s.dh), conv_out(W, s.kw, s.sw, s.pw, s.dw)
+    D = C // s.G
+    y = np.empty((N, ho, wo, C), object)
+    for n in range(N):
+        for yo in range(ho):
+            for xo in range(wo):
+                for g in range(s.G):
+                    for d in range(D):
+                        c = g * D + d
+                        acc = Fraction(0)
+                        for i in range(s.kh):
+                            for j in range(s.kw):
+                                k = i * s.kw + j
+                                ddy = Fraction(float(dy[n, yo, xo, g, k]))
+                                ddx = Fraction(float(dx[n, yo, xo, g, k]))
+                                if s.multiscale:
+                                    hy, hx = (s.kh - 1) // 2, (s.kw - 1) // 2
+                                    S = Fraction(float(sg[g]))
+                                    py = yo * s.sh - s.ph + hy + S * (i - hy + ddy)
+                                    px = xo * s.sw - s.pw + hx + S * (j - hx + ddx)
+                                else:
+                                    os_ = Fraction(s.offset_scale)
+                                    py = yo * s.sh - s.ph + i * s.dh + os_ * ddy
+                                    px = xo * s.sw - s.pw + j * s.dw + os_ * ddx
+                                y0, x0 = math.floor(py), math.floor(px)
+                                lh, lw = py - y0, px - x0
+                                v = Fraction(0)
+                                for a, wa in ((0, 1 - lh), (1, lh)):
+                                    for b, wb in ((0, 1 - lw), (1, lw)):
+                                        r, cc = y0 + a, x0 + b
+                                        if 0 <= r < H and 0 <= cc < W:
+                                            v += wa * wb * Fraction(float(x[n, r, cc, c]))
+                                acc += Fraction(float(m[n, yo, xo, g, k])) * v
+                        y[n, yo, xo, c] = acc
+    return y
+
+
+def pin_exact_rational(o):
+    """On tiny random inputs the fp64 definition agrees with exact rational
+    arithmetic to 1e-12, and the fp32 evaluation to the fp32 error bound
+    (1e-5 of the output RMS, the fp32 tolerance)."""
+    rng = np.random.default_rng(11)
+    for s in [Shape(1, 5, 6, 4, 2), Shape(1, 6, 5, 4, 2, sh=2, sw=1, dh=2, dw=1, ph=2),
+              Shape(1, 5, 5, 4, 2, offset_scale=0.75),
+              Shape(1, 6, 6, 4, 2, multiscale=True)]:
+        ho, wo = o.out_size(s)
+        K = s.K
+        x = rng.standard_normal((1, s.H, s.W, s.C)).astype(np.float32)
+        dx = rng.uniform(-2, 2, (1, ho, wo, s.G, K)).astype(np.float32)
+        dy = rng.uniform(-2, 2, (1, ho, wo, s.G, K)).astype(np.float32)
+        m = (rng.standard_normal((1, ho, wo, s.G, K)) / 3).astype(np.float32)
+        sg = np.array([1.0, 2.5], np.float32) if s.multiscale else None
+        ex = _exact_definition(s, x, dx, dy, m, sg).astype(np.float64)
+        y64, y32 = run(o, s, "f32", x, pack_om(dx, dy, m), sg)
+        rms = np.sqrt(np.mean(ex ** 2))
+        assert np.max(np.abs(y64 - ex)) <= 1e-12 * rms, f"exact f64 {s}"
+        assert np.max(np.abs(y32 - ex)) <= 1e-5 * rms, f"exact f32 {s}"
+
+
+def pin_geometry(o):
+    """Sample locations next to integers and at the image border, where the
+    fp32 sums are exact: floor, fraction and the inside test are fixed."""
+    s = Shape(1, 16, 16, 4, 1, kh=1, kw=1, ph=0, pw=0)
+    ho, wo = o.out_size(s)
+    e = 2.0 ** -20
+    # (output row, dy, expected inside, y0, lh); case number q sits at output
+    # column q with dx = 0.25
+    cases = [(5, -e, 1, 4, 1 - e), (5, e, 1, 5, e), (5, -0.0, 1, 5, 0.0),
+             (0, -1.0, 0, 0, 0.0), (0, -1 + e, 1, -1, e), (0, -0.5, 1, -1, 0.5),
+             (15, 1 - 2 * e, 1, 15, 1 - 2 * e), (15, 1.0, 0, 0, 0.0),
+             (2, 2.0 ** -149, 1, 2, 0.0), (0, 2.0 ** -149, 1, 0, 2.0 ** -149)]
+    om = np.zeros((1, ho, wo, 1, 3), np.float32)
+    om[..., 2] = 1
+    om[..., 0] = 0.25
+    for q, (r, d, *_rest) in enumerate(cases):
+        om[0, r, q, 0, 1] = d
+    g = o.geometry(s, "f32", om)
+    for q, (r, d, ins, y0, lh) in enumerate(cases):
+        t = r * wo + q
+        assert g["inside"][t] == ins, (r, d)
+        if ins:
+            assert g["y0"][t] == y0 and g["lh"][t] == np.float32(lh), (r, d, g["y0"][t], g["lh"][t])
+            assert g["x0"][t] == q and g["lw"][t] == 0.25
+    # column direction and the stride/dilation base on a 3x3 dilated, strided grid
+    s = Shape(1, 20, 20, 4, 1, sh=2, sw=3, ph=1, pw=2, dh=2, dw=1)
+    ho, wo = o.out_size(s)
+    om = np.zeros((1, ho, wo, 1, 27), np.float32)
+    om[..., 0:18:2] = 0.5     # dx
+    om[..., 1:18:2] = -0.25   # dy
+    g = o.geometry(s, "f32", om)
+    for yo in range(ho):
+        for xo in range(wo):
+            for k in range(9):
+                i, j = divmod(k, 3)
+                t = (yo * wo + xo) * 9 + k
+                py = yo * 2 - 1 + 2 * i - 0.25
+                px = xo * 3 - 2 + j + 0.5
+                inside = -1 < py < 20 and -1 < px < 20
+                assert g["inside"][t] == inside
+                if inside:
+                    assert g["y0"][t] == math.floor(py) and g["lh"][t] == py - math.floor(py)
+                    assert g["x0"][t] == math.floor(px) and g["lw"][t] == px - math.floor(px)
+
+
+def pin_codecs(o):
+    """bf16/fp16 decode is exact and encode rounds to nearest even: checked
+    against torch's bf16 cast and numpy's float16 cast (library routines)."""
+    import torch
+    # every fp16 pattern decodes like numpy
+    allh = np.arange(65536, dtype=np.uint16)
+    ref = allh.view(np.float16).astype(np.float32)
+    got = np.array([o.f16_to_f32(int(h)) for h in allh[::7]], np.float32)
+    exact_equal(got, ref[::7], "f16 decode")
+    # bf16 decode: a few known patterns
+    for h, v in [(0x3F80, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -133), (0x7F80, np.inf)]:
+        assert o.bf16_to_f32(h) == v
+    rng = np.random.default_rng(12)
+    f = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-8, 8, 4000),
+        np.array([0.0, -0.0, 1.0, 65504, 65519.996, 65520, 1e-8, 6e-8, 2.0 ** -24,
+                  2.0 ** -25, 2.0 ** -25 * 1.5, 2.0 ** -14, np.inf, -np.inf, 3.0e38], np.float32),
+        # exact halfway cases for bf16 (ties to even both ways)
+        np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80C000],
+                 np.uint32).view(np.float32)])
+    with np.errstate(over="ignore"):
+        want16 = f.astype(np.float16).view(np.uint16)
+    got16 = np.array([o.f32_to_f16(float(v)) for v in f], np.uint16)
+    exact_equal(got16, want16, "f16 encode")
+    wantb = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    gotb = np.array([o.f32_to_bf16(float(v)) for v in f], np.uint16)
+    exact_equal(gotb, wantb, "bf16 encode")
+    assert np.isnan(o.bf16_to_f32(o.f32_to_bf16(float("nan"))))
+    assert np.isnan(o.f16_to_f32(o.f32_to_f16(float("nan"))))
+
+
+ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
+            pin_affine_reproduction, pin_depthwise_conv, pin_zero_padding,
+            pin_partition_of_unity, pin_linearity, pin_multiscale,
+            pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
+            pin_exact_rational, pin_geometry, pin_codecs]
+
+
+if __name__ == "__main__":
+    # Run every pin against the oracle library given on the command line and
+    # report the first one that fails (used on mutant builds, in a child
+    # process so that a crashing mutant cannot take the test runner down).
+    import sys
+    import oracle as _oracle
+    lib = _oracle.Oracle(sys.argv[1])
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            print(f"CAUGHT {pin.__name__}: {str(e)[:200]}")
+            sys.exit(0)
+        except ValueError as e:  # the mutant rejected a valid shape
+            print(f"CAUGHT {pin.__name__} (rejected): {str(e)[:200]}")
+            sys.exit(0)
+    print("MISSED")

@@ -1,0 +1,117 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that the pins catch every one of them: a dropped term, a wrong sign or index,
+a transposed operand, a lost parameter, a rounding slip in a codec.
+
+Each mutant is one textual change of ``oracle/dcn4_oracle.c``, compiled into
+a temporary library; the pins run in a child process so that a mutant that
+reads out of bounds cannot crash the test runner."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = open(oracle._SRC).read()
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def sub(old, new):
+    return lambda s: s.replace(old, new)
+
+
+def subs(*pairs):
+    """several replacements applied one after another"""
+    def f(s):
+        for old, new in pairs:
+            s = s.replace(old, new)
+        return s
+    return f
+
+
+MUTANTS = {
+    # offsets: x and y exchanged
+    "dxdy_swapped_f32": subs(("float dx = load_f32(dtype, om, row + 2 * k);",
+                              "float dx = load_f32(dtype, om, row + 2 * k + 1);"),
+                             ("float dy = load_f32(dtype, om, row + 2 * k + 1);",
+                              "float dy = load_f32(dtype, om, row + 2 * k);")),
+    "dxdy_swapped_f64": subs(("double dx = load_f32(dtype, om, row + 2 * k);",
+                              "double dx = load_f32(dtype, om, row + 2 * k + 1);"),
+                             ("double dy = load_f32(dtype, om, row + 2 * k + 1);",
+                              "double dy = load_f32(dtype, om, row + 2 * k);")),
+    # taps enumerated column-major
+    "tap_order_f64": sub("int k = i * s->kw + j; /* R3 */", "int k = j * s->kh + i;"),
+    "tap_order_f32": sub("            int k = i * s->kw + j;\n            float dx",
+                         "            int k = j * s->kh + i;\n            float dx"),
+    # a bilinear corner dropped
+    "corner_dropped_f32": sub("for (int r = 0; r < 4; ++r)", "for (int r = 0; r < 3; ++r)"),
+    "corner_dropped_f64": sub("if (yy >= 0.0 && yy < s->H && xx >= 0.0 && xx < s->W) {\n        int64_t idx",
+                              "if (!(a && b) && yy >= 0.0 && yy < s->H && xx >= 0.0 && xx < s->W) {\n        int64_t idx"),
+    # fraction measured from the wrong side
+    "row_fraction_flipped_f32": sub("r.lh = py - fy;", "r.lh = 1.0f - (py - fy);"),
+    "col_fraction_flipped_f64": sub("double lh = py - y0, lw = px - x0;",
+                                    "double lh = py - y0, lw = 1.0 - (px - x0);"),
+    # corner weights transposed
+    "weights_transposed_f32": sub("{hh * hw, hh * q.lw, q.lh * hw, q.lh * q.lw}",
+                                  "{hh * hw, q.lh * hw, hh * q.lw, q.lh * q.lw}"),
+    "weights_transposed_f64": sub("double w = (a ? lh : 1.0 - lh) * (b ? lw : 1.0 - lw);",
+                                  "double w = (a ? lw : 1.0 - lw) * (b ? lh : 1.0 - lh);"),
+    # convolution parameters lost or misapplied
+    "dilation_ignored_f32": sub("float by = (float)(yo * s->sh - s->ph + i * s->dh);",
+                                "float by = (float)(yo * s->sh - s->ph + i);"),
+    "dilation_ignored_f64": sub("*py = (double)(yo * s->sh - s->ph + i * s->dh)",
+                                "*py = (double)(yo * s->sh - s->ph + i)"),
+    "stride_ignored_f32": sub("float bx = (float)(xo * s->sw - s->pw + j * s->dw);",
+                              "float bx = (float)(xo - s->pw + j * s->dw);"),
+    "pad_sign_f64": sub("*px = (double)(xo * s->sw - s->pw + j * s->dw)",
+                        "*px = (double)(xo * s->sw + s->pw + j * s->dw)"),
+    "offset_scale_ignored_f32": sub("float oy = s->offset_scale * dy;", "float oy = dy;"),
+    "offset_scale_ignored_f64": sub("(double)s->offset_scale * dx", "dx"),
+    # multi-scale: scale on the grid only, or centre lost
+    "ms_scale_grid_only_f32": sub("float vy = sg * uy;", "float vy = sg * (float)(i - hy) + dy;"),
+    "ms_centre_lost_f64": sub("*px = (double)(xo * s->sw - s->pw + hx) + sg",
+                              "*px = (double)(xo * s->sw - s->pw) + sg"),
+    # group bookkeeping
+    "group_channels_interleaved": sub("int c = g * D + d;", "int c = d * s->G + g;"),
+    "group_row_shared": sub("const int64_t row = (p * G + g) * 3 * K;",
+                            "const int64_t row = (p * G) * 3 * K;"),
+    "weight_index_fixed_f32": sub("float m = load_f32(dtype, om, row + 2 * K + k);",
+                                  "float m = load_f32(dtype, om, row + 2 * K);"),
+    "weight_dropped_f32": sub("float coef = m * w[r];", "float coef = w[r];"),
+    "weight_dropped_f64": sub("acc += m * bilinear_zero_pad(", "acc += bilinear_zero_pad("),
+    # borders
+    "inside_test_low_f32": sub("if (!(py > -1.0f && py < (float)s->H",
+                               "if (!(py >= 0.0f && py < (float)s->H"),
+    "inside_test_high_f32": sub("px < (float)s->W))", "px < (float)(s->W - 1)))"),
+    "corner_bound_off_by_one_f64": sub("xx < s->W) {", "xx <= s->W) {"),
+    # codecs
+    "bf16_round_half_up": sub("u += 0x7fffu + lsb;", "u += 0x8000u;"),
+    "f16_subnormal_truncated": sub("double q = nearbyint(a * ldexp(1.0, 24));",
+                                   "double q = floor(a * ldexp(1.0, 24));"),
+    "f16_decode_bias": sub("v = ldexp((double)(1024 + f), e - 25);",
+                           "v = ldexp((double)(1024 + f), e - 24);"),
+    # counters and cost model
+    "term_count_per_group": sub("terms += D;", "terms += 1;"),
+    "ideal_bytes_om_2k": sub("int64_t om = (int64_t)s->N * Ho * Wo * s->G * 3 * K;",
+                             "int64_t om = (int64_t)s->N * Ho * Wo * s->G * 2 * K;"),
+    "output_size_off_by_one": sub("ho = ho / s->sh + 1;", "ho = ho / s->sh;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = MUTANTS[name](SRC)
+    assert src != SRC, f"mutant {name} does not change the oracle source"
+    csrc = tmp_path / "dcn4_oracle.c"
+    csrc.write_text(src)
+    (tmp_path / "dcn4_oracle.h").write_text(open(os.path.join(os.path.dirname(oracle._SRC), "dcn4_oracle.h")).read())
+    lib = str(tmp_path / "libmutant.so")
+    oracle.build(str(csrc), lib)
+    r = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), lib],
+                       capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(HERE),
+                       env={**os.environ, "PYTHONPATH": os.pathsep.join(
+                           [os.path.dirname(HERE), HERE])})
+    caught = r.returncode < 0 or "CAUGHT" in r.stdout
+    assert caught, f"mutant {name} passed every pin:\n{r.stdout}\n{r.stderr[-2000:]}"

@@ -1,0 +1,170 @@
+"""Seeded synthetic workloads for the DCNv4 forward operator.
+
+This module only draws random inputs of the shapes, value distributions and
+dtypes of the pages' workloads.  It holds none of the operator's arithmetic:
+the output size (Ho, Wo) is passed in by the caller, who takes it from the
+library under test or from the oracle.
+
+Inputs stand in for the pages' workloads (no dataset or trained weights are
+used): InternImage-like stages and latent-diffusion U-Net blocks
+([DCNv4 digest] = CSDN "（论文速读）DCNv4：高效可变形卷积算子", abstract; the
+U-Net tutorial at framerc.cn "从ConvNet到Diffusion：手把手把DCNv4塞进Stable
+Diffusion的U-Net里试试效果", section 2.2, for the 1280-channel blocks) and
+FlowDCN tokens ([FlowDCN] = kler.cn "NeurIPS'24 | FlowDCN：基于可变形卷积的任意
+分辨率图像生成模型", section 3.1, per-group scale priors).
+
+Recipe (every workload): draws in float32 from numpy's PCG64 seeded with the
+workload seed, in the order input, offsets, weights; x ~ N(0,1); weights m ~
+N(0, 1/9) (standard deviation 1/3); offsets per workload (uniform U[-a,a] or
+normal with the given variance); values are then rounded to the I/O dtype with
+round-to-nearest-even (torch's CPU cast for bf16, numpy's for fp16).
+The offset/weight tensor om has layout [N,Ho,Wo,G,3K]: per group the K
+interleaved (dx, dy) pairs first, then the K weights.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str                 # "f32" | "bf16" | "f16": input, om and output
+    N: int
+    H: int
+    W: int
+    C: int
+    G: int
+    kh: int = 3
+    kw: int = 3
+    sh: int = 1
+    sw: int = 1
+    ph: int = 1
+    pw: int = 1
+    dh: int = 1
+    dw: int = 1
+    offset_scale: float = 1.0
+    multiscale: bool = False
+    offset_dist: str = "uniform"   # "uniform": U[-a,a]; "normal": N(0, a)
+    offset_param: float = 2.0      # a (half-width, or variance)
+    seed: int = 0
+
+    @property
+    def K(self) -> int:
+        return self.kh * self.kw
+
+    @property
+    def D(self) -> int:
+        return self.C // self.G
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    def describe(self) -> str:
+        off = (f"U[-{self.offset_param:g},{self.offset_param:g}]"
+               if self.offset_dist == "uniform"
+               else f"N(0,{self.offset_param:g})")
+        mode = "multi-scale" if self.multiscale else "standard"
+        return (f"{self.name}: {self.dtype} N={self.N} {self.H}x{self.W} "
+                f"C={self.C} G={self.G} k={self.kh}x{self.kw} "
+                f"s={self.sh},{self.sw} p={self.ph},{self.pw} "
+                f"d={self.dh},{self.dw} {mode} offsets {off} seed {self.seed}")
+
+
+# The pages' workloads, at their full sizes.
+WORKLOADS = {
+    # tiny fp32 case: 1x16x16x64, 4 groups of 16 channels
+    "dcn4_small_f32": Workload("dcn4_small_f32", "f32", 1, 16, 16, 64, 4,
+                               offset_dist="uniform", offset_param=2.0),
+    # InternImage-stage-like: 64 images of 56x56x64, 4 groups
+    "internimage_stage_f32": Workload("internimage_stage_f32", "f32", 64, 56,
+                                      56, 64, 4, offset_dist="uniform",
+                                      offset_param=3.0),
+    "internimage_stage_bf16": Workload("internimage_stage_bf16", "bf16", 64,
+                                       56, 56, 64, 4, offset_dist="uniform",
+                                       offset_param=3.0),
+    # latent-diffusion U-Net block: 8 x 128x128x320, 20 groups of 16
+    "ldm_unet_block_bf16": Workload("ldm_unet_block_bf16", "bf16", 8, 128,
+                                    128, 320, 20, offset_dist="normal",
+                                    offset_param=2.0),
+    # wide low-resolution block, dilation 2: 16 x 32x32x1280, 40 groups of 32
+    "wide_lowres_dil2_f16": Workload("wide_lowres_dil2_f16", "f16", 16, 32,
+                                     32, 1280, 40, dh=2, dw=2,
+                                     offset_dist="uniform", offset_param=8.0),
+    # FlowDCN groupwise multi-scale: 32 x 32x32 tokens x 1152, 16 groups of 72
+    "flowdcn_multiscale_bf16": Workload("flowdcn_multiscale_bf16", "bf16", 32,
+                                        32, 32, 1152, 16, multiscale=True,
+                                        offset_dist="uniform",
+                                        offset_param=1.0),
+}
+
+# The workload the headline throughput is quoted on.
+HEADLINE = "ldm_unet_block_bf16"
+
+
+def to_raw(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> raw storage of the I/O dtype (round to nearest even).
+    f32 stays float32; bf16 and f16 become uint16 bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return a
+    if dtype == "f16":
+        return a.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        import torch
+        t = torch.from_numpy(a).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(dtype)
+
+
+def from_raw(a: np.ndarray, dtype: str) -> np.ndarray:
+    """raw storage -> float32 values (exact)."""
+    if dtype == "f32":
+        return np.asarray(a, np.float32)
+    if dtype == "f16":
+        return np.asarray(a, np.uint16).view(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    raise ValueError(dtype)
+
+
+def group_scales(G: int) -> np.ndarray:
+    """FlowDCN per-group scale priors, log-spaced from 1 to 4:
+    s_g = 4**(g/(G-1)) evaluated in float64, stored as float32."""
+    if G == 1:
+        return np.ones(1, np.float32)
+    g = np.arange(G, dtype=np.float64)
+    return (4.0 ** (g / (G - 1))).astype(np.float32)
+
+
+@dataclass
+class Inputs:
+    x: np.ndarray                 # raw [N,H,W,C]
+    om: np.ndarray                # raw [N,Ho,Wo,G,3K]
+    scales: Optional[np.ndarray]  # float32 [G] or None
+
+
+def make_inputs(w: Workload, Ho: int, Wo: int, seed: Optional[int] = None,
+                n_images: Optional[int] = None) -> Inputs:
+    """Draw one batch of the workload.  ``seed`` overrides the workload seed
+    and ``n_images`` the batch size (a smaller batch drawn with the same
+    recipe, not a slice of the full batch)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    N = w.N if n_images is None else n_images
+    K, G = w.K, w.G
+    x = rng.standard_normal((N, w.H, w.W, w.C), dtype=np.float32)
+    if w.offset_dist == "uniform":
+        a = np.float32(w.offset_param)
+        off = rng.random((N, Ho, Wo, G, 2 * K), dtype=np.float32) * (2 * a) - a
+    elif w.offset_dist == "normal":
+        sd = np.float32(np.sqrt(w.offset_param))
+        off = rng.standard_normal((N, Ho, Wo, G, 2 * K), dtype=np.float32) * sd
+    else:
+        raise ValueError(w.offset_dist)
+    m = rng.standard_normal((N, Ho, Wo, G, K), dtype=np.float32) * np.float32(1.0 / 3.0)
+    om = np.concatenate([off, m], axis=-1)
+    scales = group_scales(G) if w.multiscale else None
+    return Inputs(to_raw(x, w.dtype), to_raw(om, w.dtype), scales)
