@@ -28,14 +28,19 @@
  *  R6 multi-scale centre: centre = yo*sh - ph + (kh-1)/2, grid_k = i - (kh-1)/2
  *     (odd kernels, dilation 1, offset_scale 1);
  *  R7 the offset/weight tensor has the I/O dtype, scales are fp32;
- *  R8 fp32 evaluation order (dcn4o_forward_f32): position = one fp32 add of
- *     the exact integer base and fl(offset_scale*delta) (multi-scale: centre +
- *     fl(s_g * fl(grid + dir))); sample skipped unless -1<py<H and -1<px<W;
- *     y0=floor(py), lh=py-y0, hh=1-lh (same for x); corner weights hh*hw,
- *     hh*lw, lh*hw, lh*lw for (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1);
- *     coefficient fl(m*w); acc = fma(coefficient, value, acc) with k outer,
- *     corner inner, acc starting at +0; output rounded to the I/O dtype by
- *     round-to-nearest-even.
+ *  R8 fp32 evaluation order (dcn4o_forward_f32): the location is kept as an
+ *     exact integer part and a fraction.  The displacement from the integer
+ *     base is t = fl(offset_scale*delta) (multi-scale: t = fl(s_g * fl(grid +
+ *     dir)), base = centre); f = floor(t); the fraction lh = fl(t - f); the
+ *     integer part yf = base + f (exact); the sample is skipped unless
+ *     -1 <= yf <= H-1 and -1 <= xf <= W-1 (NaN displacements fail the test);
+ *     y0 = yf, hh = fl(1 - lh) (same for x); corner weights fl(hh*hw),
+ *     fl(hh*lw), fl(lh*hw), fl(lh*lw) for (y0,x0), (y0,x0+1), (y0+1,x0),
+ *     (y0+1,x0+1); coefficient fl(m*w); acc = fma(coefficient, value, acc)
+ *     with k outer, corner inner, acc starting at +0; output rounded to the
+ *     I/O dtype to nearest even.  (Splitting the location keeps the fraction
+ *     accurate to ~1e-7 px whatever the image size; adding the offset to the
+ *     absolute coordinate first would round it to the coordinate's ulp.)
  */
 #include "dcn4_oracle.h"
 
@@ -303,34 +308,33 @@ typedef struct {
 
 static geom_t sample_geometry_f32(const dcn4o_shape* s, int yo, int xo, int i,
                                   int j, float dx, float dy, float sg) {
-  float py, px;
+  float by, bx; /* exact integer base of the point */
+  float ty, tx; /* displacement from the base     */
   if (s->multiscale) {
     int hy = (s->kh - 1) / 2, hx = (s->kw - 1) / 2;
-    float cy = (float)(yo * s->sh - s->ph + hy);
-    float cx = (float)(xo * s->sw - s->pw + hx);
+    by = (float)(yo * s->sh - s->ph + hy);
+    bx = (float)(xo * s->sw - s->pw + hx);
     float uy = (float)(i - hy) + dy; /* grid + direction */
     float ux = (float)(j - hx) + dx;
-    float vy = sg * uy; /* times the group's scale */
-    float vx = sg * ux;
-    py = cy + vy;
-    px = cx + vx;
+    ty = sg * uy; /* times the group's scale */
+    tx = sg * ux;
   } else {
-    float by = (float)(yo * s->sh - s->ph + i * s->dh); /* exact integer */
-    float bx = (float)(xo * s->sw - s->pw + j * s->dw);
-    float oy = s->offset_scale * dy;
-    float ox = s->offset_scale * dx;
-    py = by + oy;
-    px = bx + ox;
+    by = (float)(yo * s->sh - s->ph + i * s->dh);
+    bx = (float)(xo * s->sw - s->pw + j * s->dw);
+    ty = s->offset_scale * dy;
+    tx = s->offset_scale * dx;
   }
+  float fy = floorf(ty), fx = floorf(tx);
+  float yf = by + fy, xf = bx + fx; /* integers; exact while inside */
   geom_t r = {0, 0, 0, 0.0f, 0.0f};
-  if (!(py > -1.0f && py < (float)s->H && px > -1.0f && px < (float)s->W))
-    return r; /* all four corners are padding (and NaN locations land here) */
-  float fy = floorf(py), fx = floorf(px);
+  if (!(yf >= -1.0f && yf <= (float)(s->H - 1) && xf >= -1.0f &&
+        xf <= (float)(s->W - 1)))
+    return r; /* all four corners are padding (NaN displacements land here) */
   r.inside = 1;
-  r.y0 = (int)fy;
-  r.x0 = (int)fx;
-  r.lh = py - fy;
-  r.lw = px - fx;
+  r.y0 = (int)yf;
+  r.x0 = (int)xf;
+  r.lh = ty - fy;
+  r.lw = tx - fx;
   return r;
 }
 

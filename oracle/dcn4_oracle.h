@@ -80,8 +80,8 @@ int dcn4o_forward_f32(const dcn4o_shape* s, int dtype, const void* x,
                       const int64_t* pix, int64_t npix, int nthreads);
 
 /* Sampling geometry of the fp32 evaluation, one entry per (pixel, g, k):
- * inside = the sample passed the (-1,H)x(-1,W) test; for inside samples
- * y0=floor(py), x0=floor(px), lh=py-y0, lw=px-x0 (else all zero). */
+ * inside = the integer part of the location is in [-1,H-1]x[-1,W-1]; for
+ * inside samples y0, x0 = integer parts, lh, lw = fractions (else all zero). */
 int dcn4o_geometry(const dcn4o_shape* s, int dtype, const void* om,
                    const float* scales, int32_t* y0, int32_t* x0, float* lh,
                    float* lw, uint8_t* inside, const int64_t* pix,

@@ -524,17 +524,20 @@ def pin_exact_rational(o):
 
 
 def pin_geometry(o):
-    """Sample locations next to integers and at the image border, where the
-    fp32 sums are exact: floor, fraction and the inside test are fixed."""
+    """Sample locations next to integers and at the image border: integer
+    part, fraction and the inside test (integer part in [-1,H-1]) are fixed.
+    The fraction comes from the offset alone, so it stays exact even for a
+    subnormal offset."""
     s = Shape(1, 16, 16, 4, 1, kh=1, kw=1, ph=0, pw=0)
     ho, wo = o.out_size(s)
     e = 2.0 ** -20
     # (output row, dy, expected inside, y0, lh); case number q sits at output
     # column q with dx = 0.25
     cases = [(5, -e, 1, 4, 1 - e), (5, e, 1, 5, e), (5, -0.0, 1, 5, 0.0),
-             (0, -1.0, 0, 0, 0.0), (0, -1 + e, 1, -1, e), (0, -0.5, 1, -1, 0.5),
+             (0, -1.0, 1, -1, 0.0), (0, -1 + e, 1, -1, e), (0, -0.5, 1, -1, 0.5),
              (15, 1 - 2 * e, 1, 15, 1 - 2 * e), (15, 1.0, 0, 0, 0.0),
-             (2, 2.0 ** -149, 1, 2, 0.0), (0, 2.0 ** -149, 1, 0, 2.0 ** -149)]
+             (2, 2.0 ** -149, 1, 2, 2.0 ** -149), (0, 2.0 ** -149, 1, 0, 2.0 ** -149),
+             (0, -1.0 - e, 0, 0, 0.0), (15, 0.5, 1, 15, 0.5)]
     om = np.zeros((1, ho, wo, 1, 3), np.float32)
     om[..., 2] = 1
     om[..., 0] = 0.25
@@ -561,7 +564,7 @@ def pin_geometry(o):
                 t = (yo * wo + xo) * 9 + k
                 py = yo * 2 - 1 + 2 * i - 0.25
                 px = xo * 3 - 2 + j + 0.5
-                inside = -1 < py < 20 and -1 < px < 20
+                inside = -1 <= math.floor(py) <= 19 and -1 <= math.floor(px) <= 19
                 assert g["inside"][t] == inside
                 if inside:
                     assert g["y0"][t] == math.floor(py) and g["lh"][t] == py - math.floor(py)

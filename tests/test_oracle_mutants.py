@@ -49,7 +49,7 @@ MUTANTS = {
     "corner_dropped_f64": sub("if (yy >= 0.0 && yy < s->H && xx >= 0.0 && xx < s->W) {\n        int64_t idx",
                               "if (!(a && b) && yy >= 0.0 && yy < s->H && xx >= 0.0 && xx < s->W) {\n        int64_t idx"),
     # fraction measured from the wrong side
-    "row_fraction_flipped_f32": sub("r.lh = py - fy;", "r.lh = 1.0f - (py - fy);"),
+    "row_fraction_flipped_f32": sub("r.lh = ty - fy;", "r.lh = 1.0f - (ty - fy);"),
     "col_fraction_flipped_f64": sub("double lh = py - y0, lw = px - x0;",
                                     "double lh = py - y0, lw = 1.0 - (px - x0);"),
     # corner weights transposed
@@ -58,18 +58,18 @@ MUTANTS = {
     "weights_transposed_f64": sub("double w = (a ? lh : 1.0 - lh) * (b ? lw : 1.0 - lw);",
                                   "double w = (a ? lw : 1.0 - lw) * (b ? lh : 1.0 - lh);"),
     # convolution parameters lost or misapplied
-    "dilation_ignored_f32": sub("float by = (float)(yo * s->sh - s->ph + i * s->dh);",
-                                "float by = (float)(yo * s->sh - s->ph + i);"),
+    "dilation_ignored_f32": sub("by = (float)(yo * s->sh - s->ph + i * s->dh);",
+                                "by = (float)(yo * s->sh - s->ph + i);"),
     "dilation_ignored_f64": sub("*py = (double)(yo * s->sh - s->ph + i * s->dh)",
                                 "*py = (double)(yo * s->sh - s->ph + i)"),
-    "stride_ignored_f32": sub("float bx = (float)(xo * s->sw - s->pw + j * s->dw);",
-                              "float bx = (float)(xo - s->pw + j * s->dw);"),
+    "stride_ignored_f32": sub("bx = (float)(xo * s->sw - s->pw + j * s->dw);",
+                              "bx = (float)(xo - s->pw + j * s->dw);"),
     "pad_sign_f64": sub("*px = (double)(xo * s->sw - s->pw + j * s->dw)",
                         "*px = (double)(xo * s->sw + s->pw + j * s->dw)"),
-    "offset_scale_ignored_f32": sub("float oy = s->offset_scale * dy;", "float oy = dy;"),
+    "offset_scale_ignored_f32": sub("ty = s->offset_scale * dy;", "ty = dy;"),
     "offset_scale_ignored_f64": sub("(double)s->offset_scale * dx", "dx"),
     # multi-scale: scale on the grid only, or centre lost
-    "ms_scale_grid_only_f32": sub("float vy = sg * uy;", "float vy = sg * (float)(i - hy) + dy;"),
+    "ms_scale_grid_only_f32": sub("ty = sg * uy;", "ty = sg * (float)(i - hy) + dy;"),
     "ms_centre_lost_f64": sub("*px = (double)(xo * s->sw - s->pw + hx) + sg",
                               "*px = (double)(xo * s->sw - s->pw) + sg"),
     # group bookkeeping
@@ -81,9 +81,12 @@ MUTANTS = {
     "weight_dropped_f32": sub("float coef = m * w[r];", "float coef = w[r];"),
     "weight_dropped_f64": sub("acc += m * bilinear_zero_pad(", "acc += bilinear_zero_pad("),
     # borders
-    "inside_test_low_f32": sub("if (!(py > -1.0f && py < (float)s->H",
-                               "if (!(py >= 0.0f && py < (float)s->H"),
-    "inside_test_high_f32": sub("px < (float)s->W))", "px < (float)(s->W - 1)))"),
+    "inside_test_low_f32": sub("if (!(yf >= -1.0f && yf <= (float)(s->H - 1)",
+                               "if (!(yf >= 0.0f && yf <= (float)(s->H - 1)"),
+    "inside_test_high_f32": sub("xf <= (float)(s->W - 1)))", "xf <= (float)(s->W - 2)))"),
+    # the integer part taken from the offset alone, or the fraction's sign lost
+    "base_dropped_f32": sub("float yf = by + fy, xf = bx + fx;", "float yf = fy, xf = bx + fx;"),
+    "fraction_abs_f32": sub("r.lw = tx - fx;", "r.lw = fabsf(tx) - floorf(fabsf(tx));"),
     "corner_bound_off_by_one_f64": sub("xx < s->W) {", "xx <= s->W) {"),
     # codecs
     "bf16_round_half_up": sub("u += 0x7fffu + lsb;", "u += 0x8000u;"),
