@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the DCNv4 forward operator on one MI355X.
+
+One step = one forward pass of the operator (the whole hot path: offset and
+weight staging, sampling geometry, bilinear gathers, fp32 accumulation,
+rounding and store) over one batch of synthetic inputs that are resident in
+HBM when the timed region starts.  Several input sets are rotated so that no
+step finds its inputs in the 256 MB Infinity Cache or the L2 from the step
+before.
+
+The metric is GB/s of ideal traffic (input and output feature maps once,
+the offset/weight tensor once, plus group scales: the 2HWC + 27HWG element
+model of the DCNv4 digest page, section "GPU效率的理论分析") and its fraction
+of the MI355X HBM peak (8 TB/s); output pixels/s and outputs/s are reported
+beside it.
+
+Prints ONE JSON line.  --gpus N with N > 1 is refused: this build runs on one
+GPU (images are independent; see the design doc for how the batch would shard).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("dcn4_kernels.hip", "dcn4_internal.h", "dcn4_api.cpp"):
+        with open(os.path.join(ROOT, "dynamic_sparse_vision_dcn4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, launches_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the latent-diffusion U-Net block)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated across steps (default: enough for 1 GiB)")
+    ap.add_argument("--channels-per-lane", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} refused: this operator build measures "
+              "one GPU only (batch sharding over GPUs is a design note, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads
+    import dynamic_sparse_vision_dcn4_amd as d4
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+                   w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype)
+    plan = d4.Plan(desc, channels_per_lane=args.channels_per_lane)
+    Ho, Wo = plan.Ho, plan.Wo
+    ideal = plan.ideal_bytes
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_tensor(raw):
+        if w.dtype == "f32":
+            t = torch.from_numpy(raw)
+        else:
+            t = torch.from_numpy(raw.view(np.int16)).view(tdt)
+        return t.to(dev)
+
+    nsets = args.sets or max(2, math.ceil((1 << 30) / max(ideal, 1)))
+    sets = []
+    host0 = None
+    for r in range(nsets):
+        inp = workloads.make_inputs(w, Ho, Wo, seed=w.seed + r)
+        if r == 0:
+            host0 = inp
+        sc = None if inp.scales is None else torch.from_numpy(inp.scales).to(dev)
+        y = torch.empty(plan.out_shape(), dtype=tdt, device=dev)
+        sets.append((dev_tensor(inp.x), dev_tensor(inp.om), sc, y))
+    torch.cuda.synchronize()
+
+    def step(i):
+        x, om, sc, y = sets[i % nsets]
+        plan.forward(x, om, sc, out=y, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # the timed region: exactly `steps` steps between two synchronisations
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # kernel duration: a second pass with events around every launch, on the
+    # stream the kernel is launched on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = statistics.mean(per_launch_ms)
+
+    value = ideal / (ms_per_step * 1e-3) / 1e9
+    achieved = ideal / (kern_ms * 1e-3) / 1e9
+    out_pix = w.N * Ho * Wo
+    traffic = load_traffic(name, ideal)
+
+    line = {
+        "metric": "DCNv4 fwd GB/s (ideal bytes) and % of HBM peak; output pixels/sec",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, the workload's shapes and distributions)",
+        "config": {"workload": name, "N": w.N, "H": w.H, "W": w.W, "C": w.C,
+                   "group": w.G, "kernel": [w.kh, w.kw], "stride": [w.sh, w.sw],
+                   "pad": [w.ph, w.pw], "dilation": [w.dh, w.dw],
+                   "group_scales": w.multiscale, "Ho": Ho, "Wo": Wo,
+                   "ideal_bytes": ideal, "input_sets": nsets,
+                   "channels_per_lane": plan.info()["channels_per_lane"]},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "output_pixels_per_s": round(out_pix / (ms_per_step * 1e-3), 1),
+        "outputs_per_s": round(out_pix * w.C / (ms_per_step * 1e-3), 1),
+        "kernel_us": {"mean": round(kern_ms * 1e3, 3),
+                      "median": round(statistics.median(per_launch_ms) * 1e3, 3),
+                      "min": round(min(per_launch_ms) * 1e3, 3),
+                      "max": round(max(per_launch_ms) * 1e3, 3)},
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "kernel_source": kernel_source_digest(),
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, Ho, Wo, host0, args.cpu_reps)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, Ho, Wo, inp, reps):
+    """The CPU oracle as it stands (fp32 evaluation, OpenMP over output
+    pixels) on the host cores, on the same batch the first input set holds."""
+    import oracle
+    from oracle import Shape
+    o = oracle.get()
+    s = Shape(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+              w.dh, w.dw, w.offset_scale, w.multiscale)
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    env_t = os.environ.get("OMP_NUM_THREADS")
+    if env_t and env_t.isdigit():
+        threads = min(threads, int(env_t))
+    times = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        o.forward_f32(s, w.dtype, inp.x, inp.om, inp.scales, nthreads=threads)
+        times.append(time.perf_counter() - t)
+    med = statistics.median(times)
+    ideal = o.ideal_bytes(s, w.dtype)
+    return {"value": round(ideal / med / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full batch ({w.N} images), median of {reps} runs, "
+                      f"{med:.2f} s each, fp32 evaluation",
+            "output_pixels_per_s": round(w.N * Ho * Wo / med, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,287 @@
+"""Python binding of libdcn4.so, the MI355X (gfx950) DCNv4 forward library.
+
+The functions below carry the C ABI's names (include/dcn4.h) and only
+marshal arguments; every step of the operator runs in the HIP kernels of the
+library.  PyTorch is used by ``Plan`` for device memory and the current
+stream only.  There is no fallback: importing this package raises if the
+built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdcn4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built: run `python -m dynamic_sparse_vision_dcn4_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+# PyTorch ships its own HIP runtime under the same soname (libamdhip64.so.7)
+# and loads it by absolute path.  Importing torch first makes libdcn4.so bind
+# to that already-loaded runtime, so a process holds one HIP runtime; loading
+# the library first would leave two runtimes side by side, and the second
+# finds no device.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# dcn4_dtype
+DCN4_F32, DCN4_BF16, DCN4_F16 = 0, 1, 2
+DTYPE_CODES = {"f32": DCN4_F32, "bf16": DCN4_BF16, "f16": DCN4_F16}
+# dcn4_status
+DCN4_OK = 0
+DCN4_ERR_INVALID_ARG = -1
+DCN4_ERR_UNSUPPORTED = -2
+DCN4_ERR_MISALIGNED = -3
+DCN4_ERR_NULL = -4
+DCN4_ERR_HIP = -5
+DCN4_ERR_NOMEM = -6
+
+
+class dcn4_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("N", "H", "W", "C", "group", "kernel_h", "kernel_w",
+                 "stride_h", "stride_w", "pad_h", "pad_w", "dilation_h",
+                 "dilation_w")] + [("offset_scale", ctypes.c_float),
+                                   ("use_group_scales", ctypes.c_int32),
+                                   ("dtype", ctypes.c_int32)]
+
+
+class dcn4_launch_info(ctypes.Structure):
+    _fields_ = [("channels_per_lane", ctypes.c_int32),
+                ("vector_bytes", ctypes.c_int32),
+                ("lanes_per_group", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32),
+                ("blocks", ctypes.c_int64),
+                ("launches", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_lib.dcn4_create.argtypes = [ctypes.POINTER(dcn4_desc), ctypes.POINTER(_P)]
+_lib.dcn4_query.argtypes = [_P, ctypes.POINTER(ctypes.c_int32),
+                            ctypes.POINTER(ctypes.c_int32),
+                            ctypes.POINTER(ctypes.c_uint64)]
+_lib.dcn4_plan_info.argtypes = [_P, ctypes.POINTER(dcn4_launch_info)]
+_lib.dcn4_plan_set_channels_per_lane.argtypes = [_P, ctypes.c_int32]
+_lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
+_lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_destroy.argtypes = [_P]
+_lib.dcn4_destroy.restype = None
+_lib.dcn4_status_string.argtypes = [ctypes.c_int]
+_lib.dcn4_status_string.restype = ctypes.c_char_p
+_lib.dcn4_last_error.argtypes = []
+_lib.dcn4_last_error.restype = ctypes.c_char_p
+for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
+           "dcn4_plan_set_channels_per_lane", "dcn4_forward",
+           "dcn4_probe_geometry"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+# ---------------------------------------------------------------- C ABI
+def dcn4_create(desc: dcn4_desc) -> Tuple[int, Optional[int]]:
+    """-> (status, plan handle or None)"""
+    h = _P()
+    st = _lib.dcn4_create(ctypes.byref(desc) if desc is not None else None,
+                          ctypes.byref(h))
+    return st, h.value
+
+
+def dcn4_query(plan) -> Tuple[int, int, int, int]:
+    """-> (status, Ho, Wo, ideal_bytes)"""
+    ho, wo, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_uint64()
+    st = _lib.dcn4_query(plan, ctypes.byref(ho), ctypes.byref(wo), ctypes.byref(b))
+    return st, ho.value, wo.value, b.value
+
+
+def dcn4_plan_info(plan) -> Tuple[int, dict]:
+    info = dcn4_launch_info()
+    st = _lib.dcn4_plan_info(plan, ctypes.byref(info))
+    return st, {f: getattr(info, f) for f, _ in dcn4_launch_info._fields_}
+
+
+def dcn4_plan_set_channels_per_lane(plan, channels_per_lane: int) -> int:
+    return _lib.dcn4_plan_set_channels_per_lane(plan, channels_per_lane)
+
+
+def dcn4_forward(plan, x: int, offset_mask: int, group_scales: Optional[int],
+                 y: int, stream: Optional[int]) -> int:
+    """Raw device pointers (ints) and a hipStream_t handle (int or None)."""
+    return _lib.dcn4_forward(plan, x, offset_mask, group_scales, y, stream)
+
+
+def dcn4_probe_geometry(plan, offset_mask: int, group_scales: Optional[int],
+                        y0: int, x0: int, lh: int, lw: int, inside: int,
+                        stream: Optional[int]) -> int:
+    return _lib.dcn4_probe_geometry(plan, offset_mask, group_scales, y0, x0,
+                                    lh, lw, inside, stream)
+
+
+def dcn4_destroy(plan) -> None:
+    _lib.dcn4_destroy(plan)
+
+
+def dcn4_status_string(status: int) -> str:
+    return _lib.dcn4_status_string(status).decode()
+
+
+def dcn4_last_error() -> str:
+    return _lib.dcn4_last_error().decode()
+
+
+class DCN4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dcn4_status_string(status)} -- {dcn4_last_error()}")
+
+
+# ---------------------------------------------------------------- torch glue
+@dataclass(frozen=True)
+class Desc:
+    """Operator descriptor (see dcn4_desc in include/dcn4.h)."""
+    N: int
+    H: int
+    W: int
+    C: int
+    group: int
+    kernel_h: int = 3
+    kernel_w: int = 3
+    stride_h: int = 1
+    stride_w: int = 1
+    pad_h: int = 1
+    pad_w: int = 1
+    dilation_h: int = 1
+    dilation_w: int = 1
+    offset_scale: float = 1.0
+    use_group_scales: bool = False
+    dtype: str = "bf16"
+
+    def c_struct(self) -> dcn4_desc:
+        return dcn4_desc(self.N, self.H, self.W, self.C, self.group,
+                         self.kernel_h, self.kernel_w, self.stride_h,
+                         self.stride_w, self.pad_h, self.pad_w,
+                         self.dilation_h, self.dilation_w,
+                         float(self.offset_scale), int(bool(self.use_group_scales)),
+                         DTYPE_CODES[self.dtype])
+
+
+def _torch_dtype(name):
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[name]
+
+
+class Plan:
+    """Owns a dcn4_plan; forward() takes torch CUDA tensors."""
+
+    def __init__(self, desc: Desc, channels_per_lane: int = 0):
+        self.desc = desc
+        st, h = dcn4_create(desc.c_struct())
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_create")
+        self._h = h
+        if channels_per_lane:
+            st = dcn4_plan_set_channels_per_lane(h, channels_per_lane)
+            if st != DCN4_OK:
+                raise DCN4Error(st, "dcn4_plan_set_channels_per_lane")
+        st, self.Ho, self.Wo, self.ideal_bytes = dcn4_query(h)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_query")
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> dict:
+        st, info = dcn4_plan_info(self._h)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_plan_info")
+        return info
+
+    def set_channels_per_lane(self, dp: int) -> None:
+        st = dcn4_plan_set_channels_per_lane(self._h, dp)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_plan_set_channels_per_lane")
+
+    def out_shape(self):
+        d = self.desc
+        return (d.N, self.Ho, self.Wo, d.C)
+
+    def om_shape(self):
+        d = self.desc
+        return (d.N, self.Ho, self.Wo, d.group, 3 * d.kernel_h * d.kernel_w)
+
+    def _check(self, t, shape, dtype, name):
+        import torch
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape) and t.numel() != int(_prod(shape)):
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def forward(self, x, om, scales=None, out=None, stream=None):
+        """y[N,Ho,Wo,C] = DCNv4(x[N,H,W,C], om[N,Ho,Wo,G,3K], scales[G])."""
+        import torch
+        d = self.desc
+        dt = _torch_dtype(d.dtype)
+        self._check(x, (d.N, d.H, d.W, d.C), dt, "x")
+        self._check(om, self.om_shape(), dt, "offset_mask")
+        if scales is not None:
+            self._check(scales, (d.group,), torch.float32, "group_scales")
+        if out is None:
+            out = torch.empty(self.out_shape(), dtype=dt, device=x.device)
+        else:
+            self._check(out, self.out_shape(), dt, "out")
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = dcn4_forward(self._h, x.data_ptr(), om.data_ptr(),
+                          None if scales is None else scales.data_ptr(),
+                          out.data_ptr(), stream)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_forward")
+        return out
+
+    def probe_geometry(self, om, scales=None, stream=None):
+        """Device geometry of every (n, yo, xo, g, k): dict of tensors."""
+        import torch
+        d = self.desc
+        self._check(om, self.om_shape(), _torch_dtype(d.dtype), "offset_mask")
+        n = d.N * self.Ho * self.Wo * d.group * d.kernel_h * d.kernel_w
+        dev = om.device
+        out = dict(y0=torch.empty(n, dtype=torch.int32, device=dev),
+                   x0=torch.empty(n, dtype=torch.int32, device=dev),
+                   lh=torch.empty(n, dtype=torch.float32, device=dev),
+                   lw=torch.empty(n, dtype=torch.float32, device=dev),
+                   inside=torch.empty(n, dtype=torch.uint8, device=dev))
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = dcn4_probe_geometry(self._h, om.data_ptr(),
+                                 None if scales is None else scales.data_ptr(),
+                                 *(out[k].data_ptr() for k in ("y0", "x0", "lh", "lw", "inside")),
+                                 stream)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_probe_geometry")
+        return out
+
+    def __del__(self, _destroy=_lib.dcn4_destroy):
+        h = getattr(self, "_h", None)
+        if h:
+            _destroy(h)
+            self._h = None
+
+
+def _prod(s):
+    r = 1
+    for v in s:
+        r *= int(v)
+    return r
+
+
+def loaded_library_path() -> str:
+    return LIB_PATH

@@ -1,0 +1,258 @@
+// dcn4_api.cpp -- the C ABI of libdcn4.so: argument validation, planning and
+// error reporting.  No HIP call is made before the arguments have passed
+// validation, so every error path runs without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <new>
+
+#include "dcn4.h"
+#include "dcn4_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+dcn4_status fail(dcn4_status s, const char* msg) {
+  snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+  return s;
+}
+
+bool aligned_to(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+constexpr int64_t kCoordLimit = int64_t(1) << 20;
+
+// Output size of the convolution index arithmetic with padding and dilation.
+int64_t out_size(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
+  const int64_t span = in + 2 * p - d * (k - 1) - 1;
+  return span < 0 ? 0 : span / s + 1;
+}
+
+dcn4_status validate_desc(const dcn4_desc& d, int64_t* Ho, int64_t* Wo) {
+  if (d.dtype != DCN4_F32 && d.dtype != DCN4_BF16 && d.dtype != DCN4_F16)
+    return fail(DCN4_ERR_INVALID_ARG, "dtype must be DCN4_F32, DCN4_BF16 or DCN4_F16");
+  if (d.N < 0 || d.H < 1 || d.W < 1 || d.C < 1 || d.group < 1)
+    return fail(DCN4_ERR_INVALID_ARG, "N must be >= 0 and H, W, C, group >= 1");
+  if (d.C % d.group)
+    return fail(DCN4_ERR_INVALID_ARG, "C must be a multiple of group");
+  if (d.kernel_h < 1 || d.kernel_w < 1 || d.stride_h < 1 || d.stride_w < 1 ||
+      d.dilation_h < 1 || d.dilation_w < 1 || d.pad_h < 0 || d.pad_w < 0)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "kernel, stride and dilation must be >= 1 and pad >= 0");
+  if (d.H > kCoordLimit || d.W > kCoordLimit || d.pad_h > kCoordLimit ||
+      d.pad_w > kCoordLimit || d.stride_h > kCoordLimit || d.stride_w > kCoordLimit ||
+      int64_t(d.dilation_h) * d.kernel_h > kCoordLimit ||
+      int64_t(d.dilation_w) * d.kernel_w > kCoordLimit)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "H, W, pads, strides and dilation*kernel must be <= 2^20");
+  if (!isfinite(d.offset_scale))
+    return fail(DCN4_ERR_INVALID_ARG, "offset_scale must be finite");
+  if (d.use_group_scales) {
+    if (!(d.kernel_h & 1) || !(d.kernel_w & 1))
+      return fail(DCN4_ERR_INVALID_ARG, "group-scale mode needs odd kernel sizes");
+    if (d.dilation_h != 1 || d.dilation_w != 1 || d.offset_scale != 1.0f)
+      return fail(DCN4_ERR_INVALID_ARG,
+                  "group-scale mode needs dilation 1 and offset_scale 1");
+  }
+  *Ho = out_size(d.H, d.kernel_h, d.stride_h, d.pad_h, d.dilation_h);
+  *Wo = out_size(d.W, d.kernel_w, d.stride_w, d.pad_w, d.dilation_w);
+  if (*Ho < 1 || *Wo < 1)
+    return fail(DCN4_ERR_INVALID_ARG, "the output would be empty");
+  return DCN4_OK;
+}
+
+// Channels per lane on the vector path: prefer 16 channels (fewer geometry
+// instructions per channel) when the group allows it.
+int32_t default_dp(int32_t D, int32_t es) {
+  const int32_t vec = 16 / es;
+  if ((D * es) % 16) return 0;
+  const int32_t order_half[] = {2, 3, 1, 4};
+  const int32_t order_f32[] = {4, 2, 3, 1};
+  const int32_t* order = es == 4 ? order_f32 : order_half;
+  for (int t = 0; t < 4; ++t)
+    if (D % (order[t] * vec) == 0) return order[t] * vec;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan output pointer is NULL");
+  *plan = nullptr;
+  if (!desc) return fail(DCN4_ERR_NULL, "descriptor is NULL");
+  int64_t Ho = 0, Wo = 0;
+  dcn4_status s = validate_desc(*desc, &Ho, &Wo);
+  if (s != DCN4_OK) return s;
+
+  dcn4::Plan p{};
+  p.desc = *desc;
+  p.Ho = (int32_t)Ho;
+  p.Wo = (int32_t)Wo;
+  p.D = desc->C / desc->group;
+  p.K = desc->kernel_h * desc->kernel_w;
+  p.es = desc->dtype == DCN4_F32 ? 4 : 2;
+  p.mode = desc->use_group_scales ? dcn4::kGroupScale
+           : desc->offset_scale == 1.0f ? dcn4::kStdUnitScale
+                                        : dcn4::kStdScaled;
+  p.dp_default = default_dp(p.D, p.es);
+  p.dp = p.dp_default;
+
+  // size limits of the 32-bit device arithmetic
+  const int64_t pix = Ho * Wo;
+  const int64_t x_img = int64_t(desc->H) * desc->W * desc->C * p.es;
+  const int64_t lanes_img = pix * desc->C;  // worst case: one channel per lane
+  const int64_t lim = (int64_t(1) << 31) - (int64_t(1) << 16);
+  if (lanes_img >= lim || pix * desc->group * 3 * p.K * p.es >= lim ||
+      pix * desc->C * p.es >= lim)
+    return fail(DCN4_ERR_UNSUPPORTED, "one image's tensors exceed 2^31 bytes");
+  // corner offsets use 24-bit multiplies: pixel index and pixel bytes
+  if (int64_t(desc->H) * desc->W >= (int64_t(1) << 23) ||
+      int64_t(desc->C) * p.es >= (int64_t(1) << 23))
+    return fail(DCN4_ERR_UNSUPPORTED, "H*W and C*element bytes must be below 2^23");
+  // a workgroup touches at most kBlock + 1 pixels; its gathers address the
+  // images those pixels belong to from one 32-bit offset
+  const int64_t span_images = (dcn4::kBlock + 1) / pix + 2;
+  if (span_images * x_img >= lim)
+    return fail(DCN4_ERR_UNSUPPORTED, "input images too large for 32-bit offsets");
+  p.images_per_launch = (int32_t)(lim / (lanes_img > 0 ? lanes_img : 1));
+  if (p.images_per_launch < 1) p.images_per_launch = 1;
+  if (dcn4::forward_block(p, p.dp ? p.D / p.dp : p.D) == 0 ||
+      dcn4::forward_block(p, p.D) == 0)
+    return fail(DCN4_ERR_UNSUPPORTED,
+                "offset/weight rows of one pixel are too large for LDS");
+
+  const int64_t in_el = int64_t(desc->N) * desc->H * desc->W * desc->C;
+  const int64_t out_el = int64_t(desc->N) * pix * desc->C;
+  const int64_t om_el = int64_t(desc->N) * pix * desc->group * 3 * p.K;
+  p.ideal_bytes = uint64_t(in_el + out_el + om_el) * p.es +
+                  (desc->use_group_scales ? 4ull * desc->group : 0ull);
+
+  dcn4_plan* out = new (std::nothrow) dcn4_plan;
+  if (!out) return fail(DCN4_ERR_NOMEM, "plan allocation failed");
+  out->p = p;
+  *plan = out;
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_query(const dcn4_plan* plan, int32_t* Ho, int32_t* Wo,
+                       uint64_t* ideal_bytes) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  if (Ho) *Ho = plan->p.Ho;
+  if (Wo) *Wo = plan->p.Wo;
+  if (ideal_bytes) *ideal_bytes = plan->p.ideal_bytes;
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
+  if (!plan || !info) return fail(DCN4_ERR_NULL, "plan or info is NULL");
+  const dcn4::Plan& p = plan->p;
+  const bool vec = p.dp > 0;
+  const int32_t dp = vec ? p.dp : 1;
+  info->channels_per_lane = dp;
+  info->vector_bytes = vec ? 16 : p.es;
+  info->lanes_per_group = p.D / dp;
+  info->block_threads = dcn4::forward_block(p, p.D / dp);
+  int64_t blocks = 0;
+  int32_t launches = 0;
+  for (int32_t n0 = 0; n0 < p.desc.N; n0 += p.images_per_launch) {
+    const int32_t nb = p.desc.N - n0 < p.images_per_launch ? p.desc.N - n0
+                                                           : p.images_per_launch;
+    blocks += (int64_t(nb) * p.Ho * p.Wo * p.desc.group * (p.D / dp) +
+               info->block_threads - 1) / info->block_threads;
+    ++launches;
+  }
+  info->blocks = blocks;
+  info->launches = launches;
+  info->lds_bytes = dcn4::forward_lds_bytes(p, p.D / dp, info->block_threads);
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_plan_set_channels_per_lane(dcn4_plan* plan, int32_t dp) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  dcn4::Plan& p = plan->p;
+  if (dp == 0) {
+    p.dp = p.dp_default;
+    return DCN4_OK;
+  }
+  const int32_t vec = 16 / p.es;
+  if (dp < vec || dp % vec || dp / vec > 4 || p.D % dp || (p.D * p.es) % 16)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "channels_per_lane must be 1-4 vectors of 16 bytes and divide D");
+  if (dcn4::forward_block(p, p.D / dp) == 0)
+    return fail(DCN4_ERR_UNSUPPORTED, "offset/weight rows are too large for LDS");
+  p.dp = dp;
+  return DCN4_OK;
+}
+
+static dcn4_status check_io(const dcn4::Plan& p, const void* x, const void* om,
+                            const float* scales, const void* y, bool need_x) {
+  if (p.desc.N == 0) return DCN4_OK;
+  if ((need_x && (!x || !y)) || !om)
+    return fail(DCN4_ERR_NULL, "x, offset_mask and y must not be NULL");
+  if (p.desc.use_group_scales && !scales)
+    return fail(DCN4_ERR_NULL, "group_scales is required in group-scale mode");
+  if (!p.desc.use_group_scales && scales)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "group_scales given but the plan is not in group-scale mode");
+  const uintptr_t es = (uintptr_t)p.es;
+  if ((need_x && (!aligned_to(x, es) || !aligned_to(y, es))) || !aligned_to(om, es))
+    return fail(DCN4_ERR_MISALIGNED, "tensor pointer not aligned to its element size");
+  if (scales && !aligned_to(scales, 4))
+    return fail(DCN4_ERR_MISALIGNED, "group_scales not 4-byte aligned");
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
+                         const void* offset_mask, const float* group_scales,
+                         void* y, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  dcn4_status s = check_io(p, x, offset_mask, group_scales, y, true);
+  if (s != DCN4_OK || p.desc.N == 0) return s;
+  const bool vector_path = p.dp > 0 && aligned_to(x, 16) &&
+                           aligned_to(offset_mask, 16) && aligned_to(y, 16);
+  s = dcn4::launch_forward(p, x, offset_mask, group_scales, y, stream, vector_path);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
+                                const float* group_scales, int32_t* y0,
+                                int32_t* x0, float* lh, float* lw,
+                                uint8_t* inside, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  dcn4_status s = check_io(p, nullptr, offset_mask, group_scales, nullptr, false);
+  if (s != DCN4_OK || p.desc.N == 0) return s;
+  if (!y0 || !x0 || !lh || !lw || !inside)
+    return fail(DCN4_ERR_NULL, "probe outputs must not be NULL");
+  if (!aligned_to(y0, 4) || !aligned_to(x0, 4) || !aligned_to(lh, 4) || !aligned_to(lw, 4))
+    return fail(DCN4_ERR_MISALIGNED, "probe outputs must be 4-byte aligned");
+  s = dcn4::launch_probe(p, offset_mask, group_scales, y0, x0, lh, lw, inside, stream);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
+void dcn4_destroy(dcn4_plan* plan) { delete plan; }
+
+const char* dcn4_status_string(dcn4_status s) {
+  switch (s) {
+    case DCN4_OK: return "DCN4_OK";
+    case DCN4_ERR_INVALID_ARG: return "DCN4_ERR_INVALID_ARG: invalid argument";
+    case DCN4_ERR_UNSUPPORTED: return "DCN4_ERR_UNSUPPORTED: beyond size limits";
+    case DCN4_ERR_MISALIGNED: return "DCN4_ERR_MISALIGNED: misaligned pointer";
+    case DCN4_ERR_NULL: return "DCN4_ERR_NULL: required pointer is NULL";
+    case DCN4_ERR_HIP: return "DCN4_ERR_HIP: HIP runtime error";
+    case DCN4_ERR_NOMEM: return "DCN4_ERR_NOMEM: out of host memory";
+  }
+  return "unknown dcn4_status";
+}
+
+const char* dcn4_last_error(void) { return g_last_error; }
+
+}  // extern "C"

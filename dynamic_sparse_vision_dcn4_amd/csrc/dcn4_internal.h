@@ -1,0 +1,89 @@
+// dcn4_internal.h -- plan and kernel-argument types shared by the C ABI
+// (dcn4_api.cpp) and the gfx950 kernels (dcn4_kernels.hip).
+#pragma once
+
+#include <stdint.h>
+
+#include "dcn4.h"
+
+namespace dcn4 {
+
+// Division by a run-time invariant divisor d with one multiply-high, an add
+// and a shift ("round-up" method of Granlund & Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994): with s = ceil(log2 d)
+// and m = floor(2^32 * (2^s - d) / d) + 1, n / d == (mulhi(n, m) + n) >> s
+// for every 0 <= n < 2^31.  The host fills it; the kernels apply it.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{d, uint32_t(m), s};
+}
+
+enum Mode : int32_t {
+  kStdUnitScale = 0,  // standard geometry, offset_scale == 1
+  kStdScaled = 1,     // standard geometry, offset_scale != 1
+  kGroupScale = 2     // FlowDCN groupwise multi-scale geometry
+};
+
+// Threads per workgroup of the forward kernel: 4 wave64s, fewer when the
+// offset/weight rows one workgroup stages would exceed the LDS budget.
+constexpr int kBlock = 256;
+constexpr int kLdsBudget = 48 * 1024;
+
+// Everything a forward launch needs, by value (kernel argument).
+struct FwdArgs {
+  const char* x;         // input of this launch's first image
+  const char* om;        // offset/weight tensor of this launch's first image
+  const float* scales;   // [G] fp32 (group-scale mode)
+  char* y;               // output of this launch's first image
+  int32_t H, W, C, G, D, Ho, Wo;
+  int32_t kh, kw, sh, sw, ph, pw, dh, dw;
+  float offset_scale;
+  float Hm1, Wm1;        // H - 1, W - 1
+  int32_t L;             // lanes per group (D / D')
+  int32_t ipp;           // items (lanes) per output pixel, G * L
+  int32_t total_items;   // lanes of this launch, < 2^31
+  int32_t nblocks;       // workgroups of this launch
+  int32_t block;         // threads (= lane items) per workgroup
+  int32_t rowel;         // offset/weight elements per output pixel, G * 3K
+  uint32_t img_bytes;    // bytes of one input image, H * W * C * es
+  uint64_t x_bytes;      // input bytes of this launch
+  uint64_t om_bytes;     // offset/weight bytes of this launch
+  FastDiv div_ipp, div_L, div_hw, div_wo;
+};
+
+struct Plan {
+  dcn4_desc desc;
+  int32_t Ho, Wo, D, K, es;
+  Mode mode;
+  int32_t dp;           // channels per lane on the vector path
+  int32_t dp_default;
+  uint64_t ideal_bytes;
+  int32_t images_per_launch;  // bounds the per-launch lane count below 2^31
+};
+
+// Kernel-side entry points (dcn4_kernels.hip).  Arguments are validated by
+// the caller; these only shape and enqueue the launches.
+dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
+                           const float* scales, void* y, void* stream,
+                           bool vector_path);
+dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
+                         int32_t* y0, int32_t* x0, float* lh, float* lw,
+                         uint8_t* inside, void* stream);
+// Text of the last HIP error a launch reported on this thread.
+const char* last_hip_error();
+// LDS bytes one forward workgroup of `block` lanes stages (the offset/weight
+// rows of its pixels), and the block size a plan uses (0: rows too large).
+int32_t forward_lds_bytes(const Plan& p, int32_t lanes_per_group, int32_t block);
+int32_t forward_block(const Plan& p, int32_t lanes_per_group);
+
+}  // namespace dcn4
+
+struct dcn4_plan {
+  dcn4::Plan p;
+};

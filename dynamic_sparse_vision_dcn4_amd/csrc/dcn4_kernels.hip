@@ -1,0 +1,595 @@
+// dcn4_kernels.hip -- DCNv4 forward spatial aggregation for CDNA4 (gfx950).
+//
+// Pages cited by title and section:
+//   [DCNv4 digest] CSDN "（论文速读）DCNv4：高效可变形卷积算子"
+//   [FlowDCN]      kler.cn "NeurIPS'24 | FlowDCN：基于可变形卷积的任意分辨率
+//                  图像生成模型"
+//
+// Work decomposition.  A "lane item" is (output pixel, group g, channel slice
+// l): the lane owns D' = VEC*NV contiguous channels of group g and computes
+// the sample geometry and the bilinear coefficients once for all of them
+// ([DCNv4 digest] "方法1": one thread per several channels of a group, so the
+// offsets, weights and coefficients are read and computed once per D'
+// channels).  Items are numbered pixel-major, group, slice, and a 256-thread
+// workgroup takes 256 consecutive items.
+//
+// Memory.  The input and output are channel-last, so a lane's D' channels are
+// contiguous and move with 128-bit loads and stores ([DCNv4 digest] "方法2").
+// The offset/weight rows of the pixels a workgroup touches form one contiguous
+// byte range of the merged tensor; the workgroup copies it to LDS with 128-bit
+// loads and every lane reads its 3K values from there.  Corner gathers use
+// raw buffer loads: an out-of-range offset returns zero, so a corner outside
+// the image is fetched as 0 from a sentinel offset (no branch, no fault) and
+// its coefficient is set to 0.  Accumulation is fp32 in registers.
+//
+// Placement.  MI355X dispatches consecutive workgroup ids round-robin over
+// its 8 XCDs, each with its own L2.  Workgroup ids are remapped so that XCD x
+// runs one contiguous range of items, i.e. a band of image rows, whose
+// neighbouring gathers then hit that XCD's L2.
+//
+// Arithmetic order (every operation one IEEE fp32 op; built with
+// -ffp-contract=off): location = base + fl(os*d) (group-scale mode: centre +
+// fl(s_g*fl(grid + d))); inside iff -1<row<H and -1<col<W; y0 = floor(row),
+// lh = row - y0, hh = 1 - lh; corner weights hh*hw, hh*lw, lh*hw, lh*lw;
+// coefficient fl(m*w); acc = fma(coefficient, value, acc), points outer,
+// corners (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1) inner; acc starts at +0.
+// A corner outside the image adds fma(0, 0, acc) == acc exactly (acc is never
+// -0 because it starts at +0), so the result equals skipping that corner.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "dcn4_internal.h"
+
+namespace dcn4 {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Word 3 of a gfx9 raw buffer descriptor: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+// Offset that no descriptor covers: loads from it return zero.
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ------------------------------------------------------------ element codecs
+template <int DT> struct Io;
+template <> struct Io<DCN4_F32> {
+  static constexpr int es = 4;
+  typedef float raw;
+  __device__ static float dec(raw r) { return r; }
+  __device__ static float lane(u32x4 v, int e) { return __uint_as_float(v[e]); }
+  __device__ static raw enc(float f) { return f; }
+};
+template <> struct Io<DCN4_BF16> {
+  static constexpr int es = 2;
+  typedef uint16_t raw;
+  __device__ static float dec(raw r) { return __uint_as_float((uint32_t)r << 16); }
+  __device__ static float lane(u32x4 v, int e) {
+    uint32_t w = v[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  __device__ static raw enc(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+  }
+};
+template <> struct Io<DCN4_F16> {
+  static constexpr int es = 2;
+  typedef uint16_t raw;
+  __device__ static float dec(raw r) { return (float)__builtin_bit_cast(_Float16, r); }
+  __device__ static float lane(u32x4 v, int e) {
+    uint32_t w = v[e >> 1];
+    return dec((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  __device__ static raw enc(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+};
+
+// ------------------------------------------------------------ sample geometry
+// Shared by the forward kernel and the geometry probe, so the probe reports
+// exactly the locations the forward pass samples.  A location is an exact
+// integer base plus a displacement t; the integer part is base + floor(t) and
+// the fraction t - floor(t), so the fraction's accuracy does not depend on
+// how far the pixel is from the origin.
+struct Loc {
+  float by, bx;  // exact integer base (standard) or centre (group-scale)
+  float ty, tx;  // displacement from the base
+};
+
+// gy/gx: grid offset of the point from the centre (group-scale mode).
+template <int MODE>
+__device__ __forceinline__ Loc sample_location(float by, float bx, float gy,
+                                               float gx, float dy, float dx,
+                                               float os, float sg) {
+  Loc l;
+  l.by = by;
+  l.bx = bx;
+  if (MODE == kStdUnitScale) {
+    l.ty = dy;
+    l.tx = dx;
+  } else if (MODE == kStdScaled) {
+    l.ty = os * dy;
+    l.tx = os * dx;
+  } else {
+    // [FlowDCN] 3.1: per-group scale prior times (grid point + direction)
+    l.ty = sg * (gy + dy);
+    l.tx = sg * (gx + dx);
+  }
+  return l;
+}
+
+struct Cell {
+  int y0, x0;
+  float lh, lw;
+  bool inside;
+};
+
+// inside: the integer part lies in [-1,H-1] x [-1,W-1] (NaN fails).  For an
+// outside location y0/x0 are meaningless; every use of them is selected away
+// by `inside` (selects never read the unused arm).
+__device__ __forceinline__ Cell locate(Loc l, float Hm1, float Wm1) {
+  Cell c;
+  const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
+  const float yf = l.by + fy, xf = l.bx + fx;  // exact while inside
+  c.inside = (yf >= -1.0f) && (yf <= Hm1) && (xf >= -1.0f) && (xf <= Wm1);
+  c.y0 = (int)yf;
+  c.x0 = (int)xf;
+  c.lh = l.ty - fy;
+  c.lw = l.tx - fx;
+  return c;
+}
+
+// XCD-aware workgroup order: hardware id b runs on XCD b % 8; XCD x gets the
+// contiguous logical range [start_x, start_x + count_x).
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
+// ------------------------------------------------------------ forward kernel
+// Per-lane constants of the forward pass.
+struct LaneCtx {
+  int by0, bx0;        // base row/col of point (0,0) (centre in group-scale mode)
+  int hy, hx;          // (k-1)/2 per axis, group-scale mode
+  float sg;            // group scale (group-scale mode)
+  uint32_t lane_bytes; // byte offset of the lane's channels in its image
+  uint32_t pix_bytes, row_stride;
+};
+
+// Coefficients and corner offsets of one sample point (corners 00,01,10,11).
+struct Tap {
+  float c[4];
+  uint32_t q[4];
+};
+
+template <int DT, int MODE, int KS>
+__device__ __forceinline__ Tap tap_geometry(const FwdArgs& a, const LaneCtx& t,
+                                            const typename Io<DT>::raw* om,
+                                            int k) {
+  typedef Io<DT> io;
+  const int kw = KS ? KS : a.kw;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  const int i = k / kw, j = k - (k / kw) * kw;
+  const float dx = io::dec(om[2 * k]);
+  const float dy = io::dec(om[2 * k + 1]);
+  const float m = io::dec(om[2 * K + k]);
+  float by, bx, gy = 0.0f, gx = 0.0f;
+  if (MODE == kGroupScale) {
+    by = (float)t.by0;
+    bx = (float)t.bx0;
+    gy = (float)(i - t.hy);
+    gx = (float)(j - t.hx);
+  } else {
+    by = (float)(t.by0 + i * a.dh);
+    bx = (float)(t.bx0 + j * a.dw);
+  }
+  const Cell c = locate(sample_location<MODE>(by, bx, gy, gx, dy, dx,
+                                              a.offset_scale, t.sg),
+                        a.Hm1, a.Wm1);
+  const bool vy0 = c.inside && c.y0 >= 0, vy1 = c.inside && c.y0 < a.H - 1;
+  const bool vx0 = c.inside && c.x0 >= 0, vx1 = c.inside && c.x0 < a.W - 1;
+  const float hh = 1.0f - c.lh, hw = 1.0f - c.lw;
+  Tap r;
+  r.c[0] = (vy0 && vx0) ? m * (hh * hw) : 0.0f;
+  r.c[1] = (vy0 && vx1) ? m * (hh * c.lw) : 0.0f;
+  r.c[2] = (vy1 && vx0) ? m * (c.lh * hw) : 0.0f;
+  r.c[3] = (vy1 && vx1) ? m * (c.lh * c.lw) : 0.0f;
+  // pixel index within the lane's image fits 24 signed bits (H*W < 2^23)
+  const uint32_t o00 = t.lane_bytes +
+      (uint32_t)__mul24(__mul24(c.y0, a.W) + c.x0, (int)t.pix_bytes);
+  r.q[0] = (vy0 && vx0) ? o00 : kOutside;
+  r.q[1] = (vy0 && vx1) ? o00 + t.pix_bytes : kOutside;
+  r.q[2] = (vy1 && vx0) ? o00 + t.row_stride : kOutside;
+  r.q[3] = (vy1 && vx1) ? o00 + t.row_stride + t.pix_bytes : kOutside;
+  return r;
+}
+
+// The four corners' values of one point: NV 16-byte vectors per corner, or
+// (element path) DP single elements widened to fp32.
+template <int DT, int VEC, int NV> struct TapData {
+  u32x4 v[4][NV];
+  __device__ __forceinline__ void load(rsrc_t xr, const Tap& g) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        v[q][n] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(g.q[q] + 16 * n), 0, 0);
+  }
+  __device__ __forceinline__ void accumulate(float* acc, const Tap& g) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[n * VEC + e] = __builtin_fmaf(g.c[q], Io<DT>::lane(v[q][n], e), acc[n * VEC + e]);
+  }
+};
+template <int DT, int NV> struct TapData<DT, 1, NV> {
+  float v[4][NV];
+  __device__ __forceinline__ void load(rsrc_t xr, const Tap& g) {
+    typedef Io<DT> io;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        if (io::es == 4)
+          v[q][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, (int)(g.q[q] + 4 * e), 0, 0));
+        else
+          v[q][e] = io::dec((typename io::raw)__builtin_amdgcn_raw_buffer_load_b16(xr, (int)(g.q[q] + 2 * e), 0, 0));
+      }
+  }
+  __device__ __forceinline__ void accumulate(float* acc, const Tap& g) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) acc[e] = __builtin_fmaf(g.c[q], v[q][e], acc[e]);
+  }
+};
+
+// DT: I/O dtype; VEC: elements per load (16/es, or 1 on the element path);
+// NV: loads per corner (D' = VEC*NV); MODE: geometry; KS: 3 for a 3x3
+// kernel known at compile time, 0 for run-time kernel sizes.
+// Register budget: up to 128 VGPRs (4 waves per SIMD) for D' <= 2 vectors,
+// more for the wider lanes whose two point buffers need them.
+template <int DT, int VEC, int NV, int MODE, int KS>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
+void dcn4_forward_kernel(FwdArgs a) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  constexpr int DP = VEC * NV;
+  extern __shared__ u32x4 lds_rows[];
+
+  const int lb = xcd_block(blockIdx.x, a.nblocks);
+  const int item0 = lb * a.block;
+  const int item_last = min(item0 + a.block, a.total_items) - 1;
+
+  // ---- stage the offset/weight rows of the pixels this workgroup touches
+  const uint32_t p_first = fastdiv((uint32_t)item0, a.div_ipp);
+  const uint32_t p_last = fastdiv((uint32_t)item_last, a.div_ipp);
+  // The copy starts at the 16-byte boundary at or below the first row (an
+  // absolute address, so a tensor that is only element-aligned still gets
+  // aligned vector loads; the lead bytes lie in the same 16-byte chunk as
+  // the first row).  Bytes past the last row are not fetched (range check).
+  const uint64_t row_bytes = (uint64_t)a.rowel * es;
+  const char* first_row = a.om + (uint64_t)p_first * row_bytes;
+  const uint32_t lead = (uint32_t)((uintptr_t)first_row & 15u);
+  const char* aligned = first_row - lead;
+  const uint32_t len = lead + (uint32_t)((uint64_t)(p_last + 1 - p_first) * row_bytes);
+  {
+    const rsrc_t r = make_rsrc(aligned, (len + 3u) & ~3u);
+    const uint32_t nvec = (len + 15u) >> 4;
+    for (uint32_t v = threadIdx.x; v < nvec; v += (uint32_t)a.block)
+      lds_rows[v] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(v << 4), 0, 0);
+  }
+  __syncthreads();
+
+  const int item = item0 + (int)threadIdx.x;
+  if (item >= a.total_items) return;
+
+  // ---- which pixel, group and channel slice this lane owns
+  const uint32_t p = fastdiv((uint32_t)item, a.div_ipp);
+  const uint32_t r_in_pix = (uint32_t)item - p * (uint32_t)a.ipp;
+  const uint32_t g = fastdiv(r_in_pix, a.div_L);
+  const uint32_t l = r_in_pix - g * (uint32_t)a.L;
+  const uint32_t n = fastdiv(p, a.div_hw);
+  const uint32_t rem = p - n * (uint32_t)(a.Ho * a.Wo);
+  const uint32_t yo = fastdiv(rem, a.div_wo);
+  const uint32_t xo = rem - yo * (uint32_t)a.Wo;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+
+  // offset/weight row of (p, g) in LDS, as raw elements
+  const typename io::raw* om =
+      reinterpret_cast<const typename io::raw*>(lds_rows) + lead / es +
+      (p - p_first) * (uint32_t)a.rowel + g * (uint32_t)(3 * K);
+
+  // input: buffer based at the first image this workgroup touches
+  const uint32_t n_first = fastdiv(p_first, a.div_hw);
+  const uint64_t x_base = (uint64_t)n_first * a.img_bytes;
+  const uint64_t x_left = a.x_bytes - x_base;
+  const rsrc_t xr = make_rsrc(a.x + x_base,
+                              (uint32_t)(x_left < 0x7fffffffu ? x_left : 0x7fffffffu));
+  LaneCtx t;
+  t.pix_bytes = (uint32_t)a.C * es;
+  t.row_stride = (uint32_t)a.W * t.pix_bytes;
+  t.lane_bytes = (n - n_first) * a.img_bytes + (g * (uint32_t)a.D + l * DP) * es;
+  t.sg = (MODE == kGroupScale) ? a.scales[g] : 1.0f;
+  t.hy = ((KS ? KS : a.kh) - 1) >> 1;
+  t.hx = ((KS ? KS : a.kw) - 1) >> 1;
+  t.by0 = (int)yo * a.sh - a.ph + (MODE == kGroupScale ? t.hy : 0);
+  t.bx0 = (int)xo * a.sw - a.pw + (MODE == kGroupScale ? t.hx : 0);
+
+  float acc[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
+
+  // ---- software pipeline over the K points, two buffers: the geometry and
+  // the corner loads of the next point are issued before the multiply-adds
+  // of the current one, so one point's gathers are in flight while the other
+  // is accumulated.  The point index is wave-uniform (scalar registers); the
+  // loop is not unrolled so the compiler cannot sink the multiply-adds of all
+  // points below all the loads.
+  Tap ga = tap_geometry<DT, MODE, KS>(a, t, om, 0), gb;
+  TapData<DT, VEC, NV> da, db;
+  da.load(xr, ga);
+  int k = 0;
+#pragma unroll 1
+  for (; k + 1 < K; k += 2) {
+    gb = tap_geometry<DT, MODE, KS>(a, t, om, k + 1);
+    db.load(xr, gb);
+    da.accumulate(acc, ga);
+    if (k + 2 < K) {
+      ga = tap_geometry<DT, MODE, KS>(a, t, om, k + 2);
+      da.load(xr, ga);
+    }
+    db.accumulate(acc, gb);
+  }
+  if (k < K) da.accumulate(acc, ga);
+
+  // ---- epilogue: round to the I/O dtype, store D' contiguous channels.
+  // The empty asm pins each fp32 sum in a register, so the conversion is its
+  // own rounding (the compiler would otherwise fuse the last fma with the
+  // fp16 conversion into one rounding).
+#pragma unroll
+  for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
+  char* yp = a.y + ((uint64_t)p * (uint32_t)a.C + g * (uint32_t)a.D + l * DP) * es;
+  if (VEC > 1) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      u32x4 w;
+      if (es == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(acc[v * VEC + e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)io::enc(acc[v * VEC + 2 * e]) |
+                 ((uint32_t)io::enc(acc[v * VEC + 2 * e + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(yp + 16 * v) = w;
+    }
+  } else {
+    typedef typename io::raw R;
+#pragma unroll
+    for (int e = 0; e < DP; ++e) reinterpret_cast<R*>(yp)[e] = io::enc(acc[e]);
+  }
+}
+
+// ------------------------------------------------------------ geometry probe
+// One thread per (pixel, g, k); reads the merged tensor straight from global
+// memory and writes what the forward kernel's geometry functions compute.
+template <int DT, int MODE>
+__global__ __launch_bounds__(kBlock) void dcn4_probe_kernel(
+    FwdArgs a, int32_t* y0, int32_t* x0, float* lh, float* lw,
+    uint8_t* inside, int64_t count) {
+  typedef Io<DT> io;
+  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t >= count) return;
+  const int K = a.kh * a.kw;
+  const int64_t pg = t / K;
+  const int k = (int)(t - pg * K);
+  const int64_t p = pg / a.G;
+  const int g = (int)(pg - p * a.G);
+  const int64_t hw = (int64_t)a.Ho * a.Wo;
+  const int rem = (int)(p % hw);
+  const int yo = rem / a.Wo, xo = rem % a.Wo;
+  const int i = k / a.kw, j = k % a.kw;
+  const typename io::raw* om =
+      reinterpret_cast<const typename io::raw*>(a.om) + (p * a.G + g) * (3 * K);
+  const float dx = io::dec(om[2 * k]);
+  const float dy = io::dec(om[2 * k + 1]);
+  const float sg = (MODE == kGroupScale) ? a.scales[g] : 1.0f;
+  const int hy = (a.kh - 1) >> 1, hx = (a.kw - 1) >> 1;
+  float by, bx, gy = 0.0f, gx = 0.0f;
+  if (MODE == kGroupScale) {
+    by = (float)(yo * a.sh - a.ph + hy);
+    bx = (float)(xo * a.sw - a.pw + hx);
+    gy = (float)(i - hy);
+    gx = (float)(j - hx);
+  } else {
+    by = (float)(yo * a.sh - a.ph + i * a.dh);
+    bx = (float)(xo * a.sw - a.pw + j * a.dw);
+  }
+  const Cell c = locate(sample_location<MODE>(by, bx, gy, gx, dy, dx,
+                                              a.offset_scale, sg),
+                        a.Hm1, a.Wm1);
+  inside[t] = c.inside ? 1 : 0;
+  y0[t] = c.inside ? c.y0 : 0;
+  x0[t] = c.inside ? c.x0 : 0;
+  lh[t] = c.inside ? c.lh : 0.0f;
+  lw[t] = c.inside ? c.lw : 0.0f;
+}
+
+// ------------------------------------------------------------ host launchers
+typedef void (*fwd_fn)(FwdArgs);
+
+template <int DT, int VEC, int NV, int MODE>
+fwd_fn pick_ks(int K3) {
+  return K3 ? dcn4_forward_kernel<DT, VEC, NV, MODE, 3>
+            : dcn4_forward_kernel<DT, VEC, NV, MODE, 0>;
+}
+
+template <int DT, int VEC, int NV>
+fwd_fn pick_mode(int mode, int K3) {
+  switch (mode) {
+    case kStdUnitScale: return pick_ks<DT, VEC, NV, kStdUnitScale>(K3);
+    case kStdScaled: return pick_ks<DT, VEC, NV, kStdScaled>(K3);
+    default: return pick_ks<DT, VEC, NV, kGroupScale>(K3);
+  }
+}
+
+template <int DT>
+fwd_fn pick_vec(bool vector_path, int nv, int mode, int K3) {
+  constexpr int V = 16 / Io<DT>::es;
+  if (!vector_path) return pick_mode<DT, 1, 1>(mode, K3);
+  switch (nv) {
+    case 1: return pick_mode<DT, V, 1>(mode, K3);
+    case 2: return pick_mode<DT, V, 2>(mode, K3);
+    case 3: return pick_mode<DT, V, 3>(mode, K3);
+    default: return pick_mode<DT, V, 4>(mode, K3);
+  }
+}
+
+fwd_fn pick_forward(int dtype, bool vector_path, int nv, int mode, int K3) {
+  switch (dtype) {
+    case DCN4_F32: return pick_vec<DCN4_F32>(vector_path, nv, mode, K3);
+    case DCN4_BF16: return pick_vec<DCN4_BF16>(vector_path, nv, mode, K3);
+    default: return pick_vec<DCN4_F16>(vector_path, nv, mode, K3);
+  }
+}
+
+void fill_common(const Plan& p, FwdArgs& a) {
+  const dcn4_desc& d = p.desc;
+  a.H = d.H; a.W = d.W; a.C = d.C; a.G = d.group; a.D = p.D;
+  a.Ho = p.Ho; a.Wo = p.Wo;
+  a.kh = d.kernel_h; a.kw = d.kernel_w; a.sh = d.stride_h; a.sw = d.stride_w;
+  a.ph = d.pad_h; a.pw = d.pad_w; a.dh = d.dilation_h; a.dw = d.dilation_w;
+  a.offset_scale = d.offset_scale;
+  a.Hm1 = (float)(d.H - 1);
+  a.Wm1 = (float)(d.W - 1);
+  a.rowel = d.group * 3 * p.K;
+  a.img_bytes = (uint32_t)((uint64_t)d.H * d.W * d.C * p.es);
+  a.div_hw = make_fastdiv((uint32_t)(p.Ho * p.Wo));
+  a.div_wo = make_fastdiv((uint32_t)p.Wo);
+}
+
+}  // namespace
+
+thread_local char g_hip_error[128] = "";
+
+void note_hip_error(hipError_t e) {
+  snprintf(g_hip_error, sizeof g_hip_error, "%s (%d): %s", hipGetErrorName(e),
+           (int)e, hipGetErrorString(e));
+}
+
+const char* last_hip_error() { return g_hip_error; }
+
+int32_t forward_lds_bytes(const Plan& p, int32_t lanes_per_group, int32_t block) {
+  // pixels a range of `block` items can touch, plus one 16-byte alignment lead
+  const int64_t ipp = (int64_t)p.desc.group * lanes_per_group;
+  const int64_t pixels = (block + ipp - 1) / ipp + 1;
+  const int64_t bytes = pixels * p.desc.group * 3 * p.K * p.es + 16;
+  return (int32_t)((bytes + 15) & ~int64_t(15));
+}
+
+int32_t forward_block(const Plan& p, int32_t lanes_per_group) {
+  for (int32_t b = kBlock; b >= 64; b >>= 1)
+    if (forward_lds_bytes(p, lanes_per_group, b) <= kLdsBudget) return b;
+  return 0;
+}
+
+dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
+                           const float* scales, void* y, void* stream,
+                           bool vector_path) {
+  const dcn4_desc& d = p.desc;
+  const int dp = vector_path ? p.dp : 1;
+  const int L = p.D / dp;
+  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  fwd_fn fn = pick_forward(d.dtype, vector_path, dp / (16 / p.es), p.mode, K3);
+  const int32_t block = forward_block(p, L);
+  if (block == 0) return DCN4_ERR_UNSUPPORTED;
+  const int32_t lds = forward_lds_bytes(p, L, block);
+  FwdArgs a{};
+  fill_common(p, a);
+  a.scales = scales;
+  a.L = L;
+  a.ipp = d.group * L;
+  a.div_ipp = make_fastdiv((uint32_t)a.ipp);
+  a.div_L = make_fastdiv((uint32_t)L);
+  const uint64_t x_img = (uint64_t)d.H * d.W * d.C * p.es;
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t om_img = (uint64_t)p.Ho * p.Wo * a.rowel * p.es;
+  for (int32_t n0 = 0; n0 < d.N; n0 += p.images_per_launch) {
+    const int32_t nb = (d.N - n0) < p.images_per_launch ? (d.N - n0) : p.images_per_launch;
+    a.x = static_cast<const char*>(x) + n0 * x_img;
+    a.om = static_cast<const char*>(om) + n0 * om_img;
+    a.y = static_cast<char*>(y) + n0 * y_img;
+    a.x_bytes = nb * x_img;
+    a.om_bytes = nb * om_img;
+    a.total_items = (int32_t)((int64_t)nb * p.Ho * p.Wo * a.ipp);
+    a.block = block;
+    a.nblocks = (a.total_items + block - 1) / block;
+    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(block), lds,
+                       static_cast<hipStream_t>(stream), a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  return DCN4_OK;
+}
+
+dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
+                         int32_t* y0, int32_t* x0, float* lh, float* lw,
+                         uint8_t* inside, void* stream) {
+  FwdArgs a{};
+  fill_common(p, a);
+  a.om = static_cast<const char*>(om);
+  a.scales = scales;
+  const int64_t count = (int64_t)p.desc.N * p.Ho * p.Wo * p.desc.group * p.K;
+  if (count == 0) return DCN4_OK;
+  const int64_t blocks = (count + kBlock - 1) / kBlock;
+  typedef void (*probe_fn)(FwdArgs, int32_t*, int32_t*, float*, float*, uint8_t*, int64_t);
+  probe_fn fn;
+  const int m = p.mode;
+  switch (p.desc.dtype) {
+    case DCN4_F32:
+      fn = m == kStdUnitScale ? dcn4_probe_kernel<DCN4_F32, kStdUnitScale>
+         : m == kStdScaled ? dcn4_probe_kernel<DCN4_F32, kStdScaled>
+                           : dcn4_probe_kernel<DCN4_F32, kGroupScale>;
+      break;
+    case DCN4_BF16:
+      fn = m == kStdUnitScale ? dcn4_probe_kernel<DCN4_BF16, kStdUnitScale>
+         : m == kStdScaled ? dcn4_probe_kernel<DCN4_BF16, kStdScaled>
+                           : dcn4_probe_kernel<DCN4_BF16, kGroupScale>;
+      break;
+    default:
+      fn = m == kStdUnitScale ? dcn4_probe_kernel<DCN4_F16, kStdUnitScale>
+         : m == kStdScaled ? dcn4_probe_kernel<DCN4_F16, kStdScaled>
+                           : dcn4_probe_kernel<DCN4_F16, kGroupScale>;
+      break;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), a, y0, x0, lh, lw,
+                     inside, count);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    note_hip_error(e);
+    return DCN4_ERR_HIP;
+  }
+  return DCN4_OK;
+}
+
+}  // namespace dcn4

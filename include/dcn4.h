@@ -1,0 +1,178 @@
+/*
+ * dcn4.h -- C ABI of the MI355X (gfx950) DCNv4 forward spatial-aggregation
+ * library, libdcn4.so.
+ *
+ * The operation (pages cited by title and section):
+ *   [DCNv4 digest] CSDN "（论文速读）DCNv4：高效可变形卷积算子"
+ *   [FlowDCN]      kler.cn "NeurIPS'24 | FlowDCN：基于可变形卷积的任意分辨率
+ *                  图像生成模型"
+ *   [CANN Conv2D]  intelliparadigm "CANN ops-nn 算子与 Stable Diffusion 的卷积
+ *                  实现"
+ *
+ * For every output pixel (n, yo, xo) and channel group g (G groups of
+ * D = C/G channels), K = kernel_h*kernel_w points are sampled from the input
+ * by bilinear interpolation with zero padding and summed with per-point
+ * weights m that are not normalised (no softmax; [DCNv4 digest] section 1).
+ * All D channels of a group share the offsets and the weights ([DCNv4 digest]
+ * "方法1"); the groups' outputs are concatenated along channels ([FlowDCN]
+ * 2.2).  Point k = i*kernel_w + j of group g samples
+ *   standard mode:    row = yo*stride_h - pad_h + i*dilation_h
+ *                           + offset_scale*dy_k,   (col likewise with dx_k)
+ *   group-scale mode: row = yo*stride_h - pad_h + (kernel_h-1)/2
+ *                           + s_g*((i - (kernel_h-1)/2) + dy_k)
+ *                     (FlowDCN groupwise multi-scale, [FlowDCN] 3.1; odd
+ *                     kernels, dilation 1, offset_scale 1)
+ * and y = sum_k m_k * bilinear(x, row, col).  The base location is the
+ * convolution index of [CANN Conv2D] 2.1 with padding and dilation; the
+ * output size is Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
+ * (Wo likewise).
+ *
+ * Arithmetic: fp32 throughout.  Per sample: one fp32 add for the location
+ * (group-scale mode: fl(centre + fl(s_g*fl(grid + d)))); the sample is skipped
+ * unless -1 < row < H and -1 < col < W; y0 = floor(row), lh = row - y0,
+ * hh = 1 - lh (same for x); corner weights hh*hw, hh*lw, lh*hw, lh*lw for
+ * corners (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1); coefficient fl(m*w);
+ * corners outside the image are skipped; acc = fma(coefficient, value, acc)
+ * with points outer and corners inner, starting from +0; the result is
+ * rounded to the I/O dtype to nearest even.  Subnormals are kept.
+ *
+ * Layouts (all dense, channel-last, row-major):
+ *   x            [N, H, W, C]          I/O dtype
+ *   offset_mask  [N, Ho, Wo, G, 3K]    I/O dtype; per group the K interleaved
+ *                                      (dx_k, dy_k) pairs (x along W), then
+ *                                      the K weights m_k.  This is the single
+ *                                      tensor a merged offset/weight linear
+ *                                      layer emits ([DCNv4 digest] "方法3").
+ *   group_scales [G]                   fp32, group-scale mode only
+ *   y            [N, Ho, Wo, C]        I/O dtype
+ *
+ * Ownership and execution: the caller owns every buffer and the stream.  All
+ * data pointers are device pointers.  The library allocates no device memory;
+ * a plan holds host-side metadata only and is immutable after creation, so one
+ * plan may be used from several host threads and streams at once.  Forward
+ * calls are asynchronous on `stream` (a hipStream_t, NULL = the default
+ * stream) and never synchronise; buffers must stay alive until the stream's
+ * work has completed.  y must not overlap x or offset_mask.
+ *
+ * Errors: every call returns a status and never throws across the ABI.
+ * Arguments are validated before anything is launched, so an error status
+ * means nothing was enqueued (except DCN4_ERR_HIP, reported by the runtime at
+ * launch).  dcn4_last_error() gives a message for the calling thread's last
+ * failed call.
+ */
+#ifndef DCN4_H
+#define DCN4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DCN4_F32 = 0,  /* IEEE binary32 */
+  DCN4_BF16 = 1, /* bfloat16 (upper half of a binary32) */
+  DCN4_F16 = 2   /* IEEE binary16 */
+} dcn4_dtype;
+
+typedef enum {
+  DCN4_OK = 0,
+  DCN4_ERR_INVALID_ARG = -1, /* descriptor or argument not a valid operation */
+  DCN4_ERR_UNSUPPORTED = -2, /* valid, but beyond this library's size limits */
+  DCN4_ERR_MISALIGNED = -3,  /* pointer not aligned to its element size      */
+  DCN4_ERR_NULL = -4,        /* required pointer is NULL                       */
+  DCN4_ERR_HIP = -5,         /* the HIP runtime reported an error at launch    */
+  DCN4_ERR_NOMEM = -6        /* host allocation of the plan failed             */
+} dcn4_status;
+
+/* Operation descriptor.  Valid when: N >= 0; H, W, C, group >= 1;
+ * C % group == 0; kernel, stride, dilation >= 1; pad >= 0; the output size is
+ * at least 1x1; H, W, pads, strides and dilation*kernel <= 2^20; offset_scale
+ * finite.  With use_group_scales != 0 the kernel sizes must be odd and
+ * dilation and offset_scale must be 1. */
+typedef struct {
+  int32_t N, H, W, C, group;
+  int32_t kernel_h, kernel_w;
+  int32_t stride_h, stride_w;
+  int32_t pad_h, pad_w;
+  int32_t dilation_h, dilation_w;
+  float offset_scale;       /* multiplies (dx, dy) in standard mode        */
+  int32_t use_group_scales; /* 1: FlowDCN groupwise multi-scale geometry   */
+  int32_t dtype;            /* dcn4_dtype of x, offset_mask and y          */
+} dcn4_desc;
+
+typedef struct dcn4_plan dcn4_plan; /* opaque, immutable after creation */
+
+/* Validates `desc`, chooses the kernel variant and launch shape, and returns
+ * a plan in *plan (NULL on error).  Errors: DCN4_ERR_NULL (desc or plan NULL),
+ * DCN4_ERR_INVALID_ARG, DCN4_ERR_UNSUPPORTED (a single image's tensors beyond
+ * 2^31 bytes), DCN4_ERR_NOMEM.  Makes no HIP call. */
+dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan);
+
+/* Output size and the ideal traffic of one forward pass in bytes: input and
+ * output once, the offset/weight tensor once, plus 4G bytes of scales in
+ * group-scale mode (the 2HWC + 27HWG element model of [DCNv4 digest]
+ * "GPU效率的理论分析", with input and output at their own sizes).  Any output
+ * pointer may be NULL.  Errors: DCN4_ERR_NULL (plan NULL). */
+dcn4_status dcn4_query(const dcn4_plan* plan, int32_t* Ho, int32_t* Wo,
+                       uint64_t* ideal_bytes);
+
+/* Launch shape the plan chose (for tests, tuning and reports). */
+typedef struct {
+  int32_t channels_per_lane; /* D' -- channels one lane owns                */
+  int32_t vector_bytes;      /* bytes per load/store instruction (16 or es) */
+  int32_t lanes_per_group;   /* D / D'                                      */
+  int32_t block_threads;     /* threads per workgroup                       */
+  int64_t blocks;            /* workgroups over all launches                */
+  int32_t launches;          /* kernel launches per forward call            */
+  int32_t lds_bytes;         /* dynamic LDS per workgroup                   */
+} dcn4_launch_info;
+
+/* Fills *info for the plan as it would run with 16-byte aligned pointers.
+ * Errors: DCN4_ERR_NULL. */
+dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info);
+
+/* Overrides the channels each lane owns (D' = channels_per_lane; 0 restores
+ * the default).  D' must be a multiple of the 16-byte vector width (4 fp32 or
+ * 8 half-precision values), divide D, and be at most 4 vectors; the result is
+ * bit-identical for every valid choice.  Errors: DCN4_ERR_NULL,
+ * DCN4_ERR_INVALID_ARG.  Not safe while another thread uses the plan. */
+dcn4_status dcn4_plan_set_channels_per_lane(dcn4_plan* plan,
+                                            int32_t channels_per_lane);
+
+/* Enqueues the forward pass y = DCNv4(x, offset_mask[, group_scales]) on
+ * `stream`.  group_scales must be non-NULL exactly when the plan uses group
+ * scales.  Pointers must be aligned to the element size (4 B for fp32 and the
+ * scales, 2 B otherwise); when x, offset_mask and y are 16-byte aligned and
+ * D*es is a multiple of 16 the vectorised kernel runs, otherwise an
+ * element-wise kernel computes the identical result.  N == 0 enqueues
+ * nothing.  Errors: DCN4_ERR_NULL, DCN4_ERR_MISALIGNED, DCN4_ERR_INVALID_ARG
+ * (scales given or missing against the plan's mode), DCN4_ERR_HIP. */
+dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
+                         const void* offset_mask, const float* group_scales,
+                         void* y, void* stream);
+
+/* Test probe of the sampling geometry: for every (n, yo, xo, g, k), in that
+ * order, writes inside (1 if the sample passed the -1<row<H, -1<col<W test),
+ * and for inside samples y0 = floor(row), x0 = floor(col), lh = row - y0,
+ * lw = col - x0 (zeros otherwise), computed by the same device functions as
+ * the forward kernel.  Outputs are device arrays of N*Ho*Wo*G*K entries.
+ * Errors as dcn4_forward. */
+dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
+                                const float* group_scales, int32_t* y0,
+                                int32_t* x0, float* lh, float* lw,
+                                uint8_t* inside, void* stream);
+
+/* Frees the plan; NULL is allowed. */
+void dcn4_destroy(dcn4_plan* plan);
+
+/* Static description of a status code. */
+const char* dcn4_status_string(dcn4_status status);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* dcn4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,241 @@
+"""C ABI of libdcn4.so on the CPU: exported symbols, planning, and every
+error path (validation happens before any HIP call, so none of these touch a
+GPU).  Output sizes and ideal bytes are checked against the oracle, which
+computes them independently."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dynamic_sparse_vision_dcn4_amd as d4
+import oracle
+from oracle import Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcn4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcn4_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
+              "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
+              "dcn4_plan_info", "dcn4_plan_set_channels_per_lane"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(d4.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and they are C symbols (no C++ mangling) in the dynamic symbol table
+    out = subprocess.run(["nm", "-D", "--defined-only", d4.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    for n in declared_functions():
+        assert re.search(rf"\sT\s{n}$", out, re.M), n
+
+
+def mk(**kw):
+    base = dict(N=2, H=16, W=16, C=64, group=4, dtype="bf16")
+    base.update(kw)
+    return d4.Desc(**base)
+
+
+def create(desc):
+    st, h = d4.dcn4_create(desc.c_struct())
+    return st, h
+
+
+@pytest.mark.parametrize("kw, want", [
+    (dict(C=63), d4.DCN4_ERR_INVALID_ARG),                 # C % group != 0
+    (dict(H=0), d4.DCN4_ERR_INVALID_ARG),
+    (dict(N=-1), d4.DCN4_ERR_INVALID_ARG),
+    (dict(group=0), d4.DCN4_ERR_INVALID_ARG),
+    (dict(kernel_h=0), d4.DCN4_ERR_INVALID_ARG),
+    (dict(stride_w=0), d4.DCN4_ERR_INVALID_ARG),
+    (dict(pad_h=-1), d4.DCN4_ERR_INVALID_ARG),
+    (dict(dilation_w=0), d4.DCN4_ERR_INVALID_ARG),
+    (dict(H=2, pad_h=0), d4.DCN4_ERR_INVALID_ARG),          # empty output
+    (dict(offset_scale=float("nan")), d4.DCN4_ERR_INVALID_ARG),
+    (dict(use_group_scales=True, kernel_h=4), d4.DCN4_ERR_INVALID_ARG),
+    (dict(use_group_scales=True, dilation_h=2), d4.DCN4_ERR_INVALID_ARG),
+    (dict(use_group_scales=True, offset_scale=2.0), d4.DCN4_ERR_INVALID_ARG),
+    (dict(H=1 << 21), d4.DCN4_ERR_INVALID_ARG),
+    (dict(N=1, H=4096, W=4096, C=16, group=1), d4.DCN4_ERR_UNSUPPORTED),  # H*W >= 2^23
+    (dict(N=1, H=1024, W=1024, C=2048, group=16), d4.DCN4_ERR_UNSUPPORTED),
+])
+def test_create_rejects(kw, want):
+    st, h = create(mk(**kw))
+    assert st == want, (st, d4.dcn4_last_error())
+    assert h is None
+    assert d4.dcn4_last_error() != ""
+
+
+def test_create_null_arguments():
+    h = ctypes.c_void_p()
+    assert d4._lib.dcn4_create(None, ctypes.byref(h)) == d4.DCN4_ERR_NULL
+    desc = mk().c_struct()
+    assert d4._lib.dcn4_create(ctypes.byref(desc), None) == d4.DCN4_ERR_NULL
+    assert d4.dcn4_query(None)[0] == d4.DCN4_ERR_NULL
+    assert d4.dcn4_forward(None, 16, 16, None, 16, None) == d4.DCN4_ERR_NULL
+    d4.dcn4_destroy(None)  # NULL-safe
+
+
+def test_bad_dtype():
+    desc = mk().c_struct()
+    desc.dtype = 7
+    h = ctypes.c_void_p()
+    assert d4._lib.dcn4_create(ctypes.byref(desc), ctypes.byref(h)) == d4.DCN4_ERR_INVALID_ARG
+
+
+WORKLOAD_SHAPES = [
+    (Shape(1, 16, 16, 64, 4), "f32"),
+    (Shape(64, 56, 56, 64, 4), "bf16"),
+    (Shape(8, 128, 128, 320, 20), "bf16"),
+    (Shape(16, 32, 32, 1280, 40, dh=2, dw=2), "f16"),
+    (Shape(32, 32, 32, 1152, 16, multiscale=True), "bf16"),
+    (Shape(3, 9, 11, 24, 3, kh=5, kw=3, sh=2, sw=1, ph=2, pw=0, dh=1, dw=2,
+           offset_scale=0.5), "f32"),
+]
+
+
+def desc_of(s: Shape, dt: str) -> d4.Desc:
+    return d4.Desc(s.N, s.H, s.W, s.C, s.G, s.kh, s.kw, s.sh, s.sw, s.ph, s.pw,
+                   s.dh, s.dw, s.offset_scale, s.multiscale, dt)
+
+
+@pytest.mark.parametrize("s, dt", WORKLOAD_SHAPES)
+def test_query_matches_oracle(s, dt):
+    o = oracle.get()
+    p = d4.Plan(desc_of(s, dt))
+    assert (p.Ho, p.Wo) == o.out_size(s)
+    assert p.ideal_bytes == o.ideal_bytes(s, dt)
+    info = p.info()
+    D = s.C // s.G
+    assert D % info["channels_per_lane"] == 0
+    assert info["lanes_per_group"] * info["channels_per_lane"] == D
+    assert info["launches"] >= 1 and info["blocks"] >= 1
+
+
+def test_headline_plan_shape():
+    p = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
+    info = p.info()
+    # a lane owns a whole 16-channel group, two 128-bit loads per corner
+    assert info["channels_per_lane"] == 16 and info["vector_bytes"] == 16
+    assert info["blocks"] == 8 * 128 * 128 * 20 // 256
+
+
+def test_channels_per_lane_override():
+    p = d4.Plan(desc_of(Shape(2, 8, 8, 64, 2), "bf16"))   # D = 32
+    for dp in (8, 16, 32):
+        p.set_channels_per_lane(dp)
+        assert p.info()["channels_per_lane"] == dp
+    for bad in (4, 12, 24, 64):
+        with pytest.raises(d4.DCN4Error):
+            p.set_channels_per_lane(bad)
+    p.set_channels_per_lane(0)
+    assert p.info()["channels_per_lane"] == 16
+
+
+def test_element_path_plan_when_group_is_not_vector_wide():
+    p = d4.Plan(desc_of(Shape(1, 8, 8, 30, 3), "bf16"))   # D = 10: 20 bytes
+    info = p.info()
+    assert info["channels_per_lane"] == 1 and info["vector_bytes"] == 2
+
+
+def test_many_images_split_into_launches():
+    # lanes per launch stay below 2^31: 2^31 / (64*64*1024) = 512 images
+    p = d4.Plan(d4.Desc(N=2000, H=64, W=64, C=1024, group=64, dtype="bf16"))
+    assert p.info()["launches"] == 4
+
+
+class TestForwardValidation:
+    """dcn4_forward / dcn4_probe_geometry reject bad pointers before launching."""
+
+    def setup_method(self):
+        self.p = d4.Plan(mk())
+        self.ms = d4.Plan(mk(use_group_scales=True))
+
+    def fwd(self, p, x, om, sc, y):
+        return d4.dcn4_forward(p.handle, x, om, sc, y, None)
+
+    def test_null(self):
+        assert self.fwd(self.p, None, 256, None, 512) == d4.DCN4_ERR_NULL
+        assert self.fwd(self.p, 256, None, None, 512) == d4.DCN4_ERR_NULL
+        assert self.fwd(self.p, 256, 256, None, None) == d4.DCN4_ERR_NULL
+
+    def test_scales_against_mode(self):
+        assert self.fwd(self.p, 256, 256, 1024, 512) == d4.DCN4_ERR_INVALID_ARG
+        assert self.fwd(self.ms, 256, 256, None, 512) == d4.DCN4_ERR_NULL
+
+    def test_misaligned(self):
+        assert self.fwd(self.p, 257, 256, None, 512) == d4.DCN4_ERR_MISALIGNED
+        assert self.fwd(self.p, 256, 255, None, 512) == d4.DCN4_ERR_MISALIGNED
+        assert self.fwd(self.p, 256, 256, None, 513) == d4.DCN4_ERR_MISALIGNED
+        assert self.fwd(self.ms, 256, 256, 1026, 512) == d4.DCN4_ERR_MISALIGNED
+        f32 = d4.Plan(mk(dtype="f32"))
+        assert self.fwd(f32, 258, 256, None, 512) == d4.DCN4_ERR_MISALIGNED
+
+    def test_probe(self):
+        h = self.p.handle
+        assert d4.dcn4_probe_geometry(h, 256, None, None, 256, 256, 256, 256, None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_probe_geometry(h, 256, None, 258, 256, 256, 256, 256, None) == d4.DCN4_ERR_MISALIGNED
+        assert d4.dcn4_probe_geometry(h, None, None, 256, 256, 256, 256, 256, None) == d4.DCN4_ERR_NULL
+
+    def test_empty_batch_is_a_no_op(self):
+        p0 = d4.Plan(mk(N=0))
+        # nothing is enqueued, so no pointer is touched and no GPU is needed
+        assert d4.dcn4_forward(p0.handle, None, None, None, None, None) == d4.DCN4_OK
+        assert p0.ideal_bytes == 0
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert d4.dcn4_status_string(s).startswith("DCN4_")
+    assert "unknown" in d4.dcn4_status_string(42)
+
+
+def test_fast_division_exhaustive_ranges(tmp_path):
+    """The kernels divide by run-time invariants with the multiply-high
+    method; the host's constants must give exact quotients for n < 2^31."""
+    src = tmp_path / "fd.cpp"
+    src.write_text(r'''
+#include <cstdio>
+#include <cstdint>
+#include "dcn4_internal.h"
+int main() {
+  uint64_t bad = 0, checked = 0;
+  uint32_t ds[] = {1,2,3,4,5,7,9,20,27,40,48,64,144,900,1024,1080,3136,16384,
+                   65535,65536,1000003,(1u<<30)+7,(1u<<31)-1};
+  for (uint32_t d : ds) {
+    dcn4::FastDiv f = dcn4::make_fastdiv(d);
+    for (uint64_t n = 0; n < (1ull << 31); n += (n < 4000000 ? 1 : 999983)) {
+      uint32_t q = (uint32_t)((((uint64_t)n * f.m) >> 32) + n) >> f.s;
+      bad += (q != n / d); ++checked;
+    }
+    for (uint64_t k = 1; k * d < (1ull << 31) && k < 100000; k += 1 + k / 10) {
+      for (int64_t r = -1; r <= 1; ++r) {
+        uint64_t n = k * d + r;
+        if (n >= (1ull << 31)) continue;
+        uint32_t q = (uint32_t)((((uint64_t)n * f.m) >> 32) + n) >> f.s;
+        bad += (q != n / d); ++checked;
+      }
+    }
+  }
+  printf("%llu %llu\n", (unsigned long long)bad, (unsigned long long)checked);
+  return bad != 0;
+}
+''')
+    exe = tmp_path / "fd"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROOT, "dynamic_sparse_vision_dcn4_amd", "csrc"),
+                    str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout

@@ -1,0 +1,301 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Gates, written here:
+  * every dtype: the output is compared element by element with the oracle's
+    fp32 evaluation (same operation order, rounded the same way); the number
+    of differing elements must be 0;
+  * fp32 I/O: max_i |y_gpu - y_def| / (|y_def| + RMS(y_def)) <= 1e-5 against
+    the fp64 definition (on sampled pixels at full size);
+  * bf16/fp16 I/O: max_i |y_gpu - y_oracle| / RMS(y_oracle) <= 1e-2 with
+    y_oracle the oracle's output rounded to the I/O dtype;
+  * sample indices: the geometry probe equals the oracle's (y0, x0, lh, lw,
+    inside) bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import Shape
+from workloads import WORKLOADS, from_raw, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import dynamic_sparse_vision_dcn4_amd as d4  # noqa: E402
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+NTHREADS = 16
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(raw, dt, offset_elems=0):
+    """numpy raw -> CUDA tensor of the I/O dtype; offset_elems > 0 returns a
+    view that starts that many elements into a larger buffer (misaligned)."""
+    if dt == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(raw, np.float32))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(TORCH_DT[dt])
+    if offset_elems:
+        buf = torch.empty(t.numel() + offset_elems, dtype=t.dtype, device="cuda")
+        v = buf[offset_elems:].view(t.shape)
+        v.copy_(t.cuda())
+        return v
+    return t.cuda()
+
+
+def to_raw_np(t, dt):
+    t = t.detach().cpu().contiguous()
+    if dt == "f32":
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def desc_of(s: Shape, dt: str) -> d4.Desc:
+    return d4.Desc(s.N, s.H, s.W, s.C, s.G, s.kh, s.kw, s.sh, s.sw, s.ph, s.pw,
+                   s.dh, s.dw, s.offset_scale, s.multiscale, dt)
+
+
+def shape_of(w) -> Shape:
+    return Shape(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+                 w.dh, w.dw, w.offset_scale, w.multiscale)
+
+
+def gpu_forward(plan, inp, dt, offset_elems=0):
+    x = to_dev(inp.x, dt, offset_elems)
+    om = to_dev(inp.om, dt, offset_elems)
+    sc = None if inp.scales is None else torch.from_numpy(inp.scales).cuda()
+    out = None
+    if offset_elems:
+        buf = torch.empty(int(np.prod(plan.out_shape())) + offset_elems,
+                          dtype=TORCH_DT[dt], device="cuda")
+        out = buf[offset_elems:].view(plan.out_shape())
+    y = plan.forward(x, om, sc, out=out)
+    torch.cuda.synchronize()
+    return to_raw_np(y, dt)
+
+
+def bits_equal(a, b, dt):
+    """element-wise equality of raw encodings, NaN == NaN (any payload)"""
+    fa, fb = from_raw(a, dt), from_raw(b, dt)
+    same = (np.asarray(a).view(np.uint16 if dt != "f32" else np.uint32) ==
+            np.asarray(b).view(np.uint16 if dt != "f32" else np.uint32))
+    return same | (np.isnan(fa) & np.isnan(fb))
+
+
+def check_against_oracle(y_gpu, y_or, dt, what):
+    eq = bits_equal(y_gpu, y_or, dt)
+    ndiff = int((~eq).sum())
+    fg = from_raw(y_gpu, dt).astype(np.float64)
+    fo = from_raw(y_or, dt).astype(np.float64)
+    fin = np.isfinite(fo)
+    rms = np.sqrt(np.mean(fo[fin] ** 2)) if fin.any() else 1.0
+    rms = rms if rms > 0 else 1.0
+    err = np.abs(fg - fo)[fin].max(initial=0.0) / rms
+    say(f"{what}: {ndiff} of {eq.size} elements differ; max|d|/RMS = {err:.3g}")
+    if dt != "f32":
+        assert err <= 1e-2, f"{what}: max|d|/RMS {err} > 1e-2"
+    assert ndiff == 0, f"{what}: {ndiff} elements differ from the oracle"
+
+
+def check_fp32_gate(y_gpu, y_def, what):
+    g = from_raw(y_gpu, "f32").astype(np.float64)
+    rms = np.sqrt(np.mean(y_def ** 2))
+    rel = np.max(np.abs(g - y_def) / (np.abs(y_def) + rms))
+    say(f"{what}: fp32 relative error vs fp64 definition {rel:.3g}")
+    assert rel <= 1e-5
+
+
+# ------------------------------------------------------------------ fuzz
+def fuzz_cases(n=40, seed=1234):
+    rng = np.random.default_rng(seed)
+    cases = []
+    kernels = [(3, 3), (1, 1), (5, 5), (3, 5), (2, 2), (3, 3), (3, 3)]
+    for t in range(n):
+        dt = ["f32", "bf16", "f16"][t % 3]
+        ms = (t % 5 == 4)
+        kh, kw = kernels[rng.integers(len(kernels))]
+        if ms and (kh % 2 == 0 or kw % 2 == 0):
+            kh, kw = 3, 3
+        D = int(rng.choice([8, 16, 24, 32, 10, 72, 4]))
+        G = int(rng.integers(1, 5))
+        N = int(rng.integers(1, 4))
+        H = int(rng.integers(5, 40))
+        W = int(rng.integers(5, 40))
+        sh, sw = (1, 1) if ms else (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+        dh, dw = (1, 1) if ms else (int(rng.integers(1, 4)), int(rng.integers(1, 3)))
+        ph, pw = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        os_ = 1.0 if (ms or t % 4) else 0.5
+        s = Shape(N, H, W, G * D, G, kh, kw, sh, sw, ph, pw, dh, dw, os_, ms)
+        try:
+            oracle.get().out_size(s)
+        except ValueError:
+            continue
+        cases.append((t, s, dt))
+    return cases
+
+
+def fuzz_inputs(s, dt, Ho, Wo, seed):
+    rng = np.random.default_rng(seed)
+    K = s.K
+    x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
+    off = rng.uniform(-3, 3, (s.N, Ho, Wo, s.G, 2 * K)).astype(np.float32)
+    m = (rng.standard_normal((s.N, Ho, Wo, s.G, K)) / 3).astype(np.float32)
+    om = np.concatenate([off, m], -1)
+    scales = (rng.uniform(0.5, 3.0, s.G).astype(np.float32) if s.multiscale else None)
+    return workloads.Inputs(workloads.to_raw(x, dt), workloads.to_raw(om, dt), scales)
+
+
+@pytest.mark.parametrize("t, s, dt", fuzz_cases(), ids=lambda v: str(v) if isinstance(v, int) else None)
+def test_fuzz_parity(t, s, dt):
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=t)
+    say(f"fuzz case {t}: {s} {dt}")
+    plan = d4.Plan(desc_of(s, dt))
+    assert (plan.Ho, plan.Wo) == (Ho, Wo)
+    y = gpu_forward(plan, inp, dt)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
+    check_against_oracle(y, y_or, dt, f"fuzz {t}")
+    if dt == "f32":
+        check_fp32_gate(y, o.forward_f64(s, dt, inp.x, inp.om, inp.scales,
+                                         nthreads=NTHREADS), f"fuzz {t}")
+    # sample indices, bit for bit
+    om_dev = to_dev(inp.om, dt)
+    sc = None if inp.scales is None else torch.from_numpy(inp.scales).cuda()
+    g = plan.probe_geometry(om_dev, sc)
+    torch.cuda.synchronize()
+    ref = o.geometry(s, dt, inp.om, inp.scales)
+    for k in ("inside", "y0", "x0"):
+        assert np.array_equal(g[k].cpu().numpy(), ref[k]), k
+    for k in ("lh", "lw"):
+        assert np.array_equal(g[k].cpu().numpy().view(np.uint32), ref[k].view(np.uint32)), k
+
+
+# ------------------------------------------------------------ workloads
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    """Every pages' workload at its full size, in the launch configuration
+    the benchmark times (default plan, 16-byte aligned tensors)."""
+    w = WORKLOADS[name]
+    o = oracle.get()
+    s = shape_of(w)
+    Ho, Wo = o.out_size(s)
+    say(f"workload {w.describe()}")
+    inp = make_inputs(w, Ho, Wo)
+    plan = d4.Plan(desc_of(s, w.dtype))
+    say(f"  plan {plan.info()}")
+    y = gpu_forward(plan, inp, w.dtype)
+    y_or = o.forward_f32(s, w.dtype, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
+    check_against_oracle(y, y_or, w.dtype, name)
+    # the fp64 definition on sampled pixels
+    rng = np.random.default_rng(7)
+    npix = s.N * Ho * Wo
+    pix = np.unique(np.concatenate([rng.integers(0, npix, 3000),
+                                    [0, npix - 1, Wo - 1, npix - Wo]]))
+    y64 = o.forward_f64(s, w.dtype, inp.x, inp.om, inp.scales, pix=pix,
+                        nthreads=NTHREADS)
+    yg = y.reshape(npix, s.C)[pix]
+    if w.dtype == "f32":
+        check_fp32_gate(yg, y64, name)
+    else:
+        fg = from_raw(yg, w.dtype).astype(np.float64)
+        err = np.max(np.abs(fg - y64)) / np.sqrt(np.mean(y64 ** 2))
+        say(f"  {name}: max|y - fp64 definition|/RMS on {pix.size} pixels = {err:.3g} "
+            "(includes the output rounding)")
+    # geometry of the sampled pixels, bit for bit
+    geo = plan.probe_geometry(to_dev(inp.om, w.dtype),
+                              None if inp.scales is None else torch.from_numpy(inp.scales).cuda())
+    torch.cuda.synchronize()
+    ref = o.geometry(s, w.dtype, inp.om, inp.scales, pix=pix)
+    GK = s.G * s.K
+    sel = (pix[:, None] * GK + np.arange(GK)[None, :]).reshape(-1)
+    for k in ("inside", "y0", "x0"):
+        assert np.array_equal(geo[k].cpu().numpy()[sel], ref[k]), k
+    for k in ("lh", "lw"):
+        assert np.array_equal(geo[k].cpu().numpy()[sel].view(np.uint32),
+                              ref[k].view(np.uint32)), k
+
+
+# ------------------------------------------------------------ variants
+@pytest.mark.parametrize("dt, D, dps", [("bf16", 16, (8, 16)), ("f32", 16, (4, 8, 12, 16)),
+                                        ("f16", 32, (8, 16, 24, 32)),
+                                        ("bf16", 72, (8, 24))])
+def test_channels_per_lane_variants_identical(dt, D, dps):
+    s = Shape(2, 23, 37, 2 * D, 2)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=D)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS)
+    for dp in dps:
+        if D % dp:
+            continue
+        say(f"channels per lane {dp}: {s} {dt}")
+        plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp)
+        check_against_oracle(gpu_forward(plan, inp, dt), y_or, dt, f"D'={dp}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_element_path_for_misaligned_tensors(dt):
+    """Tensors that are only element-aligned take the element-wise kernel."""
+    s = Shape(2, 19, 21, 32, 2)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=5)
+    say(f"element path {s} {dt}")
+    plan = d4.Plan(desc_of(s, dt))
+    y = gpu_forward(plan, inp, dt, offset_elems=1)
+    check_against_oracle(y, o.forward_f32(s, dt, inp.x, inp.om, None,
+                                          nthreads=NTHREADS), dt, "element path")
+
+
+def test_nonfinite_values_propagate_like_the_oracle():
+    s = Shape(1, 12, 13, 32, 2)
+    dt = "f32"
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=9)
+    inp.x[0, 3, 4, :] = np.inf
+    inp.x[0, 7, 2, 5] = np.nan
+    inp.x[0, 0, 0, 7] = -np.inf      # a border pixel
+    inp.om[0, 2, 2, 0, 4] = np.nan   # an offset
+    inp.om[0, 5, 6, 1, 20] = np.inf  # a weight
+    inp.om[0, 0, 0, 1, 0] = np.inf   # an offset pushing a sample outside
+    plan = d4.Plan(desc_of(s, dt))
+    say("non-finite values")
+    y = gpu_forward(plan, inp, dt)
+    check_against_oracle(y, o.forward_f32(s, dt, inp.x, inp.om, None), dt, "non-finite")
+
+
+def test_repeatable_and_stream_independent():
+    w = WORKLOADS["dcn4_small_f32"].with_(N=4, H=33, W=29)
+    s = shape_of(w)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = make_inputs(w, Ho, Wo)
+    plan = d4.Plan(desc_of(s, w.dtype))
+    x, om = to_dev(inp.x, "f32"), to_dev(inp.om, "f32")
+    y1 = plan.forward(x, om)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        y2 = plan.forward(x, om)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_empty_batch():
+    plan = d4.Plan(d4.Desc(N=0, H=8, W=8, C=16, group=2, dtype="bf16"))
+    x = torch.empty((0, 8, 8, 16), dtype=torch.bfloat16, device="cuda")
+    om = torch.empty((0, 8, 8, 2, 27), dtype=torch.bfloat16, device="cuda")
+    y = plan.forward(x, om)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 8, 8, 16)
