@@ -67,6 +67,9 @@ def main():
     ap.add_argument("--channels-per-lane", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="instead of the operator, run plain device copies of MIB "
+                         "MiB (the scale reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -79,6 +82,10 @@ def main():
     import torch
     import workloads
     import dynamic_sparse_vision_dcn4_amd as d4
+
+    if args.copy_reference:
+        copy_reference(torch, args.copy_reference, args.steps)
+        return
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
@@ -185,6 +192,19 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, Ho, Wo, host0, args.cpu_reps)
     print(json.dumps(line), flush=True)
+
+
+def copy_reference(torch, mib, steps):
+    """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE
+    and WRITE_SIZE of one such copy dispatch scale the operator's counters."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_read": n * 4, "copy_reference_bytes_written": n * 4,
+                      "steps": steps}), flush=True)
 
 
 def cpu_baseline(w, Ho, Wo, inp, reps):

@@ -53,13 +53,28 @@ class dcn4_desc(ctypes.Structure):
 
 
 class dcn4_launch_info(ctypes.Structure):
-    _fields_ = [("channels_per_lane", ctypes.c_int32),
+    _fields_ = [("kernel", ctypes.c_int32),
+                ("channels_per_lane", ctypes.c_int32),
                 ("vector_bytes", ctypes.c_int32),
                 ("lanes_per_group", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32),
                 ("blocks", ctypes.c_int64),
                 ("launches", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32)]
+                ("lds_bytes", ctypes.c_int32),
+                ("tile_h", ctypes.c_int32),
+                ("tile_w", ctypes.c_int32),
+                ("tile_groups", ctypes.c_int32),
+                ("tile_margin", ctypes.c_int32)]
+
+# dcn4_option
+DCN4_OPT_CHANNELS_PER_LANE = 0
+DCN4_OPT_KERNEL = 1
+DCN4_OPT_TILE_MARGIN = 2
+DCN4_OPT_TILE_GROUPS = 3
+DCN4_OPT_TILE_PAD = 4
+OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
+           "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
+           "tile_pad": DCN4_OPT_TILE_PAD}
 
 
 _P = ctypes.c_void_p
@@ -68,7 +83,7 @@ _lib.dcn4_query.argtypes = [_P, ctypes.POINTER(ctypes.c_int32),
                             ctypes.POINTER(ctypes.c_int32),
                             ctypes.POINTER(ctypes.c_uint64)]
 _lib.dcn4_plan_info.argtypes = [_P, ctypes.POINTER(dcn4_launch_info)]
-_lib.dcn4_plan_set_channels_per_lane.argtypes = [_P, ctypes.c_int32]
+_lib.dcn4_plan_set_option.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
 _lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
 _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_destroy.argtypes = [_P]
@@ -78,7 +93,7 @@ _lib.dcn4_status_string.restype = ctypes.c_char_p
 _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
-           "dcn4_plan_set_channels_per_lane", "dcn4_forward",
+           "dcn4_plan_set_option", "dcn4_forward",
            "dcn4_probe_geometry"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -105,8 +120,8 @@ def dcn4_plan_info(plan) -> Tuple[int, dict]:
     return st, {f: getattr(info, f) for f, _ in dcn4_launch_info._fields_}
 
 
-def dcn4_plan_set_channels_per_lane(plan, channels_per_lane: int) -> int:
-    return _lib.dcn4_plan_set_channels_per_lane(plan, channels_per_lane)
+def dcn4_plan_set_option(plan, option: int, value: int) -> int:
+    return _lib.dcn4_plan_set_option(plan, option, value)
 
 
 def dcn4_forward(plan, x: int, offset_mask: int, group_scales: Optional[int],
@@ -177,16 +192,17 @@ def _torch_dtype(name):
 class Plan:
     """Owns a dcn4_plan; forward() takes torch CUDA tensors."""
 
-    def __init__(self, desc: Desc, channels_per_lane: int = 0):
+    def __init__(self, desc: Desc, channels_per_lane: int = 0, **options):
+        """options: kernel, tile_margin, tile_groups, tile_pad (dcn4_option)."""
         self.desc = desc
         st, h = dcn4_create(desc.c_struct())
         if st != DCN4_OK:
             raise DCN4Error(st, "dcn4_create")
         self._h = h
         if channels_per_lane:
-            st = dcn4_plan_set_channels_per_lane(h, channels_per_lane)
-            if st != DCN4_OK:
-                raise DCN4Error(st, "dcn4_plan_set_channels_per_lane")
+            self.set_option("channels_per_lane", channels_per_lane)
+        for k, v in options.items():
+            self.set_option(k, v)
         st, self.Ho, self.Wo, self.ideal_bytes = dcn4_query(h)
         if st != DCN4_OK:
             raise DCN4Error(st, "dcn4_query")
@@ -201,10 +217,13 @@ class Plan:
             raise DCN4Error(st, "dcn4_plan_info")
         return info
 
-    def set_channels_per_lane(self, dp: int) -> None:
-        st = dcn4_plan_set_channels_per_lane(self._h, dp)
+    def set_option(self, name: str, value: int) -> None:
+        st = dcn4_plan_set_option(self._h, OPTIONS[name], int(value))
         if st != DCN4_OK:
-            raise DCN4Error(st, "dcn4_plan_set_channels_per_lane")
+            raise DCN4Error(st, f"dcn4_plan_set_option({name})")
+
+    def set_channels_per_lane(self, dp: int) -> None:
+        self.set_option("channels_per_lane", dp)
 
     def out_shape(self):
         d = self.desc

@@ -24,6 +24,9 @@ bool aligned_to(const void* p, uintptr_t a) {
 }
 
 constexpr int64_t kCoordLimit = int64_t(1) << 20;
+// Margin of the tiled kernel's LDS window, in pixels around the footprint of
+// the tile's undisplaced sample points: offsets within it gather from LDS.
+constexpr int32_t kDefaultTileMargin = 4;
 
 // Output size of the convolution index arithmetic with padding and dilation.
 int64_t out_size(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
@@ -101,6 +104,11 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
                                         : dcn4::kStdScaled;
   p.dp_default = default_dp(p.D, p.es);
   p.dp = p.dp_default;
+  p.kernel_choice = dcn4::kKernelAuto;
+  p.tile_margin = kDefaultTileMargin;
+  p.tile_groups = 0;
+  p.tile_pad = 1;
+  dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic
   const int64_t pix = Ho * Wo;
@@ -151,11 +159,29 @@ dcn4_status dcn4_query(const dcn4_plan* plan, int32_t* Ho, int32_t* Wo,
 dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
   if (!plan || !info) return fail(DCN4_ERR_NULL, "plan or info is NULL");
   const dcn4::Plan& p = plan->p;
+  *info = dcn4_launch_info{};
   const bool vec = p.dp > 0;
   const int32_t dp = vec ? p.dp : 1;
   info->channels_per_lane = dp;
   info->vector_bytes = vec ? 16 : p.es;
   info->lanes_per_group = p.D / dp;
+  if (vec && p.tile.ok) {
+    const dcn4::TileShape& t = p.tile;
+    const int64_t tiles = int64_t((p.Ho + t.th - 1) / t.th) * ((p.Wo + t.tw - 1) / t.tw);
+    const int64_t per_image = tiles * (p.desc.group / t.gb);
+    const int64_t imgs = (int64_t(1) << 30) / per_image;
+    info->kernel = 2;
+    info->block_threads = dcn4::kBlock;
+    info->blocks = per_image * p.desc.N;
+    info->launches = p.desc.N ? (int32_t)((p.desc.N + imgs - 1) / imgs) : 0;
+    info->lds_bytes = t.lds_bytes;
+    info->tile_h = t.th;
+    info->tile_w = t.tw;
+    info->tile_groups = t.gb;
+    info->tile_margin = t.margin;
+    return DCN4_OK;
+  }
+  info->kernel = 1;
   info->block_threads = dcn4::forward_block(p, p.D / dp);
   int64_t blocks = 0;
   int32_t launches = 0;
@@ -172,20 +198,48 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
   return DCN4_OK;
 }
 
-dcn4_status dcn4_plan_set_channels_per_lane(dcn4_plan* plan, int32_t dp) {
+dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value) {
   if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
-  dcn4::Plan& p = plan->p;
-  if (dp == 0) {
-    p.dp = p.dp_default;
-    return DCN4_OK;
+  dcn4::Plan q = plan->p;  // applied only if the result is valid
+  switch (option) {
+    case DCN4_OPT_CHANNELS_PER_LANE: {
+      if (value == 0) {
+        q.dp = q.dp_default;
+        break;
+      }
+      const int32_t vec = 16 / q.es;
+      if (value < vec || value % vec || value / vec > 4 || q.D % value || (q.D * q.es) % 16)
+        return fail(DCN4_ERR_INVALID_ARG,
+                    "channels_per_lane must be 1-4 vectors of 16 bytes and divide D");
+      if (dcn4::forward_block(q, q.D / value) == 0)
+        return fail(DCN4_ERR_UNSUPPORTED, "offset/weight rows are too large for LDS");
+      q.dp = value;
+      break;
+    }
+    case DCN4_OPT_KERNEL:
+      if (value < 0 || value > 2) return fail(DCN4_ERR_INVALID_ARG, "kernel must be 0, 1 or 2");
+      q.kernel_choice = value;
+      break;
+    case DCN4_OPT_TILE_MARGIN:
+      if (value < 0 || value > 16) return fail(DCN4_ERR_INVALID_ARG, "tile margin must be 0-16");
+      q.tile_margin = value;
+      break;
+    case DCN4_OPT_TILE_GROUPS:
+      if (value < 0 || (value > 0 && q.desc.group % value))
+        return fail(DCN4_ERR_INVALID_ARG, "tile groups must divide G");
+      q.tile_groups = value;
+      break;
+    case DCN4_OPT_TILE_PAD:
+      if (value != 0 && value != 1) return fail(DCN4_ERR_INVALID_ARG, "tile pad must be 0 or 1");
+      q.tile_pad = value;
+      break;
+    default:
+      return fail(DCN4_ERR_INVALID_ARG, "unknown option");
   }
-  const int32_t vec = 16 / p.es;
-  if (dp < vec || dp % vec || dp / vec > 4 || p.D % dp || (p.D * p.es) % 16)
-    return fail(DCN4_ERR_INVALID_ARG,
-                "channels_per_lane must be 1-4 vectors of 16 bytes and divide D");
-  if (dcn4::forward_block(p, p.D / dp) == 0)
-    return fail(DCN4_ERR_UNSUPPORTED, "offset/weight rows are too large for LDS");
-  p.dp = dp;
+  dcn4::resolve_tile(q);
+  if (q.kernel_choice == dcn4::kKernelTiled && !q.tile.ok)
+    return fail(DCN4_ERR_UNSUPPORTED, "the tiled kernel does not apply to this plan");
+  plan->p = q;
   return DCN4_OK;
 }
 
@@ -216,7 +270,10 @@ dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
   if (s != DCN4_OK || p.desc.N == 0) return s;
   const bool vector_path = p.dp > 0 && aligned_to(x, 16) &&
                            aligned_to(offset_mask, 16) && aligned_to(y, 16);
-  s = dcn4::launch_forward(p, x, offset_mask, group_scales, y, stream, vector_path);
+  if (vector_path && p.tile.ok)
+    s = dcn4::launch_tiled(p, x, offset_mask, group_scales, y, stream);
+  else
+    s = dcn4::launch_forward(p, x, offset_mask, group_scales, y, stream, vector_path);
   if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
   return DCN4_OK;
 }

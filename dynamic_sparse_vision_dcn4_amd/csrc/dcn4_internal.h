@@ -57,6 +57,41 @@ struct FwdArgs {
   FastDiv div_ipp, div_L, div_hw, div_wo;
 };
 
+// Arguments of the tiled kernel.  A workgroup owns (image, TH x TW output
+// tile, chunk of GB groups); it stages a zero-padded input window of WH x WW
+// pixels (the tile's sampling footprint plus a margin of M pixels) and the
+// tile's offset/weight rows in LDS.
+struct TileArgs {
+  const char* x;         // input of this launch's first image
+  const char* om;        // offset/weight tensor of this launch's first image
+  const float* scales;
+  char* y;
+  int32_t H, W, C, G, D, Ho, Wo;
+  int32_t kh, kw, sh, sw, ph, pw, dh, dw;
+  float offset_scale, Hm1, Wm1;
+  int32_t L;             // lanes per (pixel, group), D / D'
+  int32_t GB, TH, TW, M; // groups per workgroup, tile, margin
+  int32_t WH, WW;        // window rows, cols
+  int32_t PS;            // LDS bytes per window pixel (GB*D*es, maybe padded)
+  int32_t CB;            // bytes of a pixel's GB groups, GB*D*es
+  int32_t OB;            // offset/weight bytes of a pixel's GB groups
+  int32_t om_unit;       // bytes per offset/weight copy unit (4, or 2)
+  int32_t om_lds;        // byte offset of the offset/weight area in LDS
+  int32_t tiles_x, tiles_y, chunks, nblocks, block;
+  uint32_t img_bytes;    // H*W*C*es
+  uint32_t om_img_bytes; // Ho*Wo*G*3K*es
+  uint32_t om_row_bytes; // G*3K*es
+  FastDiv div_chunks, div_tx, div_ty, div_cbv, div_ww, div_gbl, div_L, div_tw,
+      div_obu;
+};
+
+// Tile shape a plan resolved (ok == 0: the tiled kernel does not apply).
+struct TileShape {
+  int32_t ok, gb, th, tw, margin, wh, ww, ps, cb, ob, om_unit, lds_bytes;
+};
+
+enum KernelChoice : int32_t { kKernelAuto = 0, kKernelDirect = 1, kKernelTiled = 2 };
+
 struct Plan {
   dcn4_desc desc;
   int32_t Ho, Wo, D, K, es;
@@ -65,13 +100,21 @@ struct Plan {
   int32_t dp_default;
   uint64_t ideal_bytes;
   int32_t images_per_launch;  // bounds the per-launch lane count below 2^31
+  // options (dcn4_plan_set_option) and the tile shape they resolve to
+  int32_t kernel_choice, tile_margin, tile_groups, tile_pad;
+  TileShape tile;
 };
+
+// Resolves p.tile from the plan's options (the tiled kernel's shape).
+void resolve_tile(Plan& p);
 
 // Kernel-side entry points (dcn4_kernels.hip).  Arguments are validated by
 // the caller; these only shape and enqueue the launches.
 dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
                            const float* scales, void* y, void* stream,
                            bool vector_path);
+dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
+                         const float* scales, void* y, void* stream);
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
                          int32_t* y0, int32_t* x0, float* lh, float* lw,
                          uint8_t* inside, void* stream);

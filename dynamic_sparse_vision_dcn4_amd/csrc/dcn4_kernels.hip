@@ -57,6 +57,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            (int)bytes, kRsrcWord3);
 }
 
+// Global -> LDS copy without a register round trip: lane i of the wave writes
+// its `bytes` (16 or 4) at lds_wave + i*bytes, so a wave fills one contiguous
+// run; every load of a copy loop is in flight at once.  An out-of-range
+// offset writes zeros.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void copy16_to_lds(rsrc_t r, char* lds_wave, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 16, (int)off, 0, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(rsrc_t r, char* lds_wave, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 4, (int)off, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
@@ -130,6 +142,7 @@ __device__ __forceinline__ Loc sample_location(float by, float bx, float gy,
 
 struct Cell {
   int y0, x0;
+  float yf, xf;  // integer parts as exact floats (compared before converting)
   float lh, lw;
   bool inside;
 };
@@ -142,6 +155,8 @@ __device__ __forceinline__ Cell locate(Loc l, float Hm1, float Wm1) {
   const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
   const float yf = l.by + fy, xf = l.bx + fx;  // exact while inside
   c.inside = (yf >= -1.0f) && (yf <= Hm1) && (xf >= -1.0f) && (xf <= Wm1);
+  c.yf = yf;
+  c.xf = xf;
   c.y0 = (int)yf;
   c.x0 = (int)xf;
   c.lh = l.ty - fy;
@@ -290,8 +305,12 @@ void dcn4_forward_kernel(FwdArgs a) {
   {
     const rsrc_t r = make_rsrc(aligned, (len + 3u) & ~3u);
     const uint32_t nvec = (len + 15u) >> 4;
-    for (uint32_t v = threadIdx.x; v < nvec; v += (uint32_t)a.block)
-      lds_rows[v] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(v << 4), 0, 0);
+    const uint32_t lane = threadIdx.x & 63u;
+    for (uint32_t base = threadIdx.x & ~63u; base < nvec; base += (uint32_t)a.block) {
+      const uint32_t v = base + lane;
+      if (v < nvec)
+        copy16_to_lds(r, reinterpret_cast<char*>(lds_rows) + base * 16u, v << 4);
+    }
   }
   __syncthreads();
 
@@ -383,6 +402,199 @@ void dcn4_forward_kernel(FwdArgs a) {
     typedef typename io::raw R;
 #pragma unroll
     for (int e = 0; e < DP; ++e) reinterpret_cast<R*>(yp)[e] = io::enc(acc[e]);
+  }
+}
+
+
+// ------------------------------------------------------------ tiled kernel
+// Gathers from an LDS copy of the input instead of from global memory.  On
+// MI355X divergent 16-byte global gathers that miss L1 run at about 0.4 cache
+// lines per clock per CU, while random 16-byte LDS reads run at about 4.5
+// lanes per clock per CU: the workgroup therefore copies, with coalesced
+// 128-bit loads, the zero-padded input window its tile can sample (tile
+// footprint plus a margin of M pixels on every side) for its chunk of GB
+// groups, and the tile's offset/weight rows.  A point whose four corners lie
+// in the window is gathered from LDS -- corners outside the image read the
+// staged zeros, and fma(c, 0, acc) == acc for a finite coefficient.  When any
+// lane of a wave has a point outside the window, or a non-finite weight, the
+// whole wave takes the global path of the direct kernel for that point.  Both
+// paths perform the same operations on the same values, so the result does
+// not depend on which path ran.
+template <int DT, int VEC, int NV> struct LdsTap {
+  u32x4 v[4][NV];
+  __device__ __forceinline__ void load(const char* base, uint32_t addr,
+                                       uint32_t dx1, uint32_t dy1) {
+    const uint32_t off[4] = {0u, dx1, dy1, dy1 + dx1};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        v[q][n] = *reinterpret_cast<const u32x4*>(base + addr + off[q] + 16 * n);
+  }
+  __device__ __forceinline__ void accumulate(float* acc, const float* c) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[n * VEC + e] = __builtin_fmaf(c[q], Io<DT>::lane(v[q][n], e), acc[n * VEC + e]);
+  }
+};
+
+template <int DT, int VEC, int NV, int MODE, int KS>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
+void dcn4_tile_kernel(TileArgs a) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  constexpr int DP = VEC * NV;
+  extern __shared__ u32x4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+
+  // ---- workgroup -> (image, tile row, tile col, group chunk); the group
+  // chunk varies fastest so the chunks of one tile run back to back on one XCD
+  const uint32_t lb = (uint32_t)xcd_block(blockIdx.x, a.nblocks);
+  uint32_t q = fastdiv(lb, a.div_chunks);
+  const uint32_t gc = lb - q * (uint32_t)a.chunks;
+  uint32_t q2 = fastdiv(q, a.div_tx);
+  const uint32_t tx = q - q2 * (uint32_t)a.tiles_x;
+  const uint32_t n = fastdiv(q2, a.div_ty);
+  const uint32_t ty = q2 - n * (uint32_t)a.tiles_y;
+  const int ty0 = (int)ty * a.TH, tx0 = (int)tx * a.TW;
+  const int wy0 = ty0 * a.sh - a.ph - a.M, wx0 = tx0 * a.sw - a.pw - a.M;
+  const uint32_t g0 = gc * (uint32_t)a.GB;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+
+  // ---- stage the input window (zeros outside the image).  A window pixel
+  // is PS bytes in LDS: its GB groups' channels, then (when padded) one
+  // 16-byte chunk loaded as zeros, so the copy stays one contiguous run.
+  const rsrc_t xr = make_rsrc(a.x + (uint64_t)n * a.img_bytes, a.img_bytes);
+  const uint32_t lane = threadIdx.x & 63u;
+  {
+    const uint32_t cvec = (uint32_t)a.PS >> 4, dvec = (uint32_t)a.CB >> 4;
+    const uint32_t nvec = (uint32_t)(a.WH * a.WW) * cvec;
+    const uint32_t chan0 = g0 * (uint32_t)a.D * es;
+    for (uint32_t base = threadIdx.x & ~63u; base < nvec; base += (uint32_t)a.block) {
+      const uint32_t v = base + lane;
+      const uint32_t pix = fastdiv(v, a.div_cbv), ch = v - pix * cvec;
+      const uint32_t r = fastdiv(pix, a.div_ww), c = pix - r * (uint32_t)a.WW;
+      const int row = wy0 + (int)r, col = wx0 + (int)c;
+      const bool in = ch < dvec && (uint32_t)row < (uint32_t)a.H && (uint32_t)col < (uint32_t)a.W;
+      const uint32_t off = in ? (uint32_t)__mul24(__mul24(row, a.W) + col, a.C * es) + chan0 + ch * 16u
+                              : kOutside;
+      if (v < nvec) copy16_to_lds(xr, lds + base * 16u, off);
+    }
+  }
+  // ---- stage the tile's offset/weight rows (GB groups per pixel)
+  const rsrc_t omr = make_rsrc(a.om + (uint64_t)n * a.om_img_bytes, a.om_img_bytes);
+  {
+    const uint32_t upp = (uint32_t)(a.OB / a.om_unit);
+    const uint32_t nunits = (uint32_t)(a.TH * a.TW) * upp;
+    const uint32_t grp0 = g0 * (uint32_t)(3 * K * es);
+    for (uint32_t base = threadIdx.x & ~63u; base < nunits; base += (uint32_t)a.block) {
+      const uint32_t u = base + lane;
+      const uint32_t tp = fastdiv(u, a.div_obu), e = u - tp * upp;
+      const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
+      const int yo = ty0 + (int)py, xo = tx0 + (int)px;
+      const bool in = yo < a.Ho && xo < a.Wo;
+      const uint32_t off = in ? (uint32_t)(yo * a.Wo + xo) * a.om_row_bytes + grp0 +
+                                    e * (uint32_t)a.om_unit
+                              : kOutside;
+      if (u < nunits) {
+        if (a.om_unit == 4) {
+          copy4_to_lds(omr, lds + a.om_lds + base * 4u, off);
+        } else {
+          *reinterpret_cast<uint16_t*>(lds + a.om_lds + 2u * u) =
+              __builtin_amdgcn_raw_buffer_load_b16(omr, (int)off, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- lane -> (tile pixel, group in chunk, channel slice)
+  const uint32_t tp = fastdiv((uint32_t)threadIdx.x, a.div_gbl);
+  const uint32_t rr = (uint32_t)threadIdx.x - tp * (uint32_t)(a.GB * a.L);
+  const uint32_t gl = fastdiv(rr, a.div_L), l = rr - gl * (uint32_t)a.L;
+  const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
+  const int yo = ty0 + (int)py, xo = tx0 + (int)px;
+  if ((int)tp >= a.TH * a.TW || yo >= a.Ho || xo >= a.Wo) return;
+  const uint32_t g = g0 + gl;
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
+      lds + a.om_lds + (tp * (uint32_t)a.GB + gl) * (uint32_t)(3 * K * es));
+
+  LaneCtx t;
+  t.pix_bytes = (uint32_t)a.C * es;
+  t.row_stride = (uint32_t)a.W * t.pix_bytes;
+  t.lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
+  t.sg = 1.0f;
+  t.hy = ((KS ? KS : a.kh) - 1) >> 1;
+  t.hx = ((KS ? KS : a.kw) - 1) >> 1;
+  t.by0 = yo * a.sh - a.ph;
+  t.bx0 = xo * a.sw - a.pw;
+  // the geometry reads only the fields FwdArgs and TileArgs share
+  FwdArgs fa{};
+  fa.H = a.H; fa.W = a.W; fa.kh = a.kh; fa.kw = a.kw; fa.dh = a.dh; fa.dw = a.dw;
+  fa.offset_scale = a.offset_scale; fa.Hm1 = a.Hm1; fa.Wm1 = a.Wm1;
+
+  // window bounds for the corner (y0, x0): y0 in [wy0, wy0 + WH - 2]
+  const float wy_lo = (float)wy0, wy_hi = (float)(wy0 + a.WH - 2);
+  const float wx_lo = (float)wx0, wx_hi = (float)(wx0 + a.WW - 2);
+  const uint32_t lane_lds = (gl * (uint32_t)a.D + l * DP) * es;
+  const uint32_t dy1 = (uint32_t)(a.WW * a.PS);
+
+  float acc[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
+
+  const int kw = KS ? KS : a.kw;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const int i = k / kw, j = k - (k / kw) * kw;
+    const float dx = io::dec(om[2 * k]);
+    const float dy = io::dec(om[2 * k + 1]);
+    const float m = io::dec(om[2 * K + k]);
+    const float by = (float)(t.by0 + i * a.dh), bx = (float)(t.bx0 + j * a.dw);
+    const Cell c = locate(sample_location<MODE>(by, bx, 0.0f, 0.0f, dy, dx,
+                                                a.offset_scale, 1.0f),
+                          a.Hm1, a.Wm1);
+    const bool ok = (c.yf >= wy_lo) && (c.yf <= wy_hi) && (c.xf >= wx_lo) &&
+                    (c.xf <= wx_hi) && __builtin_isfinite(m);
+    if (__ballot(!ok) == 0) {
+      const float hh = 1.0f - c.lh, hw = 1.0f - c.lw;
+      const float cf[4] = {m * (hh * hw), m * (hh * c.lw), m * (c.lh * hw),
+                           m * (c.lh * c.lw)};
+      const uint32_t addr = lane_lds +
+          (uint32_t)__mul24(__mul24(c.y0 - wy0, a.WW) + (c.x0 - wx0), a.PS);
+      LdsTap<DT, VEC, NV> d;
+      d.load(lds, addr, (uint32_t)a.PS, dy1);
+      d.accumulate(acc, cf);
+    } else {
+      const Tap tg = tap_geometry<DT, MODE, KS>(fa, t, om, k);
+      TapData<DT, VEC, NV> d;
+      d.load(xr, tg);
+      d.accumulate(acc, tg);
+    }
+  }
+
+#pragma unroll
+  for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
+  char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * (uint32_t)(a.C * es) +
+             (g * (uint32_t)a.D + l * DP) * es;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    u32x4 w;
+    if (es == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(acc[v * VEC + e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)io::enc(acc[v * VEC + 2 * e]) |
+               ((uint32_t)io::enc(acc[v * VEC + 2 * e + 1]) << 16);
+    }
+    *reinterpret_cast<u32x4*>(yp + 16 * v) = w;
   }
 }
 
@@ -484,6 +696,33 @@ void fill_common(const Plan& p, FwdArgs& a) {
   a.div_wo = make_fastdiv((uint32_t)p.Wo);
 }
 
+
+typedef void (*tile_fn)(TileArgs);
+
+template <int DT, int NV, int MODE>
+tile_fn tile_ks(int K3) {
+  constexpr int V = 16 / Io<DT>::es;
+  return K3 ? dcn4_tile_kernel<DT, V, NV, MODE, 3> : dcn4_tile_kernel<DT, V, NV, MODE, 0>;
+}
+
+template <int DT>
+tile_fn tile_pick(int nv, int mode, int K3) {
+  if (mode == kStdScaled) {
+    switch (nv) {
+      case 1: return tile_ks<DT, 1, kStdScaled>(K3);
+      case 2: return tile_ks<DT, 2, kStdScaled>(K3);
+      case 3: return tile_ks<DT, 3, kStdScaled>(K3);
+      default: return tile_ks<DT, 4, kStdScaled>(K3);
+    }
+  }
+  switch (nv) {
+    case 1: return tile_ks<DT, 1, kStdUnitScale>(K3);
+    case 2: return tile_ks<DT, 2, kStdUnitScale>(K3);
+    case 3: return tile_ks<DT, 3, kStdUnitScale>(K3);
+    default: return tile_ks<DT, 4, kStdUnitScale>(K3);
+  }
+}
+
 }  // namespace
 
 thread_local char g_hip_error[128] = "";
@@ -541,6 +780,104 @@ dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
     a.block = block;
     a.nblocks = (a.total_items + block - 1) / block;
     hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(block), lds,
+                       static_cast<hipStream_t>(stream), a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  return DCN4_OK;
+}
+
+void resolve_tile(Plan& p) {
+  TileShape t{};
+  const dcn4_desc& d = p.desc;
+  p.tile = t;
+  if (p.mode == kGroupScale || p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
+  const int32_t L = p.D / p.dp;
+  // groups per workgroup: the smallest divisor of G whose channels fill at
+  // least 64 bytes of a pixel (half a cache line), unless given
+  int32_t gb = p.tile_groups;
+  if (gb <= 0) {
+    gb = d.group;
+    for (int32_t c = 1; c <= d.group; ++c)
+      if (d.group % c == 0 && c * p.D * p.es >= 64) { gb = c; break; }
+  }
+  if (gb < 1 || d.group % gb) return;
+  const int32_t lanes_px = gb * L;
+  if (lanes_px > kBlock || kBlock % lanes_px) return;
+  const int32_t tp = kBlock / lanes_px;      // tile pixels
+  int32_t tw = tp >= 16 ? 16 : tp, th = tp / tw;
+  if (tp == 64) { th = 8; tw = 8; }
+  const int32_t M = p.tile_margin;
+  const int32_t wh = (th - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
+  const int32_t ww = (tw - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 2;
+  const int32_t cb = gb * p.D * p.es;
+  if (cb % 16) return;
+  int32_t ps = cb;
+  if (p.tile_pad && ((ps / 16) % 2 == 0)) ps += 16;  // odd number of 16-byte chunks
+  const int32_t ob = gb * 3 * p.K * p.es;
+  const int32_t row = d.group * 3 * p.K * p.es;
+  const int32_t unit = (p.es == 4 || (ob % 4 == 0 && row % 4 == 0)) ? 4 : 2;
+  const int64_t win = (int64_t)wh * ww * ps;
+  const int64_t lds = ((win + 15) & ~int64_t(15)) + (((int64_t)tp * ob + 15) & ~int64_t(15));
+  if (lds > 64 * 1024) return;
+  t.ok = 1;
+  t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww; t.ps = ps;
+  t.cb = cb; t.ob = ob; t.om_unit = unit; t.lds_bytes = (int32_t)lds;
+  p.tile = t;
+}
+
+dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
+                         const float* scales, void* y, void* stream) {
+  const dcn4_desc& d = p.desc;
+  const TileShape& ts = p.tile;
+  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  const int nv = p.dp / (16 / p.es);
+  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3)
+             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3)
+                                    : tile_pick<DCN4_F16>(nv, p.mode, K3);
+  TileArgs a{};
+  a.scales = scales;
+  a.H = d.H; a.W = d.W; a.C = d.C; a.G = d.group; a.D = p.D; a.Ho = p.Ho; a.Wo = p.Wo;
+  a.kh = d.kernel_h; a.kw = d.kernel_w; a.sh = d.stride_h; a.sw = d.stride_w;
+  a.ph = d.pad_h; a.pw = d.pad_w; a.dh = d.dilation_h; a.dw = d.dilation_w;
+  a.offset_scale = d.offset_scale;
+  a.Hm1 = (float)(d.H - 1);
+  a.Wm1 = (float)(d.W - 1);
+  a.L = p.D / p.dp;
+  a.GB = ts.gb; a.TH = ts.th; a.TW = ts.tw; a.M = ts.margin;
+  a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb; a.OB = ts.ob;
+  a.om_unit = ts.om_unit;
+  a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
+  a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
+  a.tiles_y = (p.Ho + ts.th - 1) / ts.th;
+  a.chunks = d.group / ts.gb;
+  a.block = kBlock;
+  a.img_bytes = (uint32_t)((uint64_t)d.H * d.W * d.C * p.es);
+  a.om_row_bytes = (uint32_t)(d.group * 3 * p.K * p.es);
+  a.om_img_bytes = (uint32_t)((uint64_t)p.Ho * p.Wo * a.om_row_bytes);
+  a.div_chunks = make_fastdiv((uint32_t)a.chunks);
+  a.div_tx = make_fastdiv((uint32_t)a.tiles_x);
+  a.div_ty = make_fastdiv((uint32_t)a.tiles_y);
+  a.div_cbv = make_fastdiv((uint32_t)(ts.ps / 16));
+  a.div_ww = make_fastdiv((uint32_t)ts.ww);
+  a.div_gbl = make_fastdiv((uint32_t)(ts.gb * a.L));
+  a.div_L = make_fastdiv((uint32_t)a.L);
+  a.div_tw = make_fastdiv((uint32_t)ts.tw);
+  a.div_obu = make_fastdiv((uint32_t)(ts.ob / ts.om_unit));
+  const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const int64_t per_image = (int64_t)a.tiles_x * a.tiles_y * a.chunks;
+  const int32_t imgs = (int32_t)((int64_t(1) << 30) / per_image);
+  for (int32_t n0 = 0; n0 < d.N; n0 += imgs) {
+    const int32_t nb = (d.N - n0) < imgs ? (d.N - n0) : imgs;
+    a.x = static_cast<const char*>(x) + n0 * x_img;
+    a.om = static_cast<const char*>(om) + n0 * om_img;
+    a.y = static_cast<char*>(y) + n0 * y_img;
+    a.nblocks = (int32_t)(nb * per_image);
+    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.lds_bytes,
                        static_cast<hipStream_t>(stream), a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

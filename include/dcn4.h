@@ -119,6 +119,7 @@ dcn4_status dcn4_query(const dcn4_plan* plan, int32_t* Ho, int32_t* Wo,
 
 /* Launch shape the plan chose (for tests, tuning and reports). */
 typedef struct {
+  int32_t kernel;            /* 1: direct gather kernel, 2: tiled kernel    */
   int32_t channels_per_lane; /* D' -- channels one lane owns                */
   int32_t vector_bytes;      /* bytes per load/store instruction (16 or es) */
   int32_t lanes_per_group;   /* D / D'                                      */
@@ -126,19 +127,37 @@ typedef struct {
   int64_t blocks;            /* workgroups over all launches                */
   int32_t launches;          /* kernel launches per forward call            */
   int32_t lds_bytes;         /* dynamic LDS per workgroup                   */
+  int32_t tile_h, tile_w;    /* tiled kernel: output tile                   */
+  int32_t tile_groups;       /* tiled kernel: groups per workgroup          */
+  int32_t tile_margin;       /* tiled kernel: window margin in pixels       */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
  * Errors: DCN4_ERR_NULL. */
 dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info);
 
-/* Overrides the channels each lane owns (D' = channels_per_lane; 0 restores
- * the default).  D' must be a multiple of the 16-byte vector width (4 fp32 or
- * 8 half-precision values), divide D, and be at most 4 vectors; the result is
- * bit-identical for every valid choice.  Errors: DCN4_ERR_NULL,
- * DCN4_ERR_INVALID_ARG.  Not safe while another thread uses the plan. */
-dcn4_status dcn4_plan_set_channels_per_lane(dcn4_plan* plan,
-                                            int32_t channels_per_lane);
+/* Tuning options of a plan.  Every valid setting computes the identical
+ * result; they change only how the work is mapped to the GPU. */
+typedef enum {
+  /* D': channels one lane owns, 1-4 vectors of 16 bytes dividing D; 0 = default */
+  DCN4_OPT_CHANNELS_PER_LANE = 0,
+  /* 0 = automatic, 1 = direct gather kernel, 2 = tiled kernel (LDS window) */
+  DCN4_OPT_KERNEL = 1,
+  /* tiled kernel: pixels of margin around the tile's footprint, 0-16 */
+  DCN4_OPT_TILE_MARGIN = 2,
+  /* tiled kernel: groups per workgroup (a divisor of G); 0 = automatic */
+  DCN4_OPT_TILE_GROUPS = 3,
+  /* tiled kernel: 1 = pad each LDS window pixel to an odd number of 16-byte
+   * chunks (fewer bank conflicts), 0 = no padding */
+  DCN4_OPT_TILE_PAD = 4
+} dcn4_option;
+
+/* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,
+ * DCN4_ERR_INVALID_ARG (unknown option or value out of range),
+ * DCN4_ERR_UNSUPPORTED (the tiled kernel was requested but does not apply to
+ * this plan: group-scale mode, groups that are not 16-byte multiples, or a
+ * window too large for LDS).  Not safe while another thread uses the plan. */
+dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value);
 
 /* Enqueues the forward pass y = DCNv4(x, offset_mask[, group_scales]) on
  * `stream`.  group_scales must be non-NULL exactly when the plan uses group

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
               "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
-              "dcn4_plan_info", "dcn4_plan_set_channels_per_lane"):
+              "dcn4_plan_info", "dcn4_plan_set_option"):
         assert n in names
 
 
@@ -127,9 +127,55 @@ def test_query_matches_oracle(s, dt):
 def test_headline_plan_shape():
     p = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
     info = p.info()
-    # a lane owns a whole 16-channel group, two 128-bit loads per corner
+    # a lane owns a whole 16-channel group, two 128-bit loads per corner; the
+    # tiled kernel runs 8x16 output tiles of 2 groups with an LDS window
     assert info["channels_per_lane"] == 16 and info["vector_bytes"] == 16
-    assert info["blocks"] == 8 * 128 * 128 * 20 // 256
+    assert info["kernel"] == 2
+    assert (info["tile_h"], info["tile_w"], info["tile_groups"]) == (8, 16, 2)
+    assert info["blocks"] == 8 * (128 // 8) * (128 // 16) * (20 // 2)
+    assert info["lds_bytes"] <= 64 * 1024
+    p.set_option("kernel", 1)
+    info = p.info()
+    assert info["kernel"] == 1 and info["blocks"] == 8 * 128 * 128 * 20 // 256
+
+
+def test_plan_options():
+    p = d4.Plan(desc_of(Shape(2, 20, 24, 64, 4), "bf16"))
+    assert p.info()["kernel"] == 2
+    for m in (0, 3, 5):
+        p.set_option("tile_margin", m)
+        assert p.info()["tile_margin"] == m
+    for bad in (("tile_margin", -1), ("tile_margin", 17), ("tile_groups", 3),
+                ("kernel", 3), ("tile_pad", 2)):
+        with pytest.raises(d4.DCN4Error) as e:
+            p.set_option(*bad)
+        assert e.value.status == d4.DCN4_ERR_INVALID_ARG
+    assert d4.dcn4_plan_set_option(p.handle, 99, 0) == d4.DCN4_ERR_INVALID_ARG
+    # a rejected option leaves the plan as it was
+    assert p.info()["tile_margin"] == 5
+    p.set_option("tile_margin", 3)
+    p.set_option("tile_groups", 4)
+    assert p.info()["tile_groups"] == 4 and p.info()["tile_h"] * p.info()["tile_w"] == 64
+    # a margin whose window exceeds 64 KiB of LDS: automatic choice falls back
+    # to the direct kernel; a forced tiled kernel refuses it
+    p.set_option("tile_groups", 0)
+    p.set_option("tile_margin", 12)
+    assert p.info()["kernel"] == 1
+    p.set_option("tile_margin", 4)
+    p.set_option("kernel", 2)
+    with pytest.raises(d4.DCN4Error) as e:
+        p.set_option("tile_margin", 12)
+    assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
+    assert p.info()["tile_margin"] == 4
+    # group-scale plans have no tiled kernel
+    ms = d4.Plan(desc_of(Shape(2, 10, 10, 64, 4, multiscale=True), "bf16"))
+    assert ms.info()["kernel"] == 1
+    with pytest.raises(d4.DCN4Error) as e:
+        ms.set_option("kernel", 2)
+    assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
+    # a window too large for LDS falls back to the direct kernel
+    big = d4.Plan(desc_of(Shape(1, 64, 64, 64, 1), "f32"))
+    assert big.info()["kernel"] == 1
 
 
 def test_channels_per_lane_override():
@@ -151,9 +197,14 @@ def test_element_path_plan_when_group_is_not_vector_wide():
 
 
 def test_many_images_split_into_launches():
-    # lanes per launch stay below 2^31: 2^31 / (64*64*1024) = 512 images
-    p = d4.Plan(d4.Desc(N=2000, H=64, W=64, C=1024, group=64, dtype="bf16"))
+    # direct kernel: lanes per launch stay below 2^31, 2^31 / (64*64*1024) =
+    # 512 images per launch
+    p = d4.Plan(d4.Desc(N=2000, H=64, W=64, C=1024, group=64, dtype="bf16"), kernel=1)
     assert p.info()["launches"] == 4
+    # tiled kernel: workgroups per launch stay below 2^30
+    p.set_option("kernel", 0)
+    info = p.info()
+    assert info["kernel"] == 2 and info["launches"] == 1
 
 
 class TestForwardValidation:

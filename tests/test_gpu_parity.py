@@ -155,13 +155,14 @@ def fuzz_inputs(s, dt, Ho, Wo, seed):
     return workloads.Inputs(workloads.to_raw(x, dt), workloads.to_raw(om, dt), scales)
 
 
+@pytest.mark.parametrize("kernel", [0, 1], ids=["auto", "direct"])
 @pytest.mark.parametrize("t, s, dt", fuzz_cases(), ids=lambda v: str(v) if isinstance(v, int) else None)
-def test_fuzz_parity(t, s, dt):
+def test_fuzz_parity(t, s, dt, kernel):
     o = oracle.get()
     Ho, Wo = o.out_size(s)
     inp = fuzz_inputs(s, dt, Ho, Wo, seed=t)
-    say(f"fuzz case {t}: {s} {dt}")
-    plan = d4.Plan(desc_of(s, dt))
+    plan = d4.Plan(desc_of(s, dt), kernel=kernel)
+    say(f"fuzz case {t}: {s} {dt} kernel {plan.info()['kernel']}")
     assert (plan.Ho, plan.Wo) == (Ho, Wo)
     y = gpu_forward(plan, inp, dt)
     y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
@@ -185,7 +186,8 @@ def test_fuzz_parity(t, s, dt):
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_full_size(name):
     """Every pages' workload at its full size, in the launch configuration
-    the benchmark times (default plan, 16-byte aligned tensors)."""
+    the benchmark times (default plan, 16-byte aligned tensors), and with the
+    direct kernel forced."""
     w = WORKLOADS[name]
     o = oracle.get()
     s = shape_of(w)
@@ -197,6 +199,10 @@ def test_workload_full_size(name):
     y = gpu_forward(plan, inp, w.dtype)
     y_or = o.forward_f32(s, w.dtype, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
     check_against_oracle(y, y_or, w.dtype, name)
+    if plan.info()["kernel"] != 1:
+        direct = d4.Plan(desc_of(s, w.dtype), kernel=1)
+        check_against_oracle(gpu_forward(direct, inp, w.dtype), y_or, w.dtype,
+                             name + " (direct kernel)")
     # the fp64 definition on sampled pixels
     rng = np.random.default_rng(7)
     npix = s.N * Ho * Wo
@@ -227,6 +233,43 @@ def test_workload_full_size(name):
 
 
 # ------------------------------------------------------------ variants
+@pytest.mark.parametrize("margin", [0, 1, 2, 3, 5])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_tiled_kernel_margins(dt, margin):
+    """The tiled kernel gathers from LDS when a point's corners are in its
+    window and falls back to global gathers for the wave otherwise; a small
+    margin exercises the fallback on most points, a large one none.  Ragged
+    tiles (H, W not multiples of the tile) and zero padding included."""
+    w = WORKLOADS["ldm_unet_block_bf16"].with_(N=2, H=37, W=45, C=64, G=4, dtype=dt)
+    s = shape_of(w)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = make_inputs(w, Ho, Wo)
+    # fp32 lanes own 8 channels here so that the window fits in LDS
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=8 if dt == "f32" else 0,
+                   kernel=2, tile_margin=margin)
+    say(f"tiled margin {margin} {dt}: {plan.info()}")
+    y = gpu_forward(plan, inp, dt)
+    check_against_oracle(y, o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS),
+                         dt, f"tiled margin {margin}")
+
+
+@pytest.mark.parametrize("groups, pad", [(1, 0), (2, 1), (4, 0), (4, 1)])
+def test_tiled_kernel_group_chunks(groups, pad):
+    w = WORKLOADS["ldm_unet_block_bf16"].with_(N=1, H=29, W=33, C=128, G=8)
+    s = shape_of(w)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = make_inputs(w, Ho, Wo)
+    plan = d4.Plan(desc_of(s, "bf16"), tile_margin=3, kernel=2, tile_groups=groups,
+                   tile_pad=pad)
+    say(f"tiled groups {groups} pad {pad}: {plan.info()}")
+    check_against_oracle(gpu_forward(plan, inp, "bf16"),
+                         o.forward_f32(s, "bf16", inp.x, inp.om, None, nthreads=NTHREADS),
+                         "bf16", f"tiled groups {groups}")
+
+
+
 @pytest.mark.parametrize("dt, D, dps", [("bf16", 16, (8, 16)), ("f32", 16, (4, 8, 12, 16)),
                                         ("f16", 32, (8, 16, 24, 32)),
                                         ("bf16", 72, (8, 24))])
