@@ -65,6 +65,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated across steps (default: enough for 1 GiB)")
     ap.add_argument("--channels-per-lane", type=int, default=0)
+    ap.add_argument("--option", action="append", default=[], metavar="NAME=VALUE",
+                    help="plan option (kernel, tile_margin, tile_groups, tile_pad)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
@@ -91,7 +93,8 @@ def main():
     w = workloads.WORKLOADS[name]
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype)
-    plan = d4.Plan(desc, channels_per_lane=args.channels_per_lane)
+    opts = {k: int(v) for k, v in (o.split("=", 1) for o in args.option)}
+    plan = d4.Plan(desc, channels_per_lane=args.channels_per_lane, **opts)
     Ho, Wo = plan.Ho, plan.Wo
     ideal = plan.ideal_bytes
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
@@ -173,7 +176,7 @@ def main():
                    "pad": [w.ph, w.pw], "dilation": [w.dh, w.dw],
                    "group_scales": w.multiscale, "Ho": Ho, "Wo": Wo,
                    "ideal_bytes": ideal, "input_sets": nsets,
-                   "channels_per_lane": plan.info()["channels_per_lane"]},
+                   "plan": plan.info()},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "output_pixels_per_s": round(out_pix / (ms_per_step * 1e-3), 1),
         "outputs_per_s": round(out_pix * w.C / (ms_per_step * 1e-3), 1),

@@ -107,7 +107,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.kernel_choice = dcn4::kKernelAuto;
   p.tile_margin = kDefaultTileMargin;
   p.tile_groups = 0;
-  p.tile_pad = 1;
+  p.tile_pad = 0;
   dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic

@@ -469,45 +469,67 @@ void dcn4_tile_kernel(TileArgs a) {
   // ---- stage the input window (zeros outside the image).  A window pixel
   // is PS bytes in LDS: its GB groups' channels, then (when padded) one
   // 16-byte chunk loaded as zeros, so the copy stays one contiguous run.
+  // Thread t copies chunk j = t % cvec of window pixels t / cvec + i * ppp
+  // (ppp = 256 / cvec pixels per pass), stepping row and column
+  // incrementally; lane order equals LDS order, as the copy requires.
   const rsrc_t xr = make_rsrc(a.x + (uint64_t)n * a.img_bytes, a.img_bytes);
   const uint32_t lane = threadIdx.x & 63u;
   {
     const uint32_t cvec = (uint32_t)a.PS >> 4, dvec = (uint32_t)a.CB >> 4;
-    const uint32_t nvec = (uint32_t)(a.WH * a.WW) * cvec;
-    const uint32_t chan0 = g0 * (uint32_t)a.D * es;
-    for (uint32_t base = threadIdx.x & ~63u; base < nvec; base += (uint32_t)a.block) {
-      const uint32_t v = base + lane;
-      const uint32_t pix = fastdiv(v, a.div_cbv), ch = v - pix * cvec;
-      const uint32_t r = fastdiv(pix, a.div_ww), c = pix - r * (uint32_t)a.WW;
+    const uint32_t ppp = (uint32_t)a.block / cvec;        // pixels per pass
+    const uint32_t used = ppp * cvec;                     // threads that copy
+    const uint32_t npix = (uint32_t)(a.WH * a.WW);
+    const uint32_t t = threadIdx.x;
+    const uint32_t pix0 = fastdiv(t, a.div_cbv), ch = t - pix0 * cvec;
+    const uint32_t step_r = fastdiv(ppp, a.div_ww), step_c = ppp - step_r * (uint32_t)a.WW;
+    uint32_t r = fastdiv(pix0, a.div_ww), c = pix0 - r * (uint32_t)a.WW;
+    const uint32_t pix_bytes = (uint32_t)(a.C * es);
+    const uint32_t chan = g0 * (uint32_t)a.D * es + ch * 16u;
+    const bool data = ch < dvec;
+    for (uint32_t pix = pix0, slot = t; pix - pix0 < npix; pix += ppp, slot += used) {
       const int row = wy0 + (int)r, col = wx0 + (int)c;
-      const bool in = ch < dvec && (uint32_t)row < (uint32_t)a.H && (uint32_t)col < (uint32_t)a.W;
-      const uint32_t off = in ? (uint32_t)__mul24(__mul24(row, a.W) + col, a.C * es) + chan0 + ch * 16u
+      const bool in = data && (uint32_t)row < (uint32_t)a.H && (uint32_t)col < (uint32_t)a.W;
+      const uint32_t off = in ? (uint32_t)__mul24(__mul24(row, a.W) + col, (int)pix_bytes) + chan
                               : kOutside;
-      if (v < nvec) copy16_to_lds(xr, lds + base * 16u, off);
+      if (t < used && pix < npix) copy16_to_lds(xr, lds + (slot - lane) * 16u, off);
+      c += step_c;
+      r += step_r;
+      if (c >= (uint32_t)a.WW) {
+        c -= (uint32_t)a.WW;
+        r += 1;
+      }
     }
   }
-  // ---- stage the tile's offset/weight rows (GB groups per pixel)
+  // ---- stage the tile's offset/weight rows (GB groups per pixel), the same
+  // way: thread t copies unit e = t % upp of tile pixels t / upp + i * ppp
   const rsrc_t omr = make_rsrc(a.om + (uint64_t)n * a.om_img_bytes, a.om_img_bytes);
   {
     const uint32_t upp = (uint32_t)(a.OB / a.om_unit);
-    const uint32_t nunits = (uint32_t)(a.TH * a.TW) * upp;
-    const uint32_t grp0 = g0 * (uint32_t)(3 * K * es);
-    for (uint32_t base = threadIdx.x & ~63u; base < nunits; base += (uint32_t)a.block) {
-      const uint32_t u = base + lane;
-      const uint32_t tp = fastdiv(u, a.div_obu), e = u - tp * upp;
-      const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
+    const uint32_t ppp = (uint32_t)a.block / upp;
+    const uint32_t used = ppp * upp;
+    const uint32_t npix = (uint32_t)(a.TH * a.TW);
+    const uint32_t t = threadIdx.x;
+    const uint32_t tp0 = fastdiv(t, a.div_obu), e = t - tp0 * upp;
+    const uint32_t step_r = fastdiv(ppp, a.div_tw), step_c = ppp - step_r * (uint32_t)a.TW;
+    uint32_t py = fastdiv(tp0, a.div_tw), px = tp0 - py * (uint32_t)a.TW;
+    const uint32_t unit_off = g0 * (uint32_t)(3 * K * es) + e * (uint32_t)a.om_unit;
+    for (uint32_t tp = tp0, slot = t; tp - tp0 < npix; tp += ppp, slot += used) {
       const int yo = ty0 + (int)py, xo = tx0 + (int)px;
       const bool in = yo < a.Ho && xo < a.Wo;
-      const uint32_t off = in ? (uint32_t)(yo * a.Wo + xo) * a.om_row_bytes + grp0 +
-                                    e * (uint32_t)a.om_unit
-                              : kOutside;
-      if (u < nunits) {
+      const uint32_t off = in ? (uint32_t)(yo * a.Wo + xo) * a.om_row_bytes + unit_off : kOutside;
+      if (t < used && tp < npix) {
         if (a.om_unit == 4) {
-          copy4_to_lds(omr, lds + a.om_lds + base * 4u, off);
+          copy4_to_lds(omr, lds + a.om_lds + (slot - lane) * 4u, off);
         } else {
-          *reinterpret_cast<uint16_t*>(lds + a.om_lds + 2u * u) =
+          *reinterpret_cast<uint16_t*>(lds + a.om_lds + 2u * slot) =
               __builtin_amdgcn_raw_buffer_load_b16(omr, (int)off, 0, 0);
         }
+      }
+      px += step_c;
+      py += step_r;
+      if (px >= (uint32_t)a.TW) {
+        px -= (uint32_t)a.TW;
+        py += 1;
       }
     }
   }
@@ -541,8 +563,10 @@ void dcn4_tile_kernel(TileArgs a) {
   // window bounds for the corner (y0, x0): y0 in [wy0, wy0 + WH - 2]
   const float wy_lo = (float)wy0, wy_hi = (float)(wy0 + a.WH - 2);
   const float wx_lo = (float)wx0, wx_hi = (float)(wx0 + a.WW - 2);
-  const uint32_t lane_lds = (gl * (uint32_t)a.D + l * DP) * es;
-  const uint32_t dy1 = (uint32_t)(a.WW * a.PS);
+  const int row_lds = a.WW * a.PS;
+  // LDS byte address of corner (y0, x0) = win_base + y0*row_lds + x0*PS
+  const int win_base = (int)((gl * (uint32_t)a.D + l * DP) * es) - wy0 * row_lds - wx0 * a.PS;
+  const float by0f = (float)t.by0, bx0f = (float)t.bx0;
 
   float acc[DP];
 #pragma unroll
@@ -555,20 +579,25 @@ void dcn4_tile_kernel(TileArgs a) {
     const float dx = io::dec(om[2 * k]);
     const float dy = io::dec(om[2 * k + 1]);
     const float m = io::dec(om[2 * K + k]);
-    const float by = (float)(t.by0 + i * a.dh), bx = (float)(t.bx0 + j * a.dw);
+    // exact integer bases: the wave-uniform grid step is added in fp32
+    const float by = by0f + (float)(i * a.dh), bx = bx0f + (float)(j * a.dw);
     const Cell c = locate(sample_location<MODE>(by, bx, 0.0f, 0.0f, dy, dx,
                                                 a.offset_scale, 1.0f),
                           a.Hm1, a.Wm1);
-    const bool ok = (c.yf >= wy_lo) && (c.yf <= wy_hi) && (c.xf >= wx_lo) &&
-                    (c.xf <= wx_hi) && __builtin_isfinite(m);
-    if (__ballot(!ok) == 0) {
+    // one scalar mask per condition; NaN fails every comparison
+    const uint64_t off_window =
+        __builtin_amdgcn_ballot_w64(!(c.yf >= wy_lo)) |
+        __builtin_amdgcn_ballot_w64(!(c.yf <= wy_hi)) |
+        __builtin_amdgcn_ballot_w64(!(c.xf >= wx_lo)) |
+        __builtin_amdgcn_ballot_w64(!(c.xf <= wx_hi)) |
+        __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
+    if (off_window == 0) {
       const float hh = 1.0f - c.lh, hw = 1.0f - c.lw;
       const float cf[4] = {m * (hh * hw), m * (hh * c.lw), m * (c.lh * hw),
                            m * (c.lh * c.lw)};
-      const uint32_t addr = lane_lds +
-          (uint32_t)__mul24(__mul24(c.y0 - wy0, a.WW) + (c.x0 - wx0), a.PS);
+      const uint32_t addr = (uint32_t)(win_base + __mul24(c.y0, row_lds) + __mul24(c.x0, a.PS));
       LdsTap<DT, VEC, NV> d;
-      d.load(lds, addr, (uint32_t)a.PS, dy1);
+      d.load(lds, addr, (uint32_t)a.PS, (uint32_t)row_lds);
       d.accumulate(acc, cf);
     } else {
       const Tap tg = tap_geometry<DT, MODE, KS>(fa, t, om, k);
