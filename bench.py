@@ -59,7 +59,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=None,
                     help="workload name (default: the latent-diffusion U-Net block)")
     ap.add_argument("--sets", type=int, default=0,

@@ -27,14 +27,17 @@
  * output size is Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
  * (Wo likewise).
  *
- * Arithmetic: fp32 throughout.  Per sample: one fp32 add for the location
- * (group-scale mode: fl(centre + fl(s_g*fl(grid + d)))); the sample is skipped
- * unless -1 < row < H and -1 < col < W; y0 = floor(row), lh = row - y0,
+ * Arithmetic: fp32 throughout.  Per sample the location is an exact integer
+ * part plus a fraction: t = fl(offset_scale*d) (group-scale mode:
+ * fl(s_g*fl(grid + d)), measured from the integer centre); f = floor(t);
+ * lh = fl(t - f); y0 = base + f (exact); the sample is skipped unless
+ * -1 <= y0 <= H-1 and -1 <= x0 <= W-1 (a NaN displacement fails the test);
  * hh = 1 - lh (same for x); corner weights hh*hw, hh*lw, lh*hw, lh*lw for
  * corners (y0,x0), (y0,x0+1), (y0+1,x0), (y0+1,x0+1); coefficient fl(m*w);
  * corners outside the image are skipped; acc = fma(coefficient, value, acc)
  * with points outer and corners inner, starting from +0; the result is
- * rounded to the I/O dtype to nearest even.  Subnormals are kept.
+ * rounded to the I/O dtype to nearest even.  Subnormals are kept.  Every
+ * kernel variant and option gives bit-identical results.
  *
  * Layouts (all dense, channel-last, row-major):
  *   x            [N, H, W, C]          I/O dtype
@@ -172,11 +175,11 @@ dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
                          void* y, void* stream);
 
 /* Test probe of the sampling geometry: for every (n, yo, xo, g, k), in that
- * order, writes inside (1 if the sample passed the -1<row<H, -1<col<W test),
- * and for inside samples y0 = floor(row), x0 = floor(col), lh = row - y0,
- * lw = col - x0 (zeros otherwise), computed by the same device functions as
- * the forward kernel.  Outputs are device arrays of N*Ho*Wo*G*K entries.
- * Errors as dcn4_forward. */
+ * order, writes inside (1 if the integer parts passed the -1 <= y0 <= H-1,
+ * -1 <= x0 <= W-1 test), and for inside samples the integer parts y0, x0 and
+ * the fractions lh, lw of the arithmetic above (zeros otherwise), computed
+ * by the same device functions as the forward kernels.  Outputs are device
+ * arrays of N*Ho*Wo*G*K entries.  Errors as dcn4_forward. */
 dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
                                 const float* group_scales, int32_t* y0,
                                 int32_t* x0, float* lh, float* lw,
