@@ -72,9 +72,10 @@ DCN4_OPT_KERNEL = 1
 DCN4_OPT_TILE_MARGIN = 2
 DCN4_OPT_TILE_GROUPS = 3
 DCN4_OPT_TILE_PAD = 4
+DCN4_OPT_TILE_SWIZZLE = 5
 OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
            "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
-           "tile_pad": DCN4_OPT_TILE_PAD}
+           "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE}
 
 
 _P = ctypes.c_void_p
@@ -193,7 +194,9 @@ class Plan:
     """Owns a dcn4_plan; forward() takes torch CUDA tensors."""
 
     def __init__(self, desc: Desc, channels_per_lane: int = 0, **options):
-        """options: kernel, tile_margin, tile_groups, tile_pad (dcn4_option)."""
+        """options: kernel, tile_margin, tile_groups, tile_pad, tile_swizzle
+        (dcn4_option).  The kernel choice is applied last, so a forced tiled
+        kernel is checked against the tile options given with it."""
         self.desc = desc
         st, h = dcn4_create(desc.c_struct())
         if st != DCN4_OK:
@@ -201,7 +204,7 @@ class Plan:
         self._h = h
         if channels_per_lane:
             self.set_option("channels_per_lane", channels_per_lane)
-        for k, v in options.items():
+        for k, v in sorted(options.items(), key=lambda kv: kv[0] == "kernel"):
             self.set_option(k, v)
         st, self.Ho, self.Wo, self.ideal_bytes = dcn4_query(h)
         if st != DCN4_OK:

@@ -27,6 +27,9 @@ constexpr int64_t kCoordLimit = int64_t(1) << 20;
 // Margin of the tiled kernel's LDS window, in pixels around the footprint of
 // the tile's undisplaced sample points: offsets within it gather from LDS.
 constexpr int32_t kDefaultTileMargin = 4;
+// lane-index bit (plus one) that swaps a lane's vector pairs in the tiled
+// kernel: bit 3, so lanes 8 apart start on different LDS banks
+constexpr int32_t kDefaultTileSwizzle = 4;
 
 // Output size of the convolution index arithmetic with padding and dilation.
 int64_t out_size(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
@@ -108,6 +111,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.tile_margin = kDefaultTileMargin;
   p.tile_groups = 0;
   p.tile_pad = 0;
+  p.tile_swizzle = kDefaultTileSwizzle;
   dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic
@@ -167,6 +171,8 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
   info->lanes_per_group = p.D / dp;
   if (vec && p.tile.ok) {
     const dcn4::TileShape& t = p.tile;
+    info->channels_per_lane = t.dp;
+    info->lanes_per_group = p.D / t.dp;
     const int64_t tiles = int64_t((p.Ho + t.th - 1) / t.th) * ((p.Wo + t.tw - 1) / t.tw);
     const int64_t per_image = tiles * (p.desc.group / t.gb);
     const int64_t imgs = (int64_t(1) << 30) / per_image;
@@ -205,6 +211,7 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     case DCN4_OPT_CHANNELS_PER_LANE: {
       if (value == 0) {
         q.dp = q.dp_default;
+        q.dp_user = 0;
         break;
       }
       const int32_t vec = 16 / q.es;
@@ -214,6 +221,7 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
       if (dcn4::forward_block(q, q.D / value) == 0)
         return fail(DCN4_ERR_UNSUPPORTED, "offset/weight rows are too large for LDS");
       q.dp = value;
+      q.dp_user = 1;
       break;
     }
     case DCN4_OPT_KERNEL:
@@ -232,6 +240,10 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     case DCN4_OPT_TILE_PAD:
       if (value != 0 && value != 1) return fail(DCN4_ERR_INVALID_ARG, "tile pad must be 0 or 1");
       q.tile_pad = value;
+      break;
+    case DCN4_OPT_TILE_SWIZZLE:
+      if (value < 0 || value > 6) return fail(DCN4_ERR_INVALID_ARG, "tile swizzle must be 0-6");
+      q.tile_swizzle = value;
       break;
     default:
       return fail(DCN4_ERR_INVALID_ARG, "unknown option");

@@ -60,7 +60,7 @@ struct FwdArgs {
 // Arguments of the tiled kernel.  A workgroup owns (image, TH x TW output
 // tile, chunk of GB groups); it stages a zero-padded input window of WH x WW
 // pixels (the tile's sampling footprint plus a margin of M pixels) and the
-// tile's offset/weight rows in LDS.
+// tile's offset/weight values in LDS.
 struct TileArgs {
   const char* x;         // input of this launch's first image
   const char* om;        // offset/weight tensor of this launch's first image
@@ -70,24 +70,30 @@ struct TileArgs {
   int32_t kh, kw, sh, sw, ph, pw, dh, dw;
   float offset_scale, Hm1, Wm1;
   int32_t L;             // lanes per (pixel, group), D / D'
+  int32_t swz_shift;     // lane-index bit that swaps a lane's vector pairs (-1: none)
   int32_t GB, TH, TW, M; // groups per workgroup, tile, margin
   int32_t WH, WW;        // window rows, cols
   int32_t PS;            // LDS bytes per window pixel (GB*D*es, maybe padded)
   int32_t CB;            // bytes of a pixel's GB groups, GB*D*es
-  int32_t OB;            // offset/weight bytes of a pixel's GB groups
-  int32_t om_unit;       // bytes per offset/weight copy unit (4, or 2)
+  int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
+  int32_t wrpp, wpasses; // window rows per staging pass, passes
+  int32_t OSU;           // 4-byte offset/weight units per tile pixel
+  int32_t upr;           // offset/weight units per tile row, TW*OSU
+  int32_t orpp;          // tile rows per offset/weight staging pass (0: by pixels)
+  int32_t oppp;          // tile pixels per pass when orpp == 0
+  int32_t opasses;       // offset/weight staging passes
   int32_t om_lds;        // byte offset of the offset/weight area in LDS
-  int32_t tiles_x, tiles_y, chunks, nblocks, block;
+  int32_t tiles_x, tiles_y, chunks, nblocks;
   uint32_t img_bytes;    // H*W*C*es
   uint32_t om_img_bytes; // Ho*Wo*G*3K*es
-  uint32_t om_row_bytes; // G*3K*es
-  FastDiv div_chunks, div_tx, div_ty, div_cbv, div_ww, div_gbl, div_L, div_tw,
-      div_obu;
+  uint32_t om_row_bytes; // G*3K*es (a multiple of 4)
+  FastDiv div_chunks, div_tx, div_ty, div_cpr, div_cvec, div_upr, div_osu,
+      div_gbl, div_L, div_tw;
 };
 
 // Tile shape a plan resolved (ok == 0: the tiled kernel does not apply).
 struct TileShape {
-  int32_t ok, gb, th, tw, margin, wh, ww, ps, cb, ob, om_unit, lds_bytes;
+  int32_t ok, dp, gb, th, tw, margin, wh, ww, ps, cb, osu, lds_bytes;
 };
 
 enum KernelChoice : int32_t { kKernelAuto = 0, kKernelDirect = 1, kKernelTiled = 2 };
@@ -101,7 +107,8 @@ struct Plan {
   uint64_t ideal_bytes;
   int32_t images_per_launch;  // bounds the per-launch lane count below 2^31
   // options (dcn4_plan_set_option) and the tile shape they resolve to
-  int32_t kernel_choice, tile_margin, tile_groups, tile_pad;
+  int32_t kernel_choice, tile_margin, tile_groups, tile_pad, tile_swizzle;
+  int32_t dp_user;       // 1: channels per lane set by the caller
   TileShape tile;
 };
 

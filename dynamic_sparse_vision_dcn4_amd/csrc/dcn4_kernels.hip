@@ -93,6 +93,12 @@ template <> struct Io<DCN4_BF16> {
   __device__ static raw enc(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
   }
+  // two values, packed low then high (one packed round-to-nearest-even convert)
+  __device__ static uint32_t enc2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+  }
 };
 template <> struct Io<DCN4_F16> {
   static constexpr int es = 2;
@@ -104,6 +110,9 @@ template <> struct Io<DCN4_F16> {
   }
   __device__ static raw enc(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+  __device__ static uint32_t enc2(float lo, float hi) {
+    return (uint32_t)enc(lo) | ((uint32_t)enc(hi) << 16);
   }
 };
 
@@ -239,6 +248,19 @@ template <int DT, int VEC, int NV> struct TapData {
 #pragma unroll
       for (int n = 0; n < NV; ++n)
         v[q][n] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(g.q[q] + 16 * n), 0, 0);
+  }
+  // The same with the vectors of each pair swapped when r16 == 16: slot n
+  // holds vector n ^ 1 (the tiled kernel's per-lane vector order).  Offsets
+  // stay non-negative: slot 2j at q + 16r + 32j, slot 2j+1 at q + 16(1-r) + 32j.
+  __device__ __forceinline__ void load_swapped(rsrc_t xr, const Tap& g, uint32_t r16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t qe = g.q[q] + r16, qo = g.q[q] + (16u - r16);
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        v[q][n] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, (int)(((n & 1) ? qo : qe) + 16 * (n & ~1)), 0, 0);
+    }
   }
   __device__ __forceinline__ void accumulate(float* acc, const Tap& g) const {
 #pragma unroll
@@ -413,23 +435,29 @@ void dcn4_forward_kernel(FwdArgs a) {
 // lanes per clock per CU: the workgroup therefore copies, with coalesced
 // 128-bit loads, the zero-padded input window its tile can sample (tile
 // footprint plus a margin of M pixels on every side) for its chunk of GB
-// groups, and the tile's offset/weight rows.  A point whose four corners lie
-// in the window is gathered from LDS -- corners outside the image read the
-// staged zeros, and fma(c, 0, acc) == acc for a finite coefficient.  When any
-// lane of a wave has a point outside the window, or a non-finite weight, the
-// whole wave takes the global path of the direct kernel for that point.  Both
-// paths perform the same operations on the same values, so the result does
-// not depend on which path ran.
+// groups, and the tile's offset/weight values.  A point whose four corners
+// lie in the window is gathered from LDS -- corners outside the image read
+// the staged zeros, and fma(c, 0, acc) == acc for a finite coefficient.  When
+// any lane of a wave has a point outside the window, or a non-finite weight,
+// the whole wave takes the global path of the direct kernel for that point.
+// Both paths perform the same operations on the same values, so the result
+// does not depend on which path ran.
+typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
 template <int DT, int VEC, int NV> struct LdsTap {
   u32x4 v[4][NV];
-  __device__ __forceinline__ void load(const char* base, uint32_t addr,
-                                       uint32_t dx1, uint32_t dy1) {
-    const uint32_t off[4] = {0u, dx1, dy1, dy1 + dx1};
+  // e00, e10: LDS addresses of the even slots of corners (y0, x0) and
+  // (y0 + 1, x0); o00, o10 those of the odd slots (the lane's vector order is
+  // swapped pairwise or not, see TileLane); dx1: bytes to corner x0 + 1
+  __device__ __forceinline__ void load(uint32_t e00, uint32_t e10, uint32_t o00,
+                                       uint32_t o10, uint32_t dx1) {
+    const uint32_t ea[4] = {e00, e00 + dx1, e10, e10 + dx1};
+    const uint32_t oa[4] = {o00, o00 + dx1, o10, o10 + dx1};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int n = 0; n < NV; ++n)
-        v[q][n] = *reinterpret_cast<const u32x4*>(base + addr + off[q] + 16 * n);
+        v[q][n] = *reinterpret_cast<lds_u32x4*>(
+            (uintptr_t)(((n & 1) ? oa[q] : ea[q]) + 16 * (n & ~1)));
   }
   __device__ __forceinline__ void accumulate(float* acc, const float* c) const {
 #pragma unroll
@@ -442,7 +470,68 @@ template <int DT, int VEC, int NV> struct LdsTap {
   }
 };
 
-template <int DT, int VEC, int NV, int MODE, int KS>
+// Per-lane state of the tiled kernel's point loop.
+// A lane reads its NV 16-byte vectors per corner in the order n ^ r (r = 0
+// or 1, fixed per lane; r = 0 when NV is odd): lanes 2^s apart in a wave then
+// start on different LDS banks, which removes the two-way bank conflict that
+// 32-byte window pixels otherwise give 16 neighbouring lanes.  The lane's
+// accumulators follow the same order, and the output store undoes it.
+struct TileLane {
+  float lane_f;        // LDS address of the lane's even slots at window cell (c, c)
+  float row_f, ps_f;   // LDS bytes per window row / pixel
+  float ymax, xmax;    // largest corner cell minus c: WH-2-c / WW-2-c
+  float c;             // cell coordinates are taken relative to (c, c)
+  uint32_t row_lds, ps;
+  uint32_t odd;        // odd slots minus even slots, 16 - 32r (mod 2^32)
+};
+
+// One sample point of the tiled kernel.  by/bx: integer base of the point
+// relative to window cell (c, c) (exact floats); returns false when the wave
+// must take the global path for this point (nothing accumulated then).
+// SQ: the window is square and c is its centre, so the corner cell is inside
+// iff max(|yr|, |xr|) <= ymax; the IEEE maximum propagates NaN, and m*0 is
+// NaN exactly when m is not finite, which folds the weight test in.
+template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ>
+__device__ __forceinline__ bool tile_point(const TileLane& w,
+                                           float by, float bx, float dy, float dx,
+                                           float m, float os, float* acc) {
+  const Loc l = sample_location<MODE>(by, bx, 0.0f, 0.0f, dy, dx, os, 1.0f);
+  const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
+  const float yr = by + fy, xr = bx + fx;  // corner (y0, x0) minus (c, c)
+  uint64_t off_window;
+  if constexpr (SQ) {
+    const float t = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_fabsf(yr), __builtin_fabsf(xr)),
+        __builtin_fabsf(m * 0.0f));
+    off_window = __builtin_amdgcn_ballot_w64(!(t <= w.ymax));
+  } else {
+    // one scalar mask per condition; NaN fails every comparison
+    off_window = __builtin_amdgcn_ballot_w64(!(yr >= -w.c)) |
+                 __builtin_amdgcn_ballot_w64(!(yr <= w.ymax)) |
+                 __builtin_amdgcn_ballot_w64(!(xr >= -w.c)) |
+                 __builtin_amdgcn_ballot_w64(!(xr <= w.xmax)) |
+                 __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
+  }
+  if (off_window != 0) return false;
+  const float lh = l.ty - fy, lw = l.tx - fx;
+  const float hh = 1.0f - lh, hw = 1.0f - lw;
+  const float cf[4] = {m * (hh * hw), m * (hh * lw), m * (lh * hw), m * (lh * lw)};
+  // LDS byte address of corner (y0, x0): every term an integer below 2^24,
+  // so the fp32 arithmetic is exact
+  const uint32_t a00 = (uint32_t)__builtin_fmaf(yr, w.row_f, __builtin_fmaf(xr, w.ps_f, w.lane_f));
+  const uint32_t a10 = a00 + w.row_lds;
+  LdsTap<DT, VEC, NV> d;
+  if (NV > 1)
+    d.load(a00, a10, a00 + w.odd, a10 + w.odd, PSC ? (uint32_t)PSC : w.ps);
+  else
+    d.load(a00, a10, a00, a10, PSC ? (uint32_t)PSC : w.ps);
+  d.accumulate(acc, cf);
+  return true;
+}
+
+// PSC: the LDS bytes per window pixel when known at compile time (one lane
+// owns one whole group, no padding, square window), else 0.
+template <int DT, int VEC, int NV, int MODE, int KS, int PSC>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
 void dcn4_tile_kernel(TileArgs a) {
@@ -465,165 +554,219 @@ void dcn4_tile_kernel(TileArgs a) {
   const int wy0 = ty0 * a.sh - a.ph - a.M, wx0 = tx0 * a.sw - a.pw - a.M;
   const uint32_t g0 = gc * (uint32_t)a.GB;
   const int K = KS ? KS * KS : a.kh * a.kw;
+  const uint32_t t = threadIdx.x, lane = t & 63u, wave0 = t - lane;
+  const uint32_t pix_bytes = (uint32_t)(a.C * es);
 
-  // ---- stage the input window (zeros outside the image).  A window pixel
-  // is PS bytes in LDS: its GB groups' channels, then (when padded) one
-  // 16-byte chunk loaded as zeros, so the copy stays one contiguous run.
-  // Thread t copies chunk j = t % cvec of window pixels t / cvec + i * ppp
-  // (ppp = 256 / cvec pixels per pass), stepping row and column
-  // incrementally; lane order equals LDS order, as the copy requires.
+  // ---- stage the input window (zeros outside the image) in passes of wrpp
+  // whole window rows.  A window pixel is PS bytes in LDS: its GB groups'
+  // channels, then (when padded) one 16-byte chunk loaded as zeros.  Thread
+  // t copies chunk t of every pass, so lane order equals LDS order as the
+  // copy requires, and its column, chunk and column test are fixed.
   const rsrc_t xr = make_rsrc(a.x + (uint64_t)n * a.img_bytes, a.img_bytes);
-  const uint32_t lane = threadIdx.x & 63u;
   {
-    const uint32_t cvec = (uint32_t)a.PS >> 4, dvec = (uint32_t)a.CB >> 4;
-    const uint32_t ppp = (uint32_t)a.block / cvec;        // pixels per pass
-    const uint32_t used = ppp * cvec;                     // threads that copy
-    const uint32_t npix = (uint32_t)(a.WH * a.WW);
-    const uint32_t t = threadIdx.x;
-    const uint32_t pix0 = fastdiv(t, a.div_cbv), ch = t - pix0 * cvec;
-    const uint32_t step_r = fastdiv(ppp, a.div_ww), step_c = ppp - step_r * (uint32_t)a.WW;
-    uint32_t r = fastdiv(pix0, a.div_ww), c = pix0 - r * (uint32_t)a.WW;
-    const uint32_t pix_bytes = (uint32_t)(a.C * es);
-    const uint32_t chan = g0 * (uint32_t)a.D * es + ch * 16u;
-    const bool data = ch < dvec;
-    for (uint32_t pix = pix0, slot = t; pix - pix0 < npix; pix += ppp, slot += used) {
-      const int row = wy0 + (int)r, col = wx0 + (int)c;
-      const bool in = data && (uint32_t)row < (uint32_t)a.H && (uint32_t)col < (uint32_t)a.W;
-      const uint32_t off = in ? (uint32_t)__mul24(__mul24(row, a.W) + col, (int)pix_bytes) + chan
-                              : kOutside;
-      if (t < used && pix < npix) copy16_to_lds(xr, lds + (slot - lane) * 16u, off);
-      c += step_c;
-      r += step_r;
-      if (c >= (uint32_t)a.WW) {
-        c -= (uint32_t)a.WW;
-        r += 1;
+    const uint32_t cvec = (uint32_t)a.PS >> 4;
+    const uint32_t rp = fastdiv(t, a.div_cpr);  // row within the pass
+    const uint32_t cc = t - rp * (uint32_t)a.cpr;
+    const uint32_t col = fastdiv(cc, a.div_cvec), ch = cc - col * cvec;
+    const int gcol = wx0 + (int)col;
+    const bool col_ok = ch < ((uint32_t)a.CB >> 4) && (uint32_t)gcol < (uint32_t)a.W;
+    const bool copies = rp < (uint32_t)a.wrpp;
+    const uint32_t row_bytes = (uint32_t)a.W * pix_bytes;
+    int row = wy0 + (int)rp;
+    // byte offset of (row, gcol, chunk); used only while it is in the image
+    uint32_t off = (uint32_t)row * row_bytes + (uint32_t)gcol * pix_bytes +
+                   g0 * (uint32_t)(a.D * es) + ch * 16u;
+    const uint32_t pass_bytes = (uint32_t)a.wrpp * row_bytes;
+    const int row_end = wy0 + a.WH;
+    char* dst = lds + wave0 * 16u;
+    const uint32_t pass_lds = (uint32_t)(a.wrpp * a.cpr) * 16u;
+    for (int p = 0; p < a.wpasses; ++p) {
+      if (copies && row < row_end) {
+        const bool in = col_ok && (uint32_t)row < (uint32_t)a.H;
+        copy16_to_lds(xr, dst, in ? off : kOutside);
       }
+      row += a.wrpp;
+      off += pass_bytes;
+      dst += pass_lds;
     }
   }
-  // ---- stage the tile's offset/weight rows (GB groups per pixel), the same
-  // way: thread t copies unit e = t % upp of tile pixels t / upp + i * ppp
+  // ---- stage the tile's offset/weight values.  Per tile pixel the chunk's
+  // GB*3K values are OSU 4-byte units from the 4-byte boundary at or below
+  // their start (rows are 4-byte aligned, so the lead `mis` is the same for
+  // every pixel).  Passes of orpp whole tile rows when a row's units fit the
+  // workgroup (thread t then keeps its column and unit), else passes of
+  // oppp whole pixels.
   const rsrc_t omr = make_rsrc(a.om + (uint64_t)n * a.om_img_bytes, a.om_img_bytes);
-  {
-    const uint32_t upp = (uint32_t)(a.OB / a.om_unit);
-    const uint32_t ppp = (uint32_t)a.block / upp;
-    const uint32_t used = ppp * upp;
+  const uint32_t seg = g0 * (uint32_t)(3 * K * es);
+  const uint32_t mis = seg & 3u;
+  char* om_dst = lds + a.om_lds + wave0 * 4u;
+  if (a.orpp == 1) {
+    // one tile row per pass: the row is the same for every copying thread
+    const uint32_t upx = fastdiv(t, a.div_osu), e = t - upx * (uint32_t)a.OSU;
+    const int xo = tx0 + (int)upx;
+    const bool copies = t < (uint32_t)a.upr;
+    const bool col_ok = xo < a.Wo;
+    uint32_t off = ((uint32_t)ty0 * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
+                   (seg - mis) + 4u * e;
+    const uint32_t pass_bytes = (uint32_t)a.Wo * a.om_row_bytes;
+    const uint32_t pass_lds = (uint32_t)a.upr * 4u;
+    const int rows = min(a.TH, a.Ho - ty0);  // rows of the tile inside the output
+    for (int p = 0; p < a.TH; ++p) {
+      if (copies) {
+        const bool in = col_ok && p < rows;
+        copy4_to_lds(omr, om_dst, in ? off : kOutside);
+      }
+      off += pass_bytes;
+      om_dst += pass_lds;
+    }
+  } else if (a.orpp > 0) {
+    const uint32_t rp = fastdiv(t, a.div_upr);
+    const uint32_t u = t - rp * (uint32_t)a.upr;
+    const uint32_t upx = fastdiv(u, a.div_osu), e = u - upx * (uint32_t)a.OSU;
+    const int xo = tx0 + (int)upx;
+    const bool col_ok = xo < a.Wo;
+    const bool copies = rp < (uint32_t)a.orpp;
+    int yo = ty0 + (int)rp;
+    uint32_t off = ((uint32_t)yo * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
+                   (seg - mis) + 4u * e;
+    const uint32_t pass_bytes = (uint32_t)a.orpp * (uint32_t)a.Wo * a.om_row_bytes;
+    const int yo_end = ty0 + a.TH;
+    const uint32_t pass_lds = (uint32_t)(a.orpp * a.upr) * 4u;
+    for (int p = 0; p < a.opasses; ++p) {
+      if (copies && yo < yo_end) {
+        const bool in = col_ok && yo < a.Ho;
+        copy4_to_lds(omr, om_dst, in ? off : kOutside);
+      }
+      yo += a.orpp;
+      off += pass_bytes;
+      om_dst += pass_lds;
+    }
+  } else {
+    const uint32_t pp = fastdiv(t, a.div_osu), e = t - pp * (uint32_t)a.OSU;
+    const bool copies = pp < (uint32_t)a.oppp;
     const uint32_t npix = (uint32_t)(a.TH * a.TW);
-    const uint32_t t = threadIdx.x;
-    const uint32_t tp0 = fastdiv(t, a.div_obu), e = t - tp0 * upp;
-    const uint32_t step_r = fastdiv(ppp, a.div_tw), step_c = ppp - step_r * (uint32_t)a.TW;
-    uint32_t py = fastdiv(tp0, a.div_tw), px = tp0 - py * (uint32_t)a.TW;
-    const uint32_t unit_off = g0 * (uint32_t)(3 * K * es) + e * (uint32_t)a.om_unit;
-    for (uint32_t tp = tp0, slot = t; tp - tp0 < npix; tp += ppp, slot += used) {
-      const int yo = ty0 + (int)py, xo = tx0 + (int)px;
-      const bool in = yo < a.Ho && xo < a.Wo;
-      const uint32_t off = in ? (uint32_t)(yo * a.Wo + xo) * a.om_row_bytes + unit_off : kOutside;
-      if (t < used && tp < npix) {
-        if (a.om_unit == 4) {
-          copy4_to_lds(omr, lds + a.om_lds + (slot - lane) * 4u, off);
-        } else {
-          *reinterpret_cast<uint16_t*>(lds + a.om_lds + 2u * slot) =
-              __builtin_amdgcn_raw_buffer_load_b16(omr, (int)off, 0, 0);
-        }
+    const uint32_t pass_lds = (uint32_t)(a.oppp * a.OSU) * 4u;
+    for (int p = 0; p < a.opasses; ++p) {
+      const uint32_t P = (uint32_t)(p * a.oppp) + pp;
+      if (copies && P < npix) {
+        const uint32_t qy = fastdiv(P, a.div_tw), qx = P - qy * (uint32_t)a.TW;
+        const int yo = ty0 + (int)qy, xo = tx0 + (int)qx;
+        const bool in = yo < a.Ho && xo < a.Wo;
+        const uint32_t off = ((uint32_t)yo * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
+                             (seg - mis) + 4u * e;
+        copy4_to_lds(omr, om_dst, in ? off : kOutside);
       }
-      px += step_c;
-      py += step_r;
-      if (px >= (uint32_t)a.TW) {
-        px -= (uint32_t)a.TW;
-        py += 1;
-      }
+      om_dst += pass_lds;
     }
   }
   __syncthreads();
 
   // ---- lane -> (tile pixel, group in chunk, channel slice)
-  const uint32_t tp = fastdiv((uint32_t)threadIdx.x, a.div_gbl);
-  const uint32_t rr = (uint32_t)threadIdx.x - tp * (uint32_t)(a.GB * a.L);
+  const uint32_t tp = fastdiv(t, a.div_gbl);
+  const uint32_t rr = t - tp * (uint32_t)(a.GB * a.L);
   const uint32_t gl = fastdiv(rr, a.div_L), l = rr - gl * (uint32_t)a.L;
   const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
   const int yo = ty0 + (int)py, xo = tx0 + (int)px;
-  if ((int)tp >= a.TH * a.TW || yo >= a.Ho || xo >= a.Wo) return;
+  if (yo >= a.Ho || xo >= a.Wo) return;
   const uint32_t g = g0 + gl;
   const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
-      lds + a.om_lds + (tp * (uint32_t)a.GB + gl) * (uint32_t)(3 * K * es));
+      lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
 
-  LaneCtx t;
-  t.pix_bytes = (uint32_t)a.C * es;
-  t.row_stride = (uint32_t)a.W * t.pix_bytes;
-  t.lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
-  t.sg = 1.0f;
-  t.hy = ((KS ? KS : a.kh) - 1) >> 1;
-  t.hx = ((KS ? KS : a.kw) - 1) >> 1;
-  t.by0 = yo * a.sh - a.ph;
-  t.bx0 = xo * a.sw - a.pw;
-  // the geometry reads only the fields FwdArgs and TileArgs share
-  FwdArgs fa{};
+  // global-path context (points whose corners leave the window)
+  LaneCtx c;
+  c.pix_bytes = pix_bytes;
+  c.row_stride = (uint32_t)a.W * pix_bytes;
+  c.lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
+  c.sg = 1.0f;
+  c.hy = ((KS ? KS : a.kh) - 1) >> 1;
+  c.hx = ((KS ? KS : a.kw) - 1) >> 1;
+  c.by0 = yo * a.sh - a.ph;
+  c.bx0 = xo * a.sw - a.pw;
+  FwdArgs fa{};  // the geometry reads only the fields FwdArgs and TileArgs share
   fa.H = a.H; fa.W = a.W; fa.kh = a.kh; fa.kw = a.kw; fa.dh = a.dh; fa.dw = a.dw;
   fa.offset_scale = a.offset_scale; fa.Hm1 = a.Hm1; fa.Wm1 = a.Wm1;
 
-  // window bounds for the corner (y0, x0): y0 in [wy0, wy0 + WH - 2]
-  const float wy_lo = (float)wy0, wy_hi = (float)(wy0 + a.WH - 2);
-  const float wx_lo = (float)wx0, wx_hi = (float)(wx0 + a.WW - 2);
-  const int row_lds = a.WW * a.PS;
-  // LDS byte address of corner (y0, x0) = win_base + y0*row_lds + x0*PS
-  const int win_base = (int)((gl * (uint32_t)a.D + l * DP) * es) - wy0 * row_lds - wx0 * a.PS;
-  const float by0f = (float)t.by0, bx0f = (float)t.bx0;
+  TileLane w;
+  w.row_lds = (uint32_t)(a.WW * a.PS);
+  w.ps = (uint32_t)a.PS;
+  w.row_f = (float)w.row_lds;
+  w.ps_f = (float)a.PS;
+  // the window starts at the LDS allocation's base address
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  const uint32_t r16 = (NV % 2 == 0 && a.swz_shift >= 0) ? ((lane >> a.swz_shift) & 1u) * 16u : 0u;
+  w.lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es + r16);
+  w.odd = 16u - 2u * r16;
+  // cell coordinates relative to (cw, cw): the centre of a square window
+  constexpr bool SQ = PSC != 0;
+  const float cw = SQ ? 0.5f * (float)(a.WH - 2) : 0.0f;
+  w.c = cw;
+  w.ymax = (float)(a.WH - 2) - cw;
+  w.xmax = (float)(a.WW - 2) - cw;
+  w.lane_f += cw * w.row_f + cw * w.ps_f;  // exact: small multiples of 1/2
+  // base of point (0, 0) relative to window cell (cw, cw)
+  const float ry0 = (float)(c.by0 - wy0) - cw, rx0 = (float)(c.bx0 - wx0) - cw;
 
   float acc[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
-  const int kw = KS ? KS : a.kw;
+  if (KS) {
+    float bx[KS ? KS : 1];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) bx[j] = rx0 + (float)(j * a.dw);
+    const float fdh = (float)a.dh;
+    float by = ry0;
+#pragma unroll
+    for (int i = 0; i < KS; ++i, by += fdh) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int k = i * KS + j;
+        const float dx = io::dec(om[2 * k]);
+        const float dy = io::dec(om[2 * k + 1]);
+        const float m = io::dec(om[2 * K + k]);
+        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], dy, dx, m, a.offset_scale, acc)) {
+          const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
+          TapData<DT, VEC, NV> d;
+          d.load_swapped(xr, tg, r16);
+          d.accumulate(acc, tg);
+        }
+      }
+    }
+  } else {
+    const int kw = a.kw;
 #pragma unroll 1
-  for (int k = 0; k < K; ++k) {
-    const int i = k / kw, j = k - (k / kw) * kw;
-    const float dx = io::dec(om[2 * k]);
-    const float dy = io::dec(om[2 * k + 1]);
-    const float m = io::dec(om[2 * K + k]);
-    // exact integer bases: the wave-uniform grid step is added in fp32
-    const float by = by0f + (float)(i * a.dh), bx = bx0f + (float)(j * a.dw);
-    const Cell c = locate(sample_location<MODE>(by, bx, 0.0f, 0.0f, dy, dx,
-                                                a.offset_scale, 1.0f),
-                          a.Hm1, a.Wm1);
-    // one scalar mask per condition; NaN fails every comparison
-    const uint64_t off_window =
-        __builtin_amdgcn_ballot_w64(!(c.yf >= wy_lo)) |
-        __builtin_amdgcn_ballot_w64(!(c.yf <= wy_hi)) |
-        __builtin_amdgcn_ballot_w64(!(c.xf >= wx_lo)) |
-        __builtin_amdgcn_ballot_w64(!(c.xf <= wx_hi)) |
-        __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
-    if (off_window == 0) {
-      const float hh = 1.0f - c.lh, hw = 1.0f - c.lw;
-      const float cf[4] = {m * (hh * hw), m * (hh * c.lw), m * (c.lh * hw),
-                           m * (c.lh * c.lw)};
-      const uint32_t addr = (uint32_t)(win_base + __mul24(c.y0, row_lds) + __mul24(c.x0, a.PS));
-      LdsTap<DT, VEC, NV> d;
-      d.load(lds, addr, (uint32_t)a.PS, (uint32_t)row_lds);
-      d.accumulate(acc, cf);
-    } else {
-      const Tap tg = tap_geometry<DT, MODE, KS>(fa, t, om, k);
-      TapData<DT, VEC, NV> d;
-      d.load(xr, tg);
-      d.accumulate(acc, tg);
+    for (int k = 0; k < K; ++k) {
+      const int i = k / kw, j = k - (k / kw) * kw;
+      const float dx = io::dec(om[2 * k]);
+      const float dy = io::dec(om[2 * k + 1]);
+      const float m = io::dec(om[2 * K + k]);
+      const float by = ry0 + (float)(i * a.dh), bx = rx0 + (float)(j * a.dw);
+      if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, dy, dx, m, a.offset_scale, acc)) {
+        const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
+        TapData<DT, VEC, NV> d;
+        d.load_swapped(xr, tg, r16);
+        d.accumulate(acc, tg);
+      }
     }
   }
 
 #pragma unroll
   for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
-  char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * (uint32_t)(a.C * es) +
+  char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * pix_bytes +
              (g * (uint32_t)a.D + l * DP) * es;
+  char* ype = yp + r16;           // even slots
+  char* ypo = yp + (16u - r16);   // odd slots
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    u32x4 w;
-    if (es == 4) {
+    u32x4 o;
+    if constexpr (es == 4) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(acc[v * VEC + e]);
+      for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(acc[v * VEC + e]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)io::enc(acc[v * VEC + 2 * e]) |
-               ((uint32_t)io::enc(acc[v * VEC + 2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) o[e] = io::enc2(acc[v * VEC + 2 * e], acc[v * VEC + 2 * e + 1]);
     }
-    *reinterpret_cast<u32x4*>(yp + 16 * v) = w;
+    *reinterpret_cast<u32x4*>(((v & 1) ? ypo : ype) + 16 * (v & ~1)) = o;
   }
 }
 
@@ -729,26 +872,28 @@ void fill_common(const Plan& p, FwdArgs& a) {
 typedef void (*tile_fn)(TileArgs);
 
 template <int DT, int NV, int MODE>
-tile_fn tile_ks(int K3) {
+tile_fn tile_ks(int K3, bool psc) {
   constexpr int V = 16 / Io<DT>::es;
-  return K3 ? dcn4_tile_kernel<DT, V, NV, MODE, 3> : dcn4_tile_kernel<DT, V, NV, MODE, 0>;
+  if (!K3) return dcn4_tile_kernel<DT, V, NV, MODE, 0, 0>;
+  return psc ? dcn4_tile_kernel<DT, V, NV, MODE, 3, 16 * NV>
+             : dcn4_tile_kernel<DT, V, NV, MODE, 3, 0>;
 }
 
 template <int DT>
-tile_fn tile_pick(int nv, int mode, int K3) {
+tile_fn tile_pick(int nv, int mode, int K3, bool psc) {
   if (mode == kStdScaled) {
     switch (nv) {
-      case 1: return tile_ks<DT, 1, kStdScaled>(K3);
-      case 2: return tile_ks<DT, 2, kStdScaled>(K3);
-      case 3: return tile_ks<DT, 3, kStdScaled>(K3);
-      default: return tile_ks<DT, 4, kStdScaled>(K3);
+      case 1: return tile_ks<DT, 1, kStdScaled>(K3, psc);
+      case 2: return tile_ks<DT, 2, kStdScaled>(K3, psc);
+      case 3: return tile_ks<DT, 3, kStdScaled>(K3, psc);
+      default: return tile_ks<DT, 4, kStdScaled>(K3, psc);
     }
   }
   switch (nv) {
-    case 1: return tile_ks<DT, 1, kStdUnitScale>(K3);
-    case 2: return tile_ks<DT, 2, kStdUnitScale>(K3);
-    case 3: return tile_ks<DT, 3, kStdUnitScale>(K3);
-    default: return tile_ks<DT, 4, kStdUnitScale>(K3);
+    case 1: return tile_ks<DT, 1, kStdUnitScale>(K3, psc);
+    case 2: return tile_ks<DT, 2, kStdUnitScale>(K3, psc);
+    case 3: return tile_ks<DT, 3, kStdUnitScale>(K3, psc);
+    default: return tile_ks<DT, 4, kStdUnitScale>(K3, psc);
   }
 }
 
@@ -819,42 +964,67 @@ dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
   return DCN4_OK;
 }
 
-void resolve_tile(Plan& p) {
-  TileShape t{};
+namespace {
+
+// Tile shape for `gb` groups per workgroup and `dp` channels per lane;
+// false when it does not fit (lanes, staging passes or LDS).
+bool tile_shape(const Plan& p, int32_t dp, int32_t gb, TileShape& t) {
   const dcn4_desc& d = p.desc;
-  p.tile = t;
-  if (p.mode == kGroupScale || p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
-  const int32_t L = p.D / p.dp;
-  // groups per workgroup: the smallest divisor of G whose channels fill at
-  // least 64 bytes of a pixel (half a cache line), unless given
-  int32_t gb = p.tile_groups;
-  if (gb <= 0) {
-    gb = d.group;
-    for (int32_t c = 1; c <= d.group; ++c)
-      if (d.group % c == 0 && c * p.D * p.es >= 64) { gb = c; break; }
-  }
-  if (gb < 1 || d.group % gb) return;
+  const int32_t L = p.D / dp;
   const int32_t lanes_px = gb * L;
-  if (lanes_px > kBlock || kBlock % lanes_px) return;
-  const int32_t tp = kBlock / lanes_px;      // tile pixels
+  if (gb < 1 || d.group % gb || lanes_px > kBlock || kBlock % lanes_px) return false;
+  const int32_t tp = kBlock / lanes_px;  // tile pixels
   int32_t tw = tp >= 16 ? 16 : tp, th = tp / tw;
   if (tp == 64) { th = 8; tw = 8; }
   const int32_t M = p.tile_margin;
   const int32_t wh = (th - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
   const int32_t ww = (tw - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 2;
   const int32_t cb = gb * p.D * p.es;
-  if (cb % 16) return;
+  if (cb % 16) return false;
   int32_t ps = cb;
   if (p.tile_pad && ((ps / 16) % 2 == 0)) ps += 16;  // odd number of 16-byte chunks
+  if ((int64_t)ww * (ps / 16) > kBlock) return false;  // a window row per pass
+  // offset/weight units: the chunk's values from the 4-byte boundary below
+  // their start (a 2-byte lead when 16-bit values start mid-word)
   const int32_t ob = gb * 3 * p.K * p.es;
-  const int32_t row = d.group * 3 * p.K * p.es;
-  const int32_t unit = (p.es == 4 || (ob % 4 == 0 && row % 4 == 0)) ? 4 : 2;
+  const int32_t osu = (ob + (p.es == 2 ? 2 : 0) + 3) / 4;
+  if (osu > kBlock) return false;
   const int64_t win = (int64_t)wh * ww * ps;
-  const int64_t lds = ((win + 15) & ~int64_t(15)) + (((int64_t)tp * ob + 15) & ~int64_t(15));
-  if (lds > 64 * 1024) return;
+  const int64_t lds = ((win + 15) & ~int64_t(15)) + (int64_t)tp * osu * 4;
+  if (lds > 64 * 1024) return false;
   t.ok = 1;
-  t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww; t.ps = ps;
-  t.cb = cb; t.ob = ob; t.om_unit = unit; t.lds_bytes = (int32_t)lds;
+  t.dp = dp; t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww;
+  t.ps = ps; t.cb = cb; t.osu = osu; t.lds_bytes = (int32_t)lds;
+  return true;
+}
+
+}  // namespace
+
+void resolve_tile(Plan& p) {
+  const dcn4_desc& d = p.desc;
+  p.tile = TileShape{};
+  if (p.mode == kGroupScale || p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
+  // offset/weight rows must start on 4-byte boundaries (4-byte staging units)
+  if ((d.group * 3 * p.K * p.es) % 4) return;
+  // channels per lane: the caller's choice, else the plan's default and then
+  // half of it (a smaller tile per lane count keeps wide groups in LDS)
+  int32_t dps[2] = {p.dp, 0};
+  const int32_t vec = 16 / p.es;
+  if (!p.dp_user && p.dp / 2 >= vec && (p.dp / 2) % vec == 0 && p.D % (p.dp / 2) == 0)
+    dps[1] = p.dp / 2;
+  TileShape t{};
+  for (int32_t dp : dps) {
+    if (dp <= 0) continue;
+    if (p.tile_groups > 0) {
+      if (tile_shape(p, dp, p.tile_groups, t)) break;
+      continue;
+    }
+    // fewest groups per workgroup that fit: the largest output tile
+    bool found = false;
+    for (int32_t gb = 1; gb <= d.group && !found; ++gb)
+      if (d.group % gb == 0) found = tile_shape(p, dp, gb, t);
+    if (found) break;
+  }
   p.tile = t;
 }
 
@@ -863,10 +1033,13 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
   const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
-  const int nv = p.dp / (16 / p.es);
-  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3)
-             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3)
-                                    : tile_pick<DCN4_F16>(nv, p.mode, K3);
+  const int nv = ts.dp / (16 / p.es);
+  // the pixel stride is a compile-time constant when a lane owns a whole
+  // unpadded group (and the window is square: see tile_point)
+  const bool psc = ts.gb == 1 && ts.dp == p.D && ts.ps == 16 * nv && ts.wh == ts.ww;
+  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc)
+             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc)
+                                    : tile_pick<DCN4_F16>(nv, p.mode, K3, psc);
   TileArgs a{};
   a.scales = scales;
   a.H = d.H; a.W = d.W; a.C = d.C; a.G = d.group; a.D = p.D; a.Ho = p.Ho; a.Wo = p.Wo;
@@ -875,27 +1048,40 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   a.offset_scale = d.offset_scale;
   a.Hm1 = (float)(d.H - 1);
   a.Wm1 = (float)(d.W - 1);
-  a.L = p.D / p.dp;
+  a.L = p.D / ts.dp;
+  a.swz_shift = p.tile_swizzle > 0 ? p.tile_swizzle - 1 : -1;
   a.GB = ts.gb; a.TH = ts.th; a.TW = ts.tw; a.M = ts.margin;
-  a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb; a.OB = ts.ob;
-  a.om_unit = ts.om_unit;
+  a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb;
+  a.cpr = ts.ww * (ts.ps / 16);
+  a.wrpp = kBlock / a.cpr;
+  a.wpasses = (ts.wh + a.wrpp - 1) / a.wrpp;
+  a.OSU = ts.osu;
+  a.upr = ts.tw * ts.osu;
+  if (a.upr <= kBlock) {  // whole tile rows per pass
+    a.orpp = kBlock / a.upr;
+    a.opasses = (ts.th + a.orpp - 1) / a.orpp;
+  } else {                // whole pixels per pass
+    a.orpp = 0;
+    a.oppp = kBlock / ts.osu;
+    a.opasses = (ts.th * ts.tw + a.oppp - 1) / a.oppp;
+  }
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
   a.tiles_y = (p.Ho + ts.th - 1) / ts.th;
   a.chunks = d.group / ts.gb;
-  a.block = kBlock;
   a.img_bytes = (uint32_t)((uint64_t)d.H * d.W * d.C * p.es);
   a.om_row_bytes = (uint32_t)(d.group * 3 * p.K * p.es);
   a.om_img_bytes = (uint32_t)((uint64_t)p.Ho * p.Wo * a.om_row_bytes);
   a.div_chunks = make_fastdiv((uint32_t)a.chunks);
   a.div_tx = make_fastdiv((uint32_t)a.tiles_x);
   a.div_ty = make_fastdiv((uint32_t)a.tiles_y);
-  a.div_cbv = make_fastdiv((uint32_t)(ts.ps / 16));
-  a.div_ww = make_fastdiv((uint32_t)ts.ww);
+  a.div_cpr = make_fastdiv((uint32_t)a.cpr);
+  a.div_cvec = make_fastdiv((uint32_t)(ts.ps / 16));
+  a.div_upr = make_fastdiv((uint32_t)a.upr);
+  a.div_osu = make_fastdiv((uint32_t)ts.osu);
   a.div_gbl = make_fastdiv((uint32_t)(ts.gb * a.L));
   a.div_L = make_fastdiv((uint32_t)a.L);
   a.div_tw = make_fastdiv((uint32_t)ts.tw);
-  a.div_obu = make_fastdiv((uint32_t)(ts.ob / ts.om_unit));
   const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
   const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
   const int64_t per_image = (int64_t)a.tiles_x * a.tiles_y * a.chunks;

@@ -152,7 +152,10 @@ typedef enum {
   DCN4_OPT_TILE_GROUPS = 3,
   /* tiled kernel: 1 = pad each LDS window pixel to an odd number of 16-byte
    * chunks (fewer bank conflicts), 0 = no padding */
-  DCN4_OPT_TILE_PAD = 4
+  DCN4_OPT_TILE_PAD = 4,
+  /* tiled kernel: k = 1-6 makes lanes whose index has bit k-1 set read their
+   * 16-byte vectors pairwise swapped (fewer LDS bank conflicts); 0 = off */
+  DCN4_OPT_TILE_SWIZZLE = 5
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,

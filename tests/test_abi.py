@@ -128,12 +128,13 @@ def test_headline_plan_shape():
     p = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
     info = p.info()
     # a lane owns a whole 16-channel group, two 128-bit loads per corner; the
-    # tiled kernel runs 8x16 output tiles of 2 groups with an LDS window
+    # tiled kernel runs 16x16 output tiles of one group with an LDS window
+    # small enough for four workgroups per CU
     assert info["channels_per_lane"] == 16 and info["vector_bytes"] == 16
     assert info["kernel"] == 2
-    assert (info["tile_h"], info["tile_w"], info["tile_groups"]) == (8, 16, 2)
-    assert info["blocks"] == 8 * (128 // 8) * (128 // 16) * (20 // 2)
-    assert info["lds_bytes"] <= 64 * 1024
+    assert (info["tile_h"], info["tile_w"], info["tile_groups"]) == (16, 16, 1)
+    assert info["blocks"] == 8 * (128 // 16) * (128 // 16) * 20
+    assert info["lds_bytes"] <= 160 * 1024 // 4
     p.set_option("kernel", 1)
     info = p.info()
     assert info["kernel"] == 1 and info["blocks"] == 8 * 128 * 128 * 20 // 256
@@ -146,7 +147,7 @@ def test_plan_options():
         p.set_option("tile_margin", m)
         assert p.info()["tile_margin"] == m
     for bad in (("tile_margin", -1), ("tile_margin", 17), ("tile_groups", 3),
-                ("kernel", 3), ("tile_pad", 2)):
+                ("kernel", 3), ("tile_pad", 2), ("tile_swizzle", -1), ("tile_swizzle", 7)):
         with pytest.raises(d4.DCN4Error) as e:
             p.set_option(*bad)
         assert e.value.status == d4.DCN4_ERR_INVALID_ARG
@@ -156,15 +157,19 @@ def test_plan_options():
     p.set_option("tile_margin", 3)
     p.set_option("tile_groups", 4)
     assert p.info()["tile_groups"] == 4 and p.info()["tile_h"] * p.info()["tile_w"] == 64
-    # a margin whose window exceeds 64 KiB of LDS: automatic choice falls back
-    # to the direct kernel; a forced tiled kernel refuses it
+    # a wide margin first halves the channels per lane (a smaller tile of
+    # lanes); one whose window exceeds 64 KiB of LDS at every tile shape makes
+    # the automatic choice fall back to the direct kernel, and a forced tiled
+    # kernel refuses it
     p.set_option("tile_groups", 0)
     p.set_option("tile_margin", 12)
-    assert p.info()["kernel"] == 1
+    assert p.info()["kernel"] == 2 and p.info()["channels_per_lane"] == 8
+    p.set_option("tile_margin", 16)
+    assert p.info()["kernel"] == 1 and p.info()["channels_per_lane"] == 16
     p.set_option("tile_margin", 4)
     p.set_option("kernel", 2)
     with pytest.raises(d4.DCN4Error) as e:
-        p.set_option("tile_margin", 12)
+        p.set_option("tile_margin", 16)
     assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
     assert p.info()["tile_margin"] == 4
     # group-scale plans have no tiled kernel

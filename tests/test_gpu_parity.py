@@ -254,6 +254,26 @@ def test_tiled_kernel_margins(dt, margin):
                          dt, f"tiled margin {margin}")
 
 
+@pytest.mark.parametrize("swizzle", [0, 1, 3, 4, 6])
+@pytest.mark.parametrize("dt, D, dp", [("bf16", 16, 16), ("f32", 16, 8), ("f16", 32, 16),
+                                       ("bf16", 64, 32)])
+def test_tiled_kernel_vector_order(dt, D, dp, swizzle):
+    """Lanes that read their 16-byte vectors pairwise swapped (to spread LDS
+    banks) must give the same bits, on the LDS path and on the global path
+    (margin 1 sends most waves there)."""
+    s = Shape(2, 27, 35, 2 * D, 2)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=swizzle + D)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS)
+    for margin in (1, 3):
+        plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin,
+                       tile_swizzle=swizzle)
+        say(f"vector order: swizzle {swizzle} margin {margin} {dt} D={D}: {plan.info()}")
+        check_against_oracle(gpu_forward(plan, inp, dt), y_or, dt,
+                             f"swizzle {swizzle} margin {margin}")
+
+
 @pytest.mark.parametrize("groups, pad", [(1, 0), (2, 1), (4, 0), (4, 1)])
 def test_tiled_kernel_group_chunks(groups, pad):
     w = WORKLOADS["ldm_unet_block_bf16"].with_(N=1, H=29, W=33, C=128, G=8)
