@@ -20,6 +20,7 @@ GPU (images are independent; see the design doc for how the batch would shard).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -32,6 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+# VALU lane-operations per second without packed fp32: 256 CUs x 64 lanes
+# (4 SIMD16 per CU) x 2.4 GHz
+VALU_PEAK_GOPS = 256 * 64 * 2.4
 
 
 def kernel_source_digest() -> str:
@@ -157,6 +161,8 @@ def main():
     achieved = ideal / (kern_ms * 1e-3) / 1e9
     out_pix = w.N * Ho * Wo
     traffic = load_traffic(name, ideal)
+    alu_ops_per_out = 4 * w.kh * w.kw * (1 if w.dtype == "f32" else 2)
+    alu_gops = alu_ops_per_out * out_pix * w.C / (kern_ms * 1e-3) / 1e9
 
     line = {
         "metric": "DCNv4 fwd GB/s (ideal bytes) and % of HBM peak; output pixels/sec",
@@ -189,6 +195,12 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        # the second bound of this path: per output element, 4K fma and, for
+        # 16-bit inputs, 4K widenings to fp32 (one per corner value)
+        "roofline_alu": {"bound": "alu", "achieved": round(alu_gops, 1),
+                         "peak": round(VALU_PEAK_GOPS, 1), "unit": "Gop/s",
+                         "frac": round(alu_gops / VALU_PEAK_GOPS, 4),
+                         "ops_per_output": alu_ops_per_out},
         "kernel_source": kernel_source_digest(),
     }
 
@@ -210,9 +222,22 @@ def copy_reference(torch, mib, steps):
                       "steps": steps}), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, Ho, Wo, inp, reps):
     """The CPU oracle as it stands (fp32 evaluation, OpenMP over output
-    pixels) on the host cores, on the same batch the first input set holds."""
+    pixels) on the host cores: the full batch of the first input set on every
+    core the process may use, and its first image on one core."""
+    import numpy as np
     import oracle
     from oracle import Shape
     o = oracle.get()
@@ -222,18 +247,30 @@ def cpu_baseline(w, Ho, Wo, inp, reps):
     env_t = os.environ.get("OMP_NUM_THREADS")
     if env_t and env_t.isdigit():
         threads = min(threads, int(env_t))
-    times = []
-    for _ in range(reps):
-        t = time.perf_counter()
-        o.forward_f32(s, w.dtype, inp.x, inp.om, inp.scales, nthreads=threads)
-        times.append(time.perf_counter() - t)
-    med = statistics.median(times)
+
+    def timed(shape, x, om, nthreads):
+        times = []
+        for _ in range(reps):
+            t = time.perf_counter()
+            o.forward_f32(shape, w.dtype, x, om, inp.scales, nthreads=nthreads)
+            times.append(time.perf_counter() - t)
+        return statistics.median(times)
+
+    med = timed(s, inp.x, inp.om, threads)
     ideal = o.ideal_bytes(s, w.dtype)
+    s1 = dataclasses.replace(s, N=1)
+    med1 = timed(s1, np.ascontiguousarray(inp.x[:1]), np.ascontiguousarray(inp.om[:1]), 1)
+    ideal1 = o.ideal_bytes(s1, w.dtype)
     return {"value": round(ideal / med / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the full batch ({w.N} images), median of {reps} runs, "
-                      f"{med:.2f} s each, fp32 evaluation",
-            "output_pixels_per_s": round(w.N * Ho * Wo / med, 1)}
+            "sample": f"the full batch ({w.N} images) on {threads} threads, median of "
+                      f"{reps} runs of {med:.2f} s; one image on 1 thread, median of "
+                      f"{reps} runs of {med1:.2f} s; fp32 evaluation",
+            "output_pixels_per_s": round(w.N * Ho * Wo / med, 1),
+            "outputs_per_s": round(w.N * Ho * Wo * w.C / med, 1),
+            "single_thread": {"value": round(ideal1 / med1 / 1e9, 4), "unit": "GB/s",
+                              "output_pixels_per_s": round(Ho * Wo / med1, 1)},
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":
