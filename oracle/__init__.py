@@ -38,7 +38,9 @@ class _Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("N", "H", "W", "C", "G", "kh", "kw", "sh", "sw", "ph", "pw",
                  "dh", "dw")] + [("offset_scale", ctypes.c_float),
-                                 ("multiscale", ctypes.c_int32)]
+                                 ("multiscale", ctypes.c_int32),
+                                 ("pixel_scales", ctypes.c_int32),
+                                 ("max_scale", ctypes.c_float)]
 
 
 @dataclass(frozen=True)
@@ -59,6 +61,8 @@ class Shape:
     dw: int = 1
     offset_scale: float = 1.0
     multiscale: bool = False
+    pixel_scales: bool = False   # FlowDCN predicted scale per (pixel, group)
+    max_scale: float = 0.0       # > 0: Smax clamp of the effective scale
 
     @property
     def K(self) -> int:
@@ -67,7 +71,8 @@ class Shape:
     def c_struct(self) -> _Shape:
         return _Shape(self.N, self.H, self.W, self.C, self.G, self.kh, self.kw,
                       self.sh, self.sw, self.ph, self.pw, self.dh, self.dw,
-                      float(self.offset_scale), int(bool(self.multiscale)))
+                      float(self.offset_scale), int(bool(self.multiscale)),
+                      int(bool(self.pixel_scales)), float(self.max_scale))
 
 
 class Oracle:
@@ -83,13 +88,13 @@ class Oracle:
         i64p = ctypes.POINTER(ctypes.c_int64)
         sp = ctypes.POINTER(_Shape)
         lib.dcn4o_check.argtypes = [sp, i32p, i32p]
-        lib.dcn4o_forward_f64.argtypes = [sp, ctypes.c_int, P, P, P, P, P,
+        lib.dcn4o_forward_f64.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P,
                                           ctypes.c_int64, ctypes.c_int]
-        lib.dcn4o_forward_f32.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P,
+        lib.dcn4o_forward_f32.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P,
                                           ctypes.c_int64, ctypes.c_int]
-        lib.dcn4o_geometry.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P,
+        lib.dcn4o_geometry.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P,
                                        P, ctypes.c_int64]
-        lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, i64p, i64p]
+        lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, P, i64p, i64p]
         lib.dcn4o_ideal_bytes.argtypes = [sp, ctypes.c_int]
         lib.dcn4o_ideal_bytes.restype = ctypes.c_int64
         for f in ("dcn4o_bf16_to_f32", "dcn4o_f16_to_f32"):
@@ -120,7 +125,7 @@ class Oracle:
             raise ValueError(f"invalid shape {s}")
         return ho.value, wo.value
 
-    def _prep(self, s, dtype, x, om, scales):
+    def _prep(self, s, dtype, x, om, scales, pscales=None):
         dt = DTYPE_CODES[dtype]
         raw = RAW_NP[dt]
         x = None if x is None else np.ascontiguousarray(x, dtype=raw)
@@ -130,30 +135,38 @@ class Oracle:
             assert scales.size == s.G
         else:
             scales = None
-        return dt, x, om, scales
+        if s.pixel_scales:
+            ho, wo = self.out_size(s)
+            pscales = np.ascontiguousarray(pscales, dtype=np.float32)
+            assert pscales.size == s.N * ho * wo * s.G
+        else:
+            pscales = None
+        return dt, x, om, scales, pscales
 
     # -- the oracle ---------------------------------------------------------
     def forward_f64(self, s: Shape, dtype: str, x, om, scales=None, pix=None,
-                    nthreads: int = 8) -> np.ndarray:
-        """The definition in fp64; returns [N,Ho,Wo,C] (or [npix,C])."""
-        dt, x, om, scales = self._prep(s, dtype, x, om, scales)
+                    nthreads: int = 8, pscales=None) -> np.ndarray:
+        """The definition in fp64; returns [N,Ho,Wo,C] (or [npix,C]).
+        pscales: [N,Ho,Wo,G] fp32 when s.pixel_scales."""
+        dt, x, om, scales, pscales = self._prep(s, dtype, x, om, scales, pscales)
         ho, wo = self.out_size(s)
         pix, npix = self._pix(pix)
         shape = (s.N, ho, wo, s.C) if pix is None else (npix, s.C)
         y = np.empty(shape, np.float64)
         r = self.lib.dcn4o_forward_f64(ctypes.byref(s.c_struct()), dt,
                                        self._ptr(x), self._ptr(om),
-                                       self._ptr(scales), self._ptr(y),
+                                       self._ptr(scales), self._ptr(pscales),
+                                       self._ptr(y),
                                        self._ptr(pix), npix, nthreads)
         if r:
             raise ValueError("oracle rejected the call")
         return y
 
     def forward_f32(self, s: Shape, dtype: str, x, om, scales=None, pix=None,
-                    nthreads: int = 8, want_acc: bool = False):
+                    nthreads: int = 8, want_acc: bool = False, pscales=None):
         """fp32 evaluation in the fixed order; returns the output in the I/O
         dtype's raw encoding (and the fp32 accumulators if asked)."""
-        dt, x, om, scales = self._prep(s, dtype, x, om, scales)
+        dt, x, om, scales, pscales = self._prep(s, dtype, x, om, scales, pscales)
         ho, wo = self.out_size(s)
         pix, npix = self._pix(pix)
         shape = (s.N, ho, wo, s.C) if pix is None else (npix, s.C)
@@ -161,16 +174,17 @@ class Oracle:
         acc = np.empty(shape, np.float32) if want_acc else None
         r = self.lib.dcn4o_forward_f32(ctypes.byref(s.c_struct()), dt,
                                        self._ptr(x), self._ptr(om),
-                                       self._ptr(scales), self._ptr(y),
+                                       self._ptr(scales), self._ptr(pscales),
+                                       self._ptr(y),
                                        self._ptr(acc), self._ptr(pix), npix,
                                        nthreads)
         if r:
             raise ValueError("oracle rejected the call")
         return (y, acc) if want_acc else y
 
-    def geometry(self, s: Shape, dtype: str, om, scales=None, pix=None):
+    def geometry(self, s: Shape, dtype: str, om, scales=None, pix=None, pscales=None):
         """Per (pixel, g, k): dict of inside, y0, x0, lh, lw arrays."""
-        dt, _, om, scales = self._prep(s, dtype, None, om, scales)
+        dt, _, om, scales, pscales = self._prep(s, dtype, None, om, scales, pscales)
         ho, wo = self.out_size(s)
         pix, npix = self._pix(pix)
         npx = s.N * ho * wo if pix is None else npix
@@ -180,6 +194,7 @@ class Oracle:
                    inside=np.empty(n, np.uint8))
         r = self.lib.dcn4o_geometry(ctypes.byref(s.c_struct()), dt,
                                     self._ptr(om), self._ptr(scales),
+                                    self._ptr(pscales),
                                     *(self._ptr(out[k]) for k in
                                       ("y0", "x0", "lh", "lw", "inside")),
                                     self._ptr(pix), npix)
@@ -187,11 +202,12 @@ class Oracle:
             raise ValueError("oracle rejected the call")
         return out
 
-    def count_terms(self, s: Shape, dtype: str, om, scales=None):
-        dt, _, om, scales = self._prep(s, dtype, None, om, scales)
+    def count_terms(self, s: Shape, dtype: str, om, scales=None, pscales=None):
+        dt, _, om, scales, pscales = self._prep(s, dtype, None, om, scales, pscales)
         a, b = ctypes.c_int64(), ctypes.c_int64()
         r = self.lib.dcn4o_count_terms(ctypes.byref(s.c_struct()), dt,
                                        self._ptr(om), self._ptr(scales),
+                                       self._ptr(pscales),
                                        ctypes.byref(a), ctypes.byref(b))
         if r:
             raise ValueError("oracle rejected the call")

@@ -28,6 +28,14 @@
  *  R6 multi-scale centre: centre = yo*sh - ph + (kh-1)/2, grid_k = i - (kh-1)/2
  *     (odd kernels, dilation 1, offset_scale 1);
  *  R7 the offset/weight tensor has the I/O dtype, scales are fp32;
+ *  R13 FlowDCN's predicted scale ([FlowDCN] 3.1 splits the deformation into
+ *     a predicted scale and a predicted direction, each from its own linear
+ *     layer, on top of the per-group prior s_g; 3.3 bounds the scale by a
+ *     per-resolution maximum Smax; the formulas were lost): the effective
+ *     scale of group g at output pixel p is S = s_g * sigma[p, g], sigma an
+ *     fp32 input [N, Ho, Wo, G] (whatever activation the model applies comes
+ *     before it), replaced by Smax when it is larger (max_scale > 0; a NaN S
+ *     stays NaN); fp32 order: S = fl(s_g * sigma), then the clamp;
  *  R8 fp32 evaluation order (dcn4o_forward_f32): the location is kept as an
  *     exact integer part and a fraction.  The displacement from the integer
  *     base is t = fl(offset_scale*delta) (multi-scale: t = fl(s_g * fl(grid +
@@ -145,6 +153,8 @@ int dcn4o_check(const dcn4o_shape* s, int32_t* Ho, int32_t* Wo) {
     if (!(s->kh & 1) || !(s->kw & 1)) return -1;
     if (s->dh != 1 || s->dw != 1 || s->offset_scale != 1.0f) return -1;
   }
+  if (s->pixel_scales && !s->multiscale) return -1;
+  if (!(s->max_scale >= 0.0f)) return -1; /* negative or NaN */
   /* R2: standard convolution output arithmetic */
   int64_t ho = ((int64_t)s->H + 2 * s->ph - (int64_t)s->dh * (s->kh - 1) - 1);
   int64_t wo = ((int64_t)s->W + 2 * s->pw - (int64_t)s->dw * (s->kw - 1) - 1);
@@ -165,6 +175,7 @@ int64_t dcn4o_ideal_bytes(const dcn4o_shape* s, int dtype) {
   int64_t om = (int64_t)s->N * Ho * Wo * s->G * 3 * K;
   int64_t b = (in + out + om) * dtype_bytes(dtype);
   if (s->multiscale) b += 4 * (int64_t)s->G;
+  if (s->pixel_scales) b += 4 * (int64_t)s->N * Ho * Wo * s->G;
   return b;
 }
 
@@ -190,6 +201,27 @@ static double bilinear_zero_pad(const dcn4o_shape* s, int dtype, const void* x,
     }
   }
   return v;
+}
+
+/* R13: effective scale of group g at flat output pixel p.  Without pixel
+ * scales it is s_g; a clamp applies whenever max_scale > 0.  The comparison
+ * is false for NaN, so a NaN scale stays NaN. */
+static double scale_f64(const dcn4o_shape* s, const float* scales,
+                        const float* pscales, int64_t p, int g) {
+  if (!s->multiscale) return 1.0;
+  double S = (double)scales[g];
+  if (s->pixel_scales) S = S * (double)pscales[p * s->G + g];
+  if (s->max_scale > 0.0f && S > (double)s->max_scale) S = (double)s->max_scale;
+  return S;
+}
+
+static float scale_f32(const dcn4o_shape* s, const float* scales,
+                       const float* pscales, int64_t p, int g) {
+  if (!s->multiscale) return 1.0f;
+  float S = scales[g];
+  if (s->pixel_scales) S = S * pscales[p * s->G + g];
+  if (s->max_scale > 0.0f && S > s->max_scale) S = s->max_scale;
+  return S;
 }
 
 /* sample location of point k=(i,j) of group g at output (yo, xo), fp64 */
@@ -222,8 +254,8 @@ static int resolve_pixels(const dcn4o_shape* s, int32_t Ho, int32_t Wo,
 }
 
 int dcn4o_forward_f64(const dcn4o_shape* s, int dtype, const void* x,
-                      const void* om, const float* scales, double* y,
-                      const int64_t* pix, int64_t npix, int nthreads) {
+                      const void* om, const float* scales, const float* pscales,
+                      double* y, const int64_t* pix, int64_t npix, int nthreads) {
   int32_t Ho, Wo;
   int64_t count;
   if (dcn4o_check(s, &Ho, &Wo)) return -1;
@@ -238,7 +270,7 @@ int dcn4o_forward_f64(const dcn4o_shape* s, int dtype, const void* x,
     int xo = (int)(p % Wo);
     for (int g = 0; g < G; ++g) {
       const int64_t row = (p * G + g) * 3 * K; /* R4 */
-      double sg = s->multiscale ? (double)scales[g] : 1.0;
+      double sg = scale_f64(s, scales, pscales, p, g);
       for (int d = 0; d < D; ++d) {
         int c = g * D + d;
         double acc = 0.0;
@@ -261,8 +293,8 @@ int dcn4o_forward_f64(const dcn4o_shape* s, int dtype, const void* x,
 }
 
 int dcn4o_count_terms(const dcn4o_shape* s, int dtype, const void* om,
-                      const float* scales, int64_t* corner_terms,
-                      int64_t* inbounds_terms) {
+                      const float* scales, const float* pscales,
+                      int64_t* corner_terms, int64_t* inbounds_terms) {
   int32_t Ho, Wo;
   if (dcn4o_check(s, &Ho, &Wo)) return -1;
   const int K = s->kh * s->kw, G = s->G, D = s->C / G;
@@ -274,7 +306,7 @@ int dcn4o_count_terms(const dcn4o_shape* s, int dtype, const void* om,
     int yo = (int)((p / Wo) % Ho), xo = (int)(p % Wo);
     for (int g = 0; g < G; ++g) {
       const int64_t row = (p * G + g) * 3 * K;
-      double sg = s->multiscale ? (double)scales[g] : 1.0;
+      double sg = scale_f64(s, scales, pscales, p, g);
       for (int k = 0; k < K; ++k) {
         int i = k / s->kw, j = k % s->kw;
         double dx = load_f32(dtype, om, row + 2 * k);
@@ -339,8 +371,9 @@ static geom_t sample_geometry_f32(const dcn4o_shape* s, int yo, int xo, int i,
 }
 
 int dcn4o_forward_f32(const dcn4o_shape* s, int dtype, const void* x,
-                      const void* om, const float* scales, void* y, float* acc_out,
-                      const int64_t* pix, int64_t npix, int nthreads) {
+                      const void* om, const float* scales, const float* pscales,
+                      void* y, float* acc_out, const int64_t* pix, int64_t npix,
+                      int nthreads) {
   int32_t Ho, Wo;
   int64_t count;
   if (dcn4o_check(s, &Ho, &Wo)) return -1;
@@ -356,7 +389,7 @@ int dcn4o_forward_f32(const dcn4o_shape* s, int dtype, const void* x,
     int xo = (int)(p % Wo);
     for (int g = 0; g < G; ++g) {
       const int64_t row = (p * G + g) * 3 * K;
-      float sg = s->multiscale ? scales[g] : 1.0f;
+      float sg = scale_f32(s, scales, pscales, p, g);
       for (int d = 0; d < D; ++d) {
         int c = g * D + d;
         float acc = 0.0f;
@@ -389,9 +422,9 @@ int dcn4o_forward_f32(const dcn4o_shape* s, int dtype, const void* x,
 }
 
 int dcn4o_geometry(const dcn4o_shape* s, int dtype, const void* om,
-                   const float* scales, int32_t* y0, int32_t* x0, float* lh,
-                   float* lw, uint8_t* inside, const int64_t* pix,
-                   int64_t npix) {
+                   const float* scales, const float* pscales, int32_t* y0,
+                   int32_t* x0, float* lh, float* lw, uint8_t* inside,
+                   const int64_t* pix, int64_t npix) {
   int32_t Ho, Wo;
   int64_t count;
   if (dcn4o_check(s, &Ho, &Wo)) return -1;
@@ -402,7 +435,7 @@ int dcn4o_geometry(const dcn4o_shape* s, int dtype, const void* om,
     int yo = (int)((p / Wo) % Ho), xo = (int)(p % Wo);
     for (int g = 0; g < G; ++g) {
       const int64_t row = (p * G + g) * 3 * K;
-      float sg = s->multiscale ? scales[g] : 1.0f;
+      float sg = scale_f32(s, scales, pscales, p, g);
       for (int k = 0; k < K; ++k) {
         int i = k / s->kw, j = k % s->kw;
         float dx = load_f32(dtype, om, row + 2 * k);

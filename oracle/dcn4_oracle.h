@@ -49,11 +49,14 @@ typedef struct {
   int32_t sh, sw, ph, pw, dh, dw; /* stride, zero padding, dilation           */
   float offset_scale;             /* multiplies the predicted offset (std mode)*/
   int32_t multiscale;             /* 1: FlowDCN groupwise multi-scale geometry */
+  int32_t pixel_scales;           /* 1: per-pixel scales [N,Ho,Wo,G] times s_g */
+  float max_scale;                /* > 0: clamp of the effective scale (Smax)  */
 } dcn4o_shape;
 
 /* Validates the shape and returns the output size.  0 on success, -1 if the
  * shape is invalid (non-positive size, C % G != 0, empty output, a multi-scale
- * shape with an even kernel, dilation != 1 or offset_scale != 1). */
+ * shape with an even kernel, dilation != 1 or offset_scale != 1, pixel scales
+ * without multi-scale, a negative or NaN max_scale). */
 int dcn4o_check(const dcn4o_shape* s, int32_t* Ho, int32_t* Wo);
 
 /* Element codecs (exact decode; round-to-nearest-even encode). */
@@ -64,40 +67,43 @@ uint16_t dcn4o_f32_to_f16(float f);
 
 /* The definition, evaluated in fp64 (positions, weights, products, sum).
  * x: [N,H,W,C], om: [N,Ho,Wo,G,3K] in the I/O dtype `dtype`, scales: [G] fp32
- * (multi-scale only, else ignored).  y: fp64 output.
+ * (multi-scale only, else ignored), pscales: [N,Ho,Wo,G] fp32 (pixel_scales
+ * only, else ignored).  y: fp64 output.
  * pix == NULL: all N*Ho*Wo output pixels, y is [N,Ho,Wo,C].
  * pix != NULL: only the npix listed flat pixel indices (n*Ho+yo)*Wo+xo, y is
  * [npix,C].  Returns 0 or -1 (invalid shape / pixel index). */
 int dcn4o_forward_f64(const dcn4o_shape* s, int dtype, const void* x,
-                      const void* om, const float* scales, double* y,
-                      const int64_t* pix, int64_t npix, int nthreads);
+                      const void* om, const float* scales, const float* pscales,
+                      double* y, const int64_t* pix, int64_t npix, int nthreads);
 
 /* The same sum evaluated in fp32 with a fixed operation order (the reading of
  * "fp32 accumulation"), output rounded to the I/O dtype.  `acc` (nullable)
  * receives the fp32 accumulator before rounding. */
 int dcn4o_forward_f32(const dcn4o_shape* s, int dtype, const void* x,
-                      const void* om, const float* scales, void* y, float* acc,
-                      const int64_t* pix, int64_t npix, int nthreads);
+                      const void* om, const float* scales, const float* pscales,
+                      void* y, float* acc, const int64_t* pix, int64_t npix,
+                      int nthreads);
 
 /* Sampling geometry of the fp32 evaluation, one entry per (pixel, g, k):
  * inside = the integer part of the location is in [-1,H-1]x[-1,W-1]; for
  * inside samples y0, x0 = integer parts, lh, lw = fractions (else all zero). */
 int dcn4o_geometry(const dcn4o_shape* s, int dtype, const void* om,
-                   const float* scales, int32_t* y0, int32_t* x0, float* lh,
-                   float* lw, uint8_t* inside, const int64_t* pix,
-                   int64_t npix);
+                   const float* scales, const float* pscales, int32_t* y0,
+                   int32_t* x0, float* lh, float* lw, uint8_t* inside,
+                   const int64_t* pix, int64_t npix);
 
 /* Counts gathered while running the fp64 definition over every output:
  * corner_terms = bilinear corner multiply-adds the definition contains
  * (4 per sample point per channel, padded corners included);
  * inbounds_terms = those whose corner lies inside the image. */
 int dcn4o_count_terms(const dcn4o_shape* s, int dtype, const void* om,
-                      const float* scales, int64_t* corner_terms,
-                      int64_t* inbounds_terms);
+                      const float* scales, const float* pscales,
+                      int64_t* corner_terms, int64_t* inbounds_terms);
 
 /* Ideal traffic of one forward pass in bytes: input + output feature maps
  * plus the offset/weight tensor, each read or written once, plus 4G bytes of
- * fp32 scales in multi-scale mode ([DCNv4 digest], "GPU效率的理论分析"). */
+ * fp32 scales in multi-scale mode and 4*N*Ho*Wo*G bytes of pixel scales
+ * ([DCNv4 digest], "GPU效率的理论分析"). */
 int64_t dcn4o_ideal_bytes(const dcn4o_shape* s, int dtype);
 
 #ifdef __cplusplus

@@ -43,12 +43,12 @@ def dyadic(rng, shape, lo, hi, denom):
     return (a / denom).astype(np.float32)
 
 
-def run(o, s, dtype, x, om, scales=None):
+def run(o, s, dtype, x, om, scales=None, pscales=None, pix=None):
     """(fp64 definition, fp32 evaluation decoded to float64)"""
     xr, omr = to_raw(x, dtype), to_raw(om, dtype)
-    y64 = o.forward_f64(s, dtype, xr, omr, scales, nthreads=2)
-    y32 = from_raw(o.forward_f32(s, dtype, xr, omr, scales, nthreads=2),
-                   dtype).astype(np.float64)
+    y64 = o.forward_f64(s, dtype, xr, omr, scales, pix=pix, nthreads=2, pscales=pscales)
+    y32 = from_raw(o.forward_f32(s, dtype, xr, omr, scales, pix=pix, nthreads=2,
+                                 pscales=pscales), dtype).astype(np.float64)
     return y64, y32
 
 
@@ -381,6 +381,90 @@ def pin_multiscale(o):
     exact_equal(y32[sl], want[sl], "ms affine f32")
 
 
+def pin_pixel_scales(o):
+    """FlowDCN's predicted scale times the group prior, with the Smax clamp
+    (reading R13 of [FlowDCN] 3.1 and 3.3), pinned to the group-scale mode
+    (itself pinned above) and to closed forms:
+    (a) sigma = 1 everywhere and no clamp equals the group-scale mode;
+    (b) sigma = a power of two per (pixel, group) equals, pixel by pixel, the
+        group-scale mode with scales s_g * sigma (the products are exact), so
+        a transposed [N,Ho,Wo,G] index or a dropped factor fails;
+    (c) a clamp Smax below every s_g * sigma equals the group-scale mode with
+        every scale Smax; a clamp above them all changes nothing;
+    (d) sigma = 0 puts all K samples on the centre pixel: y = (sum_k m_k) *
+        x[centre] (zero when the centre is padding);
+    (e) a NaN sigma puts that group's samples nowhere: zero output there, and
+        the clamp does not turn the NaN into Smax."""
+    rng = np.random.default_rng(21)
+    base = Shape(2, 9, 10, 8, 4, multiscale=True)
+    ps = Shape(2, 9, 10, 8, 4, multiscale=True, pixel_scales=True)
+    ho, wo = o.out_size(base)
+    K, G, D = base.K, base.G, base.C // base.G
+    P = base.N * ho * wo
+    x = dyadic(rng, (base.N, base.H, base.W, base.C), -4, 4, 8)
+    dx = dyadic(rng, (base.N, ho, wo, G, K), -1, 1, 32)
+    dy = dyadic(rng, (base.N, ho, wo, G, K), -1, 1, 32)
+    m = dyadic(rng, (base.N, ho, wo, G, K), -1, 1, 8)
+    om = pack_om(dx, dy, m)
+    sg = np.array([1.0, 1.25, 2.0, 3.5], np.float32)
+    # (a)
+    ones = np.ones((base.N, ho, wo, G), np.float32)
+    for dt in ("f32", "bf16"):
+        a64, a32 = run(o, ps, dt, x, om, sg, pscales=ones)
+        b64, b32 = run(o, base, dt, x, om, sg)
+        exact_equal(a64, b64, f"pixel scales 1 f64 {dt}")
+        exact_equal(a32, b32, f"pixel scales 1 f32 {dt}")
+    # (b)
+    e = (np.arange(P)[:, None] + 2 * np.arange(G)[None, :]) % 4 - 2
+    sig = np.ldexp(np.ones((P, G), np.float32), e).astype(np.float32)
+    a64, a32 = run(o, ps, "f32", x, om, sg, pscales=sig.reshape(base.N, ho, wo, G))
+    a64 = a64.reshape(P, base.C)
+    a32 = a32.reshape(P, base.C)
+    for p in range(P):
+        b64, b32 = run(o, base, "f32", x, om, sg * sig[p], pix=[p])
+        exact_equal(a64[p], b64[0], f"pixel {p} scales f64")
+        exact_equal(a32[p], b32[0], f"pixel {p} scales f32")
+    # (c)
+    sig = dyadic(rng, (base.N, ho, wo, G), 1, 2, 8)
+    smax = 0.75
+    lo = Shape(2, 9, 10, 8, 4, multiscale=True, pixel_scales=True, max_scale=smax)
+    a64, a32 = run(o, lo, "f32", x, om, sg, pscales=sig)
+    b64, b32 = run(o, base, "f32", x, om, np.full(G, smax, np.float32))
+    exact_equal(a64, b64, "clamp below f64")
+    exact_equal(a32, b32, "clamp below f32")
+    hi = Shape(2, 9, 10, 8, 4, multiscale=True, pixel_scales=True, max_scale=8.0)
+    a64, a32 = run(o, hi, "f32", x, om, sg, pscales=sig)
+    b64, b32 = run(o, ps, "f32", x, om, sg, pscales=sig)
+    exact_equal(a64, b64, "clamp above f64")
+    exact_equal(a32, b32, "clamp above f32")
+    # (d)
+    zero = np.zeros((base.N, ho, wo, G), np.float32)
+    a64, a32 = run(o, ps, "f32", x, om, sg, pscales=zero)
+    want = np.zeros((base.N, ho, wo, base.C))
+    msum = m.astype(np.float64).sum(-1)  # [N,ho,wo,G]
+    for n in range(base.N):
+        for yo in range(ho):
+            for xo in range(wo):
+                cy, cx = yo - base.ph + 1, xo - base.pw + 1
+                if 0 <= cy < base.H and 0 <= cx < base.W:
+                    want[n, yo, xo] = np.repeat(msum[n, yo, xo], D) * x[n, cy, cx]
+    exact_equal(a64, want, "sigma 0 f64")
+    assert np.allclose(a32, want, rtol=0, atol=1e-5), "sigma 0 f32"
+    # (e)
+    sig = np.ones((base.N, ho, wo, G), np.float32)
+    sig[0, 3, 4, 2] = np.nan
+    for shp in (ps, hi):
+        a64, a32 = run(o, shp, "f32", x, om, sg, pscales=sig)
+        b64, b32 = run(o, base, "f32", x, om, sg)
+        sl = (0, 3, 4, slice(2 * D, 3 * D))
+        exact_equal(a64[sl], np.zeros(D), "NaN sigma f64")
+        exact_equal(a32[sl], np.zeros(D), "NaN sigma f32")
+        b64[sl] = 0
+        b32[sl] = 0
+        exact_equal(a64, b64, "NaN sigma elsewhere f64")
+        exact_equal(a32, b32, "NaN sigma elsewhere f32")
+
+
 def pin_nonfinite_offsets(o):
     """A NaN or infinite offset puts the sample nowhere in the image: the
     output equals the one where that point's weight is zero."""
@@ -605,7 +689,7 @@ def pin_codecs(o):
 ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
             pin_affine_reproduction, pin_depthwise_conv, pin_zero_padding,
             pin_partition_of_unity, pin_linearity, pin_multiscale,
-            pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
+            pin_pixel_scales, pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
             pin_exact_rational, pin_geometry, pin_codecs]
 
 

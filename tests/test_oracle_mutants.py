@@ -72,6 +72,17 @@ MUTANTS = {
     "ms_scale_grid_only_f32": sub("ty = sg * uy;", "ty = sg * (float)(i - hy) + dy;"),
     "ms_centre_lost_f64": sub("*px = (double)(xo * s->sw - s->pw + hx) + sg",
                               "*px = (double)(xo * s->sw - s->pw) + sg"),
+    # predicted per-pixel scale (R13): ignored, indexed transposed, clamped
+    # the other way, or clamped with fmin (which turns a NaN into Smax)
+    "pixel_scale_ignored_f32": sub("  if (s->pixel_scales) S = S * pscales[p * s->G + g];\n  if (s->max_scale > 0.0f && S > s->max_scale)",
+                                   "  if (s->max_scale > 0.0f && S > s->max_scale)"),
+    "pixel_scale_group_dropped_f64": sub("S = S * (double)pscales[p * s->G + g];",
+                                         "S = S * (double)pscales[p * s->G];"),
+    "pixel_scale_stride_f32": sub("S = S * pscales[p * s->G + g];", "S = S * pscales[p + g];"),
+    "clamp_as_floor_f32": sub("if (s->max_scale > 0.0f && S > s->max_scale) S = s->max_scale;",
+                              "if (s->max_scale > 0.0f && S < s->max_scale) S = s->max_scale;"),
+    "clamp_fmin_f32": sub("if (s->max_scale > 0.0f && S > s->max_scale) S = s->max_scale;",
+                          "if (s->max_scale > 0.0f) S = fminf(S, s->max_scale);"),
     # group bookkeeping
     "group_channels_interleaved": sub("int c = g * D + d;", "int c = d * s->G + g;"),
     "group_row_shared": sub("const int64_t row = (p * G + g) * 3 * K;",
