@@ -96,7 +96,8 @@ def main():
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
-                   w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype)
+                   w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
+                   w.pixel_scales, w.max_scale)
     opts = {k: int(v) for k, v in (o.split("=", 1) for o in args.option)}
     plan = d4.Plan(desc, channels_per_lane=args.channels_per_lane, **opts)
     Ho, Wo = plan.Ho, plan.Wo
@@ -120,13 +121,14 @@ def main():
         if r == 0:
             host0 = inp
         sc = None if inp.scales is None else torch.from_numpy(inp.scales).to(dev)
+        ps = None if inp.pscales is None else torch.from_numpy(inp.pscales).to(dev)
         y = torch.empty(plan.out_shape(), dtype=tdt, device=dev)
-        sets.append((dev_tensor(inp.x), dev_tensor(inp.om), sc, y))
+        sets.append((dev_tensor(inp.x), dev_tensor(inp.om), sc, ps, y))
     torch.cuda.synchronize()
 
     def step(i):
-        x, om, sc, y = sets[i % nsets]
-        plan.forward(x, om, sc, out=y, stream=stream.cuda_stream)
+        x, om, sc, ps, y = sets[i % nsets]
+        plan.forward(x, om, sc, out=y, stream=stream.cuda_stream, pixel_scales=ps)
 
     for i in range(args.warmup):
         step(i)
@@ -180,7 +182,8 @@ def main():
         "config": {"workload": name, "N": w.N, "H": w.H, "W": w.W, "C": w.C,
                    "group": w.G, "kernel": [w.kh, w.kw], "stride": [w.sh, w.sw],
                    "pad": [w.ph, w.pw], "dilation": [w.dh, w.dw],
-                   "group_scales": w.multiscale, "Ho": Ho, "Wo": Wo,
+                   "group_scales": w.multiscale, "pixel_scales": w.pixel_scales,
+                   "max_scale": w.max_scale, "Ho": Ho, "Wo": Wo,
                    "ideal_bytes": ideal, "input_sets": nsets,
                    "plan": plan.info()},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -242,24 +245,25 @@ def cpu_baseline(w, Ho, Wo, inp, reps):
     from oracle import Shape
     o = oracle.get()
     s = Shape(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
-              w.dh, w.dw, w.offset_scale, w.multiscale)
+              w.dh, w.dw, w.offset_scale, w.multiscale, w.pixel_scales, w.max_scale)
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     env_t = os.environ.get("OMP_NUM_THREADS")
     if env_t and env_t.isdigit():
         threads = min(threads, int(env_t))
 
-    def timed(shape, x, om, nthreads):
+    def timed(shape, x, om, ps, nthreads):
         times = []
         for _ in range(reps):
             t = time.perf_counter()
-            o.forward_f32(shape, w.dtype, x, om, inp.scales, nthreads=nthreads)
+            o.forward_f32(shape, w.dtype, x, om, inp.scales, nthreads=nthreads, pscales=ps)
             times.append(time.perf_counter() - t)
         return statistics.median(times)
 
-    med = timed(s, inp.x, inp.om, threads)
+    med = timed(s, inp.x, inp.om, inp.pscales, threads)
     ideal = o.ideal_bytes(s, w.dtype)
     s1 = dataclasses.replace(s, N=1)
-    med1 = timed(s1, np.ascontiguousarray(inp.x[:1]), np.ascontiguousarray(inp.om[:1]), 1)
+    med1 = timed(s1, np.ascontiguousarray(inp.x[:1]), np.ascontiguousarray(inp.om[:1]),
+                 None if inp.pscales is None else np.ascontiguousarray(inp.pscales[:1]), 1)
     ideal1 = o.ideal_bytes(s1, w.dtype)
     return {"value": round(ideal / med / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",

@@ -49,7 +49,9 @@ class dcn4_desc(ctypes.Structure):
                  "stride_h", "stride_w", "pad_h", "pad_w", "dilation_h",
                  "dilation_w")] + [("offset_scale", ctypes.c_float),
                                    ("use_group_scales", ctypes.c_int32),
-                                   ("dtype", ctypes.c_int32)]
+                                   ("dtype", ctypes.c_int32),
+                                   ("use_pixel_scales", ctypes.c_int32),
+                                   ("max_scale", ctypes.c_float)]
 
 
 class dcn4_launch_info(ctypes.Structure):
@@ -86,7 +88,8 @@ _lib.dcn4_query.argtypes = [_P, ctypes.POINTER(ctypes.c_int32),
 _lib.dcn4_plan_info.argtypes = [_P, ctypes.POINTER(dcn4_launch_info)]
 _lib.dcn4_plan_set_option.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
 _lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
-_lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_forward_scaled.argtypes = [_P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_destroy.argtypes = [_P]
 _lib.dcn4_destroy.restype = None
 _lib.dcn4_status_string.argtypes = [ctypes.c_int]
@@ -94,7 +97,7 @@ _lib.dcn4_status_string.restype = ctypes.c_char_p
 _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
-           "dcn4_plan_set_option", "dcn4_forward",
+           "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
            "dcn4_probe_geometry"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -131,11 +134,18 @@ def dcn4_forward(plan, x: int, offset_mask: int, group_scales: Optional[int],
     return _lib.dcn4_forward(plan, x, offset_mask, group_scales, y, stream)
 
 
-def dcn4_probe_geometry(plan, offset_mask: int, group_scales: Optional[int],
-                        y0: int, x0: int, lh: int, lw: int, inside: int,
+def dcn4_forward_scaled(plan, x: int, offset_mask: int, group_scales: Optional[int],
+                        pixel_scales: Optional[int], y: int,
                         stream: Optional[int]) -> int:
-    return _lib.dcn4_probe_geometry(plan, offset_mask, group_scales, y0, x0,
-                                    lh, lw, inside, stream)
+    return _lib.dcn4_forward_scaled(plan, x, offset_mask, group_scales,
+                                    pixel_scales, y, stream)
+
+
+def dcn4_probe_geometry(plan, offset_mask: int, group_scales: Optional[int],
+                        pixel_scales: Optional[int], y0: int, x0: int, lh: int,
+                        lw: int, inside: int, stream: Optional[int]) -> int:
+    return _lib.dcn4_probe_geometry(plan, offset_mask, group_scales, pixel_scales,
+                                    y0, x0, lh, lw, inside, stream)
 
 
 def dcn4_destroy(plan) -> None:
@@ -176,6 +186,8 @@ class Desc:
     offset_scale: float = 1.0
     use_group_scales: bool = False
     dtype: str = "bf16"
+    use_pixel_scales: bool = False
+    max_scale: float = 0.0
 
     def c_struct(self) -> dcn4_desc:
         return dcn4_desc(self.N, self.H, self.W, self.C, self.group,
@@ -183,7 +195,8 @@ class Desc:
                          self.stride_w, self.pad_h, self.pad_w,
                          self.dilation_h, self.dilation_w,
                          float(self.offset_scale), int(bool(self.use_group_scales)),
-                         DTYPE_CODES[self.dtype])
+                         DTYPE_CODES[self.dtype], int(bool(self.use_pixel_scales)),
+                         float(self.max_scale))
 
 
 def _torch_dtype(name):
@@ -247,8 +260,9 @@ class Plan:
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
 
-    def forward(self, x, om, scales=None, out=None, stream=None):
-        """y[N,Ho,Wo,C] = DCNv4(x[N,H,W,C], om[N,Ho,Wo,G,3K], scales[G])."""
+    def forward(self, x, om, scales=None, out=None, stream=None, pixel_scales=None):
+        """y[N,Ho,Wo,C] = DCNv4(x[N,H,W,C], om[N,Ho,Wo,G,3K], scales[G],
+        pixel_scales[N,Ho,Wo,G])."""
         import torch
         d = self.desc
         dt = _torch_dtype(d.dtype)
@@ -256,12 +270,23 @@ class Plan:
         self._check(om, self.om_shape(), dt, "offset_mask")
         if scales is not None:
             self._check(scales, (d.group,), torch.float32, "group_scales")
+        if pixel_scales is not None:
+            self._check(pixel_scales, (d.N, self.Ho, self.Wo, d.group), torch.float32,
+                        "pixel_scales")
         if out is None:
             out = torch.empty(self.out_shape(), dtype=dt, device=x.device)
         else:
             self._check(out, self.out_shape(), dt, "out")
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
+        if d.use_pixel_scales or pixel_scales is not None:
+            st = dcn4_forward_scaled(self._h, x.data_ptr(), om.data_ptr(),
+                                     None if scales is None else scales.data_ptr(),
+                                     None if pixel_scales is None else pixel_scales.data_ptr(),
+                                     out.data_ptr(), stream)
+            if st != DCN4_OK:
+                raise DCN4Error(st, "dcn4_forward_scaled")
+            return out
         st = dcn4_forward(self._h, x.data_ptr(), om.data_ptr(),
                           None if scales is None else scales.data_ptr(),
                           out.data_ptr(), stream)
@@ -269,7 +294,7 @@ class Plan:
             raise DCN4Error(st, "dcn4_forward")
         return out
 
-    def probe_geometry(self, om, scales=None, stream=None):
+    def probe_geometry(self, om, scales=None, stream=None, pixel_scales=None):
         """Device geometry of every (n, yo, xo, g, k): dict of tensors."""
         import torch
         d = self.desc
@@ -285,6 +310,7 @@ class Plan:
             stream = torch.cuda.current_stream(dev).cuda_stream
         st = dcn4_probe_geometry(self._h, om.data_ptr(),
                                  None if scales is None else scales.data_ptr(),
+                                 None if pixel_scales is None else pixel_scales.data_ptr(),
                                  *(out[k].data_ptr() for k in ("y0", "x0", "lh", "lw", "inside")),
                                  stream)
         if st != DCN4_OK:

@@ -63,6 +63,11 @@ dcn4_status validate_desc(const dcn4_desc& d, int64_t* Ho, int64_t* Wo) {
       return fail(DCN4_ERR_INVALID_ARG,
                   "group-scale mode needs dilation 1 and offset_scale 1");
   }
+  if (!(d.max_scale >= 0.0f))
+    return fail(DCN4_ERR_INVALID_ARG, "max_scale must be 0 (none) or positive");
+  if ((d.use_pixel_scales || d.max_scale > 0.0f) && !d.use_group_scales)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "pixel scales and max_scale need group-scale mode");
   *Ho = out_size(d.H, d.kernel_h, d.stride_h, d.pad_h, d.dilation_h);
   *Wo = out_size(d.W, d.kernel_w, d.stride_w, d.pad_w, d.dilation_w);
   if (*Ho < 1 || *Wo < 1)
@@ -142,7 +147,8 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   const int64_t out_el = int64_t(desc->N) * pix * desc->C;
   const int64_t om_el = int64_t(desc->N) * pix * desc->group * 3 * p.K;
   p.ideal_bytes = uint64_t(in_el + out_el + om_el) * p.es +
-                  (desc->use_group_scales ? 4ull * desc->group : 0ull);
+                  (desc->use_group_scales ? 4ull * desc->group : 0ull) +
+                  (desc->use_pixel_scales ? 4ull * desc->N * pix * desc->group : 0ull);
 
   dcn4_plan* out = new (std::nothrow) dcn4_plan;
   if (!out) return fail(DCN4_ERR_NOMEM, "plan allocation failed");
@@ -256,8 +262,16 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
 }
 
 static dcn4_status check_io(const dcn4::Plan& p, const void* x, const void* om,
-                            const float* scales, const void* y, bool need_x) {
+                            const float* scales, const float* pscales,
+                            const void* y, bool need_x) {
+  if (!p.desc.use_pixel_scales && pscales)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "pixel_scales given but the plan does not use pixel scales");
   if (p.desc.N == 0) return DCN4_OK;
+  if (p.desc.use_pixel_scales && !pscales)
+    return fail(DCN4_ERR_NULL, "pixel_scales is required by this plan");
+  if (pscales && !aligned_to(pscales, 4))
+    return fail(DCN4_ERR_MISALIGNED, "pixel_scales not 4-byte aligned");
   if ((need_x && (!x || !y)) || !om)
     return fail(DCN4_ERR_NULL, "x, offset_mask and y must not be NULL");
   if (p.desc.use_group_scales && !scales)
@@ -273,36 +287,51 @@ static dcn4_status check_io(const dcn4::Plan& p, const void* x, const void* om,
   return DCN4_OK;
 }
 
-dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
-                         const void* offset_mask, const float* group_scales,
-                         void* y, void* stream) {
+dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
+                                const void* offset_mask,
+                                const float* group_scales,
+                                const float* pixel_scales, void* y,
+                                void* stream) {
   if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
   const dcn4::Plan& p = plan->p;
-  dcn4_status s = check_io(p, x, offset_mask, group_scales, y, true);
+  dcn4_status s = check_io(p, x, offset_mask, group_scales, pixel_scales, y, true);
   if (s != DCN4_OK || p.desc.N == 0) return s;
   const bool vector_path = p.dp > 0 && aligned_to(x, 16) &&
                            aligned_to(offset_mask, 16) && aligned_to(y, 16);
   if (vector_path && p.tile.ok)
     s = dcn4::launch_tiled(p, x, offset_mask, group_scales, y, stream);
   else
-    s = dcn4::launch_forward(p, x, offset_mask, group_scales, y, stream, vector_path);
+    s = dcn4::launch_forward(p, x, offset_mask, group_scales, pixel_scales, y,
+                             stream, vector_path);
   if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
   return DCN4_OK;
 }
 
+dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
+                         const void* offset_mask, const float* group_scales,
+                         void* y, void* stream) {
+  if (plan && plan->p.desc.use_pixel_scales)
+    return fail(DCN4_ERR_INVALID_ARG,
+                "the plan takes pixel scales: call dcn4_forward_scaled");
+  return dcn4_forward_scaled(plan, x, offset_mask, group_scales, nullptr, y, stream);
+}
+
 dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
-                                const float* group_scales, int32_t* y0,
+                                const float* group_scales,
+                                const float* pixel_scales, int32_t* y0,
                                 int32_t* x0, float* lh, float* lw,
                                 uint8_t* inside, void* stream) {
   if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
   const dcn4::Plan& p = plan->p;
-  dcn4_status s = check_io(p, nullptr, offset_mask, group_scales, nullptr, false);
+  dcn4_status s = check_io(p, nullptr, offset_mask, group_scales, pixel_scales,
+                           nullptr, false);
   if (s != DCN4_OK || p.desc.N == 0) return s;
   if (!y0 || !x0 || !lh || !lw || !inside)
     return fail(DCN4_ERR_NULL, "probe outputs must not be NULL");
   if (!aligned_to(y0, 4) || !aligned_to(x0, 4) || !aligned_to(lh, 4) || !aligned_to(lw, 4))
     return fail(DCN4_ERR_MISALIGNED, "probe outputs must be 4-byte aligned");
-  s = dcn4::launch_probe(p, offset_mask, group_scales, y0, x0, lh, lw, inside, stream);
+  s = dcn4::launch_probe(p, offset_mask, group_scales, pixel_scales, y0, x0, lh, lw,
+                         inside, stream);
   if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
   return DCN4_OK;
 }

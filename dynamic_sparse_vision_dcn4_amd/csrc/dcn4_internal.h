@@ -40,6 +40,8 @@ struct FwdArgs {
   const char* x;         // input of this launch's first image
   const char* om;        // offset/weight tensor of this launch's first image
   const float* scales;   // [G] fp32 (group-scale mode)
+  const float* pscales;  // [pixels, G] fp32 of this launch, or null
+  float max_scale;       // > 0: clamp of the effective group scale
   char* y;               // output of this launch's first image
   int32_t H, W, C, G, D, Ho, Wo;
   int32_t kh, kw, sh, sw, ph, pw, dh, dw;
@@ -118,13 +120,13 @@ void resolve_tile(Plan& p);
 // Kernel-side entry points (dcn4_kernels.hip).  Arguments are validated by
 // the caller; these only shape and enqueue the launches.
 dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
-                           const float* scales, void* y, void* stream,
-                           bool vector_path);
+                           const float* scales, const float* pscales, void* y,
+                           void* stream, bool vector_path);
 dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
                          const float* scales, void* y, void* stream);
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
-                         int32_t* y0, int32_t* x0, float* lh, float* lw,
-                         uint8_t* inside, void* stream);
+                         const float* pscales, int32_t* y0, int32_t* x0,
+                         float* lh, float* lw, uint8_t* inside, void* stream);
 // Text of the last HIP error a launch reported on this thread.
 const char* last_hip_error();
 // LDS bytes one forward workgroup of `block` lanes stages (the offset/weight

@@ -173,6 +173,18 @@ __device__ __forceinline__ Cell locate(Loc l, float Hm1, float Wm1) {
   return c;
 }
 
+// Group-scale mode: the scale of group g at output pixel p (counted from the
+// launch's first image): the group prior s_g, times the predicted scale of
+// ([FlowDCN] 3.1) when the plan has pixel scales, replaced by the maximum
+// scale ([FlowDCN] 3.3) when larger; the comparison is false for NaN, so a NaN
+// scale stays NaN and its samples land nowhere.
+__device__ __forceinline__ float group_scale(const FwdArgs& a, uint64_t p, uint32_t g) {
+  float S = a.scales[g];
+  if (a.pscales) S = S * a.pscales[p * (uint32_t)a.G + g];
+  if (a.max_scale > 0.0f && S > a.max_scale) S = a.max_scale;
+  return S;
+}
+
 // XCD-aware workgroup order: hardware id b runs on XCD b % 8; XCD x gets the
 // contiguous logical range [start_x, start_x + count_x).
 __device__ __forceinline__ int xcd_block(int b, int nb) {
@@ -365,7 +377,7 @@ void dcn4_forward_kernel(FwdArgs a) {
   t.pix_bytes = (uint32_t)a.C * es;
   t.row_stride = (uint32_t)a.W * t.pix_bytes;
   t.lane_bytes = (n - n_first) * a.img_bytes + (g * (uint32_t)a.D + l * DP) * es;
-  t.sg = (MODE == kGroupScale) ? a.scales[g] : 1.0f;
+  t.sg = (MODE == kGroupScale) ? group_scale(a, p, g) : 1.0f;
   t.hy = ((KS ? KS : a.kh) - 1) >> 1;
   t.hx = ((KS ? KS : a.kw) - 1) >> 1;
   t.by0 = (int)yo * a.sh - a.ph + (MODE == kGroupScale ? t.hy : 0);
@@ -793,7 +805,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_probe_kernel(
       reinterpret_cast<const typename io::raw*>(a.om) + (p * a.G + g) * (3 * K);
   const float dx = io::dec(om[2 * k]);
   const float dy = io::dec(om[2 * k + 1]);
-  const float sg = (MODE == kGroupScale) ? a.scales[g] : 1.0f;
+  const float sg = (MODE == kGroupScale) ? group_scale(a, (uint64_t)p, (uint32_t)g) : 1.0f;
   const int hy = (a.kh - 1) >> 1, hx = (a.kw - 1) >> 1;
   float by, bx, gy = 0.0f, gx = 0.0f;
   if (MODE == kGroupScale) {
@@ -860,6 +872,7 @@ void fill_common(const Plan& p, FwdArgs& a) {
   a.kh = d.kernel_h; a.kw = d.kernel_w; a.sh = d.stride_h; a.sw = d.stride_w;
   a.ph = d.pad_h; a.pw = d.pad_w; a.dh = d.dilation_h; a.dw = d.dilation_w;
   a.offset_scale = d.offset_scale;
+  a.max_scale = d.use_group_scales ? d.max_scale : 0.0f;
   a.Hm1 = (float)(d.H - 1);
   a.Wm1 = (float)(d.W - 1);
   a.rowel = d.group * 3 * p.K;
@@ -923,8 +936,8 @@ int32_t forward_block(const Plan& p, int32_t lanes_per_group) {
 }
 
 dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
-                           const float* scales, void* y, void* stream,
-                           bool vector_path) {
+                           const float* scales, const float* pscales, void* y,
+                           void* stream, bool vector_path) {
   const dcn4_desc& d = p.desc;
   const int dp = vector_path ? p.dp : 1;
   const int L = p.D / dp;
@@ -937,6 +950,7 @@ dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
   fill_common(p, a);
   a.scales = scales;
   a.L = L;
+  const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;  // pixel scales per image
   a.ipp = d.group * L;
   a.div_ipp = make_fastdiv((uint32_t)a.ipp);
   a.div_L = make_fastdiv((uint32_t)L);
@@ -948,6 +962,7 @@ dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
     a.x = static_cast<const char*>(x) + n0 * x_img;
     a.om = static_cast<const char*>(om) + n0 * om_img;
     a.y = static_cast<char*>(y) + n0 * y_img;
+    a.pscales = pscales ? pscales + n0 * ps_img : nullptr;
     a.x_bytes = nb * x_img;
     a.om_bytes = nb * om_img;
     a.total_items = (int32_t)((int64_t)nb * p.Ho * p.Wo * a.ipp);
@@ -1104,12 +1119,13 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
 }
 
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
-                         int32_t* y0, int32_t* x0, float* lh, float* lw,
-                         uint8_t* inside, void* stream) {
+                         const float* pscales, int32_t* y0, int32_t* x0,
+                         float* lh, float* lw, uint8_t* inside, void* stream) {
   FwdArgs a{};
   fill_common(p, a);
   a.om = static_cast<const char*>(om);
   a.scales = scales;
+  a.pscales = pscales;
   const int64_t count = (int64_t)p.desc.N * p.Ho * p.Wo * p.desc.group * p.K;
   if (count == 0) return DCN4_OK;
   const int64_t blocks = (count + kBlock - 1) / kBlock;

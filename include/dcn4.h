@@ -19,9 +19,13 @@
  *   standard mode:    row = yo*stride_h - pad_h + i*dilation_h
  *                           + offset_scale*dy_k,   (col likewise with dx_k)
  *   group-scale mode: row = yo*stride_h - pad_h + (kernel_h-1)/2
- *                           + s_g*((i - (kernel_h-1)/2) + dy_k)
+ *                           + S*((i - (kernel_h-1)/2) + dy_k)
  *                     (FlowDCN groupwise multi-scale, [FlowDCN] 3.1; odd
- *                     kernels, dilation 1, offset_scale 1)
+ *                     kernels, dilation 1, offset_scale 1), where the scale
+ *                     S = s_g, or with pixel scales S = s_g*sigma[n,yo,xo,g]
+ *                     (the predicted scale of [FlowDCN] 3.1), and with
+ *                     max_scale > 0 the smaller of S and max_scale (the
+ *                     maximum scale Smax of [FlowDCN] 3.3; a NaN S stays NaN)
  * and y = sum_k m_k * bilinear(x, row, col).  The base location is the
  * convolution index of [CANN Conv2D] 2.1 with padding and dilation; the
  * output size is Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
@@ -29,7 +33,8 @@
  *
  * Arithmetic: fp32 throughout.  Per sample the location is an exact integer
  * part plus a fraction: t = fl(offset_scale*d) (group-scale mode:
- * fl(s_g*fl(grid + d)), measured from the integer centre); f = floor(t);
+ * fl(S*fl(grid + d)), measured from the integer centre, with
+ * S = fl(s_g*sigma) before the clamp); f = floor(t);
  * lh = fl(t - f); y0 = base + f (exact); the sample is skipped unless
  * -1 <= y0 <= H-1 and -1 <= x0 <= W-1 (a NaN displacement fails the test);
  * hh = 1 - lh (same for x); corner weights hh*hw, hh*lw, lh*hw, lh*lw for
@@ -47,6 +52,7 @@
  *                                      tensor a merged offset/weight linear
  *                                      layer emits ([DCNv4 digest] "方法3").
  *   group_scales [G]                   fp32, group-scale mode only
+ *   pixel_scales [N, Ho, Wo, G]        fp32, plans with use_pixel_scales only
  *   y            [N, Ho, Wo, C]        I/O dtype
  *
  * Ownership and execution: the caller owns every buffer and the stream.  All
@@ -92,7 +98,9 @@ typedef enum {
  * C % group == 0; kernel, stride, dilation >= 1; pad >= 0; the output size is
  * at least 1x1; H, W, pads, strides and dilation*kernel <= 2^20; offset_scale
  * finite.  With use_group_scales != 0 the kernel sizes must be odd and
- * dilation and offset_scale must be 1. */
+ * dilation and offset_scale must be 1.  use_pixel_scales and a non-zero
+ * max_scale need use_group_scales; max_scale must be 0 (no clamp) or a
+ * positive number (+inf allowed). */
 typedef struct {
   int32_t N, H, W, C, group;
   int32_t kernel_h, kernel_w;
@@ -102,6 +110,8 @@ typedef struct {
   float offset_scale;       /* multiplies (dx, dy) in standard mode        */
   int32_t use_group_scales; /* 1: FlowDCN groupwise multi-scale geometry   */
   int32_t dtype;            /* dcn4_dtype of x, offset_mask and y          */
+  int32_t use_pixel_scales; /* 1: per-pixel predicted scales times s_g     */
+  float max_scale;          /* > 0: clamp of the effective scale; 0: none  */
 } dcn4_desc;
 
 typedef struct dcn4_plan dcn4_plan; /* opaque, immutable after creation */
@@ -114,7 +124,8 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan);
 
 /* Output size and the ideal traffic of one forward pass in bytes: input and
  * output once, the offset/weight tensor once, plus 4G bytes of scales in
- * group-scale mode (the 2HWC + 27HWG element model of [DCNv4 digest]
+ * group-scale mode and 4*N*Ho*Wo*G bytes of pixel scales when the plan uses
+ * them (the 2HWC + 27HWG element model of [DCNv4 digest]
  * "GPU效率的理论分析", with input and output at their own sizes).  Any output
  * pointer may be NULL.  Errors: DCN4_ERR_NULL (plan NULL). */
 dcn4_status dcn4_query(const dcn4_plan* plan, int32_t* Ho, int32_t* Wo,
@@ -172,19 +183,34 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
  * D*es is a multiple of 16 the vectorised kernel runs, otherwise an
  * element-wise kernel computes the identical result.  N == 0 enqueues
  * nothing.  Errors: DCN4_ERR_NULL, DCN4_ERR_MISALIGNED, DCN4_ERR_INVALID_ARG
- * (scales given or missing against the plan's mode), DCN4_ERR_HIP. */
+ * (scales given or missing against the plan's mode, or a plan that takes
+ * pixel scales: those run through dcn4_forward_scaled), DCN4_ERR_HIP. */
 dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
                          const void* offset_mask, const float* group_scales,
                          void* y, void* stream);
+
+/* The forward pass of a plan with FlowDCN's predicted per-pixel scales
+ * ([FlowDCN] 3.1: the deformation split into a predicted scale and a
+ * predicted direction; 3.3: the maximum scale Smax): pixel_scales is a device
+ * array [N, Ho, Wo, G] of fp32, 4-byte aligned, required exactly when the
+ * plan has use_pixel_scales (with NULL this is dcn4_forward).  Otherwise as
+ * dcn4_forward. */
+dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
+                                const void* offset_mask,
+                                const float* group_scales,
+                                const float* pixel_scales, void* y,
+                                void* stream);
 
 /* Test probe of the sampling geometry: for every (n, yo, xo, g, k), in that
  * order, writes inside (1 if the integer parts passed the -1 <= y0 <= H-1,
  * -1 <= x0 <= W-1 test), and for inside samples the integer parts y0, x0 and
  * the fractions lh, lw of the arithmetic above (zeros otherwise), computed
  * by the same device functions as the forward kernels.  Outputs are device
- * arrays of N*Ho*Wo*G*K entries.  Errors as dcn4_forward. */
+ * arrays of N*Ho*Wo*G*K entries; pixel_scales as in dcn4_forward_scaled.
+ * Errors as dcn4_forward_scaled. */
 dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
-                                const float* group_scales, int32_t* y0,
+                                const float* group_scales,
+                                const float* pixel_scales, int32_t* y0,
                                 int32_t* x0, float* lh, float* lw,
                                 uint8_t* inside, void* stream);
 

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
               "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
-              "dcn4_plan_info", "dcn4_plan_set_option"):
+              "dcn4_plan_info", "dcn4_plan_set_option", "dcn4_forward_scaled"):
         assert n in names
 
 
@@ -101,6 +101,7 @@ WORKLOAD_SHAPES = [
     (Shape(8, 128, 128, 320, 20), "bf16"),
     (Shape(16, 32, 32, 1280, 40, dh=2, dw=2), "f16"),
     (Shape(32, 32, 32, 1152, 16, multiscale=True), "bf16"),
+    (Shape(32, 32, 32, 1152, 16, multiscale=True, pixel_scales=True, max_scale=4.0), "bf16"),
     (Shape(3, 9, 11, 24, 3, kh=5, kw=3, sh=2, sw=1, ph=2, pw=0, dh=1, dw=2,
            offset_scale=0.5), "f32"),
 ]
@@ -108,7 +109,8 @@ WORKLOAD_SHAPES = [
 
 def desc_of(s: Shape, dt: str) -> d4.Desc:
     return d4.Desc(s.N, s.H, s.W, s.C, s.G, s.kh, s.kw, s.sh, s.sw, s.ph, s.pw,
-                   s.dh, s.dw, s.offset_scale, s.multiscale, dt)
+                   s.dh, s.dw, s.offset_scale, s.multiscale, dt, s.pixel_scales,
+                   s.max_scale)
 
 
 @pytest.mark.parametrize("s, dt", WORKLOAD_SHAPES)
@@ -241,15 +243,47 @@ class TestForwardValidation:
 
     def test_probe(self):
         h = self.p.handle
-        assert d4.dcn4_probe_geometry(h, 256, None, None, 256, 256, 256, 256, None) == d4.DCN4_ERR_NULL
-        assert d4.dcn4_probe_geometry(h, 256, None, 258, 256, 256, 256, 256, None) == d4.DCN4_ERR_MISALIGNED
-        assert d4.dcn4_probe_geometry(h, None, None, 256, 256, 256, 256, 256, None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_probe_geometry(h, 256, None, None, None, 256, 256, 256, 256, None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_probe_geometry(h, 256, None, None, 258, 256, 256, 256, 256, None) == d4.DCN4_ERR_MISALIGNED
+        assert d4.dcn4_probe_geometry(h, None, None, None, 256, 256, 256, 256, 256, None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_probe_geometry(h, 256, None, 1024, 256, 256, 256, 256, 256, None) == d4.DCN4_ERR_INVALID_ARG
+
+    def test_pixel_scales(self):
+        ps = d4.Plan(mk(use_group_scales=True, use_pixel_scales=True, max_scale=4.0))
+        # the plain entry point refuses a plan that takes pixel scales
+        assert d4.dcn4_forward(ps.handle, 256, 256, 1024, 512, None) == d4.DCN4_ERR_INVALID_ARG
+        fs = lambda p, sc, pp: d4.dcn4_forward_scaled(p.handle, 256, 256, sc, pp, 512, None)
+        assert fs(ps, 1024, None) == d4.DCN4_ERR_NULL
+        assert fs(ps, 1024, 2050) == d4.DCN4_ERR_MISALIGNED
+        assert fs(self.ms, 1024, 2048) == d4.DCN4_ERR_INVALID_ARG
+        assert fs(self.p, None, 2048) == d4.DCN4_ERR_INVALID_ARG
 
     def test_empty_batch_is_a_no_op(self):
         p0 = d4.Plan(mk(N=0))
         # nothing is enqueued, so no pointer is touched and no GPU is needed
         assert d4.dcn4_forward(p0.handle, None, None, None, None, None) == d4.DCN4_OK
         assert p0.ideal_bytes == 0
+
+
+@pytest.mark.parametrize("kw", [dict(use_pixel_scales=True),
+                                dict(max_scale=2.0),
+                                dict(use_group_scales=True, max_scale=-1.0),
+                                dict(use_group_scales=True, max_scale=float("nan"))])
+def test_create_rejects_bad_scale_settings(kw):
+    st, h = d4.dcn4_create(mk(**kw).c_struct())
+    assert st == d4.DCN4_ERR_INVALID_ARG and not h
+
+
+def test_pixel_scale_plan_sizes_match_oracle():
+    s = Shape(3, 11, 13, 64, 4, multiscale=True, pixel_scales=True, max_scale=3.0)
+    p = d4.Plan(d4.Desc(s.N, s.H, s.W, s.C, s.G, use_group_scales=True, dtype="bf16",
+                        use_pixel_scales=True, max_scale=3.0))
+    o = oracle.get()
+    assert (p.Ho, p.Wo) == o.out_size(s)
+    assert p.ideal_bytes == o.ideal_bytes(s, "bf16")
+    ho, wo = o.out_size(s)
+    plain = d4.Plan(d4.Desc(s.N, s.H, s.W, s.C, s.G, use_group_scales=True, dtype="bf16"))
+    assert p.ideal_bytes - plain.ideal_bytes == 4 * s.N * ho * wo * s.G
 
 
 def test_status_strings():

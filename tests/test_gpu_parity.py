@@ -62,12 +62,18 @@ def to_raw_np(t, dt):
 
 def desc_of(s: Shape, dt: str) -> d4.Desc:
     return d4.Desc(s.N, s.H, s.W, s.C, s.G, s.kh, s.kw, s.sh, s.sw, s.ph, s.pw,
-                   s.dh, s.dw, s.offset_scale, s.multiscale, dt)
+                   s.dh, s.dw, s.offset_scale, s.multiscale, dt, s.pixel_scales,
+                   s.max_scale)
 
 
 def shape_of(w) -> Shape:
     return Shape(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
-                 w.dh, w.dw, w.offset_scale, w.multiscale)
+                 w.dh, w.dw, w.offset_scale, w.multiscale, w.pixel_scales,
+                 w.max_scale)
+
+
+def dev_f32(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
 
 
 def gpu_forward(plan, inp, dt, offset_elems=0):
@@ -79,7 +85,7 @@ def gpu_forward(plan, inp, dt, offset_elems=0):
         buf = torch.empty(int(np.prod(plan.out_shape())) + offset_elems,
                           dtype=TORCH_DT[dt], device="cuda")
         out = buf[offset_elems:].view(plan.out_shape())
-    y = plan.forward(x, om, sc, out=out)
+    y = plan.forward(x, om, sc, out=out, pixel_scales=dev_f32(inp.pscales))
     torch.cuda.synchronize()
     return to_raw_np(y, dt)
 
@@ -197,7 +203,8 @@ def test_workload_full_size(name):
     plan = d4.Plan(desc_of(s, w.dtype))
     say(f"  plan {plan.info()}")
     y = gpu_forward(plan, inp, w.dtype)
-    y_or = o.forward_f32(s, w.dtype, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
+    y_or = o.forward_f32(s, w.dtype, inp.x, inp.om, inp.scales, nthreads=NTHREADS,
+                         pscales=inp.pscales)
     check_against_oracle(y, y_or, w.dtype, name)
     if plan.info()["kernel"] != 1:
         direct = d4.Plan(desc_of(s, w.dtype), kernel=1)
@@ -209,7 +216,7 @@ def test_workload_full_size(name):
     pix = np.unique(np.concatenate([rng.integers(0, npix, 3000),
                                     [0, npix - 1, Wo - 1, npix - Wo]]))
     y64 = o.forward_f64(s, w.dtype, inp.x, inp.om, inp.scales, pix=pix,
-                        nthreads=NTHREADS)
+                        nthreads=NTHREADS, pscales=inp.pscales)
     yg = y.reshape(npix, s.C)[pix]
     if w.dtype == "f32":
         check_fp32_gate(yg, y64, name)
@@ -220,9 +227,10 @@ def test_workload_full_size(name):
             "(includes the output rounding)")
     # geometry of the sampled pixels, bit for bit
     geo = plan.probe_geometry(to_dev(inp.om, w.dtype),
-                              None if inp.scales is None else torch.from_numpy(inp.scales).cuda())
+                              None if inp.scales is None else torch.from_numpy(inp.scales).cuda(),
+                              pixel_scales=dev_f32(inp.pscales))
     torch.cuda.synchronize()
-    ref = o.geometry(s, w.dtype, inp.om, inp.scales, pix=pix)
+    ref = o.geometry(s, w.dtype, inp.om, inp.scales, pix=pix, pscales=inp.pscales)
     GK = s.G * s.K
     sel = (pix[:, None] * GK + np.arange(GK)[None, :]).reshape(-1)
     for k in ("inside", "y0", "x0"):
@@ -230,6 +238,59 @@ def test_workload_full_size(name):
     for k in ("lh", "lw"):
         assert np.array_equal(geo[k].cpu().numpy()[sel].view(np.uint32),
                               ref[k].view(np.uint32)), k
+
+
+# ------------------------------------------------- FlowDCN predicted scale
+def pixel_scale_cases():
+    rng = np.random.default_rng(77)
+    cases = []
+    for t in range(12):
+        dt = ["bf16", "f32", "f16"][t % 3]
+        k = [3, 5, 1][t % 3]
+        D = int(rng.choice([8, 16, 24, 72]))
+        G = int(rng.integers(1, 5))
+        smax = [0.0, 2.5, 0.75][t % 3 if t < 9 else 0]
+        s = Shape(int(rng.integers(1, 3)), int(rng.integers(5, 30)), int(rng.integers(5, 30)),
+                  G * D, G, k, k, 1, 1, int(rng.integers(0, 3)), int(rng.integers(0, 3)),
+                  multiscale=True, pixel_scales=True, max_scale=smax)
+        try:
+            oracle.get().out_size(s)
+        except ValueError:
+            continue
+        cases.append((t, s, dt))
+    return cases
+
+
+@pytest.mark.parametrize("t, s, dt", pixel_scale_cases(),
+                         ids=lambda v: str(v) if isinstance(v, int) else None)
+def test_pixel_scale_parity(t, s, dt):
+    """FlowDCN's predicted per-pixel scale times the group prior, with and
+    without the Smax clamp: output and sample geometry bit for bit, including
+    a NaN and a zero predicted scale."""
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=100 + t)
+    rng = np.random.default_rng(200 + t)
+    ps = rng.uniform(0.25, 2.0, (s.N, Ho, Wo, s.G)).astype(np.float32)
+    ps.reshape(-1)[0] = np.nan
+    ps.reshape(-1)[-1] = 0.0
+    inp = workloads.Inputs(inp.x, inp.om, inp.scales, ps)
+    plan = d4.Plan(desc_of(s, dt))
+    say(f"pixel scales case {t}: {s} {dt} {plan.info()}")
+    y = gpu_forward(plan, inp, dt)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS, pscales=ps)
+    check_against_oracle(y, y_or, dt, f"pixel scales {t}")
+    if dt == "f32":
+        check_fp32_gate(y, o.forward_f64(s, dt, inp.x, inp.om, inp.scales,
+                                         nthreads=NTHREADS, pscales=ps), f"pixel scales {t}")
+    g = plan.probe_geometry(to_dev(inp.om, dt), torch.from_numpy(inp.scales).cuda(),
+                            pixel_scales=dev_f32(ps))
+    torch.cuda.synchronize()
+    ref = o.geometry(s, dt, inp.om, inp.scales, pscales=ps)
+    for k in ("inside", "y0", "x0"):
+        assert np.array_equal(g[k].cpu().numpy(), ref[k]), k
+    for k in ("lh", "lw"):
+        assert np.array_equal(g[k].cpu().numpy().view(np.uint32), ref[k].view(np.uint32)), k
 
 
 # ------------------------------------------------------------ variants

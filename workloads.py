@@ -14,10 +14,14 @@ FlowDCN tokens ([FlowDCN] = kler.cn "NeurIPS'24 | FlowDCNï¼šåŸºäºŽå¯å˜å½¢å·ç§
 åˆ†è¾¨çŽ‡å›¾åƒç”Ÿæˆæ¨¡åž‹", section 3.1, per-group scale priors).
 
 Recipe (every workload): draws in float32 from numpy's PCG64 seeded with the
-workload seed, in the order input, offsets, weights; x ~ N(0,1); weights m ~
-N(0, 1/9) (standard deviation 1/3); offsets per workload (uniform U[-a,a] or
-normal with the given variance); values are then rounded to the I/O dtype with
-round-to-nearest-even (torch's CPU cast for bf16, numpy's for fp16).
+workload seed, in the order input, offsets, weights (then, for FlowDCN's
+predicted scales, the per-pixel scales); x ~ N(0,1); weights m ~ N(0, 1/9)
+(standard deviation 1/3); offsets per workload (uniform U[-a,a] or normal with
+the given variance); values are then rounded to the I/O dtype with
+round-to-nearest-even (torch's CPU cast for bf16, numpy's for fp16).  Group
+scale priors and predicted per-pixel scales stay fp32; the predicted scales
+are U[lo, hi] (the pages give no distribution: a band around 1, so that with
+the clamp Smax some groups of every pixel hit the maximum).
 The offset/weight tensor om has layout [N,Ho,Wo,G,3K]: per group the K
 interleaved (dx, dy) pairs first, then the K weights.
 """
@@ -51,6 +55,9 @@ class Workload:
     offset_dist: str = "uniform"   # "uniform": U[-a,a]; "normal": N(0, a)
     offset_param: float = 2.0      # a (half-width, or variance)
     seed: int = 0
+    pixel_scales: bool = False     # FlowDCN predicted scale per (pixel, group)
+    pixel_scale_range: tuple = (0.5, 1.5)
+    max_scale: float = 0.0         # > 0: Smax clamp of the effective scale
 
     @property
     def K(self) -> int:
@@ -68,6 +75,9 @@ class Workload:
                if self.offset_dist == "uniform"
                else f"N(0,{self.offset_param:g})")
         mode = "multi-scale" if self.multiscale else "standard"
+        if self.pixel_scales:
+            lo, hi = self.pixel_scale_range
+            mode += f" pixel scales U[{lo:g},{hi:g}] Smax {self.max_scale:g}"
         return (f"{self.name}: {self.dtype} N={self.N} {self.H}x{self.W} "
                 f"C={self.C} G={self.G} k={self.kh}x{self.kw} "
                 f"s={self.sh},{self.sw} p={self.ph},{self.pw} "
@@ -99,6 +109,12 @@ WORKLOADS = {
                                         32, 32, 1152, 16, multiscale=True,
                                         offset_dist="uniform",
                                         offset_param=1.0),
+    # the same tokens with FlowDCN's predicted per-pixel scale times the group
+    # prior and the maximum scale Smax = 4 (the largest prior)
+    "flowdcn_pixelscale_bf16": Workload("flowdcn_pixelscale_bf16", "bf16", 32,
+                                        32, 32, 1152, 16, multiscale=True,
+                                        offset_dist="uniform", offset_param=1.0,
+                                        pixel_scales=True, max_scale=4.0),
 }
 
 # The workload the headline throughput is quoted on.
@@ -145,6 +161,7 @@ class Inputs:
     x: np.ndarray                 # raw [N,H,W,C]
     om: np.ndarray                # raw [N,Ho,Wo,G,3K]
     scales: Optional[np.ndarray]  # float32 [G] or None
+    pscales: Optional[np.ndarray] = None  # float32 [N,Ho,Wo,G] or None
 
 
 def make_inputs(w: Workload, Ho: int, Wo: int, seed: Optional[int] = None,
@@ -167,4 +184,8 @@ def make_inputs(w: Workload, Ho: int, Wo: int, seed: Optional[int] = None,
     m = rng.standard_normal((N, Ho, Wo, G, K), dtype=np.float32) * np.float32(1.0 / 3.0)
     om = np.concatenate([off, m], axis=-1)
     scales = group_scales(G) if w.multiscale else None
-    return Inputs(to_raw(x, w.dtype), to_raw(om, w.dtype), scales)
+    pscales = None
+    if w.pixel_scales:
+        lo, hi = (np.float32(v) for v in w.pixel_scale_range)
+        pscales = rng.random((N, Ho, Wo, G), dtype=np.float32) * (hi - lo) + lo
+    return Inputs(to_raw(x, w.dtype), to_raw(om, w.dtype), scales, pscales)
