@@ -95,6 +95,7 @@ class Oracle:
         lib.dcn4o_geometry.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P,
                                        P, ctypes.c_int64]
         lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, P, i64p, i64p]
+        lib.dcn4o_backward.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P, i64p]
         lib.dcn4o_ideal_bytes.argtypes = [sp, ctypes.c_int]
         lib.dcn4o_ideal_bytes.restype = ctypes.c_int64
         for f in ("dcn4o_bf16_to_f32", "dcn4o_f16_to_f32"):
@@ -212,6 +213,32 @@ class Oracle:
         if r:
             raise ValueError("oracle rejected the call")
         return a.value, b.value
+
+    def backward(self, s: Shape, dtype: str, x, om, gy, scales=None, pscales=None,
+                 want_x: bool = True, want_om: bool = True):
+        """Gradients for upstream gy [N,Ho,Wo,C] (raw, I/O dtype): dict with
+        gx [N,H,W,C] and gom [N,Ho,Wo,G,3K] (fp64), their absolute-term sums
+        gx_abs, gom_abs, and max_terms."""
+        dt, x, om, scales, pscales = self._prep(s, dtype, x, om, scales, pscales)
+        gy = np.ascontiguousarray(gy, dtype=RAW_NP[dt])
+        ho, wo = self.out_size(s)
+        out = {}
+        if want_x:
+            out["gx"] = np.empty((s.N, s.H, s.W, s.C), np.float64)
+            out["gx_abs"] = np.empty_like(out["gx"])
+        if want_om:
+            out["gom"] = np.empty((s.N, ho, wo, s.G, 3 * s.K), np.float64)
+            out["gom_abs"] = np.empty_like(out["gom"])
+        mt = ctypes.c_int64()
+        r = self.lib.dcn4o_backward(ctypes.byref(s.c_struct()), dt, self._ptr(x),
+                                    self._ptr(om), self._ptr(scales), self._ptr(pscales),
+                                    self._ptr(gy), self._ptr(out.get("gx")),
+                                    self._ptr(out.get("gom")), self._ptr(out.get("gx_abs")),
+                                    self._ptr(out.get("gom_abs")), ctypes.byref(mt))
+        if r:
+            raise ValueError("oracle rejected the call")
+        out["max_terms"] = mt.value
+        return out
 
     def ideal_bytes(self, s: Shape, dtype: str) -> int:
         return int(self.lib.dcn4o_ideal_bytes(ctypes.byref(s.c_struct()),

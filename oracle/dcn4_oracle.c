@@ -36,6 +36,10 @@
  *     fp32 input [N, Ho, Wo, G] (whatever activation the model applies comes
  *     before it), replaced by Smax when it is larger (max_scale > 0; a NaN S
  *     stays NaN); fp32 order: S = fl(s_g * sigma), then the clamp;
+ *  R14 backward (the pages give no formula; the gradient of the forward
+ *     definition): at an integer location the derivative from above (the
+ *     cell of the floor), a sample that is not inside has zero gradient, and
+ *     the sampling decisions are the fp32 evaluation's (see dcn4o_backward);
  *  R8 fp32 evaluation order (dcn4o_forward_f32): the location is kept as an
  *     exact integer part and a fraction.  The displacement from the integer
  *     base is t = fl(offset_scale*delta) (multi-scale: t = fl(s_g * fl(grid +
@@ -54,6 +58,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -450,5 +455,118 @@ int dcn4o_geometry(const dcn4o_shape* s, int dtype, const void* om,
       }
     }
   }
+  return 0;
+}
+
+/* ----------------------------------------------------------------- backward
+ * Gradients of y = sum_k m_k * B(p_k) (B the zero-padded bilinear sample of
+ * one channel) for an upstream gradient gy [N,Ho,Wo,C] (reading R14):
+ *   dL/dx[n,h,w,c]  = sum over the samples whose corner (h,w) lies in the
+ *                     image of m_k * w_corner * gy[p,c]          (a scatter)
+ *   dL/dm_k         = sum_{c in g} gy[p,c] * B_c(p_k)
+ *   dL/d(dy_k)      = m_k * f * sum_{c in g} gy[p,c] * dB_c/drow
+ *   dL/d(dx_k)      = m_k * f * sum_{c in g} gy[p,c] * dB_c/dcol
+ * with f = offset_scale (standard) or the group's effective scale S
+ * (multi-scale: the location moves by S per unit of direction), and, inside
+ * the cell of corner (y0, x0) with fractions (lh, lw):
+ *   dB/drow = (1-lw)(v10 - v00) + lw(v11 - v01)
+ *   dB/dcol = (1-lh)(v01 - v00) + lh(v11 - v10)
+ * (the derivative from above at integer locations, where B has a kink).  The
+ * cell, the fractions, the inside test and S are the fp32 evaluation's
+ * (sample_geometry_f32, R8/R13), so this oracle takes the same sampling
+ * decisions as an fp32 implementation; every product and sum is fp64.
+ * Samples that are not inside contribute nothing to any gradient.
+ *
+ * Also returned, for tolerance bounds: the sum of the absolute values of the
+ * terms of every output (gx_abs, gom_abs) and the largest number of terms
+ * of any single output (max_terms). */
+int dcn4o_backward(const dcn4o_shape* s, int dtype, const void* x, const void* om,
+                   const float* scales, const float* pscales, const void* gy,
+                   double* gx, double* gom, double* gx_abs, double* gom_abs,
+                   int64_t* max_terms) {
+  int32_t Ho, Wo;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  const int K = s->kh * s->kw, G = s->G, C = s->C, D = C / G;
+  const int H = s->H, W = s->W;
+  const int64_t nx = (int64_t)s->N * H * W * C;
+  const int64_t npx = (int64_t)s->N * Ho * Wo;
+  int32_t* gx_terms = NULL;
+  if (gx) {
+    memset(gx, 0, sizeof(double) * nx);
+    if (gx_abs) memset(gx_abs, 0, sizeof(double) * nx);
+    gx_terms = (int32_t*)calloc((size_t)nx, sizeof(int32_t));
+    if (!gx_terms) return -1;
+  }
+  int64_t terms_max = 4 * (int64_t)D; /* every grad_om entry has 4D terms */
+  for (int64_t p = 0; p < npx; ++p) {
+    int n = (int)(p / ((int64_t)Ho * Wo));
+    int yo = (int)((p / Wo) % Ho);
+    int xo = (int)(p % Wo);
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (p * G + g) * 3 * K;
+      const float sg = scale_f32(s, scales, pscales, p, g);
+      const double f = s->multiscale ? (double)sg : (double)s->offset_scale;
+      for (int k = 0; k < K; ++k) {
+        int i = k / s->kw, j = k % s->kw;
+        float dx = load_f32(dtype, om, row + 2 * k);
+        float dy = load_f32(dtype, om, row + 2 * k + 1);
+        double m = load_f32(dtype, om, row + 2 * K + k);
+        geom_t q = sample_geometry_f32(s, yo, xo, i, j, dx, dy, sg);
+        double gm = 0.0, gdr = 0.0, gdc = 0.0, am = 0.0, adr = 0.0, adc = 0.0;
+        if (q.inside) {
+          const double lh = q.lh, lw = q.lw, hh = 1.0 - lh, hw = 1.0 - lw;
+          const int cy[4] = {q.y0, q.y0, q.y0 + 1, q.y0 + 1};
+          const int cx[4] = {q.x0, q.x0 + 1, q.x0, q.x0 + 1};
+          const double w[4] = {hh * hw, hh * lw, lh * hw, lh * lw};
+          for (int d = 0; d < D; ++d) {
+            const int c = g * D + d;
+            const double gyc = load_f32(dtype, gy, p * C + c);
+            double v[4];
+            int64_t idx[4];
+            for (int r = 0; r < 4; ++r) {
+              int ok = cy[r] >= 0 && cy[r] < H && cx[r] >= 0 && cx[r] < W;
+              idx[r] = ok ? (((int64_t)n * H + cy[r]) * W + cx[r]) * C + c : -1;
+              v[r] = ok ? (double)load_f32(dtype, x, idx[r]) : 0.0;
+            }
+            const double B = w[0] * v[0] + w[1] * v[1] + w[2] * v[2] + w[3] * v[3];
+            const double dBr = hw * (v[2] - v[0]) + lw * (v[3] - v[1]);
+            const double dBc = hh * (v[1] - v[0]) + lh * (v[3] - v[2]);
+            gm += gyc * B;
+            gdr += gyc * dBr;
+            gdc += gyc * dBc;
+            am += fabs(gyc) * (w[0] * fabs(v[0]) + w[1] * fabs(v[1]) +
+                               w[2] * fabs(v[2]) + w[3] * fabs(v[3]));
+            adr += fabs(gyc) * (hw * (fabs(v[2]) + fabs(v[0])) + lw * (fabs(v[3]) + fabs(v[1])));
+            adc += fabs(gyc) * (hh * (fabs(v[1]) + fabs(v[0])) + lh * (fabs(v[3]) + fabs(v[2])));
+            if (gx) {
+              for (int r = 0; r < 4; ++r) {
+                if (idx[r] < 0) continue;
+                const double t = m * w[r] * gyc;
+                gx[idx[r]] += t;
+                if (gx_abs) gx_abs[idx[r]] += fabs(t);
+                gx_terms[idx[r]] += 1;
+              }
+            }
+          }
+        }
+        if (gom) {
+          gom[row + 2 * k] = m * f * gdc;     /* dx moves the column */
+          gom[row + 2 * k + 1] = m * f * gdr; /* dy moves the row    */
+          gom[row + 2 * K + k] = gm;
+        }
+        if (gom_abs) {
+          gom_abs[row + 2 * k] = fabs(m * f) * adc;
+          gom_abs[row + 2 * k + 1] = fabs(m * f) * adr;
+          gom_abs[row + 2 * K + k] = am;
+        }
+      }
+    }
+  }
+  if (gx) {
+    for (int64_t e = 0; e < nx; ++e)
+      if (gx_terms[e] > terms_max) terms_max = gx_terms[e];
+    free(gx_terms);
+  }
+  if (max_terms) *max_terms = terms_max;
   return 0;
 }

@@ -100,6 +100,18 @@ int dcn4o_count_terms(const dcn4o_shape* s, int dtype, const void* om,
                       const float* scales, const float* pscales,
                       int64_t* corner_terms, int64_t* inbounds_terms);
 
+/* Gradients of the forward pass for an upstream gradient gy [N,Ho,Wo,C] in
+ * the I/O dtype: gx [N,H,W,C] (dL/dx), gom [N,Ho,Wo,G,3K] (dL/d offsets and
+ * dL/d weights, in the offset/weight layout), both fp64, either may be NULL.
+ * The sampling decisions (cell, fractions, inside test, effective scale) are
+ * the fp32 evaluation's; all arithmetic after them is fp64.  gx_abs/gom_abs
+ * (nullable) receive the sums of the absolute values of every output's terms
+ * and *max_terms the largest term count of any output (tolerance bounds). */
+int dcn4o_backward(const dcn4o_shape* s, int dtype, const void* x,
+                   const void* om, const float* scales, const float* pscales,
+                   const void* gy, double* gx, double* gom, double* gx_abs,
+                   double* gom_abs, int64_t* max_terms);
+
 /* Ideal traffic of one forward pass in bytes: input + output feature maps
  * plus the offset/weight tensor, each read or written once, plus 4G bytes of
  * fp32 scales in multi-scale mode and 4*N*Ho*Wo*G bytes of pixel scales

@@ -465,6 +465,106 @@ def pin_pixel_scales(o):
         exact_equal(a32, b32, "NaN sigma elsewhere f32")
 
 
+def _frac_offsets(rng, shape, lo, hi):
+    """integer part in [lo, hi), fraction a multiple of 1/32 in [1/4, 3/4]"""
+    ip = rng.integers(lo, hi, size=shape)
+    fp = rng.integers(8, 25, size=shape) / 32.0
+    return (ip + fp).astype(np.float32)
+
+
+def _bwd_inputs(o, s, seed, scales=None):
+    rng = np.random.default_rng(seed)
+    ho, wo = o.out_size(s)
+    K = s.K
+    x = dyadic(rng, (s.N, s.H, s.W, s.C), -4, 4, 8)
+    gy = dyadic(rng, (s.N, ho, wo, s.C), -2, 2, 8)
+    m = dyadic(rng, (s.N, ho, wo, s.G, K), -1, 1, 8)
+    if s.multiscale:
+        # choose the scaled displacement t = S*(grid + d) with an in-cell
+        # fraction, then d = t/S - grid (exact: S is a power of two)
+        hy = (s.kh - 1) // 2
+        grid_y = (np.arange(K) // s.kw - hy).astype(np.float32)
+        grid_x = (np.arange(K) % s.kw - (s.kw - 1) // 2).astype(np.float32)
+        S = np.asarray(scales, np.float32)[None, None, None, :, None]
+        ty = _frac_offsets(rng, (s.N, ho, wo, s.G, K), -3, 3)
+        tx = _frac_offsets(rng, (s.N, ho, wo, s.G, K), -3, 3)
+        dy = (ty / S - grid_y).astype(np.float32)
+        dx = (tx / S - grid_x).astype(np.float32)
+    else:
+        dy = (_frac_offsets(rng, (s.N, ho, wo, s.G, K), -2, 2) / s.offset_scale).astype(np.float32)
+        dx = (_frac_offsets(rng, (s.N, ho, wo, s.G, K), -2, 2) / s.offset_scale).astype(np.float32)
+    return x, dx, dy, m, gy
+
+
+BWD_SHAPES = [(Shape(2, 7, 8, 8, 2), None),
+              (Shape(1, 9, 6, 12, 3, sh=2, sw=1, ph=2, pw=0, dh=2, dw=1, offset_scale=0.5), None),
+              (Shape(2, 8, 9, 8, 2, multiscale=True), [1.0, 2.0])]
+
+
+def pin_backward_weights(o):
+    """dL/dm: the forward is linear in m, so with one-hot weights on tap k it
+    returns B_k, the bilinear samples of that tap; dL/dm_k = sum over the
+    group's channels of gy * B_k (exact on dyadic inputs)."""
+    for s, sc in BWD_SHAPES:
+        x, dx, dy, m, gy = _bwd_inputs(o, s, 31, sc)
+        scales = None if sc is None else np.asarray(sc, np.float32)
+        for dt in ("f32", "bf16"):
+            got = o.backward(s, dt, to_raw(x, dt), to_raw(pack_om(dx, dy, m), dt),
+                             to_raw(gy, dt), scales, want_x=False)["gom"]
+            D = s.C // s.G
+            for k in range(s.K):
+                onehot = np.zeros_like(m)
+                onehot[..., k] = 1
+                yk = o.forward_f64(s, dt, to_raw(x, dt), to_raw(pack_om(dx, dy, onehot), dt),
+                                   scales, nthreads=2)
+                prod = (gy.astype(np.float64) * yk).reshape(yk.shape[:-1] + (s.G, D))
+                exact_equal(got[..., 2 * s.K + k], prod.sum(-1), f"dL/dm tap {k} {dt}")
+
+
+def pin_backward_adjoint(o):
+    """dL/dx: the forward is linear in x, so for any v,
+    <gy, forward(v)> == <dL/dx, v> (exact on dyadic inputs)."""
+    rng = np.random.default_rng(32)
+    for s, sc in BWD_SHAPES:
+        x, dx, dy, m, gy = _bwd_inputs(o, s, 33, sc)
+        scales = None if sc is None else np.asarray(sc, np.float32)
+        om = pack_om(dx, dy, m)
+        for dt in ("f32", "f16"):
+            gx = o.backward(s, dt, to_raw(x, dt), to_raw(om, dt), to_raw(gy, dt), scales,
+                            want_om=False)["gx"]
+            for _ in range(3):
+                v = dyadic(rng, x.shape, -4, 4, 8)
+                fv = o.forward_f64(s, dt, to_raw(v, dt), to_raw(om, dt), scales, nthreads=2)
+                lhs = float(np.sum(gy.astype(np.float64) * fv))
+                rhs = float(np.sum(gx * v.astype(np.float64)))
+                assert lhs == rhs, f"adjoint {dt} {s}: {lhs} != {rhs}"
+
+
+def pin_backward_offsets(o):
+    """dL/d offsets: inside its cell the bilinear sample is linear in each
+    coordinate, so shifting the offsets of tap k by h = 2^-10 (every sample
+    stays in its cell) changes the loss <gy, y> by exactly h times the
+    gradient, for each axis; this also fixes the factor offset_scale
+    (standard) or the group scale (multi-scale)."""
+    h = 2.0 ** -10
+    for s, sc in BWD_SHAPES:
+        x, dx, dy, m, gy = _bwd_inputs(o, s, 34, sc)
+        scales = None if sc is None else np.asarray(sc, np.float32)
+        dt = "f32"
+        got = o.backward(s, dt, x, pack_om(dx, dy, m), gy, scales, want_x=False)["gom"]
+        y0 = o.forward_f64(s, dt, x, pack_om(dx, dy, m), scales, nthreads=2)
+        D = s.C // s.G
+        for k in range(s.K):
+            for axis, (ddx, ddy) in enumerate(((h, 0.0), (0.0, h))):
+                dx2, dy2 = dx.copy(), dy.copy()
+                dx2[..., k] += np.float32(ddx)
+                dy2[..., k] += np.float32(ddy)
+                y1 = o.forward_f64(s, dt, x, pack_om(dx2, dy2, m), scales, nthreads=2)
+                want = ((gy.astype(np.float64) * (y1 - y0)).reshape(y0.shape[:-1] + (s.G, D))
+                        .sum(-1) / h)
+                exact_equal(got[..., 2 * k + axis], want, f"dL/d offset tap {k} axis {axis} {s}")
+
+
 def pin_nonfinite_offsets(o):
     """A NaN or infinite offset puts the sample nowhere in the image: the
     output equals the one where that point's weight is zero."""
@@ -690,7 +790,8 @@ ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
             pin_affine_reproduction, pin_depthwise_conv, pin_zero_padding,
             pin_partition_of_unity, pin_linearity, pin_multiscale,
             pin_pixel_scales, pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
-            pin_exact_rational, pin_geometry, pin_codecs]
+            pin_exact_rational, pin_geometry, pin_codecs, pin_backward_weights,
+            pin_backward_adjoint, pin_backward_offsets]
 
 
 if __name__ == "__main__":

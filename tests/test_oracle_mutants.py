@@ -83,6 +83,20 @@ MUTANTS = {
                               "if (s->max_scale > 0.0f && S < s->max_scale) S = s->max_scale;"),
     "clamp_fmin_f32": sub("if (s->max_scale > 0.0f && S > s->max_scale) S = s->max_scale;",
                           "if (s->max_scale > 0.0f) S = fminf(S, s->max_scale);"),
+    # backward (R14): a factor lost, axes or corners exchanged, a sign flipped
+    "bwd_weight_lost_in_gx": sub("const double t = m * w[r] * gyc;", "const double t = w[r] * gyc;"),
+    "bwd_corner_weights_reversed_gx": sub("const double t = m * w[r] * gyc;",
+                                          "const double t = m * w[3 - r] * gyc;"),
+    "bwd_axes_swapped": subs(("gom[row + 2 * k] = m * f * gdc;", "gom[row + 2 * k] = m * f * GDR_;"),
+                             ("gom[row + 2 * k + 1] = m * f * gdr;", "gom[row + 2 * k + 1] = m * f * gdc;"),
+                             ("m * f * GDR_;", "m * f * gdr;")),
+    "bwd_scale_factor_lost": sub("const double f = s->multiscale ? (double)sg : (double)s->offset_scale;",
+                                 "const double f = 1.0;"),
+    "bwd_row_derivative_sign": sub("const double dBr = hw * (v[2] - v[0]) + lw * (v[3] - v[1]);",
+                                   "const double dBr = hw * (v[0] - v[2]) + lw * (v[3] - v[1]);"),
+    "bwd_col_derivative_weights": sub("const double dBc = hh * (v[1] - v[0]) + lh * (v[3] - v[2]);",
+                                      "const double dBc = lh * (v[1] - v[0]) + hh * (v[3] - v[2]);"),
+    "bwd_sample_unweighted": sub("gm += gyc * B;", "gm += gyc * (v[0] + v[1] + v[2] + v[3]);"),
     # group bookkeeping
     "group_channels_interleaved": sub("int c = g * D + d;", "int c = d * s->G + g;"),
     "group_row_shared": sub("const int64_t row = (p * G + g) * 3 * K;",
