@@ -73,6 +73,8 @@ def main():
                     help="plan option (kernel, tile_margin, tile_groups, tile_pad)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dcn4_backward) instead of the forward")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="instead of the operator, run plain device copies of MIB "
                          "MiB (the scale reference for the HBM byte counters)")
@@ -95,6 +97,8 @@ def main():
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
+    if args.backward:
+        return bench_backward(args, torch, np, workloads, d4, name, w)
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
@@ -210,6 +214,70 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, Ho, Wo, host0, args.cpu_reps)
     print(json.dumps(line), flush=True)
+
+
+def bench_backward(args, torch, np, workloads, d4, name, w):
+    """One step = dcn4_backward on one batch: grad_x cleared and accumulated,
+    grad_offset_mask written.  Ideal bytes: x, the offset/weight tensor and
+    grad_y read once in the I/O dtype, grad_x and grad_offset_mask written once
+    in fp32."""
+    desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+                   w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
+                   w.pixel_scales, w.max_scale)
+    plan = d4.Plan(desc)
+    Ho, Wo = plan.Ho, plan.Wo
+    es = 4 if w.dtype == "f32" else 2
+    nx = w.N * w.H * w.W * w.C
+    ny = w.N * Ho * Wo * w.C
+    nom = w.N * Ho * Wo * w.G * 3 * w.K
+    ideal = (nx + nom + ny) * es + (nx + nom) * 4
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_tensor(raw):
+        t = torch.from_numpy(raw) if w.dtype == "f32" else torch.from_numpy(raw.view(np.int16)).view(tdt)
+        return t.to(dev)
+
+    nsets = args.sets or max(2, math.ceil((1 << 30) / max(ideal, 1)))
+    sets = []
+    for r in range(nsets):
+        inp = workloads.make_inputs(w, Ho, Wo, seed=w.seed + r)
+        rng = np.random.default_rng(1000 + r)
+        gy = workloads.to_raw(rng.standard_normal((w.N, Ho, Wo, w.C), dtype=np.float32), w.dtype)
+        sc = None if inp.scales is None else torch.from_numpy(inp.scales).to(dev)
+        ps = None if inp.pscales is None else torch.from_numpy(inp.pscales).to(dev)
+        gx = torch.empty((w.N, w.H, w.W, w.C), dtype=torch.float32, device=dev)
+        gom = torch.empty(plan.om_shape(), dtype=torch.float32, device=dev)
+        sets.append((dev_tensor(inp.x), dev_tensor(inp.om), dev_tensor(gy), sc, ps, gx, gom))
+    torch.cuda.synchronize()
+
+    def step(i):
+        x, om, gy, sc, ps, gx, gom = sets[i % nsets]
+        plan.backward(x, om, gy, sc, ps, grad_x=gx, grad_om=gom, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    value = ideal / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "DCNv4 bwd GB/s (ideal bytes: x, offset/weight, grad_y read; fp32 grads written)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded, the workload's shapes and distributions)",
+        "config": {"workload": name, "pass": "backward", "ideal_bytes": ideal,
+                   "input_sets": nsets},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kernel_source": kernel_source_digest()}), flush=True)
 
 
 def copy_reference(torch, mib, steps):

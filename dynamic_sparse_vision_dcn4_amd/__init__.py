@@ -90,6 +90,7 @@ _lib.dcn4_plan_set_option.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
 _lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
 _lib.dcn4_forward_scaled.argtypes = [_P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_destroy.argtypes = [_P]
 _lib.dcn4_destroy.restype = None
 _lib.dcn4_status_string.argtypes = [ctypes.c_int]
@@ -98,7 +99,7 @@ _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
-           "dcn4_probe_geometry"):
+           "dcn4_probe_geometry", "dcn4_backward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -139,6 +140,13 @@ def dcn4_forward_scaled(plan, x: int, offset_mask: int, group_scales: Optional[i
                         stream: Optional[int]) -> int:
     return _lib.dcn4_forward_scaled(plan, x, offset_mask, group_scales,
                                     pixel_scales, y, stream)
+
+
+def dcn4_backward(plan, x: int, offset_mask: int, group_scales: Optional[int],
+                  pixel_scales: Optional[int], grad_y: int, grad_x: Optional[int],
+                  grad_offset_mask: Optional[int], stream: Optional[int]) -> int:
+    return _lib.dcn4_backward(plan, x, offset_mask, group_scales, pixel_scales, grad_y,
+                              grad_x, grad_offset_mask, stream)
 
 
 def dcn4_probe_geometry(plan, offset_mask: int, group_scales: Optional[int],
@@ -293,6 +301,41 @@ class Plan:
         if st != DCN4_OK:
             raise DCN4Error(st, "dcn4_forward")
         return out
+
+    def backward(self, x, om, grad_y, scales=None, pixel_scales=None, want_x=True,
+                 want_om=True, grad_x=None, grad_om=None, stream=None):
+        """(grad_x [N,H,W,C] fp32 or None, grad_om [N,Ho,Wo,G,3K] fp32 or
+        None) for the upstream gradient grad_y [N,Ho,Wo,C]."""
+        import torch
+        d = self.desc
+        dt = _torch_dtype(d.dtype)
+        self._check(x, (d.N, d.H, d.W, d.C), dt, "x")
+        self._check(om, self.om_shape(), dt, "offset_mask")
+        self._check(grad_y, self.out_shape(), dt, "grad_y")
+        if scales is not None:
+            self._check(scales, (d.group,), torch.float32, "group_scales")
+        if pixel_scales is not None:
+            self._check(pixel_scales, (d.N, self.Ho, self.Wo, d.group), torch.float32,
+                        "pixel_scales")
+        if want_x and grad_x is None:
+            grad_x = torch.empty((d.N, d.H, d.W, d.C), dtype=torch.float32, device=x.device)
+        if want_om and grad_om is None:
+            grad_om = torch.empty(self.om_shape(), dtype=torch.float32, device=x.device)
+        if grad_x is not None:
+            self._check(grad_x, (d.N, d.H, d.W, d.C), torch.float32, "grad_x")
+        if grad_om is not None:
+            self._check(grad_om, self.om_shape(), torch.float32, "grad_offset_mask")
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = dcn4_backward(self._h, x.data_ptr(), om.data_ptr(),
+                           None if scales is None else scales.data_ptr(),
+                           None if pixel_scales is None else pixel_scales.data_ptr(),
+                           grad_y.data_ptr(),
+                           None if grad_x is None else grad_x.data_ptr(),
+                           None if grad_om is None else grad_om.data_ptr(), stream)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_backward")
+        return grad_x, grad_om
 
     def probe_geometry(self, om, scales=None, stream=None, pixel_scales=None):
         """Device geometry of every (n, yo, xo, g, k): dict of tensors."""

@@ -316,6 +316,22 @@ dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
   return dcn4_forward_scaled(plan, x, offset_mask, group_scales, nullptr, y, stream);
 }
 
+dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
+                          const void* offset_mask, const float* group_scales,
+                          const float* pixel_scales, const void* grad_y,
+                          float* grad_x, float* grad_offset_mask, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  dcn4_status s = check_io(p, x, offset_mask, group_scales, pixel_scales, grad_y, true);
+  if (s != DCN4_OK || p.desc.N == 0) return s;
+  if ((grad_x && !aligned_to(grad_x, 4)) || (grad_offset_mask && !aligned_to(grad_offset_mask, 4)))
+    return fail(DCN4_ERR_MISALIGNED, "gradient outputs must be 4-byte aligned");
+  s = dcn4::launch_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                            grad_offset_mask, stream);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
 dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
                                 const float* group_scales,
                                 const float* pixel_scales, int32_t* y0,

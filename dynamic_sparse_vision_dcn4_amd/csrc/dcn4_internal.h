@@ -127,6 +127,11 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
                          const float* pscales, int32_t* y0, int32_t* x0,
                          float* lh, float* lw, uint8_t* inside, void* stream);
+// Backward pass: zero grad_x (if given) and accumulate it, write grad_om (if
+// given); both fp32.
+dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
+                            const float* scales, const float* pscales,
+                            const void* gy, float* gx, float* gom, void* stream);
 // Text of the last HIP error a launch reported on this thread.
 const char* last_hip_error();
 // LDS bytes one forward workgroup of `block` lanes stages (the offset/weight

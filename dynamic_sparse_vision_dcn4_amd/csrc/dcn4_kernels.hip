@@ -782,6 +782,160 @@ void dcn4_tile_kernel(TileArgs a) {
   }
 }
 
+// ------------------------------------------------------------ backward
+// Gradients of the forward pass for an upstream gradient gy (fp32 results):
+//   grad_x[corner, c] += m_k * w_corner * gy[p, c]      (scatter, fp32 atomics)
+//   grad_m[p, g, k]    = sum_c gy[p, c] * B_c
+//   grad_d{y,x}[p,g,k] = m_k * f * sum_c gy[p, c] * dB_c/d{row,col}
+// with B the bilinear sample, f = offset_scale or the group's scale, and, in
+// the cell (y0, x0) with fractions (lh, lw), dB/drow = (1-lw)(v10-v00) +
+// lw(v11-v01), dB/dcol = (1-lh)(v01-v00) + lh(v11-v10).  The sampling
+// decisions (cell, fractions, inside test, scale) come from the forward's
+// device functions, so they are the forward's bit for bit; a sample that is
+// not inside has zero gradient.
+//
+// Lanes: Lg lanes per (pixel, group) item, lane li owning channels li,
+// li + Lg, ... of the group (Lg = the largest power of two <= 16 dividing D).
+// For one channel index the Lg lanes of an item touch Lg consecutive
+// channels, so a wave's atomics and gathers cover 64/Lg contiguous runs of
+// Lg elements rather than 64 scattered cache lines.  The three per-point
+// reductions over the group's channels are xor-shuffles within the item.
+struct BwdArgs {
+  const char* x;          // input of this launch's first image
+  const char* om;         // offset/weight tensor of this launch's first image
+  const float* scales;
+  const float* pscales;   // [pixels, G] of this launch, or null
+  const char* gy;         // upstream gradient [N,Ho,Wo,C], I/O dtype
+  float* gx;              // [N,H,W,C] fp32 (accumulated), or null
+  float* gom;             // [N,Ho,Wo,G,3K] fp32 (written), or null
+  FwdArgs f;              // geometry fields shared with the forward
+  int32_t lg_shift;       // log2(Lg)
+  int64_t lanes;          // lanes of this launch
+  uint64_t x_bytes;       // input bytes of this launch
+};
+
+template <int DT, int MODE, int KS>
+__global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  const FwdArgs& a = b.f;
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (gid >= b.lanes) return;
+  const int Lg = 1 << b.lg_shift;
+  const uint32_t item = (uint32_t)(gid >> b.lg_shift);
+  const uint32_t li = (uint32_t)gid & (uint32_t)(Lg - 1);
+  const uint32_t p = fastdiv(item, a.div_ipp);  // ipp = G here
+  const uint32_t g = item - p * (uint32_t)a.G;
+  const uint32_t n = fastdiv(p, a.div_hw);
+  const uint32_t rem = p - n * (uint32_t)(a.Ho * a.Wo);
+  const uint32_t yo = fastdiv(rem, a.div_wo);
+  const uint32_t xo = rem - yo * (uint32_t)a.Wo;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  const int kw = KS ? KS : a.kw;
+  const int cpl = a.D >> b.lg_shift;  // channels per lane
+
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(b.om) +
+                               (uint64_t)item * (uint32_t)(3 * K);
+  const typename io::raw* gyp = reinterpret_cast<const typename io::raw*>(b.gy) +
+                                (uint64_t)p * (uint32_t)a.C + g * (uint32_t)a.D + li;
+  const rsrc_t xr = make_rsrc(b.x, (uint32_t)(b.x_bytes < 0x7fffffffu ? b.x_bytes : 0x7fffffffu));
+  const uint32_t pix_bytes = (uint32_t)a.C * es;
+  const uint32_t img_off = n * a.img_bytes + (g * (uint32_t)a.D + li) * es;
+  float* gxp = b.gx ? b.gx + (uint64_t)n * a.H * a.W * a.C + g * (uint32_t)a.D + li : nullptr;
+  const float sg = (MODE == kGroupScale) ? group_scale(a, p, g) : 1.0f;
+  const float f = (MODE == kGroupScale) ? sg : a.offset_scale;
+  const int hy = ((KS ? KS : a.kh) - 1) >> 1, hx = (kw - 1) >> 1;
+
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const int i = k / kw, j = k - (k / kw) * kw;
+    const float dx = io::dec(om[2 * k]);
+    const float dy = io::dec(om[2 * k + 1]);
+    const float m = io::dec(om[2 * K + k]);
+    float by, bx, gyy = 0.0f, gxx = 0.0f;
+    if (MODE == kGroupScale) {
+      by = (float)((int)yo * a.sh - a.ph + hy);
+      bx = (float)((int)xo * a.sw - a.pw + hx);
+      gyy = (float)(i - hy);
+      gxx = (float)(j - hx);
+    } else {
+      by = (float)((int)yo * a.sh - a.ph + i * a.dh);
+      bx = (float)((int)xo * a.sw - a.pw + j * a.dw);
+    }
+    const Cell c = locate(sample_location<MODE>(by, bx, gyy, gxx, dy, dx, a.offset_scale, sg),
+                          a.Hm1, a.Wm1);
+    float gm = 0.0f, gdr = 0.0f, gdc = 0.0f;
+    if (c.inside) {
+      const bool vy0 = c.y0 >= 0, vy1 = c.y0 < a.H - 1;
+      const bool vx0 = c.x0 >= 0, vx1 = c.x0 < a.W - 1;
+      const bool ok[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+      const float lh = c.lh, lw = c.lw, hh = 1.0f - lh, hw = 1.0f - lw;
+      const float w[4] = {hh * hw, hh * lw, lh * hw, lh * lw};
+      const int cy[4] = {c.y0, c.y0, c.y0 + 1, c.y0 + 1};
+      const int cx[4] = {c.x0, c.x0 + 1, c.x0, c.x0 + 1};
+      uint32_t q[4];
+      float cm[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // pixel index below 2^23 (H*W < 2^23); only used for corners in the image
+        const uint32_t pix = (uint32_t)(cy[r] * a.W + cx[r]);
+        q[r] = ok[r] ? img_off + pix * pix_bytes : kOutside;
+        cm[r] = m * w[r];
+      }
+#pragma unroll 1
+      for (int jc = 0; jc < cpl; ++jc) {
+        const uint32_t coff = ((uint32_t)jc << b.lg_shift) * es;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (es == 4)
+            v[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, (int)(q[r] + coff), 0, 0));
+          else
+            v[r] = io::dec((typename io::raw)__builtin_amdgcn_raw_buffer_load_b16(xr, (int)(q[r] + coff), 0, 0));
+        }
+        const float gyc = io::dec(gyp[jc << b.lg_shift]);
+        float B = w[0] * v[0];
+        B = __builtin_fmaf(w[1], v[1], B);
+        B = __builtin_fmaf(w[2], v[2], B);
+        B = __builtin_fmaf(w[3], v[3], B);
+        const float dBr = __builtin_fmaf(lw, v[3] - v[1], hw * (v[2] - v[0]));
+        const float dBc = __builtin_fmaf(lh, v[3] - v[2], hh * (v[1] - v[0]));
+        gm = __builtin_fmaf(gyc, B, gm);
+        gdr = __builtin_fmaf(gyc, dBr, gdr);
+        gdc = __builtin_fmaf(gyc, dBc, gdc);
+        if (gxp) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (ok[r])
+              unsafeAtomicAdd(gxp + ((uint64_t)(cy[r] * a.W + cx[r]) * (uint32_t)a.C +
+                                     ((uint32_t)jc << b.lg_shift)),
+                              cm[r] * gyc);
+        }
+      }
+    }
+    if (b.gom) {
+      // the item's Lg lanes are consecutive and Lg-aligned in the wave
+      for (int off = 1; off < Lg; off <<= 1) {
+        gm += __shfl_xor(gm, off, 64);
+        gdr += __shfl_xor(gdr, off, 64);
+        gdc += __shfl_xor(gdc, off, 64);
+      }
+      if (li == 0) {
+        float* go = b.gom + (uint64_t)item * (uint32_t)(3 * K);
+        const float mf = m * f;
+        go[2 * k] = mf * gdc;      // dx moves the column
+        go[2 * k + 1] = mf * gdr;  // dy moves the row
+        go[2 * K + k] = gm;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void dcn4_fill_zero_kernel(float* p, uint64_t n) {
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
 // ------------------------------------------------------------ geometry probe
 // One thread per (pixel, g, k); reads the merged tensor straight from global
 // memory and writes what the forward kernel's geometry functions compute.
@@ -1109,6 +1263,87 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
     a.nblocks = (int32_t)(nb * per_image);
     hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.lds_bytes,
                        static_cast<hipStream_t>(stream), a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  return DCN4_OK;
+}
+
+int32_t backward_lg_shift(int32_t D) {
+  int32_t sh = 0;
+  while (sh < 4 && (D % (2 << sh)) == 0) ++sh;
+  return sh;
+}
+
+dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
+                            const float* scales, const float* pscales,
+                            const void* gy, float* gx, float* gom, void* stream) {
+  const dcn4_desc& d = p.desc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gx) {
+    const uint64_t n = (uint64_t)d.N * d.H * d.W * d.C;
+    const uint64_t blocks = (n + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(dcn4_fill_zero_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                       dim3(kBlock), 0, st, gx, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  if (!gom && !gx) return DCN4_OK;
+  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  typedef void (*bwd_fn)(BwdArgs);
+  bwd_fn fn;
+  const int m = p.mode;
+#define DCN4_BWD_PICK(DT)                                                              \
+  fn = m == kStdUnitScale ? (K3 ? dcn4_backward_kernel<DT, kStdUnitScale, 3>          \
+                                : dcn4_backward_kernel<DT, kStdUnitScale, 0>)         \
+     : m == kStdScaled ? (K3 ? dcn4_backward_kernel<DT, kStdScaled, 3>                 \
+                             : dcn4_backward_kernel<DT, kStdScaled, 0>)                \
+                       : (K3 ? dcn4_backward_kernel<DT, kGroupScale, 3>                \
+                             : dcn4_backward_kernel<DT, kGroupScale, 0>)
+  switch (d.dtype) {
+    case DCN4_F32: DCN4_BWD_PICK(DCN4_F32); break;
+    case DCN4_BF16: DCN4_BWD_PICK(DCN4_BF16); break;
+    default: DCN4_BWD_PICK(DCN4_F16); break;
+  }
+#undef DCN4_BWD_PICK
+  BwdArgs b{};
+  fill_common(p, b.f);
+  b.f.scales = scales;
+  b.f.G = d.group;
+  b.f.ipp = d.group;
+  b.f.div_ipp = make_fastdiv((uint32_t)d.group);
+  b.scales = scales;
+  b.lg_shift = backward_lg_shift(p.D);
+  const int64_t lanes_per_image = (int64_t)p.Ho * p.Wo * d.group << b.lg_shift;
+  const uint64_t x_img = (uint64_t)d.H * d.W * d.C * p.es;
+  // per launch: lanes below 2^31 and input bytes below 2^31 (32-bit buffer
+  // offsets; a single image is validated below 2^31 bytes at plan creation)
+  int64_t imgs = ((int64_t(1) << 31) - 1) / lanes_per_image;
+  const int64_t imgs_x = (int64_t)(((uint64_t(1) << 31) - 1) / x_img);
+  if (imgs_x < imgs) imgs = imgs_x;
+  if (imgs < 1) imgs = 1;
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t om_img = (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K * p.es;
+  const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;
+  for (int64_t n0 = 0; n0 < d.N; n0 += imgs) {
+    const int64_t nb = (d.N - n0) < imgs ? (d.N - n0) : imgs;
+    b.x = static_cast<const char*>(x) + n0 * x_img;
+    b.om = static_cast<const char*>(om) + n0 * om_img;
+    b.gy = static_cast<const char*>(gy) + n0 * y_img;
+    b.pscales = pscales ? pscales + n0 * ps_img : nullptr;
+    b.f.pscales = b.pscales;
+    b.gx = gx ? gx + n0 * (uint64_t)d.H * d.W * d.C : nullptr;
+    b.gom = gom ? gom + n0 * (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K : nullptr;
+    b.x_bytes = nb * x_img;
+    b.lanes = nb * lanes_per_image;
+    const int64_t blocks = (b.lanes + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, st, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       note_hip_error(e);

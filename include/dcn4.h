@@ -201,6 +201,29 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
                                 const float* pixel_scales, void* y,
                                 void* stream);
 
+/* Backward pass: the gradients of a loss L with respect to the input and to
+ * the offset/weight tensor, given dL/dy.  grad_y is [N, Ho, Wo, C] in the I/O
+ * dtype; grad_x [N, H, W, C] and grad_offset_mask [N, Ho, Wo, G, 3K] are fp32
+ * device arrays, 4-byte aligned, either of them NULL to skip it; both are
+ * overwritten (grad_x is cleared by the library, then accumulated).  In the
+ * offset/weight layout, grad_offset_mask holds dL/d(dx_k, dy_k) and dL/dm_k:
+ *   dL/dm_k  = sum over the group's channels c of dL/dy_c * B_c(p_k),
+ *   dL/d(dy_k) = m_k * f * sum_c dL/dy_c * dB_c/drow, dL/d(dx_k) likewise
+ *              with dB/dcol, f = offset_scale or the group's scale S,
+ *   dL/dx[corner] = sum over the samples that read it of m_k * w * dL/dy,
+ * where, in the cell (y0, x0) with fractions (lh, lw), dB/drow =
+ * (1-lw)(v10-v00) + lw(v11-v01) and dB/dcol = (1-lh)(v01-v00) + lh(v11-v10):
+ * the derivative from above at integer locations.  The sampling decisions
+ * are the forward's (same device functions); a sample that is not inside has
+ * zero gradient.  No gradient of the group or pixel scales is computed.
+ * grad_x is summed with fp32 atomics in no fixed order, so it is not
+ * bit-reproducible; the fp32 sums of grad_offset_mask are.  Other arguments,
+ * validation and errors as dcn4_forward_scaled (grad_y in the role of y). */
+dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
+                          const void* offset_mask, const float* group_scales,
+                          const float* pixel_scales, const void* grad_y,
+                          float* grad_x, float* grad_offset_mask, void* stream);
+
 /* Test probe of the sampling geometry: for every (n, yo, xo, g, k), in that
  * order, writes inside (1 if the integer parts passed the -1 <= y0 <= H-1,
  * -1 <= x0 <= W-1 test), and for inside samples the integer parts y0, x0 and

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
               "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
-              "dcn4_plan_info", "dcn4_plan_set_option", "dcn4_forward_scaled"):
+              "dcn4_plan_info", "dcn4_plan_set_option", "dcn4_forward_scaled",
+              "dcn4_backward"):
         assert n in names
 
 
@@ -257,6 +258,17 @@ class TestForwardValidation:
         assert fs(ps, 1024, 2050) == d4.DCN4_ERR_MISALIGNED
         assert fs(self.ms, 1024, 2048) == d4.DCN4_ERR_INVALID_ARG
         assert fs(self.p, None, 2048) == d4.DCN4_ERR_INVALID_ARG
+
+    def test_backward(self):
+        bw = lambda p, x, om, sc, gy, gx, gom: d4.dcn4_backward(p.handle, x, om, sc, None, gy,
+                                                               gx, gom, None)
+        assert bw(self.p, 256, 256, None, None, 512, 1024) == d4.DCN4_ERR_NULL
+        assert bw(self.p, 256, 256, None, 257, 512, 1024) == d4.DCN4_ERR_MISALIGNED
+        assert bw(self.p, 256, 256, None, 256, 514, 1024) == d4.DCN4_ERR_MISALIGNED
+        assert bw(self.p, 256, 256, None, 256, 512, 1026) == d4.DCN4_ERR_MISALIGNED
+        assert bw(self.p, 256, 256, 1024, 256, 512, 1024) == d4.DCN4_ERR_INVALID_ARG
+        assert bw(self.ms, 256, 256, None, 256, 512, 1024) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_backward(None, 256, 256, None, None, 256, 512, 1024, None) == d4.DCN4_ERR_NULL
 
     def test_empty_batch_is_a_no_op(self):
         p0 = d4.Plan(mk(N=0))

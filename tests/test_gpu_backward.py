@@ -1,0 +1,147 @@
+"""Parity of the HIP backward pass (dcn4_backward) with the oracle's.
+
+grad_x is summed with fp32 atomics in no fixed order and grad_offset_mask with
+fp32 sums in the kernel's order, while the oracle sums in fp64 (with the same
+sampling decisions as the fp32 forward).  The tolerance is the fp32
+summation bound: for an output with terms t_i (at most n of them per output),
+|gpu - oracle| <= (n + 8) * 2^-24 * sum_i |t_i|, the sum of absolute terms
+coming from the oracle (n + 8 covers the n additions and the few roundings
+of each product).  The bound is checked on every element."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from oracle import Shape  # noqa: E402
+from test_gpu_parity import (NTHREADS, desc_of, dev_f32, say, shape_of,  # noqa: E402
+                             to_dev)
+from workloads import WORKLOADS, make_inputs, to_raw  # noqa: E402
+
+import dynamic_sparse_vision_dcn4_amd as d4  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def check_bound(got, want, absum, n_terms, what):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - want)
+    bound = (n_terms + 8) * U * absum + 1e-37
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    bad = ~(err <= bound)
+    say(f"{what}: max |gpu - oracle| / bound = {ratio:.3g} over {err.size} elements")
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the fp32 bound; "
+                           f"first at {np.argwhere(bad)[:3].tolist()}")
+
+
+def run_backward(plan, inp, gy_raw, dt, want_x=True, want_om=True):
+    x = to_dev(inp.x, dt)
+    om = to_dev(inp.om, dt)
+    gy = to_dev(gy_raw, dt)
+    sc = None if inp.scales is None else torch.from_numpy(inp.scales).cuda()
+    gx, gom = plan.backward(x, om, gy, sc, dev_f32(inp.pscales), want_x=want_x,
+                            want_om=want_om)
+    torch.cuda.synchronize()
+    return (None if gx is None else gx.cpu().numpy(),
+            None if gom is None else gom.cpu().numpy())
+
+
+def compare(s, dt, inp, gy_raw, plan, what):
+    o = oracle.get()
+    ref = o.backward(s, dt, inp.x, inp.om, gy_raw, inp.scales, inp.pscales)
+    gx, gom = run_backward(plan, inp, gy_raw, dt)
+    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], what + " grad_x")
+    check_bound(gom, ref["gom"], ref["gom_abs"], ref["max_terms"], what + " grad_om")
+    return gx, gom
+
+
+def bwd_cases():
+    rng = np.random.default_rng(4321)
+    cases = []
+    kernels = [(3, 3), (3, 3), (1, 1), (5, 5), (3, 5), (2, 2)]
+    for t in range(18):
+        dt = ["bf16", "f32", "f16"][t % 3]
+        mode = ["std", "std", "scaled", "ms", "ps"][t % 5]
+        kh, kw = kernels[int(rng.integers(len(kernels)))]
+        if mode in ("ms", "ps") and (kh % 2 == 0 or kw % 2 == 0):
+            kh, kw = 3, 3
+        D = int(rng.choice([16, 24, 10, 72, 4, 32, 8]))
+        G = int(rng.integers(1, 4))
+        ms = mode in ("ms", "ps")
+        sh, sw = (1, 1) if ms else (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+        dh, dw = (1, 1) if ms else (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+        s = Shape(int(rng.integers(1, 3)), int(rng.integers(5, 24)), int(rng.integers(5, 24)),
+                  G * D, G, kh, kw, sh, sw, int(rng.integers(0, 3)), int(rng.integers(0, 3)),
+                  dh, dw, 0.5 if mode == "scaled" else 1.0, ms, mode == "ps",
+                  2.5 if mode == "ps" else 0.0)
+        try:
+            oracle.get().out_size(s)
+        except ValueError:
+            continue
+        cases.append((t, s, dt))
+    return cases
+
+
+def bwd_inputs(s, dt, seed):
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    rng = np.random.default_rng(seed)
+    K = s.K
+    x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
+    off = rng.uniform(-3, 3, (s.N, Ho, Wo, s.G, 2 * K)).astype(np.float32)
+    m = (rng.standard_normal((s.N, Ho, Wo, s.G, K)) / 3).astype(np.float32)
+    scales = rng.uniform(0.5, 3.0, s.G).astype(np.float32) if s.multiscale else None
+    ps = rng.uniform(0.5, 1.5, (s.N, Ho, Wo, s.G)).astype(np.float32) if s.pixel_scales else None
+    gy = rng.standard_normal((s.N, Ho, Wo, s.C)).astype(np.float32)
+    inp = workloads.Inputs(to_raw(x, dt), to_raw(np.concatenate([off, m], -1), dt), scales, ps)
+    return inp, to_raw(gy, dt)
+
+
+@pytest.mark.parametrize("t, s, dt", bwd_cases(), ids=lambda v: str(v) if isinstance(v, int) else None)
+def test_backward_parity(t, s, dt):
+    inp, gy = bwd_inputs(s, dt, seed=t)
+    plan = d4.Plan(desc_of(s, dt))
+    say(f"backward case {t}: {s} {dt}")
+    compare(s, dt, inp, gy, plan, f"backward {t}")
+
+
+@pytest.mark.parametrize("name", ["ldm_unet_block_bf16", "flowdcn_pixelscale_bf16"])
+def test_backward_full_size(name):
+    """The headline block and FlowDCN's tokens with predicted scales, every
+    output element against the fp64 oracle."""
+    w = WORKLOADS[name]
+    s = shape_of(w)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = make_inputs(w, Ho, Wo)
+    rng = np.random.default_rng(11)
+    gy = to_raw(rng.standard_normal((s.N, Ho, Wo, s.C), dtype=np.float32), w.dtype)
+    say(f"backward full size: {w.describe()}")
+    compare(s, w.dtype, inp, gy, d4.Plan(desc_of(s, w.dtype)), name)
+
+
+def test_backward_reproducible_and_partial():
+    """grad_offset_mask is bit-reproducible (no atomics); each gradient can be
+    asked for alone and equals the one computed with both."""
+    s = Shape(2, 19, 23, 64, 4)
+    dt = "bf16"
+    inp, gy = bwd_inputs(s, dt, seed=99)
+    plan = d4.Plan(desc_of(s, dt))
+    gx1, gom1 = run_backward(plan, inp, gy, dt)
+    gx2, gom2 = run_backward(plan, inp, gy, dt)
+    assert np.array_equal(gom1.view(np.uint32), gom2.view(np.uint32))
+    _, gom3 = run_backward(plan, inp, gy, dt, want_x=False)
+    assert np.array_equal(gom1.view(np.uint32), gom3.view(np.uint32))
+    gx4, _ = run_backward(plan, inp, gy, dt, want_om=False)
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy)
+    for g in (gx1, gx2, gx4):
+        check_bound(g, ref["gx"], ref["gx_abs"], ref["max_terms"], "grad_x repeat")
+
+
+def test_backward_empty_batch():
+    p0 = d4.Plan(d4.Desc(0, 8, 8, 16, 1))
+    assert d4.dcn4_backward(p0.handle, None, None, None, None, None, None, None, None) == d4.DCN4_OK
