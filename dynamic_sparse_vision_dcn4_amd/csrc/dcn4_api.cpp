@@ -175,6 +175,10 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
   info->channels_per_lane = dp;
   info->vector_bytes = vec ? 16 : p.es;
   info->lanes_per_group = p.D / dp;
+  const int32_t bwd_lds = (vec && p.kernel_choice != dcn4::kKernelDirect)
+                              ? dcn4::tiled_backward_lds(p) : 0;
+  info->backward_kernel = bwd_lds > 0 ? 2 : 1;
+  info->backward_lds_bytes = bwd_lds;
   if (vec && p.tile.ok) {
     const dcn4::TileShape& t = p.tile;
     info->channels_per_lane = t.dp;
@@ -326,8 +330,10 @@ dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
   if (s != DCN4_OK || p.desc.N == 0) return s;
   if ((grad_x && !aligned_to(grad_x, 4)) || (grad_offset_mask && !aligned_to(grad_offset_mask, 4)))
     return fail(DCN4_ERR_MISALIGNED, "gradient outputs must be 4-byte aligned");
+  const bool vector_path = p.dp > 0 && aligned_to(x, 16) && aligned_to(offset_mask, 16) &&
+                           aligned_to(grad_y, 16);
   s = dcn4::launch_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
-                            grad_offset_mask, stream);
+                            grad_offset_mask, stream, vector_path);
   if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
   return DCN4_OK;
 }

@@ -129,9 +129,15 @@ dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
                          float* lh, float* lw, uint8_t* inside, void* stream);
 // Backward pass: zero grad_x (if given) and accumulate it, write grad_om (if
 // given); both fp32.
+// vector_path: x, offset_mask and grad_y are 16-byte aligned (the tiled
+// backward may run).
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
-                            const void* gy, float* gx, float* gom, void* stream);
+                            const void* gy, float* gx, float* gom, void* stream,
+                            bool vector_path);
+// LDS bytes of the tiled backward (offset/weight gradients only) for the plan,
+// 0 when it does not apply.
+int32_t tiled_backward_lds(const Plan& p);
 // Text of the last HIP error a launch reported on this thread.
 const char* last_hip_error();
 // LDS bytes one forward workgroup of `block` lanes stages (the offset/weight

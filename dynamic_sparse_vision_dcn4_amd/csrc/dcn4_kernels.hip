@@ -543,38 +543,44 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
 
 // PSC: the LDS bytes per window pixel when known at compile time (one lane
 // owns one whole group, no padding, square window), else 0.
-template <int DT, int VEC, int NV, int MODE, int KS, int PSC>
-__global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
-void dcn4_tile_kernel(TileArgs a) {
-  typedef Io<DT> io;
-  constexpr int es = io::es;
-  constexpr int DP = VEC * NV;
-  extern __shared__ u32x4 lds_u4[];
-  char* lds = reinterpret_cast<char*>(lds_u4);
+// Origin of a tiled workgroup: image, tile, window corner and group chunk.
+// The group chunk varies fastest in the (XCD-remapped) workgroup order, so
+// the chunks of one tile run back to back on one XCD.
+struct TileOrigin {
+  uint32_t n, g0;
+  int ty0, tx0, wy0, wx0;
+};
 
-  // ---- workgroup -> (image, tile row, tile col, group chunk); the group
-  // chunk varies fastest so the chunks of one tile run back to back on one XCD
+__device__ __forceinline__ TileOrigin tile_origin(const TileArgs& a) {
   const uint32_t lb = (uint32_t)xcd_block(blockIdx.x, a.nblocks);
   uint32_t q = fastdiv(lb, a.div_chunks);
   const uint32_t gc = lb - q * (uint32_t)a.chunks;
   uint32_t q2 = fastdiv(q, a.div_tx);
   const uint32_t tx = q - q2 * (uint32_t)a.tiles_x;
-  const uint32_t n = fastdiv(q2, a.div_ty);
-  const uint32_t ty = q2 - n * (uint32_t)a.tiles_y;
-  const int ty0 = (int)ty * a.TH, tx0 = (int)tx * a.TW;
-  const int wy0 = ty0 * a.sh - a.ph - a.M, wx0 = tx0 * a.sw - a.pw - a.M;
-  const uint32_t g0 = gc * (uint32_t)a.GB;
-  const int K = KS ? KS * KS : a.kh * a.kw;
+  TileOrigin o;
+  o.n = fastdiv(q2, a.div_ty);
+  const uint32_t ty = q2 - o.n * (uint32_t)a.tiles_y;
+  o.ty0 = (int)ty * a.TH;
+  o.tx0 = (int)tx * a.TW;
+  o.wy0 = o.ty0 * a.sh - a.ph - a.M;
+  o.wx0 = o.tx0 * a.sw - a.pw - a.M;
+  o.g0 = gc * (uint32_t)a.GB;
+  return o;
+}
+
+// Stage the input window of a tile (zeros outside the image) at `lds` in
+// passes of wrpp whole window rows.  A window pixel is PS bytes in LDS: its GB
+// groups' channels, then (when padded) one 16-byte chunk loaded as zeros.
+// Thread t copies chunk t of every pass, so lane order equals LDS order as
+// the global-to-LDS copy requires, and its column, chunk and column test are
+// fixed.  Returns the input's buffer descriptor for the image.
+template <int es>
+__device__ __forceinline__ rsrc_t stage_window(const TileArgs& a, const TileOrigin& o, char* lds) {
   const uint32_t t = threadIdx.x, lane = t & 63u, wave0 = t - lane;
   const uint32_t pix_bytes = (uint32_t)(a.C * es);
-
-  // ---- stage the input window (zeros outside the image) in passes of wrpp
-  // whole window rows.  A window pixel is PS bytes in LDS: its GB groups'
-  // channels, then (when padded) one 16-byte chunk loaded as zeros.  Thread
-  // t copies chunk t of every pass, so lane order equals LDS order as the
-  // copy requires, and its column, chunk and column test are fixed.
-  const rsrc_t xr = make_rsrc(a.x + (uint64_t)n * a.img_bytes, a.img_bytes);
+  const int wy0 = o.wy0, wx0 = o.wx0;
+  const uint32_t g0 = o.g0;
+  const rsrc_t xr = make_rsrc(a.x + (uint64_t)o.n * a.img_bytes, a.img_bytes);
   {
     const uint32_t cvec = (uint32_t)a.PS >> 4;
     const uint32_t rp = fastdiv(t, a.div_cpr);  // row within the pass
@@ -602,16 +608,25 @@ void dcn4_tile_kernel(TileArgs a) {
       dst += pass_lds;
     }
   }
-  // ---- stage the tile's offset/weight values.  Per tile pixel the chunk's
-  // GB*3K values are OSU 4-byte units from the 4-byte boundary at or below
-  // their start (rows are 4-byte aligned, so the lead `mis` is the same for
-  // every pixel).  Passes of orpp whole tile rows when a row's units fit the
-  // workgroup (thread t then keeps its column and unit), else passes of
-  // oppp whole pixels.
-  const rsrc_t omr = make_rsrc(a.om + (uint64_t)n * a.om_img_bytes, a.om_img_bytes);
+  return xr;
+}
+
+// Stage the tile's offset/weight values at `lds_om`.  Per tile pixel the
+// chunk's GB*3K values are OSU 4-byte units from the 4-byte boundary at or
+// below their start (rows are 4-byte aligned, so the lead `mis`, returned, is
+// the same for every pixel).  Passes of orpp whole tile rows when a row's
+// units fit the workgroup (thread t then keeps its column and unit), else
+// passes of oppp whole pixels.
+template <int es>
+__device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin& o, int K,
+                                             char* lds_om) {
+  const uint32_t t = threadIdx.x, lane = t & 63u, wave0 = t - lane;
+  const int ty0 = o.ty0, tx0 = o.tx0;
+  const uint32_t g0 = o.g0;
+  const rsrc_t omr = make_rsrc(a.om + (uint64_t)o.n * a.om_img_bytes, a.om_img_bytes);
   const uint32_t seg = g0 * (uint32_t)(3 * K * es);
   const uint32_t mis = seg & 3u;
-  char* om_dst = lds + a.om_lds + wave0 * 4u;
+  char* om_dst = lds_om + wave0 * 4u;
   if (a.orpp == 1) {
     // one tile row per pass: the row is the same for every copying thread
     const uint32_t upx = fastdiv(t, a.div_osu), e = t - upx * (uint32_t)a.OSU;
@@ -671,6 +686,28 @@ void dcn4_tile_kernel(TileArgs a) {
       om_dst += pass_lds;
     }
   }
+  return mis;
+}
+
+template <int DT, int VEC, int NV, int MODE, int KS, int PSC>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
+void dcn4_tile_kernel(TileArgs a) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  constexpr int DP = VEC * NV;
+  extern __shared__ u32x4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+
+  const TileOrigin org = tile_origin(a);
+  const uint32_t n = org.n, g0 = org.g0;
+  const int ty0 = org.ty0, tx0 = org.tx0, wy0 = org.wy0, wx0 = org.wx0;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  const uint32_t t = threadIdx.x, lane = t & 63u;
+  const uint32_t pix_bytes = (uint32_t)(a.C * es);
+
+  const rsrc_t xr = stage_window<es>(a, org, lds);
+  const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   __syncthreads();
 
   // ---- lane -> (tile pixel, group in chunk, channel slice)
@@ -927,6 +964,159 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
         go[2 * k + 1] = mf * gdr;  // dy moves the row
         go[2 * K + k] = gm;
       }
+    }
+  }
+}
+
+// Tiled backward for the offset/weight gradients alone (a call without
+// grad_x): the forward's tile decomposition, LDS input window and staged
+// offset/weight values; per point the same window test as the forward, the
+// corners read from LDS (or, for a wave with a point outside the window, from
+// global memory) and the three sums over the lane's channels kept in
+// registers.  When a group spans L = 2 or 4 lanes their sums are added by
+// xor-shuffles.  3x3 kernels.  grad_x is a scatter whose cost on this GPU is
+// its fp32 atomics (about one lane per clock per CU whether they land in LDS
+// or L2), so calls that want it take the direct backward kernel.
+struct BwdTileArgs {
+  const char* gy;   // [N,Ho,Wo,C] I/O dtype, this launch
+  float* gom;       // [N,Ho,Wo,G,3K] fp32, this launch (written)
+};
+
+template <int DT, int VEC, int NV, int MODE>
+__global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTileArgs bb) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  constexpr int DP = VEC * NV;
+  constexpr int KS = 3, K = 9;
+  extern __shared__ u32x4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+
+  const TileOrigin org = tile_origin(a);
+  const uint32_t n = org.n, g0 = org.g0;
+  const int ty0 = org.ty0, tx0 = org.tx0, wy0 = org.wy0, wx0 = org.wx0;
+  const uint32_t t = threadIdx.x;
+  const uint32_t pix_bytes = (uint32_t)(a.C * es);
+  const rsrc_t xr = stage_window<es>(a, org, lds);
+  const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
+  __syncthreads();
+
+  // ---- lane -> (tile pixel, group in chunk, channel slice)
+  const uint32_t tp = fastdiv(t, a.div_gbl);
+  const uint32_t rr = t - tp * (uint32_t)(a.GB * a.L);
+  const uint32_t gl = fastdiv(rr, a.div_L), l = rr - gl * (uint32_t)a.L;
+  const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
+  const int yo = ty0 + (int)py, xo = tx0 + (int)px;
+  const bool active = yo < a.Ho && xo < a.Wo;
+  const uint32_t g = g0 + gl;
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
+      lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
+
+  // upstream gradient of the lane's channels (pixel (0, 0) for idle lanes)
+  float gyv[DP];
+  {
+    const char* gp = bb.gy + (((uint64_t)n * a.Ho + (active ? yo : 0)) * a.Wo + (active ? xo : 0)) *
+                                 pix_bytes + (g * (uint32_t)a.D + l * DP) * es;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(gp + 16 * v);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) gyv[v * VEC + e] = active ? io::lane(w, e) : 0.0f;
+    }
+  }
+
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  const uint32_t row_lds = (uint32_t)(a.WW * a.PS);
+  const float row_f = (float)row_lds, ps_f = (float)a.PS;
+  const float lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es);
+  const float ymax = (float)(a.WH - 2), xmax = (float)(a.WW - 2);
+  const int by0 = yo * a.sh - a.ph, bx0 = xo * a.sw - a.pw;
+  const float ry0 = (float)(by0 - wy0), rx0 = (float)(bx0 - wx0);
+  const float f = (MODE == kStdScaled) ? a.offset_scale : 1.0f;
+  const uint32_t lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
+
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const int i = k / KS, j = k - (k / KS) * KS;
+    const float dx = io::dec(om[2 * k]), dy = io::dec(om[2 * k + 1]);
+    const float m = io::dec(om[2 * K + k]);
+    const Loc lc = sample_location<MODE>(ry0 + (float)(i * a.dh), rx0 + (float)(j * a.dw),
+                                         0.0f, 0.0f, dy, dx, a.offset_scale, 1.0f);
+    const float fy = __builtin_floorf(lc.ty), fx = __builtin_floorf(lc.tx);
+    const float yr = lc.by + fy, xr_ = lc.bx + fx;  // corner (y0, x0), window-relative
+    const uint64_t off_window =
+        __builtin_amdgcn_ballot_w64(active && !(yr >= 0.0f)) |
+        __builtin_amdgcn_ballot_w64(active && !(yr <= ymax)) |
+        __builtin_amdgcn_ballot_w64(active && !(xr_ >= 0.0f)) |
+        __builtin_amdgcn_ballot_w64(active && !(xr_ <= xmax));
+    float lh = 0.0f, lw = 0.0f;
+    bool inside = true;
+    u32x4 vv[4][NV];
+    if (off_window == 0) {
+      lh = lc.ty - fy;
+      lw = lc.tx - fx;
+      const uint32_t a00 = (uint32_t)__builtin_fmaf(yr, row_f, __builtin_fmaf(xr_, ps_f, lane_f));
+      LdsTap<DT, VEC, NV> d;
+      d.load(a00, a00 + row_lds, a00 + 16u, a00 + row_lds + 16u, (uint32_t)a.PS);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n2 = 0; n2 < NV; ++n2) vv[r][n2] = d.v[r][n2];
+    } else {
+      // global path: absolute location, global gathers (zero outside the image)
+      const Cell cc = locate(sample_location<MODE>((float)(by0 + i * a.dh), (float)(bx0 + j * a.dw),
+                                                   0.0f, 0.0f, dy, dx, a.offset_scale, 1.0f),
+                             a.Hm1, a.Wm1);
+      inside = cc.inside;
+      lh = cc.lh;
+      lw = cc.lw;
+      const bool vy0 = cc.y0 >= 0, vy1 = cc.y0 < a.H - 1;
+      const bool vx0 = cc.x0 >= 0, vx1 = cc.x0 < a.W - 1;
+      const bool ok[4] = {inside && vy0 && vx0, inside && vy0 && vx1, inside && vy1 && vx0,
+                          inside && vy1 && vx1};
+      const int cy[4] = {cc.y0, cc.y0, cc.y0 + 1, cc.y0 + 1};
+      const int cx[4] = {cc.x0, cc.x0 + 1, cc.x0, cc.x0 + 1};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t q = ok[r] ? lane_bytes + (uint32_t)(cy[r] * a.W + cx[r]) * pix_bytes : kOutside;
+#pragma unroll
+        for (int n2 = 0; n2 < NV; ++n2)
+          vv[r][n2] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(q + 16 * n2), 0, 0);
+      }
+    }
+    // a sample that is not inside reads only zeros: its sums stay zero
+    const float hh = 1.0f - lh, hw = 1.0f - lw;
+    const float w[4] = {hh * hw, hh * lw, lh * hw, lh * lw};
+    float gm = 0.0f, gdr = 0.0f, gdc = 0.0f;
+#pragma unroll
+    for (int n2 = 0; n2 < NV; ++n2)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int c = n2 * VEC + e;
+        const float v0 = io::lane(vv[0][n2], e), v1 = io::lane(vv[1][n2], e);
+        const float v2 = io::lane(vv[2][n2], e), v3 = io::lane(vv[3][n2], e);
+        float B = w[0] * v0;
+        B = __builtin_fmaf(w[1], v1, B);
+        B = __builtin_fmaf(w[2], v2, B);
+        B = __builtin_fmaf(w[3], v3, B);
+        const float dBr = __builtin_fmaf(lw, v3 - v1, hw * (v2 - v0));
+        const float dBc = __builtin_fmaf(lh, v3 - v2, hh * (v1 - v0));
+        gm = __builtin_fmaf(gyv[c], B, gm);
+        gdr = __builtin_fmaf(gyv[c], dBr, gdr);
+        gdc = __builtin_fmaf(gyv[c], dBc, gdc);
+      }
+    if (!inside) gm = gdr = gdc = 0.0f;
+    // lanes of one (pixel, group) are consecutive; L is 1, 2 or 4
+    for (int off = 1; off < a.L; off <<= 1) {
+      gm += __shfl_xor(gm, off, 64);
+      gdr += __shfl_xor(gdr, off, 64);
+      gdc += __shfl_xor(gdc, off, 64);
+    }
+    if (active && l == 0) {
+      float* go = bb.gom + ((((uint64_t)n * a.Ho + yo) * a.Wo + xo) * (uint32_t)a.G + g) * (3 * K);
+      const float mf = m * f;
+      go[2 * k] = mf * gdc;
+      go[2 * k + 1] = mf * gdr;
+      go[2 * K + k] = gm;
     }
   }
 }
@@ -1197,20 +1387,9 @@ void resolve_tile(Plan& p) {
   p.tile = t;
 }
 
-dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
-                         const float* scales, void* y, void* stream) {
+void fill_tile_args(const Plan& p, TileArgs& a) {
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
-  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
-  const int nv = ts.dp / (16 / p.es);
-  // the pixel stride is a compile-time constant when a lane owns a whole
-  // unpadded group (and the window is square: see tile_point)
-  const bool psc = ts.gb == 1 && ts.dp == p.D && ts.ps == 16 * nv && ts.wh == ts.ww;
-  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc)
-             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc)
-                                    : tile_pick<DCN4_F16>(nv, p.mode, K3, psc);
-  TileArgs a{};
-  a.scales = scales;
   a.H = d.H; a.W = d.W; a.C = d.C; a.G = d.group; a.D = p.D; a.Ho = p.Ho; a.Wo = p.Wo;
   a.kh = d.kernel_h; a.kw = d.kernel_w; a.sh = d.stride_h; a.sw = d.stride_w;
   a.ph = d.pad_h; a.pw = d.pad_w; a.dh = d.dilation_h; a.dw = d.dilation_w;
@@ -1251,6 +1430,23 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   a.div_gbl = make_fastdiv((uint32_t)(ts.gb * a.L));
   a.div_L = make_fastdiv((uint32_t)a.L);
   a.div_tw = make_fastdiv((uint32_t)ts.tw);
+}
+
+dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
+                         const float* scales, void* y, void* stream) {
+  const dcn4_desc& d = p.desc;
+  const TileShape& ts = p.tile;
+  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  const int nv = ts.dp / (16 / p.es);
+  // the pixel stride is a compile-time constant when a lane owns a whole
+  // unpadded group (and the window is square: see tile_point)
+  const bool psc = ts.gb == 1 && ts.dp == p.D && ts.ps == 16 * nv && ts.wh == ts.ww;
+  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc)
+             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc)
+                                    : tile_pick<DCN4_F16>(nv, p.mode, K3, psc);
+  TileArgs a{};
+  fill_tile_args(p, a);
+  a.scales = scales;
   const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
   const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
   const int64_t per_image = (int64_t)a.tiles_x * a.tiles_y * a.chunks;
@@ -1278,9 +1474,73 @@ int32_t backward_lg_shift(int32_t D) {
   return sh;
 }
 
+typedef void (*tile_bwd_fn)(TileArgs, BwdTileArgs);
+
+template <int DT, int MODE>
+tile_bwd_fn tile_bwd_pick(int nv) {
+  constexpr int V = 16 / Io<DT>::es;
+  switch (nv) {
+    case 1: return dcn4_tile_bwd_kernel<DT, V, 1, MODE>;
+    case 2: return dcn4_tile_bwd_kernel<DT, V, 2, MODE>;
+    case 3: return dcn4_tile_bwd_kernel<DT, V, 3, MODE>;
+    default: return dcn4_tile_bwd_kernel<DT, V, 4, MODE>;
+  }
+}
+
+// LDS bytes of the tiled backward (0: it does not apply to the plan): the
+// forward tile's window and offset/weight values.
+int32_t tiled_backward_lds(const Plan& p) {
+  const dcn4_desc& d = p.desc;
+  const TileShape& ts = p.tile;
+  if (!ts.ok || p.mode == kGroupScale || d.kernel_h != 3 || d.kernel_w != 3) return 0;
+  const int32_t L = p.D / ts.dp;
+  if (L != 1 && L != 2 && L != 4) return 0;
+  return ts.lds_bytes;
+}
+
+dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
+                                  const void* gy, float* gom, hipStream_t st) {
+  const dcn4_desc& d = p.desc;
+  const TileShape& ts = p.tile;
+  const int nv = ts.dp / (16 / p.es);
+  tile_bwd_fn fn;
+  if (p.mode == kStdScaled)
+    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kStdScaled>(nv)
+       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kStdScaled>(nv)
+                              : tile_bwd_pick<DCN4_F16, kStdScaled>(nv);
+  else
+    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kStdUnitScale>(nv)
+       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kStdUnitScale>(nv)
+                              : tile_bwd_pick<DCN4_F16, kStdUnitScale>(nv);
+  TileArgs a{};
+  fill_tile_args(p, a);
+  const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t gom_img = (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K;
+  const int64_t per_image = (int64_t)a.tiles_x * a.tiles_y * a.chunks;
+  const int32_t imgs = (int32_t)((int64_t(1) << 30) / per_image);
+  BwdTileArgs b{};
+  for (int32_t n0 = 0; n0 < d.N; n0 += imgs) {
+    const int32_t nb = (d.N - n0) < imgs ? (d.N - n0) : imgs;
+    a.x = static_cast<const char*>(x) + n0 * x_img;
+    a.om = static_cast<const char*>(om) + n0 * om_img;
+    a.nblocks = (int32_t)(nb * per_image);
+    b.gy = static_cast<const char*>(gy) + n0 * y_img;
+    b.gom = gom + n0 * gom_img;
+    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.lds_bytes, st, a, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  return DCN4_OK;
+}
+
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
-                            const void* gy, float* gx, float* gom, void* stream) {
+                            const void* gy, float* gx, float* gom, void* stream,
+                            bool vector_path) {
   const dcn4_desc& d = p.desc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (gx) {
@@ -1295,6 +1555,8 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
     }
   }
   if (!gom && !gx) return DCN4_OK;
+  if (!gx && vector_path && p.kernel_choice != kKernelDirect && tiled_backward_lds(p) > 0)
+    return launch_tiled_backward(p, x, om, gy, gom, st);
   const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
   typedef void (*bwd_fn)(BwdArgs);
   bwd_fn fn;

@@ -144,6 +144,11 @@ typedef struct {
   int32_t tile_h, tile_w;    /* tiled kernel: output tile                   */
   int32_t tile_groups;       /* tiled kernel: groups per workgroup          */
   int32_t tile_margin;       /* tiled kernel: window margin in pixels       */
+  int32_t backward_kernel;   /* dcn4_backward without grad_x: 1 direct, 2
+                                tiled (LDS window), for 16-byte aligned
+                                tensors; calls with grad_x run the direct
+                                kernel                                      */
+  int32_t backward_lds_bytes; /* dynamic LDS per tiled-backward workgroup   */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.

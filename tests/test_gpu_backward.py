@@ -125,23 +125,65 @@ def test_backward_full_size(name):
 
 
 def test_backward_reproducible_and_partial():
-    """grad_offset_mask is bit-reproducible (no atomics); each gradient can be
-    asked for alone and equals the one computed with both."""
+    """grad_offset_mask is bit-reproducible (no atomics) on each path: the
+    direct kernel (a call with grad_x) and the tiled one (a call without);
+    each gradient can be asked for alone and stays within the bound."""
     s = Shape(2, 19, 23, 64, 4)
     dt = "bf16"
     inp, gy = bwd_inputs(s, dt, seed=99)
     plan = d4.Plan(desc_of(s, dt))
+    assert plan.info()["backward_kernel"] == 2
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy)
     gx1, gom1 = run_backward(plan, inp, gy, dt)
     gx2, gom2 = run_backward(plan, inp, gy, dt)
     assert np.array_equal(gom1.view(np.uint32), gom2.view(np.uint32))
     _, gom3 = run_backward(plan, inp, gy, dt, want_x=False)
-    assert np.array_equal(gom1.view(np.uint32), gom3.view(np.uint32))
-    gx4, _ = run_backward(plan, inp, gy, dt, want_om=False)
-    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy)
-    for g in (gx1, gx2, gx4):
+    _, gom4 = run_backward(plan, inp, gy, dt, want_x=False)
+    assert np.array_equal(gom3.view(np.uint32), gom4.view(np.uint32))
+    gx5, _ = run_backward(plan, inp, gy, dt, want_om=False)
+    for g in (gom1, gom3):
+        check_bound(g, ref["gom"], ref["gom_abs"], ref["max_terms"], "grad_om repeat")
+    for g in (gx1, gx2, gx5):
         check_bound(g, ref["gx"], ref["gx_abs"], ref["max_terms"], "grad_x repeat")
 
 
 def test_backward_empty_batch():
     p0 = d4.Plan(d4.Desc(0, 8, 8, 16, 1))
     assert d4.dcn4_backward(p0.handle, None, None, None, None, None, None, None, None) == d4.DCN4_OK
+
+
+TILED_BWD = [
+    # (shape, dtype, plan options, margins)
+    (Shape(2, 21, 27, 32, 2), "bf16", {}, (0, 1, 4)),
+    (Shape(1, 19, 33, 64, 2), "f16", {}, (0, 1, 4)),             # D=32: 2 lanes per group
+    (Shape(2, 17, 22, 32, 2), "f32", {}, (0, 1, 4)),             # fp32: 8 channels per lane
+    (Shape(1, 18, 20, 32, 2), "f32", {"channels_per_lane": 4}, (0, 1, 4)),  # 4 lanes per group
+    (Shape(2, 23, 19, 32, 4), "bf16", {}, (0, 1, 4)),            # D=8: one vector per lane
+    (Shape(1, 25, 31, 64, 4, dh=2, dw=2, ph=2, pw=2), "bf16", {}, (0, 1, 4)),  # dilation 2
+    (Shape(1, 27, 23, 64, 4, sh=2, sw=2), "bf16", {}, (0, 1, 4)),  # stride 2
+    (Shape(1, 20, 24, 64, 4, offset_scale=0.5), "f16", {}, (0, 1, 4)),
+    (Shape(1, 22, 26, 128, 8), "bf16", {"tile_groups": 2}, (0, 1, 4)),
+]
+TILED_BWD_CASES = [(c, m) for c, (_, _, _, ms) in enumerate(TILED_BWD) for m in ms]
+
+
+@pytest.mark.parametrize("case, margin", TILED_BWD_CASES)
+def test_tiled_backward(case, margin):
+    """The tiled backward (offset/weight gradients from the LDS window, for
+    calls without grad_x) against the oracle; margin 0 sends every wave to the
+    global path, 1 mixes the paths.  The same plan asked for both gradients
+    runs the direct kernel, which must agree within the bound too."""
+    s, dt, opts, _ = TILED_BWD[case]
+    inp, gy = bwd_inputs(s, dt, seed=500 + case)
+    dp = opts.get("channels_per_lane", 0)
+    rest = {k: v for k, v in opts.items() if k != "channels_per_lane"}
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, tile_margin=margin, **rest)
+    info = plan.info()
+    say(f"tiled backward {case} margin {margin}: {s} {dt} {info}")
+    assert info["backward_kernel"] == 2
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
+    _, gom = run_backward(plan, inp, gy, dt, want_x=False)
+    check_bound(gom, ref["gom"], ref["gom_abs"], ref["max_terms"], f"tiled grad_om {case} m{margin}")
+    gx, gom_d = run_backward(plan, inp, gy, dt)
+    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], f"direct grad_x {case} m{margin}")
+    check_bound(gom_d, ref["gom"], ref["gom_abs"], ref["max_terms"], f"direct grad_om {case} m{margin}")
