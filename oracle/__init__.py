@@ -96,6 +96,8 @@ class Oracle:
                                        P, ctypes.c_int64]
         lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, P, i64p, i64p]
         lib.dcn4o_backward.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P, i64p]
+        lib.dcn4o_linear_f64.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int, P, P, P, P, P]
         lib.dcn4o_ideal_bytes.argtypes = [sp, ctypes.c_int]
         lib.dcn4o_ideal_bytes.restype = ctypes.c_int64
         for f in ("dcn4o_bf16_to_f32", "dcn4o_f16_to_f32"):
@@ -239,6 +241,24 @@ class Oracle:
             raise ValueError("oracle rejected the call")
         out["max_terms"] = mt.value
         return out
+
+    def linear(self, dtype: str, feat, weight, bias=None):
+        """The merged offset/weight layer in fp64: (out [M, Nout], absum).
+        feat [M, Cin] and weight [Nout, Cin] raw in the I/O dtype."""
+        dt = DTYPE_CODES[dtype]
+        feat = np.ascontiguousarray(feat, dtype=RAW_NP[dt])
+        weight = np.ascontiguousarray(weight, dtype=RAW_NP[dt])
+        M, Cin = feat.shape
+        Nout = weight.shape[0]
+        assert weight.shape[1] == Cin
+        bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        out = np.empty((M, Nout), np.float64)
+        absum = np.empty((M, Nout), np.float64)
+        r = self.lib.dcn4o_linear_f64(M, Cin, Nout, dt, self._ptr(feat), self._ptr(weight),
+                                      self._ptr(bias), self._ptr(out), self._ptr(absum))
+        if r:
+            raise ValueError("oracle rejected the call")
+        return out, absum
 
     def ideal_bytes(self, s: Shape, dtype: str) -> int:
         return int(self.lib.dcn4o_ideal_bytes(ctypes.byref(s.c_struct()),

@@ -570,3 +570,32 @@ int dcn4o_backward(const dcn4o_shape* s, int dtype, const void* x, const void* o
   if (max_terms) *max_terms = terms_max;
   return 0;
 }
+
+/* ------------------------------------------------- merged offset/weight layer
+ * The producer of the offset/weight tensor: one linear layer maps every
+ * pixel's Cin features to its G*3K offsets and weights ([DCNv4 digest]
+ * "方法3": offsets and weights from one merged linear layer), so
+ *   om[r, j] = sum_k feat[r, k] * weight[j, k] + bias[j]
+ * for rows r < M (pixels), outputs j < Nout; feat and weight in the I/O dtype,
+ * bias fp32.  fp64 throughout; absum (nullable) receives
+ * sum_k |feat*weight| + |bias| per output (tolerance bounds). */
+int dcn4o_linear_f64(int64_t M, int32_t Cin, int32_t Nout, int dtype,
+                     const void* feat, const void* weight, const float* bias,
+                     double* out, double* absum) {
+  if (M < 0 || Cin < 1 || Nout < 1) return -1;
+  for (int64_t r = 0; r < M; ++r) {
+    for (int32_t j = 0; j < Nout; ++j) {
+      double acc = 0.0, a = 0.0;
+      for (int32_t k = 0; k < Cin; ++k) {
+        const double t = (double)load_f32(dtype, feat, r * Cin + k) *
+                         (double)load_f32(dtype, weight, (int64_t)j * Cin + k);
+        acc += t;
+        a += fabs(t);
+      }
+      const double b = bias ? (double)bias[j] : 0.0;
+      out[r * Nout + j] = acc + b;
+      if (absum) absum[r * Nout + j] = a + fabs(b);
+    }
+  }
+  return 0;
+}

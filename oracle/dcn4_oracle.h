@@ -112,6 +112,15 @@ int dcn4o_backward(const dcn4o_shape* s, int dtype, const void* x,
                    const void* gy, double* gx, double* gom, double* gx_abs,
                    double* gom_abs, int64_t* max_terms);
 
+/* The merged linear layer that produces the offset/weight tensor
+ * ([DCNv4 digest] "方法3"): out[r, j] = sum_k feat[r, k] * weight[j, k] +
+ * bias[j], feat [M, Cin] and weight [Nout, Cin] in the I/O dtype, bias fp32
+ * (nullable), out fp64 [M, Nout]; absum (nullable) receives the sum of the
+ * absolute values of every output's terms.  0 or -1 (bad sizes). */
+int dcn4o_linear_f64(int64_t M, int32_t Cin, int32_t Nout, int dtype,
+                     const void* feat, const void* weight, const float* bias,
+                     double* out, double* absum);
+
 /* Ideal traffic of one forward pass in bytes: input + output feature maps
  * plus the offset/weight tensor, each read or written once, plus 4G bytes of
  * fp32 scales in multi-scale mode and 4*N*Ho*Wo*G bytes of pixel scales

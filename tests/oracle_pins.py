@@ -565,6 +565,35 @@ def pin_backward_offsets(o):
                 exact_equal(got[..., 2 * k + axis], want, f"dL/d offset tap {k} axis {axis} {s}")
 
 
+def pin_offset_linear(o):
+    """The merged offset/weight layer ([DCNv4 digest] "方法3"):
+    (a) an identity weight returns the features plus the bias;
+    (b) one-hot features pick weight columns;
+    (c) on dyadic inputs it equals numpy's matrix product exactly;
+    (d) it is linear in the features."""
+    rng = np.random.default_rng(41)
+    M, Cin = 37, 32
+    feat = dyadic(rng, (M, Cin), -4, 4, 8)
+    bias = dyadic(rng, (Cin,), -2, 2, 4)
+    for dt in ("f32", "bf16", "f16"):
+        eye = np.eye(Cin, dtype=np.float32)
+        out, _ = o.linear(dt, to_raw(feat, dt), to_raw(eye, dt), bias)
+        exact_equal(out, feat.astype(np.float64) + bias, f"identity {dt}")
+    W = dyadic(rng, (27, Cin), -1, 1, 16)
+    onehot = np.zeros((Cin, Cin), np.float32)
+    onehot[np.arange(Cin), np.arange(Cin)[::-1]] = 1
+    out, _ = o.linear("f32", onehot, W, None)
+    exact_equal(out, W.T[::-1].astype(np.float64), "one-hot rows")
+    out, absum = o.linear("f32", feat, W, bias[:27])
+    exact_equal(out, feat.astype(np.float64) @ W.T.astype(np.float64) + bias[:27], "matmul")
+    assert np.all(absum >= np.abs(out) - 1e-12)
+    f2 = dyadic(rng, (M, Cin), -4, 4, 8)
+    o1, _ = o.linear("f32", feat, W, None)
+    o2, _ = o.linear("f32", f2, W, None)
+    o3, _ = o.linear("f32", feat + f2, W, None)
+    exact_equal(o3, o1 + o2, "linearity")
+
+
 def pin_nonfinite_offsets(o):
     """A NaN or infinite offset puts the sample nowhere in the image: the
     output equals the one where that point's weight is zero."""
@@ -791,7 +820,7 @@ ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
             pin_partition_of_unity, pin_linearity, pin_multiscale,
             pin_pixel_scales, pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
             pin_exact_rational, pin_geometry, pin_codecs, pin_backward_weights,
-            pin_backward_adjoint, pin_backward_offsets]
+            pin_backward_adjoint, pin_backward_offsets, pin_offset_linear]
 
 
 if __name__ == "__main__":

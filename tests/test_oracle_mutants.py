@@ -97,6 +97,12 @@ MUTANTS = {
     "bwd_col_derivative_weights": sub("const double dBc = hh * (v[1] - v[0]) + lh * (v[3] - v[2]);",
                                       "const double dBc = lh * (v[1] - v[0]) + hh * (v[3] - v[2]);"),
     "bwd_sample_unweighted": sub("gm += gyc * B;", "gm += gyc * (v[0] + v[1] + v[2] + v[3]);"),
+    # merged offset/weight layer: weight transposed, bias lost, a term lost
+    "linear_weight_transposed": sub("(double)load_f32(dtype, weight, (int64_t)j * Cin + k);",
+                                    "(double)load_f32(dtype, weight, (int64_t)k * Nout + j);"),
+    "linear_bias_lost": sub("out[r * Nout + j] = acc + b;", "out[r * Nout + j] = acc;"),
+    "linear_last_feature_lost": sub("for (int32_t k = 0; k < Cin; ++k) {\n        const double t",
+                                    "for (int32_t k = 0; k < Cin - 1; ++k) {\n        const double t"),
     # group bookkeeping
     "group_channels_interleaved": sub("int c = g * D + d;", "int c = d * s->G + g;"),
     "group_row_shared": sub("const int64_t row = (p * G + g) * 3 * K;",
