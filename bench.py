@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dcn4_backward) instead of the forward")
+    ap.add_argument("--linear", action="store_true",
+                    help="time the offset/weight linear layer (dcn4_offset_linear) "
+                         "that produces the workload's offset/weight tensor")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="instead of the operator, run plain device copies of MIB "
                          "MiB (the scale reference for the HBM byte counters)")
@@ -99,6 +102,8 @@ def main():
     w = workloads.WORKLOADS[name]
     if args.backward:
         return bench_backward(args, torch, np, workloads, d4, name, w)
+    if args.linear:
+        return bench_linear(args, torch, np, workloads, d4, name, w)
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
@@ -278,6 +283,66 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
                    "input_sets": nsets},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kernel_source": kernel_source_digest()}), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+
+
+def bench_linear(args, torch, np, workloads, d4, name, w):
+    """One step = dcn4_offset_linear over the workload's pixels: features
+    [N*Ho*Wo, C] times the merged offset/weight matrix [G*3K, C] plus bias,
+    written as the offset/weight tensor.  Ideal bytes: features, weight and
+    bias read once, the output written once."""
+    if w.dtype == "f32":
+        raise SystemExit("bench.py --linear: the layer runs bf16 and fp16 only")
+    plan = d4.Plan(d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+                           w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
+                           w.pixel_scales, w.max_scale))
+    M, Cin, Nout = w.N * plan.Ho * plan.Wo, w.C, w.G * 3 * w.K
+    ideal = (M * Cin + Nout * Cin + M * Nout) * 2 + Nout * 4
+    flops = 2.0 * M * Cin * Nout
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    nsets = args.sets or max(2, math.ceil((1 << 30) / max(ideal, 1)))
+    sets = []
+    for r in range(nsets):
+        f, wt, b = workloads.make_linear_inputs(M, Cin, Nout, w.dtype, seed=w.seed + r)
+        sets.append((torch.from_numpy(f.view(np.int16)).view(tdt).to(dev),
+                     torch.from_numpy(wt.view(np.int16)).view(tdt).to(dev),
+                     torch.from_numpy(b).to(dev),
+                     torch.empty((M, Nout), dtype=tdt, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        f, wt, b, out = sets[i % nsets]
+        d4.offset_linear(f, wt, b, out=out, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbs = ideal / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "offset/weight linear GB/s (ideal bytes: features, weight, bias read; "
+                  "offset/weight tensor written)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded normal features and weights)",
+        "config": {"workload": name, "pass": "offset_linear", "M": M, "Cin": Cin,
+                   "Nout": Nout, "ideal_bytes": ideal, "flops": flops, "input_sets": nsets},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tflops": round(tfs, 2),
+        "pct_mfma_peak": round(100.0 * tfs / MFMA_BF16_PEAK_TFLOPS, 2)}), flush=True)
 
 
 def copy_reference(torch, mib, steps):

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdcn4.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built: run `python -m dynamic_sparse_vision_dcn4_amd.build` "
+        f"{LIB_PATH} is not built: run `python dynamic_sparse_vision_dcn4_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 # PyTorch ships its own HIP runtime under the same soname (libamdhip64.so.7)
@@ -93,6 +93,8 @@ _lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
 _lib.dcn4_forward_scaled.argtypes = [_P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_offset_linear.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, _P]
 _lib.dcn4_destroy.argtypes = [_P]
 _lib.dcn4_destroy.restype = None
 _lib.dcn4_status_string.argtypes = [ctypes.c_int]
@@ -101,7 +103,7 @@ _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
-           "dcn4_probe_geometry", "dcn4_backward"):
+           "dcn4_probe_geometry", "dcn4_backward", "dcn4_offset_linear"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -149,6 +151,35 @@ def dcn4_backward(plan, x: int, offset_mask: int, group_scales: Optional[int],
                   grad_offset_mask: Optional[int], stream: Optional[int]) -> int:
     return _lib.dcn4_backward(plan, x, offset_mask, group_scales, pixel_scales, grad_y,
                               grad_x, grad_offset_mask, stream)
+
+
+def dcn4_offset_linear(feat: int, weight: int, bias: Optional[int], offset_mask: int,
+                       M: int, Cin: int, Nout: int, dtype: int, stream: Optional[int]) -> int:
+    return _lib.dcn4_offset_linear(feat, weight, bias, offset_mask, M, Cin, Nout, dtype, stream)
+
+
+def offset_linear(feat, weight, bias=None, out=None, stream=None):
+    """offset_mask [M, Nout] = feat [M, Cin] @ weight[Nout, Cin]^T + bias
+    (torch CUDA tensors, bf16 or fp16; bias fp32)."""
+    dt = {torch.bfloat16: DCN4_BF16, torch.float16: DCN4_F16}.get(feat.dtype)
+    if dt is None or weight.dtype != feat.dtype:
+        raise TypeError("feat and weight must both be bf16 or fp16")
+    M, Cin = feat.shape
+    Nout = weight.shape[0]
+    if weight.shape[1] != Cin or not feat.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("feat [M, Cin] and weight [Nout, Cin] must be contiguous")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Nout):
+        raise ValueError("bias must be fp32 [Nout]")
+    if out is None:
+        out = torch.empty((M, Nout), dtype=feat.dtype, device=feat.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(feat.device).cuda_stream
+    st = dcn4_offset_linear(feat.data_ptr(), weight.data_ptr(),
+                            None if bias is None else bias.data_ptr(), out.data_ptr(),
+                            M, Cin, Nout, dt, stream)
+    if st != DCN4_OK:
+        raise DCN4Error(st, "dcn4_offset_linear")
+    return out
 
 
 def dcn4_probe_geometry(plan, offset_mask: int, group_scales: Optional[int],

@@ -13,7 +13,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdcn4.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("dcn4_kernels.hip", "dcn4_api.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("dcn4_kernels.hip", "dcn4_linear.hip",
+                                                   "dcn4_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -338,6 +338,36 @@ dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
   return DCN4_OK;
 }
 
+dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float* bias,
+                               void* offset_mask, int64_t M, int32_t Cin, int32_t Nout,
+                               int32_t dtype, void* stream) {
+  if (dtype != DCN4_BF16 && dtype != DCN4_F16) {
+    if (dtype == DCN4_F32)
+      return fail(DCN4_ERR_UNSUPPORTED, "the offset/weight layer runs bf16 and fp16 only");
+    return fail(DCN4_ERR_INVALID_ARG, "dtype must be DCN4_BF16 or DCN4_F16");
+  }
+  if (M < 0 || Cin < 1 || Nout < 1)
+    return fail(DCN4_ERR_INVALID_ARG, "M must be >= 0 and Cin, Nout >= 1");
+  if (Cin % 16)
+    return fail(DCN4_ERR_UNSUPPORTED, "Cin must be a multiple of 16");
+  // buffer offsets are 32-bit: the weight rows of every column chunk (up to
+  // Nout rounded up to the chunk width) and one block of feature rows
+  if ((int64_t(Nout) + dcn4::kLinearCols) * Cin * 2 > 0x7fffffff ||
+      int64_t(dcn4::kLinearRows + 1) * Cin * 2 > 0x7fffffff)
+    return fail(DCN4_ERR_UNSUPPORTED, "Cin * (Nout + 288) beyond 2^30 elements");
+  if (M == 0) return DCN4_OK;
+  if (!feat || !weight || !offset_mask)
+    return fail(DCN4_ERR_NULL, "feat, weight and offset_mask must not be NULL");
+  if (!aligned_to(feat, 16) || !aligned_to(weight, 16) || !aligned_to(offset_mask, 2) ||
+      (bias && !aligned_to(bias, 4)))
+    return fail(DCN4_ERR_MISALIGNED,
+                "feat and weight must be 16-byte aligned, offset_mask 2, bias 4");
+  dcn4_status s = dcn4::launch_linear(feat, weight, bias, offset_mask, M, Cin, Nout, dtype,
+                                      stream);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
 dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
                                 const float* group_scales,
                                 const float* pixel_scales, int32_t* y0,

@@ -138,6 +138,25 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
 // LDS bytes of the tiled backward (offset/weight gradients only) for the plan,
 // 0 when it does not apply.
 int32_t tiled_backward_lds(const Plan& p);
+// Arguments of the merged offset/weight linear layer (dcn4_linear.hip).
+// Offset/weight linear layer: a workgroup owns kLinearRows rows and
+// kLinearCols output columns.
+constexpr int kLinearRows = 128;
+constexpr int kLinearCols = 288;
+struct LinArgs {
+  const char* feat;    // [M, Cin] I/O dtype (16-bit)
+  const char* weight;  // [Nout, Cin] I/O dtype
+  const float* bias;   // [Nout] fp32, or null
+  char* out;           // [M, Nout] I/O dtype
+  int64_t M;
+  int32_t Cin, Nout;
+  uint32_t w_bytes;    // Nout * Cin * 2
+  int32_t col_chunks;  // column chunks of 288 per row block
+  int32_t nblocks;
+};
+dcn4_status launch_linear(const void* feat, const void* weight, const float* bias,
+                          void* out, int64_t M, int32_t Cin, int32_t Nout, int32_t dtype,
+                          void* stream);
 // Text of the last HIP error a launch reported on this thread.
 const char* last_hip_error();
 // LDS bytes one forward workgroup of `block` lanes stages (the offset/weight

@@ -229,6 +229,23 @@ dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
                           const float* pixel_scales, const void* grad_y,
                           float* grad_x, float* grad_offset_mask, void* stream);
 
+/* The producer of the offset/weight tensor: the merged linear layer of
+ * [DCNv4 digest] "方法3" (offsets and weights from one linear layer),
+ *   offset_mask[r, j] = sum_k feat[r, k] * weight[j, k] + bias[j],
+ * r < M, j < Nout.  With M = N*Ho*Wo pixels and Nout = G*3K this writes the
+ * offset_mask that dcn4_forward reads (the layer's output order is the
+ * per-pixel [G, 3K] layout).  feat [M, Cin] and weight [Nout, Cin] row-major
+ * in `dtype` (DCN4_BF16 or DCN4_F16; DCN4_F32 is DCN4_ERR_UNSUPPORTED), bias
+ * fp32 [Nout] or NULL; products accumulated in fp32 on the matrix cores, the
+ * sum plus bias rounded to `dtype` to nearest even.  Cin must be a multiple
+ * of 16 (DCN4_ERR_UNSUPPORTED); feat and weight 16-byte aligned, offset_mask
+ * 2-byte, bias 4-byte (DCN4_ERR_MISALIGNED).  M == 0 enqueues nothing.
+ * Asynchronous on `stream`; the caller owns every buffer. */
+dcn4_status dcn4_offset_linear(const void* feat, const void* weight,
+                               const float* bias, void* offset_mask, int64_t M,
+                               int32_t Cin, int32_t Nout, int32_t dtype,
+                               void* stream);
+
 /* Test probe of the sampling geometry: for every (n, yo, xo, g, k), in that
  * order, writes inside (1 if the integer parts passed the -1 <= y0 <= H-1,
  * -1 <= x0 <= W-1 test), and for inside samples the integer parts y0, x0 and

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
               "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
               "dcn4_plan_info", "dcn4_plan_set_option", "dcn4_forward_scaled",
-              "dcn4_backward"):
+              "dcn4_backward", "dcn4_offset_linear"):
         assert n in names
 
 
@@ -275,6 +275,40 @@ class TestForwardValidation:
         # nothing is enqueued, so no pointer is touched and no GPU is needed
         assert d4.dcn4_forward(p0.handle, None, None, None, None, None) == d4.DCN4_OK
         assert p0.ideal_bytes == 0
+
+
+class TestOffsetLinearValidation:
+    """dcn4_offset_linear rejects bad arguments before launching (fake device
+    addresses: none of these calls reaches a launch)."""
+
+    def lin(self, feat=256, weight=512, bias=None, om=1024, M=8, Cin=32, Nout=54,
+            dtype=d4.DCN4_BF16):
+        return d4.dcn4_offset_linear(feat, weight, bias, om, M, Cin, Nout, dtype, None)
+
+    def test_dtype(self):
+        assert self.lin(dtype=d4.DCN4_F32) == d4.DCN4_ERR_UNSUPPORTED
+        assert self.lin(dtype=7) == d4.DCN4_ERR_INVALID_ARG
+
+    def test_sizes(self):
+        assert self.lin(M=-1) == d4.DCN4_ERR_INVALID_ARG
+        assert self.lin(Cin=0) == d4.DCN4_ERR_INVALID_ARG
+        assert self.lin(Nout=0) == d4.DCN4_ERR_INVALID_ARG
+        assert self.lin(Cin=24) == d4.DCN4_ERR_UNSUPPORTED
+        assert self.lin(Cin=1 << 22, Nout=300) == d4.DCN4_ERR_UNSUPPORTED
+
+    def test_null_and_alignment(self):
+        assert self.lin(feat=None) == d4.DCN4_ERR_NULL
+        assert self.lin(weight=None) == d4.DCN4_ERR_NULL
+        assert self.lin(om=None) == d4.DCN4_ERR_NULL
+        assert self.lin(feat=264) == d4.DCN4_ERR_MISALIGNED
+        assert self.lin(weight=520) == d4.DCN4_ERR_MISALIGNED
+        assert self.lin(om=1025) == d4.DCN4_ERR_MISALIGNED
+        assert self.lin(bias=2050) == d4.DCN4_ERR_MISALIGNED
+        assert d4.DCN4Error  # the binding's exception type exists
+
+    def test_empty_is_a_no_op(self):
+        # nothing is enqueued, so no pointer is touched and no GPU is needed
+        assert self.lin(feat=None, weight=None, om=None, M=0) == d4.DCN4_OK
 
 
 @pytest.mark.parametrize("kw", [dict(use_pixel_scales=True),

@@ -189,3 +189,16 @@ def make_inputs(w: Workload, Ho: int, Wo: int, seed: Optional[int] = None,
         lo, hi = (np.float32(v) for v in w.pixel_scale_range)
         pscales = rng.random((N, Ho, Wo, G), dtype=np.float32) * (hi - lo) + lo
     return Inputs(to_raw(x, w.dtype), to_raw(om, w.dtype), scales, pscales)
+
+
+def make_linear_inputs(M: int, Cin: int, Nout: int, dtype: str, seed: int = 7,
+                       with_bias: bool = True):
+    """Inputs of the merged offset/weight layer: features ~ N(0, 1) (a
+    normalised token), weights ~ N(0, 1/Cin) so every output has unit
+    variance, bias ~ N(0, 0.25) in fp32.  Returns raw feat [M, Cin], raw
+    weight [Nout, Cin] in the I/O dtype and the fp32 bias (or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    feat = rng.standard_normal((M, Cin), dtype=np.float32)
+    weight = rng.standard_normal((Nout, Cin), dtype=np.float32) * np.float32(1.0 / np.sqrt(Cin))
+    bias = (rng.standard_normal(Nout, dtype=np.float32) * np.float32(0.5)) if with_bias else None
+    return to_raw(feat, dtype), to_raw(weight, dtype), bias
