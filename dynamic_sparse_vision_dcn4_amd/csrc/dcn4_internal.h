@@ -143,6 +143,8 @@ int32_t tiled_backward_lds(const Plan& p);
 // kLinearCols output columns.
 constexpr int kLinearRows = 128;
 constexpr int kLinearCols = 288;
+// Cin up to which each wave keeps its pixels' features in registers
+constexpr int kLinearRsMaxCin = 384;
 struct LinArgs {
   const char* feat;    // [M, Cin] I/O dtype (16-bit)
   const char* weight;  // [Nout, Cin] I/O dtype
@@ -153,6 +155,7 @@ struct LinArgs {
   uint32_t w_bytes;    // Nout * Cin * 2
   int32_t col_chunks;  // column chunks of 288 per row block
   int32_t nblocks;
+  int32_t vec_store;   // Nout % 4 == 0 and out 8-byte aligned: 8-byte stores
 };
 dcn4_status launch_linear(const void* feat, const void* weight, const float* bias,
                           void* out, int64_t M, int32_t Cin, int32_t Nout, int32_t dtype,

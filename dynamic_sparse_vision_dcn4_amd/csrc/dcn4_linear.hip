@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "dcn4_internal.h"
 
 namespace dcn4 {
@@ -35,6 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kRows = kLinearRows;  // rows per workgroup (4 waves x 32)
@@ -136,6 +139,219 @@ __global__ __launch_bounds__(256) void dcn4_linear_kernel(LinArgs a) {
   }
 }
 
+// Register-stationary form for Cin <= 384, in producer/consumer waves.
+//
+// kRsConsumers consumer waves each own 32 pixels and keep their features for
+// every k in registers (Cin/16 fragments).  They walk the output columns in
+// passes of two 32-wide tiles (two independent accumulation chains), issue
+// the matrix ops and store the results.  kRsProducers producer waves copy each pass's
+// weights (2 x 32 rows of Cin, contiguous in the weight matrix) and bias from
+// L2 straight into LDS with buffer-to-LDS loads, double-buffered, one pass
+// ahead, so the staging holds no registers and every wait on global loads
+// sits in the producers (on gfx9 loads and stores share one completion
+// counter: a wave that stores outputs and then waits for its own loads also
+// waits for its stores).  One wave's buffer-to-LDS loads are bounded by its
+// outstanding requests (about 20 GB/s per CU measured); kRsProducers waves
+// share each pass.
+//
+// The weights are the MFMA's A operand: lane (li, h) of a result holds
+// pixel li, columns 8(e/4) + 4h + e%4.  LDS weight layout: row j of a tile
+// occupies Q + 1 16-byte vectors (Q = Cin/8, one pad vector), so a fragment
+// read (32 rows, one vector each) touches distinct bank groups, and the
+// producer fills one row per instruction from 640 contiguous bytes.
+// Epilogue: each consumer rounds its 32 x 64 outputs into a private LDS area
+// (rows of 128 bytes plus 16 bytes of padding) and reads them back so that
+// one store instruction writes 4 pixel rows of 128 contiguous bytes.
+constexpr int kRsConsumers = 8;                 // consumer waves per workgroup
+constexpr int kRsProducers = 4;                 // producer waves per workgroup
+constexpr int kRsThreads = 64 * (kRsConsumers + kRsProducers);
+constexpr int kRsPixels = 32 * kRsConsumers;    // pixels per workgroup
+constexpr int kRsAhead = 2;                     // fragment-read steps kept in flight
+constexpr int kRsOutRow = 144;                  // bytes per pixel row of the output area
+constexpr int kRsOutBytes = 32 * kRsOutRow;     // one consumer's output area
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
+
+template <int S> struct RsLayout {
+  static constexpr int Q = 2 * S;                 // 16-byte vectors per weight row
+  static constexpr int RS = Q + 1;                // padded row stride (vectors)
+  static constexpr int kTileBytes = 32 * RS * 16; // one column tile's weights
+  static constexpr int kPassBytes = 2 * kTileBytes + 64 * 4;  // + 64 fp32 bias
+  static constexpr int kLdsBytes = 2 * kPassBytes + kRsConsumers * kRsOutBytes;
+};
+
+// buffer-to-LDS loads: lane l's 16 (4) bytes from offset voff of the buffer
+// land at dst + 16 l (4 l), dst uniform; offsets past the range write zeros.
+// The LDS pointer cast exists only in the device pass.
+#define DCN4_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DCN4_LDS_PTR(dst), 16, voff, 0, 0, 0);
+#endif
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DCN4_LDS_PTR(dst), 4, voff, 0, 0, 0);
+#endif
+}
+
+template <int DT, int S>
+__global__ __launch_bounds__(kRsThreads) void dcn4_linear_rs_kernel(LinArgs a) {
+  using L = RsLayout<S>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, li = l & 31, h = l >> 5;
+  const int64_t row0 = (int64_t)blockIdx.x * kRsPixels;
+  const int npass = (a.Nout + 63) >> 6;
+
+  if (wave >= kRsConsumers) {
+    // producer: a pass's 64 weight rows occupy 64 (Q + 1) consecutive LDS
+    // vectors, filled by Q + 1 buffer-to-LDS loads of 64 lanes: lane l of
+    // load i fills vector n = 64 i + l, row n / (Q + 1), input vector
+    // n % (Q + 1); a pad slot loads the row's last vector again (never read).
+    // Rows past Nout read as zeros (range check).
+    const rsrc_t wr = lin_rsrc(a.weight, a.w_bytes);
+    const rsrc_t br = lin_rsrc(a.bias, a.bias ? (uint32_t)a.Nout * 4u : 0u);
+    const int pw = wave - kRsConsumers;
+    auto issue = [&](int p) {
+      char* buf = lds + (p & 1) * L::kPassBytes;
+      const int pass_off = p * 64 * L::Q * 16;
+#pragma unroll 4
+      for (int i = pw; i < L::RS; i += kRsProducers) {
+        const int n = 64 * i + l, j = n / L::RS, q = n - j * L::RS;
+        lds_dma16(wr, buf + i * 1024, pass_off + (j * L::Q + (q < L::Q ? q : L::Q - 1)) * 16);
+      }
+      // bias of the pass's 64 columns (zeros past Nout or without bias)
+      if (pw == 0) lds_dma4(br, buf + 2 * L::kTileBytes, (p * 64 + l) * 4);
+    };
+    // the first pass is requested before the consumers request their
+    // features, so it does not queue behind them
+    issue(0);
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    for (int p = 0; p < npass; ++p) {
+      if (p + 1 < npass) issue(p + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // consumer: this wave's features, pixels past M read as zeros (requested
+  // after the producers have requested the first pass)
+  __syncthreads();
+  const int64_t rows_left = a.M - row0;
+  const uint64_t fbytes = (uint64_t)rows_left * (S * 32u);
+  const rsrc_t fr = lin_rsrc(a.feat + row0 * (S * 32),
+                             (uint32_t)(fbytes < 0x7fffffffu ? fbytes : 0x7fffffffu));
+  u32x4 f[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    f[s] = __builtin_amdgcn_raw_buffer_load_b128(fr, (wave * 32 + li) * (S * 32) + s * 32 + h * 16,
+                                                 0, 0);
+  // wait for the features here, once: inside the pass loop the only
+  // outstanding global operations are then this wave's stores, which nothing
+  // waits for
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  char* ostage = lds + 2 * L::kPassBytes + wave * kRsOutBytes;
+  const int64_t pix0 = row0 + wave * 32;
+  const bool vec_store = a.vec_store;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  __syncthreads();
+  for (int p = 0; p < npass; ++p) {
+    const char* cur = lds + (p & 1) * L::kPassBytes;
+    const char* wrow = cur + li * (L::RS * 16) + h * 16;
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc0[e] = acc1[e] = 0.0f;
+    u32x4 w0[S], w1[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      w0[s] = *reinterpret_cast<const u32x4*>(wrow + s * 32);
+      w1[s] = *reinterpret_cast<const u32x4*>(wrow + L::kTileBytes + s * 32);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      acc0 = Mfma<DT>::run(w0[s], f[s], acc0);
+      acc1 = Mfma<DT>::run(w1[s], f[s], acc1);
+    }
+    // schedule: kRsAhead steps of fragment reads in flight ahead of the
+    // matrix ops
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kRsAhead, 0);
+#pragma unroll
+    for (int s = 0; s < S - kRsAhead; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRsAhead, 0);
+
+    // epilogue: bias, round, pixel-major rows in this wave's output area
+    const float* bl = reinterpret_cast<const float*>(cur + 2 * L::kTileBytes);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const f32x16& acc = t ? acc1 : acc0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cl = 32 * t + 8 * g + 4 * h;
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Mfma<DT>::enc(acc[4 * g + e] + bl[cl + e]);
+        *reinterpret_cast<u32x2*>(ostage + li * kRsOutRow + cl * 2) =
+            u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+      }
+    }
+    // read back: lane l takes 8 bytes (columns 4(l%16)..+3) of row 4k + l/16
+    const int c0 = p * 64 + 4 * (l & 15);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + (l >> 4);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(ostage + r * kRsOutRow + (l & 15) * 8);
+      const int64_t pix = pix0 + r;
+      if (pix >= a.M || c0 >= a.Nout) continue;
+      uint16_t* dst = out + pix * a.Nout + c0;
+      if (vec_store) {
+        *reinterpret_cast<u32x2*>(dst) = v;
+      } else {
+        const uint16_t e4[4] = {(uint16_t)v[0], (uint16_t)(v[0] >> 16), (uint16_t)v[1],
+                                (uint16_t)(v[1] >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < a.Nout) dst[e] = e4[e];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Raises the kernel's dynamic LDS limit to `bytes` on the current device,
+// once per kernel and device (the attribute is per-device state).
+bool rs_lds_attribute_set(void (*fn)(LinArgs), size_t bytes) {
+  constexpr int kMaxDev = 64, kMaxFn = 16;
+  static std::atomic<uintptr_t> done[kMaxDev][kMaxFn];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  const uintptr_t key = reinterpret_cast<uintptr_t>(fn);
+  std::atomic<uintptr_t>* slot = nullptr;
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDev)
+    for (int i = 0; i < kMaxFn; ++i) {
+      const uintptr_t v = done[dev][i].load(std::memory_order_acquire);
+      if (v == key) return true;
+      if (v == 0) { slot = &done[dev][i]; break; }
+    }
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) {
+    note_hip_error(e);
+    return false;
+  }
+  if (slot) {
+    uintptr_t expect = 0;
+    slot->compare_exchange_strong(expect, key, std::memory_order_acq_rel);
+  }
+  return true;
+}
+
 }  // namespace
 
 dcn4_status launch_linear(const void* feat, const void* weight, const float* bias,
@@ -150,16 +366,39 @@ dcn4_status launch_linear(const void* feat, const void* weight, const float* bia
   a.Cin = Cin;
   a.Nout = Nout;
   a.w_bytes = (uint32_t)((int64_t)Nout * Cin * 2);
-  a.col_chunks = (Nout + kCols - 1) / kCols;
-  const int64_t row_blocks = (M + kRows - 1) / kRows;
-  const int64_t blocks = row_blocks * a.col_chunks;
-  if (blocks == 0) return DCN4_OK;
-  if (blocks > 0x7fffffff) return DCN4_ERR_UNSUPPORTED;
-  a.nblocks = (int32_t)blocks;
-  void (*fn)(LinArgs) = dtype == DCN4_BF16 ? dcn4_linear_kernel<DCN4_BF16>
-                                           : dcn4_linear_kernel<DCN4_F16>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  a.vec_store = (Nout % 4 == 0) && (reinterpret_cast<uintptr_t>(out) % 8 == 0);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (Cin % 64 == 0 && Cin <= kLinearRsMaxCin) {
+    const int64_t blocks = (M + kRsPixels - 1) / kRsPixels;
+    if (blocks == 0) return DCN4_OK;
+    if (blocks > 0x7fffffff) return DCN4_ERR_UNSUPPORTED;
+    void (*fn)(LinArgs) = nullptr;
+    size_t lds = 0;
+#define DCN4_RS_CASE(n)                                                              \
+  case n:                                                                           \
+    fn = dtype == DCN4_BF16 ? dcn4_linear_rs_kernel<DCN4_BF16, n>                    \
+                            : dcn4_linear_rs_kernel<DCN4_F16, n>;                   \
+    lds = RsLayout<n>::kLdsBytes;                                                    \
+    break;
+    switch (Cin / 16) {
+      DCN4_RS_CASE(4) DCN4_RS_CASE(8) DCN4_RS_CASE(12)
+      DCN4_RS_CASE(16) DCN4_RS_CASE(20) DCN4_RS_CASE(24)
+      default: return DCN4_ERR_UNSUPPORTED;
+    }
+#undef DCN4_RS_CASE
+    if (!rs_lds_attribute_set(fn, lds)) return DCN4_ERR_HIP;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kRsThreads), lds, st, a);
+  } else {
+    a.col_chunks = (Nout + kCols - 1) / kCols;
+    const int64_t row_blocks = (M + kRows - 1) / kRows;
+    const int64_t blocks = row_blocks * a.col_chunks;
+    if (blocks == 0) return DCN4_OK;
+    if (blocks > 0x7fffffff) return DCN4_ERR_UNSUPPORTED;
+    a.nblocks = (int32_t)blocks;
+    void (*fn)(LinArgs) = dtype == DCN4_BF16 ? dcn4_linear_kernel<DCN4_BF16>
+                                             : dcn4_linear_kernel<DCN4_F16>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     note_hip_error(e);

@@ -68,7 +68,12 @@ def check(got_raw, feat, weight, bias, dt, what, rows=None):
 # with the FlowDCN token width (G = 16 of 27 over 1152 channels)
 CASES = [(1, 16, 1, True), (200, 48, 54, True), (300, 64, 300, False),
          (129, 320, 540, True), (515, 320, 540, False), (260, 1152, 432, True),
-         (77, 1280, 1080, True), (128, 16, 576, True)]
+         (77, 1280, 1080, True), (128, 16, 576, True),
+         # every Cin that keeps the features in registers (64 .. 384 by 64),
+         # with Nout % 4 != 0 (2-byte stores) and == 0 (8-byte stores)
+         (300, 64, 54, True), (64, 128, 540, False), (33, 192, 81, True),
+         (1000, 256, 216, True), (257, 384, 135, True), (130, 384, 32, False),
+         (1, 320, 540, True)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
@@ -95,10 +100,11 @@ def test_linear_full_size_sampled():
     check(got, feat, weight, bias, dt, "full size (sampled rows)", rows=rows)
 
 
-def test_linear_writes_only_its_output():
+@pytest.mark.parametrize("Cin,Nout", [(32, 30), (64, 30), (320, 36)])
+def test_linear_writes_only_its_output(Cin, Nout):
     """Rows past M and columns past Nout are never written: the output sits
     inside a larger buffer whose other bytes keep their sentinel."""
-    M, Cin, Nout, dt = 130, 32, 30, "bf16"
+    M, dt = 130, "bf16"
     feat, weight, bias = make_linear_inputs(M, Cin, Nout, dt, seed=3)
     big = torch.full((M * Nout + 4096,), -7, dtype=torch.int16, device="cuda")
     out = big[:M * Nout].view(TDT[dt]).view(M, Nout)
