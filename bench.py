@@ -72,7 +72,7 @@ def main():
     ap.add_argument("--option", action="append", default=[], metavar="NAME=VALUE",
                     help="plan option (kernel, tile_margin, tile_groups, tile_pad)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=10)
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dcn4_backward) instead of the forward")
     ap.add_argument("--linear", action="store_true",
