@@ -68,7 +68,8 @@ class dcn4_launch_info(ctypes.Structure):
                 ("tile_groups", ctypes.c_int32),
                 ("tile_margin", ctypes.c_int32),
                 ("backward_kernel", ctypes.c_int32),
-                ("backward_lds_bytes", ctypes.c_int32)]
+                ("backward_lds_bytes", ctypes.c_int32),
+                ("tile_slices", ctypes.c_int32)]
 
 # dcn4_option
 DCN4_OPT_CHANNELS_PER_LANE = 0

@@ -184,7 +184,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->channels_per_lane = t.dp;
     info->lanes_per_group = p.D / t.dp;
     const int64_t tiles = int64_t((p.Ho + t.th - 1) / t.th) * ((p.Wo + t.tw - 1) / t.tw);
-    const int64_t per_image = tiles * (p.desc.group / t.gb);
+    const int64_t per_image = tiles * (p.desc.group / t.gb) * t.slices;
     const int64_t imgs = (int64_t(1) << 30) / per_image;
     info->kernel = 2;
     info->block_threads = dcn4::kBlock;
@@ -195,6 +195,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_w = t.tw;
     info->tile_groups = t.gb;
     info->tile_margin = t.margin;
+    info->tile_slices = t.slices;
     return DCN4_OK;
   }
   info->kernel = 1;
@@ -303,7 +304,7 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
   const bool vector_path = p.dp > 0 && aligned_to(x, 16) &&
                            aligned_to(offset_mask, 16) && aligned_to(y, 16);
   if (vector_path && p.tile.ok)
-    s = dcn4::launch_tiled(p, x, offset_mask, group_scales, y, stream);
+    s = dcn4::launch_tiled(p, x, offset_mask, group_scales, pixel_scales, y, stream);
   else
     s = dcn4::launch_forward(p, x, offset_mask, group_scales, pixel_scales, y,
                              stream, vector_path);

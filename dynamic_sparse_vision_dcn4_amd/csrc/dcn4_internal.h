@@ -67,6 +67,8 @@ struct TileArgs {
   const char* x;         // input of this launch's first image
   const char* om;        // offset/weight tensor of this launch's first image
   const float* scales;
+  const float* pscales;  // [pixels, G] from this launch's first image, or null
+  float max_scale;       // group-scale mode: largest scale (0: none)
   char* y;
   int32_t H, W, C, G, D, Ho, Wo;
   int32_t kh, kw, sh, sw, ph, pw, dh, dw;
@@ -75,8 +77,10 @@ struct TileArgs {
   int32_t swz_shift;     // lane-index bit that swaps a lane's vector pairs (-1: none)
   int32_t GB, TH, TW, M; // groups per workgroup, tile, margin
   int32_t WH, WW;        // window rows, cols
-  int32_t PS;            // LDS bytes per window pixel (GB*D*es, maybe padded)
-  int32_t CB;            // bytes of a pixel's GB groups, GB*D*es
+  int32_t PS;            // LDS bytes per window pixel (CB, maybe padded)
+  int32_t CB;            // window bytes per pixel: GB*D*es, or DSL*es when sliced
+  int32_t slices;        // channel slices per group (1: whole groups)
+  int32_t DSL;           // channels per slice (D when not sliced)
   int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
   int32_t wrpp, wpasses; // window rows per staging pass, passes
   int32_t OSU;           // 4-byte offset/weight units per tile pixel
@@ -90,12 +94,13 @@ struct TileArgs {
   uint32_t om_img_bytes; // Ho*Wo*G*3K*es
   uint32_t om_row_bytes; // G*3K*es (a multiple of 4)
   FastDiv div_chunks, div_tx, div_ty, div_cpr, div_cvec, div_upr, div_osu,
-      div_gbl, div_L, div_tw;
+      div_gbl, div_L, div_tw, div_slices;
 };
 
 // Tile shape a plan resolved (ok == 0: the tiled kernel does not apply).
 struct TileShape {
   int32_t ok, dp, gb, th, tw, margin, wh, ww, ps, cb, osu, lds_bytes;
+  int32_t slices;  // channel slices per group (one lane per pixel when > 1)
 };
 
 enum KernelChoice : int32_t { kKernelAuto = 0, kKernelDirect = 1, kKernelTiled = 2 };
@@ -123,7 +128,7 @@ dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
                            const float* scales, const float* pscales, void* y,
                            void* stream, bool vector_path);
 dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
-                         const float* scales, void* y, void* stream);
+                         const float* scales, const float* pscales, void* y, void* stream);
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
                          const float* pscales, int32_t* y0, int32_t* x0,
                          float* lh, float* lw, uint8_t* inside, void* stream);

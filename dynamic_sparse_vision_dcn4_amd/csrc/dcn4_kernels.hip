@@ -498,16 +498,20 @@ struct TileLane {
 };
 
 // One sample point of the tiled kernel.  by/bx: integer base of the point
-// relative to window cell (c, c) (exact floats); returns false when the wave
-// must take the global path for this point (nothing accumulated then).
+// relative to window cell (c, c) (exact floats): the grid point in the
+// standard modes, the centre in group-scale mode, where gy/gx are the grid
+// offsets and sg the lane's group scale (the direct kernel's geometry, so the
+// same fp32 operations); returns false when the wave must take the global
+// path for this point (nothing accumulated then).
 // SQ: the window is square and c is its centre, so the corner cell is inside
 // iff max(|yr|, |xr|) <= ymax; the IEEE maximum propagates NaN, and m*0 is
 // NaN exactly when m is not finite, which folds the weight test in.
 template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ>
 __device__ __forceinline__ bool tile_point(const TileLane& w,
-                                           float by, float bx, float dy, float dx,
-                                           float m, float os, float* acc) {
-  const Loc l = sample_location<MODE>(by, bx, 0.0f, 0.0f, dy, dx, os, 1.0f);
+                                           float by, float bx, float gy, float gx,
+                                           float dy, float dx, float m, float os,
+                                           float sg, float* acc) {
+  const Loc l = sample_location<MODE>(by, bx, gy, gx, dy, dx, os, sg);
   const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
   const float yr = by + fy, xr = bx + fx;  // corner (y0, x0) minus (c, c)
   uint64_t off_window;
@@ -543,11 +547,12 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
 
 // PSC: the LDS bytes per window pixel when known at compile time (one lane
 // owns one whole group, no padding, square window), else 0.
-// Origin of a tiled workgroup: image, tile, window corner and group chunk.
-// The group chunk varies fastest in the (XCD-remapped) workgroup order, so
-// the chunks of one tile run back to back on one XCD.
+// Origin of a tiled workgroup: image, tile, window corner and chunk (a chunk
+// is GB whole groups, or one channel slice of one group).  The chunk varies
+// fastest in the (XCD-remapped) workgroup order, so the chunks of one tile
+// run back to back on one XCD.
 struct TileOrigin {
-  uint32_t n, g0;
+  uint32_t n, g0, s;  // image, first group, channel slice
   int ty0, tx0, wy0, wx0;
 };
 
@@ -555,6 +560,8 @@ __device__ __forceinline__ TileOrigin tile_origin(const TileArgs& a) {
   const uint32_t lb = (uint32_t)xcd_block(blockIdx.x, a.nblocks);
   uint32_t q = fastdiv(lb, a.div_chunks);
   const uint32_t gc = lb - q * (uint32_t)a.chunks;
+  // chunk gc: group chunk gc / slices, channel slice gc % slices
+  const uint32_t gq = fastdiv(gc, a.div_slices);
   uint32_t q2 = fastdiv(q, a.div_tx);
   const uint32_t tx = q - q2 * (uint32_t)a.tiles_x;
   TileOrigin o;
@@ -564,13 +571,15 @@ __device__ __forceinline__ TileOrigin tile_origin(const TileArgs& a) {
   o.tx0 = (int)tx * a.TW;
   o.wy0 = o.ty0 * a.sh - a.ph - a.M;
   o.wx0 = o.tx0 * a.sw - a.pw - a.M;
-  o.g0 = gc * (uint32_t)a.GB;
+  o.g0 = gq * (uint32_t)a.GB;
+  o.s = gc - gq * (uint32_t)a.slices;
   return o;
 }
 
 // Stage the input window of a tile (zeros outside the image) at `lds` in
 // passes of wrpp whole window rows.  A window pixel is PS bytes in LDS: its GB
-// groups' channels, then (when padded) one 16-byte chunk loaded as zeros.
+// groups' channels (or the chunk's channel slice), then (when padded) one
+// 16-byte chunk loaded as zeros.
 // Thread t copies chunk t of every pass, so lane order equals LDS order as
 // the global-to-LDS copy requires, and its column, chunk and column test are
 // fixed.  Returns the input's buffer descriptor for the image.
@@ -593,7 +602,7 @@ __device__ __forceinline__ rsrc_t stage_window(const TileArgs& a, const TileOrig
     int row = wy0 + (int)rp;
     // byte offset of (row, gcol, chunk); used only while it is in the image
     uint32_t off = (uint32_t)row * row_bytes + (uint32_t)gcol * pix_bytes +
-                   g0 * (uint32_t)(a.D * es) + ch * 16u;
+                   g0 * (uint32_t)(a.D * es) + o.s * (uint32_t)a.CB + ch * 16u;
     const uint32_t pass_bytes = (uint32_t)a.wrpp * row_bytes;
     const int row_end = wy0 + a.WH;
     char* dst = lds + wave0 * 16u;
@@ -720,20 +729,27 @@ void dcn4_tile_kernel(TileArgs a) {
   const uint32_t g = g0 + gl;
   const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
       lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
+  // first channel of the lane within the pixel: its group, slice and lane
+  const uint32_t chan = g * (uint32_t)a.D + org.s * (uint32_t)a.DSL + l * DP;
 
+  FwdArgs fa{};  // the geometry reads only the fields FwdArgs and TileArgs share
+  fa.H = a.H; fa.W = a.W; fa.G = a.G; fa.kh = a.kh; fa.kw = a.kw; fa.dh = a.dh; fa.dw = a.dw;
+  fa.offset_scale = a.offset_scale; fa.Hm1 = a.Hm1; fa.Wm1 = a.Wm1;
+  fa.scales = a.scales; fa.pscales = a.pscales; fa.max_scale = a.max_scale;
   // global-path context (points whose corners leave the window)
   LaneCtx c;
   c.pix_bytes = pix_bytes;
   c.row_stride = (uint32_t)a.W * pix_bytes;
-  c.lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
-  c.sg = 1.0f;
+  c.lane_bytes = chan * es;
   c.hy = ((KS ? KS : a.kh) - 1) >> 1;
   c.hx = ((KS ? KS : a.kw) - 1) >> 1;
-  c.by0 = yo * a.sh - a.ph;
-  c.bx0 = xo * a.sw - a.pw;
-  FwdArgs fa{};  // the geometry reads only the fields FwdArgs and TileArgs share
-  fa.H = a.H; fa.W = a.W; fa.kh = a.kh; fa.kw = a.kw; fa.dh = a.dh; fa.dw = a.dw;
-  fa.offset_scale = a.offset_scale; fa.Hm1 = a.Hm1; fa.Wm1 = a.Wm1;
+  // group-scale mode: the lane's scale (pixel counted from the launch's first
+  // image) and the point base at the centre
+  c.sg = (MODE == kGroupScale)
+             ? group_scale(fa, ((uint64_t)n * a.Ho + (uint32_t)yo) * a.Wo + (uint32_t)xo, g)
+             : 1.0f;
+  c.by0 = yo * a.sh - a.ph + (MODE == kGroupScale ? c.hy : 0);
+  c.bx0 = xo * a.sw - a.pw + (MODE == kGroupScale ? c.hx : 0);
 
   TileLane w;
   w.row_lds = (uint32_t)(a.WW * a.PS);
@@ -759,11 +775,12 @@ void dcn4_tile_kernel(TileArgs a) {
 #pragma unroll
   for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
+  constexpr bool GS = MODE == kGroupScale;
   if (KS) {
     float bx[KS ? KS : 1];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) bx[j] = rx0 + (float)(j * a.dw);
-    const float fdh = (float)a.dh;
+    for (int j = 0; j < KS; ++j) bx[j] = GS ? rx0 : rx0 + (float)(j * a.dw);
+    const float fdh = GS ? 0.0f : (float)a.dh;
     float by = ry0;
 #pragma unroll
     for (int i = 0; i < KS; ++i, by += fdh) {
@@ -773,7 +790,9 @@ void dcn4_tile_kernel(TileArgs a) {
         const float dx = io::dec(om[2 * k]);
         const float dy = io::dec(om[2 * k + 1]);
         const float m = io::dec(om[2 * K + k]);
-        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], dy, dx, m, a.offset_scale, acc)) {
+        const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
+        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], gyy, gxx, dy, dx, m,
+                                                    a.offset_scale, c.sg, acc)) {
           const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
           TapData<DT, VEC, NV> d;
           d.load_swapped(xr, tg, r16);
@@ -789,8 +808,11 @@ void dcn4_tile_kernel(TileArgs a) {
       const float dx = io::dec(om[2 * k]);
       const float dy = io::dec(om[2 * k + 1]);
       const float m = io::dec(om[2 * K + k]);
-      const float by = ry0 + (float)(i * a.dh), bx = rx0 + (float)(j * a.dw);
-      if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, dy, dx, m, a.offset_scale, acc)) {
+      const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
+      const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
+      const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
+      if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, gyy, gxx, dy, dx, m,
+                                                  a.offset_scale, c.sg, acc)) {
         const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
         TapData<DT, VEC, NV> d;
         d.load_swapped(xr, tg, r16);
@@ -801,8 +823,7 @@ void dcn4_tile_kernel(TileArgs a) {
 
 #pragma unroll
   for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
-  char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * pix_bytes +
-             (g * (uint32_t)a.D + l * DP) * es;
+  char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * pix_bytes + chan * es;
   char* ype = yp + r16;           // even slots
   char* ypo = yp + (16u - r16);   // odd slots
 #pragma unroll
@@ -1238,6 +1259,14 @@ tile_fn tile_ks(int K3, bool psc) {
 
 template <int DT>
 tile_fn tile_pick(int nv, int mode, int K3, bool psc) {
+  if (mode == kGroupScale) {
+    switch (nv) {
+      case 1: return tile_ks<DT, 1, kGroupScale>(K3, psc);
+      case 2: return tile_ks<DT, 2, kGroupScale>(K3, psc);
+      case 3: return tile_ks<DT, 3, kGroupScale>(K3, psc);
+      default: return tile_ks<DT, 4, kGroupScale>(K3, psc);
+    }
+  }
   if (mode == kStdScaled) {
     switch (nv) {
       case 1: return tile_ks<DT, 1, kStdScaled>(K3, psc);
@@ -1327,9 +1356,12 @@ namespace {
 
 // Tile shape for `gb` groups per workgroup and `dp` channels per lane;
 // false when it does not fit (lanes, staging passes or LDS).
-bool tile_shape(const Plan& p, int32_t dp, int32_t gb, TileShape& t) {
+// slices > 1: chunks of one group's dp channels (one lane per pixel, the
+// window holds the slice only); slices == 1: chunks of gb whole groups.
+bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, TileShape& t) {
   const dcn4_desc& d = p.desc;
-  const int32_t L = p.D / dp;
+  if (slices < 1 || (slices > 1 && (gb != 1 || dp * slices != p.D))) return false;
+  const int32_t L = slices > 1 ? 1 : p.D / dp;
   const int32_t lanes_px = gb * L;
   if (gb < 1 || d.group % gb || lanes_px > kBlock || kBlock % lanes_px) return false;
   const int32_t tp = kBlock / lanes_px;  // tile pixels
@@ -1338,7 +1370,7 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, TileShape& t) {
   const int32_t M = p.tile_margin;
   const int32_t wh = (th - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
   const int32_t ww = (tw - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 2;
-  const int32_t cb = gb * p.D * p.es;
+  const int32_t cb = slices > 1 ? dp * p.es : gb * p.D * p.es;
   if (cb % 16) return false;
   int32_t ps = cb;
   if (p.tile_pad && ((ps / 16) % 2 == 0)) ps += 16;  // odd number of 16-byte chunks
@@ -1354,6 +1386,7 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, TileShape& t) {
   t.ok = 1;
   t.dp = dp; t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww;
   t.ps = ps; t.cb = cb; t.osu = osu; t.lds_bytes = (int32_t)lds;
+  t.slices = slices;
   return true;
 }
 
@@ -1362,7 +1395,7 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, TileShape& t) {
 void resolve_tile(Plan& p) {
   const dcn4_desc& d = p.desc;
   p.tile = TileShape{};
-  if (p.mode == kGroupScale || p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
+  if (p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
   // offset/weight rows must start on 4-byte boundaries (4-byte staging units)
   if ((d.group * 3 * p.K * p.es) % 4) return;
   // channels per lane: the caller's choice, else the plan's default and then
@@ -1372,18 +1405,23 @@ void resolve_tile(Plan& p) {
   if (!p.dp_user && p.dp / 2 >= vec && (p.dp / 2) % vec == 0 && p.D % (p.dp / 2) == 0)
     dps[1] = p.dp / 2;
   TileShape t{};
+  bool found = false;
   for (int32_t dp : dps) {
     if (dp <= 0) continue;
     if (p.tile_groups > 0) {
-      if (tile_shape(p, dp, p.tile_groups, t)) break;
+      if ((found = tile_shape(p, dp, p.tile_groups, 1, t))) break;
       continue;
     }
     // fewest groups per workgroup that fit: the largest output tile
-    bool found = false;
     for (int32_t gb = 1; gb <= d.group && !found; ++gb)
-      if (d.group % gb == 0) found = tile_shape(p, dp, gb, t);
+      if (d.group % gb == 0) found = tile_shape(p, dp, gb, 1, t);
     if (found) break;
   }
+  // a group too wide for whole-group windows (its lanes do not divide the
+  // workgroup, or its window does not fit): one channel slice per workgroup
+  if (!found && p.tile_groups <= 1)
+    for (int32_t dp : dps)
+      if (dp > 0 && p.D / dp > 1 && (found = tile_shape(p, dp, 1, p.D / dp, t))) break;
   p.tile = t;
 }
 
@@ -1396,7 +1434,10 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.offset_scale = d.offset_scale;
   a.Hm1 = (float)(d.H - 1);
   a.Wm1 = (float)(d.W - 1);
-  a.L = p.D / ts.dp;
+  a.L = ts.slices > 1 ? 1 : p.D / ts.dp;
+  a.slices = ts.slices;
+  a.DSL = ts.slices > 1 ? ts.dp : p.D;
+  a.max_scale = d.use_group_scales ? d.max_scale : 0.0f;
   a.swz_shift = p.tile_swizzle > 0 ? p.tile_swizzle - 1 : -1;
   a.GB = ts.gb; a.TH = ts.th; a.TW = ts.tw; a.M = ts.margin;
   a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb;
@@ -1416,7 +1457,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
   a.tiles_y = (p.Ho + ts.th - 1) / ts.th;
-  a.chunks = d.group / ts.gb;
+  a.chunks = d.group / ts.gb * ts.slices;
   a.img_bytes = (uint32_t)((uint64_t)d.H * d.W * d.C * p.es);
   a.om_row_bytes = (uint32_t)(d.group * 3 * p.K * p.es);
   a.om_img_bytes = (uint32_t)((uint64_t)p.Ho * p.Wo * a.om_row_bytes);
@@ -1430,17 +1471,20 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.div_gbl = make_fastdiv((uint32_t)(ts.gb * a.L));
   a.div_L = make_fastdiv((uint32_t)a.L);
   a.div_tw = make_fastdiv((uint32_t)ts.tw);
+  a.div_slices = make_fastdiv((uint32_t)ts.slices);
 }
 
 dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
-                         const float* scales, void* y, void* stream) {
+                         const float* scales, const float* pscales, void* y, void* stream) {
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
   const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
   const int nv = ts.dp / (16 / p.es);
-  // the pixel stride is a compile-time constant when a lane owns a whole
-  // unpadded group (and the window is square: see tile_point)
-  const bool psc = ts.gb == 1 && ts.dp == p.D && ts.ps == 16 * nv && ts.wh == ts.ww;
+  // the pixel stride is a compile-time constant when a lane owns all of an
+  // unpadded window pixel (a whole group or a slice; and the window is
+  // square: see tile_point)
+  const bool psc = ts.gb == 1 && (ts.slices > 1 || ts.dp == p.D) && ts.ps == 16 * nv &&
+                   ts.wh == ts.ww;
   tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc)
              : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc)
                                     : tile_pick<DCN4_F16>(nv, p.mode, K3, psc);
@@ -1449,6 +1493,7 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   a.scales = scales;
   const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
   const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;  // pixel scales per image
   const int64_t per_image = (int64_t)a.tiles_x * a.tiles_y * a.chunks;
   const int32_t imgs = (int32_t)((int64_t(1) << 30) / per_image);
   for (int32_t n0 = 0; n0 < d.N; n0 += imgs) {
@@ -1456,6 +1501,7 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
     a.x = static_cast<const char*>(x) + n0 * x_img;
     a.om = static_cast<const char*>(om) + n0 * om_img;
     a.y = static_cast<char*>(y) + n0 * y_img;
+    a.pscales = pscales ? pscales + n0 * ps_img : nullptr;
     a.nblocks = (int32_t)(nb * per_image);
     hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.lds_bytes,
                        static_cast<hipStream_t>(stream), a);
@@ -1492,7 +1538,8 @@ tile_bwd_fn tile_bwd_pick(int nv) {
 int32_t tiled_backward_lds(const Plan& p) {
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
-  if (!ts.ok || p.mode == kGroupScale || d.kernel_h != 3 || d.kernel_w != 3) return 0;
+  if (!ts.ok || ts.slices != 1 || p.mode == kGroupScale || d.kernel_h != 3 || d.kernel_w != 3)
+    return 0;
   const int32_t L = p.D / ts.dp;
   if (L != 1 && L != 2 && L != 4) return 0;
   return ts.lds_bytes;

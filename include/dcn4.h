@@ -149,6 +149,10 @@ typedef struct {
                                 tensors; calls with grad_x run the direct
                                 kernel                                      */
   int32_t backward_lds_bytes; /* dynamic LDS per tiled-backward workgroup   */
+  int32_t tile_slices;       /* tiled kernel: channel slices per group (1:
+                                a workgroup's window holds whole groups;
+                                > 1: one slice of channels_per_lane
+                                channels of one group, one lane per pixel) */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -177,8 +181,9 @@ typedef enum {
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,
  * DCN4_ERR_INVALID_ARG (unknown option or value out of range),
  * DCN4_ERR_UNSUPPORTED (the tiled kernel was requested but does not apply to
- * this plan: group-scale mode, groups that are not 16-byte multiples, or a
- * window too large for LDS).  Not safe while another thread uses the plan. */
+ * this plan: groups that are not 16-byte multiples, offset/weight rows not
+ * 4-byte aligned, or a window too large for LDS).  Not safe while another
+ * thread uses the plan. */
 dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value);
 
 /* Enqueues the forward pass y = DCNv4(x, offset_mask[, group_scales]) on

@@ -161,29 +161,35 @@ def test_plan_options():
     p.set_option("tile_groups", 4)
     assert p.info()["tile_groups"] == 4 and p.info()["tile_h"] * p.info()["tile_w"] == 64
     # a wide margin first halves the channels per lane (a smaller tile of
-    # lanes); one whose window exceeds 64 KiB of LDS at every tile shape makes
-    # the automatic choice fall back to the direct kernel, and a forced tiled
-    # kernel refuses it
+    # lanes); when no whole-group window fits, one channel slice of a group
+    # per workgroup (one lane per pixel)
     p.set_option("tile_groups", 0)
     p.set_option("tile_margin", 12)
     assert p.info()["kernel"] == 2 and p.info()["channels_per_lane"] == 8
+    assert p.info()["tile_slices"] == 1
     p.set_option("tile_margin", 16)
-    assert p.info()["kernel"] == 1 and p.info()["channels_per_lane"] == 16
-    p.set_option("tile_margin", 4)
-    p.set_option("kernel", 2)
-    with pytest.raises(d4.DCN4Error) as e:
-        p.set_option("tile_margin", 16)
-    assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
-    assert p.info()["tile_margin"] == 4
-    # group-scale plans have no tiled kernel
+    i = p.info()
+    assert i["kernel"] == 2 and i["channels_per_lane"] == 8 and i["tile_slices"] == 2
+    assert (i["tile_h"], i["tile_w"]) == (16, 16)
+    assert i["blocks"] == 2 * 2 * 2 * 4 * 2   # images x tiles (2 x 2) x groups x slices
+    # group-scale plans tile too
     ms = d4.Plan(desc_of(Shape(2, 10, 10, 64, 4, multiscale=True), "bf16"))
-    assert ms.info()["kernel"] == 1
-    with pytest.raises(d4.DCN4Error) as e:
-        ms.set_option("kernel", 2)
-    assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
-    # a window too large for LDS falls back to the direct kernel
+    assert ms.info()["kernel"] == 2 and ms.info()["tile_margin"] == 4
+    # FlowDCN's 72-channel groups: 24-channel slices
+    fl = d4.Plan(desc_of(Shape(2, 32, 32, 1152, 16, multiscale=True), "bf16"))
+    assert fl.info()["kernel"] == 2 and fl.info()["tile_slices"] == 3
+    assert fl.info()["channels_per_lane"] == 24 and fl.info()["backward_kernel"] == 1
+    # a window too large for LDS at every tile shape falls back to the direct
+    # kernel, and a forced tiled kernel refuses it
     big = d4.Plan(desc_of(Shape(1, 64, 64, 64, 1), "f32"))
+    big.set_option("tile_margin", 16)
     assert big.info()["kernel"] == 1
+    big.set_option("tile_margin", 4)
+    big.set_option("kernel", 2)
+    with pytest.raises(d4.DCN4Error) as e:
+        big.set_option("tile_margin", 16)
+    assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
+    assert big.info()["tile_margin"] == 4
 
 
 def test_channels_per_lane_override():

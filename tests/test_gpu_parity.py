@@ -315,6 +315,71 @@ def test_tiled_kernel_margins(dt, margin):
                          dt, f"tiled margin {margin}")
 
 
+# (dtype, D, channels per lane, kernel size, stride, pixel scales, Smax):
+# sliced windows (D 72 in 24-channel slices, D 48 in 16) and whole groups
+# (D 16, 24), 3x3 and 5x5 (the generic point loop), stride 2, FlowDCN's
+# predicted scales with and without the clamp
+GS_TILED = [("bf16", 72, 24, 3, 1, False, 0.0), ("bf16", 72, 24, 3, 1, True, 4.0),
+            ("f16", 48, 16, 3, 1, True, 0.0), ("f32", 16, 8, 3, 1, False, 0.0),
+            ("bf16", 16, 16, 5, 1, True, 2.5), ("bf16", 24, 24, 3, 1, False, 0.0),
+            ("bf16", 16, 16, 3, 2, False, 0.0), ("f16", 72, 24, 5, 1, False, 3.0)]
+
+
+@pytest.mark.parametrize("margin", [0, 2, 6, 10])
+@pytest.mark.parametrize("dt, D, dp, k, st, pix, smax", GS_TILED)
+def test_tiled_group_scale(dt, D, dp, k, st, pix, smax, margin):
+    """FlowDCN's multi-scale geometry on the tiled kernel (centre plus the
+    group scale times grid point plus direction, the lane's scale from the
+    prior, the predicted scale and Smax): bit for bit with the oracle, on
+    the LDS path and the global fallback (margin 0 sends most waves there;
+    the priors reach 4, so every margin leaves some points outside)."""
+    G = 2  # 16-bit offset/weight rows of G*3K values must be 4-byte aligned to tile
+    s = Shape(2, 21, 27, G * D, G, k, k, st, st, k // 2, k // 2,
+              multiscale=True, pixel_scales=pix, max_scale=smax)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=D + k + margin)
+    if pix:
+        rng = np.random.default_rng(300 + D + margin)
+        ps = rng.uniform(0.25, 2.0, (s.N, Ho, Wo, s.G)).astype(np.float32)
+        ps.reshape(-1)[1] = np.nan
+        ps.reshape(-1)[-2] = 0.0
+        inp = workloads.Inputs(inp.x, inp.om, inp.scales, ps)
+    try:
+        plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin)
+    except d4.DCN4Error as e:
+        # a wide margin's window can exceed LDS; margin 0 always fits here
+        assert e.status == d4.DCN4_ERR_UNSUPPORTED and margin > 0
+        return
+    info = plan.info()
+    say(f"tiled group scale {dt} D={D} dp={dp} k={k} s={st} pix={pix} smax={smax} "
+        f"margin {margin}: {info}")
+    assert info["kernel"] == 2
+    y = gpu_forward(plan, inp, dt)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS,
+                         pscales=inp.pscales)
+    check_against_oracle(y, y_or, dt, f"tiled group scale D={D} margin {margin}")
+
+
+@pytest.mark.parametrize("margin", [1, 4])
+@pytest.mark.parametrize("dt, D, dp", [("bf16", 72, 24), ("f32", 24, 8)])
+def test_tiled_channel_slices_standard_mode(dt, D, dp, margin):
+    """Groups whose lanes do not divide the workgroup run one channel slice
+    of a group per workgroup in the standard modes too (and offset_scale
+    0.5): same bits as the oracle."""
+    s = Shape(2, 23, 19, 2 * D, 2, offset_scale=0.5)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=7 + D + margin)
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin)
+    info = plan.info()
+    say(f"sliced standard {dt} D={D} dp={dp} margin {margin}: {info}")
+    assert info["kernel"] == 2 and info["tile_slices"] == D // dp
+    check_against_oracle(gpu_forward(plan, inp, dt),
+                         o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS),
+                         dt, f"sliced standard D={D} margin {margin}")
+
+
 @pytest.mark.parametrize("swizzle", [0, 1, 3, 4, 6])
 @pytest.mark.parametrize("dt, D, dp", [("bf16", 16, 16), ("f32", 16, 8), ("f16", 32, 16),
                                        ("bf16", 64, 32)])
