@@ -98,6 +98,8 @@ class Oracle:
         lib.dcn4o_backward.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P, i64p]
         lib.dcn4o_linear_f64.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int, P, P, P, P, P]
+        lib.dcn4o_dwconv3x3.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int, P, P, P, P, P]
         lib.dcn4o_ideal_bytes.argtypes = [sp, ctypes.c_int]
         lib.dcn4o_ideal_bytes.restype = ctypes.c_int64
         for f in ("dcn4o_bf16_to_f32", "dcn4o_f16_to_f32"):
@@ -259,6 +261,25 @@ class Oracle:
         if r:
             raise ValueError("oracle rejected the call")
         return out, absum
+
+    def dwconv3x3(self, dtype: str, x, w, bias=None):
+        """The depthwise 3x3 convolution (stride 1, zero padding 1) in front of
+        the offset/weight layer: (out fp64 [N,H,W,C], out raw in the I/O dtype
+        from the fp32 evaluation).  x [N,H,W,C] and w [3,3,C] raw in the I/O
+        dtype, bias fp32 [C] or None."""
+        dt = DTYPE_CODES[dtype]
+        x = np.ascontiguousarray(x, dtype=RAW_NP[dt])
+        w = np.ascontiguousarray(w, dtype=RAW_NP[dt])
+        N, H, W, C = x.shape
+        assert w.shape == (3, 3, C)
+        bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        out64 = np.empty((N, H, W, C), np.float64)
+        raw = np.empty((N, H, W, C), RAW_NP[dt])
+        r = self.lib.dcn4o_dwconv3x3(N, H, W, C, dt, self._ptr(x), self._ptr(w),
+                                     self._ptr(bias), self._ptr(out64), self._ptr(raw))
+        if r:
+            raise ValueError("oracle rejected the call")
+        return out64, raw
 
     def ideal_bytes(self, s: Shape, dtype: str) -> int:
         return int(self.lib.dcn4o_ideal_bytes(ctypes.byref(s.c_struct()),

@@ -599,3 +599,35 @@ int dcn4o_linear_f64(int64_t M, int32_t Cin, int32_t Nout, int dtype,
   }
   return 0;
 }
+
+/* ------------------------------------------------ depthwise 3x3 convolution */
+
+int dcn4o_dwconv3x3(int32_t N, int32_t H, int32_t W, int32_t C, int dtype,
+                    const void* x, const void* w, const float* bias,
+                    double* out64, void* out_raw) {
+  if (N < 0 || H < 1 || W < 1 || C < 1) return -1;
+  for (int64_t n = 0; n < N; ++n)
+    for (int32_t y = 0; y < H; ++y)
+      for (int32_t xx = 0; xx < W; ++xx)
+        for (int32_t c = 0; c < C; ++c) {
+          double s64 = 0.0;
+          float acc = 0.0f;
+          for (int i = 0; i < 3; ++i)
+            for (int j = 0; j < 3; ++j) {
+              const int32_t yy = y + i - 1, xs = xx + j - 1;
+              if (yy < 0 || yy >= H || xs < 0 || xs >= W) continue;  /* zero padding */
+              const float wv = load_f32(dtype, w, (int64_t)(i * 3 + j) * C + c);
+              const float xv = load_f32(dtype, x, ((n * H + yy) * W + xs) * (int64_t)C + c);
+              s64 += (double)wv * (double)xv;
+              acc = fmaf(wv, xv, acc);
+            }
+          const int64_t o = ((n * H + y) * W + xx) * (int64_t)C + c;
+          if (bias) {
+            s64 += (double)bias[c];
+            acc = acc + bias[c];
+          }
+          if (out64) out64[o] = s64;
+          if (out_raw) store_io(dtype, out_raw, o, acc);
+        }
+  return 0;
+}

@@ -121,6 +121,19 @@ int dcn4o_linear_f64(int64_t M, int32_t Cin, int32_t Nout, int dtype,
                      const void* feat, const void* weight, const float* bias,
                      double* out, double* absum);
 
+/* The depthwise 3x3 convolution in front of the offset/weight layer
+ * ([DCNv4 digest] "方法3": DCNv3's offset subnetwork without its LayerNorm
+ * and GELU, the separable structure of Xception; optional):
+ *   out[n,y,x,c] = sum_{i,j<3} w[i,j,c] * x[n, y+i-1, x+j-1, c] + bias[c],
+ * stride 1, zero padding 1, x and out [N,H,W,C] and w [3,3,C] in the I/O
+ * dtype, bias fp32 [C] (nullable).  out64 (nullable): the sum in fp64;
+ * out_raw (nullable): the fp32 evaluation -- acc = fma(w, x, acc) over the
+ * nine taps in row-major order (taps outside the image skipped), then
+ * acc + bias, rounded once to the I/O dtype (nearest even).  0 or -1. */
+int dcn4o_dwconv3x3(int32_t N, int32_t H, int32_t W, int32_t C, int dtype,
+                    const void* x, const void* w, const float* bias,
+                    double* out64, void* out_raw);
+
 /* Ideal traffic of one forward pass in bytes: input + output feature maps
  * plus the offset/weight tensor, each read or written once, plus 4G bytes of
  * fp32 scales in multi-scale mode and 4*N*Ho*Wo*G bytes of pixel scales

@@ -815,12 +815,64 @@ def pin_codecs(o):
     assert np.isnan(o.f16_to_f32(o.f32_to_f16(float("nan"))))
 
 
+def pin_dwconv3x3(o):
+    """The depthwise 3x3 convolution in front of the offset/weight layer
+    ([DCNv4 digest] "方法3"):
+    (a) the identity kernel (centre tap 1) returns the input, all dtypes;
+    (b) a single top-left tap moves the image one pixel down and right, with
+        zeros shifted in (fixes the tap orientation and the zero padding);
+    (c) a constant image c: interior outputs c * sum(w) + b, a corner pixel
+        c * (the four taps that stay inside) + b;
+    (d) equals torch's grouped conv2d (groups = C, padding 1; a library
+        routine) in fp64 on dyadic inputs, and the fp32 evaluation equals it
+        exactly there (every product and partial sum is exact);
+    (e) linear in the input."""
+    import torch
+    rng = np.random.default_rng(53)
+    N, H, W, C = 2, 7, 9, 5
+    x = dyadic(rng, (N, H, W, C), -4, 4, 8)
+    for dt in ("f32", "bf16", "f16"):
+        w = np.zeros((3, 3, C), np.float32)
+        w[1, 1, :] = 1.0
+        a, r = o.dwconv3x3(dt, to_raw(x, dt), to_raw(w, dt))
+        exact_equal(a, x.astype(np.float64), f"identity f64 {dt}")
+        exact_equal(from_raw(r, dt), x, f"identity raw {dt}")
+    w = np.zeros((3, 3, C), np.float32)
+    w[0, 0, :] = 0.5
+    a, _ = o.dwconv3x3("f32", x, w)
+    want = np.zeros_like(x, dtype=np.float64)
+    want[:, 1:, 1:, :] = 0.5 * x[:, :-1, :-1, :]
+    exact_equal(a, want, "top-left tap")
+    cst = np.full((1, 4, 6, C), 0.75, np.float32)
+    w = dyadic(rng, (3, 3, C), -2, 2, 4)
+    b = dyadic(rng, (C,), -1, 1, 4)
+    a, _ = o.dwconv3x3("f32", cst, w, b)
+    exact_equal(a[0, 1:3, 1:5, :], np.broadcast_to(0.75 * w.astype(np.float64).sum((0, 1)) + b,
+                                                 (2, 4, C)), "constant interior")
+    exact_equal(a[0, 0, 0, :], 0.75 * w[1:, 1:, :].astype(np.float64).sum((0, 1)) + b,
+                "constant corner")
+    w = dyadic(rng, (3, 3, C), -2, 2, 16)
+    a, r = o.dwconv3x3("f32", x, w, b)
+    ref = torch.nn.functional.conv2d(
+        torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2),
+        torch.from_numpy(w.astype(np.float64)).permute(2, 0, 1).unsqueeze(1),
+        torch.from_numpy(b.astype(np.float64)), padding=1, groups=C).permute(0, 2, 3, 1).numpy()
+    exact_equal(a, ref, "grouped conv2d")
+    exact_equal(r, ref, "fp32 evaluation on exact data")
+    x2 = dyadic(rng, (N, H, W, C), -4, 4, 8)
+    a1, _ = o.dwconv3x3("f32", x, w)
+    a2, _ = o.dwconv3x3("f32", x2, w)
+    a3, _ = o.dwconv3x3("f32", x + x2, w)
+    exact_equal(a3, a1 + a2, "linearity")
+
+
 ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
             pin_affine_reproduction, pin_depthwise_conv, pin_zero_padding,
             pin_partition_of_unity, pin_linearity, pin_multiscale,
             pin_pixel_scales, pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
             pin_exact_rational, pin_geometry, pin_codecs, pin_backward_weights,
-            pin_backward_adjoint, pin_backward_offsets, pin_offset_linear]
+            pin_backward_adjoint, pin_backward_offsets, pin_offset_linear,
+            pin_dwconv3x3]
 
 
 if __name__ == "__main__":

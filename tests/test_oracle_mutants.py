@@ -103,6 +103,15 @@ MUTANTS = {
     "linear_bias_lost": sub("out[r * Nout + j] = acc + b;", "out[r * Nout + j] = acc;"),
     "linear_last_feature_lost": sub("for (int32_t k = 0; k < Cin; ++k) {\n        const double t",
                                     "for (int32_t k = 0; k < Cin - 1; ++k) {\n        const double t"),
+    # the depthwise 3x3 convolution
+    "dwconv_taps_flipped": sub("const int32_t yy = y + i - 1, xs = xx + j - 1;",
+                               "const int32_t yy = y + 1 - i, xs = xx + 1 - j;"),
+    "dwconv_taps_transposed": sub("const float wv = load_f32(dtype, w, (int64_t)(i * 3 + j) * C + c);",
+                                  "const float wv = load_f32(dtype, w, (int64_t)(j * 3 + i) * C + c);"),
+    "dwconv_bias_lost": sub("s64 += (double)bias[c];\n            acc = acc + bias[c];",
+                            "acc = acc + bias[c];"),
+    "dwconv_border_wrapped": sub("if (yy < 0 || yy >= H || xs < 0 || xs >= W) continue;  /* zero padding */",
+                                 "if (yy < 0 || yy >= H) continue;"),
     # group bookkeeping
     "group_channels_interleaved": sub("int c = g * D + d;", "int c = d * s->G + g;"),
     "group_row_shared": sub("const int64_t row = (p * G + g) * 3 * K;",
