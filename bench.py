@@ -78,6 +78,9 @@ def main():
     ap.add_argument("--linear", action="store_true",
                     help="time the offset/weight linear layer (dcn4_offset_linear) "
                          "that produces the workload's offset/weight tensor")
+    ap.add_argument("--dwconv", action="store_true",
+                    help="time the depthwise 3x3 convolution (dcn4_dwconv3x3) on the "
+                         "workload's input feature map")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="instead of the operator, run plain device copies of MIB "
                          "MiB (the scale reference for the HBM byte counters)")
@@ -104,6 +107,8 @@ def main():
         return bench_backward(args, torch, np, workloads, d4, name, w)
     if args.linear:
         return bench_linear(args, torch, np, workloads, d4, name, w)
+    if args.dwconv:
+        return bench_dwconv(args, torch, np, workloads, d4, name, w)
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
@@ -343,6 +348,54 @@ def bench_linear(args, torch, np, workloads, d4, name, w):
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(tfs, 2),
         "pct_mfma_peak": round(100.0 * tfs / MFMA_BF16_PEAK_TFLOPS, 2)}), flush=True)
+
+
+def bench_dwconv(args, torch, np, workloads, d4, name, w):
+    """One step = dcn4_dwconv3x3 over the workload's input feature map
+    [N, H, W, C] with a [3, 3, C] weight and fp32 bias.  Ideal bytes: input,
+    weight and bias read once, output written once."""
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    es = 4 if w.dtype == "f32" else 2
+    n_el = w.N * w.H * w.W * w.C
+    ideal = 2 * n_el * es + 9 * w.C * es + 4 * w.C
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    nsets = args.sets or max(2, math.ceil((1 << 30) / max(ideal, 1)))
+    rng = np.random.default_rng(w.seed)
+    wt = torch.from_numpy(rng.standard_normal((3, 3, w.C), dtype=np.float32) / 3).to(tdt).to(dev)
+    bias = torch.from_numpy(rng.standard_normal(w.C, dtype=np.float32)).to(dev)
+    sets = []
+    for r in range(nsets):
+        x = torch.from_numpy(np.random.default_rng(w.seed + r).standard_normal(
+            (w.N, w.H, w.W, w.C), dtype=np.float32)).to(tdt).to(dev)
+        sets.append((x, torch.empty_like(x)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        x, out = sets[i % nsets]
+        d4.dwconv3x3(x, wt, bias, out=out, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbs = ideal / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "depthwise 3x3 GB/s (ideal bytes: input, weight, bias read; output written)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded normal inputs and weights)",
+        "config": {"workload": name, "pass": "dwconv3x3", "N": w.N, "H": w.H, "W": w.W,
+                   "C": w.C, "ideal_bytes": ideal, "input_sets": nsets},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
 
 
 def copy_reference(torch, mib, steps):

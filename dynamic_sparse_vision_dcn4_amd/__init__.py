@@ -96,6 +96,8 @@ _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_offset_linear.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, _P]
+_lib.dcn4_dwconv3x3.argtypes = [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
 _lib.dcn4_destroy.argtypes = [_P]
 _lib.dcn4_destroy.restype = None
 _lib.dcn4_status_string.argtypes = [ctypes.c_int]
@@ -104,7 +106,8 @@ _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
-           "dcn4_probe_geometry", "dcn4_backward", "dcn4_offset_linear"):
+           "dcn4_probe_geometry", "dcn4_backward", "dcn4_offset_linear",
+           "dcn4_dwconv3x3"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -180,6 +183,36 @@ def offset_linear(feat, weight, bias=None, out=None, stream=None):
                             M, Cin, Nout, dt, stream)
     if st != DCN4_OK:
         raise DCN4Error(st, "dcn4_offset_linear")
+    return out
+
+
+def dcn4_dwconv3x3(x: int, weight: int, bias: Optional[int], out: int, N: int, H: int,
+                   W: int, C: int, dtype: int, stream: Optional[int]) -> int:
+    return _lib.dcn4_dwconv3x3(x, weight, bias, out, N, H, W, C, dtype, stream)
+
+
+def dwconv3x3(x, weight, bias=None, out=None, stream=None):
+    """out [N,H,W,C] = depthwise 3x3 convolution of x [N,H,W,C] with weight
+    [3,3,C] (stride 1, zero padding 1) plus bias (fp32 [C] or None); torch
+    CUDA tensors of one dtype."""
+    dt = {torch.float32: DCN4_F32, torch.bfloat16: DCN4_BF16,
+          torch.float16: DCN4_F16}.get(x.dtype)
+    if dt is None or weight.dtype != x.dtype:
+        raise TypeError("x and weight must share a dtype: fp32, bf16 or fp16")
+    N, H, W, C = x.shape
+    if tuple(weight.shape) != (3, 3, C) or not x.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("x [N,H,W,C] and weight [3,3,C] must be contiguous")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != C):
+        raise ValueError("bias must be fp32 [C]")
+    if out is None:
+        out = torch.empty_like(x)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = dcn4_dwconv3x3(x.data_ptr(), weight.data_ptr(),
+                        None if bias is None else bias.data_ptr(), out.data_ptr(),
+                        N, H, W, C, dt, stream)
+    if st != DCN4_OK:
+        raise DCN4Error(st, "dcn4_dwconv3x3")
     return out
 
 

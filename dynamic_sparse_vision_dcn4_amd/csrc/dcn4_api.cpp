@@ -369,6 +369,29 @@ dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float
   return DCN4_OK;
 }
 
+dcn4_status dcn4_dwconv3x3(const void* x, const void* weight, const float* bias, void* out,
+                           int32_t N, int32_t H, int32_t W, int32_t C, int32_t dtype,
+                           void* stream) {
+  if (dtype != DCN4_F32 && dtype != DCN4_BF16 && dtype != DCN4_F16)
+    return fail(DCN4_ERR_INVALID_ARG, "dtype must be DCN4_F32, DCN4_BF16 or DCN4_F16");
+  if (N < 0 || H < 1 || W < 1 || C < 1)
+    return fail(DCN4_ERR_INVALID_ARG, "N must be >= 0 and H, W, C >= 1");
+  if (N == 0) return DCN4_OK;
+  if (!x || !weight || !out) return fail(DCN4_ERR_NULL, "x, weight and out must not be NULL");
+  const uintptr_t es = dtype == DCN4_F32 ? 4 : 2;
+  if (!aligned_to(x, es) || !aligned_to(weight, es) || !aligned_to(out, es) ||
+      (bias && !aligned_to(bias, 4)))
+    return fail(DCN4_ERR_MISALIGNED, "tensors must be aligned to the element size, bias to 4");
+  if (x == out) return fail(DCN4_ERR_INVALID_ARG, "out must not alias x");
+  const bool vector_path = (C * es) % 16 == 0 && aligned_to(x, 16) && aligned_to(weight, 16) &&
+                           aligned_to(out, 16) && (!bias || aligned_to(bias, 16));
+  dcn4_status s = dcn4::launch_dwconv(x, weight, bias, out, N, H, W, C, dtype, vector_path,
+                                      stream);
+  if (s != DCN4_OK) return fail(s, s == DCN4_ERR_HIP ? dcn4::last_hip_error()
+                                                     : "more than 2^31 workgroups");
+  return DCN4_OK;
+}
+
 dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
                                 const float* group_scales,
                                 const float* pixel_scales, int32_t* y0,

@@ -162,6 +162,21 @@ struct LinArgs {
   int32_t nblocks;
   int32_t vec_store;   // Nout % 4 == 0 and out 8-byte aligned: 8-byte stores
 };
+// Depthwise 3x3 convolution (the optional stage before the offset/weight
+// layer): a lane per (segment of pixels along a row, VEC channels).
+struct DwArgs {
+  const char* x;       // [N,H,W,C] I/O dtype
+  const char* w;       // [3,3,C] I/O dtype
+  const float* bias;   // [C] fp32, or null
+  char* out;           // [N,H,W,C] I/O dtype
+  int32_t H, W, C, cv; // cv: channel vectors per pixel, C / VEC
+  int32_t segs;        // pixel segments per row
+  int64_t lanes;
+  int32_t nblocks;
+};
+dcn4_status launch_dwconv(const void* x, const void* w, const float* bias, void* out,
+                          int32_t N, int32_t H, int32_t W, int32_t C, int32_t dtype,
+                          bool vector_path, void* stream);
 dcn4_status launch_linear(const void* feat, const void* weight, const float* bias,
                           void* out, int64_t M, int32_t Cin, int32_t Nout, int32_t dtype,
                           void* stream);

@@ -55,6 +55,17 @@ __device__ __forceinline__ int lin_xcd_block(int b, int nb) {
   return x * q + min(x, r) + (b >> 3);
 }
 
+// 16-bit codecs of the depthwise convolution (bf16/fp16 <-> fp32, round to
+// nearest even on the way out).
+template <int DT> __device__ __forceinline__ float dw_dec(uint32_t h) {
+  if constexpr (DT == DCN4_BF16) return __uint_as_float(h << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+template <int DT> __device__ __forceinline__ uint16_t dw_enc(float f) {
+  if constexpr (DT == DCN4_BF16) return __builtin_bit_cast(uint16_t, (__bf16)f);
+  else return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 template <int DT> struct Mfma;
 template <> struct Mfma<DCN4_BF16> {
   __device__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
@@ -323,6 +334,142 @@ __global__ __launch_bounds__(kRsThreads) void dcn4_linear_rs_kernel(LinArgs a) {
   }
 }
 
+// ------------------------------------------------ depthwise 3x3 convolution
+// The optional stage in front of the offset/weight layer ([DCNv4 digest]
+// "方法3": DCNv3's offset subnetwork without its LayerNorm and GELU):
+//   out[n,y,x,c] = sum_{i,j<3} w[i,j,c] * x[n, y+i-1, x+j-1, c] + bias[c],
+// stride 1, zero padding 1, channel-last.  A lane owns VEC consecutive
+// channels (16 bytes on the vector path, one element on the element path) of
+// a segment of kDwSeg pixels along a row: it keeps its nine weight vectors in
+// registers and slides a 3x3 window of input vectors along the segment, so
+// each output needs three new loads, fetched one output ahead.  fp32 fma over the nine taps in
+// row-major order, a tap outside the image skipped (so a non-finite weight
+// cannot leak into the padding), then the bias, one rounding to the I/O
+// dtype.  Consecutive lanes cover a segment's channels, then the next
+// segment, so loads and stores of a wave are contiguous runs; the XCD-aware
+// block order keeps a band of image rows (the three rows a tap row reads)
+// in one XCD's L2.
+constexpr int kDwSeg = 16;  // output pixels per lane along a row
+
+// Raw input vector of (row yy, column xs): 16 bytes (vector path) or one
+// element widened to its bit pattern (element path); zeros when !in.
+template <int DT, int VEC>
+__device__ __forceinline__ u32x4 dw_load(const DwArgs& a, int64_t img, int32_t yy, int32_t xs,
+                                         int32_t c0, bool in) {
+  constexpr int es = DT == DCN4_F32 ? 4 : 2;
+  const int64_t off = ((img * a.H + yy) * a.W + xs) * (int64_t)a.C + c0;
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (in) {
+    if constexpr (VEC > 1) r = *reinterpret_cast<const u32x4*>(a.x + off * es);
+    else if constexpr (es == 4) r[0] = reinterpret_cast<const uint32_t*>(a.x)[off];
+    else r[0] = reinterpret_cast<const uint16_t*>(a.x)[off];
+  }
+  return r;
+}
+
+// Element e of a raw vector as fp32.
+template <int DT, int VEC>
+__device__ __forceinline__ float dw_elem(const u32x4& r, int e) {
+  if constexpr (DT == DCN4_F32) return __uint_as_float(r[e]);
+  else if constexpr (VEC > 1) return dw_dec<DT>((r[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+  else return dw_dec<DT>(r[0]);
+}
+
+template <int DT, int VEC>
+__global__ __launch_bounds__(256) void dcn4_dwconv_kernel(DwArgs a) {
+  constexpr int es = DT == DCN4_F32 ? 4 : 2;
+  const int lb = lin_xcd_block(blockIdx.x, a.nblocks);
+  const int64_t lane = (int64_t)lb * 256 + threadIdx.x;
+  if (lane >= a.lanes) return;
+  // lane -> (image, row, segment, channel vector)
+  const int64_t seg = lane / a.cv;
+  const int32_t c0 = (int32_t)(lane - seg * a.cv) * VEC;
+  const int64_t row = seg / a.segs;              // n * H + y
+  const int32_t x0 = (int32_t)(seg - row * a.segs) * kDwSeg;
+  const int64_t img = row / a.H;
+  const int32_t y = (int32_t)(row - img * a.H);
+  // the nine weight vectors, widened once
+  float wv[9][VEC];
+#pragma unroll
+  for (int t = 0; t < 9; ++t) {
+    const int64_t woff = (int64_t)t * a.C + c0;
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if constexpr (VEC > 1) r = *reinterpret_cast<const u32x4*>(a.w + woff * es);
+    else if constexpr (es == 4) r[0] = reinterpret_cast<const uint32_t*>(a.w)[woff];
+    else r[0] = reinterpret_cast<const uint16_t*>(a.w)[woff];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) wv[t][e] = dw_elem<DT, VEC>(r, e);
+  }
+  float bv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) bv[e] = a.bias ? a.bias[c0 + e] : 0.0f;
+  const bool row_ok[3] = {y >= 1, true, y + 1 < a.H};
+  // raw window columns x-1, x, x+1 of rows y-1, y, y+1; column x+2 is
+  // fetched one output ahead
+  u32x4 win[3][3], nxt[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    win[i][0] = dw_load<DT, VEC>(a, img, y + i - 1, x0 - 1, c0, row_ok[i] && x0 >= 1);
+    win[i][1] = dw_load<DT, VEC>(a, img, y + i - 1, x0, c0, row_ok[i]);
+    win[i][2] = dw_load<DT, VEC>(a, img, y + i - 1, x0 + 1, c0, row_ok[i] && x0 + 1 < a.W);
+  }
+  char* dst = a.out + ((row * a.W + x0) * (int64_t)a.C + c0) * es;
+#pragma unroll
+  for (int p = 0; p < kDwSeg; ++p) {
+    const int32_t x = x0 + p;
+    if (x >= a.W) break;
+    if (p + 1 < kDwSeg) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        nxt[i] = dw_load<DT, VEC>(a, img, y + i - 1, x + 2, c0, row_ok[i] && x + 2 < a.W);
+    }
+    const bool col_ok[3] = {x >= 1, true, x + 1 < a.W};
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (!row_ok[i]) continue;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (!col_ok[j]) continue;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[e] = __builtin_fmaf(wv[i * 3 + j][e], dw_elem<DT, VEC>(win[i][j], e), acc[e]);
+      }
+    }
+    if (a.bias) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + bv[e];
+    }
+    // the empty asm keeps each fp32 sum a value of its own, so the conversion
+    // below is a separate rounding (not fused with the last add)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) asm volatile("" : "+v"(acc[e]));
+    if constexpr (VEC > 1) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (es == 4)
+          o[q] = __float_as_uint(acc[q]);
+        else
+          o[q] = (uint32_t)dw_enc<DT>(acc[2 * q]) | ((uint32_t)dw_enc<DT>(acc[2 * q + 1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(dst) = o;
+    } else {
+      if constexpr (es == 4) *reinterpret_cast<float*>(dst) = acc[0];
+      else *reinterpret_cast<uint16_t*>(dst) = dw_enc<DT>(acc[0]);
+    }
+    dst += (int64_t)a.C * es;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      win[i][0] = win[i][1];
+      win[i][1] = win[i][2];
+      win[i][2] = nxt[i];
+    }
+  }
+}
+
 // Raises the kernel's dynamic LDS limit to `bytes` on the current device,
 // once per kernel and device (the attribute is per-device state).
 bool rs_lds_attribute_set(void (*fn)(LinArgs), size_t bytes) {
@@ -353,6 +500,45 @@ bool rs_lds_attribute_set(void (*fn)(LinArgs), size_t bytes) {
 }
 
 }  // namespace
+
+dcn4_status launch_dwconv(const void* x, const void* w, const float* bias, void* out,
+                          int32_t N, int32_t H, int32_t W, int32_t C, int32_t dtype,
+                          bool vector_path, void* stream) {
+  DwArgs a{};
+  a.x = static_cast<const char*>(x);
+  a.w = static_cast<const char*>(w);
+  a.bias = bias;
+  a.out = static_cast<char*>(out);
+  a.H = H; a.W = W; a.C = C;
+  const int vec = vector_path ? (dtype == DCN4_F32 ? 4 : 8) : 1;
+  a.cv = C / vec;
+  a.segs = (W + kDwSeg - 1) / kDwSeg;
+  a.lanes = (int64_t)N * H * a.segs * a.cv;
+  const int64_t blocks = (a.lanes + 255) / 256;
+  if (blocks == 0) return DCN4_OK;
+  if (blocks > 0x7fffffff) return DCN4_ERR_UNSUPPORTED;
+  a.nblocks = (int32_t)blocks;
+  void (*fn)(DwArgs) = nullptr;
+  switch (dtype) {
+    case DCN4_F32:
+      fn = vector_path ? dcn4_dwconv_kernel<DCN4_F32, 4> : dcn4_dwconv_kernel<DCN4_F32, 1>;
+      break;
+    case DCN4_BF16:
+      fn = vector_path ? dcn4_dwconv_kernel<DCN4_BF16, 8> : dcn4_dwconv_kernel<DCN4_BF16, 1>;
+      break;
+    default:
+      fn = vector_path ? dcn4_dwconv_kernel<DCN4_F16, 8> : dcn4_dwconv_kernel<DCN4_F16, 1>;
+      break;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    note_hip_error(e);
+    return DCN4_ERR_HIP;
+  }
+  return DCN4_OK;
+}
 
 dcn4_status launch_linear(const void* feat, const void* weight, const float* bias,
                           void* out, int64_t M, int32_t Cin, int32_t Nout, int32_t dtype,

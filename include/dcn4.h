@@ -251,6 +251,24 @@ dcn4_status dcn4_offset_linear(const void* feat, const void* weight,
                                int32_t Cin, int32_t Nout, int32_t dtype,
                                void* stream);
 
+/* The optional stage in front of the offset/weight layer: a depthwise 3x3
+ * convolution ([DCNv4 digest] "方法3": DCNv3's offset subnetwork without its
+ * LayerNorm and GELU, the separable structure of Xception; dropping it is
+ * allowed when latency matters more),
+ *   out[n,y,x,c] = sum_{i,j<3} weight[i,j,c] * x[n, y+i-1, x+j-1, c] + bias[c],
+ * stride 1, zero padding 1.  x and out [N,H,W,C] and weight [3,3,C] (i along
+ * H, j along W; a PyTorch depthwise weight [C,1,3,3] permuted to (2,3,0)) in
+ * `dtype`, bias fp32 [C] or NULL.  fp32 arithmetic in a fixed order: an fma
+ * per tap in row-major order, taps outside the image contributing nothing,
+ * then the bias, one rounding to `dtype` (nearest even); the result does not
+ * depend on the launch shape.  Pointers aligned to the element size (bias to
+ * 4 bytes; DCN4_ERR_MISALIGNED); out must not alias x (DCN4_ERR_INVALID_ARG).
+ * N == 0 enqueues nothing.  Asynchronous on `stream`; the caller owns every
+ * buffer. */
+dcn4_status dcn4_dwconv3x3(const void* x, const void* weight, const float* bias,
+                           void* out, int32_t N, int32_t H, int32_t W, int32_t C,
+                           int32_t dtype, void* stream);
+
 /* Test probe of the sampling geometry: for every (n, yo, xo, g, k), in that
  * order, writes inside (1 if the integer parts passed the -1 <= y0 <= H-1,
  * -1 <= x0 <= W-1 test), and for inside samples the integer parts y0, x0 and

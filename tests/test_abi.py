@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
               "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
               "dcn4_plan_info", "dcn4_plan_set_option", "dcn4_forward_scaled",
-              "dcn4_backward", "dcn4_offset_linear"):
+              "dcn4_backward", "dcn4_offset_linear", "dcn4_dwconv3x3"):
         assert n in names
 
 
@@ -315,6 +315,34 @@ class TestOffsetLinearValidation:
     def test_empty_is_a_no_op(self):
         # nothing is enqueued, so no pointer is touched and no GPU is needed
         assert self.lin(feat=None, weight=None, om=None, M=0) == d4.DCN4_OK
+
+
+class TestDwconvValidation:
+    """dcn4_dwconv3x3 rejects bad arguments before launching (fake device
+    addresses: none of these calls reaches a launch)."""
+
+    def dw(self, x=256, w=512, bias=None, out=1024, N=1, H=4, W=5, C=16,
+           dtype=d4.DCN4_BF16):
+        return d4.dcn4_dwconv3x3(x, w, bias, out, N, H, W, C, dtype, None)
+
+    def test_arguments(self):
+        assert self.dw(dtype=5) == d4.DCN4_ERR_INVALID_ARG
+        assert self.dw(N=-1) == d4.DCN4_ERR_INVALID_ARG
+        assert self.dw(H=0) == d4.DCN4_ERR_INVALID_ARG
+        assert self.dw(C=0) == d4.DCN4_ERR_INVALID_ARG
+        assert self.dw(out=256) == d4.DCN4_ERR_INVALID_ARG   # out aliases x
+
+    def test_null_and_alignment(self):
+        assert self.dw(x=None) == d4.DCN4_ERR_NULL
+        assert self.dw(w=None) == d4.DCN4_ERR_NULL
+        assert self.dw(out=None) == d4.DCN4_ERR_NULL
+        assert self.dw(x=257) == d4.DCN4_ERR_MISALIGNED
+        assert self.dw(out=1025) == d4.DCN4_ERR_MISALIGNED
+        assert self.dw(x=258, dtype=d4.DCN4_F32) == d4.DCN4_ERR_MISALIGNED
+        assert self.dw(bias=2050) == d4.DCN4_ERR_MISALIGNED
+
+    def test_empty_is_a_no_op(self):
+        assert self.dw(x=None, w=None, out=None, N=0) == d4.DCN4_OK
 
 
 @pytest.mark.parametrize("kw", [dict(use_pixel_scales=True),
