@@ -355,7 +355,7 @@ dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float
   // Nout rounded up to the chunk width) and one block of feature rows
   if ((int64_t(Nout) + dcn4::kLinearCols) * Cin * 2 > 0x7fffffff ||
       int64_t(dcn4::kLinearRows + 1) * Cin * 2 > 0x7fffffff)
-    return fail(DCN4_ERR_UNSUPPORTED, "Cin * (Nout + 288) beyond 2^30 elements");
+    return fail(DCN4_ERR_UNSUPPORTED, "Cin * (Nout + 128) beyond 2^30 elements");
   if (M == 0) return DCN4_OK;
   if (!feat || !weight || !offset_mask)
     return fail(DCN4_ERR_NULL, "feat, weight and offset_mask must not be NULL");

@@ -144,10 +144,11 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
 // 0 when it does not apply.
 int32_t tiled_backward_lds(const Plan& p);
 // Arguments of the merged offset/weight linear layer (dcn4_linear.hip).
-// Offset/weight linear layer: a workgroup owns kLinearRows rows and
-// kLinearCols output columns.
+// Offset/weight linear layer: the K-streamed kernel's workgroup owns
+// kLinearRows pixels and kLinearCols output columns (buffer offsets stay
+// 32-bit when (Nout + kLinearCols) * Cin * 2 < 2^31).
 constexpr int kLinearRows = 128;
-constexpr int kLinearCols = 288;
+constexpr int kLinearCols = 128;
 // Cin up to which each wave keeps its pixels' features in registers
 constexpr int kLinearRsMaxCin = 384;
 struct LinArgs {
@@ -158,7 +159,7 @@ struct LinArgs {
   int64_t M;
   int32_t Cin, Nout;
   uint32_t w_bytes;    // Nout * Cin * 2
-  int32_t col_chunks;  // column chunks of 288 per row block
+  int32_t col_chunks;  // column tiles per pixel block (K-streamed kernel)
   int32_t nblocks;
   int32_t vec_store;   // Nout % 4 == 0 and out 8-byte aligned: 8-byte stores
 };

@@ -40,10 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kRows = kLinearRows;  // rows per workgroup (4 waves x 32)
-constexpr int kColTiles = 9;        // 32-column tiles per wave
-constexpr int kCols = 32 * kColTiles;
-static_assert(kRows == 128 && kCols == kLinearCols, "workgroup tile");
 
 __device__ __forceinline__ rsrc_t lin_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -82,70 +78,128 @@ template <> struct Mfma<DCN4_F16> {
   __device__ static uint16_t enc(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 };
 
+// K-streamed form for every other Cin (a multiple of 16): a workgroup owns
+// 128 output columns x 128 pixels; its four waves own 64 x 64 each (2 x 2
+// MFMA tiles).  Both operands pass through LDS kGmBK inputs at a time,
+// double-buffered: the next stage is loaded into registers while the matrix cores
+// work on this one, then written to the other LDS buffer (no stores happen
+// in the loop, so waiting for those loads never waits for stores).  LDS rows
+// are padded by 8 elements (16 bytes), which puts the 16 rows of a
+// half-wave fragment read on distinct bank groups.  The weights are the A
+// operand, so a lane's results are 4 consecutive output columns of one
+// pixel.  The column tiles of one pixel block are consecutive in the
+// XCD-aware order, so the block's features are read from HBM once and from
+// L2 afterwards.
+constexpr int kGmBM = 128, kGmBN = 128, kGmBK = 64;
+static_assert(kGmBM == kLinearRows && kGmBN == kLinearCols, "tile sizes the API checks");
+constexpr int kGmRow = kGmBK + 8;  // padded LDS row, elements
+constexpr int kGmVpr = kGmBK / 8;  // 16-byte vectors per staged row
+constexpr int kGmPass = kGmBM * kGmVpr / 256;  // staged vectors per thread and operand
+
 template <int DT>
-__global__ __launch_bounds__(256) void dcn4_linear_kernel(LinArgs a) {
+__global__ __launch_bounds__(256) void dcn4_linear_gemm_kernel(LinArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sF[2][kGmBM * kGmRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kGmBN * kGmRow];
   const int lb = lin_xcd_block(blockIdx.x, a.nblocks);
-  const int bx = lb / a.col_chunks, by = lb - bx * a.col_chunks;
-  const int64_t row0 = (int64_t)bx * kRows;
-  const int col0 = by * kCols;
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int li = l & 31, lk = (l >> 5) * 8;
+  const int bm = lb / a.col_chunks, bn = lb - bm * a.col_chunks;
+  const int64_t row0 = (int64_t)bm * kGmBM;
+  const int col0 = bn * kGmBN;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, li = l & 31, h = l >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int Cin = a.Cin;
 
-  // features of this workgroup's rows; rows past M read zeros (range check)
+  // features of the block's rows and weight rows of its columns; rows past
+  // M or Nout read as zeros
   const int64_t rows_left = a.M - row0;
-  const uint64_t fbytes = (uint64_t)rows_left * a.Cin * 2u;
-  const rsrc_t fr = lin_rsrc(a.feat + row0 * a.Cin * 2, (uint32_t)(fbytes < 0x7fffffffu ? fbytes : 0x7fffffffu));
-  const rsrc_t wr = lin_rsrc(a.weight, a.w_bytes);  // columns past Nout read zeros
-  const uint32_t a_off = (uint32_t)((wave * 32 + li) * a.Cin + lk) * 2u;
-  uint32_t b_off[kColTiles];
+  const uint64_t fbytes = (uint64_t)rows_left * Cin * 2u;
+  const rsrc_t fr = lin_rsrc(a.feat + row0 * Cin * 2,
+                             (uint32_t)(fbytes < 0x7fffffffu ? fbytes : 0x7fffffffu));
+  const uint64_t wbytes = (uint64_t)(a.Nout - col0) * Cin * 2u;
+  const rsrc_t wr = lin_rsrc(a.weight + (int64_t)col0 * Cin * 2,
+                             (uint32_t)(wbytes < 0x7fffffffu ? wbytes : 0x7fffffffu));
+  // staging: thread t moves 16-byte vector (row t/kGmVpr + (256/kGmVpr) p,
+  // inputs 8 (t%kGmVpr)..) of each operand, p < kGmPass
+  constexpr int kRowsPerPass = 256 / kGmVpr;
+  const int sr = tid / kGmVpr, sq = tid % kGmVpr;
+  u32x4 gf[kGmPass], gw[kGmPass];
+  auto gload = [&](int k0) {
+    const bool kin = k0 + 8 * sq < Cin;  // inputs past Cin are zero in both operands
 #pragma unroll
-  for (int t = 0; t < kColTiles; ++t) b_off[t] = (uint32_t)((col0 + 32 * t + li) * a.Cin + lk) * 2u;
-
-  f32x16 acc[kColTiles];
-#pragma unroll
-  for (int t = 0; t < kColTiles; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-
-  // two register sets used in turn: the fragments of one 16-wide step are in
-  // flight while the matrix cores work on the other.  A load past the last
-  // step reads the next row's inputs, or zeros past the buffer's range; its
-  // products are never issued.
-  u32x4 a0f, a1f, b0f[kColTiles], b1f[kColTiles];
-  auto load = [&](u32x4& af, u32x4* bf, int k0) {
-    const uint32_t kb = (uint32_t)k0 * 2u;
-    af = __builtin_amdgcn_raw_buffer_load_b128(fr, (int)(a_off + kb), 0, 0);
-#pragma unroll
-    for (int t = 0; t < kColTiles; ++t)
-      bf[t] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(b_off[t] + kb), 0, 0);
+    for (int p = 0; p < kGmPass; ++p) {
+      const int off = ((sr + kRowsPerPass * p) * Cin + k0 + 8 * sq) * 2;
+      gf[p] = __builtin_amdgcn_raw_buffer_load_b128(fr, off, 0, 0);
+      gw[p] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+      if (!kin) gf[p] = gw[p] = u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  const int steps = a.Cin >> 4;
-  load(a0f, b0f, 0);
-#pragma unroll 1
-  for (int s = 0; s + 1 < steps; s += 2) {
-    load(a1f, b1f, 16 * (s + 1));
+  auto sstore = [&](int st) {
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) acc[t] = Mfma<DT>::run(a0f, b0f[t], acc[t]);
-    load(a0f, b0f, 16 * (s + 2));
+    for (int p = 0; p < kGmPass; ++p) {
+      *reinterpret_cast<u32x4*>(&sF[st][(sr + kRowsPerPass * p) * kGmRow + 8 * sq]) = gf[p];
+      *reinterpret_cast<u32x4*>(&sW[st][(sr + kRowsPerPass * p) * kGmRow + 8 * sq]) = gw[p];
+    }
+  };
+
+  f32x16 acc[2][2];
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) acc[t] = Mfma<DT>::run(a1f, b1f[t], acc[t]);
-  }
-  if (steps & 1) {
+  for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) acc[t] = Mfma<DT>::run(a0f, b0f[t], acc[t]);
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tj][tp][e] = 0.0f;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int k0 = 0, st = 0; k0 < Cin; k0 += kGmBK, st ^= 1) {
+    const bool more = k0 + kGmBK < Cin;
+    if (more) gload(k0 + kGmBK);
+#pragma unroll
+    for (int kk = 0; kk < kGmBK; kk += 16) {
+      if (k0 + kk >= Cin) break;
+      u32x4 fw[2], ff[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        fw[t] = *reinterpret_cast<const u32x4*>(&sW[st][(wn * 64 + t * 32 + li) * kGmRow + kk + 8 * h]);
+        ff[t] = *reinterpret_cast<const u32x4*>(&sF[st][(wm * 64 + t * 32 + li) * kGmRow + kk + 8 * h]);
+      }
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) acc[tj][tp] = Mfma<DT>::run(fw[tj], ff[tp], acc[tj][tp]);
+    }
+    if (more) sstore(st ^ 1);
+    __syncthreads();
   }
 
-  // epilogue: bias, round to the I/O dtype, store in om's layout
+  // epilogue: element e of tile (tj, tp) is output column col0 + 64 wn +
+  // 32 tj + 8(e/4) + 4h + e%4 of pixel row0 + 64 wm + 32 tp + li
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
-  for (int t = 0; t < kColTiles; ++t) {
-    const int col = col0 + 32 * t + li;
-    if (col >= a.Nout) continue;
-    const float b = a.bias ? a.bias[col] : 0.0f;
+  for (int tp = 0; tp < 2; ++tp) {
+    const int64_t pix = row0 + wm * 64 + tp * 32 + li;
+    if (pix >= a.M) continue;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t row = row0 + wave * 32 + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
-      if (row < a.M) out[row * a.Nout + col] = Mfma<DT>::enc(acc[t][e] + b);
+    for (int tj = 0; tj < 2; ++tj) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = col0 + wn * 64 + tj * 32 + 8 * g + 4 * h;
+        if (col >= a.Nout) continue;
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float b = (a.bias && col + e < a.Nout) ? a.bias[col + e] : 0.0f;
+          v[e] = Mfma<DT>::enc(acc[tj][tp][4 * g + e] + b);
+        }
+        uint16_t* dst = out + pix * a.Nout + col;
+        if (a.vec_store) {
+          *reinterpret_cast<u32x2*>(dst) = u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < a.Nout) dst[e] = (uint16_t)v[e];
+        }
+      }
     }
   }
 }
@@ -575,14 +629,14 @@ dcn4_status launch_linear(const void* feat, const void* weight, const float* bia
     if (!rs_lds_attribute_set(fn, lds)) return DCN4_ERR_HIP;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kRsThreads), lds, st, a);
   } else {
-    a.col_chunks = (Nout + kCols - 1) / kCols;
-    const int64_t row_blocks = (M + kRows - 1) / kRows;
+    a.col_chunks = (Nout + kGmBN - 1) / kGmBN;
+    const int64_t row_blocks = (M + kGmBM - 1) / kGmBM;
     const int64_t blocks = row_blocks * a.col_chunks;
     if (blocks == 0) return DCN4_OK;
     if (blocks > 0x7fffffff) return DCN4_ERR_UNSUPPORTED;
     a.nblocks = (int32_t)blocks;
-    void (*fn)(LinArgs) = dtype == DCN4_BF16 ? dcn4_linear_kernel<DCN4_BF16>
-                                             : dcn4_linear_kernel<DCN4_F16>;
+    void (*fn)(LinArgs) = dtype == DCN4_BF16 ? dcn4_linear_gemm_kernel<DCN4_BF16>
+                                             : dcn4_linear_gemm_kernel<DCN4_F16>;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, st, a);
   }
   const hipError_t e = hipGetLastError();
