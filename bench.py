@@ -75,6 +75,10 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=10)
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dcn4_backward) instead of the forward")
+    ap.add_argument("--grads", choices=("both", "x", "om"), default="both",
+                    help="backward: the gradients asked for")
+    ap.add_argument("--scatter", action="store_true",
+                    help="backward: grad_x with fp32 atomics instead of the bucket gather")
     ap.add_argument("--linear", action="store_true",
                     help="time the offset/weight linear layer (dcn4_offset_linear) "
                          "that produces the workload's offset/weight tensor")
@@ -227,10 +231,12 @@ def main():
 
 
 def bench_backward(args, torch, np, workloads, d4, name, w):
-    """One step = dcn4_backward on one batch: grad_x cleared and accumulated,
-    grad_offset_mask written.  Ideal bytes: x, the offset/weight tensor and
-    grad_y read once in the I/O dtype, grad_x and grad_offset_mask written once
-    in fp32."""
+    """One step = dcn4_backward_ws on one batch: grad_x (gathered through a
+    workspace allocated once before the timed region, or with --scatter added
+    with fp32 atomics) and grad_offset_mask written; --grads x / om asks for
+    one of them.  Ideal bytes: the inputs the asked gradients depend on
+    (grad_x: offset/weight tensor and grad_y; grad_offset_mask: also x) read
+    once in the I/O dtype, the gradients written once in fp32."""
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
@@ -240,7 +246,9 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
     nx = w.N * w.H * w.W * w.C
     ny = w.N * Ho * Wo * w.C
     nom = w.N * Ho * Wo * w.G * 3 * w.K
-    ideal = (nx + nom + ny) * es + (nx + nom) * 4
+    want_x, want_om = args.grads in ("both", "x"), args.grads in ("both", "om")
+    ideal = ((nom + ny + (nx if want_om else 0)) * es +
+             ((nx if want_x else 0) + (nom if want_om else 0)) * 4)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -257,14 +265,19 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
         gy = workloads.to_raw(rng.standard_normal((w.N, Ho, Wo, w.C), dtype=np.float32), w.dtype)
         sc = None if inp.scales is None else torch.from_numpy(inp.scales).to(dev)
         ps = None if inp.pscales is None else torch.from_numpy(inp.pscales).to(dev)
-        gx = torch.empty((w.N, w.H, w.W, w.C), dtype=torch.float32, device=dev)
-        gom = torch.empty(plan.om_shape(), dtype=torch.float32, device=dev)
+        gx = (torch.empty((w.N, w.H, w.W, w.C), dtype=torch.float32, device=dev)
+              if want_x else None)
+        gom = torch.empty(plan.om_shape(), dtype=torch.float32, device=dev) if want_om else None
         sets.append((dev_tensor(inp.x), dev_tensor(inp.om), dev_tensor(gy), sc, ps, gx, gom))
+    ws_bytes = plan.backward_workspace_bytes() if want_x and not args.scatter else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     torch.cuda.synchronize()
 
     def step(i):
         x, om, gy, sc, ps, gx, gom = sets[i % nsets]
-        plan.backward(x, om, gy, sc, ps, grad_x=gx, grad_om=gom, stream=stream.cuda_stream)
+        plan.backward(x, om, gy, sc, ps, want_x=want_x, want_om=want_om, grad_x=gx,
+                      grad_om=gom, stream=stream.cuda_stream, workspace=ws,
+                      scatter=args.scatter)
 
     for i in range(args.warmup):
         step(i)
@@ -284,8 +297,10 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded, the workload's shapes and distributions)",
-        "config": {"workload": name, "pass": "backward", "ideal_bytes": ideal,
-                   "input_sets": nsets},
+        "config": {"workload": name, "pass": "backward", "grads": args.grads,
+                   "grad_x": ("scatter" if args.scatter else "gather") if want_x else None,
+                   "workspace_bytes": ws_bytes, "bucket_capacity": plan.info()["bucket_capacity"],
+                   "ideal_bytes": ideal, "input_sets": nsets},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "kernel_source": kernel_source_digest()}), flush=True)
 

@@ -69,7 +69,8 @@ class dcn4_launch_info(ctypes.Structure):
                 ("tile_margin", ctypes.c_int32),
                 ("backward_kernel", ctypes.c_int32),
                 ("backward_lds_bytes", ctypes.c_int32),
-                ("tile_slices", ctypes.c_int32)]
+                ("tile_slices", ctypes.c_int32),
+                ("bucket_capacity", ctypes.c_int32)]
 
 # dcn4_option
 DCN4_OPT_CHANNELS_PER_LANE = 0
@@ -78,9 +79,11 @@ DCN4_OPT_TILE_MARGIN = 2
 DCN4_OPT_TILE_GROUPS = 3
 DCN4_OPT_TILE_PAD = 4
 DCN4_OPT_TILE_SWIZZLE = 5
+DCN4_OPT_BUCKET_CAPACITY = 6
 OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
            "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
-           "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE}
+           "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE,
+           "bucket_capacity": DCN4_OPT_BUCKET_CAPACITY}
 
 
 _P = ctypes.c_void_p
@@ -94,6 +97,8 @@ _lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
 _lib.dcn4_forward_scaled.argtypes = [_P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_backward_ws.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P]
+_lib.dcn4_backward_workspace_size.argtypes = [_P, ctypes.POINTER(ctypes.c_uint64)]
 _lib.dcn4_offset_linear.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, _P]
 _lib.dcn4_dwconv3x3.argtypes = [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
@@ -106,7 +111,8 @@ _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
-           "dcn4_probe_geometry", "dcn4_backward", "dcn4_offset_linear",
+           "dcn4_probe_geometry", "dcn4_backward", "dcn4_backward_ws",
+           "dcn4_backward_workspace_size", "dcn4_offset_linear",
            "dcn4_dwconv3x3"):
     getattr(_lib, _f).restype = ctypes.c_int
 
@@ -155,6 +161,21 @@ def dcn4_backward(plan, x: int, offset_mask: int, group_scales: Optional[int],
                   grad_offset_mask: Optional[int], stream: Optional[int]) -> int:
     return _lib.dcn4_backward(plan, x, offset_mask, group_scales, pixel_scales, grad_y,
                               grad_x, grad_offset_mask, stream)
+
+
+def dcn4_backward_ws(plan, x: int, offset_mask: int, group_scales: Optional[int],
+                     pixel_scales: Optional[int], grad_y: int, grad_x: Optional[int],
+                     grad_offset_mask: Optional[int], workspace: Optional[int],
+                     workspace_bytes: int, stream: Optional[int]) -> int:
+    return _lib.dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y,
+                                 grad_x, grad_offset_mask, workspace, workspace_bytes, stream)
+
+
+def dcn4_backward_workspace_size(plan):
+    """(status, bytes)."""
+    n = ctypes.c_uint64(0)
+    st = _lib.dcn4_backward_workspace_size(plan, ctypes.byref(n) if plan is not None else None)
+    return st, n.value
 
 
 def dcn4_offset_linear(feat: int, weight: int, bias: Optional[int], offset_mask: int,
@@ -369,10 +390,21 @@ class Plan:
             raise DCN4Error(st, "dcn4_forward")
         return out
 
+    def backward_workspace_bytes(self) -> int:
+        """Device workspace the gathered grad_x needs (dcn4_backward_workspace_size)."""
+        st, n = dcn4_backward_workspace_size(self._h)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_backward_workspace_size")
+        return n
+
     def backward(self, x, om, grad_y, scales=None, pixel_scales=None, want_x=True,
-                 want_om=True, grad_x=None, grad_om=None, stream=None):
+                 want_om=True, grad_x=None, grad_om=None, stream=None, workspace=None,
+                 scatter=False):
         """(grad_x [N,H,W,C] fp32 or None, grad_om [N,Ho,Wo,G,3K] fp32 or
-        None) for the upstream gradient grad_y [N,Ho,Wo,C]."""
+        None) for the upstream gradient grad_y [N,Ho,Wo,C].  grad_x is
+        gathered through a workspace (a uint8 device tensor of at least
+        backward_workspace_bytes(); allocated here when not given), or with
+        scatter=True added with fp32 atomics and no workspace."""
         import torch
         d = self.desc
         dt = _torch_dtype(d.dtype)
@@ -392,16 +424,26 @@ class Plan:
             self._check(grad_x, (d.N, d.H, d.W, d.C), torch.float32, "grad_x")
         if grad_om is not None:
             self._check(grad_om, self.om_shape(), torch.float32, "grad_offset_mask")
+        ws_ptr, ws_bytes = None, 0
+        if grad_x is not None and not scatter:
+            need = self.backward_workspace_bytes()
+            if need and workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            if need:
+                if workspace.dtype != torch.uint8 or workspace.device != x.device:
+                    raise ValueError("workspace must be a uint8 tensor on x's device")
+                ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
-        st = dcn4_backward(self._h, x.data_ptr(), om.data_ptr(),
-                           None if scales is None else scales.data_ptr(),
-                           None if pixel_scales is None else pixel_scales.data_ptr(),
-                           grad_y.data_ptr(),
-                           None if grad_x is None else grad_x.data_ptr(),
-                           None if grad_om is None else grad_om.data_ptr(), stream)
+        st = dcn4_backward_ws(self._h, x.data_ptr(), om.data_ptr(),
+                              None if scales is None else scales.data_ptr(),
+                              None if pixel_scales is None else pixel_scales.data_ptr(),
+                              grad_y.data_ptr(),
+                              None if grad_x is None else grad_x.data_ptr(),
+                              None if grad_om is None else grad_om.data_ptr(),
+                              ws_ptr, ws_bytes, stream)
         if st != DCN4_OK:
-            raise DCN4Error(st, "dcn4_backward")
+            raise DCN4Error(st, "dcn4_backward_ws")
         return grad_x, grad_om
 
     def probe_geometry(self, om, scales=None, stream=None, pixel_scales=None):

@@ -7,6 +7,8 @@
 
 #include <new>
 
+#include <hip/hip_runtime_api.h>
+
 #include "dcn4.h"
 #include "dcn4_internal.h"
 
@@ -179,6 +181,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
                               ? dcn4::tiled_backward_lds(p) : 0;
   info->backward_kernel = bwd_lds > 0 ? 2 : 1;
   info->backward_lds_bytes = bwd_lds;
+  info->bucket_capacity = (int32_t)dcn4::bucket_capacity(p);
   if (vec && p.tile.ok) {
     const dcn4::TileShape& t = p.tile;
     info->channels_per_lane = t.dp;
@@ -256,6 +259,11 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
       if (value < 0 || value > 6) return fail(DCN4_ERR_INVALID_ARG, "tile swizzle must be 0-6");
       q.tile_swizzle = value;
       break;
+    case DCN4_OPT_BUCKET_CAPACITY:
+      if (value < 0 || value > 1024)
+        return fail(DCN4_ERR_INVALID_ARG, "bucket capacity must be 0-1024");
+      q.bucket_cap = value;
+      break;
     default:
       return fail(DCN4_ERR_INVALID_ARG, "unknown option");
   }
@@ -321,22 +329,71 @@ dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
   return dcn4_forward_scaled(plan, x, offset_mask, group_scales, nullptr, y, stream);
 }
 
+dcn4_status dcn4_backward_workspace_size(const dcn4_plan* plan, uint64_t* bytes) {
+  if (!plan || !bytes) return fail(DCN4_ERR_NULL, "plan or bytes is NULL");
+  *bytes = dcn4::backward_workspace_bytes(plan->p);
+  return DCN4_OK;
+}
+
+static dcn4_status check_backward(const dcn4::Plan& p, const void* x, const void* om,
+                                  const float* scales, const float* pscales, const void* gy,
+                                  const float* gx, const float* gom) {
+  const dcn4_status s = check_io(p, x, om, scales, pscales, gy, true);
+  if (s != DCN4_OK) return s;
+  if ((gx && !aligned_to(gx, 4)) || (gom && !aligned_to(gom, 4)))
+    return fail(DCN4_ERR_MISALIGNED, "gradient outputs must be 4-byte aligned");
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x, const void* offset_mask,
+                             const float* group_scales, const float* pixel_scales,
+                             const void* grad_y, float* grad_x, float* grad_offset_mask,
+                             void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  dcn4_status s = check_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                                 grad_offset_mask);
+  if (s != DCN4_OK) return s;
+  const uint64_t need = dcn4::backward_workspace_bytes(p);
+  if (workspace && need) {
+    if (!aligned_to(workspace, 256))
+      return fail(DCN4_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(DCN4_ERR_INVALID_ARG, "workspace smaller than dcn4_backward_workspace_size");
+  }
+  if (p.desc.N == 0) return DCN4_OK;
+  const bool vector_path = p.dp > 0 && aligned_to(x, 16) && aligned_to(offset_mask, 16) &&
+                           aligned_to(grad_y, 16);
+  s = dcn4::launch_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                            grad_offset_mask, need ? workspace : nullptr, stream, vector_path);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
 dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
                           const void* offset_mask, const float* group_scales,
                           const float* pixel_scales, const void* grad_y,
                           float* grad_x, float* grad_offset_mask, void* stream) {
   if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
-  const dcn4::Plan& p = plan->p;
-  dcn4_status s = check_io(p, x, offset_mask, group_scales, pixel_scales, grad_y, true);
-  if (s != DCN4_OK || p.desc.N == 0) return s;
-  if ((grad_x && !aligned_to(grad_x, 4)) || (grad_offset_mask && !aligned_to(grad_offset_mask, 4)))
-    return fail(DCN4_ERR_MISALIGNED, "gradient outputs must be 4-byte aligned");
-  const bool vector_path = p.dp > 0 && aligned_to(x, 16) && aligned_to(offset_mask, 16) &&
-                           aligned_to(grad_y, 16);
-  s = dcn4::launch_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
-                            grad_offset_mask, stream, vector_path);
-  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
-  return DCN4_OK;
+  const uint64_t need = dcn4::backward_workspace_bytes(plan->p);
+  if (!grad_x || !need || plan->p.desc.N == 0)
+    return dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                            grad_offset_mask, nullptr, 0, stream);
+  // validated before allocating, so a rejected call allocates nothing
+  dcn4_status s = check_backward(plan->p, x, offset_mask, group_scales, pixel_scales, grad_y,
+                                 grad_x, grad_offset_mask);
+  if (s != DCN4_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, need, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DCN4_ERR_HIP, "allocating the backward workspace failed");
+  }
+  s = dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                       grad_offset_mask, ws, need, stream);
+  if (hipFreeAsync(ws, st) != hipSuccess && s == DCN4_OK)
+    return fail(DCN4_ERR_HIP, "freeing the backward workspace failed");
+  return s;
 }
 
 dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float* bias,

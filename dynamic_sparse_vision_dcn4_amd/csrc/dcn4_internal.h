@@ -116,6 +116,7 @@ struct Plan {
   // options (dcn4_plan_set_option) and the tile shape they resolve to
   int32_t kernel_choice, tile_margin, tile_groups, tile_pad, tile_swizzle;
   int32_t dp_user;       // 1: channels per lane set by the caller
+  int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
   TileShape tile;
 };
 
@@ -132,14 +133,21 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
                          const float* pscales, int32_t* y0, int32_t* x0,
                          float* lh, float* lw, uint8_t* inside, void* stream);
-// Backward pass: zero grad_x (if given) and accumulate it, write grad_om (if
-// given); both fp32.
+// Backward pass: write grad_x (if given) and grad_om (if given); both fp32.
+// With a workspace of backward_workspace_bytes(p) bytes (256-byte aligned)
+// grad_x is gathered from per-cell buckets; without one it is cleared and
+// accumulated with atomics.
 // vector_path: x, offset_mask and grad_y are 16-byte aligned (the tiled
 // backward may run).
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
-                            const void* gy, float* gx, float* gom, void* stream,
-                            bool vector_path);
+                            const void* gy, float* gx, float* gom, void* ws,
+                            void* stream, bool vector_path);
+// Workspace of the gathered grad_x (0: a single image's indices exceed the
+// kernels' 32-bit counters, so only the atomic path applies).
+uint64_t backward_workspace_bytes(const Plan& p);
+// Records per bucket the plan's gathered grad_x uses.
+uint32_t bucket_capacity(const Plan& p);
 // LDS bytes of the tiled backward (offset/weight gradients only) for the plan,
 // 0 when it does not apply.
 int32_t tiled_backward_lds(const Plan& p);

@@ -1147,6 +1147,395 @@ __global__ __launch_bounds__(kBlock) void dcn4_fill_zero_kernel(float* p, uint64
   for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
+// ------------------------------------------------------------ grad_x by gathering
+// dL/dx is the adjoint of the bilinear gather: an inside sample (output pixel
+// p, group g, point k) in the cell whose top-left corner is (y0, x0) adds
+// fl(m*w_r) * dL/dy[p, c] to corner r of that cell, for each of the group's
+// channels c.  As a scatter that is 4*D fp32 atomic lanes per sample; device
+// atomics are served per 64-byte request (about 25e9 requests/s on this GPU,
+// a request carrying the lanes of one instruction that fall in one 64-byte
+// segment), so scattered atomics cost a request each.  Here the scatter
+// becomes a gather:
+//  1. bucket: a workgroup takes a tile of output pixels of one group and
+//     counts its samples per cell in LDS (integer LDS atomics, which run at
+//     full rate); one device atomic per non-empty cell of the tile's cell
+//     window then reserves that cell's slots, and consecutive cells of a
+//     window row are consecutive keys, so these coalesce; every sample
+//     writes the record {p, m, lh, lw} to its slot of the bucket of (image,
+//     group, cell), key = row*(W+1) + x0+1 with row = (n*G + g)*(H+1) +
+//     y0+1.  Slot t of the buckets of one row is stored for all W+1 columns
+//     side by side (record index (row*cap + t)*(W+1) + x0+1), so the gather's
+//     lanes, which take consecutive columns, read consecutive records.  A
+//     sample whose cell falls outside the window takes its slot with its own
+//     device atomic.
+//  2. gather: 2^lg_shift lanes per (input pixel (y, x), group) read the
+//     records of the four cells that have the pixel as a corner -- cell
+//     (y, x) as corner 00, (y, x-1) as 01, (y-1, x) as 10, (y-1, x-1) as 11
+//     -- and accumulate fl(m*w_r) * dL/dy per channel in registers (fused
+//     multiply-add); every sum is written once, so grad_x needs no clearing.
+//  3. overflow: a bucket holds `cap` records; a sample whose slot is beyond
+//     it is listed instead, and this launch adds its products with atomics
+//     after the gather has written grad_x.
+// The coefficients fl(m*w_r) are those of the atomic scatter; the order of
+// each sum follows the slots, which depend on the order atomics were
+// granted, so it varies from run to run as the scatter's does.
+constexpr int kBucketNS = 8;  // samples per thread of a bucket workgroup
+
+struct GatherArgs {
+  FwdArgs f;           // geometry, om, scales, pscales of this chunk
+  const char* gy;      // [imgs, Ho, Wo, C] I/O dtype
+  float* gx;           // [imgs, H, W, C] fp32
+  uint32_t* counts;    // [keys] records appended per bucket (may exceed cap)
+  uint32_t* listed;    // [1] samples whose slot is beyond the capacity
+  uint32_t* list;      // [samples] their ids
+  u32x4* recs;         // [rows][cap][W+1] {p within its image, m, lh, lw} as bits
+  uint32_t cap;
+  uint32_t samples;    // samples of this chunk, < 2^31
+  uint32_t waves;      // gather waves of this chunk
+  int32_t K, lg_shift, nchunk;  // nchunk: vectors of V channels per group
+  int32_t nblocks;     // gather workgroups
+  int32_t strips, bands;        // gather: column strips and row bands per (n, g)
+  // bucket tiles: TH x TW output pixels (TW = 1 << tw_shift), their cell
+  // window of WH x WW cells starting at (ty0*sh + wy_off, tx0*sw + wx_off)
+  int32_t TH, tw_shift, WH, WW, wy_off, wx_off, tiles_x, tiles_y;
+  FastDiv div_K, div_kw, div_G, div_W, div_H, div_WW, div_tx, div_ty;
+  FastDiv div_strips, div_bands;
+};
+
+struct SampleRec {
+  uint32_t p;        // output pixel within its image
+  int y0, x0;
+  float m, lh, lw;
+  bool inside;
+};
+
+// The forward's sampling decisions (same device functions, same operation
+// order) for point k of group g at output pixel (yo, xo); pix counts output
+// pixels from the chunk's first image.
+template <int DT, int MODE>
+__device__ __forceinline__ SampleRec sample_at(const GatherArgs& ga, uint32_t pix, uint32_t yo,
+                                               uint32_t xo, uint32_t g, int k) {
+  typedef Io<DT> io;
+  const FwdArgs& a = ga.f;
+  const int i = (int)fastdiv((uint32_t)k, ga.div_kw), j = k - i * a.kw;
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(a.om) +
+                               ((uint64_t)pix * (uint32_t)a.G + g) * (uint32_t)(3 * ga.K);
+  const float dx = io::dec(om[2 * k]);
+  const float dy = io::dec(om[2 * k + 1]);
+  SampleRec r;
+  r.m = io::dec(om[2 * ga.K + k]);
+  float by, bx, gyy = 0.0f, gxx = 0.0f, sg = 1.0f;
+  if (MODE == kGroupScale) {
+    const int hy = (a.kh - 1) >> 1, hx = (a.kw - 1) >> 1;
+    by = (float)((int)yo * a.sh - a.ph + hy);
+    bx = (float)((int)xo * a.sw - a.pw + hx);
+    gyy = (float)(i - hy);
+    gxx = (float)(j - hx);
+    sg = group_scale(a, pix, g);
+  } else {
+    by = (float)((int)yo * a.sh - a.ph + i * a.dh);
+    bx = (float)((int)xo * a.sw - a.pw + j * a.dw);
+  }
+  const Cell c = locate(sample_location<MODE>(by, bx, gyy, gxx, dy, dx, a.offset_scale, sg),
+                        a.Hm1, a.Wm1);
+  r.p = yo * (uint32_t)a.Wo + xo;
+  r.y0 = c.y0;
+  r.x0 = c.x0;
+  r.lh = c.lh;
+  r.lw = c.lw;
+  r.inside = c.inside;
+  return r;
+}
+
+__device__ __forceinline__ u32x4 pack_record(const SampleRec& r) {
+  u32x4 rec;
+  rec[0] = r.p;
+  rec[1] = __float_as_uint(r.m);
+  rec[2] = __float_as_uint(r.lh);
+  rec[3] = __float_as_uint(r.lw);
+  return rec;
+}
+
+// Bucket row of cell row y0 of group g in image n of the chunk; the cell
+// (y0, x0) has key row*(W+1) + x0+1.
+__device__ __forceinline__ uint64_t bucket_row(const FwdArgs& a, uint32_t n, uint32_t g, int y0) {
+  return (uint64_t)(n * (uint32_t)a.G + g) * (uint32_t)(a.H + 1) + (uint32_t)(y0 + 1);
+}
+
+__device__ __forceinline__ void place_record(const GatherArgs& ga, uint64_t rowk, int x0,
+                                             uint32_t slot, const u32x4& rec, uint32_t s) {
+  if (slot < ga.cap) {
+    const uint64_t cols = (uint32_t)(ga.f.W + 1);
+    ga.recs[(rowk * ga.cap + slot) * cols + (uint32_t)(x0 + 1)] = rec;
+  } else {
+    const uint32_t at = atomicAdd(ga.listed, 1u);
+    if (at < ga.samples) ga.list[at] = s;
+  }
+}
+
+// Workgroup = (image n, group g, output tile); tile x fastest, then tile y,
+// then g, then n.
+template <int DT, int MODE>
+__global__ __launch_bounds__(kBlock) void dcn4_bucket_kernel(GatherArgs ga) {
+  extern __shared__ uint32_t cnt[];  // [WH*WW] counts, then reserved bases
+  const FwdArgs& a = ga.f;
+  uint32_t b = blockIdx.x;
+  const uint32_t q1 = fastdiv(b, ga.div_tx);
+  const uint32_t txi = b - q1 * (uint32_t)ga.tiles_x;
+  const uint32_t q2 = fastdiv(q1, ga.div_ty);
+  const uint32_t tyi = q1 - q2 * (uint32_t)ga.tiles_y;
+  const uint32_t n = fastdiv(q2, ga.div_G);
+  const uint32_t g = q2 - n * (uint32_t)a.G;
+  const int TW = 1 << ga.tw_shift;
+  const int ty0 = (int)tyi * ga.TH, tx0 = (int)txi * TW;
+  const int wy0 = ty0 * a.sh + ga.wy_off, wx0 = tx0 * a.sw + ga.wx_off;
+  const int ncell = ga.WH * ga.WW;
+  for (int i = threadIdx.x; i < ncell; i += kBlock) cnt[i] = 0;
+  __syncthreads();
+  const uint32_t nloc = (uint32_t)(ga.TH * TW * ga.K);
+  const uint32_t img_pix = (uint32_t)(a.Ho * a.Wo);
+  u32x4 rec[kBucketNS];
+  int cell[kBucketNS];
+  uint32_t rank[kBucketNS], sid[kBucketNS];
+#pragma unroll
+  for (int j = 0; j < kBucketNS; ++j) {
+    cell[j] = -1;
+    const uint32_t l = (uint32_t)j * kBlock + threadIdx.x;
+    if (l >= nloc) continue;
+    const uint32_t pl = fastdiv(l, ga.div_K);
+    const int k = (int)(l - pl * (uint32_t)ga.K);
+    const uint32_t yo = (uint32_t)ty0 + (pl >> ga.tw_shift);
+    const uint32_t xo = (uint32_t)tx0 + (pl & (uint32_t)(TW - 1));
+    if (yo >= (uint32_t)a.Ho || xo >= (uint32_t)a.Wo) continue;
+    const uint32_t pix = n * img_pix + yo * (uint32_t)a.Wo + xo;
+    const SampleRec r = sample_at<DT, MODE>(ga, pix, yo, xo, g, k);
+    if (!r.inside) continue;
+    rec[j] = pack_record(r);
+    sid[j] = (pix * (uint32_t)a.G + g) * (uint32_t)ga.K + (uint32_t)k;
+    const int ly = r.y0 - wy0, lx = r.x0 - wx0;
+    if ((unsigned)ly < (unsigned)ga.WH && (unsigned)lx < (unsigned)ga.WW) {
+      cell[j] = ly * ga.WW + lx;
+      rank[j] = atomicAdd(cnt + cell[j], 1u);
+    } else {  // outside the window: a slot of its own
+      const uint64_t rowk = bucket_row(a, n, g, r.y0);
+      const uint32_t slot =
+          atomicAdd(ga.counts + rowk * (uint32_t)(a.W + 1) + (uint32_t)(r.x0 + 1), 1u);
+      place_record(ga, rowk, r.x0, slot, rec[j], sid[j]);
+    }
+  }
+  __syncthreads();
+  // one device atomic per non-empty cell reserves its slots
+  for (int i = threadIdx.x; i < ncell; i += kBlock) {
+    const uint32_t c = cnt[i];
+    if (c == 0) continue;
+    const int ly = (int)fastdiv((uint32_t)i, ga.div_WW), lx = i - ly * ga.WW;
+    cnt[i] = atomicAdd(ga.counts + bucket_row(a, n, g, wy0 + ly) * (uint32_t)(a.W + 1) +
+                           (uint32_t)(wx0 + lx + 1), c);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kBucketNS; ++j) {
+    if (cell[j] < 0) continue;
+    const int ly = (int)fastdiv((uint32_t)cell[j], ga.div_WW), lx = cell[j] - ly * ga.WW;
+    place_record(ga, bucket_row(a, n, g, wy0 + ly), wx0 + lx, cnt[cell[j]] + rank[j], rec[j],
+                 sid[j]);
+  }
+}
+
+// V consecutive elements widened to fp32 (one 16-byte load when they fill it).
+template <int DT, int V>
+__device__ __forceinline__ void load_widen(const typename Io<DT>::raw* p, float* v) {
+  typedef Io<DT> io;
+  if constexpr (V * io::es == 16) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = io::lane(q, e);
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = io::dec(p[e]);
+  }
+}
+
+// Records taken per round of a lane's bucket loop: their loads, then their
+// grad_y loads, are all in flight before the first is used.
+constexpr int kGatherU = 8;
+// Pixel rows of one band of the gather walk.
+constexpr int kGatherBand = 8;
+
+// A wave owns (image n, group g, band of pixel rows [y_lo, y_hi), strip of
+// Lc = 64 >> lg_shift bucket columns [cx0, cx0 + Lc)); lane (lc, li) takes
+// bucket column cx0 + lc and the group's channel vectors li, li + Lg, ...
+// It walks bucket rows cy = y_lo .. y_hi; each bucket's records are read once
+// and summed into four partial sums, one per corner of the cell:
+//   S_r[c] = sum over the bucket's records of fl(m*w_r) * dL/dy[p, c].
+// Bucket (cy, cx) holds the cell (cy-1, cx-1), so pixel (cy-1, cx-1) is
+// complete after row cy:
+//   (S_00(cy, cx) + S_10(cy-1, cx)) + (S_01(cy, cx-1) + S_11(cy-1, cx-1)),
+// the cx-1 terms from the lane Lg to the left (one shuffle), the cy-1 terms
+// kept from the previous row.  Strips overlap by one column; the strip's
+// first lane only feeds its right neighbour, and the band's first row only
+// the next row.
+template <int DT, int V, bool VST>
+__global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
+  typedef Io<DT> io;
+  const FwdArgs& a = ga.f;
+  const uint32_t wave =
+      ((uint32_t)xcd_block(blockIdx.x, ga.nblocks) * kBlock + threadIdx.x) >> 6;
+  if (wave >= ga.waves) return;  // whole waves leave together
+  const int lane = (int)(threadIdx.x & 63);
+  const int Lg = 1 << ga.lg_shift;
+  const int lc = lane >> ga.lg_shift, li = lane & (Lg - 1);
+  const int Lc = 64 >> ga.lg_shift;
+  const uint32_t q1 = fastdiv(wave, ga.div_strips);
+  const uint32_t strip = wave - q1 * (uint32_t)ga.strips;
+  const uint32_t q2 = fastdiv(q1, ga.div_bands);
+  const uint32_t band = q1 - q2 * (uint32_t)ga.bands;
+  const uint32_t n = fastdiv(q2, ga.div_G);
+  const uint32_t g = q2 - n * (uint32_t)a.G;
+  const int cx = (int)strip * (Lc - 1) + lc;
+  const bool col_ok = cx <= a.W;
+  const int y_lo = (int)band * kGatherBand;
+  const int y_hi = min(y_lo + kGatherBand, a.H);
+  const uint64_t row = (uint32_t)(a.W + 1);
+  const uint64_t rk0 = (uint64_t)(n * (uint32_t)a.G + g) * (uint32_t)(a.H + 1);  // bucket row 0
+  const uint64_t kb = rk0 * row + (uint32_t)(col_ok ? cx : 0);
+  const typename io::raw* gyn = reinterpret_cast<const typename io::raw*>(ga.gy) +
+                                (uint64_t)n * (uint32_t)(a.Ho * a.Wo) * (uint32_t)a.C +
+                                g * (uint32_t)a.D;
+  float* gxn = ga.gx + (uint64_t)n * (uint32_t)(a.H * a.W) * (uint32_t)a.C + g * (uint32_t)a.D;
+  const int rounds = (ga.nchunk + Lg - 1) >> ga.lg_shift;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int jc = li + (rd << ga.lg_shift);
+    const bool ch_ok = jc < ga.nchunk;
+    const bool live = col_ok && ch_ok;
+    float p10[V], p11[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) p10[e] = p11[e] = 0.0f;
+    uint32_t cnt_next = live ? min(ga.counts[kb + (uint64_t)y_lo * row], ga.cap) : 0u;
+#pragma unroll 1
+    for (int cy = y_lo; cy <= y_hi; ++cy) {
+      const uint32_t cnt = cnt_next;
+      const uint64_t key = kb + (uint64_t)cy * row;
+      if (cy < y_hi) cnt_next = live ? min(ga.counts[key + row], ga.cap) : 0u;
+      float s00[V], s01[V], s10[V], s11[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) s00[e] = s01[e] = s10[e] = s11[e] = 0.0f;
+      // slot t of this bucket: rp[t * row]
+      const u32x4* rp = ga.recs + ((rk0 + (uint32_t)cy) * ga.cap) * row + (uint32_t)(col_ok ? cx : 0);
+#pragma unroll 1
+      for (uint32_t t0 = 0; t0 < cnt; t0 += kGatherU) {
+        u32x4 rc[kGatherU];
+#pragma unroll
+        for (int u = 0; u < kGatherU; ++u)
+          if (t0 + u < cnt) rc[u] = rp[(uint64_t)(t0 + u) * row];
+        float v[kGatherU][V];
+#pragma unroll
+        for (int u = 0; u < kGatherU; ++u)
+          if (t0 + u < cnt)
+            load_widen<DT, V>(gyn + (uint64_t)rc[u][0] * (uint32_t)a.C + jc * V, v[u]);
+#pragma unroll
+        for (int u = 0; u < kGatherU; ++u) {
+          if (t0 + u >= cnt) break;
+          const float m = __uint_as_float(rc[u][1]);
+          const float lh = __uint_as_float(rc[u][2]), lw = __uint_as_float(rc[u][3]);
+          const float hh = 1.0f - lh, hw = 1.0f - lw;
+          const float c00 = m * (hh * hw), c01 = m * (hh * lw);
+          const float c10 = m * (lh * hw), c11 = m * (lh * lw);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            s00[e] = __builtin_fmaf(c00, v[u][e], s00[e]);
+            s01[e] = __builtin_fmaf(c01, v[u][e], s01[e]);
+            s10[e] = __builtin_fmaf(c10, v[u][e], s10[e]);
+            s11[e] = __builtin_fmaf(c11, v[u][e], s11[e]);
+          }
+        }
+      }
+      if (cy > y_lo) {  // pixel row cy - 1 is complete
+        float left[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) left[e] = __shfl_up(s01[e] + p11[e], (unsigned)Lg, 64);
+        if (live && lc > 0) {
+          float* o = gxn + ((uint64_t)(cy - 1) * (uint32_t)a.W + (uint32_t)(cx - 1)) *
+                               (uint32_t)a.C + jc * V;
+          float r[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) r[e] = (s00[e] + p10[e]) + left[e];
+          if constexpr (VST && V % 4 == 0) {
+#pragma unroll
+            for (int e = 0; e < V; e += 4)
+              *reinterpret_cast<float4*>(o + e) = make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = r[e];
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        p10[e] = s10[e];
+        p11[e] = s11[e];
+      }
+    }
+  }
+}
+
+// Sample s = ((pix*G) + g)*K + k of the chunk.
+template <int DT, int MODE>
+__device__ __forceinline__ SampleRec sample_record(const GatherArgs& ga, uint32_t s,
+                                                   uint32_t* n_out, uint32_t* g_out) {
+  const FwdArgs& a = ga.f;
+  const uint32_t item = fastdiv(s, ga.div_K);
+  const int k = (int)(s - item * (uint32_t)ga.K);
+  const uint32_t pix = fastdiv(item, ga.div_G);
+  const uint32_t g = item - pix * (uint32_t)a.G;
+  const uint32_t n = fastdiv(pix, a.div_hw);
+  const uint32_t rem = pix - n * (uint32_t)(a.Ho * a.Wo);
+  const uint32_t yo = fastdiv(rem, a.div_wo);
+  const uint32_t xo = rem - yo * (uint32_t)a.Wo;
+  *n_out = n;
+  *g_out = g;
+  return sample_at<DT, MODE>(ga, pix, yo, xo, g, k);
+}
+
+template <int DT, int MODE>
+__device__ __forceinline__ void overflow_sample(const GatherArgs& ga, uint32_t s, uint32_t c) {
+  typedef Io<DT> io;
+  const FwdArgs& a = ga.f;
+  uint32_t n, g;
+  const SampleRec r = sample_record<DT, MODE>(ga, s, &n, &g);  // listed samples are inside
+  const float gyc = io::dec(reinterpret_cast<const typename io::raw*>(ga.gy)[
+      ((uint64_t)n * (uint32_t)(a.Ho * a.Wo) + r.p) * (uint32_t)a.C + g * (uint32_t)a.D + c]);
+  const float hh = 1.0f - r.lh, hw = 1.0f - r.lw;
+  const float w[4] = {hh * hw, hh * r.lw, r.lh * hw, r.lh * r.lw};
+  const bool vy0 = r.y0 >= 0, vy1 = r.y0 < a.H - 1, vx0 = r.x0 >= 0, vx1 = r.x0 < a.W - 1;
+  const bool ok[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (!ok[q]) continue;
+    const uint32_t cy = (uint32_t)(r.y0 + (q >> 1)), cx = (uint32_t)(r.x0 + (q & 1));
+    unsafeAtomicAdd(ga.gx + ((uint64_t)(n * (uint32_t)a.H + cy) * (uint32_t)a.W + cx) *
+                                (uint32_t)a.C + g * (uint32_t)a.D + c,
+                    (r.m * w[q]) * gyc);
+  }
+}
+
+// Grid-stride over (listed sample, channel); exits at once when none is listed.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void dcn4_overflow_kernel(GatherArgs ga, int32_t mode) {
+  const uint32_t listed = min(*ga.listed, ga.samples);
+  const uint32_t D = (uint32_t)ga.f.D;
+  const uint64_t total = (uint64_t)listed * D;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t t = (uint64_t)blockIdx.x * kBlock + threadIdx.x; t < total; t += stride) {
+    const uint32_t e = (uint32_t)(t / D);
+    const uint32_t c = (uint32_t)(t - (uint64_t)e * D);
+    const uint32_t s = ga.list[e];
+    if (mode == kStdUnitScale) overflow_sample<DT, kStdUnitScale>(ga, s, c);
+    else if (mode == kStdScaled) overflow_sample<DT, kStdScaled>(ga, s, c);
+    else overflow_sample<DT, kGroupScale>(ga, s, c);
+  }
+}
+
 // ------------------------------------------------------------ geometry probe
 // One thread per (pixel, g, k); reads the merged tensor straight from global
 // memory and writes what the forward kernel's geometry functions compute.
@@ -1584,12 +1973,245 @@ dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
   return DCN4_OK;
 }
 
+// ------------------------------------------------------------ gathered grad_x: host
+// Records per bucket: the mean load of a bucket (K*Ho*Wo samples over
+// (H+1)*(W+1) cells) plus four standard deviations of a Poisson count plus 8,
+// rounded up to a multiple of 4; samples beyond it take the overflow path.
+uint32_t bucket_capacity(const Plan& p) {
+  if (p.bucket_cap > 0) return (uint32_t)p.bucket_cap;
+  const dcn4_desc& d = p.desc;
+  const double mu = (double)p.K * p.Ho * p.Wo / ((double)(d.H + 1) * (d.W + 1));
+  uint32_t cap = (uint32_t)__builtin_ceil(mu + 4.0 * __builtin_sqrt(mu) + 8.0);
+  cap = (cap + 3u) & ~3u;
+  return cap < 8u ? 8u : cap > 1024u ? 1024u : cap;
+}
+
+namespace {
+
+constexpr uint64_t kGatherChunkBytes = uint64_t(2) << 30;  // workspace per launch chunk
+
+uint64_t round256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
+
+// log2 of the lanes per (bucket column, group): enough for the group's
+// vectors, at most 16 so that a wave spans at least 4 columns
+int gather_lg(int D, int V) {
+  const int nchunk = D / V;
+  int lg = 0;
+  while ((1 << lg) < nchunk && lg < 4) ++lg;
+  return lg;
+}
+
+// Workspace of one chunk of images: [0, 256) the overflow counter; from 256
+// the bucket counts (4 bytes per key); then the overflow list (4 bytes per
+// sample); then the records (16 bytes x cap per key).
+struct GatherShape {
+  bool ok;        // indices of one image fit the kernels' 32-bit counters
+  int64_t imgs;   // images per chunk
+  uint32_t cap;
+  uint64_t keys_img, samples_img;
+  uint64_t list_off, recs_off, bytes;
+};
+
+GatherShape gather_shape(const Plan& p) {
+  GatherShape s{};
+  const dcn4_desc& d = p.desc;
+  s.cap = bucket_capacity(p);
+  s.keys_img = (uint64_t)(d.H + 1) * (d.W + 1) * d.group;
+  s.samples_img = (uint64_t)p.Ho * p.Wo * d.group * p.K;
+  const uint64_t lim = (uint64_t(1) << 31) - 1;
+  if (d.N < 1 || s.keys_img > lim || s.samples_img > lim) return s;
+  const uint64_t per_img = 4 * s.keys_img + 4 * s.samples_img + 16 * s.keys_img * s.cap;
+  uint64_t imgs = (uint64_t)d.N;
+  const uint64_t caps[3] = {lim / s.keys_img, lim / s.samples_img, kGatherChunkBytes / per_img};
+  for (uint64_t c : caps) imgs = c < imgs ? c : imgs;
+  if (imgs < 1) imgs = 1;
+  s.imgs = (int64_t)imgs;
+  s.list_off = 256 + round256(4 * imgs * s.keys_img);
+  s.recs_off = s.list_off + round256(4 * imgs * s.samples_img);
+  s.bytes = s.recs_off + 16 * imgs * s.keys_img * s.cap;
+  s.ok = true;
+  return s;
+}
+
+typedef void (*gather_fn)(GatherArgs);
+
+// Output tile of a bucket workgroup (at most kBucketNS samples per thread)
+// and the window of cells it counts in LDS: the tile's base rows/cols (the
+// centres in group-scale mode, where the grid spreads the points by up to
+// (k-1)/2 scaled steps) widened by a margin on each side.
+struct BucketTile {
+  int32_t TH, tw_shift, WH, WW, wy_off, wx_off;
+  int32_t lds_bytes;
+};
+
+BucketTile bucket_tile(const Plan& p) {
+  const dcn4_desc& d = p.desc;
+  static const int shapes[][2] = {{8, 4}, {8, 3}, {4, 3}, {4, 2}, {2, 2}, {2, 1}, {1, 1}, {1, 0}};
+  const bool gs = p.mode == kGroupScale;
+  const int hy = (d.kernel_h - 1) >> 1, hx = (d.kernel_w - 1) >> 1;
+  const int M = gs ? 4 + 4 * (hy > hx ? hy : hx) : 4;
+  BucketTile t{};
+  for (const auto& sh : shapes) {
+    t.TH = sh[0];
+    t.tw_shift = sh[1];
+    const int TW = 1 << sh[1];
+    if (t.TH * TW * p.K > kBucketNS * kBlock) continue;
+    if (gs) {
+      t.WH = (t.TH - 1) * d.stride_h + 2 * M + 1;
+      t.WW = (TW - 1) * d.stride_w + 2 * M + 1;
+      t.wy_off = -d.pad_h + hy - M;
+      t.wx_off = -d.pad_w + hx - M;
+    } else {
+      t.WH = (t.TH - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 1;
+      t.WW = (TW - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 1;
+      t.wy_off = -d.pad_h - M;
+      t.wx_off = -d.pad_w - M;
+    }
+    t.lds_bytes = t.WH * t.WW * 4;
+    if (t.lds_bytes <= kLdsBudget) return t;
+  }
+  // windows too large for LDS: every sample takes its slot with its own atomic
+  t.WH = t.WW = 1;
+  t.wy_off = t.wx_off = -(1 << 30);
+  t.lds_bytes = 4;
+  return t;
+}
+
+template <int DT>
+gather_fn pick_bucket(int mode) {
+  return mode == kStdUnitScale ? dcn4_bucket_kernel<DT, kStdUnitScale>
+       : mode == kStdScaled ? dcn4_bucket_kernel<DT, kStdScaled>
+                            : dcn4_bucket_kernel<DT, kGroupScale>;
+}
+
+template <int DT>
+gather_fn pick_gather(bool vec, bool vst) {
+  constexpr int V = 16 / Io<DT>::es;
+  if (!vec) return dcn4_gather_kernel<DT, 1, false>;
+  return vst ? dcn4_gather_kernel<DT, V, true> : dcn4_gather_kernel<DT, V, false>;
+}
+
+dcn4_status check_launch() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    note_hip_error(e);
+    return DCN4_ERR_HIP;
+  }
+  return DCN4_OK;
+}
+
+dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
+                          const float* pscales, const void* gy, float* gx, void* ws,
+                          hipStream_t st) {
+  const dcn4_desc& d = p.desc;
+  const GatherShape sh = gather_shape(p);
+  const bool vec = p.D % (16 / p.es) == 0 && ((uintptr_t)gy & 15) == 0;
+  const bool vst = vec && ((uintptr_t)gx & 15) == 0;
+  const int V = vec ? 16 / p.es : 1;
+  gather_fn bucket, gather;
+  typedef void (*overflow_fn)(GatherArgs, int32_t);
+  overflow_fn ovf;
+  switch (d.dtype) {
+    case DCN4_F32:
+      bucket = pick_bucket<DCN4_F32>(p.mode);
+      gather = pick_gather<DCN4_F32>(vec, vst);
+      ovf = dcn4_overflow_kernel<DCN4_F32>;
+      break;
+    case DCN4_BF16:
+      bucket = pick_bucket<DCN4_BF16>(p.mode);
+      gather = pick_gather<DCN4_BF16>(vec, vst);
+      ovf = dcn4_overflow_kernel<DCN4_BF16>;
+      break;
+    default:
+      bucket = pick_bucket<DCN4_F16>(p.mode);
+      gather = pick_gather<DCN4_F16>(vec, vst);
+      ovf = dcn4_overflow_kernel<DCN4_F16>;
+      break;
+  }
+  GatherArgs ga{};
+  fill_common(p, ga.f);
+  ga.f.scales = scales;
+  ga.cap = sh.cap;
+  ga.K = p.K;
+  ga.nchunk = p.D / V;
+  ga.lg_shift = gather_lg(p.D, V);
+  ga.div_K = make_fastdiv((uint32_t)p.K);
+  ga.div_kw = make_fastdiv((uint32_t)d.kernel_w);
+  ga.div_G = make_fastdiv((uint32_t)d.group);
+  ga.div_W = make_fastdiv((uint32_t)d.W);
+  ga.div_H = make_fastdiv((uint32_t)d.H);
+  const BucketTile bt = bucket_tile(p);
+  ga.TH = bt.TH;
+  ga.tw_shift = bt.tw_shift;
+  ga.WH = bt.WH;
+  ga.WW = bt.WW;
+  ga.wy_off = bt.wy_off;
+  ga.wx_off = bt.wx_off;
+  ga.tiles_y = (p.Ho + bt.TH - 1) / bt.TH;
+  ga.tiles_x = (p.Wo + (1 << bt.tw_shift) - 1) >> bt.tw_shift;
+  ga.div_WW = make_fastdiv((uint32_t)bt.WW);
+  ga.div_tx = make_fastdiv((uint32_t)ga.tiles_x);
+  ga.div_ty = make_fastdiv((uint32_t)ga.tiles_y);
+  const int Lc = 64 >> ga.lg_shift;
+  ga.strips = (d.W + Lc - 2) / (Lc - 1);
+  ga.bands = (d.H + kGatherBand - 1) / kGatherBand;
+  ga.div_strips = make_fastdiv((uint32_t)ga.strips);
+  ga.div_bands = make_fastdiv((uint32_t)ga.bands);
+  char* w = static_cast<char*>(ws);
+  ga.listed = reinterpret_cast<uint32_t*>(w);
+  ga.counts = reinterpret_cast<uint32_t*>(w + 256);
+  ga.list = reinterpret_cast<uint32_t*>(w + sh.list_off);
+  ga.recs = reinterpret_cast<u32x4*>(w + sh.recs_off);
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t om_img = (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K * p.es;
+  const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;
+  const uint64_t x_img = (uint64_t)d.H * d.W * d.C;
+  for (int64_t n0 = 0; n0 < d.N; n0 += sh.imgs) {
+    const int64_t nb = (d.N - n0) < sh.imgs ? (d.N - n0) : sh.imgs;
+    ga.f.om = static_cast<const char*>(om) + n0 * om_img;
+    ga.f.pscales = pscales ? pscales + n0 * ps_img : nullptr;
+    ga.gy = static_cast<const char*>(gy) + n0 * y_img;
+    ga.gx = gx + n0 * x_img;
+    ga.samples = (uint32_t)(nb * sh.samples_img);
+    ga.waves = (uint32_t)((uint64_t)nb * d.group * ga.bands * ga.strips);
+    ga.nblocks = (int32_t)((ga.waves + kBlock / 64 - 1) / (kBlock / 64));
+    const uint64_t zero_words = 64 + (uint64_t)nb * sh.keys_img;
+    const uint64_t zb = (zero_words + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(dcn4_fill_zero_kernel, dim3((unsigned)(zb < 65536 ? zb : 65536)),
+                       dim3(kBlock), 0, st, reinterpret_cast<float*>(w), zero_words);
+    dcn4_status s = check_launch();
+    if (s != DCN4_OK) return s;
+    const uint64_t bblocks = (uint64_t)nb * d.group * ga.tiles_y * ga.tiles_x;
+    hipLaunchKernelGGL(bucket, dim3((unsigned)bblocks), dim3(kBlock), bt.lds_bytes, st, ga);
+    if ((s = check_launch()) != DCN4_OK) return s;
+    hipLaunchKernelGGL(gather, dim3((unsigned)ga.nblocks), dim3(kBlock), 0, st, ga);
+    if ((s = check_launch()) != DCN4_OK) return s;
+    const uint64_t ob = ((uint64_t)ga.samples * p.D + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(ovf, dim3((unsigned)(ob < 512 ? ob : 512)), dim3(kBlock), 0, st, ga,
+                       (int32_t)p.mode);
+    if ((s = check_launch()) != DCN4_OK) return s;
+  }
+  return DCN4_OK;
+}
+
+}  // namespace
+
+uint64_t backward_workspace_bytes(const Plan& p) {
+  const GatherShape s = gather_shape(p);
+  return s.ok ? s.bytes : 0;
+}
+
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
-                            const void* gy, float* gx, float* gom, void* stream,
-                            bool vector_path) {
+                            const void* gy, float* gx, float* gom, void* ws,
+                            void* stream, bool vector_path) {
   const dcn4_desc& d = p.desc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gx && ws) {
+    const dcn4_status s = launch_gather(p, om, scales, pscales, gy, gx, ws, st);
+    if (s != DCN4_OK) return s;
+    gx = nullptr;  // done: what remains is grad_om
+  }
   if (gx) {
     const uint64_t n = (uint64_t)d.N * d.H * d.W * d.C;
     const uint64_t blocks = (n + kBlock - 1) / kBlock;

@@ -144,15 +144,17 @@ typedef struct {
   int32_t tile_h, tile_w;    /* tiled kernel: output tile                   */
   int32_t tile_groups;       /* tiled kernel: groups per workgroup          */
   int32_t tile_margin;       /* tiled kernel: window margin in pixels       */
-  int32_t backward_kernel;   /* dcn4_backward without grad_x: 1 direct, 2
-                                tiled (LDS window), for 16-byte aligned
-                                tensors; calls with grad_x run the direct
-                                kernel                                      */
+  int32_t backward_kernel;   /* grad_offset_mask of dcn4_backward: 1 direct,
+                                2 tiled (LDS window), for 16-byte aligned
+                                tensors, when grad_x is gathered or not
+                                asked for; a call that scatters grad_x
+                                (no workspace) runs the direct kernel      */
   int32_t backward_lds_bytes; /* dynamic LDS per tiled-backward workgroup   */
   int32_t tile_slices;       /* tiled kernel: channel slices per group (1:
                                 a workgroup's window holds whole groups;
                                 > 1: one slice of channels_per_lane
                                 channels of one group, one lane per pixel) */
+  int32_t bucket_capacity;   /* gathered grad_x: records per bucket          */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -175,7 +177,12 @@ typedef enum {
   DCN4_OPT_TILE_PAD = 4,
   /* tiled kernel: k = 1-6 makes lanes whose index has bit k-1 set read their
    * 16-byte vectors pairwise swapped (fewer LDS bank conflicts); 0 = off */
-  DCN4_OPT_TILE_SWIZZLE = 5
+  DCN4_OPT_TILE_SWIZZLE = 5,
+  /* backward, gathered grad_x: records per (cell, group) bucket, 1-1024;
+   * samples beyond it are added by the overflow kernel's atomics; 0 =
+   * automatic (the mean bucket load plus four Poisson standard deviations
+   * plus 8).  Changes the workspace size. */
+  DCN4_OPT_BUCKET_CAPACITY = 6
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,
@@ -215,8 +222,8 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
  * the offset/weight tensor, given dL/dy.  grad_y is [N, Ho, Wo, C] in the I/O
  * dtype; grad_x [N, H, W, C] and grad_offset_mask [N, Ho, Wo, G, 3K] are fp32
  * device arrays, 4-byte aligned, either of them NULL to skip it; both are
- * overwritten (grad_x is cleared by the library, then accumulated).  In the
- * offset/weight layout, grad_offset_mask holds dL/d(dx_k, dy_k) and dL/dm_k:
+ * overwritten.  In the offset/weight layout, grad_offset_mask holds
+ * dL/d(dx_k, dy_k) and dL/dm_k:
  *   dL/dm_k  = sum over the group's channels c of dL/dy_c * B_c(p_k),
  *   dL/d(dy_k) = m_k * f * sum_c dL/dy_c * dB_c/drow, dL/d(dx_k) likewise
  *              with dB/dcol, f = offset_scale or the group's scale S,
@@ -226,13 +233,45 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
  * the derivative from above at integer locations.  The sampling decisions
  * are the forward's (same device functions); a sample that is not inside has
  * zero gradient.  No gradient of the group or pixel scales is computed.
- * grad_x is summed with fp32 atomics in no fixed order, so it is not
- * bit-reproducible; the fp32 sums of grad_offset_mask are.  Other arguments,
+ * grad_x is the adjoint of the bilinear gather ([DCNv4 digest] "GPU效率的
+ * 理论分析": every sample reads four corners of its group's D channels):
+ * with a workspace each sample is appended to the bucket of its cell and
+ * group and every input pixel gathers the buckets of the four cells it is a
+ * corner of, accumulating fl(m_k*w) * dL/dy with fp32 fused multiply-adds;
+ * without one every product fl(fl(m_k*w) * dL/dy) is added with an fp32
+ * atomic.  Either way the order of the sum varies from run to run, so grad_x
+ * is not bit-reproducible; the fp32 sums of grad_offset_mask are.  This entry point
+ * allocates the workspace (dcn4_backward_workspace_size bytes) with
+ * hipMallocAsync on `stream` and frees it with hipFreeAsync after the
+ * launches; an allocation failure is DCN4_ERR_HIP.  Other arguments,
  * validation and errors as dcn4_forward_scaled (grad_y in the role of y). */
 dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
                           const void* offset_mask, const float* group_scales,
                           const float* pixel_scales, const void* grad_y,
                           float* grad_x, float* grad_offset_mask, void* stream);
+
+/* Bytes of device workspace dcn4_backward_ws needs to gather grad_x: for
+ * each chunk of images one launch sequence handles, a 256-byte counter, a
+ * 4-byte count per (cell, group) bucket ((H+1)*(W+1)*G per image), a 4-byte
+ * overflow entry per sample (Ho*Wo*G*K per image) and 16 * capacity bytes of
+ * records per bucket; chunks hold at most 2 GiB unless one image needs more.
+ * 0 when one image has 2^31 or more samples, buckets or gather lanes: then
+ * grad_x is always scattered with atomics.  Errors: DCN4_ERR_NULL. */
+dcn4_status dcn4_backward_workspace_size(const dcn4_plan* plan, uint64_t* bytes);
+
+/* dcn4_backward with a caller-owned workspace: `workspace` is a device
+ * buffer of workspace_bytes bytes, 256-byte aligned (DCN4_ERR_MISALIGNED),
+ * at least dcn4_backward_workspace_size (DCN4_ERR_INVALID_ARG), overlapping
+ * no other argument; its contents on entry do not matter and on return are
+ * undefined.  workspace NULL (or a size query of 0) selects the atomic
+ * scatter for grad_x, which needs no workspace.  Calls that share a
+ * workspace must be ordered (same stream, or synchronised). */
+dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x,
+                             const void* offset_mask, const float* group_scales,
+                             const float* pixel_scales, const void* grad_y,
+                             float* grad_x, float* grad_offset_mask,
+                             void* workspace, uint64_t workspace_bytes,
+                             void* stream);
 
 /* The producer of the offset/weight tensor: the merged linear layer of
  * [DCNv4 digest] "方法3" (offsets and weights from one linear layer),

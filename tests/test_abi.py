@@ -3,6 +3,8 @@ error path (validation happens before any HIP call, so none of these touch a
 GPU).  Output sizes and ideal bytes are checked against the oracle, which
 computes them independently."""
 import ctypes
+
+import numpy as np
 import os
 import re
 import subprocess
@@ -28,7 +30,8 @@ def test_header_declares_the_entry_points():
     for n in ("dcn4_create", "dcn4_forward", "dcn4_destroy", "dcn4_query",
               "dcn4_status_string", "dcn4_probe_geometry", "dcn4_last_error",
               "dcn4_plan_info", "dcn4_plan_set_option", "dcn4_forward_scaled",
-              "dcn4_backward", "dcn4_offset_linear", "dcn4_dwconv3x3"):
+              "dcn4_backward", "dcn4_backward_ws", "dcn4_backward_workspace_size",
+              "dcn4_offset_linear", "dcn4_dwconv3x3"):
         assert n in names
 
 
@@ -275,6 +278,57 @@ class TestForwardValidation:
         assert bw(self.p, 256, 256, 1024, 256, 512, 1024) == d4.DCN4_ERR_INVALID_ARG
         assert bw(self.ms, 256, 256, None, 256, 512, 1024) == d4.DCN4_ERR_NULL
         assert d4.dcn4_backward(None, 256, 256, None, None, 256, 512, 1024, None) == d4.DCN4_ERR_NULL
+
+    def test_backward_workspace_checks(self):
+        st, need = d4.dcn4_backward_workspace_size(self.p.handle)
+        assert st == d4.DCN4_OK and need > 0
+        assert d4.dcn4_backward_workspace_size(None)[0] == d4.DCN4_ERR_NULL
+        bws = lambda ws, nb, gx=1024, x=256: d4.dcn4_backward_ws(
+            self.p.handle, x, 256, None, None, 512, gx, 2048, ws, nb, None)
+        assert bws(4096, need - 1) == d4.DCN4_ERR_INVALID_ARG
+        assert bws(4096 + 16, need) == d4.DCN4_ERR_MISALIGNED
+        # the other arguments are checked first
+        assert bws(4096, need - 1, gx=1026) == d4.DCN4_ERR_MISALIGNED
+        assert bws(4096, need - 1, x=None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_backward_ws(None, 256, 256, None, None, 512, 1024, 2048, 4096, need,
+                                   None) == d4.DCN4_ERR_NULL
+
+    def test_backward_workspace_size(self):
+        """The documented layout: a 256-byte counter, 4 bytes per (cell,
+        group) bucket, 4 bytes per sample, 16 * capacity bytes per bucket,
+        each of the first three regions rounded up to 256 bytes; batches
+        beyond 2 GiB are split into chunks of whole images."""
+        r256 = lambda b: (b + 255) // 256 * 256
+        for desc, cap in ((mk(), 0), (mk(N=3, H=21, W=13, kernel_h=5, kernel_w=5, pad_h=2,
+                                         pad_w=2), 7),
+                          (mk(N=2, H=30, W=30, stride_h=2, stride_w=2), 0)):
+            plan = d4.Plan(desc, bucket_capacity=cap)
+            c = plan.info()["bucket_capacity"]
+            if cap:
+                assert c == cap
+            keys = desc.N * (desc.H + 1) * (desc.W + 1) * desc.group
+            samples = desc.N * plan.Ho * plan.Wo * desc.group * desc.kernel_h * desc.kernel_w
+            want = 256 + r256(4 * keys) + r256(4 * samples) + 16 * keys * c
+            assert plan.backward_workspace_bytes() == want
+        big = d4.Plan(mk(N=64, H=64, W=64, C=64, group=4), bucket_capacity=1024)
+        per_img = 65 * 65 * 4 * (4 + 16 * 1024) + 64 * 64 * 4 * 9 * 4
+        imgs = (2 << 30) // per_img
+        assert 1 < imgs < 64
+        assert big.backward_workspace_bytes() == (256 + r256(4 * imgs * 65 * 65 * 4) +
+                                                  r256(4 * imgs * 64 * 64 * 4 * 9) +
+                                                  16 * imgs * 65 * 65 * 4 * 1024)
+
+    def test_bucket_capacity_option(self):
+        p = d4.Plan(mk())
+        # the automatic capacity: mean load + 4 Poisson deviations + 8, to a multiple of 4
+        mu = 9 * 16 * 16 / (17 * 17)
+        auto = int(np.ceil(mu + 4 * np.sqrt(mu) + 8))
+        assert p.info()["bucket_capacity"] == (auto + 3) // 4 * 4
+        for bad in (-1, 1025):
+            assert d4.dcn4_plan_set_option(p.handle, d4.DCN4_OPT_BUCKET_CAPACITY, bad) == \
+                d4.DCN4_ERR_INVALID_ARG
+        assert d4.dcn4_plan_set_option(p.handle, d4.DCN4_OPT_BUCKET_CAPACITY, 3) == d4.DCN4_OK
+        assert p.info()["bucket_capacity"] == 3
 
     def test_empty_batch_is_a_no_op(self):
         p0 = d4.Plan(mk(N=0))

@@ -1,8 +1,11 @@
-"""Parity of the HIP backward pass (dcn4_backward) with the oracle's.
+"""Parity of the HIP backward pass (dcn4_backward_ws / dcn4_backward) with the
+oracle's.
 
-grad_x is summed with fp32 atomics in no fixed order and grad_offset_mask with
-fp32 sums in the kernel's order, while the oracle sums in fp64 (with the same
-sampling decisions as the fp32 forward).  The tolerance is the fp32
+grad_x is summed in fp32 in no fixed order -- gathered from per-cell buckets
+(the default, with a workspace) or scattered with fp32 atomics (no
+workspace) -- and grad_offset_mask with fp32 sums in the kernel's order,
+while the oracle sums in fp64 (with the same sampling decisions as the fp32
+forward).  The tolerance is the fp32
 summation bound: for an output with terms t_i (at most n of them per output),
 |gpu - oracle| <= (n + 8) * 2^-24 * sum_i |t_i|, the sum of absolute terms
 coming from the oracle (n + 8 covers the n additions and the few roundings
@@ -38,24 +41,25 @@ def check_bound(got, want, absum, n_terms, what):
                            f"first at {np.argwhere(bad)[:3].tolist()}")
 
 
-def run_backward(plan, inp, gy_raw, dt, want_x=True, want_om=True):
+def run_backward(plan, inp, gy_raw, dt, want_x=True, want_om=True, scatter=False):
     x = to_dev(inp.x, dt)
     om = to_dev(inp.om, dt)
     gy = to_dev(gy_raw, dt)
     sc = None if inp.scales is None else torch.from_numpy(inp.scales).cuda()
     gx, gom = plan.backward(x, om, gy, sc, dev_f32(inp.pscales), want_x=want_x,
-                            want_om=want_om)
+                            want_om=want_om, scatter=scatter)
     torch.cuda.synchronize()
     return (None if gx is None else gx.cpu().numpy(),
             None if gom is None else gom.cpu().numpy())
 
 
-def compare(s, dt, inp, gy_raw, plan, what):
+def compare(s, dt, inp, gy_raw, plan, what, paths=("gather",)):
     o = oracle.get()
     ref = o.backward(s, dt, inp.x, inp.om, gy_raw, inp.scales, inp.pscales)
-    gx, gom = run_backward(plan, inp, gy_raw, dt)
-    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], what + " grad_x")
-    check_bound(gom, ref["gom"], ref["gom_abs"], ref["max_terms"], what + " grad_om")
+    for path in paths:
+        gx, gom = run_backward(plan, inp, gy_raw, dt, scatter=path == "scatter")
+        check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], f"{what} {path} grad_x")
+        check_bound(gom, ref["gom"], ref["gom_abs"], ref["max_terms"], f"{what} {path} grad_om")
     return gx, gom
 
 
@@ -103,10 +107,11 @@ def bwd_inputs(s, dt, seed):
 
 @pytest.mark.parametrize("t, s, dt", bwd_cases(), ids=lambda v: str(v) if isinstance(v, int) else None)
 def test_backward_parity(t, s, dt):
+    """Both grad_x paths: gathered (workspace) and scattered (atomics)."""
     inp, gy = bwd_inputs(s, dt, seed=t)
     plan = d4.Plan(desc_of(s, dt))
     say(f"backward case {t}: {s} {dt}")
-    compare(s, dt, inp, gy, plan, f"backward {t}")
+    compare(s, dt, inp, gy, plan, f"backward {t}", paths=("gather", "scatter"))
 
 
 @pytest.mark.parametrize("name", ["ldm_unet_block_bf16", "flowdcn_pixelscale_bf16"])
@@ -121,29 +126,32 @@ def test_backward_full_size(name):
     rng = np.random.default_rng(11)
     gy = to_raw(rng.standard_normal((s.N, Ho, Wo, s.C), dtype=np.float32), w.dtype)
     say(f"backward full size: {w.describe()}")
-    compare(s, w.dtype, inp, gy, d4.Plan(desc_of(s, w.dtype)), name)
+    compare(s, w.dtype, inp, gy, d4.Plan(desc_of(s, w.dtype)), name,
+            paths=("gather", "scatter"))
 
 
 def test_backward_reproducible_and_partial():
     """grad_offset_mask is bit-reproducible (no atomics) on each path: the
-    direct kernel (a call with grad_x) and the tiled one (a call without);
-    each gradient can be asked for alone and stays within the bound."""
+    direct kernel (a call that scatters grad_x) and the tiled one (a call
+    that gathers grad_x, or asks for no grad_x: the same kernel, so the same
+    bits); each gradient can be asked for alone and stays within the bound."""
     s = Shape(2, 19, 23, 64, 4)
     dt = "bf16"
     inp, gy = bwd_inputs(s, dt, seed=99)
     plan = d4.Plan(desc_of(s, dt))
     assert plan.info()["backward_kernel"] == 2
     ref = oracle.get().backward(s, dt, inp.x, inp.om, gy)
-    gx1, gom1 = run_backward(plan, inp, gy, dt)
-    gx2, gom2 = run_backward(plan, inp, gy, dt)
+    gx1, gom1 = run_backward(plan, inp, gy, dt, scatter=True)
+    gx2, gom2 = run_backward(plan, inp, gy, dt, scatter=True)
     assert np.array_equal(gom1.view(np.uint32), gom2.view(np.uint32))
-    _, gom3 = run_backward(plan, inp, gy, dt, want_x=False)
+    gx3, gom3 = run_backward(plan, inp, gy, dt)
     _, gom4 = run_backward(plan, inp, gy, dt, want_x=False)
     assert np.array_equal(gom3.view(np.uint32), gom4.view(np.uint32))
     gx5, _ = run_backward(plan, inp, gy, dt, want_om=False)
+    gx6, _ = run_backward(plan, inp, gy, dt, want_om=False, scatter=True)
     for g in (gom1, gom3):
         check_bound(g, ref["gom"], ref["gom_abs"], ref["max_terms"], "grad_om repeat")
-    for g in (gx1, gx2, gx5):
+    for g in (gx1, gx2, gx3, gx5, gx6):
         check_bound(g, ref["gx"], ref["gx_abs"], ref["max_terms"], "grad_x repeat")
 
 
@@ -170,9 +178,10 @@ TILED_BWD_CASES = [(c, m) for c, (_, _, _, ms) in enumerate(TILED_BWD) for m in 
 @pytest.mark.parametrize("case, margin", TILED_BWD_CASES)
 def test_tiled_backward(case, margin):
     """The tiled backward (offset/weight gradients from the LDS window, for
-    calls without grad_x) against the oracle; margin 0 sends every wave to the
-    global path, 1 mixes the paths.  The same plan asked for both gradients
-    runs the direct kernel, which must agree within the bound too."""
+    calls without grad_x or with a gathered one) against the oracle; margin 0
+    sends every wave to the global path, 1 mixes the paths.  The same plan
+    scattering grad_x runs the direct kernel for both gradients, which must
+    agree within the bound too."""
     s, dt, opts, _ = TILED_BWD[case]
     inp, gy = bwd_inputs(s, dt, seed=500 + case)
     dp = opts.get("channels_per_lane", 0)
@@ -184,6 +193,70 @@ def test_tiled_backward(case, margin):
     ref = oracle.get().backward(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
     _, gom = run_backward(plan, inp, gy, dt, want_x=False)
     check_bound(gom, ref["gom"], ref["gom_abs"], ref["max_terms"], f"tiled grad_om {case} m{margin}")
-    gx, gom_d = run_backward(plan, inp, gy, dt)
+    gxg, gom_g = run_backward(plan, inp, gy, dt)
+    assert np.array_equal(gom.view(np.uint32), gom_g.view(np.uint32))
+    check_bound(gxg, ref["gx"], ref["gx_abs"], ref["max_terms"], f"gathered grad_x {case} m{margin}")
+    gx, gom_d = run_backward(plan, inp, gy, dt, scatter=True)
     check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], f"direct grad_x {case} m{margin}")
     check_bound(gom_d, ref["gom"], ref["gom_abs"], ref["max_terms"], f"direct grad_om {case} m{margin}")
+
+
+OVERFLOW = [
+    # (shape, dtype, bucket capacities): capacities far below the ~9 samples
+    # of a cell send most samples through the overflow kernel's atomics
+    (Shape(2, 19, 23, 64, 4), "bf16", (1, 2, 5)),
+    (Shape(1, 21, 17, 48, 3, sh=2, sw=2, ph=1, pw=1), "f32", (1, 3)),
+    (Shape(1, 16, 20, 40, 4, dh=2, dw=2, ph=2, pw=2), "f16", (1, 4)),  # D=10: element path
+    (Shape(1, 18, 18, 32, 2, multiscale=True), "bf16", (1, 2)),
+    (Shape(1, 18, 18, 32, 2, multiscale=True, pixel_scales=True, max_scale=2.5), "f16", (2,)),
+    (Shape(1, 15, 17, 32, 2, offset_scale=0.5), "bf16", (1,)),
+]
+OVERFLOW_CASES = [(c, cap) for c, (_, _, caps) in enumerate(OVERFLOW) for cap in caps]
+
+
+@pytest.mark.parametrize("case, cap", OVERFLOW_CASES)
+def test_gather_overflow(case, cap):
+    """Full buckets: the samples beyond a bucket's capacity are listed and
+    added with atomics after the gather; the sum must stay within the bound."""
+    s, dt, _ = OVERFLOW[case]
+    inp, gy = bwd_inputs(s, dt, seed=700 + case)
+    plan = d4.Plan(desc_of(s, dt), bucket_capacity=cap)
+    assert plan.info()["bucket_capacity"] == cap
+    say(f"gather overflow {case} cap {cap}: {s} {dt}")
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
+    gx, _ = run_backward(plan, inp, gy, dt, want_om=False)
+    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], f"overflow {case} cap {cap}")
+
+
+def test_gather_chunks():
+    """A workspace above 2 GiB for the batch (1024 records per bucket) is
+    split into chunks of images that reuse one workspace."""
+    s = Shape(8, 64, 64, 64, 4)
+    dt = "bf16"
+    plan = d4.Plan(desc_of(s, dt), bucket_capacity=1024)
+    one = d4.Plan(desc_of(Shape(1, 64, 64, 64, 4), dt), bucket_capacity=1024)
+    ws = plan.backward_workspace_bytes()
+    assert ws < 8 * one.backward_workspace_bytes() and ws > 4 * one.backward_workspace_bytes()
+    inp, gy = bwd_inputs(s, dt, seed=808)
+    say(f"gather chunks: {s} {dt}, workspace {ws} bytes")
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy)
+    gx, _ = run_backward(plan, inp, gy, dt, want_om=False)
+    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], "gather chunks")
+
+
+def test_backward_allocating_entry():
+    """dcn4_backward allocates its workspace stream-ordered and gathers."""
+    s = Shape(2, 17, 19, 64, 4)
+    dt = "bf16"
+    inp, gy_raw = bwd_inputs(s, dt, seed=909)
+    plan = d4.Plan(desc_of(s, dt))
+    x, om, gy = to_dev(inp.x, dt), to_dev(inp.om, dt), to_dev(gy_raw, dt)
+    gx = torch.full((s.N, s.H, s.W, s.C), float("nan"), dtype=torch.float32, device="cuda")
+    gom = torch.empty(plan.om_shape(), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert d4.dcn4_backward(plan.handle, x.data_ptr(), om.data_ptr(), None, None,
+                            gy.data_ptr(), gx.data_ptr(), gom.data_ptr(), st) == d4.DCN4_OK
+    torch.cuda.synchronize()
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy_raw)
+    check_bound(gx.cpu().numpy(), ref["gx"], ref["gx_abs"], ref["max_terms"], "allocating grad_x")
+    check_bound(gom.cpu().numpy(), ref["gom"], ref["gom_abs"], ref["max_terms"], "allocating grad_om")
