@@ -1054,8 +1054,9 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
   const float ry0 = (float)(by0 - wy0), rx0 = (float)(bx0 - wx0);
   const float f = (MODE == kStdScaled) ? a.offset_scale : 1.0f;
   const uint32_t lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
+  float res[3 * K];  // the lane's row of grad_offset_mask, in the tensor's order
 
-#pragma unroll 1
+#pragma unroll
   for (int k = 0; k < K; ++k) {
     const int i = k / KS, j = k - (k / KS) * KS;
     const float dx = io::dec(om[2 * k]), dy = io::dec(om[2 * k + 1]);
@@ -1132,13 +1133,36 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
       gdr += __shfl_xor(gdr, off, 64);
       gdc += __shfl_xor(gdc, off, 64);
     }
-    if (active && l == 0) {
-      float* go = bb.gom + ((((uint64_t)n * a.Ho + yo) * a.Wo + xo) * (uint32_t)a.G + g) * (3 * K);
-      const float mf = m * f;
-      go[2 * k] = mf * gdc;
-      go[2 * k + 1] = mf * gdr;
-      go[2 * K + k] = gm;
-    }
+    const float mf = m * f;
+    res[2 * k] = mf * gdc;      // dx moves the column
+    res[2 * k + 1] = mf * gdr;  // dy moves the row
+    res[2 * K + k] = gm;
+  }
+
+  // Write-out through LDS: a row per (pixel, group) item, 3K floats at odd
+  // stride (no bank conflicts), then each wave stores its own rows with
+  // consecutive lanes on consecutive floats, so a store instruction touches
+  // a few cache lines instead of one per lane.  The window and the staged
+  // offsets are dead once every wave has finished its points.
+  __syncthreads();
+  const uint32_t l_shift = a.L == 4 ? 2u : a.L == 2 ? 1u : 0u;
+  const uint32_t rows_wave = 64u >> l_shift;
+  float* res_lds = reinterpret_cast<float*>(lds);
+  uint64_t* base_lds = reinterpret_cast<uint64_t*>(lds + (uint32_t)(kBlock * 3 * K * 4) / (uint32_t)a.L);
+  if (l == 0) {
+    const uint32_t r = t >> l_shift;
+#pragma unroll
+    for (int c = 0; c < 3 * K; ++c) res_lds[r * (3 * K) + c] = res[c];
+    base_lds[r] = active ? ((((uint64_t)n * a.Ho + yo) * a.Wo + xo) * (uint32_t)a.G + g) * (3 * K)
+                         : ~uint64_t(0);
+  }
+  // each wave reads back only the rows its own lanes wrote
+  const uint32_t wave = t >> 6, lane = t & 63u;
+  const uint32_t r0 = wave * rows_wave;
+  for (uint32_t e = lane; e < rows_wave * (3 * K); e += 64) {
+    const uint32_t rl = e / (3 * K), c = e - rl * (3 * K);
+    const uint64_t base = base_lds[r0 + rl];
+    if (base != ~uint64_t(0)) bb.gom[base + c] = res_lds[(r0 + rl) * (3 * K) + c];
   }
 }
 
@@ -1931,7 +1955,10 @@ int32_t tiled_backward_lds(const Plan& p) {
     return 0;
   const int32_t L = p.D / ts.dp;
   if (L != 1 && L != 2 && L != 4) return 0;
-  return ts.lds_bytes;
+  // the write-out reuses the window: a row of 27 floats and an 8-byte base
+  // per (pixel, group) item
+  const int32_t out_bytes = kBlock / L * (27 * 4 + 8);
+  return ts.lds_bytes > out_bytes ? ts.lds_bytes : out_bytes;
 }
 
 dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
@@ -1963,7 +1990,7 @@ dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
     a.nblocks = (int32_t)(nb * per_image);
     b.gy = static_cast<const char*>(gy) + n0 * y_img;
     b.gom = gom + n0 * gom_img;
-    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.lds_bytes, st, a, b);
+    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), tiled_backward_lds(p), st, a, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       note_hip_error(e);
