@@ -1215,19 +1215,25 @@ struct GatherArgs {
   u32x4* recs;         // [rows][cap][W+1] {p within its image, m, lh, lw} as bits
   uint32_t cap;
   uint32_t samples;    // samples of this chunk, < 2^31
-  uint32_t waves;      // gather waves of this chunk
   int32_t K, lg_shift, nchunk;  // nchunk: vectors of V channels per group
   int32_t nblocks;     // gather workgroups
   int32_t strips, bands;        // gather: column strips and row bands per (n, g)
+  int32_t band_groups;          // gather workgroups per strip: kGatherWaves bands each
+  int32_t band_rows;            // pixel rows of one band
+  uint32_t xs;                  // bits of the output column in a record's pixel
+  // gather: window of grad_y staged in LDS per workgroup (OWH x OWW output
+  // pixels of the workgroup's group from (floor((y_lo + oy_off) / sh),
+  // floor((cx0 + ox_off) / sw))); OWH = 0: not staged
+  int32_t OWH, OWW, oy_off, ox_off;
   // bucket tiles: TH x TW output pixels (TW = 1 << tw_shift), their cell
   // window of WH x WW cells starting at (ty0*sh + wy_off, tx0*sw + wx_off)
   int32_t TH, tw_shift, WH, WW, wy_off, wx_off, tiles_x, tiles_y;
   FastDiv div_K, div_kw, div_G, div_W, div_H, div_WW, div_tx, div_ty;
-  FastDiv div_strips, div_bands;
+  FastDiv div_strips, div_bgroups, div_OWW, div_vpp;
 };
 
 struct SampleRec {
-  uint32_t p;        // output pixel within its image
+  uint32_t p;        // output pixel within its image, (yo << xs) | xo
   int y0, x0;
   float m, lh, lw;
   bool inside;
@@ -1262,7 +1268,7 @@ __device__ __forceinline__ SampleRec sample_at(const GatherArgs& ga, uint32_t pi
   }
   const Cell c = locate(sample_location<MODE>(by, bx, gyy, gxx, dy, dx, a.offset_scale, sg),
                         a.Hm1, a.Wm1);
-  r.p = yo * (uint32_t)a.Wo + xo;
+  r.p = (yo << ga.xs) | xo;
   r.y0 = c.y0;
   r.x0 = c.x0;
   r.lh = c.lh;
@@ -1380,11 +1386,13 @@ __device__ __forceinline__ void load_widen(const typename Io<DT>::raw* p, float*
   }
 }
 
-// Records taken per round of a lane's bucket loop: their loads, then their
-// grad_y loads, are all in flight before the first is used.
-constexpr int kGatherU = 8;
-// Pixel rows of one band of the gather walk.
-constexpr int kGatherBand = 8;
+
+// Waves per gather workgroup: consecutive bands of one strip.
+constexpr int kGatherWaves = 4;
+
+__device__ __forceinline__ int floor_div(int a, int b) {
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
 
 // A wave owns (image n, group g, band of pixel rows [y_lo, y_hi), strip of
 // Lc = 64 >> lg_shift bucket columns [cx0, cx0 + Lc)); lane (lc, li) takes
@@ -1399,34 +1407,67 @@ constexpr int kGatherBand = 8;
 // kept from the previous row.  Strips overlap by one column; the strip's
 // first lane only feeds its right neighbour, and the band's first row only
 // the next row.
-template <int DT, int V, bool VST>
+// A workgroup is kGatherWaves bands of one strip.  STAGE: it first copies
+// the grad_y vectors of its group at the output pixels its cells' samples
+// come from when their displacement is within the margin (a window of
+// OWH x OWW pixels) to LDS; a record from outside the window reads grad_y
+// from global memory.  Each vector is then fetched from global memory once
+// per workgroup instead of once per record (K records per output pixel).
+// U: records taken per round of a lane's bucket loop; their loads, then
+// their grad_y loads, are all in flight before the first is used.
+template <int DT, int V, bool VST, bool STAGE, int U>
 __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
   typedef Io<DT> io;
+  constexpr int es = io::es;
+  extern __shared__ u32x4 gather_lds[];
   const FwdArgs& a = ga.f;
-  const uint32_t wave =
-      ((uint32_t)xcd_block(blockIdx.x, ga.nblocks) * kBlock + threadIdx.x) >> 6;
-  if (wave >= ga.waves) return;  // whole waves leave together
+  const uint32_t wg = (uint32_t)xcd_block(blockIdx.x, ga.nblocks);
+  const uint32_t q1 = fastdiv(wg, ga.div_strips);
+  const uint32_t strip = wg - q1 * (uint32_t)ga.strips;
+  const uint32_t q2 = fastdiv(q1, ga.div_bgroups);
+  const uint32_t bgrp = q1 - q2 * (uint32_t)ga.band_groups;
+  const uint32_t n = fastdiv(q2, ga.div_G);
+  const uint32_t g = q2 - n * (uint32_t)a.G;
   const int lane = (int)(threadIdx.x & 63);
+  const int wave = (int)(threadIdx.x >> 6);
   const int Lg = 1 << ga.lg_shift;
   const int lc = lane >> ga.lg_shift, li = lane & (Lg - 1);
   const int Lc = 64 >> ga.lg_shift;
-  const uint32_t q1 = fastdiv(wave, ga.div_strips);
-  const uint32_t strip = wave - q1 * (uint32_t)ga.strips;
-  const uint32_t q2 = fastdiv(q1, ga.div_bands);
-  const uint32_t band = q1 - q2 * (uint32_t)ga.bands;
-  const uint32_t n = fastdiv(q2, ga.div_G);
-  const uint32_t g = q2 - n * (uint32_t)a.G;
-  const int cx = (int)strip * (Lc - 1) + lc;
-  const bool col_ok = cx <= a.W;
-  const int y_lo = (int)band * kGatherBand;
-  const int y_hi = min(y_lo + kGatherBand, a.H);
-  const uint64_t row = (uint32_t)(a.W + 1);
-  const uint64_t rk0 = (uint64_t)(n * (uint32_t)a.G + g) * (uint32_t)(a.H + 1);  // bucket row 0
-  const uint64_t kb = rk0 * row + (uint32_t)(col_ok ? cx : 0);
+  const int cx0 = (int)strip * (Lc - 1);
+  const int wy_lo = (int)bgrp * (kGatherWaves * ga.band_rows);
   const typename io::raw* gyn = reinterpret_cast<const typename io::raw*>(ga.gy) +
                                 (uint64_t)n * (uint32_t)(a.Ho * a.Wo) * (uint32_t)a.C +
                                 g * (uint32_t)a.D;
+  const uint32_t pbytes = (uint32_t)(a.D * es);  // bytes of one staged pixel
+  int oy0 = 0, ox0 = 0;
+  if constexpr (STAGE) {
+    oy0 = floor_div(wy_lo + ga.oy_off, a.sh);
+    ox0 = floor_div(cx0 + ga.ox_off, a.sw);
+    const uint32_t vpp = pbytes >> 4;  // 16-byte vectors per pixel
+    const uint32_t total = (uint32_t)(ga.OWH * ga.OWW) * vpp;
+    char* lds = reinterpret_cast<char*>(gather_lds);
+    for (uint32_t i = threadIdx.x; i < total; i += kBlock) {
+      const uint32_t pix = fastdiv(i, ga.div_vpp), v = i - pix * vpp;
+      const uint32_t wy = fastdiv(pix, ga.div_OWW), wx = pix - wy * (uint32_t)ga.OWW;
+      const int yo = oy0 + (int)wy, xo = ox0 + (int)wx;
+      if ((unsigned)yo < (unsigned)a.Ho && (unsigned)xo < (unsigned)a.Wo)
+        *reinterpret_cast<u32x4*>(lds + pix * pbytes + v * 16u) = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(gyn + ((uint32_t)yo * (uint32_t)a.Wo + (uint32_t)xo) *
+                                                    (uint32_t)a.C) + v * 16u);
+    }
+    __syncthreads();  // the only barrier: waves without a band may leave after it
+  }
+  const int band = (int)bgrp * kGatherWaves + wave;
+  if (band >= ga.bands) return;
+  const int cx = cx0 + lc;
+  const bool col_ok = cx <= a.W;
+  const int y_lo = band * ga.band_rows;
+  const int y_hi = min(y_lo + ga.band_rows, a.H);
+  const uint64_t row = (uint32_t)(a.W + 1);
+  const uint64_t rk0 = (uint64_t)(n * (uint32_t)a.G + g) * (uint32_t)(a.H + 1);  // bucket row 0
+  const uint64_t kb = rk0 * row + (uint32_t)(col_ok ? cx : 0);
   float* gxn = ga.gx + (uint64_t)n * (uint32_t)(a.H * a.W) * (uint32_t)a.C + g * (uint32_t)a.D;
+  const uint32_t xmask = (1u << ga.xs) - 1u;
   const int rounds = (ga.nchunk + Lg - 1) >> ga.lg_shift;
   for (int rd = 0; rd < rounds; ++rd) {
     const int jc = li + (rd << ga.lg_shift);
@@ -1447,18 +1488,33 @@ __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
       // slot t of this bucket: rp[t * row]
       const u32x4* rp = ga.recs + ((rk0 + (uint32_t)cy) * ga.cap) * row + (uint32_t)(col_ok ? cx : 0);
 #pragma unroll 1
-      for (uint32_t t0 = 0; t0 < cnt; t0 += kGatherU) {
-        u32x4 rc[kGatherU];
+      for (uint32_t t0 = 0; t0 < cnt; t0 += U) {
+        u32x4 rc[U];
 #pragma unroll
-        for (int u = 0; u < kGatherU; ++u)
+        for (int u = 0; u < U; ++u)
           if (t0 + u < cnt) rc[u] = rp[(uint64_t)(t0 + u) * row];
-        float v[kGatherU][V];
+        float v[U][V];
 #pragma unroll
-        for (int u = 0; u < kGatherU; ++u)
-          if (t0 + u < cnt)
-            load_widen<DT, V>(gyn + (uint64_t)rc[u][0] * (uint32_t)a.C + jc * V, v[u]);
+        for (int u = 0; u < U; ++u) {
+          if (t0 + u >= cnt) continue;
+          const uint32_t yo = rc[u][0] >> ga.xs, xo = rc[u][0] & xmask;
+          bool staged = false;
+          if constexpr (STAGE) {
+            const uint32_t wy = yo - (uint32_t)oy0, wx = xo - (uint32_t)ox0;
+            staged = wy < (uint32_t)ga.OWH && wx < (uint32_t)ga.OWW;
+            if (staged) {
+              const char* lds = reinterpret_cast<const char*>(gather_lds);
+              const u32x4 q = *reinterpret_cast<const u32x4*>(
+                  lds + (wy * (uint32_t)ga.OWW + wx) * pbytes + (uint32_t)(jc * V * es));
 #pragma unroll
-        for (int u = 0; u < kGatherU; ++u) {
+              for (int e = 0; e < V; ++e) v[u][e] = io::lane(q, e);
+            }
+          }
+          if (!staged)
+            load_widen<DT, V>(gyn + (yo * (uint32_t)a.Wo + xo) * (uint32_t)a.C + jc * V, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
           if (t0 + u >= cnt) break;
           const float m = __uint_as_float(rc[u][1]);
           const float lh = __uint_as_float(rc[u][2]), lw = __uint_as_float(rc[u][3]);
@@ -1528,7 +1584,8 @@ __device__ __forceinline__ void overflow_sample(const GatherArgs& ga, uint32_t s
   uint32_t n, g;
   const SampleRec r = sample_record<DT, MODE>(ga, s, &n, &g);  // listed samples are inside
   const float gyc = io::dec(reinterpret_cast<const typename io::raw*>(ga.gy)[
-      ((uint64_t)n * (uint32_t)(a.Ho * a.Wo) + r.p) * (uint32_t)a.C + g * (uint32_t)a.D + c]);
+      ((uint64_t)n * (uint32_t)(a.Ho * a.Wo) + (r.p >> ga.xs) * (uint32_t)a.Wo +
+       (r.p & ((1u << ga.xs) - 1u))) * (uint32_t)a.C + g * (uint32_t)a.D + c]);
   const float hh = 1.0f - r.lh, hw = 1.0f - r.lw;
   const float w[4] = {hh * hw, hh * r.lw, r.lh * hw, r.lh * r.lw};
   const bool vy0 = r.y0 >= 0, vy1 = r.y0 < a.H - 1, vx0 = r.x0 >= 0, vx1 = r.x0 < a.W - 1;
@@ -2111,12 +2168,29 @@ gather_fn pick_bucket(int mode) {
                             : dcn4_bucket_kernel<DT, kGroupScale>;
 }
 
-template <int DT>
-gather_fn pick_gather(bool vec, bool vst) {
+template <int DT, int U>
+gather_fn pick_gather_u(bool vec, bool vst, bool stage) {
   constexpr int V = 16 / Io<DT>::es;
-  if (!vec) return dcn4_gather_kernel<DT, 1, false>;
-  return vst ? dcn4_gather_kernel<DT, V, true> : dcn4_gather_kernel<DT, V, false>;
+  if (!vec) return dcn4_gather_kernel<DT, 1, false, false, U>;
+  if (stage)
+    return vst ? dcn4_gather_kernel<DT, V, true, true, U> : dcn4_gather_kernel<DT, V, false, true, U>;
+  return vst ? dcn4_gather_kernel<DT, V, true, false, U> : dcn4_gather_kernel<DT, V, false, false, U>;
 }
+
+// Shape of the gather walk (measured on the workloads): short bands and two
+// records per round where occupancy matters more than loads in flight -- a
+// staged grad_y window (the window then covers fewer rows and takes less
+// LDS) or groups spanning 8 or more lanes (few columns per wave); otherwise
+// 8-row bands with 8 records per round.
+template <int DT>
+gather_fn pick_gather(bool vec, bool vst, bool stage, bool short_band) {
+  return short_band ? pick_gather_u<DT, 2>(vec, vst, stage) : pick_gather_u<DT, 8>(vec, vst, stage);
+}
+
+// LDS budget of the gather's staged grad_y window: four workgroups per CU.
+// Larger windows (64-byte groups: fp32 or D = 32) measured slower staged, at
+// two workgroups per CU, than reading grad_y from global memory.
+constexpr int kGatherLdsBudget = 40 * 1024;
 
 dcn4_status check_launch() {
   const hipError_t e = hipGetLastError();
@@ -2135,23 +2209,41 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   const bool vec = p.D % (16 / p.es) == 0 && ((uintptr_t)gy & 15) == 0;
   const bool vst = vec && ((uintptr_t)gx & 15) == 0;
   const int V = vec ? 16 / p.es : 1;
+  // grad_y window of a gather workgroup: the output pixels whose samples
+  // land in its cells when the displacement is within the margin M
+  const int lg = gather_lg(p.D, V), Lc = 64 >> lg;
+  const bool gsm = p.mode == kGroupScale;
+  const int hy = (d.kernel_h - 1) >> 1, hx = (d.kernel_w - 1) >> 1;
+  const int M = gsm ? 4 + 4 * (hy > hx ? hy : hx) : 4;
+  // the staging test takes the short band's window; without staging, short
+  // bands pay only where a wave spans few columns
+  const int short_rows = 4, long_rows = 8;
+  const int rows_wg = kGatherWaves * short_rows;
+  const int oy_off = gsm ? -1 + d.pad_h - hy - M : -1 + d.pad_h - (d.kernel_h - 1) * d.dilation_h - M;
+  const int ox_off = gsm ? -1 + d.pad_w - hx - M : -1 + d.pad_w - (d.kernel_w - 1) * d.dilation_w - M;
+  const int span_y = rows_wg + 2 * M + (gsm ? 0 : (d.kernel_h - 1) * d.dilation_h);
+  const int span_x = Lc - 1 + 2 * M + (gsm ? 0 : (d.kernel_w - 1) * d.dilation_w);
+  const int OWH = span_y / d.stride_h + 2, OWW = span_x / d.stride_w + 2;
+  const int64_t stage_bytes = (int64_t)OWH * OWW * p.D * p.es;
+  const bool stage = vec && stage_bytes <= kGatherLdsBudget;
+  const bool short_band = stage || lg >= 3;
   gather_fn bucket, gather;
   typedef void (*overflow_fn)(GatherArgs, int32_t);
   overflow_fn ovf;
   switch (d.dtype) {
     case DCN4_F32:
       bucket = pick_bucket<DCN4_F32>(p.mode);
-      gather = pick_gather<DCN4_F32>(vec, vst);
+      gather = pick_gather<DCN4_F32>(vec, vst, stage, short_band);
       ovf = dcn4_overflow_kernel<DCN4_F32>;
       break;
     case DCN4_BF16:
       bucket = pick_bucket<DCN4_BF16>(p.mode);
-      gather = pick_gather<DCN4_BF16>(vec, vst);
+      gather = pick_gather<DCN4_BF16>(vec, vst, stage, short_band);
       ovf = dcn4_overflow_kernel<DCN4_BF16>;
       break;
     default:
       bucket = pick_bucket<DCN4_F16>(p.mode);
-      gather = pick_gather<DCN4_F16>(vec, vst);
+      gather = pick_gather<DCN4_F16>(vec, vst, stage, short_band);
       ovf = dcn4_overflow_kernel<DCN4_F16>;
       break;
   }
@@ -2179,11 +2271,21 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   ga.div_WW = make_fastdiv((uint32_t)bt.WW);
   ga.div_tx = make_fastdiv((uint32_t)ga.tiles_x);
   ga.div_ty = make_fastdiv((uint32_t)ga.tiles_y);
-  const int Lc = 64 >> ga.lg_shift;
   ga.strips = (d.W + Lc - 2) / (Lc - 1);
-  ga.bands = (d.H + kGatherBand - 1) / kGatherBand;
+  ga.band_rows = short_band ? short_rows : long_rows;
+  ga.bands = (d.H + ga.band_rows - 1) / ga.band_rows;
+  ga.band_groups = (ga.bands + kGatherWaves - 1) / kGatherWaves;
   ga.div_strips = make_fastdiv((uint32_t)ga.strips);
-  ga.div_bands = make_fastdiv((uint32_t)ga.bands);
+  ga.div_bgroups = make_fastdiv((uint32_t)ga.band_groups);
+  ga.xs = 0;
+  while ((1u << ga.xs) < (uint32_t)p.Wo) ++ga.xs;
+  ga.OWH = stage ? OWH : 0;
+  ga.OWW = stage ? OWW : 1;
+  ga.oy_off = oy_off;
+  ga.ox_off = ox_off;
+  ga.div_OWW = make_fastdiv((uint32_t)ga.OWW);
+  ga.div_vpp = make_fastdiv((uint32_t)((p.D * p.es) >> 4 > 0 ? (p.D * p.es) >> 4 : 1));
+  const int gather_lds = stage ? (int)stage_bytes : 0;
   char* w = static_cast<char*>(ws);
   ga.listed = reinterpret_cast<uint32_t*>(w);
   ga.counts = reinterpret_cast<uint32_t*>(w + 256);
@@ -2200,8 +2302,7 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
     ga.gy = static_cast<const char*>(gy) + n0 * y_img;
     ga.gx = gx + n0 * x_img;
     ga.samples = (uint32_t)(nb * sh.samples_img);
-    ga.waves = (uint32_t)((uint64_t)nb * d.group * ga.bands * ga.strips);
-    ga.nblocks = (int32_t)((ga.waves + kBlock / 64 - 1) / (kBlock / 64));
+    ga.nblocks = (int32_t)((uint64_t)nb * d.group * ga.band_groups * ga.strips);
     const uint64_t zero_words = 64 + (uint64_t)nb * sh.keys_img;
     const uint64_t zb = (zero_words + kBlock - 1) / kBlock;
     hipLaunchKernelGGL(dcn4_fill_zero_kernel, dim3((unsigned)(zb < 65536 ? zb : 65536)),
@@ -2211,7 +2312,7 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
     const uint64_t bblocks = (uint64_t)nb * d.group * ga.tiles_y * ga.tiles_x;
     hipLaunchKernelGGL(bucket, dim3((unsigned)bblocks), dim3(kBlock), bt.lds_bytes, st, ga);
     if ((s = check_launch()) != DCN4_OK) return s;
-    hipLaunchKernelGGL(gather, dim3((unsigned)ga.nblocks), dim3(kBlock), 0, st, ga);
+    hipLaunchKernelGGL(gather, dim3((unsigned)ga.nblocks), dim3(kBlock), gather_lds, st, ga);
     if ((s = check_launch()) != DCN4_OK) return s;
     const uint64_t ob = ((uint64_t)ga.samples * p.D + kBlock - 1) / kBlock;
     hipLaunchKernelGGL(ovf, dim3((unsigned)(ob < 512 ? ob : 512)), dim3(kBlock), 0, st, ga,
