@@ -90,13 +90,13 @@ def bwd_cases():
     return cases
 
 
-def bwd_inputs(s, dt, seed):
+def bwd_inputs(s, dt, seed, off_range=3.0):
     o = oracle.get()
     Ho, Wo = o.out_size(s)
     rng = np.random.default_rng(seed)
     K = s.K
     x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
-    off = rng.uniform(-3, 3, (s.N, Ho, Wo, s.G, 2 * K)).astype(np.float32)
+    off = rng.uniform(-off_range, off_range, (s.N, Ho, Wo, s.G, 2 * K)).astype(np.float32)
     m = (rng.standard_normal((s.N, Ho, Wo, s.G, K)) / 3).astype(np.float32)
     scales = rng.uniform(0.5, 3.0, s.G).astype(np.float32) if s.multiscale else None
     ps = rng.uniform(0.5, 1.5, (s.N, Ho, Wo, s.G)).astype(np.float32) if s.pixel_scales else None
@@ -260,3 +260,26 @@ def test_backward_allocating_entry():
     ref = oracle.get().backward(s, dt, inp.x, inp.om, gy_raw)
     check_bound(gx.cpu().numpy(), ref["gx"], ref["gx_abs"], ref["max_terms"], "allocating grad_x")
     check_bound(gom.cpu().numpy(), ref["gom"], ref["gom_abs"], ref["max_terms"], "allocating grad_om")
+
+
+FAR = [
+    # shapes whose gather stages grad_y in LDS (groups of 16, 32 or 48 bytes),
+    # with displacements up to 12 pixels: many records come from output
+    # pixels outside the staged window and read global memory
+    (Shape(2, 37, 41, 64, 4), "bf16"),
+    (Shape(1, 35, 70, 32, 4), "f16"),                               # D=8: 64 columns per strip
+    (Shape(1, 33, 29, 72, 3), "bf16"),                              # D=24: 3 vectors per group
+    (Shape(1, 40, 36, 64, 4, sh=2, sw=2, dh=2, dw=2, ph=2, pw=2), "bf16"),
+    (Shape(1, 30, 34, 64, 4, multiscale=True), "f16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FAR)))
+def test_gather_far_samples(case):
+    s, dt = FAR[case]
+    inp, gy = bwd_inputs(s, dt, seed=900 + case, off_range=12.0)
+    plan = d4.Plan(desc_of(s, dt))
+    say(f"gather far samples {case}: {s} {dt}")
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
+    gx, _ = run_backward(plan, inp, gy, dt, want_om=False)
+    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], f"far samples {case}")
