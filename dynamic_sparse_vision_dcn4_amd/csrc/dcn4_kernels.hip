@@ -585,7 +585,10 @@ __device__ __forceinline__ TileOrigin tile_origin(const TileArgs& a) {
 // fixed.  Returns the input's buffer descriptor for the image.
 template <int es>
 __device__ __forceinline__ rsrc_t stage_window(const TileArgs& a, const TileOrigin& o, char* lds) {
-  const uint32_t t = threadIdx.x, lane = t & 63u, wave0 = t - lane;
+  const uint32_t t = threadIdx.x, lane = t & 63u;
+  // first thread of the wave, made provably uniform: the LDS destination of
+  // a global-to-LDS copy must be, or the compiler loops over its values
+  const uint32_t wave0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(t - lane));
   const uint32_t pix_bytes = (uint32_t)(a.C * es);
   const int wy0 = o.wy0, wx0 = o.wx0;
   const uint32_t g0 = o.g0;
@@ -629,7 +632,10 @@ __device__ __forceinline__ rsrc_t stage_window(const TileArgs& a, const TileOrig
 template <int es>
 __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin& o, int K,
                                              char* lds_om) {
-  const uint32_t t = threadIdx.x, lane = t & 63u, wave0 = t - lane;
+  const uint32_t t = threadIdx.x, lane = t & 63u;
+  // first thread of the wave, made provably uniform: the LDS destination of
+  // a global-to-LDS copy must be, or the compiler loops over its values
+  const uint32_t wave0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(t - lane));
   const int ty0 = o.ty0, tx0 = o.tx0;
   const uint32_t g0 = o.g0;
   const rsrc_t omr = make_rsrc(a.om + (uint64_t)o.n * a.om_img_bytes, a.om_img_bytes);
