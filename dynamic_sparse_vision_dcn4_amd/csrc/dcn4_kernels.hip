@@ -876,6 +876,7 @@ struct BwdArgs {
   int32_t lg_shift;       // log2(Lg)
   int64_t lanes;          // lanes of this launch
   uint64_t x_bytes;       // input bytes of this launch
+  int32_t nvec;           // vector kernel: 16-byte vectors per group, D*es/16
 };
 
 template <int DT, int MODE, int KS>
@@ -993,6 +994,127 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
       }
     }
   }
+}
+
+// grad_offset_mask alone (grad_x gathered or not asked for) where the tiled
+// kernel does not apply, for groups of whole 16-byte vectors and 16-byte
+// aligned tensors: Lg lanes per (pixel, group) item, lane li owning the
+// group's vectors li, li + Lg, ...; per point one 16-byte corner load per
+// vector (zero outside, via the buffer range check), grad_y loaded once per
+// item; the three sums of the item reduced by xor-shuffles.  The item's row
+// of 3K values collects in LDS; a workgroup's items are consecutive, so
+// their rows are one contiguous block of the tensor, stored with consecutive
+// threads on consecutive floats.  Sampling decisions and the per-channel
+// arithmetic are those of dcn4_backward_kernel (channels summed in another
+// order).
+template <int DT, int MODE, int KS>
+__global__ __launch_bounds__(kBlock) void dcn4_backward_om_kernel(BwdArgs b) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  constexpr int V = 16 / es;
+  extern __shared__ float om_rows[];  // [kBlock >> lg_shift][3K]
+  const FwdArgs& a = b.f;
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const bool active = gid < b.lanes;
+  const int Lg = 1 << b.lg_shift;
+  const uint32_t item = (uint32_t)((active ? gid : 0) >> b.lg_shift);
+  const uint32_t li = (uint32_t)threadIdx.x & (uint32_t)(Lg - 1);
+  const uint32_t p = fastdiv(item, a.div_ipp);  // ipp = G here
+  const uint32_t g = item - p * (uint32_t)a.G;
+  const uint32_t n = fastdiv(p, a.div_hw);
+  const uint32_t rem = p - n * (uint32_t)(a.Ho * a.Wo);
+  const uint32_t yo = fastdiv(rem, a.div_wo);
+  const uint32_t xo = rem - yo * (uint32_t)a.Wo;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  const int kw = KS ? KS : a.kw;
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(b.om) +
+                               (uint64_t)item * (uint32_t)(3 * K);
+  const rsrc_t xr = make_rsrc(b.x, (uint32_t)(b.x_bytes < 0x7fffffffu ? b.x_bytes : 0x7fffffffu));
+  const uint32_t pix_bytes = (uint32_t)a.C * es;
+  const uint32_t img_off = n * a.img_bytes + g * (uint32_t)(a.D * es);
+  const char* gyp = b.gy + ((uint64_t)p * (uint32_t)a.C + g * (uint32_t)a.D) * es;
+  const float sg = (MODE == kGroupScale) ? group_scale(a, p, g) : 1.0f;
+  const float f = (MODE == kGroupScale) ? sg : a.offset_scale;
+  const int hy = ((KS ? KS : a.kh) - 1) >> 1, hx = (kw - 1) >> 1;
+  const uint32_t row0 = threadIdx.x >> b.lg_shift;  // the item's row in this workgroup
+
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const int i = k / kw, j = k - (k / kw) * kw;
+    const float dx = io::dec(om[2 * k]);
+    const float dy = io::dec(om[2 * k + 1]);
+    const float m = io::dec(om[2 * K + k]);
+    float by, bx, gyy = 0.0f, gxx = 0.0f;
+    if (MODE == kGroupScale) {
+      by = (float)((int)yo * a.sh - a.ph + hy);
+      bx = (float)((int)xo * a.sw - a.pw + hx);
+      gyy = (float)(i - hy);
+      gxx = (float)(j - hx);
+    } else {
+      by = (float)((int)yo * a.sh - a.ph + i * a.dh);
+      bx = (float)((int)xo * a.sw - a.pw + j * a.dw);
+    }
+    const Cell c = locate(sample_location<MODE>(by, bx, gyy, gxx, dy, dx, a.offset_scale, sg),
+                          a.Hm1, a.Wm1);
+    float gm = 0.0f, gdr = 0.0f, gdc = 0.0f;
+    if (c.inside) {
+      const bool vy0 = c.y0 >= 0, vy1 = c.y0 < a.H - 1;
+      const bool vx0 = c.x0 >= 0, vx1 = c.x0 < a.W - 1;
+      const bool ok[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+      const float lh = c.lh, lw = c.lw, hh = 1.0f - lh, hw = 1.0f - lw;
+      const float w[4] = {hh * hw, hh * lw, lh * hw, lh * lw};
+      const int cy[4] = {c.y0, c.y0, c.y0 + 1, c.y0 + 1};
+      const int cx[4] = {c.x0, c.x0 + 1, c.x0, c.x0 + 1};
+      uint32_t q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        q[r] = ok[r] ? img_off + (uint32_t)(cy[r] * a.W + cx[r]) * pix_bytes : kOutside;
+#pragma unroll 1
+      for (int jv = (int)li; jv < b.nvec; jv += Lg) {
+        u32x4 vv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vv[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(q[r] + 16u * (uint32_t)jv), 0, 0);
+        const u32x4 gw = *reinterpret_cast<const u32x4*>(gyp + 16 * jv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float v0 = io::lane(vv[0], e), v1 = io::lane(vv[1], e);
+          const float v2 = io::lane(vv[2], e), v3 = io::lane(vv[3], e);
+          const float gyc = io::lane(gw, e);
+          float B = w[0] * v0;
+          B = __builtin_fmaf(w[1], v1, B);
+          B = __builtin_fmaf(w[2], v2, B);
+          B = __builtin_fmaf(w[3], v3, B);
+          const float dBr = __builtin_fmaf(lw, v3 - v1, hw * (v2 - v0));
+          const float dBc = __builtin_fmaf(lh, v3 - v2, hh * (v1 - v0));
+          gm = __builtin_fmaf(gyc, B, gm);
+          gdr = __builtin_fmaf(gyc, dBr, gdr);
+          gdc = __builtin_fmaf(gyc, dBc, gdc);
+        }
+      }
+    }
+    // the item's Lg lanes are consecutive and Lg-aligned in the wave
+    for (int off = 1; off < Lg; off <<= 1) {
+      gm += __shfl_xor(gm, off, 64);
+      gdr += __shfl_xor(gdr, off, 64);
+      gdc += __shfl_xor(gdc, off, 64);
+    }
+    if (li == 0) {
+      float* row = om_rows + row0 * (uint32_t)(3 * K);
+      const float mf = m * f;
+      row[2 * k] = mf * gdc;      // dx moves the column
+      row[2 * k + 1] = mf * gdr;  // dy moves the row
+      row[2 * K + k] = gm;
+    }
+  }
+  __syncthreads();
+  // rows of this workgroup's items: one contiguous block from item0
+  const int64_t item0 = ((int64_t)blockIdx.x * kBlock) >> b.lg_shift;
+  const int64_t items_total = b.lanes >> b.lg_shift;
+  const int64_t rows = min((int64_t)(kBlock >> b.lg_shift), items_total - item0);
+  const int64_t vals = rows * (3 * K);
+  float* go = b.gom + item0 * (3 * K);
+  for (int64_t e = threadIdx.x; e < vals; e += kBlock) go[e] = om_rows[e];
 }
 
 // Tiled backward for the offset/weight gradients alone (a call without
@@ -2361,20 +2483,36 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
   if (!gx && vector_path && p.kernel_choice != kKernelDirect && tiled_backward_lds(p) > 0)
     return launch_tiled_backward(p, x, om, gy, gom, st);
   const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  // grad_offset_mask alone on whole 16-byte vectors: the vector kernel, its
+  // rows collected in LDS
+  const int nvec = (p.D * p.es) % 16 == 0 ? p.D * p.es / 16 : 0;
+  int vec_lg = 0;
+  while ((1 << vec_lg) < nvec && vec_lg < 4) ++vec_lg;
+  const int om_lds = (kBlock >> vec_lg) * 3 * p.K * 4;
+  const bool om_vec = !gx && vector_path && nvec > 0 && om_lds <= kLdsBudget;
   typedef void (*bwd_fn)(BwdArgs);
   bwd_fn fn;
   const int m = p.mode;
-#define DCN4_BWD_PICK(DT)                                                              \
-  fn = m == kStdUnitScale ? (K3 ? dcn4_backward_kernel<DT, kStdUnitScale, 3>          \
-                                : dcn4_backward_kernel<DT, kStdUnitScale, 0>)         \
-     : m == kStdScaled ? (K3 ? dcn4_backward_kernel<DT, kStdScaled, 3>                 \
-                             : dcn4_backward_kernel<DT, kStdScaled, 0>)                \
-                       : (K3 ? dcn4_backward_kernel<DT, kGroupScale, 3>                \
-                             : dcn4_backward_kernel<DT, kGroupScale, 0>)
+#define DCN4_BWD_PICK(KERNEL, DT)                                                      \
+  fn = m == kStdUnitScale ? (K3 ? KERNEL<DT, kStdUnitScale, 3>                        \
+                                : KERNEL<DT, kStdUnitScale, 0>)                       \
+     : m == kStdScaled ? (K3 ? KERNEL<DT, kStdScaled, 3>                               \
+                             : KERNEL<DT, kStdScaled, 0>)                              \
+                       : (K3 ? KERNEL<DT, kGroupScale, 3>                              \
+                             : KERNEL<DT, kGroupScale, 0>)
   switch (d.dtype) {
-    case DCN4_F32: DCN4_BWD_PICK(DCN4_F32); break;
-    case DCN4_BF16: DCN4_BWD_PICK(DCN4_BF16); break;
-    default: DCN4_BWD_PICK(DCN4_F16); break;
+    case DCN4_F32:
+      if (om_vec) DCN4_BWD_PICK(dcn4_backward_om_kernel, DCN4_F32);
+      else DCN4_BWD_PICK(dcn4_backward_kernel, DCN4_F32);
+      break;
+    case DCN4_BF16:
+      if (om_vec) DCN4_BWD_PICK(dcn4_backward_om_kernel, DCN4_BF16);
+      else DCN4_BWD_PICK(dcn4_backward_kernel, DCN4_BF16);
+      break;
+    default:
+      if (om_vec) DCN4_BWD_PICK(dcn4_backward_om_kernel, DCN4_F16);
+      else DCN4_BWD_PICK(dcn4_backward_kernel, DCN4_F16);
+      break;
   }
 #undef DCN4_BWD_PICK
   BwdArgs b{};
@@ -2384,7 +2522,8 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
   b.f.ipp = d.group;
   b.f.div_ipp = make_fastdiv((uint32_t)d.group);
   b.scales = scales;
-  b.lg_shift = backward_lg_shift(p.D);
+  b.lg_shift = om_vec ? vec_lg : backward_lg_shift(p.D);
+  b.nvec = nvec;
   const int64_t lanes_per_image = (int64_t)p.Ho * p.Wo * d.group << b.lg_shift;
   const uint64_t x_img = (uint64_t)d.H * d.W * d.C * p.es;
   // per launch: lanes below 2^31 and input bytes below 2^31 (32-bit buffer
@@ -2408,7 +2547,7 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
     b.x_bytes = nb * x_img;
     b.lanes = nb * lanes_per_image;
     const int64_t blocks = (b.lanes + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), 0, st, b);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), om_vec ? om_lds : 0, st, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       note_hip_error(e);
