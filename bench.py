@@ -240,7 +240,8 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
-    plan = d4.Plan(desc)
+    opts = {k: int(v) for k, v in (o.split("=", 1) for o in args.option)}
+    plan = d4.Plan(desc, channels_per_lane=args.channels_per_lane, **opts)
     Ho, Wo = plan.Ho, plan.Wo
     es = 4 if w.dtype == "f32" else 2
     nx = w.N * w.H * w.W * w.C
