@@ -1,8 +1,11 @@
 /* A plain C client of libdcn4.so: no PyTorch, only the C ABI and the HIP
  * runtime for device memory.  Runs one forward pass of a small bf16 problem
  * whose exact result is known (integer offsets and one-hot weights make the
- * output a shifted copy of the input, zero where the shift leaves the image)
- * and prints "OK" or the first mismatch.  Exit status 0 on success. */
+ * output a shifted copy of the input, zero where the shift leaves the image),
+ * then the backward pass of the same problem, whose grad_x is grad_y shifted
+ * back (one term per element, exact), through dcn4_backward (which allocates
+ * its workspace) and dcn4_backward_ws (a workspace from hipMalloc); prints
+ * "OK" or the first mismatch.  Exit status 0 on success. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -71,10 +74,61 @@ int main(void) {
             return 1;
           }
         }
+  /* backward: grad_x[n, r, q, c] = grad_y at the output pixel whose sample
+   * of weight 1 lands on (r, q), 0 where no output pixel does */
+  uint16_t* hg = malloc(ny * 2);
+  float* hgx = malloc(nx * 4);
+  for (size_t i = 0; i < ny; ++i) hg[i] = bf16((float)((int)(i % 13) - 6));
+  void *dg, *dgx, *ws;
+  uint64_t wsb = 0;
+  if (dcn4_backward_workspace_size(plan, &wsb) != DCN4_OK || wsb == 0) {
+    printf("workspace size: %s\n", dcn4_last_error());
+    return 1;
+  }
+  if (hipMalloc(&dg, ny * 2) || hipMalloc(&dgx, nx * 4) || hipMalloc(&ws, wsb)) {
+    printf("hipMalloc failed\n");
+    return 1;
+  }
+  hipMemcpy(dg, hg, ny * 2, hipMemcpyHostToDevice);
+  for (int pass = 0; pass < 2; ++pass) {
+    hipMemset(dgx, 0xff, nx * 4); /* NaN: every element must be written */
+    st = pass == 0 ? dcn4_backward(plan, dx, dom, NULL, NULL, dg, (float*)dgx, NULL, NULL)
+                   : dcn4_backward_ws(plan, dx, dom, NULL, NULL, dg, (float*)dgx, NULL, ws, wsb,
+                                      NULL);
+    if (st != DCN4_OK) { printf("backward pass %d: %s\n", pass, dcn4_last_error()); return 1; }
+    if (hipDeviceSynchronize() != hipSuccess) { printf("sync failed\n"); return 1; }
+    hipMemcpy(hgx, dgx, nx * 4, hipMemcpyDeviceToHost);
+    for (int n = 0; n < N; ++n)
+      for (int r = 0; r < H; ++r)
+        for (int q = 0; q < W; ++q)
+          for (int c = 0; c < C; ++c) {
+            const int g = c / D;
+            const int yo = g == 0 ? r - 2 : r, xo = g == 0 ? q - 1 : q + 1;
+            float want = 0.0f;
+            if (yo >= 0 && yo < Ho && xo >= 0 && xo < Wo) {
+              const uint32_t u = (uint32_t)hg[(((size_t)n * Ho + yo) * Wo + xo) * C + c] << 16;
+              memcpy(&want, &u, 4);
+            }
+            const float got = hgx[(((size_t)n * H + r) * W + q) * C + c];
+            if (got != want) {
+              printf("backward pass %d mismatch n=%d y=%d x=%d c=%d got %g want %g\n", pass, n, r,
+                     q, c, got, want);
+              return 1;
+            }
+          }
+  }
   dcn4_destroy(plan);
   hipFree(dx);
   hipFree(dom);
   hipFree(dy);
+  hipFree(dg);
+  hipFree(dgx);
+  hipFree(ws);
+  free(hx);
+  free(hom);
+  free(hy);
+  free(hg);
+  free(hgx);
   printf("OK\n");
   return 0;
 }

@@ -1,6 +1,8 @@
 """The C ABI used from plain C (no PyTorch): tests/c/abi_forward.c, built by
 __graft_entry__.build(), allocates with hipMalloc, runs dcn4_forward on a
-problem whose exact output is a shifted copy of the input, and checks it."""
+problem whose exact output is a shifted copy of the input, then the backward
+(dcn4_backward and dcn4_backward_ws) whose exact grad_x is grad_y shifted
+back, and checks both."""
 import os
 import subprocess
 
