@@ -1313,18 +1313,20 @@ __global__ __launch_bounds__(kBlock) void dcn4_fill_zero_kernel(float* p, uint64
 //     full rate); one device atomic per non-empty cell of the tile's cell
 //     window then reserves that cell's slots, and consecutive cells of a
 //     window row are consecutive keys, so these coalesce; every sample
-//     writes the record {p, m, lh, lw} to its slot of the bucket of (image,
-//     group, cell), key = row*(W+1) + x0+1 with row = (n*G + g)*(H+1) +
-//     y0+1.  Slot t of the buckets of one row is stored for all W+1 columns
+//     writes the record {p, m, lh, lw} (p = output row << xs | output
+//     column) to its slot of the bucket of (image, group, cell), key =
+//     row*(W+1) + x0+1 with row = (n*G + g)*(H+1) + y0+1.  Slot t of the buckets of one row is stored for all W+1 columns
 //     side by side (record index (row*cap + t)*(W+1) + x0+1), so the gather's
 //     lanes, which take consecutive columns, read consecutive records.  A
 //     sample whose cell falls outside the window takes its slot with its own
 //     device atomic.
-//  2. gather: 2^lg_shift lanes per (input pixel (y, x), group) read the
-//     records of the four cells that have the pixel as a corner -- cell
-//     (y, x) as corner 00, (y, x-1) as 01, (y-1, x) as 10, (y-1, x-1) as 11
-//     -- and accumulate fl(m*w_r) * dL/dy per channel in registers (fused
-//     multiply-add); every sum is written once, so grad_x needs no clearing.
+//  2. gather: input pixel (y, x) is corner 00 of cell (y, x), 01 of
+//     (y, x-1), 10 of (y-1, x) and 11 of (y-1, x-1).  A wave walks a strip
+//     of bucket columns down a band of rows, reads each bucket's records
+//     once and accumulates fl(m*w_r) * dL/dy per channel into one partial
+//     sum per corner (fused multiply-add); a pixel adds the four partial
+//     sums of its cells (one from the lane to its left, two from the
+//     previous row) and is written once, so grad_x needs no clearing.
 //  3. overflow: a bucket holds `cap` records; a sample whose slot is beyond
 //     it is listed instead, and this launch adds its products with atomics
 //     after the gather has written grad_x.
