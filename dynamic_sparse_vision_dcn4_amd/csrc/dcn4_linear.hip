@@ -123,13 +123,17 @@ __global__ __launch_bounds__(256) void dcn4_linear_gemm_kernel(LinArgs a) {
   const int sr = tid / kGmVpr, sq = tid % kGmVpr;
   u32x4 gf[kGmPass], gw[kGmPass];
   auto gload = [&](int k0) {
-    const bool kin = k0 + 8 * sq < Cin;  // inputs past Cin are zero in both operands
 #pragma unroll
     for (int p = 0; p < kGmPass; ++p) {
       const int off = ((sr + kRowsPerPass * p) * Cin + k0 + 8 * sq) * 2;
       gf[p] = __builtin_amdgcn_raw_buffer_load_b128(fr, off, 0, 0);
       gw[p] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
-      if (!kin) gf[p] = gw[p] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (k0 + kGmBK > Cin) {  // the last, partial stage: inputs past Cin are zero
+      const bool kin = k0 + 8 * sq < Cin;
+#pragma unroll
+      for (int p = 0; p < kGmPass; ++p)
+        if (!kin) gf[p] = gw[p] = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto sstore = [&](int st) {
