@@ -283,3 +283,27 @@ def test_gather_far_samples(case):
     ref = oracle.get().backward(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
     gx, _ = run_backward(plan, inp, gy, dt, want_om=False)
     check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], f"far samples {case}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_backward_element_paths(dt):
+    """Tensors that are only element-aligned -- x, the offset/weight tensor
+    and grad_y one element into their buffers, grad_x one float into its --
+    take the element-wise gather and the direct offset/weight-gradient
+    kernel; both gradients within the bound, on both grad_x paths."""
+    s = Shape(2, 19, 21, 32, 2)
+    inp, gy_raw = bwd_inputs(s, dt, seed=77)
+    plan = d4.Plan(desc_of(s, dt))
+    x, om, gy = (to_dev(inp.x, dt, offset_elems=1), to_dev(inp.om, dt, offset_elems=1),
+                 to_dev(gy_raw, dt, offset_elems=1))
+    ref = oracle.get().backward(s, dt, inp.x, inp.om, gy_raw)
+    say(f"backward element paths {s} {dt}")
+    for scatter in (False, True):
+        gxbuf = torch.empty(s.N * s.H * s.W * s.C + 1, dtype=torch.float32, device="cuda")
+        gx = gxbuf[1:].view(s.N, s.H, s.W, s.C)
+        gom = torch.empty(plan.om_shape(), dtype=torch.float32, device="cuda")
+        plan.backward(x, om, gy, grad_x=gx, grad_om=gom, scatter=scatter)
+        torch.cuda.synchronize()
+        what = f"element paths {dt} {'scatter' if scatter else 'gather'}"
+        check_bound(gx.cpu().numpy(), ref["gx"], ref["gx_abs"], ref["max_terms"], what + " grad_x")
+        check_bound(gom.cpu().numpy(), ref["gom"], ref["gom_abs"], ref["max_terms"], what + " grad_om")
