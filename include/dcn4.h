@@ -144,11 +144,13 @@ typedef struct {
   int32_t tile_h, tile_w;    /* tiled kernel: output tile                   */
   int32_t tile_groups;       /* tiled kernel: groups per workgroup          */
   int32_t tile_margin;       /* tiled kernel: window margin in pixels       */
-  int32_t backward_kernel;   /* grad_offset_mask of dcn4_backward: 1 direct,
-                                2 tiled (LDS window), for 16-byte aligned
-                                tensors, when grad_x is gathered or not
-                                asked for; a call that scatters grad_x
-                                (no workspace) runs the direct kernel      */
+  int32_t backward_kernel;   /* grad_offset_mask of dcn4_backward: 2 tiled
+                                (LDS window) for 16-byte aligned tensors
+                                when grad_x is gathered or not asked for;
+                                1 direct otherwise: one lane per 16-byte
+                                channel vector when the tensors allow it,
+                                channel-strided lanes when they do not or
+                                when grad_x is scattered (no workspace)     */
   int32_t backward_lds_bytes; /* dynamic LDS per tiled-backward workgroup   */
   int32_t tile_slices;       /* tiled kernel: channel slices per group (1:
                                 a workgroup's window holds whole groups;
