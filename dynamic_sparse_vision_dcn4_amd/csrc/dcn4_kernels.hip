@@ -857,6 +857,10 @@ void dcn4_tile_kernel(TileArgs a) {
 // decisions (cell, fractions, inside test, scale) come from the forward's
 // device functions, so they are the forward's bit for bit; a sample that is
 // not inside has zero gradient.
+// All three are linear in the corner values, so the kernels first sum
+// S_r = sum_c gy[p, c] * v_r,c per corner r (one fma per channel and corner)
+// and then combine the four sums (point_grads); every term of the
+// definitions above still enters once, with its own fp32 rounding.
 //
 // Lanes: Lg lanes per (pixel, group) item, lane li owning channels li,
 // li + Lg, ... of the group (Lg = the largest power of two <= 16 dividing D).
@@ -878,6 +882,20 @@ struct BwdArgs {
   uint64_t x_bytes;       // input bytes of this launch
   int32_t nvec;           // vector kernel: 16-byte vectors per group, D*es/16
 };
+
+// The point's three gradient sums from its corner sums S (order 00, 01, 10,
+// 11), bilinear weights w and fractions: sum_c gy*B, sum_c gy*dB/drow,
+// sum_c gy*dB/dcol (the latter two before the factor m*f).
+__device__ __forceinline__ void point_grads(const float* S, const float* w, float lh, float lw,
+                                            float& gm, float& gdr, float& gdc) {
+  const float hh = 1.0f - lh, hw = 1.0f - lw;
+  gm = w[0] * S[0];
+  gm = __builtin_fmaf(w[1], S[1], gm);
+  gm = __builtin_fmaf(w[2], S[2], gm);
+  gm = __builtin_fmaf(w[3], S[3], gm);
+  gdr = __builtin_fmaf(lw, S[3] - S[1], hw * (S[2] - S[0]));
+  gdc = __builtin_fmaf(lh, S[3] - S[2], hh * (S[1] - S[0]));
+}
 
 template <int DT, int MODE, int KS>
 __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
@@ -940,6 +958,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
       const int cx[4] = {c.x0, c.x0 + 1, c.x0, c.x0 + 1};
       uint32_t q[4];
       float cm[4];
+      float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // corner sums of gy * v
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // pixel index below 2^23 (H*W < 2^23); only used for corners in the image
@@ -959,15 +978,8 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
             v[r] = io::dec((typename io::raw)__builtin_amdgcn_raw_buffer_load_b16(xr, (int)(q[r] + coff), 0, 0));
         }
         const float gyc = io::dec(gyp[jc << b.lg_shift]);
-        float B = w[0] * v[0];
-        B = __builtin_fmaf(w[1], v[1], B);
-        B = __builtin_fmaf(w[2], v[2], B);
-        B = __builtin_fmaf(w[3], v[3], B);
-        const float dBr = __builtin_fmaf(lw, v[3] - v[1], hw * (v[2] - v[0]));
-        const float dBc = __builtin_fmaf(lh, v[3] - v[2], hh * (v[1] - v[0]));
-        gm = __builtin_fmaf(gyc, B, gm);
-        gdr = __builtin_fmaf(gyc, dBr, gdr);
-        gdc = __builtin_fmaf(gyc, dBc, gdc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[r] = __builtin_fmaf(gyc, v[r], S[r]);
         if (gxp) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
@@ -977,6 +989,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
                               cm[r] * gyc);
         }
       }
+      point_grads(S, w, lh, lw, gm, gdr, gdc);
     }
     if (b.gom) {
       // the item's Lg lanes are consecutive and Lg-aligned in the wave
@@ -1069,6 +1082,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_om_kernel(BwdArgs b) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         q[r] = ok[r] ? img_off + (uint32_t)(cy[r] * a.W + cx[r]) * pix_bytes : kOutside;
+      float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // corner sums of gy * v
 #pragma unroll 1
       for (int jv = (int)li; jv < b.nvec; jv += Lg) {
         u32x4 vv[4];
@@ -1078,20 +1092,12 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_om_kernel(BwdArgs b) {
         const u32x4 gw = *reinterpret_cast<const u32x4*>(gyp + 16 * jv);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const float v0 = io::lane(vv[0], e), v1 = io::lane(vv[1], e);
-          const float v2 = io::lane(vv[2], e), v3 = io::lane(vv[3], e);
           const float gyc = io::lane(gw, e);
-          float B = w[0] * v0;
-          B = __builtin_fmaf(w[1], v1, B);
-          B = __builtin_fmaf(w[2], v2, B);
-          B = __builtin_fmaf(w[3], v3, B);
-          const float dBr = __builtin_fmaf(lw, v3 - v1, hw * (v2 - v0));
-          const float dBc = __builtin_fmaf(lh, v3 - v2, hh * (v1 - v0));
-          gm = __builtin_fmaf(gyc, B, gm);
-          gdr = __builtin_fmaf(gyc, dBr, gdr);
-          gdc = __builtin_fmaf(gyc, dBc, gdc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[r] = __builtin_fmaf(gyc, io::lane(vv[r], e), S[r]);
         }
       }
+      point_grads(S, w, lh, lw, gm, gdr, gdc);
     }
     // the item's Lg lanes are consecutive and Lg-aligned in the wave
     for (int off = 1; off < Lg; off <<= 1) {
@@ -1236,24 +1242,17 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
     // a sample that is not inside reads only zeros: its sums stay zero
     const float hh = 1.0f - lh, hw = 1.0f - lw;
     const float w[4] = {hh * hw, hh * lw, lh * hw, lh * lw};
-    float gm = 0.0f, gdr = 0.0f, gdc = 0.0f;
+    float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // corner sums of gy * v
 #pragma unroll
     for (int n2 = 0; n2 < NV; ++n2)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const int c = n2 * VEC + e;
-        const float v0 = io::lane(vv[0][n2], e), v1 = io::lane(vv[1][n2], e);
-        const float v2 = io::lane(vv[2][n2], e), v3 = io::lane(vv[3][n2], e);
-        float B = w[0] * v0;
-        B = __builtin_fmaf(w[1], v1, B);
-        B = __builtin_fmaf(w[2], v2, B);
-        B = __builtin_fmaf(w[3], v3, B);
-        const float dBr = __builtin_fmaf(lw, v3 - v1, hw * (v2 - v0));
-        const float dBc = __builtin_fmaf(lh, v3 - v2, hh * (v1 - v0));
-        gm = __builtin_fmaf(gyv[c], B, gm);
-        gdr = __builtin_fmaf(gyv[c], dBr, gdr);
-        gdc = __builtin_fmaf(gyv[c], dBc, gdc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[r] = __builtin_fmaf(gyv[c], io::lane(vv[r][n2], e), S[r]);
       }
+    float gm, gdr, gdc;
+    point_grads(S, w, lh, lw, gm, gdr, gdc);
     if (!inside) gm = gdr = gdc = 0.0f;
     // lanes of one (pixel, group) are consecutive; L is 1, 2 or 4
     for (int off = 1; off < a.L; off <<= 1) {
