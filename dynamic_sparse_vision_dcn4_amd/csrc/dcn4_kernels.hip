@@ -1123,21 +1123,25 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_om_kernel(BwdArgs b) {
   for (int64_t e = threadIdx.x; e < vals; e += kBlock) go[e] = om_rows[e];
 }
 
-// Tiled backward for the offset/weight gradients alone (a call without
-// grad_x): the forward's tile decomposition, LDS input window and staged
-// offset/weight values; per point the same window test as the forward, the
-// corners read from LDS (or, for a wave with a point outside the window, from
-// global memory) and the three sums over the lane's channels kept in
-// registers.  When a group spans L = 2 or 4 lanes their sums are added by
-// xor-shuffles.  3x3 kernels.  grad_x is a scatter whose cost on this GPU is
-// its fp32 atomics (about one lane per clock per CU whether they land in LDS
-// or L2), so calls that want it take the direct backward kernel.
+// Tiled backward for the offset/weight gradients (grad_x gathered separately
+// or not asked for): the forward's tile decomposition, LDS input window and
+// staged offset/weight values; per point the same window test as the
+// forward, the corners read from LDS (or, for a wave with a point outside the
+// window, from global memory) and the three sums over the lane's channels
+// kept in registers.  When a group spans L = 2 or 4 lanes their sums are
+// added by xor-shuffles.  A group too wide for one window (channel slices:
+// FlowDCN's 72 channels as three slices of 24) is done by one workgroup slice
+// after slice, the window restaged for each and the sums added in slice
+// order, so the result stays bit-reproducible.  Every mode (group scales:
+// the lane's scale and the centre-based geometry of the forward).  3x3
+// kernels.
 struct BwdTileArgs {
   const char* gy;   // [N,Ho,Wo,C] I/O dtype, this launch
   float* gom;       // [N,Ho,Wo,G,3K] fp32, this launch (written)
+  int32_t nslices;  // channel slices per group, done in turn (1: whole groups)
 };
 
-template <int DT, int VEC, int NV, int MODE>
+template <int DT, int VEC, int NV, int MODE, bool SL>
 __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTileArgs bb) {
   typedef Io<DT> io;
   constexpr int es = io::es;
@@ -1146,7 +1150,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
   extern __shared__ u32x4 lds_u4[];
   char* lds = reinterpret_cast<char*>(lds_u4);
 
-  const TileOrigin org = tile_origin(a);
+  TileOrigin org = tile_origin(a);  // org.s: the slice in the window
   const uint32_t n = org.n, g0 = org.g0;
   const int ty0 = org.ty0, tx0 = org.tx0, wy0 = org.wy0, wx0 = org.wx0;
   const uint32_t t = threadIdx.x;
@@ -1166,11 +1170,43 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
   const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
       lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
 
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  const uint32_t row_lds = (uint32_t)(a.WW * a.PS);
+  const float row_f = (float)row_lds, ps_f = (float)a.PS;
+  const float lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es);
+  const float ymax = (float)(a.WH - 2), xmax = (float)(a.WW - 2);
+  constexpr bool GS = MODE == kGroupScale;
+  constexpr int hy = (KS - 1) >> 1, hx = (KS - 1) >> 1;
+  // point base: the grid point's row/column (standard), the centre (group scales)
+  const int by0 = yo * a.sh - a.ph + (GS ? hy : 0), bx0 = xo * a.sw - a.pw + (GS ? hx : 0);
+  const float ry0 = (float)(by0 - wy0), rx0 = (float)(bx0 - wx0);
+  float sg = 1.0f;  // the lane's group scale (pixel 0 for idle lanes)
+  if constexpr (GS) {
+    FwdArgs fa{};
+    fa.G = a.G; fa.scales = a.scales; fa.pscales = a.pscales; fa.max_scale = a.max_scale;
+    sg = group_scale(fa, active ? ((uint64_t)n * a.Ho + (uint32_t)yo) * a.Wo + (uint32_t)xo : 0, g);
+  }
+  const float f = GS ? sg : (MODE == kStdScaled) ? a.offset_scale : 1.0f;
+  // per point, summed over the slices: sum gy*dB/dcol, sum gy*dB/drow, sum gy*B
+  float res[3 * K];  // then the lane's row of grad_offset_mask, in the tensor's order
+#pragma unroll
+  for (int c = 0; c < 3 * K; ++c) res[c] = 0.0f;
+
+  const int nsl = SL ? bb.nslices : 1;
+  for (int sl = 0; sl < nsl; ++sl) {
+  if (SL && sl > 0) {
+    __syncthreads();  // every wave is done with the previous slice's window
+    org.s = (uint32_t)sl;
+    stage_window<es>(a, org, lds);
+    __syncthreads();
+  }
+  // first channel of the lane: group, slice, lane
+  const uint32_t lane_bytes = (g * (uint32_t)a.D + (uint32_t)sl * (uint32_t)a.DSL + l * DP) * es;
   // upstream gradient of the lane's channels (pixel (0, 0) for idle lanes)
   float gyv[DP];
   {
     const char* gp = bb.gy + (((uint64_t)n * a.Ho + (active ? yo : 0)) * a.Wo + (active ? xo : 0)) *
-                                 pix_bytes + (g * (uint32_t)a.D + l * DP) * es;
+                                 pix_bytes + lane_bytes;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(gp + 16 * v);
@@ -1179,24 +1215,15 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
     }
   }
 
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  const uint32_t row_lds = (uint32_t)(a.WW * a.PS);
-  const float row_f = (float)row_lds, ps_f = (float)a.PS;
-  const float lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es);
-  const float ymax = (float)(a.WH - 2), xmax = (float)(a.WW - 2);
-  const int by0 = yo * a.sh - a.ph, bx0 = xo * a.sw - a.pw;
-  const float ry0 = (float)(by0 - wy0), rx0 = (float)(bx0 - wx0);
-  const float f = (MODE == kStdScaled) ? a.offset_scale : 1.0f;
-  const uint32_t lane_bytes = (g * (uint32_t)a.D + l * DP) * es;
-  float res[3 * K];  // the lane's row of grad_offset_mask, in the tensor's order
-
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int i = k / KS, j = k - (k / KS) * KS;
     const float dx = io::dec(om[2 * k]), dy = io::dec(om[2 * k + 1]);
     const float m = io::dec(om[2 * K + k]);
-    const Loc lc = sample_location<MODE>(ry0 + (float)(i * a.dh), rx0 + (float)(j * a.dw),
-                                         0.0f, 0.0f, dy, dx, a.offset_scale, 1.0f);
+    const float gyy = GS ? (float)(i - hy) : 0.0f, gxx = GS ? (float)(j - hx) : 0.0f;
+    const Loc lc = sample_location<MODE>(GS ? ry0 : ry0 + (float)(i * a.dh),
+                                         GS ? rx0 : rx0 + (float)(j * a.dw), gyy, gxx, dy, dx,
+                                         a.offset_scale, sg);
     const float fy = __builtin_floorf(lc.ty), fx = __builtin_floorf(lc.tx);
     const float yr = lc.by + fy, xr_ = lc.bx + fx;  // corner (y0, x0), window-relative
     const uint64_t off_window =
@@ -1219,8 +1246,9 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
         for (int n2 = 0; n2 < NV; ++n2) vv[r][n2] = d.v[r][n2];
     } else {
       // global path: absolute location, global gathers (zero outside the image)
-      const Cell cc = locate(sample_location<MODE>((float)(by0 + i * a.dh), (float)(bx0 + j * a.dw),
-                                                   0.0f, 0.0f, dy, dx, a.offset_scale, 1.0f),
+      const Cell cc = locate(sample_location<MODE>((float)(GS ? by0 : by0 + i * a.dh),
+                                                   (float)(GS ? bx0 : bx0 + j * a.dw), gyy, gxx,
+                                                   dy, dx, a.offset_scale, sg),
                              a.Hm1, a.Wm1);
       inside = cc.inside;
       lh = cc.lh;
@@ -1260,10 +1288,25 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
       gdr += __shfl_xor(gdr, off, 64);
       gdc += __shfl_xor(gdc, off, 64);
     }
-    const float mf = m * f;
-    res[2 * k] = mf * gdc;      // dx moves the column
-    res[2 * k + 1] = mf * gdr;  // dy moves the row
-    res[2 * K + k] = gm;
+    if constexpr (SL) {
+      res[2 * k] += gdc;      // dx moves the column
+      res[2 * k + 1] += gdr;  // dy moves the row
+      res[2 * K + k] += gm;
+    } else {
+      const float mf = m * f;
+      res[2 * k] = mf * gdc;
+      res[2 * k + 1] = mf * gdr;
+      res[2 * K + k] = gm;
+    }
+  }
+  }  // slices
+  if constexpr (SL) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float mf = io::dec(om[2 * K + k]) * f;
+      res[2 * k] = mf * res[2 * k];
+      res[2 * k + 1] = mf * res[2 * k + 1];
+    }
   }
 
   // Write-out through LDS: a row per (pixel, group) item, 3K floats at odd
@@ -2121,15 +2164,21 @@ int32_t backward_lg_shift(int32_t D) {
 
 typedef void (*tile_bwd_fn)(TileArgs, BwdTileArgs);
 
-template <int DT, int MODE>
-tile_bwd_fn tile_bwd_pick(int nv) {
+template <int DT, int MODE, bool SL>
+tile_bwd_fn tile_bwd_nv(int nv) {
   constexpr int V = 16 / Io<DT>::es;
   switch (nv) {
-    case 1: return dcn4_tile_bwd_kernel<DT, V, 1, MODE>;
-    case 2: return dcn4_tile_bwd_kernel<DT, V, 2, MODE>;
-    case 3: return dcn4_tile_bwd_kernel<DT, V, 3, MODE>;
-    default: return dcn4_tile_bwd_kernel<DT, V, 4, MODE>;
+    case 1: return dcn4_tile_bwd_kernel<DT, V, 1, MODE, SL>;
+    case 2: return dcn4_tile_bwd_kernel<DT, V, 2, MODE, SL>;
+    case 3: return dcn4_tile_bwd_kernel<DT, V, 3, MODE, SL>;
+    default: return dcn4_tile_bwd_kernel<DT, V, 4, MODE, SL>;
   }
+}
+
+// sliced: a workgroup does its group's channel slices in turn
+template <int DT, int MODE>
+tile_bwd_fn tile_bwd_pick(int nv, bool sliced) {
+  return sliced ? tile_bwd_nv<DT, MODE, true>(nv) : tile_bwd_nv<DT, MODE, false>(nv);
 }
 
 // LDS bytes of the tiled backward (0: it does not apply to the plan): the
@@ -2137,9 +2186,8 @@ tile_bwd_fn tile_bwd_pick(int nv) {
 int32_t tiled_backward_lds(const Plan& p) {
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
-  if (!ts.ok || ts.slices != 1 || p.mode == kGroupScale || d.kernel_h != 3 || d.kernel_w != 3)
-    return 0;
-  const int32_t L = p.D / ts.dp;
+  if (!ts.ok || d.kernel_h != 3 || d.kernel_w != 3) return 0;
+  const int32_t L = ts.slices > 1 ? 1 : p.D / ts.dp;
   if (L != 1 && L != 2 && L != 4) return 0;
   // the write-out reuses the window: a row of 27 floats and an 8-byte base
   // per (pixel, group) item
@@ -2148,31 +2196,46 @@ int32_t tiled_backward_lds(const Plan& p) {
 }
 
 dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
-                                  const void* gy, float* gom, hipStream_t st) {
+                                  const float* scales, const float* pscales, const void* gy,
+                                  float* gom, hipStream_t st) {
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
   const int nv = ts.dp / (16 / p.es);
+  const bool sl = ts.slices > 1;
   tile_bwd_fn fn;
-  if (p.mode == kStdScaled)
-    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kStdScaled>(nv)
-       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kStdScaled>(nv)
-                              : tile_bwd_pick<DCN4_F16, kStdScaled>(nv);
+  if (p.mode == kGroupScale)
+    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kGroupScale>(nv, sl)
+       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kGroupScale>(nv, sl)
+                              : tile_bwd_pick<DCN4_F16, kGroupScale>(nv, sl);
+  else if (p.mode == kStdScaled)
+    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kStdScaled>(nv, sl)
+       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kStdScaled>(nv, sl)
+                              : tile_bwd_pick<DCN4_F16, kStdScaled>(nv, sl);
   else
-    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kStdUnitScale>(nv)
-       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kStdUnitScale>(nv)
-                              : tile_bwd_pick<DCN4_F16, kStdUnitScale>(nv);
+    fn = d.dtype == DCN4_F32 ? tile_bwd_pick<DCN4_F32, kStdUnitScale>(nv, sl)
+       : d.dtype == DCN4_BF16 ? tile_bwd_pick<DCN4_BF16, kStdUnitScale>(nv, sl)
+                              : tile_bwd_pick<DCN4_F16, kStdUnitScale>(nv, sl);
   TileArgs a{};
   fill_tile_args(p, a);
+  a.scales = scales;
+  BwdTileArgs b{};
+  // a workgroup takes every slice of its group in turn: chunks are groups
+  b.nslices = ts.slices;
+  a.slices = 1;
+  a.div_slices = make_fastdiv(1u);
+  a.chunks = d.group / ts.gb;
+  a.div_chunks = make_fastdiv((uint32_t)a.chunks);
   const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
   const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
   const uint64_t gom_img = (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K;
+  const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;  // pixel scales per image
   const int64_t per_image = (int64_t)a.tiles_x * a.tiles_y * a.chunks;
   const int32_t imgs = (int32_t)((int64_t(1) << 30) / per_image);
-  BwdTileArgs b{};
   for (int32_t n0 = 0; n0 < d.N; n0 += imgs) {
     const int32_t nb = (d.N - n0) < imgs ? (d.N - n0) : imgs;
     a.x = static_cast<const char*>(x) + n0 * x_img;
     a.om = static_cast<const char*>(om) + n0 * om_img;
+    a.pscales = pscales ? pscales + n0 * ps_img : nullptr;
     a.nblocks = (int32_t)(nb * per_image);
     b.gy = static_cast<const char*>(gy) + n0 * y_img;
     b.gom = gom + n0 * gom_img;
@@ -2482,7 +2545,7 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
   }
   if (!gom && !gx) return DCN4_OK;
   if (!gx && vector_path && p.kernel_choice != kKernelDirect && tiled_backward_lds(p) > 0)
-    return launch_tiled_backward(p, x, om, gy, gom, st);
+    return launch_tiled_backward(p, x, om, scales, pscales, gy, gom, st);
   const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
   // grad_offset_mask alone on whole 16-byte vectors: the vector kernel, its
   // rows collected in LDS

@@ -171,6 +171,12 @@ TILED_BWD = [
     (Shape(1, 27, 23, 64, 4, sh=2, sw=2), "bf16", {}, (0, 1, 4)),  # stride 2
     (Shape(1, 20, 24, 64, 4, offset_scale=0.5), "f16", {}, (0, 1, 4)),
     (Shape(1, 22, 26, 128, 8), "bf16", {"tile_groups": 2}, (0, 1, 4)),
+    (Shape(1, 18, 18, 32, 2, multiscale=True), "bf16", {}, (0, 1, 4)),  # group scales
+    (Shape(1, 18, 20, 32, 2, multiscale=True, pixel_scales=True, max_scale=2.5), "f16", {},
+     (0, 4)),                                                     # predicted scales, Smax
+    (Shape(1, 13, 15, 144, 2, multiscale=True), "bf16", {}, (0, 1, 4)),  # D=72: 3 slices
+    (Shape(2, 12, 14, 144, 2), "bf16", {}, (1, 4)),               # slices, standard geometry
+    (Shape(1, 20, 24, 64, 4), "bf16", {}, (16,)),             # margin 16: 2 slices of 8
 ]
 TILED_BWD_CASES = [(c, m) for c, (_, _, _, ms) in enumerate(TILED_BWD) for m in ms]
 
