@@ -1387,7 +1387,8 @@ struct GatherArgs {
   u32x4* recs;         // [rows][cap][W+1] {p within its image, m, lh, lw} as bits
   uint32_t cap;
   uint32_t samples;    // samples of this chunk, < 2^31
-  int32_t K, lg_shift, nchunk;  // nchunk: vectors of V channels per group
+  int32_t K, nchunk;  // nchunk: vectors of V channels per group
+  int32_t Lg;         // gather: lanes per bucket column, min(nchunk, 16)
   int32_t nblocks;     // gather workgroups
   int32_t strips, bands;        // gather: column strips and row bands per (n, g)
   int32_t band_groups;          // gather workgroups per strip: kGatherWaves bands each
@@ -1567,8 +1568,11 @@ __device__ __forceinline__ int floor_div(int a, int b) {
 }
 
 // A wave owns (image n, group g, band of pixel rows [y_lo, y_hi), strip of
-// Lc = 64 >> lg_shift bucket columns [cx0, cx0 + Lc)); lane (lc, li) takes
-// bucket column cx0 + lc and the group's channel vectors li, li + Lg, ...
+// Lc = floor(64 / Lg) bucket columns [cx0, cx0 + Lc)); lane (lc, li) =
+// (lane / Lg, lane % Lg) takes bucket column cx0 + lc and the group's
+// channel vectors li, li + Lg, ...  Lg is the group's vector count (at most
+// 16), not rounded to a power of two, so a group of 9 vectors keeps 63 of
+// the 64 lanes busy; lanes past the last column only idle.
 // It walks bucket rows cy = y_lo .. y_hi; each bucket's records are read once
 // and summed into four partial sums, one per corner of the cell:
 //   S_r[c] = sum over the bucket's records of fl(m*w_r) * dL/dy[p, c].
@@ -1602,9 +1606,9 @@ __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
   const uint32_t g = q2 - n * (uint32_t)a.G;
   const int lane = (int)(threadIdx.x & 63);
   const int wave = (int)(threadIdx.x >> 6);
-  const int Lg = 1 << ga.lg_shift;
-  const int lc = lane >> ga.lg_shift, li = lane & (Lg - 1);
-  const int Lc = 64 >> ga.lg_shift;
+  const int Lg = ga.Lg;
+  const int lc = lane / Lg, li = lane - lc * Lg;
+  const int Lc = 64 / Lg;
   const int cx0 = (int)strip * (Lc - 1);
   const int wy_lo = (int)bgrp * (kGatherWaves * ga.band_rows);
   const typename io::raw* gyn = reinterpret_cast<const typename io::raw*>(ga.gy) +
@@ -1632,7 +1636,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
   const int band = (int)bgrp * kGatherWaves + wave;
   if (band >= ga.bands) return;
   const int cx = cx0 + lc;
-  const bool col_ok = cx <= a.W;
+  const bool col_ok = lc < Lc && cx <= a.W;
   const int y_lo = band * ga.band_rows;
   const int y_hi = min(y_lo + ga.band_rows, a.H);
   const uint64_t row = (uint32_t)(a.W + 1);
@@ -1640,9 +1644,9 @@ __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
   const uint64_t kb = rk0 * row + (uint32_t)(col_ok ? cx : 0);
   float* gxn = ga.gx + (uint64_t)n * (uint32_t)(a.H * a.W) * (uint32_t)a.C + g * (uint32_t)a.D;
   const uint32_t xmask = (1u << ga.xs) - 1u;
-  const int rounds = (ga.nchunk + Lg - 1) >> ga.lg_shift;
+  const int rounds = (ga.nchunk + Lg - 1) / Lg;
   for (int rd = 0; rd < rounds; ++rd) {
-    const int jc = li + (rd << ga.lg_shift);
+    const int jc = li + rd * Lg;
     const bool ch_ok = jc < ga.nchunk;
     const bool live = col_ok && ch_ok;
     float p10[V], p11[V];
@@ -2268,13 +2272,11 @@ constexpr uint64_t kGatherChunkBytes = uint64_t(2) << 30;  // workspace per laun
 
 uint64_t round256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 
-// log2 of the lanes per (bucket column, group): enough for the group's
-// vectors, at most 16 so that a wave spans at least 4 columns
-int gather_lg(int D, int V) {
+// Lanes per (bucket column, group): one per vector of the group, at most 16
+// so that a wave spans at least 4 columns
+int gather_lanes(int D, int V) {
   const int nchunk = D / V;
-  int lg = 0;
-  while ((1 << lg) < nchunk && lg < 4) ++lg;
-  return lg;
+  return nchunk < 16 ? nchunk : 16;
 }
 
 // Workspace of one chunk of images: [0, 256) the overflow counter; from 256
@@ -2403,7 +2405,7 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   const int V = vec ? 16 / p.es : 1;
   // grad_y window of a gather workgroup: the output pixels whose samples
   // land in its cells when the displacement is within the margin M
-  const int lg = gather_lg(p.D, V), Lc = 64 >> lg;
+  const int Lg = gather_lanes(p.D, V), Lc = 64 / Lg;
   const bool gsm = p.mode == kGroupScale;
   const int hy = (d.kernel_h - 1) >> 1, hx = (d.kernel_w - 1) >> 1;
   const int M = gsm ? 4 + 4 * (hy > hx ? hy : hx) : 4;
@@ -2418,7 +2420,7 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   const int OWH = span_y / d.stride_h + 2, OWW = span_x / d.stride_w + 2;
   const int64_t stage_bytes = (int64_t)OWH * OWW * p.D * p.es;
   const bool stage = vec && stage_bytes <= kGatherLdsBudget;
-  const bool short_band = stage || lg >= 3;
+  const bool short_band = stage || Lg > 4;
   gather_fn bucket, gather;
   typedef void (*overflow_fn)(GatherArgs, int32_t);
   overflow_fn ovf;
@@ -2445,7 +2447,7 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   ga.cap = sh.cap;
   ga.K = p.K;
   ga.nchunk = p.D / V;
-  ga.lg_shift = gather_lg(p.D, V);
+  ga.Lg = Lg;
   ga.div_K = make_fastdiv((uint32_t)p.K);
   ga.div_kw = make_fastdiv((uint32_t)d.kernel_w);
   ga.div_G = make_fastdiv((uint32_t)d.group);
