@@ -119,6 +119,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.tile_groups = 0;
   p.tile_pad = 0;
   p.tile_swizzle = kDefaultTileSwizzle;
+  p.tile_window = 0;
   dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic
@@ -199,6 +200,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_groups = t.gb;
     info->tile_margin = t.margin;
     info->tile_slices = t.slices;
+    info->tile_window = t.whole ? 2 : 1;
     return DCN4_OK;
   }
   info->kernel = 1;
@@ -258,6 +260,10 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     case DCN4_OPT_TILE_SWIZZLE:
       if (value < 0 || value > 6) return fail(DCN4_ERR_INVALID_ARG, "tile swizzle must be 0-6");
       q.tile_swizzle = value;
+      break;
+    case DCN4_OPT_TILE_WINDOW:
+      if (value < 0 || value > 2) return fail(DCN4_ERR_INVALID_ARG, "tile window must be 0, 1 or 2");
+      q.tile_window = value;
       break;
     case DCN4_OPT_BUCKET_CAPACITY:
       if (value < 0 || value > 1024)

@@ -80,6 +80,7 @@ struct TileArgs {
   int32_t PS;            // LDS bytes per window pixel (CB, maybe padded)
   int32_t CB;            // window bytes per pixel: GB*D*es, or DSL*es when sliced
   int32_t slices;        // channel slices per group (1: whole groups)
+  int32_t whole;         // 1: the window is the whole image plus a 1-pixel zero border
   int32_t DSL;           // channels per slice (D when not sliced)
   int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
   int32_t wrpp, wpasses; // window rows per staging pass, passes
@@ -101,6 +102,7 @@ struct TileArgs {
 struct TileShape {
   int32_t ok, dp, gb, th, tw, margin, wh, ww, ps, cb, osu, lds_bytes;
   int32_t slices;  // channel slices per group (one lane per pixel when > 1)
+  int32_t whole;   // window = the whole image plus a 1-pixel zero border
 };
 
 enum KernelChoice : int32_t { kKernelAuto = 0, kKernelDirect = 1, kKernelTiled = 2 };
@@ -115,6 +117,7 @@ struct Plan {
   int32_t images_per_launch;  // bounds the per-launch lane count below 2^31
   // options (dcn4_plan_set_option) and the tile shape they resolve to
   int32_t kernel_choice, tile_margin, tile_groups, tile_pad, tile_swizzle;
+  int32_t tile_window;   // 0 automatic, 1 tile footprint plus margin, 2 whole image
   int32_t dp_user;       // 1: channels per lane set by the caller
   int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
   TileShape tile;

@@ -506,20 +506,34 @@ struct TileLane {
 // SQ: the window is square and c is its centre, so the corner cell is inside
 // iff max(|yr|, |xr|) <= ymax; the IEEE maximum propagates NaN, and m*0 is
 // NaN exactly when m is not finite, which folds the weight test in.
+// whole: the window is the whole image plus its zero border, so a cell
+// outside it is not inside the image (the definition of `inside` in
+// locate), and its sample adds nothing: only that lane skips the point
+// (the global path adds fma(0, 0, acc) = acc there, acc never being -0);
+// a non-finite weight still sends the wave to the global path, which
+// weights a corner outside the image by an exact 0 rather than m * w.
 template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ>
 __device__ __forceinline__ bool tile_point(const TileLane& w,
                                            float by, float bx, float gy, float gx,
                                            float dy, float dx, float m, float os,
-                                           float sg, float* acc) {
+                                           float sg, float* acc, bool whole) {
   const Loc l = sample_location<MODE>(by, bx, gy, gx, dy, dx, os, sg);
   const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
   const float yr = by + fy, xr = bx + fx;  // corner (y0, x0) minus (c, c)
   uint64_t off_window;
+  bool skip = false;
   if constexpr (SQ) {
-    const float t = __builtin_elementwise_maximum(
-        __builtin_elementwise_maximum(__builtin_fabsf(yr), __builtin_fabsf(xr)),
-        __builtin_fabsf(m * 0.0f));
-    off_window = __builtin_amdgcn_ballot_w64(!(t <= w.ymax));
+    const float tc = __builtin_elementwise_maximum(__builtin_fabsf(yr), __builtin_fabsf(xr));
+    if (whole) {
+      skip = !(tc <= w.ymax);
+      off_window = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
+    } else {
+      const float t = __builtin_elementwise_maximum(tc, __builtin_fabsf(m * 0.0f));
+      off_window = __builtin_amdgcn_ballot_w64(!(t <= w.ymax));
+    }
+  } else if (whole) {
+    skip = !(yr >= -w.c) || !(yr <= w.ymax) || !(xr >= -w.c) || !(xr <= w.xmax);
+    off_window = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
   } else {
     // one scalar mask per condition; NaN fails every comparison
     off_window = __builtin_amdgcn_ballot_w64(!(yr >= -w.c)) |
@@ -529,6 +543,7 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
                  __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
   }
   if (off_window != 0) return false;
+  if (skip) return true;  // outside the image: nothing to add
   const float lh = l.ty - fy, lw = l.tx - fx;
   const float hh = 1.0f - lh, hw = 1.0f - lw;
   const float cf[4] = {m * (hh * hw), m * (hh * lw), m * (lh * hw), m * (lh * lw)};
@@ -569,8 +584,10 @@ __device__ __forceinline__ TileOrigin tile_origin(const TileArgs& a) {
   const uint32_t ty = q2 - o.n * (uint32_t)a.tiles_y;
   o.ty0 = (int)ty * a.TH;
   o.tx0 = (int)tx * a.TW;
-  o.wy0 = o.ty0 * a.sh - a.ph - a.M;
-  o.wx0 = o.tx0 * a.sw - a.pw - a.M;
+  // the window: the tile's footprint plus the margin, or the whole image and
+  // its zero border
+  o.wy0 = a.whole ? -1 : o.ty0 * a.sh - a.ph - a.M;
+  o.wx0 = a.whole ? -1 : o.tx0 * a.sw - a.pw - a.M;
   o.g0 = gq * (uint32_t)a.GB;
   o.s = gc - gq * (uint32_t)a.slices;
   return o;
@@ -782,6 +799,7 @@ void dcn4_tile_kernel(TileArgs a) {
   for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
   constexpr bool GS = MODE == kGroupScale;
+  const bool whole = a.whole != 0;
   if (KS) {
     float bx[KS ? KS : 1];
 #pragma unroll
@@ -798,7 +816,7 @@ void dcn4_tile_kernel(TileArgs a) {
         const float m = io::dec(om[2 * K + k]);
         const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
         if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], gyy, gxx, dy, dx, m,
-                                                    a.offset_scale, c.sg, acc)) {
+                                                    a.offset_scale, c.sg, acc, whole)) {
           const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
           TapData<DT, VEC, NV> d;
           d.load_swapped(xr, tg, r16);
@@ -818,7 +836,7 @@ void dcn4_tile_kernel(TileArgs a) {
       const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
       const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
       if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, gyy, gxx, dy, dx, m,
-                                                  a.offset_scale, c.sg, acc)) {
+                                                  a.offset_scale, c.sg, acc, whole)) {
         const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
         TapData<DT, VEC, NV> d;
         d.load_swapped(xr, tg, r16);
@@ -1226,18 +1244,20 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
                                          a.offset_scale, sg);
     const float fy = __builtin_floorf(lc.ty), fx = __builtin_floorf(lc.tx);
     const float yr = lc.by + fy, xr_ = lc.bx + fx;  // corner (y0, x0), window-relative
-    const uint64_t off_window =
-        __builtin_amdgcn_ballot_w64(active && !(yr >= 0.0f)) |
-        __builtin_amdgcn_ballot_w64(active && !(yr <= ymax)) |
-        __builtin_amdgcn_ballot_w64(active && !(xr_ >= 0.0f)) |
-        __builtin_amdgcn_ballot_w64(active && !(xr_ <= xmax));
+    // whole-image window: a cell outside it is not inside the image, its
+    // sample has zero gradient, and the lane reads window cell (0, 0)
+    // instead; otherwise a cell outside the window sends the wave global
+    const bool out = !(yr >= 0.0f) || !(yr <= ymax) || !(xr_ >= 0.0f) || !(xr_ <= xmax);
+    const uint64_t off_window = a.whole ? 0 : __builtin_amdgcn_ballot_w64(active && out);
     float lh = 0.0f, lw = 0.0f;
     bool inside = true;
     u32x4 vv[4][NV];
     if (off_window == 0) {
       lh = lc.ty - fy;
       lw = lc.tx - fx;
-      const uint32_t a00 = (uint32_t)__builtin_fmaf(yr, row_f, __builtin_fmaf(xr_, ps_f, lane_f));
+      if (out) inside = false;  // whole-image window only
+      const float yq = out ? 0.0f : yr, xq = out ? 0.0f : xr_;
+      const uint32_t a00 = (uint32_t)__builtin_fmaf(yq, row_f, __builtin_fmaf(xq, ps_f, lane_f));
       LdsTap<DT, VEC, NV> d;
       d.load(a00, a00 + row_lds, a00 + 16u, a00 + row_lds + 16u, (uint32_t)a.PS);
 #pragma unroll
@@ -2004,7 +2024,8 @@ namespace {
 // false when it does not fit (lanes, staging passes or LDS).
 // slices > 1: chunks of one group's dp channels (one lane per pixel, the
 // window holds the slice only); slices == 1: chunks of gb whole groups.
-bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, TileShape& t) {
+bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whole,
+                TileShape& t) {
   const dcn4_desc& d = p.desc;
   if (slices < 1 || (slices > 1 && (gb != 1 || dp * slices != p.D))) return false;
   const int32_t L = slices > 1 ? 1 : p.D / dp;
@@ -2014,8 +2035,12 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, TileShape
   int32_t tw = tp >= 16 ? 16 : tp, th = tp / tw;
   if (tp == 64) { th = 8; tw = 8; }
   const int32_t M = p.tile_margin;
-  const int32_t wh = (th - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
-  const int32_t ww = (tw - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 2;
+  // the footprint of the tile's points plus the margin (and one more for the
+  // bilinear corners), or the image with a zero row/column on every side
+  const int32_t wh = whole ? d.H + 2
+                           : (th - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
+  const int32_t ww = whole ? d.W + 2
+                           : (tw - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 2;
   const int32_t cb = slices > 1 ? dp * p.es : gb * p.D * p.es;
   if (cb % 16) return false;
   int32_t ps = cb;
@@ -2033,17 +2058,13 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, TileShape
   t.dp = dp; t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww;
   t.ps = ps; t.cb = cb; t.osu = osu; t.lds_bytes = (int32_t)lds;
   t.slices = slices;
+  t.whole = whole ? 1 : 0;
   return true;
 }
 
-}  // namespace
-
-void resolve_tile(Plan& p) {
+// The tile shape for one kind of window (see resolve_tile).
+TileShape search_tile(const Plan& p, bool whole) {
   const dcn4_desc& d = p.desc;
-  p.tile = TileShape{};
-  if (p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
-  // offset/weight rows must start on 4-byte boundaries (4-byte staging units)
-  if ((d.group * 3 * p.K * p.es) % 4) return;
   // channels per lane: the caller's choice, else the plan's default and then
   // half of it (a smaller tile per lane count keeps wide groups in LDS)
   int32_t dps[2] = {p.dp, 0};
@@ -2055,20 +2076,49 @@ void resolve_tile(Plan& p) {
   for (int32_t dp : dps) {
     if (dp <= 0) continue;
     if (p.tile_groups > 0) {
-      if ((found = tile_shape(p, dp, p.tile_groups, 1, t))) break;
+      if ((found = tile_shape(p, dp, p.tile_groups, 1, whole, t))) break;
       continue;
     }
     // fewest groups per workgroup that fit: the largest output tile
     for (int32_t gb = 1; gb <= d.group && !found; ++gb)
-      if (d.group % gb == 0) found = tile_shape(p, dp, gb, 1, t);
+      if (d.group % gb == 0) found = tile_shape(p, dp, gb, 1, whole, t);
     if (found) break;
   }
   // a group too wide for whole-group windows (its lanes do not divide the
   // workgroup, or its window does not fit): one channel slice per workgroup
   if (!found && p.tile_groups <= 1)
     for (int32_t dp : dps)
-      if (dp > 0 && p.D / dp > 1 && (found = tile_shape(p, dp, 1, p.D / dp, t))) break;
-  p.tile = t;
+      if (dp > 0 && p.D / dp > 1 && (found = tile_shape(p, dp, 1, p.D / dp, whole, t))) break;
+  if (!found) t = TileShape{};
+  return t;
+}
+
+// LDS window bytes a tile shape stages per image: window bytes times
+// workgroups per image
+double staged_bytes(const Plan& p, const TileShape& t) {
+  const double tiles = (double)((p.Ho + t.th - 1) / t.th) * ((p.Wo + t.tw - 1) / t.tw);
+  const double chunks = (double)(p.desc.group / t.gb) * t.slices;
+  return (double)t.wh * t.ww * t.ps * tiles * chunks;
+}
+
+}  // namespace
+
+void resolve_tile(Plan& p) {
+  const dcn4_desc& d = p.desc;
+  p.tile = TileShape{};
+  if (p.dp <= 0 || p.kernel_choice == kKernelDirect) return;
+  // offset/weight rows must start on 4-byte boundaries (4-byte staging units)
+  if ((d.group * 3 * p.K * p.es) % 4) return;
+  // The window: the tile's footprint plus the margin (points whose corners
+  // leave it take the global path), or the whole image plus a zero border
+  // (no point ever leaves it).  Automatic: the whole image when its window
+  // fits and stages at most 1.25 times the bytes of the margin window.
+  const TileShape tm = p.tile_window == 2 ? TileShape{} : search_tile(p, false);
+  const TileShape tw = p.tile_window == 1 ? TileShape{} : search_tile(p, true);
+  if (p.tile_window == 1) p.tile = tm;
+  else if (p.tile_window == 2) p.tile = tw;
+  else if (tw.ok && (!tm.ok || staged_bytes(p, tw) <= 1.25 * staged_bytes(p, tm))) p.tile = tw;
+  else p.tile = tm;
 }
 
 void fill_tile_args(const Plan& p, TileArgs& a) {
@@ -2086,6 +2136,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.max_scale = d.use_group_scales ? d.max_scale : 0.0f;
   a.swz_shift = p.tile_swizzle > 0 ? p.tile_swizzle - 1 : -1;
   a.GB = ts.gb; a.TH = ts.th; a.TW = ts.tw; a.M = ts.margin;
+  a.whole = ts.whole;
   a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb;
   a.cpr = ts.ww * (ts.ps / 16);
   a.wrpp = kBlock / a.cpr;

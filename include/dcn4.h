@@ -157,6 +157,9 @@ typedef struct {
                                 > 1: one slice of channels_per_lane
                                 channels of one group, one lane per pixel) */
   int32_t bucket_capacity;   /* gathered grad_x: records per bucket          */
+  int32_t tile_window;       /* tiled kernel's LDS window: 1 the tile's
+                                footprint plus the margin, 2 the whole image
+                                plus a one-pixel zero border (0: no tile)   */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -184,7 +187,13 @@ typedef enum {
    * samples beyond it are added by the overflow kernel's atomics; 0 =
    * automatic (the mean bucket load plus four Poisson standard deviations
    * plus 8).  Changes the workspace size. */
-  DCN4_OPT_BUCKET_CAPACITY = 6
+  DCN4_OPT_BUCKET_CAPACITY = 6,
+  /* tiled kernels' LDS window: 1 = the tile's footprint plus the margin (a
+   * wave with a point whose corners leave it gathers that point from global
+   * memory), 2 = the whole image plus a one-pixel zero border (no point
+   * leaves it; only where it fits LDS), 0 = automatic (the whole image when
+   * it fits and stages at most 1.25 times the bytes of the margin window) */
+  DCN4_OPT_TILE_WINDOW = 7
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,

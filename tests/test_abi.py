@@ -147,13 +147,16 @@ def test_headline_plan_shape():
 
 
 def test_plan_options():
-    p = d4.Plan(desc_of(Shape(2, 20, 24, 64, 4), "bf16"))
-    assert p.info()["kernel"] == 2
+    # the margin window throughout (a 20x24 image's whole-image window would
+    # otherwise win at the wider margins)
+    p = d4.Plan(desc_of(Shape(2, 20, 24, 64, 4), "bf16"), tile_window=1)
+    assert p.info()["kernel"] == 2 and p.info()["tile_window"] == 1
     for m in (0, 3, 5):
         p.set_option("tile_margin", m)
         assert p.info()["tile_margin"] == m
     for bad in (("tile_margin", -1), ("tile_margin", 17), ("tile_groups", 3),
-                ("kernel", 3), ("tile_pad", 2), ("tile_swizzle", -1), ("tile_swizzle", 7)):
+                ("kernel", 3), ("tile_pad", 2), ("tile_swizzle", -1), ("tile_swizzle", 7),
+                ("tile_window", 3), ("tile_window", -1)):
         with pytest.raises(d4.DCN4Error) as e:
             p.set_option(*bad)
         assert e.value.status == d4.DCN4_ERR_INVALID_ARG

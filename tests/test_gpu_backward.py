@@ -177,6 +177,13 @@ TILED_BWD = [
     (Shape(1, 13, 15, 144, 2, multiscale=True), "bf16", {}, (0, 1, 4)),  # D=72: 3 slices
     (Shape(2, 12, 14, 144, 2), "bf16", {}, (1, 4)),               # slices, standard geometry
     (Shape(1, 20, 24, 64, 4), "bf16", {}, (16,)),             # margin 16: 2 slices of 8
+    # the whole-image window (samples off the image read window cell (0, 0)
+    # and are zeroed)
+    (Shape(2, 21, 27, 32, 2), "bf16", {"tile_window": 2}, (4,)),
+    (Shape(2, 17, 22, 32, 2), "f32", {"tile_window": 2}, (4,)),
+    (Shape(1, 18, 18, 32, 2, multiscale=True, pixel_scales=True, max_scale=2.5), "bf16",
+     {"tile_window": 2}, (4,)),
+    (Shape(1, 13, 15, 144, 2, multiscale=True), "bf16", {"tile_window": 2}, (4,)),
 ]
 TILED_BWD_CASES = [(c, m) for c, (_, _, _, ms) in enumerate(TILED_BWD) for m in ms]
 
@@ -192,6 +199,7 @@ def test_tiled_backward(case, margin):
     inp, gy = bwd_inputs(s, dt, seed=500 + case)
     dp = opts.get("channels_per_lane", 0)
     rest = {k: v for k, v in opts.items() if k != "channels_per_lane"}
+    rest.setdefault("tile_window", 1)  # the margin window unless the case asks otherwise
     plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, tile_margin=margin, **rest)
     info = plan.info()
     say(f"tiled backward {case} margin {margin}: {s} {dt} {info}")

@@ -308,7 +308,7 @@ def test_tiled_kernel_margins(dt, margin):
     inp = make_inputs(w, Ho, Wo)
     # fp32 lanes own 8 channels here so that the window fits in LDS
     plan = d4.Plan(desc_of(s, dt), channels_per_lane=8 if dt == "f32" else 0,
-                   kernel=2, tile_margin=margin)
+                   kernel=2, tile_margin=margin, tile_window=1)
     say(f"tiled margin {margin} {dt}: {plan.info()}")
     y = gpu_forward(plan, inp, dt)
     check_against_oracle(y, o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS),
@@ -346,7 +346,8 @@ def test_tiled_group_scale(dt, D, dp, k, st, pix, smax, margin):
         ps.reshape(-1)[-2] = 0.0
         inp = workloads.Inputs(inp.x, inp.om, inp.scales, ps)
     try:
-        plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin)
+        plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin,
+                       tile_window=1)
     except d4.DCN4Error as e:
         # a wide margin's window can exceed LDS; margin 0 always fits here
         assert e.status == d4.DCN4_ERR_UNSUPPORTED and margin > 0
@@ -371,7 +372,8 @@ def test_tiled_channel_slices_standard_mode(dt, D, dp, margin):
     o = oracle.get()
     Ho, Wo = o.out_size(s)
     inp = fuzz_inputs(s, dt, Ho, Wo, seed=7 + D + margin)
-    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin)
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin,
+                   tile_window=1)
     info = plan.info()
     say(f"sliced standard {dt} D={D} dp={dp} margin {margin}: {info}")
     assert info["kernel"] == 2 and info["tile_slices"] == D // dp
@@ -394,10 +396,94 @@ def test_tiled_kernel_vector_order(dt, D, dp, swizzle):
     y_or = o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS)
     for margin in (1, 3):
         plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_margin=margin,
-                       tile_swizzle=swizzle)
+                       tile_swizzle=swizzle, tile_window=1)
         say(f"vector order: swizzle {swizzle} margin {margin} {dt} D={D}: {plan.info()}")
         check_against_oracle(gpu_forward(plan, inp, dt), y_or, dt,
                              f"swizzle {swizzle} margin {margin}")
+
+
+# (shape, dtype, channels per lane): square images (the centred window test)
+# and others, dilation, stride, 5x5 (the generic point loop), offset_scale,
+# group scales with predicted scales and Smax, 72-channel groups in slices
+WHOLE = [(Shape(2, 24, 24, 64, 2, dh=2, dw=2, ph=2, pw=2), "f16", 16),
+         (Shape(2, 19, 27, 32, 2), "bf16", 0),
+         (Shape(1, 21, 21, 32, 2), "f32", 8),
+         (Shape(2, 20, 20, 32, 2, multiscale=True), "bf16", 0),
+         (Shape(1, 17, 23, 32, 2, multiscale=True, pixel_scales=True, max_scale=2.5), "f16", 0),
+         (Shape(1, 16, 16, 144, 2, multiscale=True), "bf16", 24),
+         (Shape(2, 25, 18, 64, 4, sh=2, sw=2), "bf16", 0),
+         (Shape(1, 22, 22, 32, 2, 5, 5, ph=2, pw=2), "bf16", 0),
+         (Shape(1, 20, 20, 64, 2, offset_scale=0.5), "f16", 0)]
+
+
+def wide_offset_inputs(s, dt, Ho, Wo, seed, reach=8.0):
+    """x ~ N(0,1), offsets U[-reach, reach] (many samples leave the image),
+    weights N(0, 1/9); group priors U[0.5, 3]; predicted scales U[0.25, 2]."""
+    rng = np.random.default_rng(seed)
+    K = s.K
+    x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
+    off = rng.uniform(-reach, reach, (s.N, Ho, Wo, s.G, 2 * K)).astype(np.float32)
+    m = (rng.standard_normal((s.N, Ho, Wo, s.G, K)) / 3).astype(np.float32)
+    om = np.concatenate([off, m], -1)
+    scales = rng.uniform(0.5, 3.0, s.G).astype(np.float32) if s.multiscale else None
+    ps = (rng.uniform(0.25, 2.0, (s.N, Ho, Wo, s.G)).astype(np.float32)
+          if s.pixel_scales else None)
+    return workloads.Inputs(workloads.to_raw(x, dt), workloads.to_raw(om, dt), scales, ps)
+
+
+@pytest.mark.parametrize("case", range(len(WHOLE)))
+def test_tiled_whole_image_window(case):
+    """The whole-image window (the image plus a zero border in LDS): a
+    sample whose cell leaves it is outside the image and adds nothing, so
+    no wave takes the global path for it.  Offsets up to 8 pixels send many
+    samples off the image; bit for bit with the oracle and with the margin
+    window."""
+    s, dt, dp = WHOLE[case]
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = wide_offset_inputs(s, dt, Ho, Wo, seed=40 + case)
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_window=2)
+    info = plan.info()
+    say(f"whole-image window {case}: {s} {dt} {info}")
+    assert info["kernel"] == 2 and info["tile_window"] == 2
+    y = gpu_forward(plan, inp, dt)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS,
+                         pscales=inp.pscales)
+    check_against_oracle(y, y_or, dt, f"whole-image window {case}")
+    margin = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_window=1,
+                     tile_margin=2)
+    assert margin.info()["tile_window"] == 1
+    assert np.array_equal(bits_equal(gpu_forward(margin, inp, dt), y, dt),
+                          np.ones(y.shape, bool))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_whole_image_window_nonfinite(dt):
+    """Non-finite inputs under the whole-image window: an infinite or NaN
+    weight still sends its wave to the global path (which weights corners
+    outside the image by an exact zero), a NaN or infinite offset puts its
+    sample outside the image, a NaN or infinite input value reaches the
+    outputs that sample it."""
+    s = Shape(1, 14, 14, 32, 2)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = wide_offset_inputs(s, "f32", Ho, Wo, seed=77, reach=4.0)
+    x = from_raw(inp.x, "f32").copy()
+    om = from_raw(inp.om, "f32").copy()
+    x[0, 3, 4, :] = np.inf
+    x[0, 7, 2, 5] = np.nan
+    x[0, 0, 0, 7] = -np.inf
+    om[0, 2, 2, 0, 4] = np.nan     # an offset
+    om[0, 5, 6, 1, 20] = np.inf    # a weight
+    om[0, 9, 9, 0, 19] = np.nan    # a weight
+    om[0, 0, 0, 1, 0] = np.inf     # an offset pushing a sample outside
+    inp = workloads.Inputs(workloads.to_raw(x, dt), workloads.to_raw(om, dt), None)
+    plan = d4.Plan(desc_of(s, dt), kernel=2, tile_window=2)
+    assert plan.info()["tile_window"] == 2
+    say(f"whole-image window, non-finite values {dt}: {plan.info()}")
+    check_against_oracle(gpu_forward(plan, inp, dt),
+                         o.forward_f32(s, dt, inp.x, inp.om, None, nthreads=NTHREADS),
+                         dt, "whole-image non-finite")
 
 
 @pytest.mark.parametrize("groups, pad", [(1, 0), (2, 1), (4, 0), (4, 1)])
@@ -408,7 +494,7 @@ def test_tiled_kernel_group_chunks(groups, pad):
     Ho, Wo = o.out_size(s)
     inp = make_inputs(w, Ho, Wo)
     plan = d4.Plan(desc_of(s, "bf16"), tile_margin=3, kernel=2, tile_groups=groups,
-                   tile_pad=pad)
+                   tile_pad=pad, tile_window=1)
     say(f"tiled groups {groups} pad {pad}: {plan.info()}")
     check_against_oracle(gpu_forward(plan, inp, "bf16"),
                          o.forward_f32(s, "bf16", inp.x, inp.om, None, nthreads=NTHREADS),
