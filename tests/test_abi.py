@@ -198,6 +198,27 @@ def test_plan_options():
     assert big.info()["tile_margin"] == 4
 
 
+def test_tile_window_choice():
+    """The whole-image window where it fits and stages at most 1.25x the
+    margin window's bytes: the 32x32 wide block (two 16-channel slices of its
+    32-channel groups, 16x16 tiles); the 128x128 U-Net block keeps the margin
+    window, and forcing the whole image there leaves no tile."""
+    wide = d4.Plan(desc_of(Shape(16, 32, 32, 1280, 40, dh=2, dw=2, ph=2, pw=2), "f16"))
+    i = wide.info()
+    assert i["kernel"] == 2 and i["tile_window"] == 2
+    assert i["tile_slices"] == 2 and (i["tile_h"], i["tile_w"]) == (16, 16)
+    assert i["blocks"] == 16 * 4 * 40 * 2   # images x tiles x groups x slices
+    wide.set_option("tile_window", 1)
+    assert wide.info()["tile_window"] == 1 and wide.info()["tile_slices"] == 1
+    unet = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
+    assert unet.info()["tile_window"] == 1
+    unet.set_option("tile_window", 2)
+    assert unet.info()["kernel"] == 1 and unet.info()["tile_window"] == 0
+    with pytest.raises(d4.DCN4Error) as e:
+        unet.set_option("kernel", 2)
+    assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
+
+
 def test_channels_per_lane_override():
     p = d4.Plan(desc_of(Shape(2, 8, 8, 64, 2), "bf16"))   # D = 32
     for dp in (8, 16, 32):
