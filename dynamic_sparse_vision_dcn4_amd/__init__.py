@@ -71,7 +71,8 @@ class dcn4_launch_info(ctypes.Structure):
                 ("backward_lds_bytes", ctypes.c_int32),
                 ("tile_slices", ctypes.c_int32),
                 ("bucket_capacity", ctypes.c_int32),
-                ("tile_window", ctypes.c_int32)]
+                ("tile_window", ctypes.c_int32),
+                ("tile_passes", ctypes.c_int32)]
 
 # dcn4_option
 DCN4_OPT_CHANNELS_PER_LANE = 0
@@ -82,10 +83,12 @@ DCN4_OPT_TILE_PAD = 4
 DCN4_OPT_TILE_SWIZZLE = 5
 DCN4_OPT_BUCKET_CAPACITY = 6
 DCN4_OPT_TILE_WINDOW = 7
+DCN4_OPT_TILE_PASSES = 8
 OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
            "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
            "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE,
-           "bucket_capacity": DCN4_OPT_BUCKET_CAPACITY, "tile_window": DCN4_OPT_TILE_WINDOW}
+           "bucket_capacity": DCN4_OPT_BUCKET_CAPACITY, "tile_window": DCN4_OPT_TILE_WINDOW,
+           "tile_passes": DCN4_OPT_TILE_PASSES}
 
 
 _P = ctypes.c_void_p
@@ -306,7 +309,7 @@ class Plan:
 
     def __init__(self, desc: Desc, channels_per_lane: int = 0, **options):
         """options: kernel, tile_margin, tile_groups, tile_pad, tile_swizzle,
-        tile_window, bucket_capacity (dcn4_option).  The kernel choice is applied last, so a forced tiled
+        tile_window, tile_passes, bucket_capacity (dcn4_option).  The kernel choice is applied last, so a forced tiled
         kernel is checked against the tile options given with it."""
         self.desc = desc
         st, h = dcn4_create(desc.c_struct())

@@ -120,6 +120,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.tile_pad = 0;
   p.tile_swizzle = kDefaultTileSwizzle;
   p.tile_window = 0;
+  p.tile_passes = 0;
   dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic
@@ -187,7 +188,8 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     const dcn4::TileShape& t = p.tile;
     info->channels_per_lane = t.dp;
     info->lanes_per_group = p.D / t.dp;
-    const int64_t tiles = int64_t((p.Ho + t.th - 1) / t.th) * ((p.Wo + t.tw - 1) / t.tw);
+    const int64_t rows = t.th * (t.passes > 0 ? t.passes : 1);  // output rows per workgroup
+    const int64_t tiles = int64_t((p.Ho + rows - 1) / rows) * ((p.Wo + t.tw - 1) / t.tw);
     const int64_t per_image = tiles * (p.desc.group / t.gb) * t.slices;
     const int64_t imgs = (int64_t(1) << 30) / per_image;
     info->kernel = 2;
@@ -201,6 +203,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_margin = t.margin;
     info->tile_slices = t.slices;
     info->tile_window = t.whole ? 2 : 1;
+    info->tile_passes = t.passes;
     return DCN4_OK;
   }
   info->kernel = 1;
@@ -264,6 +267,10 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     case DCN4_OPT_TILE_WINDOW:
       if (value < 0 || value > 2) return fail(DCN4_ERR_INVALID_ARG, "tile window must be 0, 1 or 2");
       q.tile_window = value;
+      break;
+    case DCN4_OPT_TILE_PASSES:
+      if (value < 0 || value > 64) return fail(DCN4_ERR_INVALID_ARG, "tile passes must be 0-64");
+      q.tile_passes = value;
       break;
     case DCN4_OPT_BUCKET_CAPACITY:
       if (value < 0 || value > 1024)

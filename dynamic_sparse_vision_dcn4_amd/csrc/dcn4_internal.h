@@ -81,6 +81,7 @@ struct TileArgs {
   int32_t CB;            // window bytes per pixel: GB*D*es, or DSL*es when sliced
   int32_t slices;        // channel slices per group (1: whole groups)
   int32_t whole;         // 1: the window is the whole image plus a 1-pixel zero border
+  int32_t passes;        // tile rows per workgroup under one window staging (whole image)
   int32_t DSL;           // channels per slice (D when not sliced)
   int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
   int32_t wrpp, wpasses; // window rows per staging pass, passes
@@ -103,6 +104,7 @@ struct TileShape {
   int32_t ok, dp, gb, th, tw, margin, wh, ww, ps, cb, osu, lds_bytes;
   int32_t slices;  // channel slices per group (one lane per pixel when > 1)
   int32_t whole;   // window = the whole image plus a 1-pixel zero border
+  int32_t passes;  // forward: tile rows a workgroup takes under one staging
 };
 
 enum KernelChoice : int32_t { kKernelAuto = 0, kKernelDirect = 1, kKernelTiled = 2 };
@@ -118,6 +120,7 @@ struct Plan {
   // options (dcn4_plan_set_option) and the tile shape they resolve to
   int32_t kernel_choice, tile_margin, tile_groups, tile_pad, tile_swizzle;
   int32_t tile_window;   // 0 automatic, 1 tile footprint plus margin, 2 whole image
+  int32_t tile_passes;   // whole-image window: tile rows per workgroup (0: automatic)
   int32_t dp_user;       // 1: channels per lane set by the caller
   int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
   TileShape tile;

@@ -582,7 +582,7 @@ __device__ __forceinline__ TileOrigin tile_origin(const TileArgs& a) {
   TileOrigin o;
   o.n = fastdiv(q2, a.div_ty);
   const uint32_t ty = q2 - o.n * (uint32_t)a.tiles_y;
-  o.ty0 = (int)ty * a.TH;
+  o.ty0 = (int)ty * a.TH * a.passes;
   o.tx0 = (int)tx * a.TW;
   // the window: the tile's footprint plus the margin, or the whole image and
   // its zero border
@@ -733,7 +733,7 @@ void dcn4_tile_kernel(TileArgs a) {
 
   const TileOrigin org = tile_origin(a);
   const uint32_t n = org.n, g0 = org.g0;
-  const int ty0 = org.ty0, tx0 = org.tx0, wy0 = org.wy0, wx0 = org.wx0;
+  const int tx0 = org.tx0, wy0 = org.wy0, wx0 = org.wx0;
   const int K = KS ? KS * KS : a.kh * a.kw;
   const uint32_t t = threadIdx.x, lane = t & 63u;
   const uint32_t pix_bytes = (uint32_t)(a.C * es);
@@ -742,80 +742,103 @@ void dcn4_tile_kernel(TileArgs a) {
   const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   __syncthreads();
 
-  // ---- lane -> (tile pixel, group in chunk, channel slice)
-  const uint32_t tp = fastdiv(t, a.div_gbl);
-  const uint32_t rr = t - tp * (uint32_t)(a.GB * a.L);
-  const uint32_t gl = fastdiv(rr, a.div_L), l = rr - gl * (uint32_t)a.L;
-  const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
-  const int yo = ty0 + (int)py, xo = tx0 + (int)px;
-  if (yo >= a.Ho || xo >= a.Wo) return;
-  const uint32_t g = g0 + gl;
-  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
-      lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
-  // first channel of the lane within the pixel: its group, slice and lane
-  const uint32_t chan = g * (uint32_t)a.D + org.s * (uint32_t)a.DSL + l * DP;
+  // One tile row of outputs from the staged window and offset/weight rows;
+  // a lane outside the output returns from it.
+  auto tile_rows = [&](const int ty0) {
+    // ---- lane -> (tile pixel, group in chunk, channel slice)
+    const uint32_t tp = fastdiv(t, a.div_gbl);
+    const uint32_t rr = t - tp * (uint32_t)(a.GB * a.L);
+    const uint32_t gl = fastdiv(rr, a.div_L), l = rr - gl * (uint32_t)a.L;
+    const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
+    const int yo = ty0 + (int)py, xo = tx0 + (int)px;
+    if (yo >= a.Ho || xo >= a.Wo) return;
+    const uint32_t g = g0 + gl;
+    const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
+        lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
+    // first channel of the lane within the pixel: its group, slice and lane
+    const uint32_t chan = g * (uint32_t)a.D + org.s * (uint32_t)a.DSL + l * DP;
 
-  FwdArgs fa{};  // the geometry reads only the fields FwdArgs and TileArgs share
-  fa.H = a.H; fa.W = a.W; fa.G = a.G; fa.kh = a.kh; fa.kw = a.kw; fa.dh = a.dh; fa.dw = a.dw;
-  fa.offset_scale = a.offset_scale; fa.Hm1 = a.Hm1; fa.Wm1 = a.Wm1;
-  fa.scales = a.scales; fa.pscales = a.pscales; fa.max_scale = a.max_scale;
-  // global-path context (points whose corners leave the window)
-  LaneCtx c;
-  c.pix_bytes = pix_bytes;
-  c.row_stride = (uint32_t)a.W * pix_bytes;
-  c.lane_bytes = chan * es;
-  c.hy = ((KS ? KS : a.kh) - 1) >> 1;
-  c.hx = ((KS ? KS : a.kw) - 1) >> 1;
-  // group-scale mode: the lane's scale (pixel counted from the launch's first
-  // image) and the point base at the centre
-  c.sg = (MODE == kGroupScale)
-             ? group_scale(fa, ((uint64_t)n * a.Ho + (uint32_t)yo) * a.Wo + (uint32_t)xo, g)
-             : 1.0f;
-  c.by0 = yo * a.sh - a.ph + (MODE == kGroupScale ? c.hy : 0);
-  c.bx0 = xo * a.sw - a.pw + (MODE == kGroupScale ? c.hx : 0);
+    FwdArgs fa{};  // the geometry reads only the fields FwdArgs and TileArgs share
+    fa.H = a.H; fa.W = a.W; fa.G = a.G; fa.kh = a.kh; fa.kw = a.kw; fa.dh = a.dh; fa.dw = a.dw;
+    fa.offset_scale = a.offset_scale; fa.Hm1 = a.Hm1; fa.Wm1 = a.Wm1;
+    fa.scales = a.scales; fa.pscales = a.pscales; fa.max_scale = a.max_scale;
+    // global-path context (points whose corners leave the window)
+    LaneCtx c;
+    c.pix_bytes = pix_bytes;
+    c.row_stride = (uint32_t)a.W * pix_bytes;
+    c.lane_bytes = chan * es;
+    c.hy = ((KS ? KS : a.kh) - 1) >> 1;
+    c.hx = ((KS ? KS : a.kw) - 1) >> 1;
+    // group-scale mode: the lane's scale (pixel counted from the launch's first
+    // image) and the point base at the centre
+    c.sg = (MODE == kGroupScale)
+               ? group_scale(fa, ((uint64_t)n * a.Ho + (uint32_t)yo) * a.Wo + (uint32_t)xo, g)
+               : 1.0f;
+    c.by0 = yo * a.sh - a.ph + (MODE == kGroupScale ? c.hy : 0);
+    c.bx0 = xo * a.sw - a.pw + (MODE == kGroupScale ? c.hx : 0);
 
-  TileLane w;
-  w.row_lds = (uint32_t)(a.WW * a.PS);
-  w.ps = (uint32_t)a.PS;
-  w.row_f = (float)w.row_lds;
-  w.ps_f = (float)a.PS;
-  // the window starts at the LDS allocation's base address
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  const uint32_t r16 = (NV % 2 == 0 && a.swz_shift >= 0) ? ((lane >> a.swz_shift) & 1u) * 16u : 0u;
-  w.lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es + r16);
-  w.odd = 16u - 2u * r16;
-  // cell coordinates relative to (cw, cw): the centre of a square window
-  constexpr bool SQ = PSC != 0;
-  const float cw = SQ ? 0.5f * (float)(a.WH - 2) : 0.0f;
-  w.c = cw;
-  w.ymax = (float)(a.WH - 2) - cw;
-  w.xmax = (float)(a.WW - 2) - cw;
-  w.lane_f += cw * w.row_f + cw * w.ps_f;  // exact: small multiples of 1/2
-  // base of point (0, 0) relative to window cell (cw, cw)
-  const float ry0 = (float)(c.by0 - wy0) - cw, rx0 = (float)(c.bx0 - wx0) - cw;
+    TileLane w;
+    w.row_lds = (uint32_t)(a.WW * a.PS);
+    w.ps = (uint32_t)a.PS;
+    w.row_f = (float)w.row_lds;
+    w.ps_f = (float)a.PS;
+    // the window starts at the LDS allocation's base address
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    const uint32_t r16 = (NV % 2 == 0 && a.swz_shift >= 0) ? ((lane >> a.swz_shift) & 1u) * 16u : 0u;
+    w.lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es + r16);
+    w.odd = 16u - 2u * r16;
+    // cell coordinates relative to (cw, cw): the centre of a square window
+    constexpr bool SQ = PSC != 0;
+    const float cw = SQ ? 0.5f * (float)(a.WH - 2) : 0.0f;
+    w.c = cw;
+    w.ymax = (float)(a.WH - 2) - cw;
+    w.xmax = (float)(a.WW - 2) - cw;
+    w.lane_f += cw * w.row_f + cw * w.ps_f;  // exact: small multiples of 1/2
+    // base of point (0, 0) relative to window cell (cw, cw)
+    const float ry0 = (float)(c.by0 - wy0) - cw, rx0 = (float)(c.bx0 - wx0) - cw;
 
-  float acc[DP];
-#pragma unroll
-  for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
+    float acc[DP];
+  #pragma unroll
+    for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
-  constexpr bool GS = MODE == kGroupScale;
-  const bool whole = a.whole != 0;
-  if (KS) {
-    float bx[KS ? KS : 1];
-#pragma unroll
-    for (int j = 0; j < KS; ++j) bx[j] = GS ? rx0 : rx0 + (float)(j * a.dw);
-    const float fdh = GS ? 0.0f : (float)a.dh;
-    float by = ry0;
-#pragma unroll
-    for (int i = 0; i < KS; ++i, by += fdh) {
-#pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const int k = i * KS + j;
+    constexpr bool GS = MODE == kGroupScale;
+    const bool whole = a.whole != 0;
+    if (KS) {
+      float bx[KS ? KS : 1];
+  #pragma unroll
+      for (int j = 0; j < KS; ++j) bx[j] = GS ? rx0 : rx0 + (float)(j * a.dw);
+      const float fdh = GS ? 0.0f : (float)a.dh;
+      float by = ry0;
+  #pragma unroll
+      for (int i = 0; i < KS; ++i, by += fdh) {
+  #pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          const int k = i * KS + j;
+          const float dx = io::dec(om[2 * k]);
+          const float dy = io::dec(om[2 * k + 1]);
+          const float m = io::dec(om[2 * K + k]);
+          const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
+          if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], gyy, gxx, dy, dx, m,
+                                                      a.offset_scale, c.sg, acc, whole)) {
+            const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
+            TapData<DT, VEC, NV> d;
+            d.load_swapped(xr, tg, r16);
+            d.accumulate(acc, tg);
+          }
+        }
+      }
+    } else {
+      const int kw = a.kw;
+  #pragma unroll 1
+      for (int k = 0; k < K; ++k) {
+        const int i = k / kw, j = k - (k / kw) * kw;
         const float dx = io::dec(om[2 * k]);
         const float dy = io::dec(om[2 * k + 1]);
         const float m = io::dec(om[2 * K + k]);
+        const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
+        const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
         const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], gyy, gxx, dy, dx, m,
+        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, gyy, gxx, dy, dx, m,
                                                     a.offset_scale, c.sg, acc, whole)) {
           const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
           TapData<DT, VEC, NV> d;
@@ -824,43 +847,35 @@ void dcn4_tile_kernel(TileArgs a) {
         }
       }
     }
-  } else {
-    const int kw = a.kw;
-#pragma unroll 1
-    for (int k = 0; k < K; ++k) {
-      const int i = k / kw, j = k - (k / kw) * kw;
-      const float dx = io::dec(om[2 * k]);
-      const float dy = io::dec(om[2 * k + 1]);
-      const float m = io::dec(om[2 * K + k]);
-      const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
-      const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
-      const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-      if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, gyy, gxx, dy, dx, m,
-                                                  a.offset_scale, c.sg, acc, whole)) {
-        const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
-        TapData<DT, VEC, NV> d;
-        d.load_swapped(xr, tg, r16);
-        d.accumulate(acc, tg);
-      }
-    }
-  }
 
-#pragma unroll
-  for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
-  char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * pix_bytes + chan * es;
-  char* ype = yp + r16;           // even slots
-  char* ypo = yp + (16u - r16);   // odd slots
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    u32x4 o;
-    if constexpr (es == 4) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(acc[v * VEC + e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = io::enc2(acc[v * VEC + 2 * e], acc[v * VEC + 2 * e + 1]);
+  #pragma unroll
+    for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
+    char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * pix_bytes + chan * es;
+    char* ype = yp + r16;           // even slots
+    char* ypo = yp + (16u - r16);   // odd slots
+  #pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      u32x4 o;
+      if constexpr (es == 4) {
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(acc[v * VEC + e]);
+      } else {
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = io::enc2(acc[v * VEC + 2 * e], acc[v * VEC + 2 * e + 1]);
+      }
+      *reinterpret_cast<u32x4*>(((v & 1) ? ypo : ype) + 16 * (v & ~1)) = o;
     }
-    *reinterpret_cast<u32x4*>(((v & 1) ? ypo : ype) + 16 * (v & ~1)) = o;
+  };
+  // Whole-image window: `passes` consecutive tile rows share one staging of
+  // the window; each pass restages only the offset/weight rows.
+  for (int pass = 0;;) {
+    tile_rows(org.ty0 + pass * a.TH);
+    if (++pass >= a.passes) break;
+    __syncthreads();  // every lane is done with the previous rows' offsets
+    TileOrigin op = org;
+    op.ty0 = org.ty0 + pass * a.TH;
+    stage_om<es>(a, op, K, lds + a.om_lds);
+    __syncthreads();
   }
 }
 
@@ -2059,6 +2074,18 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   t.ps = ps; t.cb = cb; t.osu = osu; t.lds_bytes = (int32_t)lds;
   t.slices = slices;
   t.whole = whole ? 1 : 0;
+  t.passes = 1;
+  if (whole) {
+    // tile rows per workgroup: as many as keep at least four workgroups per
+    // CU, so that one staging of the image serves more outputs
+    const int64_t rows = (p.Ho + th - 1) / th;
+    const int64_t cols_chunks = (int64_t)((p.Wo + tw - 1) / tw) * (d.group / gb) * slices;
+    int64_t passes = rows;
+    while (passes > 1 && (int64_t)d.N * ((rows + passes - 1) / passes) * cols_chunks < 4 * 256)
+      passes = (passes + 1) / 2;
+    if (p.tile_passes > 0) passes = p.tile_passes < rows ? p.tile_passes : rows;
+    t.passes = (int32_t)passes;
+  }
   return true;
 }
 
@@ -2096,7 +2123,8 @@ TileShape search_tile(const Plan& p, bool whole) {
 // LDS window bytes a tile shape stages per image: window bytes times
 // workgroups per image
 double staged_bytes(const Plan& p, const TileShape& t) {
-  const double tiles = (double)((p.Ho + t.th - 1) / t.th) * ((p.Wo + t.tw - 1) / t.tw);
+  const int32_t rows = t.th * (t.passes > 0 ? t.passes : 1);  // output rows per workgroup
+  const double tiles = (double)((p.Ho + rows - 1) / rows) * ((p.Wo + t.tw - 1) / t.tw);
   const double chunks = (double)(p.desc.group / t.gb) * t.slices;
   return (double)t.wh * t.ww * t.ps * tiles * chunks;
 }
@@ -2137,6 +2165,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.swz_shift = p.tile_swizzle > 0 ? p.tile_swizzle - 1 : -1;
   a.GB = ts.gb; a.TH = ts.th; a.TW = ts.tw; a.M = ts.margin;
   a.whole = ts.whole;
+  a.passes = ts.passes > 0 ? ts.passes : 1;
   a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb;
   a.cpr = ts.ww * (ts.ps / 16);
   a.wrpp = kBlock / a.cpr;
@@ -2153,7 +2182,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   }
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
-  a.tiles_y = (p.Ho + ts.th - 1) / ts.th;
+  a.tiles_y = (p.Ho + ts.th * a.passes - 1) / (ts.th * a.passes);
   a.chunks = d.group / ts.gb * ts.slices;
   a.img_bytes = (uint32_t)((uint64_t)d.H * d.W * d.C * p.es);
   a.om_row_bytes = (uint32_t)(d.group * 3 * p.K * p.es);
@@ -2274,6 +2303,10 @@ dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
   fill_tile_args(p, a);
   a.scales = scales;
   BwdTileArgs b{};
+  // one tile row per workgroup (the forward's passes are not used here)
+  a.passes = 1;
+  a.tiles_y = (p.Ho + ts.th - 1) / ts.th;
+  a.div_ty = make_fastdiv((uint32_t)a.tiles_y);
   // a workgroup takes every slice of its group in turn: chunks are groups
   b.nslices = ts.slices;
   a.slices = 1;

@@ -160,6 +160,9 @@ typedef struct {
   int32_t tile_window;       /* tiled kernel's LDS window: 1 the tile's
                                 footprint plus the margin, 2 the whole image
                                 plus a one-pixel zero border (0: no tile)   */
+  int32_t tile_passes;       /* tiled forward: tile rows a workgroup takes
+                                under one staging of its window (1 for the
+                                margin window)                               */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -193,7 +196,11 @@ typedef enum {
    * memory), 2 = the whole image plus a one-pixel zero border (no point
    * leaves it; only where it fits LDS), 0 = automatic (the whole image when
    * it fits and stages at most 1.25 times the bytes of the margin window) */
-  DCN4_OPT_TILE_WINDOW = 7
+  DCN4_OPT_TILE_WINDOW = 7,
+  /* tiled forward under the whole-image window: tile rows each workgroup
+   * computes from one staging of the image, 1-64 (at most the image's tile
+   * rows); 0 = automatic (as many as keep four workgroups per CU) */
+  DCN4_OPT_TILE_PASSES = 8
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,

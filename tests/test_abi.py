@@ -207,7 +207,15 @@ def test_tile_window_choice():
     i = wide.info()
     assert i["kernel"] == 2 and i["tile_window"] == 2
     assert i["tile_slices"] == 2 and (i["tile_h"], i["tile_w"]) == (16, 16)
-    assert i["blocks"] == 16 * 4 * 40 * 2   # images x tiles x groups x slices
+    # images x tile columns x groups x slices: a workgroup walks both tile
+    # rows of its column under one staging (four workgroups per CU remain)
+    assert i["tile_passes"] == 2 and i["blocks"] == 16 * 2 * 40 * 2
+    wide.set_option("tile_passes", 1)
+    assert wide.info()["tile_passes"] == 1 and wide.info()["blocks"] == 16 * 4 * 40 * 2
+    wide.set_option("tile_passes", 9)   # at most the image's tile rows
+    assert wide.info()["tile_passes"] == 2
+    with pytest.raises(d4.DCN4Error):
+        wide.set_option("tile_passes", 65)
     wide.set_option("tile_window", 1)
     assert wide.info()["tile_window"] == 1 and wide.info()["tile_slices"] == 1
     unet = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
