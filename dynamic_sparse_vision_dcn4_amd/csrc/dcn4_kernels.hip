@@ -512,11 +512,11 @@ struct TileLane {
 // (the global path adds fma(0, 0, acc) = acc there, acc never being -0);
 // a non-finite weight still sends the wave to the global path, which
 // weights a corner outside the image by an exact 0 rather than m * w.
-template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ>
+template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ, bool WHOLE>
 __device__ __forceinline__ bool tile_point(const TileLane& w,
                                            float by, float bx, float gy, float gx,
                                            float dy, float dx, float m, float os,
-                                           float sg, float* acc, bool whole) {
+                                           float sg, float* acc) {
   const Loc l = sample_location<MODE>(by, bx, gy, gx, dy, dx, os, sg);
   const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
   const float yr = by + fy, xr = bx + fx;  // corner (y0, x0) minus (c, c)
@@ -524,14 +524,14 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
   bool skip = false;
   if constexpr (SQ) {
     const float tc = __builtin_elementwise_maximum(__builtin_fabsf(yr), __builtin_fabsf(xr));
-    if (whole) {
+    if constexpr (WHOLE) {
       skip = !(tc <= w.ymax);
       off_window = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
     } else {
       const float t = __builtin_elementwise_maximum(tc, __builtin_fabsf(m * 0.0f));
       off_window = __builtin_amdgcn_ballot_w64(!(t <= w.ymax));
     }
-  } else if (whole) {
+  } else if constexpr (WHOLE) {
     skip = !(yr >= -w.c) || !(yr <= w.ymax) || !(xr >= -w.c) || !(xr <= w.xmax);
     off_window = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
   } else {
@@ -721,7 +721,7 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
   return mis;
 }
 
-template <int DT, int VEC, int NV, int MODE, int KS, int PSC>
+template <int DT, int VEC, int NV, int MODE, int KS, int PSC, bool WHOLE>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
 void dcn4_tile_kernel(TileArgs a) {
@@ -742,16 +742,26 @@ void dcn4_tile_kernel(TileArgs a) {
   const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   __syncthreads();
 
-  // One tile row of outputs from the staged window and offset/weight rows;
-  // a lane outside the output returns from it.
-  auto tile_rows = [&](const int ty0) {
+  // Whole-image window: `passes` consecutive tile rows share one staging of
+  // the window, each pass restaging only the offset/weight rows (one pass
+  // for the margin window).
+  const int npass = WHOLE ? a.passes : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    if (WHOLE && pass > 0) {
+      __syncthreads();  // every lane is done with the previous rows' offsets
+      TileOrigin op = org;
+      op.ty0 = org.ty0 + pass * a.TH;
+      stage_om<es>(a, op, K, lds + a.om_lds);
+      __syncthreads();
+    }
+    const int ty0 = org.ty0 + pass * a.TH;
     // ---- lane -> (tile pixel, group in chunk, channel slice)
     const uint32_t tp = fastdiv(t, a.div_gbl);
     const uint32_t rr = t - tp * (uint32_t)(a.GB * a.L);
     const uint32_t gl = fastdiv(rr, a.div_L), l = rr - gl * (uint32_t)a.L;
     const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
     const int yo = ty0 + (int)py, xo = tx0 + (int)px;
-    if (yo >= a.Ho || xo >= a.Wo) return;
+    if (yo >= a.Ho || xo >= a.Wo) continue;  // this pass has no output here
     const uint32_t g = g0 + gl;
     const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
         lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
@@ -798,28 +808,27 @@ void dcn4_tile_kernel(TileArgs a) {
     const float ry0 = (float)(c.by0 - wy0) - cw, rx0 = (float)(c.bx0 - wx0) - cw;
 
     float acc[DP];
-  #pragma unroll
+#pragma unroll
     for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
     constexpr bool GS = MODE == kGroupScale;
-    const bool whole = a.whole != 0;
     if (KS) {
       float bx[KS ? KS : 1];
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < KS; ++j) bx[j] = GS ? rx0 : rx0 + (float)(j * a.dw);
       const float fdh = GS ? 0.0f : (float)a.dh;
       float by = ry0;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < KS; ++i, by += fdh) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < KS; ++j) {
           const int k = i * KS + j;
           const float dx = io::dec(om[2 * k]);
           const float dy = io::dec(om[2 * k + 1]);
           const float m = io::dec(om[2 * K + k]);
           const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-          if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx[j], gyy, gxx, dy, dx, m,
-                                                      a.offset_scale, c.sg, acc, whole)) {
+          if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE>(w, by, bx[j], gyy, gxx, dy, dx,
+                                                             m, a.offset_scale, c.sg, acc)) {
             const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
             TapData<DT, VEC, NV> d;
             d.load_swapped(xr, tg, r16);
@@ -829,7 +838,7 @@ void dcn4_tile_kernel(TileArgs a) {
       }
     } else {
       const int kw = a.kw;
-  #pragma unroll 1
+#pragma unroll 1
       for (int k = 0; k < K; ++k) {
         const int i = k / kw, j = k - (k / kw) * kw;
         const float dx = io::dec(om[2 * k]);
@@ -838,8 +847,8 @@ void dcn4_tile_kernel(TileArgs a) {
         const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
         const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
         const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ>(w, by, bx, gyy, gxx, dy, dx, m,
-                                                    a.offset_scale, c.sg, acc, whole)) {
+        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE>(w, by, bx, gyy, gxx, dy, dx, m,
+                                                           a.offset_scale, c.sg, acc)) {
           const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
           TapData<DT, VEC, NV> d;
           d.load_swapped(xr, tg, r16);
@@ -848,34 +857,23 @@ void dcn4_tile_kernel(TileArgs a) {
       }
     }
 
-  #pragma unroll
+#pragma unroll
     for (int e = 0; e < DP; ++e) asm volatile("" : "+v"(acc[e]));
     char* yp = a.y + (((uint64_t)n * a.Ho + yo) * a.Wo + xo) * pix_bytes + chan * es;
     char* ype = yp + r16;           // even slots
     char* ypo = yp + (16u - r16);   // odd slots
-  #pragma unroll
+#pragma unroll
     for (int v = 0; v < NV; ++v) {
       u32x4 o;
       if constexpr (es == 4) {
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(acc[v * VEC + e]);
       } else {
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = io::enc2(acc[v * VEC + 2 * e], acc[v * VEC + 2 * e + 1]);
       }
       *reinterpret_cast<u32x4*>(((v & 1) ? ypo : ype) + 16 * (v & ~1)) = o;
     }
-  };
-  // Whole-image window: `passes` consecutive tile rows share one staging of
-  // the window; each pass restages only the offset/weight rows.
-  for (int pass = 0;;) {
-    tile_rows(org.ty0 + pass * a.TH);
-    if (++pass >= a.passes) break;
-    __syncthreads();  // every lane is done with the previous rows' offsets
-    TileOrigin op = org;
-    op.ty0 = org.ty0 + pass * a.TH;
-    stage_om<es>(a, op, K, lds + a.om_lds);
-    __syncthreads();
   }
 }
 
@@ -1930,37 +1928,44 @@ void fill_common(const Plan& p, FwdArgs& a) {
 
 typedef void (*tile_fn)(TileArgs);
 
-template <int DT, int NV, int MODE>
-tile_fn tile_ks(int K3, bool psc) {
+template <int DT, int NV, int MODE, bool WHOLE>
+tile_fn tile_kw(int K3, bool psc) {
   constexpr int V = 16 / Io<DT>::es;
-  if (!K3) return dcn4_tile_kernel<DT, V, NV, MODE, 0, 0>;
-  return psc ? dcn4_tile_kernel<DT, V, NV, MODE, 3, 16 * NV>
-             : dcn4_tile_kernel<DT, V, NV, MODE, 3, 0>;
+  if (!K3) return dcn4_tile_kernel<DT, V, NV, MODE, 0, 0, WHOLE>;
+  return psc ? dcn4_tile_kernel<DT, V, NV, MODE, 3, 16 * NV, WHOLE>
+             : dcn4_tile_kernel<DT, V, NV, MODE, 3, 0, WHOLE>;
+}
+
+// whole: the whole-image window, an instantiation of its own so that the
+// margin window's point loop carries no test of the window kind
+template <int DT, int NV, int MODE>
+tile_fn tile_ks(int K3, bool psc, bool whole) {
+  return whole ? tile_kw<DT, NV, MODE, true>(K3, psc) : tile_kw<DT, NV, MODE, false>(K3, psc);
 }
 
 template <int DT>
-tile_fn tile_pick(int nv, int mode, int K3, bool psc) {
+tile_fn tile_pick(int nv, int mode, int K3, bool psc, bool whole) {
   if (mode == kGroupScale) {
     switch (nv) {
-      case 1: return tile_ks<DT, 1, kGroupScale>(K3, psc);
-      case 2: return tile_ks<DT, 2, kGroupScale>(K3, psc);
-      case 3: return tile_ks<DT, 3, kGroupScale>(K3, psc);
-      default: return tile_ks<DT, 4, kGroupScale>(K3, psc);
+      case 1: return tile_ks<DT, 1, kGroupScale>(K3, psc, whole);
+      case 2: return tile_ks<DT, 2, kGroupScale>(K3, psc, whole);
+      case 3: return tile_ks<DT, 3, kGroupScale>(K3, psc, whole);
+      default: return tile_ks<DT, 4, kGroupScale>(K3, psc, whole);
     }
   }
   if (mode == kStdScaled) {
     switch (nv) {
-      case 1: return tile_ks<DT, 1, kStdScaled>(K3, psc);
-      case 2: return tile_ks<DT, 2, kStdScaled>(K3, psc);
-      case 3: return tile_ks<DT, 3, kStdScaled>(K3, psc);
-      default: return tile_ks<DT, 4, kStdScaled>(K3, psc);
+      case 1: return tile_ks<DT, 1, kStdScaled>(K3, psc, whole);
+      case 2: return tile_ks<DT, 2, kStdScaled>(K3, psc, whole);
+      case 3: return tile_ks<DT, 3, kStdScaled>(K3, psc, whole);
+      default: return tile_ks<DT, 4, kStdScaled>(K3, psc, whole);
     }
   }
   switch (nv) {
-    case 1: return tile_ks<DT, 1, kStdUnitScale>(K3, psc);
-    case 2: return tile_ks<DT, 2, kStdUnitScale>(K3, psc);
-    case 3: return tile_ks<DT, 3, kStdUnitScale>(K3, psc);
-    default: return tile_ks<DT, 4, kStdUnitScale>(K3, psc);
+    case 1: return tile_ks<DT, 1, kStdUnitScale>(K3, psc, whole);
+    case 2: return tile_ks<DT, 2, kStdUnitScale>(K3, psc, whole);
+    case 3: return tile_ks<DT, 3, kStdUnitScale>(K3, psc, whole);
+    default: return tile_ks<DT, 4, kStdUnitScale>(K3, psc, whole);
   }
 }
 
@@ -2211,9 +2216,10 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   // square: see tile_point)
   const bool psc = ts.gb == 1 && (ts.slices > 1 || ts.dp == p.D) && ts.ps == 16 * nv &&
                    ts.wh == ts.ww;
-  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc)
-             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc)
-                                    : tile_pick<DCN4_F16>(nv, p.mode, K3, psc);
+  const bool whole = ts.whole != 0;
+  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc, whole)
+             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc, whole)
+                                    : tile_pick<DCN4_F16>(nv, p.mode, K3, psc, whole);
   TileArgs a{};
   fill_tile_args(p, a);
   a.scales = scales;
