@@ -575,6 +575,52 @@ def test_repeatable_and_stream_independent():
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+# degenerate images: one row or column, a single pixel, images smaller than
+# the kernel's footprint (every sample partly or wholly off the image)
+TINY = [Shape(2, 1, 1, 32, 2), Shape(1, 1, 7, 32, 2), Shape(1, 5, 1, 16, 1),
+        Shape(2, 2, 3, 64, 4), Shape(1, 3, 3, 32, 2, multiscale=True),
+        Shape(1, 2, 2, 32, 2, 5, 5, ph=2, pw=2)]
+
+
+@pytest.mark.parametrize("case", range(len(TINY)))
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_degenerate_images(case, dt):
+    """Tiny images on the automatic plan, the margin window, the whole-image
+    window and the direct kernel: bit for bit with the oracle; and the
+    backward within its bound."""
+    s = TINY[case]
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = wide_offset_inputs(s, dt, Ho, Wo, seed=900 + case, reach=2.5)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
+    dp = 8 if dt == "f32" else 0
+    variants = [dict(), dict(kernel=1), dict(kernel=2, tile_window=1),
+                dict(kernel=2, tile_window=2)]
+    for opts in variants:
+        try:
+            plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, **opts)
+        except d4.DCN4Error as e:
+            # a forced tiled kernel may not fit some shapes' windows
+            assert e.status == d4.DCN4_ERR_UNSUPPORTED and opts.get("kernel") == 2
+            continue
+        say(f"tiny {s} {dt} {opts}: {plan.info()}")
+        check_against_oracle(gpu_forward(plan, inp, dt), y_or, dt, f"tiny {case} {opts}")
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp)
+    gy = workloads.to_raw(np.random.default_rng(5 + case).standard_normal(
+        (s.N, Ho, Wo, s.C)).astype(np.float32), dt)
+    ref = o.backward(s, dt, inp.x, inp.om, gy, inp.scales)
+    x, om, g = to_dev(inp.x, dt), to_dev(inp.om, dt), to_dev(gy, dt)
+    sc = None if inp.scales is None else torch.from_numpy(inp.scales).cuda()
+    for scatter in (False, True):
+        gx, gom = plan.backward(x, om, g, sc, None, scatter=scatter)
+        torch.cuda.synchronize()
+        for got, want, absum, what in ((gx, ref["gx"], ref["gx_abs"], "grad_x"),
+                                       (gom, ref["gom"], ref["gom_abs"], "grad_om")):
+            err = np.abs(got.cpu().numpy().astype(np.float64) - want)
+            bound = (ref["max_terms"] + 8) * 2.0 ** -24 * absum + 1e-37
+            assert (err <= bound).all(), f"tiny {case} {what} scatter={scatter}"
+
+
 def test_empty_batch():
     plan = d4.Plan(d4.Desc(N=0, H=8, W=8, C=16, group=2, dtype="bf16"))
     x = torch.empty((0, 8, 8, 16), dtype=torch.bfloat16, device="cuda")
