@@ -203,7 +203,7 @@ def test_tile_window_choice():
     margin window's bytes: the 32x32 wide block (two 16-channel slices of its
     32-channel groups, 16x16 tiles); the 128x128 U-Net block keeps the margin
     window, and forcing the whole image there leaves no tile."""
-    wide = d4.Plan(desc_of(Shape(16, 32, 32, 1280, 40, dh=2, dw=2, ph=2, pw=2), "f16"))
+    wide = d4.Plan(desc_of(Shape(16, 32, 32, 1280, 40, dh=2, dw=2), "f16"))  # 30x30 output
     i = wide.info()
     assert i["kernel"] == 2 and i["tile_window"] == 2
     assert i["tile_slices"] == 2 and (i["tile_h"], i["tile_w"]) == (16, 16)
