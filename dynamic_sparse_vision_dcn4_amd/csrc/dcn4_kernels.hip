@@ -1359,13 +1359,19 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
     base_lds[r] = active ? ((((uint64_t)n * a.Ho + yo) * a.Wo + xo) * (uint32_t)a.G + g) * (3 * K)
                          : ~uint64_t(0);
   }
-  // each wave reads back only the rows its own lanes wrote
+  // each wave reads back only the rows its own lanes wrote, three floats (a
+  // point's dx, dy gradients or three weight gradients) per lane and store
+  typedef float f3 __attribute__((ext_vector_type(3), aligned(4)));
   const uint32_t wave = t >> 6, lane = t & 63u;
   const uint32_t r0 = wave * rows_wave;
-  for (uint32_t e = lane; e < rows_wave * (3 * K); e += 64) {
-    const uint32_t rl = e / (3 * K), c = e - rl * (3 * K);
+  for (uint32_t e = lane; e < rows_wave * K; e += 64) {
+    const uint32_t rl = e / K, c = 3 * (e - rl * K);
     const uint64_t base = base_lds[r0 + rl];
-    if (base != ~uint64_t(0)) bb.gom[base + c] = res_lds[(r0 + rl) * (3 * K) + c];
+    if (base != ~uint64_t(0)) {
+      const float* src = res_lds + (r0 + rl) * (3 * K) + c;
+      const f3 v = {src[0], src[1], src[2]};
+      *reinterpret_cast<f3*>(bb.gom + base + c) = v;
+    }
   }
 }
 
