@@ -161,7 +161,7 @@ int32_t tiled_backward_lds(const Plan& p);
 // Offset/weight linear layer: the K-streamed kernel's workgroup owns
 // kLinearRows pixels and kLinearCols output columns (buffer offsets stay
 // 32-bit when (Nout + kLinearCols) * Cin * 2 < 2^31).
-constexpr int kLinearRows = 128;
+constexpr int kLinearRows = 256;
 constexpr int kLinearCols = 128;
 // Cin up to which each wave keeps its pixels' features in registers
 constexpr int kLinearRsMaxCin = 384;

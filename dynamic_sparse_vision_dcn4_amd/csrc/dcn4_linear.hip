@@ -78,72 +78,133 @@ template <> struct Mfma<DCN4_F16> {
   __device__ static uint16_t enc(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 };
 
-// K-streamed form for every other Cin (a multiple of 16): a workgroup owns
-// 128 output columns x 128 pixels; its four waves own 64 x 64 each (2 x 2
-// MFMA tiles).  Both operands pass through LDS kGmBK inputs at a time,
-// double-buffered: the next stage is loaded into registers while the matrix cores
-// work on this one, then written to the other LDS buffer (no stores happen
-// in the loop, so waiting for those loads never waits for stores).  LDS rows
-// are padded by 8 elements (16 bytes), which puts the 16 rows of a
-// half-wave fragment read on distinct bank groups.  The weights are the A
+// buffer-to-LDS loads: lane l's 16 (4) bytes from offset voff of the buffer
+// land at dst + 16 l (4 l), dst uniform; offsets past the range write zeros.
+// The LDS pointer cast exists only in the device pass.
+#define DCN4_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DCN4_LDS_PTR(dst), 16, voff, 0, 0, 0);
+#endif
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DCN4_LDS_PTR(dst), 4, voff, 0, 0, 0);
+#endif
+}
+
+// s_waitcnt immediates (gfx9 encoding, expcnt and lgkmcnt not waited):
+// vmcnt 0, and vmcnt n (n < 16)
+constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
+constexpr int wait_vmcnt(int n) { return n | (7 << 4) | (15 << 8); }
+
+// K-streamed form for every other Cin (a multiple of 16), in producer and
+// consumer waves.  A workgroup owns 256 pixels x 128 output columns; eight
+// consumer waves own 64 x 64 each (2 x 2 MFMA tiles of 32 x 32).  The k
+// dimension streams through three LDS stages of kGmBK inputs: four producer
+// waves copy the features (256 rows) and the weights (128 rows) of a stage
+// straight from L2/HBM into LDS with 16-byte buffer-to-LDS loads and keep two
+// stages in flight while the consumers multiply the third, so neither the
+// staging registers nor the waits on global loads sit in the waves that issue
+// matrix ops (one barrier per stage; a producer waits only for the stage the
+// consumers take next).  A stage row is the 128 bytes of 64 inputs with its
+// 16-byte chunks XOR-swizzled by the row index mod 8 (chunk c of row r at
+// position c ^ (r & 7)): the copies write LDS in lane order, so the swizzle is
+// applied to the global addresses, and a half-wave's fragment read (32
+// consecutive rows, one chunk each) spreads over the bank groups.  Inputs
+// past Cin and rows past M or Nout read as zeros.  The weights are the A
 // operand, so a lane's results are 4 consecutive output columns of one
 // pixel.  The column tiles of one pixel block are consecutive in the
 // XCD-aware order, so the block's features are read from HBM once and from
 // L2 afterwards.
-constexpr int kGmBM = 128, kGmBN = 128, kGmBK = 64;
+constexpr int kGmBM = 256, kGmBN = 128, kGmBK = 64;
 static_assert(kGmBM == kLinearRows && kGmBN == kLinearCols, "tile sizes the API checks");
-constexpr int kGmRow = kGmBK + 8;  // padded LDS row, elements
-constexpr int kGmVpr = kGmBK / 8;  // 16-byte vectors per staged row
-constexpr int kGmPass = kGmBM * kGmVpr / 256;  // staged vectors per thread and operand
+constexpr int kGmCons = 8, kGmProd = 4;                    // consumer and producer waves
+constexpr int kGmThreads = 64 * (kGmCons + kGmProd);
+constexpr int kGmStages = 3;
+constexpr int kGmRowBytes = kGmBK * 2;                      // one staged row, 128 bytes
+constexpr int kGmFBytes = kGmBM * kGmRowBytes;              // features of a stage
+constexpr int kGmWBytes = kGmBN * kGmRowBytes;              // weights of a stage
+constexpr int kGmStageBytes = kGmFBytes + kGmWBytes;
+constexpr int kGmLdsBytes = kGmStages * kGmStageBytes;      // 147,456 B
+// copies of 64 x 16 bytes (8 rows) per stage, and per producer wave
+constexpr int kGmFCopies = kGmFBytes / 1024, kGmWCopies = kGmWBytes / 1024;
+constexpr int kGmCopiesPerProd = (kGmFCopies + kGmWCopies) / kGmProd;
+static_assert(kGmFCopies % kGmProd == 0 && kGmWCopies % kGmProd == 0, "copies split evenly");
+static_assert(kGmCopiesPerProd < 16, "one stage's copies fit a vmcnt wait immediate");
 
 template <int DT>
-__global__ __launch_bounds__(256) void dcn4_linear_gemm_kernel(LinArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sF[2][kGmBM * kGmRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kGmBN * kGmRow];
+__global__ __launch_bounds__(kGmThreads) void dcn4_linear_gemm_kernel(LinArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lb = lin_xcd_block(blockIdx.x, a.nblocks);
   const int bm = lb / a.col_chunks, bn = lb - bm * a.col_chunks;
   const int64_t row0 = (int64_t)bm * kGmBM;
   const int col0 = bn * kGmBN;
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, li = l & 31, h = l >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
   const int Cin = a.Cin;
+  const int nk = (Cin + kGmBK - 1) / kGmBK;
 
-  // features of the block's rows and weight rows of its columns; rows past
-  // M or Nout read as zeros
-  const int64_t rows_left = a.M - row0;
-  const uint64_t fbytes = (uint64_t)rows_left * Cin * 2u;
-  const rsrc_t fr = lin_rsrc(a.feat + row0 * Cin * 2,
-                             (uint32_t)(fbytes < 0x7fffffffu ? fbytes : 0x7fffffffu));
-  const uint64_t wbytes = (uint64_t)(a.Nout - col0) * Cin * 2u;
-  const rsrc_t wr = lin_rsrc(a.weight + (int64_t)col0 * Cin * 2,
-                             (uint32_t)(wbytes < 0x7fffffffu ? wbytes : 0x7fffffffu));
-  // staging: thread t moves 16-byte vector (row t/kGmVpr + (256/kGmVpr) p,
-  // inputs 8 (t%kGmVpr)..) of each operand, p < kGmPass
-  constexpr int kRowsPerPass = 256 / kGmVpr;
-  const int sr = tid / kGmVpr, sq = tid % kGmVpr;
-  u32x4 gf[kGmPass], gw[kGmPass];
-  auto gload = [&](int k0) {
+  if (wave >= kGmCons) {
+    // ---- producer: stages kt = 0, 1 first, then stage kt + 2 while the
+    // consumers take stage kt
+    // the producer index, made provably wave-uniform: the LDS destination of
+    // a buffer-to-LDS copy must be, or the compiler loops over its values
+    const int pw = __builtin_amdgcn_readfirstlane(wave - kGmCons);
+    const int64_t rows_left = a.M - row0;
+    const uint64_t fbytes = (uint64_t)rows_left * Cin * 2u;
+    const rsrc_t fr = lin_rsrc(a.feat + row0 * Cin * 2,
+                               (uint32_t)(fbytes < 0x7fffffffu ? fbytes : 0x7fffffffu));
+    const uint64_t wbytes = (uint64_t)(a.Nout - col0) * Cin * 2u;
+    const rsrc_t wr = lin_rsrc(a.weight + (int64_t)col0 * Cin * 2,
+                               (uint32_t)(wbytes < 0x7fffffffu ? wbytes : 0x7fffffffu));
+    // lane l of copy j writes row 8 j + l / 8, position l % 8, i.e. chunk
+    // (l % 8) ^ (row % 8) of that row; the row's offset in the operand
+    const int lr = l >> 3, lpos = l & 7;
+    const int chunk = lpos ^ lr;  // rows 8 j + lr have row % 8 == lr
+    auto issue = [&](int kt) {
+      char* st = lds + (kt % kGmStages) * kGmStageBytes;
+      const int k = kt * kGmBK + 8 * chunk;
+      const bool kin = k < Cin;
 #pragma unroll
-    for (int p = 0; p < kGmPass; ++p) {
-      const int off = ((sr + kRowsPerPass * p) * Cin + k0 + 8 * sq) * 2;
-      gf[p] = __builtin_amdgcn_raw_buffer_load_b128(fr, off, 0, 0);
-      gw[p] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
-    }
-    if (k0 + kGmBK > Cin) {  // the last, partial stage: inputs past Cin are zero
-      const bool kin = k0 + 8 * sq < Cin;
+      for (int i = 0; i < kGmFCopies / kGmProd; ++i) {
+        const int j = pw + kGmProd * i;
+        const int row = 8 * j + lr;
+        lds_dma16(fr, st + j * 1024, kin ? (row * Cin + k) * 2 : (int)0x80000000);
+      }
 #pragma unroll
-      for (int p = 0; p < kGmPass; ++p)
-        if (!kin) gf[p] = gw[p] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < kGmWCopies / kGmProd; ++i) {
+        const int j = pw + kGmProd * i;
+        const int row = 8 * j + lr;
+        lds_dma16(wr, st + kGmFBytes + j * 1024, kin ? (row * Cin + k) * 2 : (int)0x80000000);
+      }
+    };
+    // The producers' barriers are bare s_barrier: the fence of __syncthreads
+    // would make them wait for every copy in flight, the next stage's too.
+    // A stage's copies have written LDS once vmcnt says so, and the
+    // consumers order their own LDS reads around the same barriers.
+    issue(0);
+    if (nk > 1) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(kGmCopiesPerProd));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int p = 0; p < kGmPass; ++p) {
-      *reinterpret_cast<u32x4*>(&sF[st][(sr + kRowsPerPass * p) * kGmRow + 8 * sq]) = gf[p];
-      *reinterpret_cast<u32x4*>(&sW[st][(sr + kRowsPerPass * p) * kGmRow + 8 * sq]) = gw[p];
+    __builtin_amdgcn_s_barrier();  // stage 0 in LDS
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 2 < nk) {
+        issue(kt + 2);  // into the buffer of stage kt - 1, read before the last barrier
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(kGmCopiesPerProd));  // stage kt + 1 has landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
+      __builtin_amdgcn_s_barrier();
     }
-  };
+    return;
+  }
 
+  // ---- consumer
+  const int li = l & 31, h = l >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[2][2];
 #pragma unroll
   for (int tj = 0; tj < 2; ++tj)
@@ -151,29 +212,29 @@ __global__ __launch_bounds__(256) void dcn4_linear_gemm_kernel(LinArgs a) {
     for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[tj][tp][e] = 0.0f;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int k0 = 0, st = 0; k0 < Cin; k0 += kGmBK, st ^= 1) {
-    const bool more = k0 + kGmBK < Cin;
-    if (more) gload(k0 + kGmBK);
+  // fragment rows of this lane: weights wn*64 + 32 t + li, features
+  // wm*64 + 32 t + li; their swizzle (row % 8 == li % 8 for both)
+  const int sw = li & 7;
+  const int wrow = (wn * 64 + li) * kGmRowBytes, frow = (wm * 64 + li) * kGmRowBytes;
+  __syncthreads();  // stage 0 in LDS
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* st = lds + (kt % kGmStages) * kGmStageBytes;
 #pragma unroll
     for (int kk = 0; kk < kGmBK; kk += 16) {
-      if (k0 + kk >= Cin) break;
+      if (kt * kGmBK + kk >= Cin) break;
+      const int pos = 16 * (((kk >> 3) + h) ^ sw);
       u32x4 fw[2], ff[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        fw[t] = *reinterpret_cast<const u32x4*>(&sW[st][(wn * 64 + t * 32 + li) * kGmRow + kk + 8 * h]);
-        ff[t] = *reinterpret_cast<const u32x4*>(&sF[st][(wm * 64 + t * 32 + li) * kGmRow + kk + 8 * h]);
+        fw[t] = *reinterpret_cast<const u32x4*>(st + kGmFBytes + wrow + t * 32 * kGmRowBytes + pos);
+        ff[t] = *reinterpret_cast<const u32x4*>(st + frow + t * 32 * kGmRowBytes + pos);
       }
 #pragma unroll
       for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) acc[tj][tp] = Mfma<DT>::run(fw[tj], ff[tp], acc[tj][tp]);
     }
-    if (more) sstore(st ^ 1);
-    __syncthreads();
+    __syncthreads();  // done with stage kt; stage kt + 1 has landed
   }
 
   // epilogue: element e of tile (tj, tp) is output column col0 + 64 wn +
@@ -238,8 +299,6 @@ constexpr int kRsPixels = 32 * kRsConsumers;    // pixels per workgroup
 constexpr int kRsAhead = 2;                     // fragment-read steps kept in flight
 constexpr int kRsOutRow = 144;                  // bytes per pixel row of the output area
 constexpr int kRsOutBytes = 32 * kRsOutRow;     // one consumer's output area
-// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited
-constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 
 template <int S> struct RsLayout {
   static constexpr int Q = 2 * S;                 // 16-byte vectors per weight row
@@ -249,20 +308,6 @@ template <int S> struct RsLayout {
   static constexpr int kLdsBytes = 2 * kPassBytes + kRsConsumers * kRsOutBytes;
 };
 
-// buffer-to-LDS loads: lane l's 16 (4) bytes from offset voff of the buffer
-// land at dst + 16 l (4 l), dst uniform; offsets past the range write zeros.
-// The LDS pointer cast exists only in the device pass.
-#define DCN4_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-__device__ __forceinline__ void lds_dma16(rsrc_t r, char* dst, int voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DCN4_LDS_PTR(dst), 16, voff, 0, 0, 0);
-#endif
-}
-__device__ __forceinline__ void lds_dma4(rsrc_t r, char* dst, int voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, DCN4_LDS_PTR(dst), 4, voff, 0, 0, 0);
-#endif
-}
 
 template <int DT, int S>
 __global__ __launch_bounds__(kRsThreads) void dcn4_linear_rs_kernel(LinArgs a) {
@@ -641,7 +686,8 @@ dcn4_status launch_linear(const void* feat, const void* weight, const float* bia
     a.nblocks = (int32_t)blocks;
     void (*fn)(LinArgs) = dtype == DCN4_BF16 ? dcn4_linear_gemm_kernel<DCN4_BF16>
                                              : dcn4_linear_gemm_kernel<DCN4_F16>;
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    if (!rs_lds_attribute_set(fn, kGmLdsBytes)) return DCN4_ERR_HIP;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kGmThreads), kGmLdsBytes, st, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -73,7 +73,11 @@ CASES = [(1, 16, 1, True), (200, 48, 54, True), (300, 64, 300, False),
          # with Nout % 4 != 0 (2-byte stores) and == 0 (8-byte stores)
          (300, 64, 54, True), (64, 128, 540, False), (33, 192, 81, True),
          (1000, 256, 216, True), (257, 384, 135, True), (130, 384, 32, False),
-         (1, 320, 540, True)]
+         (1, 320, 540, True),
+         # the K-streamed GEMM's pipeline: two stages with a partial last
+         # one, three stages, seven with a partial last one; ragged row
+         # blocks of 256 and column chunks of 128
+         (513, 80, 128, False), (600, 144, 100, True), (300, 400, 270, True)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
