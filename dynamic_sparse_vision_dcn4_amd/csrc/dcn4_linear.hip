@@ -99,15 +99,18 @@ constexpr int kWaitVmcnt0 = (7 << 4) | (15 << 8);
 constexpr int wait_vmcnt(int n) { return n | (7 << 4) | (15 << 8); }
 
 // K-streamed form for every other Cin (a multiple of 16), in producer and
-// consumer waves.  A workgroup owns 256 pixels x 128 output columns; eight
+// consumer waves.  A workgroup owns 128 pixels x 128 output columns; four
 // consumer waves own 64 x 64 each (2 x 2 MFMA tiles of 32 x 32).  The k
-// dimension streams through three LDS stages of kGmBK inputs: four producer
-// waves copy the features (256 rows) and the weights (128 rows) of a stage
-// straight from L2/HBM into LDS with 16-byte buffer-to-LDS loads and keep two
-// stages in flight while the consumers multiply the third, so neither the
-// staging registers nor the waits on global loads sit in the waves that issue
-// matrix ops (one barrier per stage; a producer waits only for the stage the
-// consumers take next).  A stage row is the 128 bytes of 64 inputs with its
+// dimension streams through two LDS stages of kGmBK inputs: four producer
+// waves copy the features and the weights (128 rows each) of the next stage
+// straight from L2/HBM into LDS with 16-byte buffer-to-LDS loads while the
+// consumers multiply this one, so neither the staging registers nor the
+// waits on global loads sit in the waves that issue matrix ops (one barrier
+// per stage).  64 KB of LDS: two workgroups per CU, so one workgroup's
+// prologue and epilogue overlap the other's stages (measured against 256
+// pixels in eight consumer waves with three stages, one workgroup per CU:
+// the wide block's 1280 -> 1080 layer 76.2 -> 64.7 us, FlowDCN's 1152 -> 432
+// 56.0 -> 57.3 us).  A stage row is the 128 bytes of 64 inputs with its
 // 16-byte chunks XOR-swizzled by the row index mod 8 (chunk c of row r at
 // position c ^ (r & 7)): the copies write LDS in lane order, so the swizzle is
 // applied to the global addresses, and a half-wave's fragment read (32
@@ -117,11 +120,12 @@ constexpr int wait_vmcnt(int n) { return n | (7 << 4) | (15 << 8); }
 // pixel.  The column tiles of one pixel block are consecutive in the
 // XCD-aware order, so the block's features are read from HBM once and from
 // L2 afterwards.
-constexpr int kGmBM = 256, kGmBN = 128, kGmBK = 64;
-static_assert(kGmBM == kLinearRows && kGmBN == kLinearCols, "tile sizes the API checks");
-constexpr int kGmCons = 8, kGmProd = 4;                    // consumer and producer waves
+constexpr int kGmBM = 128, kGmBN = 128, kGmBK = 64;
+static_assert(kGmBM <= kLinearRows && kGmBN <= kLinearCols, "tile sizes the API checks");
+constexpr int kGmCons = (kGmBM / 64) * (kGmBN / 64), kGmProd = 4;  // consumer and producer waves
 constexpr int kGmThreads = 64 * (kGmCons + kGmProd);
-constexpr int kGmStages = 3;
+constexpr int kGmStages = 2;
+constexpr int kGmAhead = kGmStages - 1;  // stages in flight beyond the one being multiplied
 constexpr int kGmRowBytes = kGmBK * 2;                      // one staged row, 128 bytes
 constexpr int kGmFBytes = kGmBM * kGmRowBytes;              // features of a stage
 constexpr int kGmWBytes = kGmBN * kGmRowBytes;              // weights of a stage
@@ -182,8 +186,9 @@ __global__ __launch_bounds__(kGmThreads) void dcn4_linear_gemm_kernel(LinArgs a)
     // would make them wait for every copy in flight, the next stage's too.
     // A stage's copies have written LDS once vmcnt says so, and the
     // consumers order their own LDS reads around the same barriers.
+    static_assert(kGmAhead == 1 || kGmAhead == 2, "one or two stages ahead");
     issue(0);
-    if (nk > 1) {
+    if (kGmAhead == 2 && nk > 1) {
       issue(1);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(kGmCopiesPerProd));
     } else {
@@ -191,13 +196,16 @@ __global__ __launch_bounds__(kGmThreads) void dcn4_linear_gemm_kernel(LinArgs a)
     }
     __builtin_amdgcn_s_barrier();  // stage 0 in LDS
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 2 < nk) {
-        issue(kt + 2);  // into the buffer of stage kt - 1, read before the last barrier
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(kGmCopiesPerProd));  // stage kt + 1 has landed
+      // into the buffer of stage kt + kGmAhead - kGmStages = kt - 1, whose
+      // reads ended before the last barrier
+      if (kt + kGmAhead < nk) {
+        issue(kt + kGmAhead);
+        if (kGmAhead == 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kGmCopiesPerProd));
+        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       } else {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       }
-      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();  // stage kt + 1 has landed
     }
     return;
   }
