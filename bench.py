@@ -14,8 +14,9 @@ model of the DCNv4 digest page, section "GPU效率的理论分析") and its frac
 of the MI355X HBM peak (8 TB/s); output pixels/s and outputs/s are reported
 beside it.
 
-Prints ONE JSON line.  --gpus N with N > 1 is refused: this build runs on one
-GPU (images are independent; see the design doc for how the batch would shard).
+Prints ONE JSON line.  --gpus N with N > 1 is refused: the benchmark measures
+one GPU (images are independent, so a batch would shard across GPUs by image
+with no communication in the forward pass).
 """
 from __future__ import annotations
 
@@ -91,8 +92,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} refused: this operator build measures "
-              "one GPU only (batch sharding over GPUs is a design note, not built)",
+        print(f"bench.py: --gpus {args.gpus} refused: the benchmark measures one GPU "
+              "only (sharding a batch over GPUs by image is not built)",
               file=sys.stderr)
         sys.exit(2)
 
