@@ -34,8 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
-# VALU lane-operations per second without packed fp32: 256 CUs x 64 lanes
-# (4 SIMD16 per CU) x 2.4 GHz
+# fp32 fma per second on the vector ALU without packed fp32: 256 CUs x 64
+# lanes (4 SIMD16 per CU) x 2.4 GHz
 VALU_PEAK_GOPS = 256 * 64 * 2.4
 
 
@@ -47,17 +47,49 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, launches_bytes: float):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def load_profile_summary(kind: str, workload: str):
+    """A committed rocprofv3 counter summary (profiles/<kind>_<workload>.json)
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain
+    copy's counters), or None when the counters predate the source."""
+    t = load_profile_summary("traffic", workload)
+    return None if t is None else t.get("hbm_bytes_per_launch")
+
+
+def copy_ceiling(torch, mib=512, reps=5):
+    """Plain device copies of `mib` MiB on the current stream: bytes read plus
+    bytes written per second (the achievable HBM rate of a streaming copy on
+    this GPU, the context for the operator's fraction of the 8 TB/s peak)."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = statistics.median(times)
+    del a, b
+    return {"gbs": round(2 * n / t / 1e9, 1), "bytes_moved": 2 * n,
+            "pct_hbm_peak": round(100.0 * 2 * n / t / 1e9 / HBM_PEAK_GBS, 2),
+            "what": f"median of {reps} device copies of {mib} MiB (read + write)"}
 
 
 def main():
@@ -179,11 +211,19 @@ def main():
     kern_ms = statistics.mean(per_launch_ms)
 
     value = ideal / (ms_per_step * 1e-3) / 1e9
-    achieved = ideal / (kern_ms * 1e-3) / 1e9
+    # the roofline uses the same time base as `value`: the average duration
+    # of one launch over the timed region (HIP events on the launch stream
+    # around the K steps; one launch per step, back to back)
+    achieved = value
     out_pix = w.N * Ho * Wo
-    traffic = load_traffic(name, ideal)
-    alu_ops_per_out = 4 * w.kh * w.kw * (1 if w.dtype == "f32" else 2)
-    alu_gops = alu_ops_per_out * out_pix * w.C / (kern_ms * 1e-3) / 1e9
+    traffic = load_traffic(name)
+    # the arithmetic floor: 4 multiply-adds per point and output element
+    # (the pages' 36HWC for 3x3), fp32 fma on the vector ALU; the counters'
+    # VALU instructions per output element beside it when a summary of the
+    # current source is committed
+    fma_per_out = 4 * w.kh * w.kw
+    alu_gops = fma_per_out * out_pix * w.C / (ms_per_step * 1e-3) / 1e9
+    valu = load_profile_summary("valu", name)
 
     line = {
         "metric": "DCNv4 fwd GB/s (ideal bytes) and % of HBM peak; output pixels/sec",
@@ -216,13 +256,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        # the second bound of this path: per output element, 4K fma and, for
-        # 16-bit inputs, 4K widenings to fp32 (one per corner value)
+                     "traffic": traffic,
+                     "time_base": "mean launch duration over the timed region "
+                                  "(= ms_per_step: one launch per step)"},
         "roofline_alu": {"bound": "alu", "achieved": round(alu_gops, 1),
-                         "peak": round(VALU_PEAK_GOPS, 1), "unit": "Gop/s",
+                         "peak": round(VALU_PEAK_GOPS, 1), "unit": "Gfma/s",
                          "frac": round(alu_gops / VALU_PEAK_GOPS, 4),
-                         "ops_per_output": alu_ops_per_out},
+                         "fma_per_output": fma_per_out,
+                         "valu_insts_per_output_measured":
+                             None if valu is None else valu.get("valu_insts_per_output")},
+        "copy_ceiling": copy_ceiling(torch),
         "kernel_source": kernel_source_digest(),
     }
 

@@ -72,7 +72,8 @@ class dcn4_launch_info(ctypes.Structure):
                 ("tile_slices", ctypes.c_int32),
                 ("bucket_capacity", ctypes.c_int32),
                 ("tile_window", ctypes.c_int32),
-                ("tile_passes", ctypes.c_int32)]
+                ("tile_passes", ctypes.c_int32),
+                ("tile_f16_window", ctypes.c_int32)]
 
 # dcn4_option
 DCN4_OPT_CHANNELS_PER_LANE = 0
@@ -84,11 +85,12 @@ DCN4_OPT_TILE_SWIZZLE = 5
 DCN4_OPT_BUCKET_CAPACITY = 6
 DCN4_OPT_TILE_WINDOW = 7
 DCN4_OPT_TILE_PASSES = 8
+DCN4_OPT_TILE_F16_WINDOW = 9
 OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
            "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
            "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE,
            "bucket_capacity": DCN4_OPT_BUCKET_CAPACITY, "tile_window": DCN4_OPT_TILE_WINDOW,
-           "tile_passes": DCN4_OPT_TILE_PASSES}
+           "tile_passes": DCN4_OPT_TILE_PASSES, "tile_f16_window": DCN4_OPT_TILE_F16_WINDOW}
 
 
 _P = ctypes.c_void_p
@@ -183,6 +185,23 @@ def dcn4_backward_workspace_size(plan):
     return st, n.value
 
 
+def _require(t, shape, dtype, name, device=None):
+    """A CUDA tensor of exactly `shape` and `dtype`, contiguous, on `device`
+    (when given): the C ABI sees only pointers, so sizes are checked here."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def dcn4_offset_linear(feat: int, weight: int, bias: Optional[int], offset_mask: int,
                        M: int, Cin: int, Nout: int, dtype: int, stream: Optional[int]) -> int:
     return _lib.dcn4_offset_linear(feat, weight, bias, offset_mask, M, Cin, Nout, dtype, stream)
@@ -191,17 +210,24 @@ def dcn4_offset_linear(feat: int, weight: int, bias: Optional[int], offset_mask:
 def offset_linear(feat, weight, bias=None, out=None, stream=None):
     """offset_mask [M, Nout] = feat [M, Cin] @ weight[Nout, Cin]^T + bias
     (torch CUDA tensors, bf16 or fp16; bias fp32)."""
+    if not isinstance(feat, torch.Tensor) or feat.dim() != 2:
+        raise ValueError("feat must be a 2-d tensor [M, Cin]")
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be a 2-d tensor [Nout, Cin]")
     dt = {torch.bfloat16: DCN4_BF16, torch.float16: DCN4_F16}.get(feat.dtype)
-    if dt is None or weight.dtype != feat.dtype:
-        raise TypeError("feat and weight must both be bf16 or fp16")
+    if dt is None:
+        raise TypeError("feat must be bf16 or fp16")
     M, Cin = feat.shape
     Nout = weight.shape[0]
-    if weight.shape[1] != Cin or not feat.is_contiguous() or not weight.is_contiguous():
-        raise ValueError("feat [M, Cin] and weight [Nout, Cin] must be contiguous")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Nout):
-        raise ValueError("bias must be fp32 [Nout]")
+    _require(feat, (M, Cin), feat.dtype, "feat")
+    dev = feat.device
+    _require(weight, (Nout, Cin), feat.dtype, "weight", dev)
+    if bias is not None:
+        _require(bias, (Nout,), torch.float32, "bias", dev)
     if out is None:
-        out = torch.empty((M, Nout), dtype=feat.dtype, device=feat.device)
+        out = torch.empty((M, Nout), dtype=feat.dtype, device=dev)
+    else:
+        _require(out, (M, Nout), feat.dtype, "out", dev)
     if stream is None:
         stream = torch.cuda.current_stream(feat.device).cuda_stream
     st = dcn4_offset_linear(feat.data_ptr(), weight.data_ptr(),
@@ -221,17 +247,22 @@ def dwconv3x3(x, weight, bias=None, out=None, stream=None):
     """out [N,H,W,C] = depthwise 3x3 convolution of x [N,H,W,C] with weight
     [3,3,C] (stride 1, zero padding 1) plus bias (fp32 [C] or None); torch
     CUDA tensors of one dtype."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("x must be a 4-d tensor [N, H, W, C]")
     dt = {torch.float32: DCN4_F32, torch.bfloat16: DCN4_BF16,
           torch.float16: DCN4_F16}.get(x.dtype)
-    if dt is None or weight.dtype != x.dtype:
-        raise TypeError("x and weight must share a dtype: fp32, bf16 or fp16")
+    if dt is None:
+        raise TypeError("x must be fp32, bf16 or fp16")
     N, H, W, C = x.shape
-    if tuple(weight.shape) != (3, 3, C) or not x.is_contiguous() or not weight.is_contiguous():
-        raise ValueError("x [N,H,W,C] and weight [3,3,C] must be contiguous")
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != C):
-        raise ValueError("bias must be fp32 [C]")
+    _require(x, (N, H, W, C), x.dtype, "x")
+    dev = x.device
+    _require(weight, (3, 3, C), x.dtype, "weight", dev)
+    if bias is not None:
+        _require(bias, (C,), torch.float32, "bias", dev)
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _require(out, (N, H, W, C), x.dtype, "out", dev)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     st = dcn4_dwconv3x3(x.data_ptr(), weight.data_ptr(),
@@ -309,7 +340,8 @@ class Plan:
 
     def __init__(self, desc: Desc, channels_per_lane: int = 0, **options):
         """options: kernel, tile_margin, tile_groups, tile_pad, tile_swizzle,
-        tile_window, tile_passes, bucket_capacity (dcn4_option).  The kernel choice is applied last, so a forced tiled
+        tile_window, tile_passes, tile_f16_window, bucket_capacity (dcn4_option).  The
+        kernel choice is applied last, so a forced tiled
         kernel is checked against the tile options given with it."""
         self.desc = desc
         st, h = dcn4_create(desc.c_struct())
@@ -350,16 +382,8 @@ class Plan:
         d = self.desc
         return (d.N, self.Ho, self.Wo, d.group, 3 * d.kernel_h * d.kernel_w)
 
-    def _check(self, t, shape, dtype, name):
-        import torch
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError(f"{name} must be a CUDA tensor")
-        if t.dtype != dtype:
-            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-        if tuple(t.shape) != tuple(shape) and t.numel() != int(_prod(shape)):
-            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    def _check(self, t, shape, dtype, name, device=None):
+        _require(t, shape, dtype, name, device)
 
     def forward(self, x, om, scales=None, out=None, stream=None, pixel_scales=None):
         """y[N,Ho,Wo,C] = DCNv4(x[N,H,W,C], om[N,Ho,Wo,G,3K], scales[G],
@@ -368,16 +392,17 @@ class Plan:
         d = self.desc
         dt = _torch_dtype(d.dtype)
         self._check(x, (d.N, d.H, d.W, d.C), dt, "x")
-        self._check(om, self.om_shape(), dt, "offset_mask")
+        dev = x.device
+        self._check(om, self.om_shape(), dt, "offset_mask", dev)
         if scales is not None:
-            self._check(scales, (d.group,), torch.float32, "group_scales")
+            self._check(scales, (d.group,), torch.float32, "group_scales", dev)
         if pixel_scales is not None:
             self._check(pixel_scales, (d.N, self.Ho, self.Wo, d.group), torch.float32,
-                        "pixel_scales")
+                        "pixel_scales", dev)
         if out is None:
-            out = torch.empty(self.out_shape(), dtype=dt, device=x.device)
+            out = torch.empty(self.out_shape(), dtype=dt, device=dev)
         else:
-            self._check(out, self.out_shape(), dt, "out")
+            self._check(out, self.out_shape(), dt, "out", dev)
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
         if d.use_pixel_scales or pixel_scales is not None:
@@ -414,29 +439,31 @@ class Plan:
         d = self.desc
         dt = _torch_dtype(d.dtype)
         self._check(x, (d.N, d.H, d.W, d.C), dt, "x")
-        self._check(om, self.om_shape(), dt, "offset_mask")
-        self._check(grad_y, self.out_shape(), dt, "grad_y")
+        dev = x.device
+        self._check(om, self.om_shape(), dt, "offset_mask", dev)
+        self._check(grad_y, self.out_shape(), dt, "grad_y", dev)
         if scales is not None:
-            self._check(scales, (d.group,), torch.float32, "group_scales")
+            self._check(scales, (d.group,), torch.float32, "group_scales", dev)
         if pixel_scales is not None:
             self._check(pixel_scales, (d.N, self.Ho, self.Wo, d.group), torch.float32,
-                        "pixel_scales")
+                        "pixel_scales", dev)
         if want_x and grad_x is None:
             grad_x = torch.empty((d.N, d.H, d.W, d.C), dtype=torch.float32, device=x.device)
         if want_om and grad_om is None:
             grad_om = torch.empty(self.om_shape(), dtype=torch.float32, device=x.device)
         if grad_x is not None:
-            self._check(grad_x, (d.N, d.H, d.W, d.C), torch.float32, "grad_x")
+            self._check(grad_x, (d.N, d.H, d.W, d.C), torch.float32, "grad_x", dev)
         if grad_om is not None:
-            self._check(grad_om, self.om_shape(), torch.float32, "grad_offset_mask")
+            self._check(grad_om, self.om_shape(), torch.float32, "grad_offset_mask", dev)
         ws_ptr, ws_bytes = None, 0
         if grad_x is not None and not scatter:
             need = self.backward_workspace_bytes()
             if need and workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
             if need:
-                if workspace.dtype != torch.uint8 or workspace.device != x.device:
-                    raise ValueError("workspace must be a uint8 tensor on x's device")
+                if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
+                        or workspace.device != x.device or not workspace.is_contiguous()):
+                    raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
                 ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
         if stream is None:
             stream = torch.cuda.current_stream(x.device).cuda_stream
@@ -479,13 +506,6 @@ class Plan:
         if h:
             _destroy(h)
             self._h = None
-
-
-def _prod(s):
-    r = 1
-    for v in s:
-        r *= int(v)
-    return r
 
 
 def loaded_library_path() -> str:

@@ -121,6 +121,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.tile_swizzle = kDefaultTileSwizzle;
   p.tile_window = 0;
   p.tile_passes = 0;
+  p.f16_window = 1;
   dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic
@@ -204,6 +205,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_slices = t.slices;
     info->tile_window = t.whole ? 2 : 1;
     info->tile_passes = t.passes;
+    info->tile_f16_window = dcn4::tile_f16_window(p) ? 1 : 0;
     return DCN4_OK;
   }
   info->kernel = 1;
@@ -272,6 +274,11 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
       if (value < 0 || value > 64) return fail(DCN4_ERR_INVALID_ARG, "tile passes must be 0-64");
       q.tile_passes = value;
       break;
+    case DCN4_OPT_TILE_F16_WINDOW:
+      if (value != 0 && value != 1)
+        return fail(DCN4_ERR_INVALID_ARG, "tile f16 window must be 0 or 1");
+      q.f16_window = value;
+      break;
     case DCN4_OPT_BUCKET_CAPACITY:
       if (value < 0 || value > 1024)
         return fail(DCN4_ERR_INVALID_ARG, "bucket capacity must be 0-1024");
@@ -285,6 +292,40 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     return fail(DCN4_ERR_UNSUPPORTED, "the tiled kernel does not apply to this plan");
   plan->p = q;
   return DCN4_OK;
+}
+
+// Whether the byte ranges [a, a + na) and [b, b + nb) intersect (an empty or
+// NULL range intersects nothing).
+static bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Byte sizes of a plan's tensors.
+struct IoBytes {
+  uint64_t x, om, y, scales, pscales;
+};
+static IoBytes io_bytes(const dcn4::Plan& p) {
+  const dcn4_desc& d = p.desc;
+  const uint64_t pix = uint64_t(d.N) * p.Ho * p.Wo;
+  IoBytes b;
+  b.x = uint64_t(d.N) * d.H * d.W * d.C * p.es;
+  b.om = pix * d.group * 3 * p.K * p.es;
+  b.y = pix * d.C * p.es;
+  b.scales = d.use_group_scales ? 4ull * d.group : 0;
+  b.pscales = d.use_pixel_scales ? 4ull * pix * d.group : 0;
+  return b;
+}
+
+// An output range that intersects any input range of the call.
+static bool output_overlaps_inputs(const dcn4::Plan& p, const void* out, uint64_t n,
+                                   const void* x, const void* om, const float* scales,
+                                   const float* pscales, const void* gy) {
+  const IoBytes b = io_bytes(p);
+  return overlaps(out, n, x, b.x) || overlaps(out, n, om, b.om) ||
+         overlaps(out, n, scales, b.scales) || overlaps(out, n, pscales, b.pscales) ||
+         overlaps(out, n, gy, b.y);
 }
 
 static dcn4_status check_io(const dcn4::Plan& p, const void* x, const void* om,
@@ -322,6 +363,9 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
   const dcn4::Plan& p = plan->p;
   dcn4_status s = check_io(p, x, offset_mask, group_scales, pixel_scales, y, true);
   if (s != DCN4_OK || p.desc.N == 0) return s;
+  if (output_overlaps_inputs(p, y, io_bytes(p).y, x, offset_mask, group_scales, pixel_scales,
+                             nullptr))
+    return fail(DCN4_ERR_INVALID_ARG, "y overlaps an input");
   const bool vector_path = p.dp > 0 && aligned_to(x, 16) &&
                            aligned_to(offset_mask, 16) && aligned_to(y, 16);
   if (vector_path && p.tile.ok)
@@ -355,6 +399,12 @@ static dcn4_status check_backward(const dcn4::Plan& p, const void* x, const void
   if (s != DCN4_OK) return s;
   if ((gx && !aligned_to(gx, 4)) || (gom && !aligned_to(gom, 4)))
     return fail(DCN4_ERR_MISALIGNED, "gradient outputs must be 4-byte aligned");
+  const IoBytes b = io_bytes(p);
+  const uint64_t ngx = b.x / p.es * 4, ngom = b.om / p.es * 4;
+  if (output_overlaps_inputs(p, gx, ngx, x, om, scales, pscales, gy) ||
+      output_overlaps_inputs(p, gom, ngom, x, om, scales, pscales, gy) ||
+      overlaps(gx, ngx, gom, ngom))
+    return fail(DCN4_ERR_INVALID_ARG, "a gradient output overlaps an input or the other output");
   return DCN4_OK;
 }
 
@@ -373,6 +423,12 @@ dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x, const void* o
       return fail(DCN4_ERR_MISALIGNED, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
       return fail(DCN4_ERR_INVALID_ARG, "workspace smaller than dcn4_backward_workspace_size");
+    const IoBytes b = io_bytes(p);
+    if (output_overlaps_inputs(p, workspace, need, x, offset_mask, group_scales, pixel_scales,
+                               grad_y) ||
+        overlaps(workspace, need, grad_x, b.x / p.es * 4) ||
+        overlaps(workspace, need, grad_offset_mask, b.om / p.es * 4))
+      return fail(DCN4_ERR_INVALID_ARG, "the workspace overlaps another argument");
   }
   if (p.desc.N == 0) return DCN4_OK;
   const bool vector_path = p.dp > 0 && aligned_to(x, 16) && aligned_to(offset_mask, 16) &&
@@ -433,6 +489,11 @@ dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float
       (bias && !aligned_to(bias, 4)))
     return fail(DCN4_ERR_MISALIGNED,
                 "feat and weight must be 16-byte aligned, offset_mask 2, bias 4");
+  const uint64_t nout = uint64_t(M) * Nout * 2;
+  if (overlaps(offset_mask, nout, feat, uint64_t(M) * Cin * 2) ||
+      overlaps(offset_mask, nout, weight, uint64_t(Nout) * Cin * 2) ||
+      overlaps(offset_mask, nout, bias, bias ? 4ull * Nout : 0))
+    return fail(DCN4_ERR_INVALID_ARG, "offset_mask overlaps feat, weight or bias");
   dcn4_status s = dcn4::launch_linear(feat, weight, bias, offset_mask, M, Cin, Nout, dtype,
                                       stream);
   if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
@@ -452,7 +513,10 @@ dcn4_status dcn4_dwconv3x3(const void* x, const void* weight, const float* bias,
   if (!aligned_to(x, es) || !aligned_to(weight, es) || !aligned_to(out, es) ||
       (bias && !aligned_to(bias, 4)))
     return fail(DCN4_ERR_MISALIGNED, "tensors must be aligned to the element size, bias to 4");
-  if (x == out) return fail(DCN4_ERR_INVALID_ARG, "out must not alias x");
+  const uint64_t nx = uint64_t(N) * H * W * C * es;
+  if (overlaps(out, nx, x, nx) || overlaps(out, nx, weight, 9ull * C * es) ||
+      overlaps(out, nx, bias, bias ? 4ull * C : 0))
+    return fail(DCN4_ERR_INVALID_ARG, "out overlaps x, weight or bias");
   const bool vector_path = (C * es) % 16 == 0 && aligned_to(x, 16) && aligned_to(weight, 16) &&
                            aligned_to(out, 16) && (!bias || aligned_to(bias, 16));
   dcn4_status s = dcn4::launch_dwconv(x, weight, bias, out, N, H, W, C, dtype, vector_path,

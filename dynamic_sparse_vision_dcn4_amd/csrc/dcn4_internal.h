@@ -91,6 +91,10 @@ struct TileArgs {
   int32_t oppp;          // tile pixels per pass when orpp == 0
   int32_t opasses;       // offset/weight staging passes
   int32_t om_lds;        // byte offset of the offset/weight area in LDS
+  int32_t f16_window;    // bf16: stage the window as fp16 when it converts exactly
+                         // (set only when wpasses fits the register staging)
+  int32_t flag_lds;      // byte offset of 16 bytes of LDS for the workgroup's
+                         // agreement on the window encoding
   int32_t tiles_x, tiles_y, chunks, nblocks;
   uint32_t img_bytes;    // H*W*C*es
   uint32_t om_img_bytes; // Ho*Wo*G*3K*es
@@ -123,11 +127,15 @@ struct Plan {
   int32_t tile_passes;   // whole-image window: tile rows per workgroup (0: automatic)
   int32_t dp_user;       // 1: channels per lane set by the caller
   int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
+  int32_t f16_window;    // bf16 tiled forward: 1 = fp16 window when exact, 0 = never
   TileShape tile;
 };
 
 // Resolves p.tile from the plan's options (the tiled kernel's shape).
 void resolve_tile(Plan& p);
+// Whether the plan's tiled forward stages a bf16 window through registers
+// and re-encodes it as fp16 when every value converts exactly.
+bool tile_f16_window(const Plan& p);
 
 // Kernel-side entry points (dcn4_kernels.hip).  Arguments are validated by
 // the caller; these only shape and enqueue the launches.
@@ -158,9 +166,10 @@ uint32_t bucket_capacity(const Plan& p);
 // 0 when it does not apply.
 int32_t tiled_backward_lds(const Plan& p);
 // Arguments of the merged offset/weight linear layer (dcn4_linear.hip).
-// Offset/weight linear layer: the K-streamed kernel's workgroup owns
-// kLinearRows pixels and kLinearCols output columns (buffer offsets stay
-// 32-bit when (Nout + kLinearCols) * Cin * 2 < 2^31).
+// Offset/weight linear layer, size limit of its 32-bit buffer offsets: the
+// weight rows of every column block (Nout rounded up by kLinearCols) and
+// kLinearRows + 1 feature rows must stay below 2^31 bytes; both bound the
+// K-streamed kernel's blocks (128 pixels x 128 columns) from above.
 constexpr int kLinearRows = 256;
 constexpr int kLinearCols = 128;
 // Cin up to which each wave keeps its pixels' features in registers

@@ -455,6 +455,9 @@ void dcn4_forward_kernel(FwdArgs a) {
 // Both paths perform the same operations on the same values, so the result
 // does not depend on which path ran.
 typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+// F16W: the window holds the fp16 encoding of the bf16 input (see
+// stage_window_f16), so a corner value widens inside the fma (v_fma_mix_f32
+// takes an fp16 operand) instead of costing a shift or mask of its own.
 template <int DT, int VEC, int NV> struct LdsTap {
   u32x4 v[4][NV];
   // e00, e10: LDS addresses of the even slots of corners (y0, x0) and
@@ -471,6 +474,7 @@ template <int DT, int VEC, int NV> struct LdsTap {
         v[q][n] = *reinterpret_cast<lds_u32x4*>(
             (uintptr_t)(((n & 1) ? oa[q] : ea[q]) + 16 * (n & ~1)));
   }
+  template <bool F16W>
   __device__ __forceinline__ void accumulate(float* acc, const float* c) const {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -478,7 +482,9 @@ template <int DT, int VEC, int NV> struct LdsTap {
       for (int n = 0; n < NV; ++n)
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
-          acc[n * VEC + e] = __builtin_fmaf(c[q], Io<DT>::lane(v[q][n], e), acc[n * VEC + e]);
+          acc[n * VEC + e] = __builtin_fmaf(
+              c[q], F16W ? Io<DCN4_F16>::lane(v[q][n], e) : Io<DT>::lane(v[q][n], e),
+              acc[n * VEC + e]);
   }
 };
 
@@ -512,7 +518,7 @@ struct TileLane {
 // (the global path adds fma(0, 0, acc) = acc there, acc never being -0);
 // a non-finite weight still sends the wave to the global path, which
 // weights a corner outside the image by an exact 0 rather than m * w.
-template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ, bool WHOLE>
+template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ, bool WHOLE, bool F16W>
 __device__ __forceinline__ bool tile_point(const TileLane& w,
                                            float by, float bx, float gy, float gx,
                                            float dy, float dx, float m, float os,
@@ -556,7 +562,7 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
     d.load(a00, a10, a00 + w.odd, a10 + w.odd, PSC ? (uint32_t)PSC : w.ps);
   else
     d.load(a00, a10, a00, a10, PSC ? (uint32_t)PSC : w.ps);
-  d.accumulate(acc, cf);
+  d.template accumulate<F16W>(acc, cf);
   return true;
 }
 
@@ -640,6 +646,107 @@ __device__ __forceinline__ rsrc_t stage_window(const TileArgs& a, const TileOrig
   return xr;
 }
 
+// bf16 -> fp16 re-encoding of the tiled kernel's window.  The inner loop costs
+// an fma and a widening per bf16 corner value (a shift or a mask: no gfx950
+// fma takes a bf16 operand), but only an fma per fp16 value (v_fma_mix_f32
+// widens fp16 inside the fma).  A bf16 value is an fp16 value exactly when it
+// is zero or its magnitude lies in [2^-17, 65280]: its exponent is then one of
+// fp16's normal exponents or lands on fp16's subnormal grid (steps of 2^-24,
+// which the 7 fraction bits of 2^-17 just reach), and its 7 fraction bits fit
+// fp16's 10.  The window is restaged as fp16 only when every value of it is
+// such a value, so the sum sees the same fp32 operands either way.
+constexpr uint32_t kF16MagMax = 0x477fu;   // bf16 magnitude bits of 65280
+constexpr uint32_t kF16MagMin1 = 0x36ffu;  // bf16 magnitude bits of 2^-17, minus 1
+constexpr int kF16WinPasses = 10;          // staging passes held in registers
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Two bf16 values (low, high half) to two fp16 values; exact for the values
+// above (the rounding mode of the packed conversion never applies).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t u) {
+  const float lo = __uint_as_float(u << 16), hi = __uint_as_float(u & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// stage_window for bf16 windows of at most kF16WinPasses passes, through
+// registers: every thread loads its chunks, the workgroup agrees (one word
+// per wave at `flags`, 16 bytes of LDS, and a barrier) whether every staged
+// value converts exactly, and the window is written to LDS as fp16 if so,
+// as the unchanged bf16 bits if not.  Returns true when LDS holds fp16.  The
+// window's LDS writes are issued but not waited for: the caller's barrier
+// orders them before the first read.
+__device__ __forceinline__ bool stage_window_f16(const TileArgs& a, const TileOrigin& o,
+                                                 char* lds, rsrc_t xr, char* flags) {
+  const uint32_t t = threadIdx.x, lane = t & 63u;
+  const uint32_t pix_bytes = (uint32_t)a.C * 2u;
+  const uint32_t cvec = (uint32_t)a.PS >> 4;
+  const uint32_t rp = fastdiv(t, a.div_cpr);  // row within the pass
+  const uint32_t cc = t - rp * (uint32_t)a.cpr;
+  const uint32_t col = fastdiv(cc, a.div_cvec), ch = cc - col * cvec;
+  const int gcol = o.wx0 + (int)col;
+  const bool col_ok = ch < ((uint32_t)a.CB >> 4) && (uint32_t)gcol < (uint32_t)a.W;
+  const bool copies = rp < (uint32_t)a.wrpp;
+  const uint32_t row_bytes = (uint32_t)a.W * pix_bytes;
+  const int row0 = o.wy0 + (int)rp;
+  uint32_t off = (uint32_t)row0 * row_bytes + (uint32_t)gcol * pix_bytes +
+                 o.g0 * (uint32_t)(a.D * 2) + o.s * (uint32_t)a.CB + ch * 16u;
+  const uint32_t pass_bytes = (uint32_t)a.wrpp * row_bytes;
+  const int row_end = o.wy0 + a.WH;
+  // passes beyond wpasses are skipped by a scalar branch; a lane without a
+  // chunk in a pass loads zeros (out-of-range offset) and writes nothing
+  u32x4 v[kF16WinPasses];
+#pragma unroll
+  for (int p = 0; p < kF16WinPasses; ++p) {
+    v[p] = (u32x4){0u, 0u, 0u, 0u};
+    if (p < a.wpasses) {
+      const int row = row0 + p * a.wrpp;
+      const bool in = copies && col_ok && row < row_end && (uint32_t)row < (uint32_t)a.H;
+      v[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(in ? off : kOutside), 0, 0);
+    }
+    off += pass_bytes;
+  }
+  // largest magnitude, and smallest magnitude minus one (zero wraps to the
+  // largest), per half-word lane of the packed 16-bit operations
+  u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
+#pragma unroll
+  for (int p = 0; p < kF16WinPasses; ++p) {
+    if (p < a.wpasses) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u16x2 m = __builtin_bit_cast(u16x2, v[p][e] & 0x7fff7fffu);
+        mx = __builtin_elementwise_max(mx, m);
+        mn = __builtin_elementwise_min(mn, m + (u16x2){0xffff, 0xffff});
+      }
+    }
+  }
+  const bool ok = (uint32_t)__builtin_elementwise_max(mx.x, mx.y) <= kF16MagMax &&
+                  (uint32_t)__builtin_elementwise_min(mn.x, mn.y) >= kF16MagMin1;
+  const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  if (lane == 0)
+    *reinterpret_cast<lds_u32*>((uintptr_t)(__attribute__((address_space(3))) char*)(flags + (t >> 6) * 4u)) =
+        bad == 0 ? 1u : 0u;
+  __syncthreads();
+  const u32x4 f = *reinterpret_cast<lds_u32x4*>(
+      (uintptr_t)(__attribute__((address_space(3))) char*)flags);
+  const bool f16 = __builtin_amdgcn_readfirstlane((int)(f[0] & f[1] & f[2] & f[3])) != 0;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4_w;
+  const uint32_t dst0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds + t * 16u;
+  const uint32_t pass_lds = (uint32_t)(a.wrpp * a.cpr) * 16u;
+#pragma unroll
+  for (int p = 0; p < kF16WinPasses; ++p) {
+    if (p < a.wpasses) {
+      if (f16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[p][e] = bf16x2_to_f16x2(v[p][e]);
+      }
+      const int row = row0 + p * a.wrpp;
+      if (copies && row < row_end)
+        *reinterpret_cast<lds_u32x4_w*>((uintptr_t)(dst0 + (uint32_t)p * pass_lds)) = v[p];
+    }
+  }
+  return f16;
+}
+
 // Stage the tile's offset/weight values at `lds_om`.  Per tile pixel the
 // chunk's GB*3K values are OSU 4-byte units from the 4-byte boundary at or
 // below their start (rows are 4-byte aligned, so the lead `mis`, returned, is
@@ -721,6 +828,64 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
   return mis;
 }
 
+// The point loop of the tiled kernel: every point of the lane from LDS, or
+// from global memory for a wave with a point outside the window.  F16W: the
+// window holds fp16 (see stage_window_f16).
+template <int DT, int VEC, int NV, int MODE, int KS, int PSC, bool WHOLE, bool F16W>
+__device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa,
+                                            const LaneCtx& c, const TileLane& w,
+                                            const typename Io<DT>::raw* om, rsrc_t xr,
+                                            uint32_t r16, float ry0, float rx0, float* acc) {
+  typedef Io<DT> io;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  constexpr bool SQ = PSC != 0;
+  constexpr bool GS = MODE == kGroupScale;
+  if (KS) {
+    float bx[KS ? KS : 1];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) bx[j] = GS ? rx0 : rx0 + (float)(j * a.dw);
+    const float fdh = GS ? 0.0f : (float)a.dh;
+    float by = ry0;
+#pragma unroll
+    for (int i = 0; i < KS; ++i, by += fdh) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int k = i * KS + j;
+        const float dx = io::dec(om[2 * k]);
+        const float dy = io::dec(om[2 * k + 1]);
+        const float m = io::dec(om[2 * K + k]);
+        const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
+        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx[j], gyy, gxx, dy, dx,
+                                                           m, a.offset_scale, c.sg, acc)) {
+          const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
+          TapData<DT, VEC, NV> d;
+          d.load_swapped(xr, tg, r16);
+          d.accumulate(acc, tg);
+        }
+      }
+    }
+  } else {
+    const int kw = a.kw;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+      const int i = k / kw, j = k - (k / kw) * kw;
+      const float dx = io::dec(om[2 * k]);
+      const float dy = io::dec(om[2 * k + 1]);
+      const float m = io::dec(om[2 * K + k]);
+      const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
+      const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
+      const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
+      if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx, gyy, gxx, dy, dx, m,
+                                                         a.offset_scale, c.sg, acc)) {
+        const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
+        TapData<DT, VEC, NV> d;
+        d.load_swapped(xr, tg, r16);
+        d.accumulate(acc, tg);
+      }
+    }
+  }
+}
+
 template <int DT, int VEC, int NV, int MODE, int KS, int PSC, bool WHOLE>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
@@ -738,7 +903,20 @@ void dcn4_tile_kernel(TileArgs a) {
   const uint32_t t = threadIdx.x, lane = t & 63u;
   const uint32_t pix_bytes = (uint32_t)(a.C * es);
 
-  const rsrc_t xr = stage_window<es>(a, org, lds);
+  // bf16 windows of few enough passes go through registers and become fp16
+  // when every value converts exactly (stage_window_f16)
+  bool f16w = false;
+  rsrc_t xr;
+  if constexpr (DT == DCN4_BF16) {
+    if (a.f16_window) {
+      xr = make_rsrc(a.x + (uint64_t)org.n * a.img_bytes, a.img_bytes);
+      f16w = stage_window_f16(a, org, lds, xr, lds + a.flag_lds);
+    } else {
+      xr = stage_window<es>(a, org, lds);
+    }
+  } else {
+    xr = stage_window<es>(a, org, lds);
+  }
   const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   __syncthreads();
 
@@ -811,50 +989,13 @@ void dcn4_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
-    constexpr bool GS = MODE == kGroupScale;
-    if (KS) {
-      float bx[KS ? KS : 1];
-#pragma unroll
-      for (int j = 0; j < KS; ++j) bx[j] = GS ? rx0 : rx0 + (float)(j * a.dw);
-      const float fdh = GS ? 0.0f : (float)a.dh;
-      float by = ry0;
-#pragma unroll
-      for (int i = 0; i < KS; ++i, by += fdh) {
-#pragma unroll
-        for (int j = 0; j < KS; ++j) {
-          const int k = i * KS + j;
-          const float dx = io::dec(om[2 * k]);
-          const float dy = io::dec(om[2 * k + 1]);
-          const float m = io::dec(om[2 * K + k]);
-          const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-          if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE>(w, by, bx[j], gyy, gxx, dy, dx,
-                                                             m, a.offset_scale, c.sg, acc)) {
-            const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
-            TapData<DT, VEC, NV> d;
-            d.load_swapped(xr, tg, r16);
-            d.accumulate(acc, tg);
-          }
-        }
-      }
+    if constexpr (DT == DCN4_BF16) {
+      if (f16w)
+        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, true>(a, fa, c, w, om, xr, r16, ry0, rx0, acc);
+      else
+        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false>(a, fa, c, w, om, xr, r16, ry0, rx0, acc);
     } else {
-      const int kw = a.kw;
-#pragma unroll 1
-      for (int k = 0; k < K; ++k) {
-        const int i = k / kw, j = k - (k / kw) * kw;
-        const float dx = io::dec(om[2 * k]);
-        const float dy = io::dec(om[2 * k + 1]);
-        const float m = io::dec(om[2 * K + k]);
-        const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
-        const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
-        const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE>(w, by, bx, gyy, gxx, dy, dx, m,
-                                                           a.offset_scale, c.sg, acc)) {
-          const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
-          TapData<DT, VEC, NV> d;
-          d.load_swapped(xr, tg, r16);
-          d.accumulate(acc, tg);
-        }
-      }
+      tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false>(a, fa, c, w, om, xr, r16, ry0, rx0, acc);
     }
 
 #pragma unroll
@@ -2078,7 +2219,10 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   const int32_t osu = (ob + (p.es == 2 ? 2 : 0) + 3) / 4;
   if (osu > kBlock) return false;
   const int64_t win = (int64_t)wh * ww * ps;
-  const int64_t lds = ((win + 15) & ~int64_t(15)) + (int64_t)tp * osu * 4;
+  // window, offset/weight values, and (bf16) 16 bytes for the workgroup's
+  // agreement on the window encoding
+  const int64_t lds = ((win + 15) & ~int64_t(15)) + (int64_t)tp * osu * 4 +
+                      (d.dtype == DCN4_BF16 ? 16 : 0);
   if (lds > 64 * 1024) return false;
   t.ok = 1;
   t.dp = dp; t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww;
@@ -2160,6 +2304,14 @@ void resolve_tile(Plan& p) {
   else p.tile = tm;
 }
 
+bool tile_f16_window(const Plan& p) {
+  const TileShape& ts = p.tile;
+  if (!ts.ok || p.desc.dtype != DCN4_BF16 || !p.f16_window) return false;
+  const int32_t cpr = ts.ww * (ts.ps / 16);
+  const int32_t wrpp = kBlock / cpr;
+  return (ts.wh + wrpp - 1) / wrpp <= kF16WinPasses;
+}
+
 void fill_tile_args(const Plan& p, TileArgs& a) {
   const dcn4_desc& d = p.desc;
   const TileShape& ts = p.tile;
@@ -2192,6 +2344,8 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
     a.opasses = (ts.th * ts.tw + a.oppp - 1) / a.oppp;
   }
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
+  a.flag_lds = a.om_lds + ts.th * ts.tw * ts.osu * 4;
+  a.f16_window = tile_f16_window(p) ? 1 : 0;
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
   a.tiles_y = (p.Ho + ts.th * a.passes - 1) / (ts.th * a.passes);
   a.chunks = d.group / ts.gb * ts.slices;

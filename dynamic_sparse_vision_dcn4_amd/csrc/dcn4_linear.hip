@@ -16,10 +16,16 @@
 // row-major [M, Cin] and weight row-major [Nout, Cin] both fragments are one
 // 16-byte load of 8 consecutive inputs.
 //
-// Work: a workgroup owns 128 rows x 288 output columns; wave w computes rows
-// 32w..32w+31 against 9 column tiles of 32 (144 fp32 accumulators per lane).
-// The workgroups of one row block (its column chunks) are consecutive in the
-// XCD-aware order, so the second read of the block's features hits the L2.
+// Two kernels.  dcn4_linear_rs_kernel (Cin <= 384): 8 consumer waves each
+// keep 32 pixels' features in registers for all of Cin and walk the output
+// columns in passes of 64, while 4 producer waves stage each pass's weight
+// rows in LDS one pass ahead.  dcn4_linear_gemm_kernel (any other Cin that
+// is a multiple of 16): a K-streamed GEMM whose workgroup owns 128 pixels x
+// 128 output columns, four consumer waves of 64 x 64 multiplying one 64-wide
+// stage of features and weights while four producer waves copy the next
+// stage into LDS (two stages).  In both the workgroups of one pixel block
+// are consecutive in the XCD-aware order, so the block's features come from
+// HBM once and from L2 afterwards.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -121,7 +127,8 @@ constexpr int wait_vmcnt(int n) { return n | (7 << 4) | (15 << 8); }
 // XCD-aware order, so the block's features are read from HBM once and from
 // L2 afterwards.
 constexpr int kGmBM = 128, kGmBN = 128, kGmBK = 64;
-static_assert(kGmBM <= kLinearRows && kGmBN <= kLinearCols, "tile sizes the API checks");
+static_assert(kGmBM <= kLinearRows && kGmBN <= kLinearCols,
+              "the API's 32-bit offset limit covers one pixel block and one column block");
 constexpr int kGmCons = (kGmBM / 64) * (kGmBN / 64), kGmProd = 4;  // consumer and producer waves
 constexpr int kGmThreads = 64 * (kGmCons + kGmProd);
 constexpr int kGmStages = 2;
@@ -130,7 +137,7 @@ constexpr int kGmRowBytes = kGmBK * 2;                      // one staged row, 1
 constexpr int kGmFBytes = kGmBM * kGmRowBytes;              // features of a stage
 constexpr int kGmWBytes = kGmBN * kGmRowBytes;              // weights of a stage
 constexpr int kGmStageBytes = kGmFBytes + kGmWBytes;
-constexpr int kGmLdsBytes = kGmStages * kGmStageBytes;      // 147,456 B
+constexpr int kGmLdsBytes = kGmStages * kGmStageBytes;      // 65,536 B: two workgroups per CU
 // copies of 64 x 16 bytes (8 rows) per stage, and per producer wave
 constexpr int kGmFCopies = kGmFBytes / 1024, kGmWCopies = kGmWBytes / 1024;
 constexpr int kGmCopiesPerProd = (kGmFCopies + kGmWCopies) / kGmProd;
@@ -333,7 +340,9 @@ __global__ __launch_bounds__(kRsThreads) void dcn4_linear_rs_kernel(LinArgs a) {
     // Rows past Nout read as zeros (range check).
     const rsrc_t wr = lin_rsrc(a.weight, a.w_bytes);
     const rsrc_t br = lin_rsrc(a.bias, a.bias ? (uint32_t)a.Nout * 4u : 0u);
-    const int pw = wave - kRsConsumers;
+    // the producer index, made provably wave-uniform: the LDS destination of
+    // a buffer-to-LDS copy must be, or the compiler loops over its values
+    const int pw = __builtin_amdgcn_readfirstlane(wave - kRsConsumers);
     auto issue = [&](int p) {
       char* buf = lds + (p & 1) * L::kPassBytes;
       const int pass_off = p * 64 * L::Q * 16;

@@ -8,6 +8,8 @@
  *                  图像生成模型"
  *   [CANN Conv2D]  intelliparadigm "CANN ops-nn 算子与 Stable Diffusion 的卷积
  *                  实现"
+ *   [SD U-Net tutorial] framerc.cn "从ConvNet到Diffusion：手把手把DCNv4塞进
+ *                  Stable Diffusion的U-Net里试试效果"
  *
  * For every output pixel (n, yo, xo) and channel group g (G groups of
  * D = C/G channels), K = kernel_h*kernel_w points are sampled from the input
@@ -56,12 +58,16 @@
  *   y            [N, Ho, Wo, C]        I/O dtype
  *
  * Ownership and execution: the caller owns every buffer and the stream.  All
- * data pointers are device pointers.  The library allocates no device memory;
- * a plan holds host-side metadata only and is immutable after creation, so one
- * plan may be used from several host threads and streams at once.  Forward
- * calls are asynchronous on `stream` (a hipStream_t, NULL = the default
- * stream) and never synchronise; buffers must stay alive until the stream's
- * work has completed.  y must not overlap x or offset_mask.
+ * data pointers are device pointers.  No call allocates device memory except
+ * dcn4_backward, which takes its workspace with hipMallocAsync on the call's
+ * stream and returns it with hipFreeAsync (dcn4_backward_ws takes a
+ * caller-owned workspace instead); a plan holds host-side metadata only and
+ * is immutable after creation, so one plan may be used from several host
+ * threads and streams at once.  Calls are asynchronous on `stream` (a
+ * hipStream_t, NULL = the default stream) and never synchronise; buffers must
+ * stay alive until the stream's work has completed.  No output may overlap
+ * an input or another output of the same call: the byte ranges the plan
+ * implies are compared before launching (DCN4_ERR_INVALID_ARG).
  *
  * Errors: every call returns a status and never throws across the ABI.
  * Arguments are validated before anything is launched, so an error status
@@ -117,7 +123,12 @@ typedef struct {
 typedef struct dcn4_plan dcn4_plan; /* opaque, immutable after creation */
 
 /* Validates `desc`, chooses the kernel variant and launch shape, and returns
- * a plan in *plan (NULL on error).  Errors: DCN4_ERR_NULL (desc or plan NULL),
+ * a plan in *plan (NULL on error).  The descriptor carries the module
+ * arguments of the DCNv4 layer ([SD U-Net tutorial] 2.2: channels, kernel
+ * size, stride, pad, dilation, group) with the output size of the
+ * convolution index arithmetic ([CANN Conv2D] 2.1), plus FlowDCN's scale
+ * options ([FlowDCN] 3.1, 3.3).  The plan is owned by the caller until
+ * dcn4_destroy.  Errors: DCN4_ERR_NULL (desc or plan NULL),
  * DCN4_ERR_INVALID_ARG, DCN4_ERR_UNSUPPORTED (a single image's tensors beyond
  * 2^31 bytes), DCN4_ERR_NOMEM.  Makes no HIP call. */
 dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan);
@@ -163,6 +174,10 @@ typedef struct {
   int32_t tile_passes;       /* tiled forward: tile rows a workgroup takes
                                 under one staging of its window (1 for the
                                 margin window)                               */
+  int32_t tile_f16_window;   /* tiled bf16 forward: 1 when a workgroup
+                                re-encodes its window as fp16 whenever every
+                                value of it converts exactly (the fma then
+                                widens the value; other windows stay bf16)  */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -200,7 +215,12 @@ typedef enum {
   /* tiled forward under the whole-image window: tile rows each workgroup
    * computes from one staging of the image, 1-64 (at most the image's tile
    * rows); 0 = automatic (as many as keep four workgroups per CU) */
-  DCN4_OPT_TILE_PASSES = 8
+  DCN4_OPT_TILE_PASSES = 8,
+  /* tiled bf16 forward: 1 = a workgroup whose window values are all zero or
+   * of magnitude in [2^-17, 65280] (exactly representable in fp16) stages
+   * them as fp16, which its fp32 fmas widen for free; other windows stay
+   * bf16.  0 = always bf16.  Default 1. */
+  DCN4_OPT_TILE_F16_WINDOW = 9
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,
@@ -212,7 +232,11 @@ typedef enum {
 dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value);
 
 /* Enqueues the forward pass y = DCNv4(x, offset_mask[, group_scales]) on
- * `stream`.  group_scales must be non-NULL exactly when the plan uses group
+ * `stream`: the spatial aggregation defined at the top of this file ([DCNv4
+ * digest] section 1 and "方法1"; [FlowDCN] 3.1 in group-scale mode), on the
+ * channel-last layouts of [DCNv4 digest] "方法2".  x and offset_mask are read,
+ * y [N, Ho, Wo, C] is written and must not overlap them (DCN4_ERR_INVALID_ARG).
+ * group_scales must be non-NULL exactly when the plan uses group
  * scales.  Pointers must be aligned to the element size (4 B for fp32 and the
  * scales, 2 B otherwise); when x, offset_mask and y are 16-byte aligned and
  * D*es is a multiple of 16 the vectorised kernel runs, otherwise an
@@ -301,7 +325,8 @@ dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x,
  * fp32 [Nout] or NULL; products accumulated in fp32 on the matrix cores, the
  * sum plus bias rounded to `dtype` to nearest even.  Cin must be a multiple
  * of 16 (DCN4_ERR_UNSUPPORTED); feat and weight 16-byte aligned, offset_mask
- * 2-byte, bias 4-byte (DCN4_ERR_MISALIGNED).  M == 0 enqueues nothing.
+ * 2-byte, bias 4-byte (DCN4_ERR_MISALIGNED); offset_mask must not overlap
+ * feat, weight or bias (DCN4_ERR_INVALID_ARG).  M == 0 enqueues nothing.
  * Asynchronous on `stream`; the caller owns every buffer. */
 dcn4_status dcn4_offset_linear(const void* feat, const void* weight,
                                const float* bias, void* offset_mask, int64_t M,
@@ -319,7 +344,8 @@ dcn4_status dcn4_offset_linear(const void* feat, const void* weight,
  * per tap in row-major order, taps outside the image contributing nothing,
  * then the bias, one rounding to `dtype` (nearest even); the result does not
  * depend on the launch shape.  Pointers aligned to the element size (bias to
- * 4 bytes; DCN4_ERR_MISALIGNED); out must not alias x (DCN4_ERR_INVALID_ARG).
+ * 4 bytes; DCN4_ERR_MISALIGNED); out must not overlap x, weight or bias
+ * (DCN4_ERR_INVALID_ARG).
  * N == 0 enqueues nothing.  Asynchronous on `stream`; the caller owns every
  * buffer. */
 dcn4_status dcn4_dwconv3x3(const void* x, const void* weight, const float* bias,
@@ -339,7 +365,10 @@ dcn4_status dcn4_probe_geometry(const dcn4_plan* plan, const void* offset_mask,
                                 int32_t* x0, float* lh, float* lw,
                                 uint8_t* inside, void* stream);
 
-/* Frees the plan; NULL is allowed. */
+/* Frees a plan made by dcn4_create (the host-side description of one DCNv4
+ * layer, [SD U-Net tutorial] 2.2); NULL is allowed.  The caller must not
+ * destroy a plan while another thread is calling with it; work already
+ * enqueued does not use the plan. */
 void dcn4_destroy(dcn4_plan* plan);
 
 /* Static description of a status code. */

@@ -227,6 +227,35 @@ def test_tile_window_choice():
     assert e.value.status == d4.DCN4_ERR_UNSUPPORTED
 
 
+def test_f16_window_option():
+    """bf16 tiled plans re-encode their windows as fp16 by default when the
+    staging fits the kernel's register passes; other dtypes and the direct
+    kernel never do; the option switches it off and back."""
+    unet = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
+    assert unet.info()["tile_f16_window"] == 1
+    unet.set_option("tile_f16_window", 0)
+    assert unet.info()["tile_f16_window"] == 0
+    unet.set_option("tile_f16_window", 1)
+    assert unet.info()["tile_f16_window"] == 1
+    for bad in (-1, 2):
+        with pytest.raises(d4.DCN4Error) as e:
+            unet.set_option("tile_f16_window", bad)
+        assert e.value.status == d4.DCN4_ERR_INVALID_ARG
+    # FlowDCN's 24-channel slices: 48-byte window pixels, nine staging passes
+    fl = d4.Plan(desc_of(Shape(2, 32, 32, 1152, 16, multiscale=True), "bf16"))
+    assert fl.info()["tile_f16_window"] == 1
+    for dt in ("f16", "f32"):
+        p = d4.Plan(desc_of(Shape(2, 40, 40, 64, 4), dt), channels_per_lane=8 if dt == "f32" else 0)
+        assert p.info()["kernel"] == 2 and p.info()["tile_f16_window"] == 0
+    direct = d4.Plan(desc_of(Shape(2, 40, 40, 64, 4), "bf16"), kernel=1)
+    assert direct.info()["tile_f16_window"] == 0
+    # a window of more staging passes than the registers hold stays bf16
+    # (margin 16: 52 window rows, two to four per pass)
+    wide = d4.Plan(desc_of(Shape(1, 96, 96, 64, 4), "bf16"), tile_window=1, tile_margin=16)
+    i = wide.info()
+    assert i["kernel"] == 2 and i["tile_f16_window"] == 0
+
+
 def test_channels_per_lane_override():
     p = d4.Plan(desc_of(Shape(2, 8, 8, 64, 2), "bf16"))   # D = 32
     for dp in (8, 16, 32):
@@ -315,15 +344,50 @@ class TestForwardValidation:
         st, need = d4.dcn4_backward_workspace_size(self.p.handle)
         assert st == d4.DCN4_OK and need > 0
         assert d4.dcn4_backward_workspace_size(None)[0] == d4.DCN4_ERR_NULL
-        bws = lambda ws, nb, gx=1024, x=256: d4.dcn4_backward_ws(
-            self.p.handle, x, 256, None, None, 512, gx, 2048, ws, nb, None)
-        assert bws(4096, need - 1) == d4.DCN4_ERR_INVALID_ARG
-        assert bws(4096 + 16, need) == d4.DCN4_ERR_MISALIGNED
+        # fake device addresses 16 MiB apart: no two ranges overlap
+        M = 1 << 24
+        bws = lambda ws, nb, gx=4 * M, x=M: d4.dcn4_backward_ws(
+            self.p.handle, x, 2 * M, None, None, 3 * M, gx, 5 * M, ws, nb, None)
+        assert bws(8 * M, need - 1) == d4.DCN4_ERR_INVALID_ARG
+        assert bws(8 * M + 16, need) == d4.DCN4_ERR_MISALIGNED
         # the other arguments are checked first
-        assert bws(4096, need - 1, gx=1026) == d4.DCN4_ERR_MISALIGNED
-        assert bws(4096, need - 1, x=None) == d4.DCN4_ERR_NULL
-        assert d4.dcn4_backward_ws(None, 256, 256, None, None, 512, 1024, 2048, 4096, need,
+        assert bws(8 * M, need - 1, gx=4 * M + 2) == d4.DCN4_ERR_MISALIGNED
+        assert bws(8 * M, need - 1, x=None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_backward_ws(None, M, 2 * M, None, None, 3 * M, 4 * M, 5 * M, 8 * M, need,
                                    None) == d4.DCN4_ERR_NULL
+        # a workspace overlapping an input or an output
+        assert bws(2 * M, need) == d4.DCN4_ERR_INVALID_ARG
+        assert bws(4 * M + 256, need) == d4.DCN4_ERR_INVALID_ARG
+        assert bws(5 * M - 256, need) == d4.DCN4_ERR_INVALID_ARG
+
+    def test_overlapping_outputs_rejected(self):
+        """No output may overlap an input or another output of the call (the
+        byte ranges the plan implies); adjacent ranges are fine, so the
+        rejection is the overlap itself."""
+        M = 1 << 24
+        p = self.p                                    # 2x16x16x64 bf16: 64 KiB tensors
+        nx = 2 * 16 * 16 * 64 * 2
+        fwd = lambda x, om, y: d4.dcn4_forward(p.handle, x, om, None, y, None)
+        assert fwd(M, 2 * M, M + nx - 16) == d4.DCN4_ERR_INVALID_ARG      # y inside x
+        assert fwd(M, 2 * M, M - nx + 16) == d4.DCN4_ERR_INVALID_ARG      # y's end inside x
+        assert fwd(M, 2 * M, 2 * M + 4096) == d4.DCN4_ERR_INVALID_ARG     # y inside offset_mask
+        ms = self.ms
+        assert d4.dcn4_forward(ms.handle, M, 2 * M, 3 * M, 3 * M - 16, None) == \
+            d4.DCN4_ERR_INVALID_ARG                                       # y over the scales
+        bw = lambda x, om, gy, gx, gom: d4.dcn4_backward_ws(p.handle, x, om, None, None, gy,
+                                                            gx, gom, None, 0, None)
+        assert bw(M, 2 * M, 3 * M, M + 64, None) == d4.DCN4_ERR_INVALID_ARG   # grad_x over x
+        assert bw(M, 2 * M, 3 * M, None, 3 * M) == d4.DCN4_ERR_INVALID_ARG    # grad_om over grad_y
+        assert bw(M, 2 * M, 3 * M, 4 * M, 4 * M + 1024) == d4.DCN4_ERR_INVALID_ARG  # each other
+        lin = lambda f, w, b, o: d4.dcn4_offset_linear(f, w, b, o, 1000, 64, 108,
+                                                       d4.DCN4_BF16, None)
+        assert lin(M, 2 * M, None, M + 1024) == d4.DCN4_ERR_INVALID_ARG      # over feat
+        assert lin(M, 2 * M, None, 2 * M - 1000) == d4.DCN4_ERR_INVALID_ARG  # over weight
+        assert lin(M, 2 * M, 3 * M, 3 * M - 64) == d4.DCN4_ERR_INVALID_ARG   # over bias
+        dw = lambda x, w, b, o: d4.dcn4_dwconv3x3(x, w, b, o, 2, 16, 16, 64, d4.DCN4_BF16, None)
+        assert dw(M, 2 * M, None, M + nx // 2) == d4.DCN4_ERR_INVALID_ARG    # over x
+        assert dw(M, 2 * M, None, 2 * M - 64) == d4.DCN4_ERR_INVALID_ARG     # over the weight
+        assert dw(M, 2 * M, 3 * M, 3 * M) == d4.DCN4_ERR_INVALID_ARG         # over the bias
 
     def test_backward_workspace_size(self):
         """The documented layout: a 256-byte counter, 4 bytes per (cell,
@@ -495,3 +559,78 @@ int main() {
                     str(src), "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout
+
+
+class TestBindingChecks:
+    """The Python binding checks every tensor before a pointer reaches the C
+    ABI (which sees no sizes): dtype, exact shape, contiguity, then device.
+    CPU tensors exercise every check up to the device one."""
+
+    def setup_method(self):
+        import torch
+        self.torch = torch
+        self.plan = d4.Plan(mk(N=2, H=8, W=6, C=32, group=2))   # x [2,8,6,32]
+
+    def test_forward_tensor_checks(self):
+        torch = self.torch
+        x = torch.zeros((2, 8, 6, 32), dtype=torch.bfloat16)
+        om = torch.zeros(self.plan.om_shape(), dtype=torch.bfloat16)
+        with pytest.raises(TypeError, match="x must be torch.bfloat16"):
+            self.plan.forward(x.float(), om)
+        # same element count, transposed [N, W, H, C]: rejected by shape
+        with pytest.raises(ValueError, match="x must have shape"):
+            self.plan.forward(torch.zeros((2, 6, 8, 32), dtype=torch.bfloat16), om)
+        with pytest.raises(ValueError, match="x must be contiguous"):
+            self.plan.forward(x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3), om)
+        with pytest.raises(ValueError, match="offset_mask must have shape"):
+            self.plan._check(om.view(2, 8, 6, -1), self.plan.om_shape(), torch.bfloat16,
+                             "offset_mask")
+        with pytest.raises(TypeError, match="x must be a CUDA tensor"):
+            self.plan.forward(x, om)
+        with pytest.raises(TypeError, match="torch tensor"):
+            self.plan.forward(x.float().numpy(), om)
+
+    def test_backward_tensor_checks(self):
+        torch = self.torch
+        x = torch.zeros((2, 8, 6, 32), dtype=torch.bfloat16)
+        om = torch.zeros(self.plan.om_shape(), dtype=torch.bfloat16)
+        gy = torch.zeros(self.plan.out_shape(), dtype=torch.float16)
+        with pytest.raises(TypeError, match="x must be a CUDA tensor"):
+            self.plan.backward(x, om, gy.bfloat16())
+        p16 = d4.Plan(mk(N=2, H=8, W=6, C=32, group=2, dtype="f16"))
+        with pytest.raises(TypeError, match="grad_y must be torch.float16"):
+            # reaches grad_y only after x and offset_mask pass their CPU-side checks
+            p16._check(gy.bfloat16(), p16.out_shape(), torch.float16, "grad_y")
+
+    def test_producer_tensor_checks(self):
+        """offset_linear and dwconv3x3 check feat/x first (shape, dtype,
+        device), then weight, bias and out against it with the same helper;
+        on the CPU the first tensor stops at the device check, so the helper
+        is exercised directly for the others."""
+        torch = self.torch
+        feat = torch.zeros((100, 64), dtype=torch.bfloat16)
+        w = torch.zeros((108, 64), dtype=torch.bfloat16)
+        with pytest.raises(TypeError, match="feat must be a CUDA tensor"):
+            d4.offset_linear(feat, w)
+        with pytest.raises(TypeError, match="feat must be bf16 or fp16"):
+            d4.offset_linear(feat.float(), w)
+        with pytest.raises(ValueError, match="feat must be a 2-d tensor"):
+            d4.offset_linear(feat.view(10, 10, 64), w)
+        with pytest.raises(ValueError, match="weight must have shape"):
+            d4._require(torch.zeros((108, 32), dtype=torch.bfloat16), (108, 64),
+                        torch.bfloat16, "weight")
+        with pytest.raises(TypeError, match="bias must be torch.float32"):
+            d4._require(torch.zeros(108, dtype=torch.bfloat16), (108,), torch.float32, "bias")
+        with pytest.raises(ValueError, match="out must have shape"):
+            d4._require(torch.zeros((100, 54), dtype=torch.bfloat16), (100, 108),
+                        torch.bfloat16, "out")
+        with pytest.raises(TypeError, match="out must be a CUDA tensor"):
+            d4._require(torch.zeros((100, 108), dtype=torch.bfloat16), (100, 108),
+                        torch.bfloat16, "out")
+        x = torch.zeros((2, 8, 6, 32), dtype=torch.float16)
+        with pytest.raises(TypeError, match="x must be a CUDA tensor"):
+            d4.dwconv3x3(x, torch.zeros((3, 3, 32), dtype=torch.float16))
+        with pytest.raises(ValueError, match="x must be a 4-d tensor"):
+            d4.dwconv3x3(x[0], torch.zeros((3, 3, 32), dtype=torch.float16))
+        with pytest.raises(TypeError, match="x must be fp32, bf16 or fp16"):
+            d4.dwconv3x3(x.to(torch.int16), torch.zeros((3, 3, 32), dtype=torch.float16))

@@ -559,6 +559,54 @@ def test_nonfinite_values_propagate_like_the_oracle():
     check_against_oracle(y, o.forward_f32(s, dt, inp.x, inp.om, None), dt, "non-finite")
 
 
+# bf16 bit patterns at the edges of exact fp16 representability: a window
+# holding only values of the first list is re-encoded as fp16, one holding any
+# of the second stays bf16 (zero, magnitudes in [2^-17, 65280]; below 2^-17,
+# above 65280, bf16 subnormals, inf, NaN)
+F16_OK = [0x3700, 0xB700, 0x477F, 0xC77F, 0x8000, 0x0000, 0x3701, 0x387F, 0x3880]
+F16_NOT = [0x36FF, 0xB6FF, 0x4780, 0xC780, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC0]
+# (shape, plan options): the margin window with whole groups, the whole-image
+# window, and FlowDCN's 24-channel slices in group-scale mode
+F16_CASES = [(Shape(2, 40, 36, 64, 4), {"tile_window": 1}),
+             (Shape(2, 20, 22, 64, 4), {"tile_window": 2}),
+             (Shape(1, 33, 35, 144, 2, multiscale=True), {"tile_window": 1})]
+
+
+@pytest.mark.parametrize("case", range(len(F16_CASES)))
+def test_f16_window_boundaries(case):
+    """bf16 windows whose values all convert exactly are staged as fp16; any
+    other window stays bf16.  Values at both sides of the boundaries
+    (2^-17, 65280, subnormals, inf, NaN) are planted in some tiles' windows
+    and not in others, so both encodings run in one launch; the output
+    equals the oracle's and the plan without the re-encoding bit for bit."""
+    s, opts = F16_CASES[case]
+    dt = "bf16"
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=300 + case)
+    x = inp.x.view(np.uint16)
+    rng = np.random.default_rng(400 + case)
+    # the representable values anywhere; the others in the first image only,
+    # in its top-left quarter, so that tiles of both kinds exist
+    for v in F16_OK:
+        n, yy, xx, c = (rng.integers(0, d) for d in x.shape)
+        x[n, yy, xx, c] = v
+    for v in F16_NOT:
+        yy, xx = rng.integers(0, max(s.H // 4, 1)), rng.integers(0, max(s.W // 4, 1))
+        x[0, yy, xx, rng.integers(0, s.C)] = v
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
+    outs = []
+    for f16w in (1, 0):
+        plan = d4.Plan(desc_of(s, dt), kernel=2, tile_f16_window=f16w, **opts)
+        info = plan.info()
+        say(f"f16 window case {case} ({f16w}): {s} {info}")
+        assert info["tile_f16_window"] == f16w
+        y = gpu_forward(plan, inp, dt)
+        check_against_oracle(y, y_or, dt, f"f16 window case {case} option {f16w}")
+        outs.append(y)
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_repeatable_and_stream_independent():
     w = WORKLOADS["dcn4_small_f32"].with_(N=4, H=33, W=29)
     s = shape_of(w)
