@@ -105,6 +105,7 @@ _lib.dcn4_forward_scaled.argtypes = [_P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward_ws.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P]
+_lib.dcn4_backward_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward_workspace_size.argtypes = [_P, ctypes.POINTER(ctypes.c_uint64)]
 _lib.dcn4_offset_linear.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, _P]
@@ -118,7 +119,7 @@ _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
-           "dcn4_probe_geometry", "dcn4_backward", "dcn4_backward_ws",
+           "dcn4_probe_geometry", "dcn4_backward", "dcn4_backward_ws", "dcn4_backward_noalloc",
            "dcn4_backward_workspace_size", "dcn4_offset_linear",
            "dcn4_dwconv3x3"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -176,6 +177,13 @@ def dcn4_backward_ws(plan, x: int, offset_mask: int, group_scales: Optional[int]
                      workspace_bytes: int, stream: Optional[int]) -> int:
     return _lib.dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y,
                                  grad_x, grad_offset_mask, workspace, workspace_bytes, stream)
+
+
+def dcn4_backward_noalloc(plan, x: int, offset_mask: int, group_scales: Optional[int],
+                          pixel_scales: Optional[int], grad_y: int, grad_x: Optional[int],
+                          grad_offset_mask: Optional[int], stream: Optional[int]) -> int:
+    return _lib.dcn4_backward_noalloc(plan, x, offset_mask, group_scales, pixel_scales,
+                                      grad_y, grad_x, grad_offset_mask, stream)
 
 
 def dcn4_backward_workspace_size(plan):

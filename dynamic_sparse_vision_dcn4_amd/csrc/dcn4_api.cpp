@@ -465,6 +465,33 @@ dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
   return s;
 }
 
+dcn4_status dcn4_backward_noalloc(const dcn4_plan* plan, const void* x,
+                                  const void* offset_mask, const float* group_scales,
+                                  const float* pixel_scales, const void* grad_y,
+                                  float* grad_x, float* grad_offset_mask, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  const uint64_t need = dcn4::backward_workspace_bytes(p);
+  // only the gathered grad_x uses a workspace; without it this is dcn4_backward_ws
+  if (!grad_x || !need || p.desc.N == 0)
+    return dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                            grad_offset_mask, nullptr, 0, stream);
+  dcn4_status s = check_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                                 grad_offset_mask);
+  if (s != DCN4_OK) return s;
+  if (need > dcn4::kScratchBytes)
+    return fail(DCN4_ERR_UNSUPPORTED,
+                "the gathered grad_x needs more workspace than the library's 64 MiB static "
+                "scratch: call dcn4_backward_ws with a workspace of "
+                "dcn4_backward_workspace_size bytes");
+  void* ws = nullptr;
+  s = dcn4::scratch_address(&ws);
+  if (s != DCN4_OK) return fail(s, s == DCN4_ERR_HIP ? dcn4::last_hip_error()
+                                                     : "device index beyond 63");
+  return dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                          grad_offset_mask, ws, need, stream);
+}
+
 dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float* bias,
                                void* offset_mask, int64_t M, int32_t Cin, int32_t Nout,
                                int32_t dtype, void* stream) {

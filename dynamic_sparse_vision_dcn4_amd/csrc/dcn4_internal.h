@@ -160,6 +160,10 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
 // Workspace of the gathered grad_x (0: a single image's indices exceed the
 // kernels' 32-bit counters, so only the atomic path applies).
 uint64_t backward_workspace_bytes(const Plan& p);
+// The static device workspace of dcn4_backward_noalloc: its size, and its
+// address on the current device (looked up once per device).
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+dcn4_status scratch_address(void** ptr);
 // Records per bucket the plan's gathered grad_x uses.
 uint32_t bucket_capacity(const Plan& p);
 // LDS bytes of the tiled backward (offset/weight gradients only) for the plan,

@@ -39,6 +39,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "dcn4_internal.h"
 
 namespace dcn4 {
@@ -2771,6 +2773,41 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
 uint64_t backward_workspace_bytes(const Plan& p) {
   const GatherShape s = gather_shape(p);
   return s.ok ? s.bytes : 0;
+}
+
+// The library's own workspace for callers that cannot allocate
+// (dcn4_backward_noalloc): one static device array per GPU, kScratchBytes
+// long, held from module load until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); it looks up the array's device address once per device with
+// hipGetSymbolAddress, with that device current, and uses that address.
+namespace {
+__device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+dcn4_status scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    note_hip_error(e);
+    return DCN4_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DCN4_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !q) {
+      note_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return DCN4_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = q;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DCN4_OK;
 }
 
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,

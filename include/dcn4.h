@@ -315,6 +315,23 @@ dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x,
                              void* workspace, uint64_t workspace_bytes,
                              void* stream);
 
+/* dcn4_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the gathered grad_x takes its workspace from a static device array of the
+ * library, 64 MiB per GPU, held from the library's load until the process
+ * ends; the call allocates nothing.  Problems whose workspace
+ * (dcn4_backward_workspace_size) exceeds 64 MiB are refused with
+ * DCN4_ERR_UNSUPPORTED before anything is enqueued (use dcn4_backward_ws).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or threads without ordering) race and give
+ * wrong gradients; calls ordered on one stream are safe.  The array's
+ * counters are cleared by a kernel at the start of each call.  Arguments,
+ * results, validation and other errors as dcn4_backward. */
+dcn4_status dcn4_backward_noalloc(const dcn4_plan* plan, const void* x,
+                                  const void* offset_mask, const float* group_scales,
+                                  const float* pixel_scales, const void* grad_y,
+                                  float* grad_x, float* grad_offset_mask, void* stream);
+
 /* The producer of the offset/weight tensor: the merged linear layer of
  * [DCNv4 digest] "方法3" (offsets and weights from one linear layer),
  *   offset_mask[r, j] = sum_k feat[r, k] * weight[j, k] + bias[j],

@@ -360,6 +360,25 @@ class TestForwardValidation:
         assert bws(4 * M + 256, need) == d4.DCN4_ERR_INVALID_ARG
         assert bws(5 * M - 256, need) == d4.DCN4_ERR_INVALID_ARG
 
+    def test_noalloc_refuses_beyond_its_scratch(self):
+        """dcn4_backward_noalloc gathers grad_x in the library's static 64 MiB
+        workspace: a problem needing more is refused before anything is
+        enqueued, with a message naming the entry point to use instead."""
+        G1 = 1 << 30   # fake device addresses 1 GiB apart: no overlap
+        big = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
+        assert big.backward_workspace_bytes() > (64 << 20)
+        st = d4.dcn4_backward_noalloc(big.handle, G1, 2 * G1, None, None, 3 * G1, 4 * G1,
+                                      5 * G1, None)
+        assert st == d4.DCN4_ERR_UNSUPPORTED
+        assert "dcn4_backward_ws" in d4.dcn4_last_error()
+        # argument errors come first, as in dcn4_backward
+        assert d4.dcn4_backward_noalloc(big.handle, G1 + 1, 2 * G1, None, None, 3 * G1, 4 * G1,
+                                        5 * G1, None) == d4.DCN4_ERR_MISALIGNED
+        assert d4.dcn4_backward_noalloc(None, G1, 2 * G1, None, None, 3 * G1, 4 * G1, 5 * G1,
+                                        None) == d4.DCN4_ERR_NULL
+        assert d4.dcn4_backward_noalloc(big.handle, G1, 2 * G1, None, None, 3 * G1, G1 + 64,
+                                        5 * G1, None) == d4.DCN4_ERR_INVALID_ARG
+
     def test_overlapping_outputs_rejected(self):
         """No output may overlap an input or another output of the call (the
         byte ranges the plan implies); adjacent ranges are fine, so the
