@@ -96,6 +96,7 @@ class Oracle:
                                        P, ctypes.c_int64]
         lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, P, i64p, i64p]
         lib.dcn4o_backward.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P, i64p]
+        lib.dcn4o_backward_scales.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P]
         lib.dcn4o_linear_f64.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int, P, P, P, P, P]
         lib.dcn4o_dwconv3x3.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -242,6 +243,26 @@ class Oracle:
         if r:
             raise ValueError("oracle rejected the call")
         out["max_terms"] = mt.value
+        return out
+
+    def backward_scales(self, s: Shape, dtype: str, x, om, gy, scales, pscales=None):
+        """Gradients of the group scales (group-scale mode) for upstream gy
+        [N,Ho,Wo,C] (raw, I/O dtype): dict with gs [G] (dL/ds_g), gs_abs, and
+        with pixel scales gp [N,Ho,Wo,G] (dL/dsigma), gp_abs; fp64."""
+        dt, x, om, scales, pscales = self._prep(s, dtype, x, om, scales, pscales)
+        gy = np.ascontiguousarray(gy, dtype=RAW_NP[dt])
+        ho, wo = self.out_size(s)
+        out = {"gs": np.empty(s.G, np.float64), "gs_abs": np.empty(s.G, np.float64)}
+        if s.pixel_scales:
+            out["gp"] = np.empty((s.N, ho, wo, s.G), np.float64)
+            out["gp_abs"] = np.empty_like(out["gp"])
+        r = self.lib.dcn4o_backward_scales(ctypes.byref(s.c_struct()), dt, self._ptr(x),
+                                           self._ptr(om), self._ptr(scales), self._ptr(pscales),
+                                           self._ptr(gy), self._ptr(out["gs"]),
+                                           self._ptr(out["gs_abs"]), self._ptr(out.get("gp")),
+                                           self._ptr(out.get("gp_abs")))
+        if r:
+            raise ValueError("oracle rejected the call")
         return out
 
     def linear(self, dtype: str, feat, weight, bias=None):

@@ -571,6 +571,88 @@ int dcn4o_backward(const dcn4o_shape* s, int dtype, const void* x, const void* o
   return 0;
 }
 
+/* --------------------------------------------------- gradients of the scales
+ * Group-scale mode only (reading R17).  Point k of group g at output pixel p
+ * samples centre + S * u_k on each axis, u_k = fl(grid_k + d_k) the fp32
+ * value the evaluation multiplies by the effective scale S (R8, R13), so
+ *   dL/dS[p,g] = sum_k m_k * (u_y,k * sum_c gy * dB_c/drow
+ *                            + u_x,k * sum_c gy * dB_c/dcol)
+ * over the inside samples, with the cell, fractions and inside test of the
+ * fp32 evaluation and fp64 arithmetic after them, as in dcn4o_backward.
+ * Below the clamp S = s_g * sigma[p,g] (sigma = 1 without pixel scales):
+ *   dL/dsigma[p,g] = s_g * dL/dS[p,g],  dL/ds_g = sum_p sigma[p,g] * dL/dS[p,g];
+ * where the evaluation clamps (fl(s_g * sigma) > Smax) S is the constant Smax
+ * and both derivatives are 0; at equality S is not clamped.  A NaN S puts no
+ * sample inside: zero gradient.
+ * gs, gs_abs [G] (nullable): dL/ds_g and its sum of absolute terms;
+ * gp, gp_abs [N,Ho,Wo,G] (nullable; plans with pixel scales): dL/dsigma and
+ * its sum of absolute terms. */
+int dcn4o_backward_scales(const dcn4o_shape* s, int dtype, const void* x, const void* om,
+                          const float* scales, const float* pscales, const void* gy,
+                          double* gs, double* gs_abs, double* gp, double* gp_abs) {
+  int32_t Ho, Wo;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  if (!s->multiscale || (gp && !s->pixel_scales)) return -1;
+  const int K = s->kh * s->kw, G = s->G, C = s->C, D = C / G;
+  const int H = s->H, W = s->W;
+  const int hy = (s->kh - 1) / 2, hx = (s->kw - 1) / 2;
+  const int64_t npx = (int64_t)s->N * Ho * Wo;
+  for (int g = 0; g < G; ++g) {
+    if (gs) gs[g] = 0.0;
+    if (gs_abs) gs_abs[g] = 0.0;
+  }
+  for (int64_t p = 0; p < npx; ++p) {
+    int n = (int)(p / ((int64_t)Ho * Wo));
+    int yo = (int)((p / Wo) % Ho);
+    int xo = (int)(p % Wo);
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = (p * G + g) * 3 * K;
+      const float sg = scale_f32(s, scales, pscales, p, g);
+      float sun = scales[g];
+      if (s->pixel_scales) sun = sun * pscales[p * G + g];
+      const int clamped = s->max_scale > 0.0f && sun > s->max_scale;
+      const double sig = s->pixel_scales ? (double)pscales[p * G + g] : 1.0;
+      double dS = 0.0, aS = 0.0;
+      for (int k = 0; k < K; ++k) {
+        int i = k / s->kw, j = k % s->kw;
+        float dx = load_f32(dtype, om, row + 2 * k);
+        float dy = load_f32(dtype, om, row + 2 * k + 1);
+        double m = load_f32(dtype, om, row + 2 * K + k);
+        geom_t q = sample_geometry_f32(s, yo, xo, i, j, dx, dy, sg);
+        if (!q.inside) continue;
+        const double uy = (float)(i - hy) + dy; /* the fp32 value grid + direction */
+        const double ux = (float)(j - hx) + dx;
+        const double lh = q.lh, lw = q.lw, hh = 1.0 - lh, hw = 1.0 - lw;
+        const int cy[4] = {q.y0, q.y0, q.y0 + 1, q.y0 + 1};
+        const int cx[4] = {q.x0, q.x0 + 1, q.x0, q.x0 + 1};
+        double gdr = 0.0, gdc = 0.0, adr = 0.0, adc = 0.0;
+        for (int d = 0; d < D; ++d) {
+          const int c = g * D + d;
+          const double gyc = load_f32(dtype, gy, p * C + c);
+          double v[4];
+          for (int r = 0; r < 4; ++r) {
+            int ok = cy[r] >= 0 && cy[r] < H && cx[r] >= 0 && cx[r] < W;
+            v[r] = ok ? (double)load_f32(dtype, x, (((int64_t)n * H + cy[r]) * W + cx[r]) * C + c)
+                      : 0.0;
+          }
+          gdr += gyc * (hw * (v[2] - v[0]) + lw * (v[3] - v[1]));
+          gdc += gyc * (hh * (v[1] - v[0]) + lh * (v[3] - v[2]));
+          adr += fabs(gyc) * (hw * (fabs(v[2]) + fabs(v[0])) + lw * (fabs(v[3]) + fabs(v[1])));
+          adc += fabs(gyc) * (hh * (fabs(v[1]) + fabs(v[0])) + lh * (fabs(v[3]) + fabs(v[2])));
+        }
+        dS += m * (uy * gdr + ux * gdc);
+        aS += fabs(m) * (fabs(uy) * adr + fabs(ux) * adc);
+      }
+      if (clamped) dS = aS = 0.0;
+      if (gp) gp[p * G + g] = (double)scales[g] * dS;
+      if (gp_abs) gp_abs[p * G + g] = fabs((double)scales[g]) * aS;
+      if (gs) gs[g] += sig * dS;
+      if (gs_abs) gs_abs[g] += fabs(sig) * aS;
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------- merged offset/weight layer
  * The producer of the offset/weight tensor: one linear layer maps every
  * pixel's Cin features to its G*3K offsets and weights ([DCNv4 digest]

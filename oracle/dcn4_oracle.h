@@ -112,6 +112,19 @@ int dcn4o_backward(const dcn4o_shape* s, int dtype, const void* x,
                    const void* gy, double* gx, double* gom, double* gx_abs,
                    double* gom_abs, int64_t* max_terms);
 
+/* Gradients of the group scales (group-scale mode): gs [G] = dL/ds_g and,
+ * for plans with pixel scales, gp [N,Ho,Wo,G] = dL/dsigma, both fp64 and
+ * nullable, for an upstream gradient gy; the location moves by
+ * u = fl(grid + direction) per unit of the effective scale, which is
+ * s_g * sigma below the clamp and the constant Smax above it.  Sampling
+ * decisions of the fp32 evaluation, fp64 arithmetic after them; gs_abs and
+ * gp_abs (nullable) receive the sums of the absolute values of the terms.
+ * 0, or -1 for a plan without group scales (or gp without pixel scales). */
+int dcn4o_backward_scales(const dcn4o_shape* s, int dtype, const void* x,
+                          const void* om, const float* scales, const float* pscales,
+                          const void* gy, double* gs, double* gs_abs, double* gp,
+                          double* gp_abs);
+
 /* The merged linear layer that produces the offset/weight tensor
  * ([DCNv4 digest] "方法3"): out[r, j] = sum_k feat[r, k] * weight[j, k] +
  * bias[j], feat [M, Cin] and weight [Nout, Cin] in the I/O dtype, bias fp32

@@ -565,6 +565,84 @@ def pin_backward_offsets(o):
                 exact_equal(got[..., 2 * k + axis], want, f"dL/d offset tap {k} axis {axis} {s}")
 
 
+def _scale_grad_inputs(o, s, seed, S):
+    """dyadic inputs whose samples sit at fractions 1/4, 1/2 or 3/4 of their
+    cells for the effective scale S [N,Ho,Wo,G] (powers of two): the scaled
+    displacement t = S*(grid + d) is chosen first, then d = t/S - grid."""
+    rng = np.random.default_rng(seed)
+    ho, wo = o.out_size(s)
+    K = s.K
+    x = dyadic(rng, (s.N, s.H, s.W, s.C), -2, 2, 8)
+    gy = dyadic(rng, (s.N, ho, wo, s.C), -2, 2, 8)
+    m = dyadic(rng, (s.N, ho, wo, s.G, K), -1, 1, 8)
+    grid_y = (np.arange(K) // s.kw - (s.kh - 1) // 2).astype(np.float32)
+    grid_x = (np.arange(K) % s.kw - (s.kw - 1) // 2).astype(np.float32)
+    St = S[..., None]
+    shape = (s.N, ho, wo, s.G, K)
+    ty = rng.integers(-3, 3, size=shape) + rng.integers(1, 4, size=shape) / 4.0
+    tx = rng.integers(-3, 3, size=shape) + rng.integers(1, 4, size=shape) / 4.0
+    dy = (ty / St - grid_y).astype(np.float32)
+    dx = (tx / St - grid_x).astype(np.float32)
+    return x, pack_om(dx, dy, m), gy
+
+
+def pin_backward_scales(o):
+    """Gradients of FlowDCN's scales (reading R17): inside its cell the
+    bilinear sample is a polynomial of degree 2 in a step h of the scale
+    (both coordinates move by h*(grid + direction)), so the symmetric
+    difference (L(s + h) - L(s - h)) / 2h of the loss L = <gy, y> is exactly
+    its derivative on dyadic inputs with every sample kept in its cell:
+    (a) per group prior s_g, with some groups above the clamp Smax (their
+        effective scale is the constant Smax: derivative 0);
+    (b) the predicted per-pixel scales along a random dyadic direction v:
+        the difference equals sum dL/dsigma * v, pixels above the clamp
+        included (zero there), and the prior's gradient sums sigma * dL/dS."""
+    h = 2.0 ** -6
+    loss = lambda s_, x, om, gy, sc, ps=None: float(np.sum(
+        gy.astype(np.float64) * o.forward_f64(s_, "f32", x, om, sc, nthreads=2, pscales=ps)))
+    # (a) group priors, groups 2 and 3 clamped (s_g = 4 > Smax = 2); no
+    # prior at the clamp itself, where the derivative is one-sided
+    s = Shape(2, 7, 8, 8, 4, multiscale=True, max_scale=2.0)
+    ho, wo = o.out_size(s)
+    sg = np.array([1.0, 0.5, 4.0, 4.0], np.float32)
+    S = np.broadcast_to(np.minimum(sg, 2.0), (s.N, ho, wo, s.G)).astype(np.float32)
+    x, om, gy = _scale_grad_inputs(o, s, 51, S)
+    got = o.backward_scales(s, "f32", x, om, gy, sg)["gs"]
+    for g in range(s.G):
+        up, dn = sg.copy(), sg.copy()
+        up[g] += np.float32(h)
+        dn[g] -= np.float32(h)
+        want = (loss(s, x, om, gy, up) - loss(s, x, om, gy, dn)) / (2 * h)
+        assert got[g] == want, f"dL/ds_g group {g}: {got[g]} != {want}"
+    assert got[2] == 0.0 and got[3] == 0.0
+    # (b) pixel scales: sigma in {1/2, 1, 2}, priors 1/2 and 8, Smax 2: group
+    # 0 below the clamp (S <= 1), group 1 above it (S = 2)
+    s = Shape(2, 6, 7, 8, 2, multiscale=True, pixel_scales=True, max_scale=2.0)
+    ho, wo = o.out_size(s)
+    rng = np.random.default_rng(52)
+    sg = np.array([0.5, 8.0], np.float32)
+    sig = np.ldexp(np.ones((s.N, ho, wo, s.G), np.float32),
+                   rng.integers(-1, 2, size=(s.N, ho, wo, s.G))).astype(np.float32)
+    S = np.minimum(sg * sig, 2.0).astype(np.float32)
+    x, om, gy = _scale_grad_inputs(o, s, 53, S)
+    r = o.backward_scales(s, "f32", x, om, gy, sg, sig)
+    v = rng.choice(np.array([-1.0, -0.5, 0.5, 1.0], np.float32), size=sig.shape)
+    up = (sig + np.float32(h) * v).astype(np.float32)
+    dn = (sig - np.float32(h) * v).astype(np.float32)
+    want = (loss(s, x, om, gy, sg, up) - loss(s, x, om, gy, sg, dn)) / (2 * h)
+    got = float(np.sum(r["gp"] * v.astype(np.float64)))
+    assert got == want, f"dL/dsigma along v: {got} != {want}"
+    clamped = sg * sig > 2.0
+    assert clamped.any() and np.all(r["gp"][clamped] == 0.0)
+    assert np.any(r["gp"][~clamped] != 0.0)
+    for g in range(s.G):
+        up, dn = sg.copy(), sg.copy()
+        up[g] += np.float32(h)
+        dn[g] -= np.float32(h)
+        want = (loss(s, x, om, gy, up, sig) - loss(s, x, om, gy, dn, sig)) / (2 * h)
+        assert r["gs"][g] == want, f"dL/ds_g with pixel scales, group {g}"
+
+
 def pin_offset_linear(o):
     """The merged offset/weight layer ([DCNv4 digest] "方法3"):
     (a) an identity weight returns the features plus the bias;
@@ -871,8 +949,8 @@ ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
             pin_partition_of_unity, pin_linearity, pin_multiscale,
             pin_pixel_scales, pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
             pin_exact_rational, pin_geometry, pin_codecs, pin_backward_weights,
-            pin_backward_adjoint, pin_backward_offsets, pin_offset_linear,
-            pin_dwconv3x3]
+            pin_backward_adjoint, pin_backward_offsets, pin_backward_scales,
+            pin_offset_linear, pin_dwconv3x3]
 
 
 if __name__ == "__main__":

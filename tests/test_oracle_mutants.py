@@ -97,6 +97,16 @@ MUTANTS = {
     "bwd_col_derivative_weights": sub("const double dBc = hh * (v[1] - v[0]) + lh * (v[3] - v[2]);",
                                       "const double dBc = lh * (v[1] - v[0]) + hh * (v[3] - v[2]);"),
     "bwd_sample_unweighted": sub("gm += gyc * B;", "gm += gyc * (v[0] + v[1] + v[2] + v[3]);"),
+    # gradients of the scales (R17): the clamp, an axis, the direction or a
+    # chain-rule factor lost
+    "scale_grad_clamp_ignored": sub("if (clamped) dS = aS = 0.0;", "if (0) dS = aS = 0.0;"),
+    "scale_grad_axes_swapped": sub("dS += m * (uy * gdr + ux * gdc);",
+                                   "dS += m * (ux * gdr + uy * gdc);"),
+    "scale_grad_direction_dropped": sub("const double uy = (float)(i - hy) + dy;",
+                                        "const double uy = (float)(i - hy);"),
+    "scale_grad_sigma_factor_lost": sub("if (gs) gs[g] += sig * dS;", "if (gs) gs[g] += dS;"),
+    "scale_grad_prior_factor_lost": sub("if (gp) gp[p * G + g] = (double)scales[g] * dS;",
+                                        "if (gp) gp[p * G + g] = dS;"),
     # merged offset/weight layer: weight transposed, bias lost, a term lost
     "linear_weight_transposed": sub("(double)load_f32(dtype, weight, (int64_t)j * Cin + k);",
                                     "(double)load_f32(dtype, weight, (int64_t)k * Nout + j);"),
