@@ -106,6 +106,7 @@ _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward_ws.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P]
 _lib.dcn4_backward_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_backward_scales.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward_workspace_size.argtypes = [_P, ctypes.POINTER(ctypes.c_uint64)]
 _lib.dcn4_offset_linear.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, _P]
@@ -119,7 +120,7 @@ _lib.dcn4_last_error.argtypes = []
 _lib.dcn4_last_error.restype = ctypes.c_char_p
 for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
-           "dcn4_probe_geometry", "dcn4_backward", "dcn4_backward_ws", "dcn4_backward_noalloc",
+           "dcn4_probe_geometry", "dcn4_backward", "dcn4_backward_ws", "dcn4_backward_noalloc", "dcn4_backward_scales",
            "dcn4_backward_workspace_size", "dcn4_offset_linear",
            "dcn4_dwconv3x3"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -184,6 +185,14 @@ def dcn4_backward_noalloc(plan, x: int, offset_mask: int, group_scales: Optional
                           grad_offset_mask: Optional[int], stream: Optional[int]) -> int:
     return _lib.dcn4_backward_noalloc(plan, x, offset_mask, group_scales, pixel_scales,
                                       grad_y, grad_x, grad_offset_mask, stream)
+
+
+def dcn4_backward_scales(plan, x: int, offset_mask: int, group_scales: Optional[int],
+                         pixel_scales: Optional[int], grad_y: int,
+                         grad_group_scales: Optional[int], grad_pixel_scales: Optional[int],
+                         stream: Optional[int]) -> int:
+    return _lib.dcn4_backward_scales(plan, x, offset_mask, group_scales, pixel_scales, grad_y,
+                                     grad_group_scales, grad_pixel_scales, stream)
 
 
 def dcn4_backward_workspace_size(plan):
@@ -485,6 +494,34 @@ class Plan:
         if st != DCN4_OK:
             raise DCN4Error(st, "dcn4_backward_ws")
         return grad_x, grad_om
+
+    def backward_scales(self, x, om, grad_y, scales, pixel_scales=None, want_group=True,
+                        want_pixel=True, stream=None):
+        """(grad_group_scales [G] fp32 or None, grad_pixel_scales [N,Ho,Wo,G]
+        fp32 or None) for the upstream gradient grad_y (group-scale plans)."""
+        import torch
+        d = self.desc
+        dt = _torch_dtype(d.dtype)
+        self._check(x, (d.N, d.H, d.W, d.C), dt, "x")
+        dev = x.device
+        self._check(om, self.om_shape(), dt, "offset_mask", dev)
+        self._check(grad_y, self.out_shape(), dt, "grad_y", dev)
+        self._check(scales, (d.group,), torch.float32, "group_scales", dev)
+        if pixel_scales is not None:
+            self._check(pixel_scales, (d.N, self.Ho, self.Wo, d.group), torch.float32,
+                        "pixel_scales", dev)
+        gsg = torch.empty(d.group, dtype=torch.float32, device=dev) if want_group else None
+        gps = (torch.empty((d.N, self.Ho, self.Wo, d.group), dtype=torch.float32, device=dev)
+               if want_pixel and d.use_pixel_scales else None)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = dcn4_backward_scales(self._h, x.data_ptr(), om.data_ptr(), scales.data_ptr(),
+                                  None if pixel_scales is None else pixel_scales.data_ptr(),
+                                  grad_y.data_ptr(), None if gsg is None else gsg.data_ptr(),
+                                  None if gps is None else gps.data_ptr(), stream)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_backward_scales")
+        return gsg, gps
 
     def probe_geometry(self, om, scales=None, stream=None, pixel_scales=None):
         """Device geometry of every (n, yo, xo, g, k): dict of tensors."""

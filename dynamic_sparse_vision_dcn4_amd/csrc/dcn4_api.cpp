@@ -465,6 +465,43 @@ dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
   return s;
 }
 
+dcn4_status dcn4_backward_scales(const dcn4_plan* plan, const void* x,
+                                 const void* offset_mask, const float* group_scales,
+                                 const float* pixel_scales, const void* grad_y,
+                                 float* grad_group_scales, float* grad_pixel_scales,
+                                 void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  if (!p.desc.use_group_scales)
+    return fail(DCN4_ERR_INVALID_ARG, "the plan has no group scales");
+  if (grad_pixel_scales && !p.desc.use_pixel_scales)
+    return fail(DCN4_ERR_INVALID_ARG, "grad_pixel_scales given but the plan has no pixel scales");
+  if ((int64_t)p.desc.group * 4 > 64 * 1024)
+    return fail(DCN4_ERR_UNSUPPORTED, "more than 16384 groups");
+  dcn4_status s = check_io(p, x, offset_mask, group_scales, pixel_scales, grad_y, true);
+  if (s != DCN4_OK) return s;
+  if ((grad_group_scales && !aligned_to(grad_group_scales, 4)) ||
+      (grad_pixel_scales && !aligned_to(grad_pixel_scales, 4)))
+    return fail(DCN4_ERR_MISALIGNED, "gradient outputs must be 4-byte aligned");
+  const IoBytes b = io_bytes(p);
+  const uint64_t ngs = 4ull * p.desc.group;
+  if (output_overlaps_inputs(p, grad_group_scales, ngs, x, offset_mask, group_scales,
+                             pixel_scales, grad_y) ||
+      output_overlaps_inputs(p, grad_pixel_scales, b.pscales, x, offset_mask, group_scales,
+                             pixel_scales, grad_y) ||
+      overlaps(grad_group_scales, ngs, grad_pixel_scales, b.pscales))
+    return fail(DCN4_ERR_INVALID_ARG, "a gradient output overlaps an input or the other output");
+  if (p.desc.N == 0) {
+    if (!grad_group_scales) return DCN4_OK;  // the group gradient is still written: zeros
+  } else if (!grad_group_scales && !grad_pixel_scales) {
+    return DCN4_OK;
+  }
+  s = dcn4::launch_scale_grads(p, x, offset_mask, group_scales, pixel_scales, grad_y,
+                               grad_group_scales, grad_pixel_scales, stream);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
 dcn4_status dcn4_backward_noalloc(const dcn4_plan* plan, const void* x,
                                   const void* offset_mask, const float* group_scales,
                                   const float* pixel_scales, const void* grad_y,

@@ -157,6 +157,11 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
                             const void* gy, float* gx, float* gom, void* ws,
                             void* stream, bool vector_path);
+// Gradients of the group-scale mode's scales: gsg [G] (cleared here, then
+// accumulated with fp32 atomics) and gps [N,Ho,Wo,G] (written), either null.
+dcn4_status launch_scale_grads(const Plan& p, const void* x, const void* om,
+                               const float* scales, const float* pscales, const void* gy,
+                               float* gsg, float* gps, void* stream);
 // Workspace of the gathered grad_x (0: a single image's indices exceed the
 // kernels' 32-bit counters, so only the atomic path applies).
 uint64_t backward_workspace_bytes(const Plan& p);

@@ -1183,6 +1183,115 @@ __global__ __launch_bounds__(kBlock) void dcn4_backward_kernel(BwdArgs b) {
   }
 }
 
+// Gradients of FlowDCN's scales (group-scale mode).  Point k of the item's
+// group samples centre + S * u_k on each axis, u_k = fl(grid_k + d_k) the
+// value sample_location multiplies by the effective scale S, so
+//   dL/dS = sum_k m_k * (u_y,k * sum_c gy dB/drow + u_x,k * sum_c gy dB/dcol)
+// over the inside samples (the forward's sampling decisions); below the clamp
+// S = s_g * sigma, so dL/dsigma = s_g * dL/dS and dL/ds_g sums sigma * dL/dS
+// over the pixels; above it (fl(s_g * sigma) > Smax) both are 0.  Lanes as in
+// dcn4_backward_kernel: Lg channel-strided lanes per (pixel, group) item, each
+// with its partial sums over its channels; the item's lanes are added by
+// xor-shuffles, the items of a workgroup per group in LDS, and the workgroup
+// adds one fp32 atomic per group into gsg (cleared by the launcher), so
+// dL/ds_g is summed in no fixed order.
+template <int DT, int KS>
+__global__ __launch_bounds__(kBlock) void dcn4_scale_grad_kernel(BwdArgs b, float* gsg,
+                                                                 float* gps) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  extern __shared__ float g_lds[];  // [G] per-group partial sums of the workgroup
+  const FwdArgs& a = b.f;
+  for (uint32_t e = threadIdx.x; e < (uint32_t)a.G; e += kBlock) g_lds[e] = 0.0f;
+  __syncthreads();
+  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const bool active = gid < b.lanes;
+  const int Lg = 1 << b.lg_shift;
+  const uint32_t item = (uint32_t)((active ? gid : 0) >> b.lg_shift);
+  const uint32_t li = (uint32_t)threadIdx.x & (uint32_t)(Lg - 1);
+  const uint32_t p = fastdiv(item, a.div_ipp);  // ipp = G here
+  const uint32_t g = item - p * (uint32_t)a.G;
+  const uint32_t n = fastdiv(p, a.div_hw);
+  const uint32_t rem = p - n * (uint32_t)(a.Ho * a.Wo);
+  const uint32_t yo = fastdiv(rem, a.div_wo);
+  const uint32_t xo = rem - yo * (uint32_t)a.Wo;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  const int kw = KS ? KS : a.kw;
+  const int cpl = a.D >> b.lg_shift;  // channels per lane
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(b.om) +
+                               (uint64_t)item * (uint32_t)(3 * K);
+  const typename io::raw* gyp = reinterpret_cast<const typename io::raw*>(b.gy) +
+                                (uint64_t)p * (uint32_t)a.C + g * (uint32_t)a.D + li;
+  const rsrc_t xr = make_rsrc(b.x, (uint32_t)(b.x_bytes < 0x7fffffffu ? b.x_bytes : 0x7fffffffu));
+  const uint32_t pix_bytes = (uint32_t)a.C * es;
+  const uint32_t img_off = n * a.img_bytes + (g * (uint32_t)a.D + li) * es;
+  const float sg = group_scale(a, p, g);
+  const int hy = ((KS ? KS : a.kh) - 1) >> 1, hx = (kw - 1) >> 1;
+  float dS = 0.0f;  // this lane's part of dL/dS
+  if (active) {
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+      const int i = k / kw, j = k - (k / kw) * kw;
+      const float dx = io::dec(om[2 * k]);
+      const float dy = io::dec(om[2 * k + 1]);
+      const float m = io::dec(om[2 * K + k]);
+      const float gyy = (float)(i - hy), gxx = (float)(j - hx);
+      const Cell c = locate(sample_location<kGroupScale>((float)((int)yo * a.sh - a.ph + hy),
+                                                         (float)((int)xo * a.sw - a.pw + hx),
+                                                         gyy, gxx, dy, dx, a.offset_scale, sg),
+                            a.Hm1, a.Wm1);
+      if (!c.inside) continue;
+      const bool vy0 = c.y0 >= 0, vy1 = c.y0 < a.H - 1;
+      const bool vx0 = c.x0 >= 0, vx1 = c.x0 < a.W - 1;
+      const bool ok[4] = {vy0 && vx0, vy0 && vx1, vy1 && vx0, vy1 && vx1};
+      const float lh = c.lh, lw = c.lw, hh = 1.0f - lh, hw = 1.0f - lw;
+      const float w[4] = {hh * hw, hh * lw, lh * hw, lh * lw};
+      const int cy[4] = {c.y0, c.y0, c.y0 + 1, c.y0 + 1};
+      const int cx[4] = {c.x0, c.x0 + 1, c.x0, c.x0 + 1};
+      uint32_t q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        q[r] = ok[r] ? img_off + (uint32_t)(cy[r] * a.W + cx[r]) * pix_bytes : kOutside;
+      float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // corner sums of gy * v
+#pragma unroll 1
+      for (int jc = 0; jc < cpl; ++jc) {
+        const uint32_t coff = ((uint32_t)jc << b.lg_shift) * es;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (es == 4)
+            v[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, (int)(q[r] + coff), 0, 0));
+          else
+            v[r] = io::dec((typename io::raw)__builtin_amdgcn_raw_buffer_load_b16(xr, (int)(q[r] + coff), 0, 0));
+        }
+        const float gyc = io::dec(gyp[jc << b.lg_shift]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[r] = __builtin_fmaf(gyc, v[r], S[r]);
+      }
+      float gm, gdr, gdc;
+      point_grads(S, w, lh, lw, gm, gdr, gdc);
+      // u = grid + direction, the same fp32 sums sample_location scales
+      dS = __builtin_fmaf(m, __builtin_fmaf(gyy + dy, gdr, (gxx + dx) * gdc), dS);
+    }
+  }
+  // the item's Lg lanes are consecutive and Lg-aligned in the wave
+  for (int off = 1; off < Lg; off <<= 1) dS += __shfl_xor(dS, off, 64);
+  if (active && li == 0) {
+    float Su = a.scales[g];
+    const float sig = a.pscales ? a.pscales[(uint64_t)p * (uint32_t)a.G + g] : 1.0f;
+    if (a.pscales) Su = Su * sig;
+    if (a.max_scale > 0.0f && Su > a.max_scale) dS = 0.0f;  // S is the constant Smax
+    if (gps) gps[(uint64_t)p * (uint32_t)a.G + g] = a.scales[g] * dS;
+    if (gsg) atomicAdd(&g_lds[g], sig * dS);
+  }
+  if (!gsg) return;
+  __syncthreads();
+  for (uint32_t e = threadIdx.x; e < (uint32_t)a.G; e += kBlock) {
+    const float v = g_lds[e];
+    if (v != 0.0f) unsafeAtomicAdd(gsg + e, v);
+  }
+}
+
 // grad_offset_mask alone (grad_x gathered or not asked for) where the tiled
 // kernel does not apply, for groups of whole 16-byte vectors and 16-byte
 // aligned tensors: Lg lanes per (pixel, group) item, lane li owning the
@@ -2901,6 +3010,66 @@ dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
     b.lanes = nb * lanes_per_image;
     const int64_t blocks = (b.lanes + kBlock - 1) / kBlock;
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), om_vec ? om_lds : 0, st, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  return DCN4_OK;
+}
+
+dcn4_status launch_scale_grads(const Plan& p, const void* x, const void* om,
+                               const float* scales, const float* pscales, const void* gy,
+                               float* gsg, float* gps, void* stream) {
+  const dcn4_desc& d = p.desc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gsg) {
+    hipLaunchKernelGGL(dcn4_fill_zero_kernel, dim3(1), dim3(kBlock), 0, st, gsg,
+                       (uint64_t)d.group);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  typedef void (*sg_fn)(BwdArgs, float*, float*);
+  sg_fn fn;
+  switch (d.dtype) {
+    case DCN4_F32: fn = K3 ? dcn4_scale_grad_kernel<DCN4_F32, 3> : dcn4_scale_grad_kernel<DCN4_F32, 0>; break;
+    case DCN4_BF16: fn = K3 ? dcn4_scale_grad_kernel<DCN4_BF16, 3> : dcn4_scale_grad_kernel<DCN4_BF16, 0>; break;
+    default: fn = K3 ? dcn4_scale_grad_kernel<DCN4_F16, 3> : dcn4_scale_grad_kernel<DCN4_F16, 0>; break;
+  }
+  BwdArgs b{};
+  fill_common(p, b.f);
+  b.f.scales = scales;
+  b.f.G = d.group;
+  b.f.ipp = d.group;
+  b.f.div_ipp = make_fastdiv((uint32_t)d.group);
+  b.scales = scales;
+  b.lg_shift = backward_lg_shift(p.D);
+  const int64_t lanes_per_image = (int64_t)p.Ho * p.Wo * d.group << b.lg_shift;
+  const uint64_t x_img = (uint64_t)d.H * d.W * d.C * p.es;
+  int64_t imgs = ((int64_t(1) << 31) - 1) / lanes_per_image;
+  const int64_t imgs_x = (int64_t)(((uint64_t(1) << 31) - 1) / x_img);
+  if (imgs_x < imgs) imgs = imgs_x;
+  if (imgs < 1) imgs = 1;
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t om_img = (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K * p.es;
+  const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;
+  for (int64_t n0 = 0; n0 < d.N; n0 += imgs) {
+    const int64_t nb = (d.N - n0) < imgs ? (d.N - n0) : imgs;
+    b.x = static_cast<const char*>(x) + n0 * x_img;
+    b.om = static_cast<const char*>(om) + n0 * om_img;
+    b.gy = static_cast<const char*>(gy) + n0 * y_img;
+    b.pscales = pscales ? pscales + n0 * ps_img : nullptr;
+    b.f.pscales = b.pscales;
+    b.x_bytes = nb * x_img;
+    b.lanes = nb * lanes_per_image;
+    const int64_t blocks = (b.lanes + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kBlock), (size_t)d.group * 4, st, b, gsg,
+                       gps ? gps + n0 * ps_img : nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       note_hip_error(e);

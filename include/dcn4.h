@@ -274,7 +274,8 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
  * (1-lw)(v10-v00) + lw(v11-v01) and dB/dcol = (1-lh)(v01-v00) + lh(v11-v10):
  * the derivative from above at integer locations.  The sampling decisions
  * are the forward's (same device functions); a sample that is not inside has
- * zero gradient.  No gradient of the group or pixel scales is computed.
+ * zero gradient.  The gradients of the group and pixel scales come from
+ * dcn4_backward_scales.
  * grad_x is the adjoint of the bilinear gather ([DCNv4 digest] "GPU效率的
  * 理论分析": every sample reads four corners of its group's D channels):
  * with a workspace each sample is appended to the bucket of its cell and
@@ -314,6 +315,30 @@ dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x,
                              float* grad_x, float* grad_offset_mask,
                              void* workspace, uint64_t workspace_bytes,
                              void* stream);
+
+/* Gradients of FlowDCN's scales ([FlowDCN] 3.1: the deformation's scale is
+ * predicted per pixel by a linear layer of its own, on top of the group
+ * prior; 3.3: the maximum scale), for plans in group-scale mode.  Point k
+ * of group g samples centre + S * u_k on each axis, u_k = fl(grid_k + d_k),
+ * so dL/dS = sum_k m_k (u_y,k sum_c dL/dy_c dB_c/drow + u_x,k sum_c dL/dy_c
+ * dB_c/dcol) over the inside samples (the forward's sampling decisions, the
+ * derivatives of dcn4_backward); below the clamp S = s_g * sigma, so
+ *   grad_pixel_scales[n,yo,xo,g] = s_g * dL/dS   (plans with pixel scales)
+ *   grad_group_scales[g]         = sum over pixels of sigma * dL/dS
+ * (sigma = 1 without pixel scales); where fl(s_g * sigma) > max_scale the
+ * scale is the constant max_scale and both are 0.  grad_group_scales [G] and
+ * grad_pixel_scales [N, Ho, Wo, G] are fp32 device arrays, 4-byte aligned,
+ * either NULL to skip it, both overwritten; the group sums are fp32 atomics
+ * in no fixed order.  x, offset_mask, group_scales, pixel_scales and grad_y as
+ * in dcn4_backward.  Errors: DCN4_ERR_INVALID_ARG (a plan without group
+ * scales, grad_pixel_scales without pixel scales, an output overlapping an
+ * input or the other output), DCN4_ERR_UNSUPPORTED (more than 16384 groups),
+ * and those of dcn4_backward. */
+dcn4_status dcn4_backward_scales(const dcn4_plan* plan, const void* x,
+                                 const void* offset_mask, const float* group_scales,
+                                 const float* pixel_scales, const void* grad_y,
+                                 float* grad_group_scales, float* grad_pixel_scales,
+                                 void* stream);
 
 /* dcn4_backward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

@@ -379,6 +379,26 @@ class TestForwardValidation:
         assert d4.dcn4_backward_noalloc(big.handle, G1, 2 * G1, None, None, 3 * G1, G1 + 64,
                                         5 * G1, None) == d4.DCN4_ERR_INVALID_ARG
 
+    def test_backward_scales_checks(self):
+        """dcn4_backward_scales validates before launching: group-scale plans
+        only, pixel-scale gradients only with pixel scales, aligned and
+        non-overlapping outputs."""
+        M = 1 << 24
+        ms = d4.Plan(mk(use_group_scales=True))
+        ps = d4.Plan(mk(use_group_scales=True, use_pixel_scales=True, max_scale=2.0))
+        bs = lambda p, sc, pp, gs, gp: d4.dcn4_backward_scales(p.handle, M, 2 * M, sc, pp, 3 * M,
+                                                               gs, gp, None)
+        assert d4.dcn4_backward_scales(None, M, 2 * M, 4 * M, None, 3 * M, 5 * M, None,
+                                       None) == d4.DCN4_ERR_NULL
+        assert bs(self.p, None, None, 5 * M, None) == d4.DCN4_ERR_INVALID_ARG   # no group scales
+        assert bs(ms, 4 * M, None, 5 * M, 6 * M) == d4.DCN4_ERR_INVALID_ARG     # no pixel scales
+        assert bs(ms, None, None, 5 * M, None) == d4.DCN4_ERR_NULL              # scales missing
+        assert bs(ms, 4 * M, None, 5 * M + 2, None) == d4.DCN4_ERR_MISALIGNED
+        assert bs(ps, 4 * M, 7 * M, 5 * M, 6 * M + 2) == d4.DCN4_ERR_MISALIGNED
+        assert bs(ms, 4 * M, None, M + 64, None) == d4.DCN4_ERR_INVALID_ARG     # over x
+        assert bs(ps, 4 * M, 7 * M, 5 * M, 7 * M) == d4.DCN4_ERR_INVALID_ARG    # over sigma
+        assert bs(ps, 4 * M, 7 * M, 6 * M + 8, 6 * M) == d4.DCN4_ERR_INVALID_ARG  # each other
+
     def test_overlapping_outputs_rejected(self):
         """No output may overlap an input or another output of the call (the
         byte ranges the plan implies); adjacent ranges are fine, so the

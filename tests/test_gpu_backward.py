@@ -321,3 +321,103 @@ def test_backward_element_paths(dt):
         what = f"element paths {dt} {'scatter' if scatter else 'gather'}"
         check_bound(gx.cpu().numpy(), ref["gx"], ref["gx_abs"], ref["max_terms"], what + " grad_x")
         check_bound(gom.cpu().numpy(), ref["gom"], ref["gom_abs"], ref["max_terms"], what + " grad_om")
+
+
+# ----------------------------------------------------- gradients of the scales
+def scale_grad_cases():
+    """group-scale plans: with and without predicted pixel scales and the
+    Smax clamp, every dtype, 3x3 (compile-time kernel) and 5x5 / 1x1, group
+    widths over 1 to 16 lanes"""
+    rng = np.random.default_rng(8765)
+    cases = []
+    for t in range(12):
+        dt = ["bf16", "f32", "f16"][t % 3]
+        k = [3, 3, 5, 1][t % 4]
+        ps = t % 2 == 1
+        smax = [0.0, 2.0, 1.25][t % 3] if ps or t % 3 else 0.0
+        D = int(rng.choice([8, 24, 72, 10, 16]))
+        G = int(rng.integers(1, 5))
+        s = Shape(int(rng.integers(1, 3)), int(rng.integers(5, 20)), int(rng.integers(5, 20)),
+                  G * D, G, k, k, 1, 1, int(rng.integers(0, 3)), int(rng.integers(0, 3)),
+                  multiscale=True, pixel_scales=ps, max_scale=smax)
+        try:
+            oracle.get().out_size(s)
+        except ValueError:
+            continue
+        cases.append((t, s, dt))
+    return cases
+
+
+def run_scale_grads(plan, s, inp, gy_raw, dt):
+    x, om, gy = to_dev(inp.x, dt), to_dev(inp.om, dt), to_dev(gy_raw, dt)
+    sc = torch.from_numpy(inp.scales).cuda()
+    gsg, gps = plan.backward_scales(x, om, gy, sc, dev_f32(inp.pscales))
+    torch.cuda.synchronize()
+    return gsg.cpu().numpy(), None if gps is None else gps.cpu().numpy()
+
+
+def check_scale_grads(s, dt, inp, gy, plan, what):
+    """dL/dsigma within the fp32 bound of its 4DK terms; dL/ds_g within the
+    bound with the per-pixel partial sums added on top (atomics)"""
+    o = oracle.get()
+    ref = o.backward_scales(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
+    gsg, gps = run_scale_grads(plan, s, inp, gy, dt)
+    n_item = 4 * (s.C // s.G) * s.K + 16
+    Ho, Wo = o.out_size(s)
+    check_bound(gsg, ref["gs"], ref["gs_abs"], n_item + s.N * Ho * Wo, f"{what} dL/ds_g")
+    if s.pixel_scales:
+        check_bound(gps, ref["gp"], ref["gp_abs"], n_item, f"{what} dL/dsigma")
+        if s.max_scale > 0:
+            clamped = inp.scales[None, None, None, :] * inp.pscales > np.float32(s.max_scale)
+            assert np.all(gps[clamped] == 0.0), f"{what}: nonzero gradient above the clamp"
+
+
+@pytest.mark.parametrize("t, s, dt", scale_grad_cases(),
+                         ids=lambda v: str(v) if isinstance(v, int) else None)
+def test_scale_gradients(t, s, dt):
+    inp, gy = bwd_inputs(s, dt, seed=700 + t)
+    plan = d4.Plan(desc_of(s, dt))
+    say(f"scale gradients case {t}: {s} {dt}")
+    check_scale_grads(s, dt, inp, gy, plan, f"scale grads {t}")
+
+
+def test_scale_gradients_full_size():
+    """FlowDCN's tokens with predicted scales and Smax 4 at full size."""
+    w = WORKLOADS["flowdcn_pixelscale_bf16"]
+    s = shape_of(w)
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = make_inputs(w, Ho, Wo)
+    gy = to_raw(np.random.default_rng(11).standard_normal((s.N, Ho, Wo, s.C), dtype=np.float32),
+                w.dtype)
+    say(f"scale gradients, full size {w.describe()}")
+    check_scale_grads(s, w.dtype, inp, gy, d4.Plan(desc_of(s, w.dtype)), "flowdcn full size")
+
+
+def test_scale_gradients_requests():
+    """Either output may be skipped; the group gradient of an empty batch is
+    zero; a plan without group scales is refused."""
+    s = Shape(2, 9, 8, 48, 2, multiscale=True, pixel_scales=True, max_scale=2.0)
+    dt = "bf16"
+    inp, gy = bwd_inputs(s, dt, seed=777)
+    plan = d4.Plan(desc_of(s, dt))
+    x, om, g = to_dev(inp.x, dt), to_dev(inp.om, dt), to_dev(gy, dt)
+    sc, ps = torch.from_numpy(inp.scales).cuda(), dev_f32(inp.pscales)
+    a, b = plan.backward_scales(x, om, g, sc, ps)
+    a2, none = plan.backward_scales(x, om, g, sc, ps, want_pixel=False)
+    none2, b2 = plan.backward_scales(x, om, g, sc, ps, want_group=False)
+    torch.cuda.synchronize()
+    assert none is None and none2 is None
+    assert torch.equal(b.view(torch.int32), b2.view(torch.int32))
+    ref = oracle.get().backward_scales(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
+    n = 4 * 24 * 9 + 16 + s.N * 9 * 8
+    check_bound(a2.cpu().numpy(), ref["gs"], ref["gs_abs"], n, "group gradient alone")
+    empty = d4.Plan(desc_of(Shape(0, 9, 8, 48, 2, multiscale=True), dt))
+    z = torch.full((2,), float("nan"), device="cuda")
+    st = d4.dcn4_backward_scales(empty.handle, None, None, sc.data_ptr(), None, None,
+                                 z.data_ptr(), None, None)
+    torch.cuda.synchronize()
+    assert st == d4.DCN4_OK and torch.equal(z.cpu(), torch.zeros(2))
+    std = d4.Plan(desc_of(Shape(1, 9, 8, 48, 2), dt))
+    assert d4.dcn4_backward_scales(std.handle, x.data_ptr(), om.data_ptr(), None, None,
+                                   g.data_ptr(), z.data_ptr(), None, None) == d4.DCN4_ERR_INVALID_ARG
