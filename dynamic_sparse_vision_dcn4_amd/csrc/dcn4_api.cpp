@@ -408,12 +408,13 @@ static dcn4_status check_backward(const dcn4::Plan& p, const void* x, const void
   return DCN4_OK;
 }
 
-dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x, const void* offset_mask,
-                             const float* group_scales, const float* pixel_scales,
-                             const void* grad_y, float* grad_x, float* grad_offset_mask,
-                             void* workspace, uint64_t workspace_bytes, void* stream) {
-  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
-  const dcn4::Plan& p = plan->p;
+// The backward with a workspace of ws_bytes >= min_bytes (or none: atomic
+// scatter); the chunks of the gathered grad_x are as large as fit ws_bytes.
+static dcn4_status backward_with(const dcn4::Plan& p, const void* x, const void* offset_mask,
+                                 const float* group_scales, const float* pixel_scales,
+                                 const void* grad_y, float* grad_x, float* grad_offset_mask,
+                                 void* workspace, uint64_t ws_bytes, uint64_t min_bytes,
+                                 const char* too_small, void* stream) {
   dcn4_status s = check_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
                                  grad_offset_mask);
   if (s != DCN4_OK) return s;
@@ -421,22 +422,34 @@ dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x, const void* o
   if (workspace && need) {
     if (!aligned_to(workspace, 256))
       return fail(DCN4_ERR_MISALIGNED, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-      return fail(DCN4_ERR_INVALID_ARG, "workspace smaller than dcn4_backward_workspace_size");
+    if (ws_bytes < min_bytes) return fail(DCN4_ERR_INVALID_ARG, too_small);
     const IoBytes b = io_bytes(p);
-    if (output_overlaps_inputs(p, workspace, need, x, offset_mask, group_scales, pixel_scales,
-                               grad_y) ||
-        overlaps(workspace, need, grad_x, b.x / p.es * 4) ||
-        overlaps(workspace, need, grad_offset_mask, b.om / p.es * 4))
+    if (output_overlaps_inputs(p, workspace, ws_bytes, x, offset_mask, group_scales,
+                               pixel_scales, grad_y) ||
+        overlaps(workspace, ws_bytes, grad_x, b.x / p.es * 4) ||
+        overlaps(workspace, ws_bytes, grad_offset_mask, b.om / p.es * 4))
       return fail(DCN4_ERR_INVALID_ARG, "the workspace overlaps another argument");
   }
   if (p.desc.N == 0) return DCN4_OK;
   const bool vector_path = p.dp > 0 && aligned_to(x, 16) && aligned_to(offset_mask, 16) &&
                            aligned_to(grad_y, 16);
   s = dcn4::launch_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
-                            grad_offset_mask, need ? workspace : nullptr, stream, vector_path);
+                            grad_offset_mask, need ? workspace : nullptr,
+                            need ? ws_bytes : 0, stream, vector_path);
   if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
   return DCN4_OK;
+}
+
+dcn4_status dcn4_backward_ws(const dcn4_plan* plan, const void* x, const void* offset_mask,
+                             const float* group_scales, const float* pixel_scales,
+                             const void* grad_y, float* grad_x, float* grad_offset_mask,
+                             void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  return backward_with(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                       grad_offset_mask, workspace, workspace_bytes,
+                       dcn4::backward_workspace_bytes(p),
+                       "workspace smaller than dcn4_backward_workspace_size", stream);
 }
 
 dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
@@ -516,17 +529,18 @@ dcn4_status dcn4_backward_noalloc(const dcn4_plan* plan, const void* x,
   dcn4_status s = check_backward(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
                                  grad_offset_mask);
   if (s != DCN4_OK) return s;
-  if (need > dcn4::kScratchBytes)
+  // the scratch holds chunks of as many (image, group) pairs as fit it
+  if (dcn4::backward_min_workspace_bytes(p) > dcn4::kScratchBytes)
     return fail(DCN4_ERR_UNSUPPORTED,
-                "the gathered grad_x needs more workspace than the library's 64 MiB static "
-                "scratch: call dcn4_backward_ws with a workspace of "
-                "dcn4_backward_workspace_size bytes");
+                "one image and group of the gathered grad_x need more workspace than the "
+                "library's 64 MiB static scratch: call dcn4_backward_ws");
   void* ws = nullptr;
   s = dcn4::scratch_address(&ws);
   if (s != DCN4_OK) return fail(s, s == DCN4_ERR_HIP ? dcn4::last_hip_error()
                                                      : "device index beyond 63");
-  return dcn4_backward_ws(plan, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
-                          grad_offset_mask, ws, need, stream);
+  return backward_with(p, x, offset_mask, group_scales, pixel_scales, grad_y, grad_x,
+                       grad_offset_mask, ws, dcn4::kScratchBytes,
+                       dcn4::backward_min_workspace_bytes(p), "static scratch too small", stream);
 }
 
 dcn4_status dcn4_offset_linear(const void* feat, const void* weight, const float* bias,

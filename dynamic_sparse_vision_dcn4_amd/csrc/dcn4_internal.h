@@ -148,23 +148,28 @@ dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
                          const float* pscales, int32_t* y0, int32_t* x0,
                          float* lh, float* lw, uint8_t* inside, void* stream);
 // Backward pass: write grad_x (if given) and grad_om (if given); both fp32.
-// With a workspace of backward_workspace_bytes(p) bytes (256-byte aligned)
-// grad_x is gathered from per-cell buckets; without one it is cleared and
-// accumulated with atomics.
+// With a workspace of ws_bytes >= backward_min_workspace_bytes(p) bytes
+// (256-byte aligned) grad_x is gathered from per-cell buckets; without one it
+// is cleared and accumulated with atomics.
 // vector_path: x, offset_mask and grad_y are 16-byte aligned (the tiled
 // backward may run).
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
                             const void* gy, float* gx, float* gom, void* ws,
-                            void* stream, bool vector_path);
+                            uint64_t ws_bytes, void* stream, bool vector_path);
 // Gradients of the group-scale mode's scales: gsg [G] (cleared here, then
 // accumulated with fp32 atomics) and gps [N,Ho,Wo,G] (written), either null.
 dcn4_status launch_scale_grads(const Plan& p, const void* x, const void* om,
                                const float* scales, const float* pscales, const void* gy,
                                float* gsg, float* gps, void* stream);
 // Workspace of the gathered grad_x (0: a single image's indices exceed the
-// kernels' 32-bit counters, so only the atomic path applies).
+// kernels' 32-bit counters, so only the atomic path applies): chunks of
+// (image, group) pairs within the operator's ideal traffic bytes (at least
+// one pair, at most 2 GiB).  A launch given ws_bytes of workspace uses
+// chunks as large as fit it; the smallest workspace that works holds one
+// (image, group) pair.
 uint64_t backward_workspace_bytes(const Plan& p);
+uint64_t backward_min_workspace_bytes(const Plan& p);
 // The static device workspace of dcn4_backward_noalloc: its size, and its
 // address on the current device (looked up once per device).
 constexpr uint64_t kScratchBytes = uint64_t(64) << 20;

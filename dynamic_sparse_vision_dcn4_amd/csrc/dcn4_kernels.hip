@@ -1692,7 +1692,10 @@ struct GatherArgs {
   // bucket tiles: TH x TW output pixels (TW = 1 << tw_shift), their cell
   // window of WH x WW cells starting at (ty0*sh + wy_off, tx0*sw + wx_off)
   int32_t TH, tw_shift, WH, WW, wy_off, wx_off, tiles_x, tiles_y;
-  FastDiv div_K, div_kw, div_G, div_W, div_H, div_WW, div_tx, div_ty;
+  // the chunk's groups: g0 .. g0 + gc - 1 (bucket keys, sample ids and
+  // workgroups count groups from g0; tensors are addressed with g0 + local)
+  int32_t g0, gc;
+  FastDiv div_K, div_kw, div_gc, div_W, div_H, div_WW, div_tx, div_ty;
   FastDiv div_strips, div_bgroups, div_OWW, div_vpp;
 };
 
@@ -1750,10 +1753,11 @@ __device__ __forceinline__ u32x4 pack_record(const SampleRec& r) {
   return rec;
 }
 
-// Bucket row of cell row y0 of group g in image n of the chunk; the cell
-// (y0, x0) has key row*(W+1) + x0+1.
-__device__ __forceinline__ uint64_t bucket_row(const FwdArgs& a, uint32_t n, uint32_t g, int y0) {
-  return (uint64_t)(n * (uint32_t)a.G + g) * (uint32_t)(a.H + 1) + (uint32_t)(y0 + 1);
+// Bucket row of cell row y0 of the chunk's group gl in image n of the chunk;
+// the cell (y0, x0) has key row*(W+1) + x0+1.
+__device__ __forceinline__ uint64_t bucket_row(const GatherArgs& ga, uint32_t n, uint32_t gl,
+                                               int y0) {
+  return (uint64_t)(n * (uint32_t)ga.gc + gl) * (uint32_t)(ga.f.H + 1) + (uint32_t)(y0 + 1);
 }
 
 __device__ __forceinline__ void place_record(const GatherArgs& ga, uint64_t rowk, int x0,
@@ -1778,8 +1782,9 @@ __global__ __launch_bounds__(kBlock) void dcn4_bucket_kernel(GatherArgs ga) {
   const uint32_t txi = b - q1 * (uint32_t)ga.tiles_x;
   const uint32_t q2 = fastdiv(q1, ga.div_ty);
   const uint32_t tyi = q1 - q2 * (uint32_t)ga.tiles_y;
-  const uint32_t n = fastdiv(q2, ga.div_G);
-  const uint32_t g = q2 - n * (uint32_t)a.G;
+  const uint32_t n = fastdiv(q2, ga.div_gc);
+  const uint32_t gl = q2 - n * (uint32_t)ga.gc;  // group within the chunk
+  const uint32_t g = (uint32_t)ga.g0 + gl;
   const int TW = 1 << ga.tw_shift;
   const int ty0 = (int)tyi * ga.TH, tx0 = (int)txi * TW;
   const int wy0 = ty0 * a.sh + ga.wy_off, wx0 = tx0 * a.sw + ga.wx_off;
@@ -1805,13 +1810,13 @@ __global__ __launch_bounds__(kBlock) void dcn4_bucket_kernel(GatherArgs ga) {
     const SampleRec r = sample_at<DT, MODE>(ga, pix, yo, xo, g, k);
     if (!r.inside) continue;
     rec[j] = pack_record(r);
-    sid[j] = (pix * (uint32_t)a.G + g) * (uint32_t)ga.K + (uint32_t)k;
+    sid[j] = (pix * (uint32_t)ga.gc + gl) * (uint32_t)ga.K + (uint32_t)k;
     const int ly = r.y0 - wy0, lx = r.x0 - wx0;
     if ((unsigned)ly < (unsigned)ga.WH && (unsigned)lx < (unsigned)ga.WW) {
       cell[j] = ly * ga.WW + lx;
       rank[j] = atomicAdd(cnt + cell[j], 1u);
     } else {  // outside the window: a slot of its own
-      const uint64_t rowk = bucket_row(a, n, g, r.y0);
+      const uint64_t rowk = bucket_row(ga, n, gl, r.y0);
       const uint32_t slot =
           atomicAdd(ga.counts + rowk * (uint32_t)(a.W + 1) + (uint32_t)(r.x0 + 1), 1u);
       place_record(ga, rowk, r.x0, slot, rec[j], sid[j]);
@@ -1823,7 +1828,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_bucket_kernel(GatherArgs ga) {
     const uint32_t c = cnt[i];
     if (c == 0) continue;
     const int ly = (int)fastdiv((uint32_t)i, ga.div_WW), lx = i - ly * ga.WW;
-    cnt[i] = atomicAdd(ga.counts + bucket_row(a, n, g, wy0 + ly) * (uint32_t)(a.W + 1) +
+    cnt[i] = atomicAdd(ga.counts + bucket_row(ga, n, gl, wy0 + ly) * (uint32_t)(a.W + 1) +
                            (uint32_t)(wx0 + lx + 1), c);
   }
   __syncthreads();
@@ -1831,7 +1836,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_bucket_kernel(GatherArgs ga) {
   for (int j = 0; j < kBucketNS; ++j) {
     if (cell[j] < 0) continue;
     const int ly = (int)fastdiv((uint32_t)cell[j], ga.div_WW), lx = cell[j] - ly * ga.WW;
-    place_record(ga, bucket_row(a, n, g, wy0 + ly), wx0 + lx, cnt[cell[j]] + rank[j], rec[j],
+    place_record(ga, bucket_row(ga, n, gl, wy0 + ly), wx0 + lx, cnt[cell[j]] + rank[j], rec[j],
                  sid[j]);
   }
 }
@@ -1893,8 +1898,9 @@ __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
   const uint32_t strip = wg - q1 * (uint32_t)ga.strips;
   const uint32_t q2 = fastdiv(q1, ga.div_bgroups);
   const uint32_t bgrp = q1 - q2 * (uint32_t)ga.band_groups;
-  const uint32_t n = fastdiv(q2, ga.div_G);
-  const uint32_t g = q2 - n * (uint32_t)a.G;
+  const uint32_t n = fastdiv(q2, ga.div_gc);
+  const uint32_t gl = q2 - n * (uint32_t)ga.gc;  // group within the chunk
+  const uint32_t g = (uint32_t)ga.g0 + gl;
   const int lane = (int)(threadIdx.x & 63);
   const int wave = (int)(threadIdx.x >> 6);
   const int Lg = ga.Lg;
@@ -1931,7 +1937,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_gather_kernel(GatherArgs ga) {
   const int y_lo = band * ga.band_rows;
   const int y_hi = min(y_lo + ga.band_rows, a.H);
   const uint64_t row = (uint32_t)(a.W + 1);
-  const uint64_t rk0 = (uint64_t)(n * (uint32_t)a.G + g) * (uint32_t)(a.H + 1);  // bucket row 0
+  const uint64_t rk0 = (uint64_t)(n * (uint32_t)ga.gc + gl) * (uint32_t)(a.H + 1);  // bucket row 0
   const uint64_t kb = rk0 * row + (uint32_t)(col_ok ? cx : 0);
   float* gxn = ga.gx + (uint64_t)n * (uint32_t)(a.H * a.W) * (uint32_t)a.C + g * (uint32_t)a.D;
   const uint32_t xmask = (1u << ga.xs) - 1u;
@@ -2033,8 +2039,8 @@ __device__ __forceinline__ SampleRec sample_record(const GatherArgs& ga, uint32_
   const FwdArgs& a = ga.f;
   const uint32_t item = fastdiv(s, ga.div_K);
   const int k = (int)(s - item * (uint32_t)ga.K);
-  const uint32_t pix = fastdiv(item, ga.div_G);
-  const uint32_t g = item - pix * (uint32_t)a.G;
+  const uint32_t pix = fastdiv(item, ga.div_gc);
+  const uint32_t g = (uint32_t)ga.g0 + (item - pix * (uint32_t)ga.gc);
   const uint32_t n = fastdiv(pix, a.div_hw);
   const uint32_t rem = pix - n * (uint32_t)(a.Ho * a.Wo);
   const uint32_t yo = fastdiv(rem, a.div_wo);
@@ -2640,36 +2646,75 @@ int gather_lanes(int D, int V) {
   return nchunk < 16 ? nchunk : 16;
 }
 
-// Workspace of one chunk of images: [0, 256) the overflow counter; from 256
-// the bucket counts (4 bytes per key); then the overflow list (4 bytes per
-// sample); then the records (16 bytes x cap per key).
+// The gathered grad_x runs over the batch in chunks of imgs images x gc
+// groups.  Workspace of one chunk: [0, 256) the overflow counter; from 256
+// the bucket counts (4 bytes per key, (H+1)*(W+1) keys per image and
+// group); then the overflow list (4 bytes per sample, Ho*Wo*K per image and
+// group); then the records (16 bytes x cap per key).
 struct GatherShape {
   bool ok;        // indices of one image fit the kernels' 32-bit counters
   int64_t imgs;   // images per chunk
+  int32_t gc;     // groups per chunk
   uint32_t cap;
-  uint64_t keys_img, samples_img;
+  uint64_t keys_ig, samples_ig;  // per image and group
   uint64_t list_off, recs_off, bytes;
 };
 
-GatherShape gather_shape(const Plan& p) {
+uint64_t chunk_bytes(uint64_t keys_ig, uint64_t samples_ig, uint32_t cap, uint64_t pairs) {
+  return 256 + round256(4 * pairs * keys_ig) + round256(4 * pairs * samples_ig) +
+         16 * pairs * keys_ig * cap;
+}
+
+// Chunks of at most as many (image, group) pairs as fit `budget` bytes of
+// workspace (at least one pair, even beyond the budget), as few as possible.
+GatherShape gather_shape(const Plan& p, uint64_t budget) {
   GatherShape s{};
   const dcn4_desc& d = p.desc;
   s.cap = bucket_capacity(p);
-  s.keys_img = (uint64_t)(d.H + 1) * (d.W + 1) * d.group;
-  s.samples_img = (uint64_t)p.Ho * p.Wo * d.group * p.K;
+  s.keys_ig = (uint64_t)(d.H + 1) * (d.W + 1);
+  s.samples_ig = (uint64_t)p.Ho * p.Wo * p.K;
   const uint64_t lim = (uint64_t(1) << 31) - 1;
-  if (d.N < 1 || s.keys_img > lim || s.samples_img > lim) return s;
-  const uint64_t per_img = 4 * s.keys_img + 4 * s.samples_img + 16 * s.keys_img * s.cap;
-  uint64_t imgs = (uint64_t)d.N;
-  const uint64_t caps[3] = {lim / s.keys_img, lim / s.samples_img, kGatherChunkBytes / per_img};
-  for (uint64_t c : caps) imgs = c < imgs ? c : imgs;
-  if (imgs < 1) imgs = 1;
-  s.imgs = (int64_t)imgs;
-  s.list_off = 256 + round256(4 * imgs * s.keys_img);
-  s.recs_off = s.list_off + round256(4 * imgs * s.samples_img);
-  s.bytes = s.recs_off + 16 * imgs * s.keys_img * s.cap;
+  if (d.N < 1 || s.keys_ig * d.group > lim || s.samples_ig * d.group > lim) return s;
+  // pairs per chunk: the budget and the kernels' 32-bit key and sample counts
+  uint64_t lo = 1, hi = (uint64_t)d.N * d.group;
+  const uint64_t lims[2] = {lim / s.keys_ig, lim / s.samples_ig};
+  for (uint64_t c : lims) hi = c < hi ? c : hi;
+  while (lo < hi) {  // the largest count that fits
+    const uint64_t mid = (lo + hi + 1) / 2;
+    if (chunk_bytes(s.keys_ig, s.samples_ig, s.cap, mid) <= budget) lo = mid; else hi = mid - 1;
+  }
+  const uint64_t pairs = lo;
+  // the split into images x groups with the fewest chunks (each chunk is a
+  // launch sequence), then the chunks evened out (the smallest workspace for
+  // that many chunks)
+  uint64_t best_chunks = ~uint64_t(0), best = 0;
+  const uint64_t N = (uint64_t)d.N, G = (uint64_t)d.group;
+  for (uint64_t gc = G; gc >= 1; --gc) {
+    uint64_t imgs = pairs / gc;
+    if (imgs > N) imgs = N;
+    if (imgs == 0) continue;
+    const uint64_t ci = (N + imgs - 1) / imgs, cg = (G + gc - 1) / gc;
+    const uint64_t i2 = (N + ci - 1) / ci, g2 = (G + cg - 1) / cg;  // evened out
+    if (ci * cg < best_chunks || (ci * cg == best_chunks && i2 * g2 < best)) {
+      best_chunks = ci * cg;
+      best = i2 * g2;
+      s.imgs = (int64_t)i2;
+      s.gc = (int32_t)g2;
+    }
+  }
+  s.list_off = 256 + round256(4 * best * s.keys_ig);
+  s.recs_off = s.list_off + round256(4 * best * s.samples_ig);
+  s.bytes = chunk_bytes(s.keys_ig, s.samples_ig, s.cap, best);
   s.ok = true;
   return s;
+}
+
+// Default workspace budget: the operator's ideal traffic bytes, at least one
+// (image, group) pair's workspace, at most kGatherChunkBytes.
+uint64_t default_gather_budget(const Plan& p) {
+  uint64_t b = p.ideal_bytes < kGatherChunkBytes ? p.ideal_bytes : kGatherChunkBytes;
+  const GatherShape one = gather_shape(p, 0);
+  return one.ok && one.bytes > b ? one.bytes : b;
 }
 
 typedef void (*gather_fn)(GatherArgs);
@@ -2758,9 +2803,9 @@ dcn4_status check_launch() {
 
 dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
                           const float* pscales, const void* gy, float* gx, void* ws,
-                          hipStream_t st) {
+                          uint64_t ws_bytes, hipStream_t st) {
   const dcn4_desc& d = p.desc;
-  const GatherShape sh = gather_shape(p);
+  const GatherShape sh = gather_shape(p, ws_bytes < kGatherChunkBytes ? ws_bytes : kGatherChunkBytes);
   const bool vec = p.D % (16 / p.es) == 0 && ((uintptr_t)gy & 15) == 0;
   const bool vst = vec && ((uintptr_t)gx & 15) == 0;
   const int V = vec ? 16 / p.es : 1;
@@ -2811,7 +2856,8 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   ga.Lg = Lg;
   ga.div_K = make_fastdiv((uint32_t)p.K);
   ga.div_kw = make_fastdiv((uint32_t)d.kernel_w);
-  ga.div_G = make_fastdiv((uint32_t)d.group);
+  ga.gc = sh.gc;
+  ga.div_gc = make_fastdiv((uint32_t)sh.gc);
   ga.div_W = make_fastdiv((uint32_t)d.W);
   ga.div_H = make_fastdiv((uint32_t)d.H);
   const BucketTile bt = bucket_tile(p);
@@ -2850,21 +2896,26 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
   const uint64_t om_img = (uint64_t)p.Ho * p.Wo * d.group * 3 * p.K * p.es;
   const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;
   const uint64_t x_img = (uint64_t)d.H * d.W * d.C;
-  for (int64_t n0 = 0; n0 < d.N; n0 += sh.imgs) {
+  for (int64_t n0 = 0; n0 < d.N; n0 += sh.imgs)
+  for (int32_t g0 = 0; g0 < d.group; g0 += sh.gc) {
     const int64_t nb = (d.N - n0) < sh.imgs ? (d.N - n0) : sh.imgs;
+    const int32_t gc = (d.group - g0) < sh.gc ? (d.group - g0) : sh.gc;
+    ga.g0 = g0;
+    ga.gc = gc;
+    ga.div_gc = make_fastdiv((uint32_t)gc);
     ga.f.om = static_cast<const char*>(om) + n0 * om_img;
     ga.f.pscales = pscales ? pscales + n0 * ps_img : nullptr;
     ga.gy = static_cast<const char*>(gy) + n0 * y_img;
     ga.gx = gx + n0 * x_img;
-    ga.samples = (uint32_t)(nb * sh.samples_img);
-    ga.nblocks = (int32_t)((uint64_t)nb * d.group * ga.band_groups * ga.strips);
-    const uint64_t zero_words = 64 + (uint64_t)nb * sh.keys_img;
+    ga.samples = (uint32_t)(nb * gc * sh.samples_ig);
+    ga.nblocks = (int32_t)((uint64_t)nb * gc * ga.band_groups * ga.strips);
+    const uint64_t zero_words = 64 + (uint64_t)nb * gc * sh.keys_ig;
     const uint64_t zb = (zero_words + kBlock - 1) / kBlock;
     hipLaunchKernelGGL(dcn4_fill_zero_kernel, dim3((unsigned)(zb < 65536 ? zb : 65536)),
                        dim3(kBlock), 0, st, reinterpret_cast<float*>(w), zero_words);
     dcn4_status s = check_launch();
     if (s != DCN4_OK) return s;
-    const uint64_t bblocks = (uint64_t)nb * d.group * ga.tiles_y * ga.tiles_x;
+    const uint64_t bblocks = (uint64_t)nb * gc * ga.tiles_y * ga.tiles_x;
     hipLaunchKernelGGL(bucket, dim3((unsigned)bblocks), dim3(kBlock), bt.lds_bytes, st, ga);
     if ((s = check_launch()) != DCN4_OK) return s;
     hipLaunchKernelGGL(gather, dim3((unsigned)ga.nblocks), dim3(kBlock), gather_lds, st, ga);
@@ -2880,7 +2931,12 @@ dcn4_status launch_gather(const Plan& p, const void* om, const float* scales,
 }  // namespace
 
 uint64_t backward_workspace_bytes(const Plan& p) {
-  const GatherShape s = gather_shape(p);
+  const GatherShape s = gather_shape(p, default_gather_budget(p));
+  return s.ok ? s.bytes : 0;
+}
+
+uint64_t backward_min_workspace_bytes(const Plan& p) {
+  const GatherShape s = gather_shape(p, 0);
   return s.ok ? s.bytes : 0;
 }
 
@@ -2922,11 +2978,11 @@ dcn4_status scratch_address(void** ptr) {
 dcn4_status launch_backward(const Plan& p, const void* x, const void* om,
                             const float* scales, const float* pscales,
                             const void* gy, float* gx, float* gom, void* ws,
-                            void* stream, bool vector_path) {
+                            uint64_t ws_bytes, void* stream, bool vector_path) {
   const dcn4_desc& d = p.desc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (gx && ws) {
-    const dcn4_status s = launch_gather(p, om, scales, pscales, gy, gx, ws, st);
+    const dcn4_status s = launch_gather(p, om, scales, pscales, gy, gx, ws, ws_bytes, st);
     if (s != DCN4_OK) return s;
     gx = nullptr;  // done: what remains is grad_om
   }

@@ -293,13 +293,17 @@ dcn4_status dcn4_backward(const dcn4_plan* plan, const void* x,
                           const float* pixel_scales, const void* grad_y,
                           float* grad_x, float* grad_offset_mask, void* stream);
 
-/* Bytes of device workspace dcn4_backward_ws needs to gather grad_x: for
- * each chunk of images one launch sequence handles, a 256-byte counter, a
- * 4-byte count per (cell, group) bucket ((H+1)*(W+1)*G per image), a 4-byte
- * overflow entry per sample (Ho*Wo*G*K per image) and 16 * capacity bytes of
- * records per bucket; chunks hold at most 2 GiB unless one image needs more.
- * 0 when one image has 2^31 or more samples, buckets or gather lanes: then
- * grad_x is always scattered with atomics.  Errors: DCN4_ERR_NULL. */
+/* Bytes of device workspace dcn4_backward_ws needs to gather grad_x.  The
+ * gather runs over the batch in chunks of images x groups: at most as many
+ * (image, group) pairs per chunk as fit the operator's ideal traffic bytes
+ * (dcn4_query; at least one pair, at most 2 GiB), as few chunks as that
+ * allows, of even size; a chunk's workspace is a
+ * 256-byte counter, a 4-byte count per bucket ((H+1)*(W+1) cells per image
+ * and group), a 4-byte overflow entry per sample (Ho*Wo*K per image and
+ * group), each of these three rounded up to 256 bytes, and 16 * capacity
+ * bytes of records per bucket.  0 when one image has 2^31 or more samples or
+ * buckets: then grad_x is always scattered with atomics.  Errors:
+ * DCN4_ERR_NULL. */
 dcn4_status dcn4_backward_workspace_size(const dcn4_plan* plan, uint64_t* bytes);
 
 /* dcn4_backward with a caller-owned workspace: `workspace` is a device
@@ -344,9 +348,10 @@ dcn4_status dcn4_backward_scales(const dcn4_plan* plan, const void* x,
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the gathered grad_x takes its workspace from a static device array of the
  * library, 64 MiB per GPU, held from the library's load until the process
- * ends; the call allocates nothing.  Problems whose workspace
- * (dcn4_backward_workspace_size) exceeds 64 MiB are refused with
- * DCN4_ERR_UNSUPPORTED before anything is enqueued (use dcn4_backward_ws).
+ * ends, in chunks of as many (image, group) pairs as fit it; the call
+ * allocates nothing.  A problem whose single (image, group) pair needs more
+ * than 64 MiB is refused with DCN4_ERR_UNSUPPORTED before anything is
+ * enqueued (use dcn4_backward_ws).
  * Every call on one GPU shares that GPU's array: calls that overlap in time
  * on one GPU (different streams, or threads without ordering) race and give
  * wrong gradients; calls ordered on one stream are safe.  The array's

@@ -362,10 +362,11 @@ class TestForwardValidation:
 
     def test_noalloc_refuses_beyond_its_scratch(self):
         """dcn4_backward_noalloc gathers grad_x in the library's static 64 MiB
-        workspace: a problem needing more is refused before anything is
-        enqueued, with a message naming the entry point to use instead."""
+        workspace, in chunks of (image, group) pairs that fit it: a problem
+        whose single pair needs more is refused before anything is enqueued,
+        with a message naming the entry point to use instead."""
         G1 = 1 << 30   # fake device addresses 1 GiB apart: no overlap
-        big = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
+        big = d4.Plan(desc_of(Shape(1, 1024, 1024, 16, 1), "bf16"))
         assert big.backward_workspace_bytes() > (64 << 20)
         st = d4.dcn4_backward_noalloc(big.handle, G1, 2 * G1, None, None, 3 * G1, 4 * G1,
                                       5 * G1, None)
@@ -429,29 +430,48 @@ class TestForwardValidation:
         assert dw(M, 2 * M, 3 * M, 3 * M) == d4.DCN4_ERR_INVALID_ARG         # over the bias
 
     def test_backward_workspace_size(self):
-        """The documented layout: a 256-byte counter, 4 bytes per (cell,
-        group) bucket, 4 bytes per sample, 16 * capacity bytes per bucket,
-        each of the first three regions rounded up to 256 bytes; batches
-        beyond 2 GiB are split into chunks of whole images."""
+        """The documented layout: chunks of images x groups of at most as many
+        (image, group) pairs as fit the operator's ideal traffic bytes (at
+        least one pair, at most 2 GiB), as few chunks as possible and those
+        evened out; a chunk's
+        workspace is a 256-byte counter, 4 bytes per bucket, 4 bytes per
+        sample (the first three regions rounded up to 256 bytes) and
+        16 * capacity bytes per bucket."""
         r256 = lambda b: (b + 255) // 256 * 256
+
+        def expected(plan, desc, cap):
+            keys = (desc.H + 1) * (desc.W + 1)
+            samples = plan.Ho * plan.Wo * desc.kernel_h * desc.kernel_w
+            f = lambda n: 256 + r256(4 * n * keys) + r256(4 * n * samples) + 16 * n * keys * cap
+            budget = max(min(plan.ideal_bytes, 2 << 30), f(1))
+            pairs = max(n for n in range(1, desc.N * desc.group + 1) if f(n) <= budget) \
+                if f(1) <= budget else 1
+            # fewest chunks, then evened out: the smallest chunk for that count
+            opts = []
+            for gc in range(1, desc.group + 1):
+                imgs = min(desc.N, pairs // gc)
+                if imgs:
+                    ci, cg = -(-desc.N // imgs), -(-desc.group // gc)
+                    opts.append((ci * cg, -(-desc.N // ci) * -(-desc.group // cg)))
+            return f(min(opts)[1])
+
         for desc, cap in ((mk(), 0), (mk(N=3, H=21, W=13, kernel_h=5, kernel_w=5, pad_h=2,
                                          pad_w=2), 7),
-                          (mk(N=2, H=30, W=30, stride_h=2, stride_w=2), 0)):
+                          (mk(N=2, H=30, W=30, stride_h=2, stride_w=2), 0),
+                          (mk(N=5, H=40, W=36, C=96, group=6), 4),
+                          (mk(N=64, H=64, W=64, C=64, group=4), 1024)):
             plan = d4.Plan(desc, bucket_capacity=cap)
             c = plan.info()["bucket_capacity"]
             if cap:
                 assert c == cap
-            keys = desc.N * (desc.H + 1) * (desc.W + 1) * desc.group
-            samples = desc.N * plan.Ho * plan.Wo * desc.group * desc.kernel_h * desc.kernel_w
-            want = 256 + r256(4 * keys) + r256(4 * samples) + 16 * keys * c
-            assert plan.backward_workspace_bytes() == want
-        big = d4.Plan(mk(N=64, H=64, W=64, C=64, group=4), bucket_capacity=1024)
-        per_img = 65 * 65 * 4 * (4 + 16 * 1024) + 64 * 64 * 4 * 9 * 4
-        imgs = (2 << 30) // per_img
-        assert 1 < imgs < 64
-        assert big.backward_workspace_bytes() == (256 + r256(4 * imgs * 65 * 65 * 4) +
-                                                  r256(4 * imgs * 64 * 64 * 4 * 9) +
-                                                  16 * imgs * 65 * 65 * 4 * 1024)
+            want = expected(plan, desc, c)
+            assert plan.backward_workspace_bytes() == want, (desc, want)
+            one = expected(plan, desc.__class__(**{**desc.__dict__, "N": 1, "group": 1,
+                                                   "C": desc.C // desc.group}), c)
+            assert want <= max(plan.ideal_bytes, one)
+        # the latent-diffusion block's workspace stays within its ideal bytes
+        unet = d4.Plan(desc_of(Shape(8, 128, 128, 320, 20), "bf16"))
+        assert 0 < unet.backward_workspace_bytes() <= unet.ideal_bytes
 
     def test_bucket_capacity_option(self):
         p = d4.Plan(mk())

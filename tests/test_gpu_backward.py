@@ -243,19 +243,29 @@ def test_gather_overflow(case, cap):
 
 
 def test_gather_chunks():
-    """A workspace above 2 GiB for the batch (1024 records per bucket) is
-    split into chunks of images that reuse one workspace."""
+    """The gathered grad_x runs in chunks of (image, group) pairs that reuse
+    one workspace: with 1024 records per bucket one pair needs more than the
+    operator's ideal bytes, so the default workspace holds one pair (32
+    chunks); a caller's workspace of three and a half pairs runs the fewest
+    chunks that fit it, three images of one group (the last chunk of each
+    group holding two images)."""
     s = Shape(8, 64, 64, 64, 4)
     dt = "bf16"
     plan = d4.Plan(desc_of(s, dt), bucket_capacity=1024)
-    one = d4.Plan(desc_of(Shape(1, 64, 64, 64, 4), dt), bucket_capacity=1024)
+    one = d4.Plan(desc_of(Shape(1, 64, 64, 16, 1), dt), bucket_capacity=1024)
     ws = plan.backward_workspace_bytes()
-    assert ws < 8 * one.backward_workspace_bytes() and ws > 4 * one.backward_workspace_bytes()
+    assert ws == one.backward_workspace_bytes() and ws > plan.ideal_bytes
     inp, gy = bwd_inputs(s, dt, seed=808)
     say(f"gather chunks: {s} {dt}, workspace {ws} bytes")
     ref = oracle.get().backward(s, dt, inp.x, inp.om, gy)
     gx, _ = run_backward(plan, inp, gy, dt, want_om=False)
-    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], "gather chunks")
+    check_bound(gx, ref["gx"], ref["gx_abs"], ref["max_terms"], "gather chunks of one pair")
+    big = torch.empty(ws * 7 // 2, dtype=torch.uint8, device="cuda")
+    x, om, g = to_dev(inp.x, dt), to_dev(inp.om, dt), to_dev(gy, dt)
+    gx2, _ = plan.backward(x, om, g, want_om=False, workspace=big)
+    torch.cuda.synchronize()
+    check_bound(gx2.cpu().numpy(), ref["gx"], ref["gx_abs"], ref["max_terms"],
+                "gather chunks of three images")
 
 
 def test_backward_allocating_entry():
