@@ -97,6 +97,7 @@ class Oracle:
         lib.dcn4o_count_terms.argtypes = [sp, ctypes.c_int, P, P, P, i64p, i64p]
         lib.dcn4o_backward.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P, i64p]
         lib.dcn4o_backward_scales.argtypes = [sp, ctypes.c_int, P, P, P, P, P, P, P, P, P]
+        lib.dcn4o_softmax_weights.argtypes = [sp, ctypes.c_int, P, P]
         lib.dcn4o_linear_f64.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int, P, P, P, P, P]
         lib.dcn4o_dwconv3x3.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -264,6 +265,40 @@ class Oracle:
         if r:
             raise ValueError("oracle rejected the call")
         return out
+
+    def softmax_weights(self, s: Shape, dtype: str, om) -> np.ndarray:
+        """DCNv3's softmax over each (pixel, group) row's K weights (reading
+        R18), offsets unchanged: fp64 [N,Ho,Wo,G,3K] from the raw om."""
+        dt = DTYPE_CODES[dtype]
+        om = np.ascontiguousarray(om, dtype=RAW_NP[dt])
+        ho, wo = self.out_size(s)
+        out = np.empty((s.N, ho, wo, s.G, 3 * s.K), np.float64)
+        assert om.size == out.size
+        r = self.lib.dcn4o_softmax_weights(ctypes.byref(s.c_struct()), dt,
+                                           self._ptr(om), self._ptr(out))
+        if r:
+            raise ValueError("oracle rejected the call")
+        return out
+
+    def dcnv3_forward_f64(self, s: Shape, dtype: str, x, om, pix=None,
+                          nthreads: int = 8):
+        """The DCNv3-style output: the aggregation with softmax weights,
+        sum_k w_k * bilinear(x, p_k), in fp64, and the sum of the absolute
+        values of its terms (the aggregation of |x| with the same weights,
+        which are positive). The weights enter the fp64 aggregation rounded to fp32 (a relative
+        change of at most 2^-24 each); x is decoded exactly."""
+        w = self.softmax_weights(s, dtype, om).astype(np.float32)
+        dt = DTYPE_CODES[dtype]
+        xr = np.ascontiguousarray(x, dtype=RAW_NP[dt])
+        if dt == 0:
+            xf = xr
+        elif dt == 1:
+            xf = (xr.astype(np.uint32) << 16).view(np.float32)
+        else:
+            xf = xr.view(np.float16).astype(np.float32)
+        y = self.forward_f64(s, "f32", xf, w, pix=pix, nthreads=nthreads)
+        a = self.forward_f64(s, "f32", np.abs(xf), w, pix=pix, nthreads=nthreads)
+        return y, a
 
     def linear(self, dtype: str, feat, weight, bias=None):
         """The merged offset/weight layer in fp64: (out [M, Nout], absum).

@@ -40,6 +40,8 @@
  *     definition): at an integer location the derivative from above (the
  *     cell of the floor), a sample that is not inside has zero gradient, and
  *     the sampling decisions are the fp32 evaluation's (see dcn4o_backward);
+ *  R18 DCNv3's softmax (dcn4o_softmax_weights): over the K weights of each
+ *     (pixel, group) row, offsets unchanged ([DCNv4 digest] section 1);
  *  R8 fp32 evaluation order (dcn4o_forward_f32): the location is kept as an
  *     exact integer part and a fraction.  The displacement from the integer
  *     base is t = fl(offset_scale*delta) (multi-scale: t = fl(s_g * fl(grid +
@@ -649,6 +651,31 @@ int dcn4o_backward_scales(const dcn4o_shape* s, int dtype, const void* x, const 
       if (gs) gs[g] += sig * dS;
       if (gs_abs) gs_abs[g] += fabs(sig) * aS;
     }
+  }
+  return 0;
+}
+
+/* ----------------------------------------------- DCNv3's softmax weights (R18)
+ * The largest weight is found by comparisons, which a NaN never wins; the
+ * NaN then reaches every weight of its row through the sum.  With M = +inf,
+ * exp(+inf - inf) is NaN; a row of -inf has M = -inf and -inf - -inf = NaN. */
+int dcn4o_softmax_weights(const dcn4o_shape* s, int dtype, const void* om, double* out) {
+  int32_t Ho, Wo;
+  if (dcn4o_check(s, &Ho, &Wo)) return -1;
+  const int K = s->kh * s->kw;
+  const int64_t rows = (int64_t)s->N * Ho * Wo * s->G;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t base = r * 3 * K;
+    for (int i = 0; i < 2 * K; ++i) out[base + i] = load_f32(dtype, om, base + i);
+    double M = -INFINITY;
+    for (int k = 0; k < K; ++k) {
+      const double m = load_f32(dtype, om, base + 2 * K + k);
+      if (m > M) M = m;
+    }
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += exp((double)load_f32(dtype, om, base + 2 * K + k) - M);
+    for (int k = 0; k < K; ++k)
+      out[base + 2 * K + k] = exp((double)load_f32(dtype, om, base + 2 * K + k) - M) / sum;
   }
   return 0;
 }

@@ -147,6 +147,17 @@ int dcn4o_dwconv3x3(int32_t N, int32_t H, int32_t W, int32_t C, int dtype,
                     const void* x, const void* w, const float* bias,
                     double* out64, void* out_raw);
 
+/* DCNv3's normalisation of the aggregation weights, the step DCNv4 removes
+ * ([DCNv4 digest] abstract and section 1 "移除Softmax归一化": DCNv3 passes
+ * the weights through a softmax, bounding them to (0, 1)).  Reading R18: a
+ * softmax over the K weights of each (output pixel, group) row,
+ *   w_k = exp(m_k - M) / sum_j exp(m_j - M),  M = the largest m_j,
+ * the offsets unchanged.  om is [N,Ho,Wo,G,3K] in the I/O dtype (R4); out
+ * (fp64, same shape) receives the offsets as decoded and the exact weights.
+ * A NaN or +inf weight makes its whole row's weights NaN, as does a row of
+ * -inf.  0 or -1 (invalid shape). */
+int dcn4o_softmax_weights(const dcn4o_shape* s, int dtype, const void* om, double* out);
+
 /* Ideal traffic of one forward pass in bytes: input + output feature maps
  * plus the offset/weight tensor, each read or written once, plus 4G bytes of
  * fp32 scales in multi-scale mode and 4*N*Ho*Wo*G bytes of pixel scales

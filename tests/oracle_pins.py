@@ -944,13 +944,94 @@ def pin_dwconv3x3(o):
     exact_equal(a3, a1 + a2, "linearity")
 
 
+def pin_softmax_weights(o):
+    """DCNv3's softmax over each (pixel, group) row's K weights (reading R18;
+    [DCNv4 digest] section 1 names it as the step DCNv4 removes):
+    (a) equal weights give the uniform 1/K; a 1x1 kernel gives exactly 1;
+    (b) equals scipy's softmax (library routine) along the K weights of each
+        (pixel, group), every dtype, with the offsets passed through unchanged;
+    (c) adding a constant to a row's weights changes nothing;
+    (d) a weight of 1000 (fp32) takes the whole row without overflow;
+    (e) a NaN or +inf weight makes its row NaN and only its row; -inf
+        weights get 0 next to finite ones;
+    (f) with zero offsets and equal weights the DCNv3 output is the K-point
+        box average: torch's depthwise conv2d with a 1/K kernel."""
+    import scipy.special
+    import torch
+    rng = np.random.default_rng(61)
+    # (a)
+    s = Shape(1, 5, 6, 8, 2)
+    ho, wo = o.out_size(s)
+    z = np.zeros((s.N, ho, wo, s.G, s.K), np.float32)
+    m = np.broadcast_to(dyadic(rng, (s.N, ho, wo, s.G, 1), -2, 2, 4), z.shape)
+    w = o.softmax_weights(s, "f32", pack_om(z, z, m))[..., 2 * s.K:]
+    assert np.all(w == 1.0 / s.K), "equal weights: uniform"
+    s1 = Shape(1, 4, 5, 6, 3, kh=1, kw=1, ph=0, pw=0)
+    ho1, wo1 = o.out_size(s1)
+    om1 = rng.standard_normal((s1.N, ho1, wo1, s1.G, 3)).astype(np.float32) * 4
+    assert np.all(o.softmax_weights(s1, "f32", om1)[..., 2] == 1.0), "1x1: weight 1"
+    # (b)
+    for dtype, s in [("f32", Shape(2, 6, 7, 12, 3)), ("bf16", Shape(1, 5, 5, 8, 4, kh=3, kw=5, pw=2)),
+                     ("f16", Shape(1, 6, 4, 4, 1, sh=2))]:
+        ho, wo = o.out_size(s)
+        om = (rng.standard_normal((s.N, ho, wo, s.G, 3 * s.K)) * 2).astype(np.float32)
+        raw = to_raw(om, dtype)
+        dec = from_raw(raw, dtype).astype(np.float64)
+        got = o.softmax_weights(s, dtype, raw)
+        exact_equal(got[..., :2 * s.K], dec[..., :2 * s.K], f"offsets unchanged {dtype}")
+        want = scipy.special.softmax(dec[..., 2 * s.K:], axis=-1)
+        np.testing.assert_allclose(got[..., 2 * s.K:], want, rtol=1e-14, atol=0,
+                                   err_msg=f"softmax {dtype}")
+    # (c)
+    s = Shape(1, 4, 4, 4, 2)
+    ho, wo = o.out_size(s)
+    om = dyadic(rng, (s.N, ho, wo, s.G, 3 * s.K), -3, 3, 16)
+    om2 = om.copy()
+    om2[..., 2 * s.K:] += 5.0
+    np.testing.assert_allclose(o.softmax_weights(s, "f32", om2),
+                               o.softmax_weights(s, "f32", om), rtol=1e-14, atol=0,
+                               err_msg="shift invariance")
+    # (d)
+    om3 = om.copy()
+    om3[..., 2 * s.K:] = 0.0
+    om3[..., 2 * s.K + 4] = 1000.0
+    w = o.softmax_weights(s, "f32", om3)[..., 2 * s.K:]
+    assert np.all(w[..., 4] == 1.0) and np.all(np.delete(w, 4, axis=-1) == 0.0), "large weight"
+    # (e)
+    om4 = om.copy()
+    om4[0, 1, 2, 0, 2 * s.K + 3] = np.nan
+    om4[0, 2, 1, 1, 2 * s.K + 7] = np.inf
+    om4[0, 3, 3, 0, 2 * s.K:2 * s.K + 4] = -np.inf
+    w = o.softmax_weights(s, "f32", om4)[..., 2 * s.K:]
+    ref = o.softmax_weights(s, "f32", om)[..., 2 * s.K:]
+    assert np.all(np.isnan(w[0, 1, 2, 0])) and np.all(np.isnan(w[0, 2, 1, 1])), "NaN rows"
+    assert np.all(w[0, 3, 3, 0, :4] == 0.0) and np.isclose(w[0, 3, 3, 0].sum(), 1.0, rtol=1e-15)
+    keep = np.ones(w.shape[:-1], bool)
+    keep[0, 1, 2, 0] = keep[0, 2, 1, 1] = keep[0, 3, 3, 0] = False
+    exact_equal(w[keep], ref[keep], "other rows untouched")
+    # (f)
+    s = Shape(2, 7, 9, 6, 3)
+    ho, wo = o.out_size(s)
+    x = rng.standard_normal((s.N, s.H, s.W, s.C)).astype(np.float32)
+    z = np.zeros((s.N, ho, wo, s.G, s.K), np.float32)
+    mm = np.broadcast_to(rng.standard_normal((s.N, ho, wo, s.G, 1)).astype(np.float32), z.shape)
+    y, a = o.dcnv3_forward_f64(s, "f32", x, pack_om(z, z, mm))
+    ref = torch.nn.functional.conv2d(
+        torch.from_numpy(x.astype(np.float64)).permute(0, 3, 1, 2),
+        torch.full((s.C, 1, 3, 3), 1.0 / 9.0, dtype=torch.float64), padding=1, groups=s.C)
+    ref = ref.permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-6 * np.abs(ref).max(),
+                               err_msg="DCNv3 box average")
+    assert np.all(a >= np.abs(y) - 1e-12), "absolute sum bounds the output"
+
+
 ALL_PINS = [pin_output_size, pin_identity, pin_integer_gather,
             pin_affine_reproduction, pin_depthwise_conv, pin_zero_padding,
             pin_partition_of_unity, pin_linearity, pin_multiscale,
             pin_pixel_scales, pin_nonfinite_offsets, pin_term_count, pin_ideal_bytes,
             pin_exact_rational, pin_geometry, pin_codecs, pin_backward_weights,
             pin_backward_adjoint, pin_backward_offsets, pin_backward_scales,
-            pin_offset_linear, pin_dwconv3x3]
+            pin_offset_linear, pin_dwconv3x3, pin_softmax_weights]
 
 
 if __name__ == "__main__":

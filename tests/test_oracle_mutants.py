@@ -107,6 +107,21 @@ MUTANTS = {
     "scale_grad_sigma_factor_lost": sub("if (gs) gs[g] += sig * dS;", "if (gs) gs[g] += dS;"),
     "scale_grad_prior_factor_lost": sub("if (gp) gp[p * G + g] = (double)scales[g] * dS;",
                                         "if (gp) gp[p * G + g] = dS;"),
+    # DCNv3's softmax weights (R18): no max shift, the sum over the offsets,
+    # a term of the sum lost, the offsets not passed through, the maximum
+    # taken without the first weight
+    "softmax_no_max_shift": subs(
+        ("sum += exp((double)load_f32(dtype, om, base + 2 * K + k) - M);",
+         "sum += exp((double)load_f32(dtype, om, base + 2 * K + k));"),
+        ("exp((double)load_f32(dtype, om, base + 2 * K + k) - M) / sum;",
+         "exp((double)load_f32(dtype, om, base + 2 * K + k)) / sum;")),
+    "softmax_sum_over_offsets": sub("sum += exp((double)load_f32(dtype, om, base + 2 * K + k) - M);",
+                                    "sum += exp((double)load_f32(dtype, om, base + k) - M);"),
+    "softmax_last_term_lost": sub("for (int k = 0; k < K; ++k) sum +=", "for (int k = 0; k < K - 1; ++k) sum +="),
+    "softmax_offsets_half_copied": sub("for (int i = 0; i < 2 * K; ++i) out[base + i]",
+                                       "for (int i = 0; i < K; ++i) out[base + i]"),
+    "softmax_max_skips_first": sub("for (int k = 0; k < K; ++k) {\n      const double m = load_f32(dtype, om, base + 2 * K + k);",
+                                   "for (int k = 1; k < K; ++k) {\n      const double m = load_f32(dtype, om, base + 2 * K + k);"),
     # merged offset/weight layer: weight transposed, bias lost, a term lost
     "linear_weight_transposed": sub("(double)load_f32(dtype, weight, (int64_t)j * Cin + k);",
                                     "(double)load_f32(dtype, weight, (int64_t)k * Nout + j);"),
