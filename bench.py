@@ -118,6 +118,13 @@ def main():
     ap.add_argument("--dwconv", action="store_true",
                     help="time the depthwise 3x3 convolution (dcn4_dwconv3x3) on the "
                          "workload's input feature map")
+    ap.add_argument("--eager", action="store_true",
+                    help="time one launch per Python call instead of replaying the "
+                         "captured K steps")
+    ap.add_argument("--dcnv3", action="store_true",
+                    help="time the DCNv3-style comparison (softmax pass, then the "
+                         "one-thread-per-channel aggregation) beside the default "
+                         "DCNv4 plan on the same inputs")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="instead of the operator, run plain device copies of MIB "
                          "MiB (the scale reference for the HBM byte counters)")
@@ -146,6 +153,8 @@ def main():
         return bench_linear(args, torch, np, workloads, d4, name, w)
     if args.dwconv:
         return bench_dwconv(args, torch, np, workloads, d4, name, w)
+    if args.dcnv3:
+        return bench_dcnv3(args, torch, np, workloads, d4, name, w)
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
@@ -177,13 +186,28 @@ def main():
         sets.append((dev_tensor(inp.x), dev_tensor(inp.om), sc, ps, y))
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, st=None):
         x, om, sc, ps, y = sets[i % nsets]
-        plan.forward(x, om, sc, out=y, stream=stream.cuda_stream, pixel_scales=ps)
+        plan.forward(x, om, sc, out=y, stream=(st or stream).cuda_stream, pixel_scales=ps)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    # The K steps are captured once in a HIP graph and the timed region
+    # replays it: one host call enqueues every launch, so the GPU runs them
+    # back to back whatever the host thread is doing (eagerly, the host's
+    # enqueue time per step varied between ~8 and ~190 us from run to run
+    # on the same box).  --eager times the launches one Python call each.
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream(dev)
+            for i in range(args.steps):
+                step(i, cap)
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
 
     # the timed region: exactly `steps` steps between two synchronisations
     t0 = torch.cuda.Event(enable_timing=True)
@@ -191,9 +215,13 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     t1.record(stream)
+    host_enqueue = time.perf_counter() - wall0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
@@ -244,6 +272,7 @@ def main():
                    "group_scales": w.multiscale, "pixel_scales": w.pixel_scales,
                    "max_scale": w.max_scale, "Ho": Ho, "Wo": Wo,
                    "ideal_bytes": ideal, "input_sets": nsets,
+                   "launch": "eager" if graph is None else "hip_graph",
                    "plan": plan.info()},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "output_pixels_per_s": round(out_pix / (ms_per_step * 1e-3), 1),
@@ -253,6 +282,7 @@ def main():
                       "min": round(min(per_launch_ms) * 1e3, 3),
                       "max": round(max(per_launch_ms) * 1e3, 3)},
         "wall_s_timed": round(wall, 4),
+        "host_enqueue_us_per_step": round(host_enqueue / args.steps * 1e6, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -347,6 +377,98 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
                    "workspace_bytes": ws_bytes, "bucket_capacity": plan.info()["bucket_capacity"],
                    "ideal_bytes": ideal, "input_sets": nsets},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kernel_source": kernel_source_digest()}), flush=True)
+
+
+def timed_steps(torch, dev, stream, step, args):
+    """ms per step of `step(i, hip_stream)` over args.steps steps after
+    args.warmup eager ones; the steps replayed from a captured HIP graph
+    unless args.eager."""
+    for i in range(args.warmup):
+        step(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream(dev).cuda_stream
+            for i in range(args.steps):
+                step(i, cap)
+        graph.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i, stream.cuda_stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / args.steps
+
+
+def bench_dcnv3(args, torch, np, workloads, d4, name, w):
+    """DCNv4 against DCNv3's design on the same inputs and GPU ([DCNv4
+    digest] abstract: DCNv4's forward reported more than three times as fast
+    as DCNv3's).  Three timed legs of `steps` launches each, inputs rotated
+    as in the forward benchmark: the default DCNv4 plan (dcn4_forward), the
+    one-thread-per-channel aggregation (dcn4_dcnv3_forward, the same result
+    bit for bit), and the softmax pass (dcn4_dcnv3_softmax).  DCNv3's
+    operator is the aggregation; its module also runs the softmax, reported
+    as a second ratio.  Ideal bytes as in the forward benchmark (the softmax
+    pass: the offset/weight tensor read and written once)."""
+    desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+                   w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
+                   w.pixel_scales, w.max_scale)
+    plan = d4.Plan(desc)
+    Ho, Wo = plan.Ho, plan.Wo
+    ideal = plan.ideal_bytes
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_tensor(raw):
+        t = torch.from_numpy(raw) if w.dtype == "f32" else torch.from_numpy(raw.view(np.int16)).view(tdt)
+        return t.to(dev)
+
+    nsets = args.sets or max(2, math.ceil((1 << 30) / max(ideal, 1)))
+    sets = []
+    for r in range(nsets):
+        inp = workloads.make_inputs(w, Ho, Wo, seed=w.seed + r)
+        om = dev_tensor(inp.om)
+        sets.append((dev_tensor(inp.x), om, torch.empty_like(om),
+                     torch.empty(plan.out_shape(), dtype=tdt, device=dev)))
+    torch.cuda.synchronize()
+    legs = {
+        "dcn4_forward": lambda i, st: plan.forward(
+            sets[i % nsets][0], sets[i % nsets][1], out=sets[i % nsets][3], stream=st),
+        "dcnv3_aggregation": lambda i, st: plan.dcnv3_forward(
+            sets[i % nsets][0], sets[i % nsets][1], out=sets[i % nsets][3], stream=st),
+        "dcnv3_softmax": lambda i, st: plan.dcnv3_softmax(
+            sets[i % nsets][1], out=sets[i % nsets][2], stream=st),
+    }
+    us = {}
+    for leg, step in legs.items():
+        us[leg] = timed_steps(torch, dev, stream, step, args) * 1e3
+        print(f"# {leg}: {us[leg]:.2f} us per launch", file=sys.stderr, flush=True)
+    om_bytes = w.N * Ho * Wo * w.G * 3 * w.K * (4 if w.dtype == "f32" else 2)
+    v4 = us["dcn4_forward"]
+    print(json.dumps({
+        "metric": "DCNv4 forward against DCNv3's design: time ratio (DCNv3 / DCNv4)",
+        "value": round(us["dcnv3_aggregation"] / v4, 3), "unit": "x",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(v4 * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded, the workload's shapes and distributions)",
+        "config": {"workload": name, "ideal_bytes": ideal, "input_sets": nsets,
+                   "launch": "eager" if args.eager else "hip_graph", "plan": plan.info()},
+        "us_per_launch": {k: round(v, 3) for k, v in us.items()},
+        "ideal_gbs": {"dcn4_forward": round(ideal / v4 * 1e-3, 1),
+                      "dcnv3_aggregation": round(ideal / us["dcnv3_aggregation"] * 1e-3, 1),
+                      "dcnv3_softmax": round(2 * om_bytes / us["dcnv3_softmax"] * 1e-3, 1)},
+        "ratio_with_softmax": round((us["dcnv3_aggregation"] + us["dcnv3_softmax"]) / v4, 3),
         "kernel_source": kernel_source_digest()}), flush=True)
 
 

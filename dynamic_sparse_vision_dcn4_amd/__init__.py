@@ -102,6 +102,8 @@ _lib.dcn4_plan_info.argtypes = [_P, ctypes.POINTER(dcn4_launch_info)]
 _lib.dcn4_plan_set_option.argtypes = [_P, ctypes.c_int32, ctypes.c_int32]
 _lib.dcn4_forward.argtypes = [_P, _P, _P, _P, _P, _P]
 _lib.dcn4_forward_scaled.argtypes = [_P, _P, _P, _P, _P, _P, _P]
+_lib.dcn4_dcnv3_softmax.argtypes = [_P, _P, _P, _P]
+_lib.dcn4_dcnv3_forward.argtypes = [_P, _P, _P, _P, _P]
 _lib.dcn4_probe_geometry.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.dcn4_backward_ws.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P]
@@ -122,7 +124,7 @@ for _f in ("dcn4_create", "dcn4_query", "dcn4_plan_info",
            "dcn4_plan_set_option", "dcn4_forward", "dcn4_forward_scaled",
            "dcn4_probe_geometry", "dcn4_backward", "dcn4_backward_ws", "dcn4_backward_noalloc", "dcn4_backward_scales",
            "dcn4_backward_workspace_size", "dcn4_offset_linear",
-           "dcn4_dwconv3x3"):
+           "dcn4_dwconv3x3", "dcn4_dcnv3_softmax", "dcn4_dcnv3_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -163,6 +165,14 @@ def dcn4_forward_scaled(plan, x: int, offset_mask: int, group_scales: Optional[i
                         stream: Optional[int]) -> int:
     return _lib.dcn4_forward_scaled(plan, x, offset_mask, group_scales,
                                     pixel_scales, y, stream)
+
+
+def dcn4_dcnv3_softmax(plan, offset_mask: int, out: int, stream: Optional[int]) -> int:
+    return _lib.dcn4_dcnv3_softmax(plan, offset_mask, out, stream)
+
+
+def dcn4_dcnv3_forward(plan, x: int, offset_mask: int, y: int, stream: Optional[int]) -> int:
+    return _lib.dcn4_dcnv3_forward(plan, x, offset_mask, y, stream)
 
 
 def dcn4_backward(plan, x: int, offset_mask: int, group_scales: Optional[int],
@@ -435,6 +445,43 @@ class Plan:
                           out.data_ptr(), stream)
         if st != DCN4_OK:
             raise DCN4Error(st, "dcn4_forward")
+        return out
+
+    def dcnv3_softmax(self, om, out=None, stream=None):
+        """DCNv3's softmax over each (pixel, group) row's K weights of
+        om[N,Ho,Wo,G,3K], offsets unchanged (dcn4_dcnv3_softmax)."""
+        import torch
+        dt = _torch_dtype(self.desc.dtype)
+        self._check(om, self.om_shape(), dt, "offset_mask")
+        if out is None:
+            out = torch.empty(self.om_shape(), dtype=dt, device=om.device)
+        else:
+            self._check(out, self.om_shape(), dt, "out", om.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(om.device).cuda_stream
+        st = dcn4_dcnv3_softmax(self._h, om.data_ptr(), out.data_ptr(), stream)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_dcnv3_softmax")
+        return out
+
+    def dcnv3_forward(self, x, om, out=None, stream=None):
+        """The aggregation with DCNv3's one-thread-per-channel layout
+        (dcn4_dcnv3_forward); bit for bit dcn4_forward's result."""
+        import torch
+        d = self.desc
+        dt = _torch_dtype(d.dtype)
+        self._check(x, (d.N, d.H, d.W, d.C), dt, "x")
+        dev = x.device
+        self._check(om, self.om_shape(), dt, "offset_mask", dev)
+        if out is None:
+            out = torch.empty(self.out_shape(), dtype=dt, device=dev)
+        else:
+            self._check(out, self.out_shape(), dt, "out", dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        st = dcn4_dcnv3_forward(self._h, x.data_ptr(), om.data_ptr(), out.data_ptr(), stream)
+        if st != DCN4_OK:
+            raise DCN4Error(st, "dcn4_dcnv3_forward")
         return out
 
     def backward_workspace_bytes(self) -> int:

@@ -386,6 +386,40 @@ dcn4_status dcn4_forward(const dcn4_plan* plan, const void* x,
   return dcn4_forward_scaled(plan, x, offset_mask, group_scales, nullptr, y, stream);
 }
 
+dcn4_status dcn4_dcnv3_softmax(const dcn4_plan* plan, const void* offset_mask, void* out,
+                               void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  if (p.desc.use_group_scales)
+    return fail(DCN4_ERR_UNSUPPORTED, "the DCNv3-style path takes the standard geometry only");
+  if (p.desc.N == 0) return DCN4_OK;
+  if (!offset_mask || !out) return fail(DCN4_ERR_NULL, "offset_mask and out must not be NULL");
+  if (!aligned_to(offset_mask, (uintptr_t)p.es) || !aligned_to(out, (uintptr_t)p.es))
+    return fail(DCN4_ERR_MISALIGNED, "tensor pointer not aligned to its element size");
+  const uint64_t n = io_bytes(p).om;
+  if (overlaps(out, n, offset_mask, n)) return fail(DCN4_ERR_INVALID_ARG, "out overlaps offset_mask");
+  const dcn4_status s = dcn4::launch_dcnv3_softmax(p, offset_mask, out, stream);
+  if (s == DCN4_ERR_UNSUPPORTED)
+    return fail(s, "offset/weight rows too large for the softmax pass");
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
+dcn4_status dcn4_dcnv3_forward(const dcn4_plan* plan, const void* x, const void* offset_mask,
+                               void* y, void* stream) {
+  if (!plan) return fail(DCN4_ERR_NULL, "plan is NULL");
+  const dcn4::Plan& p = plan->p;
+  if (p.desc.use_group_scales)
+    return fail(DCN4_ERR_UNSUPPORTED, "the DCNv3-style path takes the standard geometry only");
+  dcn4_status s = check_io(p, x, offset_mask, nullptr, nullptr, y, true);
+  if (s != DCN4_OK || p.desc.N == 0) return s;
+  if (output_overlaps_inputs(p, y, io_bytes(p).y, x, offset_mask, nullptr, nullptr, nullptr))
+    return fail(DCN4_ERR_INVALID_ARG, "y overlaps an input");
+  s = dcn4::launch_dcnv3(p, x, offset_mask, y, stream);
+  if (s != DCN4_OK) return fail(s, dcn4::last_hip_error());
+  return DCN4_OK;
+}
+
 dcn4_status dcn4_backward_workspace_size(const dcn4_plan* plan, uint64_t* bytes) {
   if (!plan || !bytes) return fail(DCN4_ERR_NULL, "plan or bytes is NULL");
   *bytes = dcn4::backward_workspace_bytes(plan->p);

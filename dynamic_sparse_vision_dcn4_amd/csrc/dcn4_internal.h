@@ -142,6 +142,12 @@ bool tile_f16_window(const Plan& p);
 dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
                            const float* scales, const float* pscales, void* y,
                            void* stream, bool vector_path);
+// DCNv3-style comparison: the softmax pass over each (pixel, group) row's
+// weights (rows of at most kDcnv3SoftmaxLds bytes per workgroup in LDS) and
+// the one-thread-per-channel aggregation (standard geometry only).
+constexpr int32_t kDcnv3SoftmaxLds = 32768;
+dcn4_status launch_dcnv3_softmax(const Plan& p, const void* om, void* out, void* stream);
+dcn4_status launch_dcnv3(const Plan& p, const void* x, const void* om, void* y, void* stream);
 dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
                          const float* scales, const float* pscales, void* y, void* stream);
 dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,

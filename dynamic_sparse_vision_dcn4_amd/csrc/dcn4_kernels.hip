@@ -442,6 +442,104 @@ void dcn4_forward_kernel(FwdArgs a) {
 }
 
 
+// ------------------------------------------------ DCNv3-style comparison
+// DCNv3, the predecessor ([DCNv4 digest] abstract, section 1 and "方法1"),
+// normalises each (pixel, group) row's K weights with a softmax, and its
+// kernel gives every (output pixel, channel) a thread of its own, so the D
+// threads of a group each read the group's offsets and weights from memory
+// and each compute the same sampling geometry.  Built to measure DCNv4's
+// design against on this GPU.  The arithmetic per output is R8's, so on the
+// same offset/weight tensor the aggregation equals dcn4_forward bit for bit.
+
+// Softmax pass: a workgroup owns R consecutive rows of the offset/weight
+// tensor (R * 3K contiguous elements): coalesced element copies into LDS,
+// one thread per row normalises its K weights in fp32 (the largest weight
+// subtracted, expf, the sum in point order, one division, rounded to the
+// I/O dtype), coalesced copies back out with the offsets unchanged.  The
+// largest weight is found by comparisons a NaN never wins, so a NaN weight
+// reaches the row's every weight through the sum.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void dcn4_dcnv3_softmax_kernel(
+    const typename Io<DT>::raw* in, typename Io<DT>::raw* out, uint64_t rows,
+    int32_t K, int32_t R) {
+  typedef Io<DT> io;
+  typedef typename io::raw Rw;
+  extern __shared__ u32x4 lds_softmax[];
+  Rw* buf = reinterpret_cast<Rw*>(lds_softmax);
+  const uint64_t row0 = (uint64_t)blockIdx.x * (uint32_t)R;
+  const uint64_t left = rows - row0;
+  const uint32_t nr = left < (uint64_t)R ? (uint32_t)left : (uint32_t)R;
+  const uint32_t rowel = 3u * (uint32_t)K;
+  const uint32_t nel = nr * rowel;
+  const Rw* src = in + row0 * rowel;
+  Rw* dst = out + row0 * rowel;
+  for (uint32_t i = threadIdx.x; i < nel; i += kBlock) buf[i] = src[i];
+  __syncthreads();
+  if (threadIdx.x < nr) {
+    Rw* w = buf + threadIdx.x * rowel + 2 * K;
+    float M = -__builtin_inff();
+    for (int k = 0; k < K; ++k) {
+      const float m = io::dec(w[k]);
+      if (m > M) M = m;
+    }
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum += expf(io::dec(w[k]) - M);
+    for (int k = 0; k < K; ++k) w[k] = io::enc(expf(io::dec(w[k]) - M) / sum);
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < nel; i += kBlock) dst[i] = buf[i];
+}
+
+// Aggregation: one thread per (output pixel, channel) of the launch, the
+// channel fastest (a wave covers 64 consecutive channels of a pixel); the
+// offset/weight row is read from global memory by each of its D threads;
+// per point the direct kernel's geometry and one element per corner.
+template <int DT, int MODE, int KS>
+__global__ __launch_bounds__(kBlock) void dcn4_dcnv3_kernel(FwdArgs a) {
+  typedef Io<DT> io;
+  constexpr int es = io::es;
+  const uint32_t item0 = blockIdx.x * (uint32_t)kBlock;
+  const uint32_t item = item0 + threadIdx.x;
+  if (item >= (uint32_t)a.total_items) return;
+  const uint32_t p = fastdiv(item, a.div_ipp);  // ipp = C
+  const uint32_t c = item - p * (uint32_t)a.C;
+  const uint32_t g = fastdiv(c, a.div_L);       // L = D
+  const uint32_t n = fastdiv(p, a.div_hw);
+  const uint32_t rem = p - n * (uint32_t)(a.Ho * a.Wo);
+  const uint32_t yo = fastdiv(rem, a.div_wo);
+  const uint32_t xo = rem - yo * (uint32_t)a.Wo;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  const typename io::raw* om = reinterpret_cast<const typename io::raw*>(a.om) +
+                               ((uint64_t)p * (uint32_t)a.G + g) * (uint32_t)(3 * K);
+
+  // input buffer based at the image of the workgroup's first thread
+  const uint32_t n_first = fastdiv(fastdiv(item0, a.div_ipp), a.div_hw);
+  const uint64_t x_base = (uint64_t)n_first * a.img_bytes;
+  const uint64_t x_left = a.x_bytes - x_base;
+  const rsrc_t xr = make_rsrc(a.x + x_base,
+                              (uint32_t)(x_left < 0x7fffffffu ? x_left : 0x7fffffffu));
+  LaneCtx t;
+  t.pix_bytes = (uint32_t)a.C * es;
+  t.row_stride = (uint32_t)a.W * t.pix_bytes;
+  t.lane_bytes = (n - n_first) * a.img_bytes + c * es;
+  t.sg = 1.0f;
+  t.hy = t.hx = 0;
+  t.by0 = (int)yo * a.sh - a.ph;
+  t.bx0 = (int)xo * a.sw - a.pw;
+
+  float acc = 0.0f;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const Tap q = tap_geometry<DT, MODE, KS>(a, t, om, k);
+    TapData<DT, 1, 1> d;
+    d.load(xr, q);
+    d.accumulate(&acc, q);
+  }
+  asm volatile("" : "+v"(acc));  // the conversion is its own rounding
+  reinterpret_cast<typename io::raw*>(a.y)[(uint64_t)p * (uint32_t)a.C + c] = io::enc(acc);
+}
+
+
 // ------------------------------------------------------------ tiled kernel
 // Gathers from an LDS copy of the input instead of from global memory.  On
 // MI355X divergent 16-byte global gathers that miss L1 run at about 0.4 cache
@@ -2293,6 +2391,82 @@ dcn4_status launch_forward(const Plan& p, const void* x, const void* om,
     a.nblocks = (a.total_items + block - 1) / block;
     hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(block), lds,
                        static_cast<hipStream_t>(stream), a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return DCN4_ERR_HIP;
+    }
+  }
+  return DCN4_OK;
+}
+
+dcn4_status launch_dcnv3_softmax(const Plan& p, const void* om, void* out, void* stream) {
+  const dcn4_desc& d = p.desc;
+  const uint64_t rows = (uint64_t)d.N * p.Ho * p.Wo * d.group;
+  const int32_t row_bytes = 3 * p.K * p.es;
+  int32_t R = kDcnv3SoftmaxLds / row_bytes;
+  if (R > kBlock) R = kBlock;
+  if (R < 1) return DCN4_ERR_UNSUPPORTED;
+  const uint64_t nb = (rows + R - 1) / R;
+  if (nb > 0x7fffffffu) return DCN4_ERR_UNSUPPORTED;
+  const int32_t lds = R * row_bytes;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (d.dtype) {
+    case DCN4_F32:
+      hipLaunchKernelGGL(dcn4_dcnv3_softmax_kernel<DCN4_F32>, dim3((uint32_t)nb), dim3(kBlock), lds, st,
+                         static_cast<const float*>(om), static_cast<float*>(out), rows, p.K, R);
+      break;
+    case DCN4_BF16:
+      hipLaunchKernelGGL(dcn4_dcnv3_softmax_kernel<DCN4_BF16>, dim3((uint32_t)nb), dim3(kBlock), lds, st,
+                         static_cast<const uint16_t*>(om), static_cast<uint16_t*>(out), rows, p.K, R);
+      break;
+    default:
+      hipLaunchKernelGGL(dcn4_dcnv3_softmax_kernel<DCN4_F16>, dim3((uint32_t)nb), dim3(kBlock), lds, st,
+                         static_cast<const uint16_t*>(om), static_cast<uint16_t*>(out), rows, p.K, R);
+      break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    note_hip_error(e);
+    return DCN4_ERR_HIP;
+  }
+  return DCN4_OK;
+}
+
+template <int DT>
+fwd_fn dcnv3_pick(int mode, int K3) {
+  if (mode == kStdUnitScale)
+    return K3 ? dcn4_dcnv3_kernel<DT, kStdUnitScale, 3> : dcn4_dcnv3_kernel<DT, kStdUnitScale, 0>;
+  return K3 ? dcn4_dcnv3_kernel<DT, kStdScaled, 3> : dcn4_dcnv3_kernel<DT, kStdScaled, 0>;
+}
+
+dcn4_status launch_dcnv3(const Plan& p, const void* x, const void* om, void* y, void* stream) {
+  const dcn4_desc& d = p.desc;
+  if (p.mode == kGroupScale) return DCN4_ERR_UNSUPPORTED;
+  const int K3 = (d.kernel_h == 3 && d.kernel_w == 3) ? 1 : 0;
+  fwd_fn fn = d.dtype == DCN4_F32 ? dcnv3_pick<DCN4_F32>(p.mode, K3)
+            : d.dtype == DCN4_BF16 ? dcnv3_pick<DCN4_BF16>(p.mode, K3)
+                                   : dcnv3_pick<DCN4_F16>(p.mode, K3);
+  FwdArgs a{};
+  fill_common(p, a);
+  a.L = p.D;
+  a.ipp = d.C;
+  a.div_ipp = make_fastdiv((uint32_t)d.C);
+  a.div_L = make_fastdiv((uint32_t)p.D);
+  const uint64_t x_img = (uint64_t)d.H * d.W * d.C * p.es;
+  const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
+  const uint64_t om_img = (uint64_t)p.Ho * p.Wo * a.rowel * p.es;
+  for (int32_t n0 = 0; n0 < d.N; n0 += p.images_per_launch) {
+    const int32_t nb = (d.N - n0) < p.images_per_launch ? (d.N - n0) : p.images_per_launch;
+    a.x = static_cast<const char*>(x) + n0 * x_img;
+    a.om = static_cast<const char*>(om) + n0 * om_img;
+    a.y = static_cast<char*>(y) + n0 * y_img;
+    a.x_bytes = nb * x_img;
+    a.om_bytes = nb * om_img;
+    a.total_items = (int32_t)((int64_t)nb * p.Ho * p.Wo * d.C);
+    a.block = kBlock;
+    a.nblocks = (a.total_items + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       note_hip_error(e);

@@ -260,6 +260,35 @@ dcn4_status dcn4_forward_scaled(const dcn4_plan* plan, const void* x,
                                 const float* pixel_scales, void* y,
                                 void* stream);
 
+/* DCNv3-style comparison ([DCNv4 digest] abstract: DCNv4's forward pass is
+ * reported more than three times as fast as DCNv3's; section 1: DCNv3
+ * normalises the aggregation weights with a softmax; "方法1": DCNv3's kernel
+ * gives each channel of each output position its own thread, which reads the
+ * group's offsets and weights again).  Two calls, for plans in the standard
+ * geometry (group-scale plans: DCN4_ERR_UNSUPPORTED):
+ *
+ * dcn4_dcnv3_softmax writes `out` = offset_mask with each (pixel, group)
+ * row's K weights m_k replaced by exp(m_k - M) / sum_j exp(m_j - M), M the
+ * row's largest weight, computed in fp32 (expf, the sum in point order, one
+ * division) and rounded to the I/O dtype to nearest even; the offsets are
+ * copied unchanged.  A NaN or +inf weight, or a row of -inf, makes the row's
+ * weights NaN.  offset_mask and out are [N, Ho, Wo, G, 3K] in the I/O dtype,
+ * aligned to the element size, and must not overlap (DCN4_ERR_INVALID_ARG).
+ *
+ * dcn4_dcnv3_forward computes exactly what dcn4_forward computes (the same
+ * fp32 operations, bit for bit) with DCNv3's thread layout: one thread per
+ * (output pixel, channel), each reading its group's offset/weight row from
+ * global memory and computing the sampling geometry itself; pass it the
+ * output of dcn4_dcnv3_softmax for DCNv3's operator.  Same arguments and
+ * errors as dcn4_forward without scales.
+ *
+ * N == 0 enqueues nothing.  Errors: DCN4_ERR_NULL, DCN4_ERR_MISALIGNED,
+ * DCN4_ERR_INVALID_ARG, DCN4_ERR_UNSUPPORTED, DCN4_ERR_HIP. */
+dcn4_status dcn4_dcnv3_softmax(const dcn4_plan* plan, const void* offset_mask, void* out,
+                               void* stream);
+dcn4_status dcn4_dcnv3_forward(const dcn4_plan* plan, const void* x, const void* offset_mask,
+                               void* y, void* stream);
+
 /* Backward pass: the gradients of a loss L with respect to the input and to
  * the offset/weight tensor, given dL/dy.  grad_y is [N, Ho, Wo, C] in the I/O
  * dtype; grad_x [N, H, W, C] and grad_offset_mask [N, Ho, Wo, G, 3K] are fp32

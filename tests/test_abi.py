@@ -429,6 +429,32 @@ class TestForwardValidation:
         assert dw(M, 2 * M, None, 2 * M - 64) == d4.DCN4_ERR_INVALID_ARG     # over the weight
         assert dw(M, 2 * M, 3 * M, 3 * M) == d4.DCN4_ERR_INVALID_ARG         # over the bias
 
+    def test_dcnv3_checks(self):
+        """dcn4_dcnv3_softmax and dcn4_dcnv3_forward validate before
+        launching: standard-geometry plans only, non-NULL and aligned
+        tensors, no overlap of an output with an input."""
+        M = 1 << 24
+        p, ms = self.p, self.ms
+        sm = lambda pl, om, out: d4.dcn4_dcnv3_softmax(pl.handle if pl else None, om, out, None)
+        fw = lambda pl, x, om, y: d4.dcn4_dcnv3_forward(pl.handle if pl else None, x, om, y, None)
+        assert sm(None, M, 2 * M) == d4.DCN4_ERR_NULL
+        assert sm(p, None, 2 * M) == d4.DCN4_ERR_NULL
+        assert sm(p, M, None) == d4.DCN4_ERR_NULL
+        assert sm(p, M + 1, 2 * M) == d4.DCN4_ERR_MISALIGNED
+        assert sm(p, M, 2 * M + 1) == d4.DCN4_ERR_MISALIGNED
+        assert sm(p, M, M + 4096) == d4.DCN4_ERR_INVALID_ARG            # out over offset_mask
+        assert sm(ms, M, 2 * M) == d4.DCN4_ERR_UNSUPPORTED              # group scales
+        assert fw(None, M, 2 * M, 3 * M) == d4.DCN4_ERR_NULL
+        assert fw(p, None, 2 * M, 3 * M) == d4.DCN4_ERR_NULL
+        assert fw(p, M, 2 * M, None) == d4.DCN4_ERR_NULL
+        assert fw(p, M + 1, 2 * M, 3 * M) == d4.DCN4_ERR_MISALIGNED
+        assert fw(p, M, 2 * M, M + 64) == d4.DCN4_ERR_INVALID_ARG       # y over x
+        assert fw(p, M, 2 * M, 2 * M - 64) == d4.DCN4_ERR_INVALID_ARG   # y's end over offset_mask
+        assert fw(ms, M, 2 * M, 3 * M) == d4.DCN4_ERR_UNSUPPORTED
+        p0 = d4.Plan(mk(N=0))
+        assert d4.dcn4_dcnv3_softmax(p0.handle, None, None, None) == d4.DCN4_OK
+        assert d4.dcn4_dcnv3_forward(p0.handle, None, None, None, None) == d4.DCN4_OK
+
     def test_backward_workspace_size(self):
         """The documented layout: chunks of images x groups of at most as many
         (image, group) pairs as fit the operator's ideal traffic bytes (at
