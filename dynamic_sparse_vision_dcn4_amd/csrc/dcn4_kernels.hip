@@ -549,10 +549,10 @@ __global__ __launch_bounds__(kBlock) void dcn4_dcnv3_kernel(FwdArgs a) {
 // footprint plus a margin of M pixels on every side) for its chunk of GB
 // groups, and the tile's offset/weight values.  A point whose four corners
 // lie in the window is gathered from LDS -- corners outside the image read
-// the staged zeros, and fma(c, 0, acc) == acc for a finite coefficient.  When
-// any lane of a wave has a point outside the window, or a non-finite weight,
-// the whole wave takes the global path of the direct kernel for that point.
-// Both paths perform the same operations on the same values, so the result
+// the staged zeros, and fma(c, 0, acc) == acc for a finite coefficient.  A
+// lane whose point leaves the window, or whose weight is not finite, takes
+// the global path of the direct kernel for that point (its wave's other
+// lanes stay on LDS).  Both paths perform the same operations on the same values, so the result
 // does not depend on which path ran.
 typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
 // F16W: the window holds the fp16 encoding of the bf16 input (see
@@ -607,17 +607,20 @@ struct TileLane {
 // relative to window cell (c, c) (exact floats): the grid point in the
 // standard modes, the centre in group-scale mode, where gy/gx are the grid
 // offsets and sg the lane's group scale (the direct kernel's geometry, so the
-// same fp32 operations); returns false when the wave must take the global
-// path for this point (nothing accumulated then).
+// same fp32 operations); returns true when this lane must take the global
+// path for this point (nothing accumulated then).  The decision is per lane:
+// lanes whose corners lie in the window gather from LDS even when others of
+// their wave do not, so a point that leaves the window for a few lanes costs
+// global loads for those lanes only.
 // SQ: the window is square and c is its centre, so the corner cell is inside
 // iff max(|yr|, |xr|) <= ymax; the IEEE maximum propagates NaN, and m*0 is
 // NaN exactly when m is not finite, which folds the weight test in.
 // whole: the window is the whole image plus its zero border, so a cell
 // outside it is not inside the image (the definition of `inside` in
-// locate), and its sample adds nothing: only that lane skips the point
-// (the global path adds fma(0, 0, acc) = acc there, acc never being -0);
-// a non-finite weight still sends the wave to the global path, which
-// weights a corner outside the image by an exact 0 rather than m * w.
+// locate), and its sample adds nothing: that lane skips the point (the
+// global path adds fma(0, 0, acc) = acc there, acc never being -0); a
+// non-finite weight still sends its lane to the global path, which weights a
+// corner outside the image by an exact 0 rather than m * w.
 template <int DT, int VEC, int NV, int MODE, int PSC, bool SQ, bool WHOLE, bool F16W>
 __device__ __forceinline__ bool tile_point(const TileLane& w,
                                            float by, float bx, float gy, float gx,
@@ -626,30 +629,26 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
   const Loc l = sample_location<MODE>(by, bx, gy, gx, dy, dx, os, sg);
   const float fy = __builtin_floorf(l.ty), fx = __builtin_floorf(l.tx);
   const float yr = by + fy, xr = bx + fx;  // corner (y0, x0) minus (c, c)
-  uint64_t off_window;
+  bool off_window;
   bool skip = false;
   if constexpr (SQ) {
     const float tc = __builtin_elementwise_maximum(__builtin_fabsf(yr), __builtin_fabsf(xr));
     if constexpr (WHOLE) {
       skip = !(tc <= w.ymax);
-      off_window = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
+      off_window = !__builtin_isfinite(m);
     } else {
       const float t = __builtin_elementwise_maximum(tc, __builtin_fabsf(m * 0.0f));
-      off_window = __builtin_amdgcn_ballot_w64(!(t <= w.ymax));
+      off_window = !(t <= w.ymax);
     }
   } else if constexpr (WHOLE) {
     skip = !(yr >= -w.c) || !(yr <= w.ymax) || !(xr >= -w.c) || !(xr <= w.xmax);
-    off_window = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
+    off_window = !__builtin_isfinite(m);
   } else {
-    // one scalar mask per condition; NaN fails every comparison
-    off_window = __builtin_amdgcn_ballot_w64(!(yr >= -w.c)) |
-                 __builtin_amdgcn_ballot_w64(!(yr <= w.ymax)) |
-                 __builtin_amdgcn_ballot_w64(!(xr >= -w.c)) |
-                 __builtin_amdgcn_ballot_w64(!(xr <= w.xmax)) |
-                 __builtin_amdgcn_ballot_w64(!__builtin_isfinite(m));
+    // NaN fails every comparison
+    off_window = !(yr >= -w.c) || !(yr <= w.ymax) || !(xr >= -w.c) || !(xr <= w.xmax) ||
+                 !__builtin_isfinite(m);
   }
-  if (off_window != 0) return false;
-  if (skip) return true;  // outside the image: nothing to add
+  if (off_window || skip) return off_window;  // skip: outside the image, nothing to add
   const float lh = l.ty - fy, lw = l.tx - fx;
   const float hh = 1.0f - lh, hw = 1.0f - lw;
   const float cf[4] = {m * (hh * hw), m * (hh * lw), m * (lh * hw), m * (lh * lw)};
@@ -663,7 +662,7 @@ __device__ __forceinline__ bool tile_point(const TileLane& w,
   else
     d.load(a00, a10, a00, a10, PSC ? (uint32_t)PSC : w.ps);
   d.template accumulate<F16W>(acc, cf);
-  return true;
+  return false;
 }
 
 // PSC: the LDS bytes per window pixel when known at compile time (one lane
@@ -955,8 +954,8 @@ __device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa
         const float dy = io::dec(om[2 * k + 1]);
         const float m = io::dec(om[2 * K + k]);
         const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-        if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx[j], gyy, gxx, dy, dx,
-                                                           m, a.offset_scale, c.sg, acc)) {
+        if (tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx[j], gyy, gxx, dy, dx,
+                                                          m, a.offset_scale, c.sg, acc)) {
           const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
           TapData<DT, VEC, NV> d;
           d.load_swapped(xr, tg, r16);
@@ -975,8 +974,8 @@ __device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa
       const float by = GS ? ry0 : ry0 + (float)(i * a.dh);
       const float bx = GS ? rx0 : rx0 + (float)(j * a.dw);
       const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
-      if (!tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx, gyy, gxx, dy, dx, m,
-                                                         a.offset_scale, c.sg, acc)) {
+      if (tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx, gyy, gxx, dy, dx, m,
+                                                        a.offset_scale, c.sg, acc)) {
         const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
         TapData<DT, VEC, NV> d;
         d.load_swapped(xr, tg, r16);
