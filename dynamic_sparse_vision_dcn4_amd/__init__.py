@@ -73,7 +73,8 @@ class dcn4_launch_info(ctypes.Structure):
                 ("bucket_capacity", ctypes.c_int32),
                 ("tile_window", ctypes.c_int32),
                 ("tile_passes", ctypes.c_int32),
-                ("tile_f16_window", ctypes.c_int32)]
+                ("tile_f16_window", ctypes.c_int32),
+                ("tile_om_unit", ctypes.c_int32)]
 
 # dcn4_option
 DCN4_OPT_CHANNELS_PER_LANE = 0
@@ -86,11 +87,13 @@ DCN4_OPT_BUCKET_CAPACITY = 6
 DCN4_OPT_TILE_WINDOW = 7
 DCN4_OPT_TILE_PASSES = 8
 DCN4_OPT_TILE_F16_WINDOW = 9
+DCN4_OPT_TILE_OM_UNIT = 10
 OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
            "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
            "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE,
            "bucket_capacity": DCN4_OPT_BUCKET_CAPACITY, "tile_window": DCN4_OPT_TILE_WINDOW,
-           "tile_passes": DCN4_OPT_TILE_PASSES, "tile_f16_window": DCN4_OPT_TILE_F16_WINDOW}
+           "tile_passes": DCN4_OPT_TILE_PASSES, "tile_f16_window": DCN4_OPT_TILE_F16_WINDOW,
+           "tile_om_unit": DCN4_OPT_TILE_OM_UNIT}
 
 
 _P = ctypes.c_void_p

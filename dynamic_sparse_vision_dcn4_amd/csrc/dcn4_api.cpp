@@ -122,6 +122,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.tile_window = 0;
   p.tile_passes = 0;
   p.f16_window = 1;
+  p.tile_om_unit = 0;
   dcn4::resolve_tile(p);
 
   // size limits of the 32-bit device arithmetic
@@ -206,6 +207,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_window = t.whole ? 2 : 1;
     info->tile_passes = t.passes;
     info->tile_f16_window = dcn4::tile_f16_window(p) ? 1 : 0;
+    info->tile_om_unit = t.omu;
     return DCN4_OK;
   }
   info->kernel = 1;
@@ -273,6 +275,11 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     case DCN4_OPT_TILE_PASSES:
       if (value < 0 || value > 64) return fail(DCN4_ERR_INVALID_ARG, "tile passes must be 0-64");
       q.tile_passes = value;
+      break;
+    case DCN4_OPT_TILE_OM_UNIT:
+      if (value != 0 && value != 4 && value != 16)
+        return fail(DCN4_ERR_INVALID_ARG, "tile om unit must be 0, 4 or 16");
+      q.tile_om_unit = value;
       break;
     case DCN4_OPT_TILE_F16_WINDOW:
       if (value != 0 && value != 1)

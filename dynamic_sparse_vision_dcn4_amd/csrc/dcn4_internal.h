@@ -33,6 +33,7 @@ enum Mode : int32_t {
 // Threads per workgroup of the forward kernel: 4 wave64s, fewer when the
 // offset/weight rows one workgroup stages would exceed the LDS budget.
 constexpr int kBlock = 256;
+constexpr int64_t kLdsPerCu = 160 * 1024;  // LDS of one compute unit (gfx950)
 constexpr int kLdsBudget = 48 * 1024;
 
 // Everything a forward launch needs, by value (kernel argument).
@@ -85,7 +86,8 @@ struct TileArgs {
   int32_t DSL;           // channels per slice (D when not sliced)
   int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
   int32_t wrpp, wpasses; // window rows per staging pass, passes
-  int32_t OSU;           // 4-byte offset/weight units per tile pixel
+  int32_t OSU;           // offset/weight units per tile pixel
+  int32_t OMU;           // bytes per offset/weight unit: 4 or 16
   int32_t upr;           // offset/weight units per tile row, TW*OSU
   int32_t orpp;          // tile rows per offset/weight staging pass (0: by pixels)
   int32_t oppp;          // tile pixels per pass when orpp == 0
@@ -105,7 +107,7 @@ struct TileArgs {
 
 // Tile shape a plan resolved (ok == 0: the tiled kernel does not apply).
 struct TileShape {
-  int32_t ok, dp, gb, th, tw, margin, wh, ww, ps, cb, osu, lds_bytes;
+  int32_t ok, dp, gb, th, tw, margin, wh, ww, ps, cb, osu, omu, lds_bytes;
   int32_t slices;  // channel slices per group (one lane per pixel when > 1)
   int32_t whole;   // window = the whole image plus a 1-pixel zero border
   int32_t passes;  // forward: tile rows a workgroup takes under one staging
@@ -128,6 +130,7 @@ struct Plan {
   int32_t dp_user;       // 1: channels per lane set by the caller
   int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
   int32_t f16_window;    // bf16 tiled forward: 1 = fp16 window when exact, 0 = never
+  int32_t tile_om_unit;  // tiled kernels' offset/weight copy unit: 0 automatic, 4, 16
   TileShape tile;
 };
 

@@ -70,6 +70,13 @@ __device__ __forceinline__ void copy16_to_lds(rsrc_t r, char* lds_wave, uint32_t
 __device__ __forceinline__ void copy4_to_lds(rsrc_t r, char* lds_wave, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 4, (int)off, 0, 0, 0);
 }
+// The same with `unit` (4 or 16, wave-uniform) bytes per lane.
+__device__ __forceinline__ void copy_unit_to_lds(int unit, rsrc_t r, char* lds_wave, uint32_t off) {
+  if (unit == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 16, (int)off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 4, (int)off, 0, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
   return (__umulhi(n, f.m) + n) >> f.s;
@@ -847,9 +854,11 @@ __device__ __forceinline__ bool stage_window_f16(const TileArgs& a, const TileOr
 }
 
 // Stage the tile's offset/weight values at `lds_om`.  Per tile pixel the
-// chunk's GB*3K values are OSU 4-byte units from the 4-byte boundary at or
-// below their start (rows are 4-byte aligned, so the lead `mis`, returned, is
-// the same for every pixel).  Passes of orpp whole tile rows when a row's
+// chunk's GB*3K values are OSU units of OMU bytes (4 or 16: fewer copy
+// instructions for the larger unit) from the 4-byte boundary at or below their
+// start (rows are 4-byte aligned, so the lead `mis`, returned, is the same
+// for every pixel); a unit may run into the next chunk's values, which are
+// never read.  Passes of orpp whole tile rows when a row's
 // units fit the workgroup (thread t then keeps its column and unit), else
 // passes of oppp whole pixels.
 template <int es>
@@ -864,7 +873,8 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
   const rsrc_t omr = make_rsrc(a.om + (uint64_t)o.n * a.om_img_bytes, a.om_img_bytes);
   const uint32_t seg = g0 * (uint32_t)(3 * K * es);
   const uint32_t mis = seg & 3u;
-  char* om_dst = lds_om + wave0 * 4u;
+  const int unit = a.OMU;
+  char* om_dst = lds_om + wave0 * (uint32_t)unit;
   if (a.orpp == 1) {
     // one tile row per pass: the row is the same for every copying thread
     const uint32_t upx = fastdiv(t, a.div_osu), e = t - upx * (uint32_t)a.OSU;
@@ -872,14 +882,14 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
     const bool copies = t < (uint32_t)a.upr;
     const bool col_ok = xo < a.Wo;
     uint32_t off = ((uint32_t)ty0 * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
-                   (seg - mis) + 4u * e;
+                   (seg - mis) + (uint32_t)unit * e;
     const uint32_t pass_bytes = (uint32_t)a.Wo * a.om_row_bytes;
-    const uint32_t pass_lds = (uint32_t)a.upr * 4u;
+    const uint32_t pass_lds = (uint32_t)a.upr * (uint32_t)unit;
     const int rows = min(a.TH, a.Ho - ty0);  // rows of the tile inside the output
     for (int p = 0; p < a.TH; ++p) {
       if (copies) {
         const bool in = col_ok && p < rows;
-        copy4_to_lds(omr, om_dst, in ? off : kOutside);
+        copy_unit_to_lds(unit, omr, om_dst, in ? off : kOutside);
       }
       off += pass_bytes;
       om_dst += pass_lds;
@@ -893,14 +903,14 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
     const bool copies = rp < (uint32_t)a.orpp;
     int yo = ty0 + (int)rp;
     uint32_t off = ((uint32_t)yo * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
-                   (seg - mis) + 4u * e;
+                   (seg - mis) + (uint32_t)unit * e;
     const uint32_t pass_bytes = (uint32_t)a.orpp * (uint32_t)a.Wo * a.om_row_bytes;
     const int yo_end = ty0 + a.TH;
-    const uint32_t pass_lds = (uint32_t)(a.orpp * a.upr) * 4u;
+    const uint32_t pass_lds = (uint32_t)(a.orpp * a.upr) * (uint32_t)unit;
     for (int p = 0; p < a.opasses; ++p) {
       if (copies && yo < yo_end) {
         const bool in = col_ok && yo < a.Ho;
-        copy4_to_lds(omr, om_dst, in ? off : kOutside);
+        copy_unit_to_lds(unit, omr, om_dst, in ? off : kOutside);
       }
       yo += a.orpp;
       off += pass_bytes;
@@ -910,7 +920,7 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
     const uint32_t pp = fastdiv(t, a.div_osu), e = t - pp * (uint32_t)a.OSU;
     const bool copies = pp < (uint32_t)a.oppp;
     const uint32_t npix = (uint32_t)(a.TH * a.TW);
-    const uint32_t pass_lds = (uint32_t)(a.oppp * a.OSU) * 4u;
+    const uint32_t pass_lds = (uint32_t)(a.oppp * a.OSU) * (uint32_t)unit;
     for (int p = 0; p < a.opasses; ++p) {
       const uint32_t P = (uint32_t)(p * a.oppp) + pp;
       if (copies && P < npix) {
@@ -918,8 +928,8 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
         const int yo = ty0 + (int)qy, xo = tx0 + (int)qx;
         const bool in = yo < a.Ho && xo < a.Wo;
         const uint32_t off = ((uint32_t)yo * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
-                             (seg - mis) + 4u * e;
-        copy4_to_lds(omr, om_dst, in ? off : kOutside);
+                             (seg - mis) + (uint32_t)unit * e;
+        copy_unit_to_lds(unit, omr, om_dst, in ? off : kOutside);
       }
       om_dst += pass_lds;
     }
@@ -1002,6 +1012,9 @@ void dcn4_tile_kernel(TileArgs a) {
   const uint32_t t = threadIdx.x, lane = t & 63u;
   const uint32_t pix_bytes = (uint32_t)(a.C * es);
 
+  // the offset/weight copies are requested first, so that their latency
+  // overlaps the window's (both are waited for at the barriers below)
+  const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   // bf16 windows of few enough passes go through registers and become fp16
   // when every value converts exactly (stage_window_f16)
   bool f16w = false;
@@ -1016,7 +1029,6 @@ void dcn4_tile_kernel(TileArgs a) {
   } else {
     xr = stage_window<es>(a, org, lds);
   }
-  const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   __syncthreads();
 
   // Whole-image window: `passes` consecutive tile rows share one staging of
@@ -1041,7 +1053,7 @@ void dcn4_tile_kernel(TileArgs a) {
     if (yo >= a.Ho || xo >= a.Wo) continue;  // this pass has no output here
     const uint32_t g = g0 + gl;
     const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
-        lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
+        lds + a.om_lds + tp * (uint32_t)(a.OSU * a.OMU) + mis + gl * (uint32_t)(3 * K * es));
     // first channel of the lane within the pixel: its group, slice and lane
     const uint32_t chan = g * (uint32_t)a.D + org.s * (uint32_t)a.DSL + l * DP;
 
@@ -1548,7 +1560,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
   const bool active = yo < a.Ho && xo < a.Wo;
   const uint32_t g = g0 + gl;
   const typename io::raw* om = reinterpret_cast<const typename io::raw*>(
-      lds + a.om_lds + tp * (uint32_t)(a.OSU * 4) + mis + gl * (uint32_t)(3 * K * es));
+      lds + a.om_lds + tp * (uint32_t)(a.OSU * a.OMU) + mis + gl * (uint32_t)(3 * K * es));
 
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   const uint32_t row_lds = (uint32_t)(a.WW * a.PS);
@@ -2504,19 +2516,41 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   if (p.tile_pad && ((ps / 16) % 2 == 0)) ps += 16;  // odd number of 16-byte chunks
   if ((int64_t)ww * (ps / 16) > kBlock) return false;  // a window row per pass
   // offset/weight units: the chunk's values from the 4-byte boundary below
-  // their start (a 2-byte lead when 16-bit values start mid-word)
-  const int32_t ob = gb * 3 * p.K * p.es;
-  const int32_t osu = (ob + (p.es == 2 ? 2 : 0) + 3) / 4;
-  if (osu > kBlock) return false;
+  // their start (a 2-byte lead when 16-bit values start mid-word), in units
+  // of 4 or 16 bytes
+  const int32_t ob = gb * 3 * p.K * p.es + (p.es == 2 ? 2 : 0);
   const int64_t win = (int64_t)wh * ww * ps;
   // window, offset/weight values, and (bf16) 16 bytes for the workgroup's
   // agreement on the window encoding
-  const int64_t lds = ((win + 15) & ~int64_t(15)) + (int64_t)tp * osu * 4 +
-                      (d.dtype == DCN4_BF16 ? 16 : 0);
-  if (lds > 64 * 1024) return false;
+  auto lds_for = [&](int32_t u) {
+    const int32_t n = (ob + u - 1) / u;
+    return ((win + 15) & ~int64_t(15)) + (int64_t)tp * n * u + (d.dtype == DCN4_BF16 ? 16 : 0);
+  };
+  const int64_t lds4 = lds_for(4);
+  if ((ob + 3) / 4 > kBlock || lds4 > 64 * 1024) return false;
+  // automatic unit: 16 bytes (a quarter of the copy instructions) when that
+  // keeps the workgroups per CU and the lanes' reads of their values stay at
+  // most 4-way bank conflicted: a lane reads its pixel's values at a stride
+  // of osu * 16 bytes, so 64 lanes share gcd(osu * 4, 64) of the 64 banks'
+  // 4-byte words per bank (measured: 16-byte units on the 56-byte bf16 rows
+  // of the U-Net block, a 64-byte stride, 120.6 -> 134.0 us; on the fp32
+  // InternImage stage, a 112-byte stride, 68.1 -> 61.2 us)
+  int32_t omu = 4;
+  if (p.tile_om_unit) {
+    omu = p.tile_om_unit;
+  } else {
+    const int64_t l16 = lds_for(16);
+    const int32_t osu16 = (ob + 15) / 16;
+    int32_t g = osu16 * 4, m = 64;
+    while (m) { const int32_t r = g % m; g = m; m = r; }  // gcd(osu16 * 4, 64)
+    if (l16 <= 64 * 1024 && kLdsPerCu / l16 >= kLdsPerCu / lds4 && g <= 4) omu = 16;
+  }
+  const int32_t osu = (ob + omu - 1) / omu;
+  const int64_t lds = lds_for(omu);
+  if (osu > kBlock || lds > 64 * 1024) return false;
   t.ok = 1;
   t.dp = dp; t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww;
-  t.ps = ps; t.cb = cb; t.osu = osu; t.lds_bytes = (int32_t)lds;
+  t.ps = ps; t.cb = cb; t.osu = osu; t.omu = omu; t.lds_bytes = (int32_t)lds;
   t.slices = slices;
   t.whole = whole ? 1 : 0;
   t.passes = 1;
@@ -2624,6 +2658,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.wrpp = kBlock / a.cpr;
   a.wpasses = (ts.wh + a.wrpp - 1) / a.wrpp;
   a.OSU = ts.osu;
+  a.OMU = ts.omu;
   a.upr = ts.tw * ts.osu;
   if (a.upr <= kBlock) {  // whole tile rows per pass
     a.orpp = kBlock / a.upr;
@@ -2634,7 +2669,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
     a.opasses = (ts.th * ts.tw + a.oppp - 1) / a.oppp;
   }
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
-  a.flag_lds = a.om_lds + ts.th * ts.tw * ts.osu * 4;
+  a.flag_lds = a.om_lds + ts.th * ts.tw * ts.osu * ts.omu;
   a.f16_window = tile_f16_window(p) ? 1 : 0;
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
   a.tiles_y = (p.Ho + ts.th * a.passes - 1) / (ts.th * a.passes);

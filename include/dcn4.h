@@ -178,6 +178,8 @@ typedef struct {
                                 re-encodes its window as fp16 whenever every
                                 value of it converts exactly (the fma then
                                 widens the value; other windows stay bf16)  */
+  int32_t tile_om_unit;      /* tiled kernels: bytes per lane of an
+                                offset/weight copy instruction (4 or 16)    */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -220,7 +222,12 @@ typedef enum {
    * of magnitude in [2^-17, 65280] (exactly representable in fp16) stages
    * them as fp16, which its fp32 fmas widen for free; other windows stay
    * bf16.  0 = always bf16.  Default 1. */
-  DCN4_OPT_TILE_F16_WINDOW = 9
+  DCN4_OPT_TILE_F16_WINDOW = 9,
+  /* tiled kernels: bytes each lane copies per offset/weight copy instruction,
+   * 4 or 16 (16: a quarter of the instructions, up to 14 padding bytes per
+   * pixel in LDS); 0 = automatic (16 when it keeps the workgroups per
+   * compute unit).  Same results. */
+  DCN4_OPT_TILE_OM_UNIT = 10
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,

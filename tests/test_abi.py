@@ -256,6 +256,24 @@ def test_f16_window_option():
     assert i["kernel"] == 2 and i["tile_f16_window"] == 0
 
 
+def test_om_unit_option():
+    """Offset/weight copy units: 16 bytes automatically when the per-pixel
+    stride keeps the lanes' reads at most 4-way bank conflicted and the
+    occupancy holds (fp32 InternImage stage), 4 bytes otherwise (the bf16
+    U-Net block's 56-byte rows would get a 64-byte stride); either can be
+    forced; other values are rejected."""
+    f32 = d4.Plan(d4.Desc(64, 56, 56, 64, 4, dtype="f32"))
+    assert f32.info()["tile_om_unit"] == 16
+    unet = d4.Plan(d4.Desc(8, 128, 128, 320, 20, dtype="bf16"))
+    assert unet.info()["tile_om_unit"] == 4
+    unet.set_option("tile_om_unit", 16)
+    assert unet.info()["tile_om_unit"] == 16
+    assert d4.dcn4_plan_set_option(unet.handle, d4.DCN4_OPT_TILE_OM_UNIT, 12) == d4.DCN4_ERR_INVALID_ARG
+    assert d4.dcn4_plan_set_option(unet.handle, d4.DCN4_OPT_TILE_OM_UNIT, 8) == d4.DCN4_ERR_INVALID_ARG
+    unet.set_option("tile_om_unit", 0)
+    assert unet.info()["tile_om_unit"] == 4
+
+
 def test_channels_per_lane_override():
     p = d4.Plan(desc_of(Shape(2, 8, 8, 64, 2), "bf16"))   # D = 32
     for dp in (8, 16, 32):

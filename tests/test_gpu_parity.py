@@ -510,6 +510,32 @@ def test_tiled_kernel_group_chunks(groups, pad):
 
 
 
+OM_UNIT_CASES = [("bf16", Shape(1, 29, 33, 128, 8), {"tile_groups": 1}),
+                 ("bf16", Shape(1, 29, 33, 128, 8), {"tile_groups": 2, "tile_pad": 1}),
+                 ("f32", Shape(2, 23, 21, 64, 4), {}),
+                 ("f16", Shape(1, 20, 18, 128, 4, dh=2, dw=2, ph=2, pw=2), {}),
+                 ("bf16", Shape(1, 19, 21, 144, 2, multiscale=True), {}),
+                 ("bf16", Shape(1, 12, 12, 64, 4), {"tile_window": 2})]
+
+
+@pytest.mark.parametrize("case", range(len(OM_UNIT_CASES)))
+@pytest.mark.parametrize("unit", [4, 16])
+def test_tiled_om_copy_units(case, unit):
+    """The tile's offset/weight values copied in 4- or 16-byte units (odd
+    groups' 2-byte leads, group chunks, fp32 rows, whole-image windows,
+    group-scale slices): the oracle bit for bit either way."""
+    dt, s, opts = OM_UNIT_CASES[case]
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=700 + case)
+    plan = d4.Plan(desc_of(s, dt), kernel=2, tile_om_unit=unit, **opts)
+    assert plan.info()["tile_om_unit"] == unit
+    say(f"om unit {unit} case {case}: {plan.info()}")
+    check_against_oracle(gpu_forward(plan, inp, dt),
+                         o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS),
+                         dt, f"om unit {unit} case {case}")
+
+
 @pytest.mark.parametrize("dt, D, dps", [("bf16", 16, (8, 16)), ("f32", 16, (4, 8, 12, 16)),
                                         ("f16", 32, (8, 16, 24, 32)),
                                         ("bf16", 72, (8, 24))])
