@@ -118,6 +118,10 @@ def main():
     ap.add_argument("--dwconv", action="store_true",
                     help="time the depthwise 3x3 convolution (dcn4_dwconv3x3) on the "
                          "workload's input feature map")
+    ap.add_argument("--producer", action="store_true",
+                    help="time the offset/weight producer (the depthwise 3x3, then the "
+                         "linear layer) and the operator after it, alone and in sequence "
+                         "(workloads whose output is the size of their input)")
     ap.add_argument("--eager", action="store_true",
                     help="time one launch per Python call instead of replaying the "
                          "captured K steps")
@@ -155,6 +159,8 @@ def main():
         return bench_dwconv(args, torch, np, workloads, d4, name, w)
     if args.dcnv3:
         return bench_dcnv3(args, torch, np, workloads, d4, name, w)
+    if args.producer:
+        return bench_producer(args, torch, np, workloads, d4, name, w)
     desc = d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
                    w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
                    w.pixel_scales, w.max_scale)
@@ -407,6 +413,71 @@ def timed_steps(torch, dev, stream, step, args):
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / args.steps
+
+
+def bench_producer(args, torch, np, workloads, d4, name, w):
+    """The producer of the operator's offset/weight tensor on the workload
+    (depthwise 3x3 of the input feature map, dcn4_dwconv3x3, then the merged
+    linear layer, dcn4_offset_linear), the operator, and the three in
+    sequence as one step; each leg's launches replayed from a graph on
+    rotated inputs.  `value`: the sequence's output pixels per second."""
+    if w.dtype == "f32":
+        raise SystemExit("bench.py --producer: the layer runs bf16 and fp16 only")
+    plan = d4.Plan(d4.Desc(w.N, w.H, w.W, w.C, w.G, w.kh, w.kw, w.sh, w.sw, w.ph, w.pw,
+                           w.dh, w.dw, w.offset_scale, w.multiscale, w.dtype,
+                           w.pixel_scales, w.max_scale))
+    if (plan.Ho, plan.Wo) != (w.H, w.W):
+        raise SystemExit("bench.py --producer: needs an output the size of the input")
+    M, Cin, Nout = w.N * w.H * w.W, w.C, w.G * 3 * w.K
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    nsets = args.sets or max(2, math.ceil((1 << 30) / max(plan.ideal_bytes, 1)))
+    sets = []
+    for r in range(nsets):
+        inp = workloads.make_inputs(w, plan.Ho, plan.Wo, seed=w.seed + r)
+        rng = np.random.default_rng(3000 + r)
+        t16 = lambda a: torch.from_numpy(workloads.to_raw(a, w.dtype).view(np.int16)).view(tdt).to(dev)
+        x = torch.from_numpy(inp.x.view(np.int16)).view(tdt).to(dev)
+        dw = t16((rng.standard_normal((3, 3, Cin)) / 3).astype(np.float32))
+        db = torch.from_numpy(rng.standard_normal(Cin).astype(np.float32) / 4).to(dev)
+        wt = t16((rng.standard_normal((Nout, Cin)) / np.sqrt(Cin)).astype(np.float32))
+        b = torch.from_numpy(rng.standard_normal(Nout).astype(np.float32) / 4).to(dev)
+        sets.append(dict(x=x, dw=dw, db=db, w=wt, b=b, feat=torch.empty_like(x),
+                         om=torch.empty(plan.om_shape(), dtype=tdt, device=dev),
+                         y=torch.empty(plan.out_shape(), dtype=tdt, device=dev)))
+    torch.cuda.synchronize()
+
+    def two(i, st):
+        t = sets[i % nsets]
+        d4.dwconv3x3(t["x"], t["dw"], t["db"], out=t["feat"], stream=st)
+        d4.offset_linear(t["feat"].view(M, Cin), t["w"], t["b"], out=t["om"].view(M, Nout),
+                         stream=st)
+
+    def op(i, st):
+        t = sets[i % nsets]
+        plan.forward(t["x"], t["om"], out=t["y"], stream=st)
+
+    def pipeline(i, st):
+        two(i, st)
+        op(i, st)
+
+    us = {}
+    for leg, step in (("dwconv_then_linear", two), ("operator", op),
+                      ("producer_then_operator", pipeline)):
+        us[leg] = timed_steps(torch, dev, stream, step, args) * 1e3
+        print(f"# {leg}: {us[leg]:.2f} us per step", file=sys.stderr, flush=True)
+    v = us["producer_then_operator"]
+    print(json.dumps({
+        "metric": "offset/weight producer and DCNv4 forward in sequence: output pixels/s",
+        "value": round(M / (v * 1e-6), 1), "unit": "pixels/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(v * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; the workload's input, normal weights)",
+        "config": {"workload": name, "M": M, "Cin": Cin, "Nout": Nout,
+                   "input_sets": nsets, "launch": "eager" if args.eager else "hip_graph"},
+        "us_per_step": {k: round(t, 3) for k, t in us.items()},
+        "kernel_source": kernel_source_digest()}), flush=True)
 
 
 def bench_dcnv3(args, torch, np, workloads, d4, name, w):

@@ -67,9 +67,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void copy16_to_lds(rsrc_t r, char* lds_wave, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 16, (int)off, 0, 0, 0);
 }
-__device__ __forceinline__ void copy4_to_lds(rsrc_t r, char* lds_wave, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave, 4, (int)off, 0, 0, 0);
-}
 // The same with `unit` (4 or 16, wave-uniform) bytes per lane.
 __device__ __forceinline__ void copy_unit_to_lds(int unit, rsrc_t r, char* lds_wave, uint32_t off) {
   if (unit == 16)
