@@ -354,23 +354,12 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, st):
         x, om, gy, sc, ps, gx, gom = sets[i % nsets]
         plan.backward(x, om, gy, sc, ps, want_x=want_x, want_om=want_om, grad_x=gx,
-                      grad_om=gom, stream=stream.cuda_stream, workspace=ws,
-                      scatter=args.scatter)
+                      grad_om=gom, stream=st, workspace=ws, scatter=args.scatter)
 
-    for i in range(args.warmup):
-        step(i)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = timed_steps(torch, dev, stream, step, args)
     value = ideal / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "DCNv4 bwd GB/s (ideal bytes: x, offset/weight, grad_y read; fp32 grads written)",
@@ -572,21 +561,11 @@ def bench_linear(args, torch, np, workloads, d4, name, w):
                      torch.empty((M, Nout), dtype=tdt, device=dev)))
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, st):
         f, wt, b, out = sets[i % nsets]
-        d4.offset_linear(f, wt, b, out=out, stream=stream.cuda_stream)
+        d4.offset_linear(f, wt, b, out=out, stream=st)
 
-    for i in range(args.warmup):
-        step(i)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = timed_steps(torch, dev, stream, step, args)
     gbs = ideal / (ms * 1e-3) / 1e9
     tfs = flops / (ms * 1e-3) / 1e12
     print(json.dumps({
@@ -624,21 +603,11 @@ def bench_dwconv(args, torch, np, workloads, d4, name, w):
         sets.append((x, torch.empty_like(x)))
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, st):
         x, out = sets[i % nsets]
-        d4.dwconv3x3(x, wt, bias, out=out, stream=stream.cuda_stream)
+        d4.dwconv3x3(x, wt, bias, out=out, stream=st)
 
-    for i in range(args.warmup):
-        step(i)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = timed_steps(torch, dev, stream, step, args)
     gbs = ideal / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "depthwise 3x3 GB/s (ideal bytes: input, weight, bias read; output written)",
