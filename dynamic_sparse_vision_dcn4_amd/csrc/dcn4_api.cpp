@@ -198,7 +198,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->block_threads = dcn4::kBlock;
     info->blocks = per_image * p.desc.N;
     info->launches = p.desc.N ? (int32_t)((p.desc.N + imgs - 1) / imgs) : 0;
-    info->lds_bytes = t.lds_bytes;
+    info->lds_bytes = t.fwd_lds_bytes;
     info->tile_h = t.th;
     info->tile_w = t.tw;
     info->tile_groups = t.gb;
@@ -207,7 +207,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_window = t.whole ? 2 : 1;
     info->tile_passes = t.passes;
     info->tile_f16_window = dcn4::tile_f16_window(p) ? 1 : 0;
-    info->tile_om_unit = t.omu;
+    info->tile_om_unit = t.om_direct ? 1 : t.omu;
     return DCN4_OK;
   }
   info->kernel = 1;
@@ -277,8 +277,8 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
       q.tile_passes = value;
       break;
     case DCN4_OPT_TILE_OM_UNIT:
-      if (value != 0 && value != 4 && value != 16)
-        return fail(DCN4_ERR_INVALID_ARG, "tile om unit must be 0, 4 or 16");
+      if (value != 0 && value != 1 && value != 4 && value != 16)
+        return fail(DCN4_ERR_INVALID_ARG, "tile om unit must be 0, 1, 4 or 16");
       q.tile_om_unit = value;
       break;
     case DCN4_OPT_TILE_F16_WINDOW:

@@ -88,6 +88,8 @@ struct TileArgs {
   int32_t wrpp, wpasses; // window rows per staging pass, passes
   int32_t OSU;           // offset/weight units per tile pixel
   int32_t OMU;           // bytes per offset/weight unit: 4 or 16
+  int32_t om_direct;     // 1: forward lanes read their offset/weight rows from
+                         // global memory into registers (nothing staged in LDS)
   int32_t upr;           // offset/weight units per tile row, TW*OSU
   int32_t orpp;          // tile rows per offset/weight staging pass (0: by pixels)
   int32_t oppp;          // tile pixels per pass when orpp == 0
@@ -111,6 +113,9 @@ struct TileShape {
   int32_t slices;  // channel slices per group (one lane per pixel when > 1)
   int32_t whole;   // window = the whole image plus a 1-pixel zero border
   int32_t passes;  // forward: tile rows a workgroup takes under one staging
+  int32_t om_direct;      // forward: offset/weight rows read into registers
+  int32_t fwd_lds_bytes;  // forward's LDS (lds_bytes less the offset/weight
+                          // area when om_direct; the backward stages it)
 };
 
 enum KernelChoice : int32_t { kKernelAuto = 0, kKernelDirect = 1, kKernelTiled = 2 };

@@ -214,17 +214,12 @@ struct Tap {
   uint32_t q[4];
 };
 
-template <int DT, int MODE, int KS>
-__device__ __forceinline__ Tap tap_geometry(const FwdArgs& a, const LaneCtx& t,
-                                            const typename Io<DT>::raw* om,
-                                            int k) {
-  typedef Io<DT> io;
+// Point k's geometry from its decoded offsets and weight.
+template <int MODE, int KS>
+__device__ __forceinline__ Tap tap_geometry_v(const FwdArgs& a, const LaneCtx& t, float dx,
+                                              float dy, float m, int k) {
   const int kw = KS ? KS : a.kw;
-  const int K = KS ? KS * KS : a.kh * a.kw;
   const int i = k / kw, j = k - (k / kw) * kw;
-  const float dx = io::dec(om[2 * k]);
-  const float dy = io::dec(om[2 * k + 1]);
-  const float m = io::dec(om[2 * K + k]);
   float by, bx, gy = 0.0f, gx = 0.0f;
   if (MODE == kGroupScale) {
     by = (float)t.by0;
@@ -254,6 +249,16 @@ __device__ __forceinline__ Tap tap_geometry(const FwdArgs& a, const LaneCtx& t,
   r.q[2] = (vy1 && vx0) ? o00 + t.row_stride : kOutside;
   r.q[3] = (vy1 && vx1) ? o00 + t.row_stride + t.pix_bytes : kOutside;
   return r;
+}
+
+// The same with point k's values read from the pixel's offset/weight row.
+template <int DT, int MODE, int KS>
+__device__ __forceinline__ Tap tap_geometry(const FwdArgs& a, const LaneCtx& t,
+                                            const typename Io<DT>::raw* om, int k) {
+  typedef Io<DT> io;
+  const int K = KS ? KS * KS : a.kh * a.kw;
+  return tap_geometry_v<MODE, KS>(a, t, io::dec(om[2 * k]), io::dec(om[2 * k + 1]),
+                                  io::dec(om[2 * K + k]), k);
 }
 
 // The four corners' values of one point: NV 16-byte vectors per corner, or
@@ -934,14 +939,73 @@ __device__ __forceinline__ uint32_t stage_om(const TileArgs& a, const TileOrigin
   return mis;
 }
 
+// Words of a 3x3 kernel's offset/weight row held in registers: 27 16-bit
+// values from the 4-byte boundary at or below the row (56 bytes), or 27
+// fp32 values.
+template <int es> constexpr int kOmWords = es == 2 ? 14 : 27;
+
+// Value j of a lane's offset/weight row held in registers: w holds the row
+// from a 4-byte boundary; with 16-bit values P = 1 when the row starts at an
+// odd 16-bit position (a group's row of 3K values, K odd, is 2-byte aligned
+// every other group).
+template <int DT, int P>
+__device__ __forceinline__ float om_packed(const uint32_t* w, int j) {
+  if constexpr (DT == DCN4_F32) {
+    return __uint_as_float(w[j]);
+  } else {
+    const int h = j + P;
+    const uint32_t v = w[h >> 1];
+    if constexpr (DT == DCN4_BF16)
+      return __uint_as_float((h & 1) ? (v & 0xffff0000u) : (v << 16));
+    else
+      return Io<DT>::dec((typename Io<DT>::raw)((h & 1) ? (v >> 16) : (v & 0xffffu)));
+  }
+}
+
+// A lane's offset/weight row of a 3x3 kernel read from global memory into
+// registers: kOmWords words from the 4-byte boundary at or below the row of
+// group g0 at the lane's tile pixel (one group per workgroup); a pixel
+// outside the output reads zeros.
+template <int es>
+__device__ __forceinline__ void load_om_row(const TileArgs& a, uint32_t n, uint32_t g0, int ty0,
+                                            int tx0, uint32_t* w) {
+  constexpr int words = kOmWords<es>;
+  const uint32_t t = threadIdx.x;
+  const uint32_t tp = fastdiv(t, a.div_gbl);
+  const uint32_t py = fastdiv(tp, a.div_tw), px = tp - py * (uint32_t)a.TW;
+  const int yo = ty0 + (int)py, xo = tx0 + (int)px;
+  const rsrc_t omr = make_rsrc(a.om + (uint64_t)n * a.om_img_bytes, a.om_img_bytes);
+  const uint32_t seg = g0 * (uint32_t)(27 * es);
+  const uint32_t off = (yo < a.Ho && xo < a.Wo)
+                           ? ((uint32_t)yo * (uint32_t)a.Wo + (uint32_t)xo) * a.om_row_bytes +
+                                 (seg & ~3u)
+                           : kOutside;
+#pragma unroll
+  for (int q = 0; q < words / 4; ++q) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(omr, (int)(off + 16u * q), 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[4 * q + e] = v[e];
+  }
+  constexpr int q4 = words / 4 * 4;
+  if constexpr (words - q4 >= 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(omr, (int)(off + 4u * q4), 0, 0);
+    w[q4] = v[0];
+    w[q4 + 1] = v[1];
+  }
+  if constexpr ((words - q4) % 2)
+    w[words - 1] = __builtin_amdgcn_raw_buffer_load_b32(omr, (int)(off + 4u * (words - 1)), 0, 0);
+}
+
 // The point loop of the tiled kernel: every point of the lane from LDS, or
 // from global memory for a wave with a point outside the window.  F16W: the
 // window holds fp16 (see stage_window_f16).
-template <int DT, int VEC, int NV, int MODE, int KS, int PSC, bool WHOLE, bool F16W>
+template <int DT, int VEC, int NV, int MODE, int KS, int PSC, bool WHOLE, bool F16W, int OMP>
 __device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa,
                                             const LaneCtx& c, const TileLane& w,
-                                            const typename Io<DT>::raw* om, rsrc_t xr,
-                                            uint32_t r16, float ry0, float rx0, float* acc) {
+                                            const typename Io<DT>::raw* om, const uint32_t* omw,
+                                            rsrc_t xr, uint32_t r16, float ry0, float rx0,
+                                            float* acc) {
   typedef Io<DT> io;
   const int K = KS ? KS * KS : a.kh * a.kw;
   constexpr bool SQ = PSC != 0;
@@ -957,13 +1021,20 @@ __device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const int k = i * KS + j;
-        const float dx = io::dec(om[2 * k]);
-        const float dy = io::dec(om[2 * k + 1]);
-        const float m = io::dec(om[2 * K + k]);
+        float dx, dy, m;
+        if constexpr (OMP > 0) {
+          dx = om_packed<DT, OMP - 1>(omw, 2 * k);
+          dy = om_packed<DT, OMP - 1>(omw, 2 * k + 1);
+          m = om_packed<DT, OMP - 1>(omw, 2 * K + k);
+        } else {
+          dx = io::dec(om[2 * k]);
+          dy = io::dec(om[2 * k + 1]);
+          m = io::dec(om[2 * K + k]);
+        }
         const float gyy = GS ? (float)(i - c.hy) : 0.0f, gxx = GS ? (float)(j - c.hx) : 0.0f;
         if (tile_point<DT, VEC, NV, MODE, PSC, SQ, WHOLE, F16W>(w, by, bx[j], gyy, gxx, dy, dx,
                                                           m, a.offset_scale, c.sg, acc)) {
-          const Tap tg = tap_geometry<DT, MODE, KS>(fa, c, om, k);
+          const Tap tg = tap_geometry_v<MODE, KS>(fa, c, dx, dy, m, k);
           TapData<DT, VEC, NV> d;
           d.load_swapped(xr, tg, r16);
           d.accumulate(acc, tg);
@@ -1011,7 +1082,16 @@ void dcn4_tile_kernel(TileArgs a) {
 
   // the offset/weight copies are requested first, so that their latency
   // overlaps the window's (both are waited for at the barriers below)
-  const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
+  constexpr bool PK = KS == 3;
+  uint32_t omw[kOmWords<es>];
+  const bool omd = PK && a.om_direct;
+  uint32_t mis;
+  if (PK && omd) {
+    mis = (org.g0 * (uint32_t)(27 * es)) & 3u;
+    load_om_row<es>(a, org.n, org.g0, org.ty0, org.tx0, omw);
+  } else {
+    mis = stage_om<es>(a, org, K, lds + a.om_lds);
+  }
   // bf16 windows of few enough passes go through registers and become fp16
   // when every value converts exactly (stage_window_f16)
   bool f16w = false;
@@ -1034,11 +1114,15 @@ void dcn4_tile_kernel(TileArgs a) {
   const int npass = WHOLE ? a.passes : 1;
   for (int pass = 0; pass < npass; ++pass) {
     if (WHOLE && pass > 0) {
-      __syncthreads();  // every lane is done with the previous rows' offsets
-      TileOrigin op = org;
-      op.ty0 = org.ty0 + pass * a.TH;
-      stage_om<es>(a, op, K, lds + a.om_lds);
-      __syncthreads();
+      if (PK && omd) {
+        load_om_row<es>(a, org.n, org.g0, org.ty0 + pass * a.TH, org.tx0, omw);
+      } else {
+        __syncthreads();  // every lane is done with the previous rows' offsets
+        TileOrigin op = org;
+        op.ty0 = org.ty0 + pass * a.TH;
+        stage_om<es>(a, op, K, lds + a.om_lds);
+        __syncthreads();
+      }
     }
     const int ty0 = org.ty0 + pass * a.TH;
     // ---- lane -> (tile pixel, group in chunk, channel slice)
@@ -1097,13 +1181,47 @@ void dcn4_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int e = 0; e < DP; ++e) acc[e] = 0.0f;
 
+    // 16-bit offset/weight rows of a 3x3 kernel, one group per workgroup: the
+    // lane's 27 values are read up front as seven 8-byte words (the row
+    // start is 8-byte aligned: tile pixels are OSU*OMU bytes apart, a
+    // multiple of 8 here) instead of one 2-byte read before each point
+    const bool pk = PK && (omd || (es == 2 && a.GB == 1 && ((a.OSU * a.OMU) & 7) == 0));
+    if (PK && es == 2 && pk && !omd) {
+      typedef const __attribute__((address_space(3))) uint64_t lds_u64;
+      const uint32_t b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
+                             reinterpret_cast<const char*>(om) - mis);
+#pragma unroll
+      for (int q = 0; q < 7; ++q) {
+        const uint64_t v = *reinterpret_cast<lds_u64*>((uintptr_t)(b + 8u * q));
+        omw[2 * q] = (uint32_t)v;
+        omw[2 * q + 1] = (uint32_t)(v >> 32);
+      }
+    }
     if constexpr (DT == DCN4_BF16) {
-      if (f16w)
-        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, true>(a, fa, c, w, om, xr, r16, ry0, rx0, acc);
+      if (f16w) {
+        if (PK && pk && mis)
+          tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, true, 2>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+        else if (PK && pk)
+          tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, true, 1>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+        else
+          tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, true, 0>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+      } else {
+        if (PK && pk && mis)
+          tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, 2>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+        else if (PK && pk)
+          tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, 1>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+        else
+          tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, 0>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+      }
+    } else if constexpr (PK) {
+      if (es == 2 && pk && mis)
+        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, (es == 2 ? 2 : 1)>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
+      else if (pk)
+        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, 1>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
       else
-        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false>(a, fa, c, w, om, xr, r16, ry0, rx0, acc);
+        tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, 0>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
     } else {
-      tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false>(a, fa, c, w, om, xr, r16, ry0, rx0, acc);
+      tile_points<DT, VEC, NV, MODE, KS, PSC, WHOLE, false, 0>(a, fa, c, w, om, omw, xr, r16, ry0, rx0, acc);
     }
 
 #pragma unroll
@@ -2533,7 +2651,9 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   // of the U-Net block, a 64-byte stride, 120.6 -> 134.0 us; on the fp32
   // InternImage stage, a 112-byte stride, 68.1 -> 61.2 us)
   int32_t omu = 4;
-  if (p.tile_om_unit) {
+  if (p.tile_om_unit == 1) {
+    omu = 4;  // the backward's staging (and the forward's where rows cannot be read directly)
+  } else if (p.tile_om_unit) {
     omu = p.tile_om_unit;
   } else {
     const int64_t l16 = lds_for(16);
@@ -2548,6 +2668,18 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   t.ok = 1;
   t.dp = dp; t.gb = gb; t.th = th; t.tw = tw; t.margin = M; t.wh = wh; t.ww = ww;
   t.ps = ps; t.cb = cb; t.osu = osu; t.omu = omu; t.lds_bytes = (int32_t)lds;
+  // Rows of a 3x3 kernel (27 values: 56 bytes from the 4-byte boundary below
+  // a 16-bit row, 108 bytes of fp32), one group per workgroup: each forward
+  // lane reads its own row from global memory into registers, so nothing
+  // waits on the staging barrier and the LDS holds the window alone (more
+  // workgroups per CU).  Measured on graph-replayed steps: U-Net block
+  // 120.7 -> 118.3 us, FlowDCN 115.0 -> 102.8 us, InternImage bf16 45.7 ->
+  // 41.5 us, fp32 61.4 -> 57.2 us, wide low-resolution block 62.6 -> 55.2 us.
+  const bool can_direct = gb == 1 && d.kernel_h == 3 && d.kernel_w == 3;
+  t.om_direct = can_direct && p.tile_om_unit <= 1 ? 1 : 0;
+  t.fwd_lds_bytes = t.om_direct
+                        ? (int32_t)(((win + 15) & ~int64_t(15)) + (d.dtype == DCN4_BF16 ? 16 : 0))
+                        : t.lds_bytes;
   t.slices = slices;
   t.whole = whole ? 1 : 0;
   t.passes = 1;
@@ -2666,6 +2798,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
     a.opasses = (ts.th * ts.tw + a.oppp - 1) / a.oppp;
   }
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
+  a.om_direct = 0;  // set by the forward launch
   a.flag_lds = a.om_lds + ts.th * ts.tw * ts.osu * ts.omu;
   a.f16_window = tile_f16_window(p) ? 1 : 0;
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
@@ -2705,6 +2838,10 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   TileArgs a{};
   fill_tile_args(p, a);
   a.scales = scales;
+  if (ts.om_direct) {  // no offset/weight area: the flag word follows the window
+    a.om_direct = 1;
+    a.flag_lds = a.om_lds;
+  }
   const uint64_t x_img = a.img_bytes, om_img = a.om_img_bytes;
   const uint64_t y_img = (uint64_t)p.Ho * p.Wo * d.C * p.es;
   const uint64_t ps_img = (uint64_t)p.Ho * p.Wo * d.group;  // pixel scales per image
@@ -2717,7 +2854,7 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
     a.y = static_cast<char*>(y) + n0 * y_img;
     a.pscales = pscales ? pscales + n0 * ps_img : nullptr;
     a.nblocks = (int32_t)(nb * per_image);
-    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.lds_bytes,
+    hipLaunchKernelGGL(fn, dim3(a.nblocks), dim3(kBlock), ts.fwd_lds_bytes,
                        static_cast<hipStream_t>(stream), a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {

@@ -178,8 +178,9 @@ typedef struct {
                                 re-encodes its window as fp16 whenever every
                                 value of it converts exactly (the fma then
                                 widens the value; other windows stay bf16)  */
-  int32_t tile_om_unit;      /* tiled kernels: bytes per lane of an
-                                offset/weight copy instruction (4 or 16)    */
+  int32_t tile_om_unit;      /* tiled forward: bytes per lane of an
+                                offset/weight copy instruction (4 or 16),
+                                or 1: rows read into registers, not staged */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -223,10 +224,14 @@ typedef enum {
    * them as fp16, which its fp32 fmas widen for free; other windows stay
    * bf16.  0 = always bf16.  Default 1. */
   DCN4_OPT_TILE_F16_WINDOW = 9,
-  /* tiled kernels: bytes each lane copies per offset/weight copy instruction,
-   * 4 or 16 (16: a quarter of the instructions, up to 14 padding bytes per
-   * pixel in LDS); 0 = automatic (16 when it keeps the workgroups per
-   * compute unit).  Same results. */
+  /* tiled kernels: how a workgroup's offset/weight rows reach its lanes.
+   * 4 or 16: staged in LDS by copy instructions of that many bytes per lane
+   * (16: a quarter of the instructions, up to 14 padding bytes per pixel).
+   * 1: the forward's lanes read their own rows from global memory into
+   * registers, nothing staged (3x3 kernels with 16-bit values and one group
+   * per workgroup; other plans, and the backward, stage 4-byte units).
+   * 0 = automatic: 1 where it applies, else 16 when it keeps the
+   * workgroups per compute unit, else 4.  Same results. */
   DCN4_OPT_TILE_OM_UNIT = 10
 } dcn4_option;
 

@@ -257,21 +257,39 @@ def test_f16_window_option():
 
 
 def test_om_unit_option():
-    """Offset/weight copy units: 16 bytes automatically when the per-pixel
-    stride keeps the lanes' reads at most 4-way bank conflicted and the
-    occupancy holds (fp32 InternImage stage), 4 bytes otherwise (the bf16
-    U-Net block's 56-byte rows would get a 64-byte stride); either can be
-    forced; other values are rejected."""
+    """Offset/weight rows: read by the forward's lanes into registers (1)
+    automatically for 3x3 kernels with one group per workgroup (the U-Net
+    block, the InternImage stages); otherwise staged in 16-byte units when the
+    per-pixel stride keeps the lanes' reads at most 4-way bank conflicted and
+    the occupancy holds (fp32 InternImage stage), else 4-byte units; each can
+    be forced (1 falls back to 4-byte units where rows cannot be read
+    directly); other values are rejected.  Reading the rows directly leaves
+    the window alone in the forward's LDS."""
     f32 = d4.Plan(d4.Desc(64, 56, 56, 64, 4, dtype="f32"))
+    assert f32.info()["tile_om_unit"] == 1
+    f32.set_option("tile_om_unit", 4)
+    assert f32.info()["tile_om_unit"] == 4
+    f32.set_option("tile_om_unit", 16)
     assert f32.info()["tile_om_unit"] == 16
+    five = d4.Plan(d4.Desc(4, 20, 20, 64, 4, kernel_h=5, kernel_w=5, pad_h=2, pad_w=2,
+                           dtype="bf16"), tile_om_unit=1)
+    assert five.info()["tile_om_unit"] in (4, 16)   # 5x5: staged
     unet = d4.Plan(d4.Desc(8, 128, 128, 320, 20, dtype="bf16"))
-    assert unet.info()["tile_om_unit"] == 4
-    unet.set_option("tile_om_unit", 16)
-    assert unet.info()["tile_om_unit"] == 16
+    info = unet.info()
+    assert info["tile_om_unit"] == 1
+    window = info["tile_h"] + 2 + 2 * info["tile_margin"] + 1
+    assert info["lds_bytes"] == window * window * 32 + 16   # window + encoding flags
+    for unit in (4, 16):
+        unet.set_option("tile_om_unit", unit)
+        assert unet.info()["tile_om_unit"] == unit
+        assert unet.info()["lds_bytes"] > info["lds_bytes"]
     assert d4.dcn4_plan_set_option(unet.handle, d4.DCN4_OPT_TILE_OM_UNIT, 12) == d4.DCN4_ERR_INVALID_ARG
     assert d4.dcn4_plan_set_option(unet.handle, d4.DCN4_OPT_TILE_OM_UNIT, 8) == d4.DCN4_ERR_INVALID_ARG
+    assert d4.dcn4_plan_set_option(unet.handle, d4.DCN4_OPT_TILE_OM_UNIT, 2) == d4.DCN4_ERR_INVALID_ARG
     unet.set_option("tile_om_unit", 0)
-    assert unet.info()["tile_om_unit"] == 4
+    assert unet.info()["tile_om_unit"] == 1
+    grouped = d4.Plan(d4.Desc(8, 128, 128, 320, 20, dtype="bf16"), tile_groups=2)
+    assert grouped.info()["tile_om_unit"] in (4, 16)   # two groups per workgroup: staged
 
 
 def test_channels_per_lane_override():

@@ -519,17 +519,20 @@ OM_UNIT_CASES = [("bf16", Shape(1, 29, 33, 128, 8), {"tile_groups": 1}),
 
 
 @pytest.mark.parametrize("case", range(len(OM_UNIT_CASES)))
-@pytest.mark.parametrize("unit", [4, 16])
+@pytest.mark.parametrize("unit", [1, 4, 16])
 def test_tiled_om_copy_units(case, unit):
-    """The tile's offset/weight values copied in 4- or 16-byte units (odd
-    groups' 2-byte leads, group chunks, fp32 rows, whole-image windows,
-    group-scale slices): the oracle bit for bit either way."""
+    """The tile's offset/weight values read by each lane from global memory
+    into registers (1; one group per workgroup, else 4-byte units) or copied to LDS in 4- or 16-byte units (odd groups' 2-byte
+    leads, group chunks, fp32 rows, whole-image windows whose later tile
+    rows load their rows again, group-scale slices): the oracle bit for bit
+    every way."""
     dt, s, opts = OM_UNIT_CASES[case]
     o = oracle.get()
     Ho, Wo = o.out_size(s)
     inp = fuzz_inputs(s, dt, Ho, Wo, seed=700 + case)
     plan = d4.Plan(desc_of(s, dt), kernel=2, tile_om_unit=unit, **opts)
-    assert plan.info()["tile_om_unit"] == unit
+    direct_ok = opts.get("tile_groups", 1) == 1
+    assert plan.info()["tile_om_unit"] == (4 if unit == 1 and not direct_ok else unit)
     say(f"om unit {unit} case {case}: {plan.info()}")
     check_against_oracle(gpu_forward(plan, inp, dt),
                          o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS),
