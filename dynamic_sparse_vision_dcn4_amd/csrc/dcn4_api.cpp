@@ -29,6 +29,12 @@ constexpr int64_t kCoordLimit = int64_t(1) << 20;
 // Margin of the tiled kernel's LDS window, in pixels around the footprint of
 // the tile's undisplaced sample points: offsets within it gather from LDS.
 constexpr int32_t kDefaultTileMargin = 4;
+// In group-scale mode a group's points sit at s_g times the grid (FlowDCN's
+// scale priors reach 4), so they spread further from the tile's footprint:
+// one pixel more (measured with offset/weight rows read into registers:
+// FlowDCN tokens 102.6 us at margin 4, 95.7 at 5, 97.4 at 6; the U-Net
+// block, standard mode, 117.7 at 4, 121.0 at 5).
+constexpr int32_t kDefaultTileMarginGroupScale = 5;
 // lane-index bit (plus one) that swaps a lane's vector pairs in the tiled
 // kernel: bit 3, so lanes 8 apart start on different LDS banks
 constexpr int32_t kDefaultTileSwizzle = 4;
@@ -115,7 +121,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.dp_default = default_dp(p.D, p.es);
   p.dp = p.dp_default;
   p.kernel_choice = dcn4::kKernelAuto;
-  p.tile_margin = kDefaultTileMargin;
+  p.tile_margin = desc->use_group_scales ? kDefaultTileMarginGroupScale : kDefaultTileMargin;
   p.tile_groups = 0;
   p.tile_pad = 0;
   p.tile_swizzle = kDefaultTileSwizzle;

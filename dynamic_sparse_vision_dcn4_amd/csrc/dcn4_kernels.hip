@@ -765,7 +765,11 @@ __device__ __forceinline__ rsrc_t stage_window(const TileArgs& a, const TileOrig
 // such a value, so the sum sees the same fp32 operands either way.
 constexpr uint32_t kF16MagMax = 0x477fu;   // bf16 magnitude bits of 65280
 constexpr uint32_t kF16MagMin1 = 0x36ffu;  // bf16 magnitude bits of 2^-17, minus 1
-constexpr int kF16WinPasses = 10;          // staging passes held in registers
+// Staging passes held in registers.  16 was measured slower: the longer
+// unrolled staging costs the U-Net block and the InternImage stage ~1-3 us,
+// and FlowDCN's 15-pass fp16 window (margin 5) 102.3 us against 94.6 us
+// for its bf16 window copied straight to LDS.
+constexpr int kF16WinPasses = 10;
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Two bf16 values (low, high half) to two fp16 values; exact for the values
@@ -2964,13 +2968,17 @@ dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
 
 // ------------------------------------------------------------ gathered grad_x: host
 // Records per bucket: the mean load of a bucket (K*Ho*Wo samples over
-// (H+1)*(W+1) cells) plus four standard deviations of a Poisson count plus 8,
-// rounded up to a multiple of 4; samples beyond it take the overflow path.
+// (H+1)*(W+1) cells) plus three standard deviations of a Poisson count plus
+// 4, rounded up to a multiple of 4; samples beyond it take the overflow path.
+// The capacity sets the workspace, hence the chunks a bounded workspace
+// takes (U-Net block, both gradients, default workspace: capacity 32, five
+// chunks, 0.958 ms; 24, 0.868 ms; 20, 0.867 ms; 16, where overflows start
+// to cost, 1.005 ms).
 uint32_t bucket_capacity(const Plan& p) {
   if (p.bucket_cap > 0) return (uint32_t)p.bucket_cap;
   const dcn4_desc& d = p.desc;
   const double mu = (double)p.K * p.Ho * p.Wo / ((double)(d.H + 1) * (d.W + 1));
-  uint32_t cap = (uint32_t)__builtin_ceil(mu + 4.0 * __builtin_sqrt(mu) + 8.0);
+  uint32_t cap = (uint32_t)__builtin_ceil(mu + 3.0 * __builtin_sqrt(mu) + 4.0);
   cap = (cap + 3u) & ~3u;
   return cap < 8u ? 8u : cap > 1024u ? 1024u : cap;
 }

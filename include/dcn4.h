@@ -194,7 +194,8 @@ typedef enum {
   DCN4_OPT_CHANNELS_PER_LANE = 0,
   /* 0 = automatic, 1 = direct gather kernel, 2 = tiled kernel (LDS window) */
   DCN4_OPT_KERNEL = 1,
-  /* tiled kernel: pixels of margin around the tile's footprint, 0-16 */
+  /* tiled kernel: pixels of margin around the tile's footprint, 0-16;
+   * default 4, 5 in group-scale mode */
   DCN4_OPT_TILE_MARGIN = 2,
   /* tiled kernel: groups per workgroup (a divisor of G); 0 = automatic */
   DCN4_OPT_TILE_GROUPS = 3,
@@ -206,8 +207,8 @@ typedef enum {
   DCN4_OPT_TILE_SWIZZLE = 5,
   /* backward, gathered grad_x: records per (cell, group) bucket, 1-1024;
    * samples beyond it are added by the overflow kernel's atomics; 0 =
-   * automatic (the mean bucket load plus four Poisson standard deviations
-   * plus 8).  Changes the workspace size. */
+   * automatic (the mean bucket load plus three Poisson standard deviations
+   * plus 4, to a multiple of 4).  Changes the workspace size. */
   DCN4_OPT_BUCKET_CAPACITY = 6,
   /* tiled kernels' LDS window: 1 = the tile's footprint plus the margin (a
    * wave with a point whose corners leave it gathers that point from global

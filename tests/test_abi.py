@@ -178,9 +178,10 @@ def test_plan_options():
     assert i["kernel"] == 2 and i["channels_per_lane"] == 8 and i["tile_slices"] == 2
     assert (i["tile_h"], i["tile_w"]) == (16, 16)
     assert i["blocks"] == 2 * 2 * 2 * 4 * 2   # images x tiles (2 x 2) x groups x slices
-    # group-scale plans tile too
+    # group-scale plans tile too, with one pixel more of margin by default
+    # (their points reach s_g times the grid)
     ms = d4.Plan(desc_of(Shape(2, 10, 10, 64, 4, multiscale=True), "bf16"))
-    assert ms.info()["kernel"] == 2 and ms.info()["tile_margin"] == 4
+    assert ms.info()["kernel"] == 2 and ms.info()["tile_margin"] == 5
     # FlowDCN's 72-channel groups: 24-channel slices
     fl = d4.Plan(desc_of(Shape(2, 32, 32, 1152, 16, multiscale=True), "bf16"))
     assert fl.info()["kernel"] == 2 and fl.info()["tile_slices"] == 3
@@ -241,16 +242,20 @@ def test_f16_window_option():
         with pytest.raises(d4.DCN4Error) as e:
             unet.set_option("tile_f16_window", bad)
         assert e.value.status == d4.DCN4_ERR_INVALID_ARG
-    # FlowDCN's 24-channel slices: 48-byte window pixels, nine staging passes
-    fl = d4.Plan(desc_of(Shape(2, 32, 32, 1152, 16, multiscale=True), "bf16"))
+    # FlowDCN's 24-channel slices: 48-byte window pixels; at margin 4 nine
+    # staging passes (fp16 window), at the group-scale default margin of 5
+    # fifteen, more than the registers hold (bf16 window)
+    fl = d4.Plan(desc_of(Shape(2, 32, 32, 1152, 16, multiscale=True), "bf16"), tile_margin=4)
     assert fl.info()["tile_f16_window"] == 1
+    fl.set_option("tile_margin", 5)
+    assert fl.info()["tile_f16_window"] == 0
     for dt in ("f16", "f32"):
         p = d4.Plan(desc_of(Shape(2, 40, 40, 64, 4), dt), channels_per_lane=8 if dt == "f32" else 0)
         assert p.info()["kernel"] == 2 and p.info()["tile_f16_window"] == 0
     direct = d4.Plan(desc_of(Shape(2, 40, 40, 64, 4), "bf16"), kernel=1)
     assert direct.info()["tile_f16_window"] == 0
     # a window of more staging passes than the registers hold stays bf16
-    # (margin 16: 52 window rows, two to four per pass)
+    # (margin 16: 52 window rows of 16-byte pixels, four per pass: 13 passes)
     wide = d4.Plan(desc_of(Shape(1, 96, 96, 64, 4), "bf16"), tile_window=1, tile_margin=16)
     i = wide.info()
     assert i["kernel"] == 2 and i["tile_f16_window"] == 0
@@ -537,9 +542,9 @@ class TestForwardValidation:
 
     def test_bucket_capacity_option(self):
         p = d4.Plan(mk())
-        # the automatic capacity: mean load + 4 Poisson deviations + 8, to a multiple of 4
+        # the automatic capacity: mean load + 3 Poisson deviations + 4, to a multiple of 4
         mu = 9 * 16 * 16 / (17 * 17)
-        auto = int(np.ceil(mu + 4 * np.sqrt(mu) + 8))
+        auto = int(np.ceil(mu + 3 * np.sqrt(mu) + 4))
         assert p.info()["bucket_capacity"] == (auto + 3) // 4 * 4
         for bad in (-1, 1025):
             assert d4.dcn4_plan_set_option(p.handle, d4.DCN4_OPT_BUCKET_CAPACITY, bad) == \

@@ -598,7 +598,7 @@ F16_NOT = [0x36FF, 0xB6FF, 0x4780, 0xC780, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC
 # window, and FlowDCN's 24-channel slices in group-scale mode
 F16_CASES = [(Shape(2, 40, 36, 64, 4), {"tile_window": 1}),
              (Shape(2, 20, 22, 64, 4), {"tile_window": 2}),
-             (Shape(1, 33, 35, 144, 2, multiscale=True), {"tile_window": 1})]
+             (Shape(1, 33, 35, 144, 2, multiscale=True), {"tile_window": 1, "tile_margin": 4})]
 
 
 @pytest.mark.parametrize("case", range(len(F16_CASES)))
