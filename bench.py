@@ -92,6 +92,30 @@ def copy_ceiling(torch, mib=512, reps=5):
             "what": f"median of {reps} device copies of {mib} MiB (read + write)"}
 
 
+def settle_clocks(torch, ms):
+    """Keep the GPU busy for about `ms` milliseconds with a plain elementwise
+    kernel (torch.sin over 256 MiB of fp32, unrelated to the operator and its
+    inputs) before the warmup steps.  From idle, this GPU raises its clocks
+    over the first ~100 ms of sustained work: the operator's launches took
+    136-155 us for the first 40 and ~121 us from about the 200th on in a
+    fresh process, and the same curve came back after a 1 s idle gap, while
+    after 0.3 s of this elementwise kernel they took 122-124 us from the
+    start.  A handful of warmup steps alone would therefore time the clock
+    ramp, not the kernel.  Returns the busy time in ms."""
+    if ms <= 0:
+        return 0.0
+    a = torch.randn(64 << 20, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            a = torch.sin(a)
+        torch.cuda.synchronize()
+    busy = (time.perf_counter() - t0) * 1e3
+    del a
+    return round(busy, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +128,10 @@ def main():
     ap.add_argument("--channels-per-lane", type=int, default=0)
     ap.add_argument("--option", action="append", default=[], metavar="NAME=VALUE",
                     help="plan option (kernel, tile_margin, tile_groups, tile_pad)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="busy the GPU with a plain elementwise kernel for this long "
+                         "before the warmup steps, so that the timed steps run at the "
+                         "clocks of sustained work (0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=10)
     ap.add_argument("--backward", action="store_true",
@@ -148,6 +176,7 @@ def main():
     if args.copy_reference:
         copy_reference(torch, args.copy_reference, args.steps)
         return
+    args.settled_ms = 0.0
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
@@ -196,6 +225,7 @@ def main():
         x, om, sc, ps, y = sets[i % nsets]
         plan.forward(x, om, sc, out=y, stream=(st or stream).cuda_stream, pixel_scales=ps)
 
+    args.settled_ms = settle_clocks(torch, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -265,7 +295,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "clock_settle_ms": args.settled_ms,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -364,7 +394,7 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
     print(json.dumps({
         "metric": "DCNv4 bwd GB/s (ideal bytes: x, offset/weight, grad_y read; fp32 grads written)",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "clock_settle_ms": args.settled_ms, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded, the workload's shapes and distributions)",
         "config": {"workload": name, "pass": "backward", "grads": args.grads,
@@ -377,8 +407,9 @@ def bench_backward(args, torch, np, workloads, d4, name, w):
 
 def timed_steps(torch, dev, stream, step, args):
     """ms per step of `step(i, hip_stream)` over args.steps steps after
-    args.warmup eager ones; the steps replayed from a captured HIP graph
-    unless args.eager."""
+    args.warmup eager ones (preceded by settle_clocks); the steps replayed
+    from a captured HIP graph unless args.eager."""
+    args.settled_ms = settle_clocks(torch, args.settle_ms)
     for i in range(args.warmup):
         step(i, stream.cuda_stream)
     torch.cuda.synchronize()
@@ -460,7 +491,7 @@ def bench_producer(args, torch, np, workloads, d4, name, w):
     print(json.dumps({
         "metric": "offset/weight producer and DCNv4 forward in sequence: output pixels/s",
         "value": round(M / (v * 1e-6), 1), "unit": "pixels/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(v * 1e-3, 5),
+        "steps": args.steps, "warmup": args.warmup, "clock_settle_ms": args.settled_ms, "ms_per_step": round(v * 1e-3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded; the workload's input, normal weights)",
         "config": {"workload": name, "M": M, "Cin": Cin, "Nout": Nout,
@@ -518,7 +549,7 @@ def bench_dcnv3(args, torch, np, workloads, d4, name, w):
     print(json.dumps({
         "metric": "DCNv4 forward against DCNv3's design: time ratio (DCNv3 / DCNv4)",
         "value": round(us["dcnv3_aggregation"] / v4, 3), "unit": "x",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "clock_settle_ms": args.settled_ms,
         "ms_per_step": round(v4 * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded, the workload's shapes and distributions)",
@@ -572,7 +603,7 @@ def bench_linear(args, torch, np, workloads, d4, name, w):
         "metric": "offset/weight linear GB/s (ideal bytes: features, weight, bias read; "
                   "offset/weight tensor written)",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "clock_settle_ms": args.settled_ms, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded normal features and weights)",
         "config": {"workload": name, "pass": "offset_linear", "M": M, "Cin": Cin,
@@ -612,7 +643,7 @@ def bench_dwconv(args, torch, np, workloads, d4, name, w):
     print(json.dumps({
         "metric": "depthwise 3x3 GB/s (ideal bytes: input, weight, bias read; output written)",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "clock_settle_ms": args.settled_ms, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded normal inputs and weights)",
         "config": {"workload": name, "pass": "dwconv3x3", "N": w.N, "H": w.H, "W": w.W,

@@ -33,6 +33,9 @@ enum Mode : int32_t {
 // Threads per workgroup of the forward kernel: 4 wave64s, fewer when the
 // offset/weight rows one workgroup stages would exceed the LDS budget.
 constexpr int kBlock = 256;
+// Tile rows of the forward's margin window that one workgroup takes under one
+// staging of their joint window (the option tile_passes overrides it).
+constexpr int32_t kDefaultMarginPasses = 1;
 constexpr int64_t kLdsPerCu = 160 * 1024;  // LDS of one compute unit (gfx950)
 constexpr int kLdsBudget = 48 * 1024;
 
@@ -78,11 +81,13 @@ struct TileArgs {
   int32_t swz_shift;     // lane-index bit that swaps a lane's vector pairs (-1: none)
   int32_t GB, TH, TW, M; // groups per workgroup, tile, margin
   int32_t WH, WW;        // window rows, cols
+  int32_t WSQ;           // rows of the window one tile row alone stages (WH for the
+                         // whole image); the square test of a pass uses this square
   int32_t PS;            // LDS bytes per window pixel (CB, maybe padded)
   int32_t CB;            // window bytes per pixel: GB*D*es, or DSL*es when sliced
   int32_t slices;        // channel slices per group (1: whole groups)
   int32_t whole;         // 1: the window is the whole image plus a 1-pixel zero border
-  int32_t passes;        // tile rows per workgroup under one window staging (whole image)
+  int32_t passes;        // tile rows per workgroup under one window staging
   int32_t DSL;           // channels per slice (D when not sliced)
   int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
   int32_t wrpp, wpasses; // window rows per staging pass, passes
@@ -106,6 +111,23 @@ struct TileArgs {
   FastDiv div_chunks, div_tx, div_ty, div_cpr, div_cvec, div_upr, div_osu,
       div_gbl, div_L, div_tw, div_slices;
 };
+
+typedef void (*tile_fn)(TileArgs);
+// The tiled forward kernel of one dtype (0 f32, 1 bf16, 2 f16) and sampling
+// mode (Mode) for nv 16-byte vectors per lane, a 3x3 kernel (K3), a
+// compile-time pixel stride (psc) and the whole-image window (whole); each
+// pair is compiled in a translation unit of its own (dcn4_tile_part.hip).
+#define DCN4_TILE_PART_FN_(DT, MODE) tile_part_##DT##_##MODE
+#define DCN4_TILE_PART_FN(DT, MODE) DCN4_TILE_PART_FN_(DT, MODE)
+tile_fn tile_part_0_0(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_0_1(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_0_2(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_1_0(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_1_1(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_1_2(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_2_0(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_2_1(int nv, int K3, bool psc, bool whole);
+tile_fn tile_part_2_2(int nv, int K3, bool psc, bool whole);
 
 // Tile shape a plan resolved (ok == 0: the tiled kernel does not apply).
 struct TileShape {

@@ -606,7 +606,7 @@ template <int DT, int VEC, int NV> struct LdsTap {
 struct TileLane {
   float lane_f;        // LDS address of the lane's even slots at window cell (c, c)
   float row_f, ps_f;   // LDS bytes per window row / pixel
-  float ymax, xmax;    // largest corner cell minus c: WH-2-c / WW-2-c
+  float ymax, xmax;    // largest corner cell minus c: WSQ-2-c / WW-2-c (square), else WH-2 / WW-2
   float c;             // cell coordinates are taken relative to (c, c)
   uint32_t row_lds, ps;
   uint32_t odd;        // odd slots minus even slots, 16 - 32r (mod 2^32)
@@ -1067,9 +1067,12 @@ __device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa
   }
 }
 
+#ifndef DCN4_TILE_WAVES_NV2
+#define DCN4_TILE_WAVES_NV2 4
+#endif
 template <int DT, int VEC, int NV, int MODE, int KS, int PSC, bool WHOLE>
 __global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(NV <= 2 ? 4 : (NV == 3 ? 3 : 2))))
+__attribute__((amdgpu_waves_per_eu(NV <= 2 ? DCN4_TILE_WAVES_NV2 : (NV == 3 ? 3 : 2))))
 void dcn4_tile_kernel(TileArgs a) {
   typedef Io<DT> io;
   constexpr int es = io::es;
@@ -1112,12 +1115,12 @@ void dcn4_tile_kernel(TileArgs a) {
   }
   __syncthreads();
 
-  // Whole-image window: `passes` consecutive tile rows share one staging of
-  // the window, each pass restaging only the offset/weight rows (one pass
-  // for the margin window).
-  const int npass = WHOLE ? a.passes : 1;
+  // `passes` consecutive tile rows share one staging of the window (the
+  // whole image, or the rows' footprints plus the margin), each pass
+  // restaging only the offset/weight rows.
+  const int npass = a.passes;
   for (int pass = 0; pass < npass; ++pass) {
-    if (WHOLE && pass > 0) {
+    if (pass > 0) {
       if (PK && omd) {
         load_om_row<es>(a, org.n, org.g0, org.ty0 + pass * a.TH, org.tx0, omw);
       } else {
@@ -1171,15 +1174,18 @@ void dcn4_tile_kernel(TileArgs a) {
     const uint32_t r16 = (NV % 2 == 0 && a.swz_shift >= 0) ? ((lane >> a.swz_shift) & 1u) * 16u : 0u;
     w.lane_f = (float)(lds_base + (gl * (uint32_t)a.D + l * DP) * es + r16);
     w.odd = 16u - 2u * r16;
-    // cell coordinates relative to (cw, cw): the centre of a square window
+    // cell coordinates relative to (cy, cw): the centre of a square window
+    // (with margin-window passes, of the square WSQ rows high that this
+    // pass's tile row alone would stage, pass * TH * sh rows down)
     constexpr bool SQ = PSC != 0;
-    const float cw = SQ ? 0.5f * (float)(a.WH - 2) : 0.0f;
+    const float cw = SQ ? 0.5f * (float)(a.WSQ - 2) : 0.0f;
+    const float cy = (SQ && !WHOLE) ? cw + (float)(pass * a.TH * a.sh) : cw;
     w.c = cw;
-    w.ymax = (float)(a.WH - 2) - cw;
+    w.ymax = SQ ? (float)(a.WSQ - 2) - cw : (float)(a.WH - 2);
     w.xmax = (float)(a.WW - 2) - cw;
-    w.lane_f += cw * w.row_f + cw * w.ps_f;  // exact: small multiples of 1/2
-    // base of point (0, 0) relative to window cell (cw, cw)
-    const float ry0 = (float)(c.by0 - wy0) - cw, rx0 = (float)(c.bx0 - wx0) - cw;
+    w.lane_f += cy * w.row_f + cw * w.ps_f;  // exact: small multiples of 1/2
+    // base of point (0, 0) relative to window cell (cy, cw)
+    const float ry0 = (float)(c.by0 - wy0) - cy, rx0 = (float)(c.bx0 - wx0) - cw;
 
     float acc[DP];
 #pragma unroll
@@ -2364,6 +2370,7 @@ __global__ __launch_bounds__(kBlock) void dcn4_probe_kernel(
 }
 
 // ------------------------------------------------------------ host launchers
+#ifndef DCN4_TILE_PART_DT
 typedef void (*fwd_fn)(FwdArgs);
 
 template <int DT, int VEC, int NV, int MODE>
@@ -2418,7 +2425,7 @@ void fill_common(const Plan& p, FwdArgs& a) {
 }
 
 
-typedef void (*tile_fn)(TileArgs);
+#endif  // !DCN4_TILE_PART_DT
 
 template <int DT, int NV, int MODE, bool WHOLE>
 tile_fn tile_kw(int K3, bool psc) {
@@ -2435,30 +2442,38 @@ tile_fn tile_ks(int K3, bool psc, bool whole) {
   return whole ? tile_kw<DT, NV, MODE, true>(K3, psc) : tile_kw<DT, NV, MODE, false>(K3, psc);
 }
 
-template <int DT>
-tile_fn tile_pick(int nv, int mode, int K3, bool psc, bool whole) {
-  if (mode == kGroupScale) {
-    switch (nv) {
-      case 1: return tile_ks<DT, 1, kGroupScale>(K3, psc, whole);
-      case 2: return tile_ks<DT, 2, kGroupScale>(K3, psc, whole);
-      case 3: return tile_ks<DT, 3, kGroupScale>(K3, psc, whole);
-      default: return tile_ks<DT, 4, kGroupScale>(K3, psc, whole);
-    }
-  }
-  if (mode == kStdScaled) {
-    switch (nv) {
-      case 1: return tile_ks<DT, 1, kStdScaled>(K3, psc, whole);
-      case 2: return tile_ks<DT, 2, kStdScaled>(K3, psc, whole);
-      case 3: return tile_ks<DT, 3, kStdScaled>(K3, psc, whole);
-      default: return tile_ks<DT, 4, kStdScaled>(K3, psc, whole);
-    }
-  }
+template <int DT, int MODE>
+tile_fn tile_pick_nv(int nv, int K3, bool psc, bool whole) {
   switch (nv) {
-    case 1: return tile_ks<DT, 1, kStdUnitScale>(K3, psc, whole);
-    case 2: return tile_ks<DT, 2, kStdUnitScale>(K3, psc, whole);
-    case 3: return tile_ks<DT, 3, kStdUnitScale>(K3, psc, whole);
-    default: return tile_ks<DT, 4, kStdUnitScale>(K3, psc, whole);
+    case 1: return tile_ks<DT, 1, MODE>(K3, psc, whole);
+    case 2: return tile_ks<DT, 2, MODE>(K3, psc, whole);
+    case 3: return tile_ks<DT, 3, MODE>(K3, psc, whole);
+    default: return tile_ks<DT, 4, MODE>(K3, psc, whole);
   }
+}
+
+}  // namespace
+
+#ifdef DCN4_TILE_PART_DT
+// A translation unit of its own per (dtype, mode) pair instantiates that
+// pair's tiled forward kernels (dcn4_tile_part.hip), so the library's
+// kernels compile in parallel.
+tile_fn DCN4_TILE_PART_FN(DCN4_TILE_PART_DT, DCN4_TILE_PART_MODE)(int nv, int K3, bool psc,
+                                                                  bool whole) {
+  return tile_pick_nv<DCN4_TILE_PART_DT, DCN4_TILE_PART_MODE>(nv, K3, psc, whole);
+}
+}  // namespace dcn4
+#else
+namespace {
+
+tile_fn tile_pick(int dtype, int mode, int nv, int K3, bool psc, bool whole) {
+#define DCN4_TILE_CASE(DT, MODE) \
+  if (dtype == DT && mode == MODE) return DCN4_TILE_PART_FN(DT, MODE)(nv, K3, psc, whole);
+  DCN4_TILE_CASE(0, 0) DCN4_TILE_CASE(0, 1) DCN4_TILE_CASE(0, 2)
+  DCN4_TILE_CASE(1, 0) DCN4_TILE_CASE(1, 1) DCN4_TILE_CASE(1, 2)
+  DCN4_TILE_CASE(2, 0) DCN4_TILE_CASE(2, 1) DCN4_TILE_CASE(2, 2)
+#undef DCN4_TILE_CASE
+  return nullptr;
 }
 
 }  // namespace
@@ -2612,8 +2627,8 @@ namespace {
 // false when it does not fit (lanes, staging passes or LDS).
 // slices > 1: chunks of one group's dp channels (one lane per pixel, the
 // window holds the slice only); slices == 1: chunks of gb whole groups.
-bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whole,
-                TileShape& t) {
+bool tile_shape_mp(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whole,
+                   int32_t mp, TileShape& t) {
   const dcn4_desc& d = p.desc;
   if (slices < 1 || (slices > 1 && (gb != 1 || dp * slices != p.D))) return false;
   const int32_t L = slices > 1 ? 1 : p.D / dp;
@@ -2623,10 +2638,12 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   int32_t tw = tp >= 16 ? 16 : tp, th = tp / tw;
   if (tp == 64) { th = 8; tw = 8; }
   const int32_t M = p.tile_margin;
-  // the footprint of the tile's points plus the margin (and one more for the
-  // bilinear corners), or the image with a zero row/column on every side
+  // margin window: mp consecutive tile rows per workgroup under one staging
+  if (whole) mp = 1;
+  // the footprint of the tile rows' points plus the margin (and one more for
+  // the bilinear corners), or the image with a zero row/column on every side
   const int32_t wh = whole ? d.H + 2
-                           : (th - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
+                           : (th * mp - 1) * d.stride_h + (d.kernel_h - 1) * d.dilation_h + 2 * M + 2;
   const int32_t ww = whole ? d.W + 2
                            : (tw - 1) * d.stride_w + (d.kernel_w - 1) * d.dilation_w + 2 * M + 2;
   const int32_t cb = slices > 1 ? dp * p.es : gb * p.D * p.es;
@@ -2686,7 +2703,7 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
                         : t.lds_bytes;
   t.slices = slices;
   t.whole = whole ? 1 : 0;
-  t.passes = 1;
+  t.passes = mp;
   if (whole) {
     // tile rows per workgroup: as many as keep at least four workgroups per
     // CU, so that one staging of the image serves more outputs
@@ -2699,6 +2716,24 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
     t.passes = (int32_t)passes;
   }
   return true;
+}
+
+// tile_shape_mp for the plan's margin-window passes (the option, else the
+// default; fewer when the window does not fit, never more than the tile rows
+// of the output).
+bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whole,
+                TileShape& t) {
+  if (whole) return tile_shape_mp(p, dp, gb, slices, true, 1, t);
+  const int32_t lanes_px = gb * (slices > 1 ? 1 : p.D / (dp > 0 ? dp : 1));
+  const int32_t tp = lanes_px > 0 && lanes_px <= kBlock ? kBlock / lanes_px : 1;
+  int32_t th = (tp >= 16 ? 16 : tp);
+  th = tp == 64 ? 8 : tp / th;
+  const int32_t rows = (p.Ho + th - 1) / th;
+  int32_t mp = p.tile_passes > 0 ? p.tile_passes : kDefaultMarginPasses;
+  if (mp > rows) mp = rows;
+  for (; mp > 1; --mp)
+    if (tile_shape_mp(p, dp, gb, slices, false, mp, t)) return true;
+  return tile_shape_mp(p, dp, gb, slices, false, 1, t);
 }
 
 // The tile shape for one kind of window (see resolve_tile).
@@ -2787,6 +2822,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.whole = ts.whole;
   a.passes = ts.passes > 0 ? ts.passes : 1;
   a.WH = ts.wh; a.WW = ts.ww; a.PS = ts.ps; a.CB = ts.cb;
+  a.WSQ = ts.whole ? ts.wh : ts.wh - ts.th * (a.passes - 1) * d.stride_h;
   a.cpr = ts.ww * (ts.ps / 16);
   a.wrpp = kBlock / a.cpr;
   a.wpasses = (ts.wh + a.wrpp - 1) / a.wrpp;
@@ -2833,12 +2869,12 @@ dcn4_status launch_tiled(const Plan& p, const void* x, const void* om,
   // the pixel stride is a compile-time constant when a lane owns all of an
   // unpadded window pixel (a whole group or a slice; and the window is
   // square: see tile_point)
+  const int32_t wsq = ts.whole ? ts.wh : ts.wh - ts.th * (ts.passes - 1) * d.stride_h;
   const bool psc = ts.gb == 1 && (ts.slices > 1 || ts.dp == p.D) && ts.ps == 16 * nv &&
-                   ts.wh == ts.ww;
+                   wsq == ts.ww;
   const bool whole = ts.whole != 0;
-  tile_fn fn = d.dtype == DCN4_F32 ? tile_pick<DCN4_F32>(nv, p.mode, K3, psc, whole)
-             : d.dtype == DCN4_BF16 ? tile_pick<DCN4_BF16>(nv, p.mode, K3, psc, whole)
-                                    : tile_pick<DCN4_F16>(nv, p.mode, K3, psc, whole);
+  tile_fn fn = tile_pick(d.dtype, p.mode, nv, K3, psc, whole);
+  if (!fn) return DCN4_ERR_UNSUPPORTED;
   TileArgs a{};
   fill_tile_args(p, a);
   a.scales = scales;
@@ -2932,7 +2968,12 @@ dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
   fill_tile_args(p, a);
   a.scales = scales;
   BwdTileArgs b{};
-  // one tile row per workgroup (the forward's passes are not used here)
+  // one tile row per workgroup (the forward's passes are not used here); a
+  // margin window covers that row alone
+  if (!ts.whole && a.passes > 1) {
+    a.WH = a.WSQ;
+    a.wpasses = (a.WH + a.wrpp - 1) / a.wrpp;
+  }
   a.passes = 1;
   a.tiles_y = (p.Ho + ts.th - 1) / ts.th;
   a.div_ty = make_fastdiv((uint32_t)a.tiles_y);
@@ -3528,3 +3569,4 @@ dcn4_status launch_probe(const Plan& p, const void* om, const float* scales,
 }
 
 }  // namespace dcn4
+#endif  // DCN4_TILE_PART_DT

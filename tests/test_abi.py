@@ -255,10 +255,14 @@ def test_f16_window_option():
     direct = d4.Plan(desc_of(Shape(2, 40, 40, 64, 4), "bf16"), kernel=1)
     assert direct.info()["tile_f16_window"] == 0
     # a window of more staging passes than the registers hold stays bf16
-    # (margin 16: 52 window rows of 16-byte pixels, four per pass: 13 passes)
-    wide = d4.Plan(desc_of(Shape(1, 96, 96, 64, 4), "bf16"), tile_window=1, tile_margin=16)
+    # (margin 14 and two tile rows per workgroup: 63 x 47 window pixels of 16
+    # bytes, five rows per pass: 13 passes; one tile row: 47 rows, 10 passes)
+    wide = d4.Plan(desc_of(Shape(1, 96, 96, 64, 4), "bf16"), tile_window=1, tile_margin=14,
+                   tile_passes=2)
     i = wide.info()
-    assert i["kernel"] == 2 and i["tile_f16_window"] == 0
+    assert i["kernel"] == 2 and i["tile_passes"] == 2 and i["tile_f16_window"] == 0
+    wide.set_option("tile_passes", 1)
+    assert wide.info()["tile_f16_window"] == 1
 
 
 def test_om_unit_option():

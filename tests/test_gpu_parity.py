@@ -315,6 +315,55 @@ def test_tiled_kernel_margins(dt, margin):
                          dt, f"tiled margin {margin}")
 
 
+# (shape, dtype, channels per lane, extra options): margin windows shared by
+# several tile rows -- 16-channel groups (square per-pass test), 3x3 and 5x5
+# (generic point loop, whole-window test), stride 2, FlowDCN's geometry on
+# 16-channel slices with predicted scales, two groups per workgroup; the heights leave
+# the last workgroup's rows ragged or past the image
+MARGIN_PASSES = [
+    (Shape(2, 37, 45, 64, 4), "bf16", 0, {}),
+    (Shape(2, 37, 45, 64, 4), "f16", 0, {}),
+    (Shape(1, 50, 33, 64, 4), "f32", 8, {}),
+    (Shape(1, 41, 35, 64, 8, 5, 5, 1, 1, 2, 2), "bf16", 0, {}),
+    (Shape(2, 47, 30, 16, 2, 3, 3, 2, 2, 1, 1), "bf16", 0, {}),
+    (Shape(1, 35, 29, 96, 2, multiscale=True, pixel_scales=True, max_scale=4.0),
+     "bf16", 16, {}),
+    (Shape(1, 40, 36, 64, 8), "bf16", 0, {"tile_groups": 2}),
+]
+
+
+@pytest.mark.parametrize("passes", [2, 3, 5])
+@pytest.mark.parametrize("margin", [1, 4])
+@pytest.mark.parametrize("case", range(len(MARGIN_PASSES)))
+def test_tiled_margin_window_passes(case, margin, passes):
+    """Several tile rows per workgroup under one staging of their joint
+    margin window: each row tests its points against its own square (or the
+    joint window) and takes the global path outside it; bit for bit with the
+    oracle, and with the one-row plan."""
+    s, dt, dp, extra = MARGIN_PASSES[case]
+    o = oracle.get()
+    Ho, Wo = o.out_size(s)
+    inp = fuzz_inputs(s, dt, Ho, Wo, seed=500 + 10 * case + margin)
+    if s.pixel_scales:
+        rng = np.random.default_rng(600 + case)
+        ps = rng.uniform(0.25, 2.0, (s.N, Ho, Wo, s.G)).astype(np.float32)
+        inp = workloads.Inputs(inp.x, inp.om, inp.scales, ps)
+    one = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_window=1,
+                  tile_margin=margin, tile_passes=1, **extra)
+    plan = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_window=1,
+                   tile_margin=margin, tile_passes=passes, **extra)
+    info = plan.info()
+    say(f"margin passes {passes} case {case} {s} {dt} margin {margin}: {info}")
+    assert info["kernel"] == 2 and info["tile_window"] == 1 and info["tile_passes"] > 1
+    assert one.info()["tile_passes"] == 1
+    y = gpu_forward(plan, inp, dt)
+    y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS,
+                         pscales=inp.pscales)
+    check_against_oracle(y, y_or, dt, f"margin passes {passes} case {case}")
+    assert np.array_equal(bits_equal(gpu_forward(one, inp, dt), y, dt),
+                          np.ones(y.shape, bool))
+
+
 # (dtype, D, channels per lane, kernel size, stride, pixel scales, Smax):
 # sliced windows (D 72 in 24-channel slices, D 48 in 16) and whole groups
 # (D 16, 24), 3x3 and 5x5 (the generic point loop), stride 2, FlowDCN's
