@@ -95,7 +95,9 @@ def copy_ceiling(torch, mib=512, reps=5):
 def settle_clocks(torch, ms):
     """Keep the GPU busy for about `ms` milliseconds with a plain elementwise
     kernel (torch.sin over 256 MiB of fp32, unrelated to the operator and its
-    inputs) before the warmup steps.  From idle, this GPU raises its clocks
+    inputs) right before the warmup steps, which are enqueued behind it (the
+    graph of the timed steps is captured before, so no host work leaves the
+    GPU idle in between).  From idle, this GPU raises its clocks
     over the first ~100 ms of sustained work: the operator's launches took
     136-155 us for the first 40 and ~121 us from about the 200th on in a
     fresh process, and the same curve came back after a 1 s idle gap, while
@@ -107,9 +109,11 @@ def settle_clocks(torch, ms):
     a = torch.randn(64 << 20, device="cuda")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    while (time.perf_counter() - t0) * 1e3 < ms:
+    while True:
         for _ in range(10):
             a = torch.sin(a)
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            break  # the last batch still runs: the caller's launches follow it
         torch.cuda.synchronize()
     busy = (time.perf_counter() - t0) * 1e3
     del a
@@ -225,16 +229,17 @@ def main():
         x, om, sc, ps, y = sets[i % nsets]
         plan.forward(x, om, sc, out=y, stream=(st or stream).cuda_stream, pixel_scales=ps)
 
-    args.settled_ms = settle_clocks(torch, args.settle_ms)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
     # The K steps are captured once in a HIP graph and the timed region
     # replays it: one host call enqueues every launch, so the GPU runs them
     # back to back whatever the host thread is doing (eagerly, the host's
     # enqueue time per step varied between ~8 and ~190 us from run to run
     # on the same box).  --eager times the launches one Python call each.
+    # The capture comes first (after the first warmup step, which also loads
+    # the kernels), so that the clock settling, the other warmup steps and
+    # one untimed replay then run back to back.
+    if args.warmup > 0:
+        step(0)
+        torch.cuda.synchronize()
     graph = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
@@ -242,8 +247,12 @@ def main():
             cap = torch.cuda.current_stream(dev)
             for i in range(args.steps):
                 step(i, cap)
+    args.settled_ms = settle_clocks(torch, args.settle_ms)
+    for i in range(1, args.warmup):
+        step(i)
+    if graph is not None:
         graph.replay()  # one untimed replay
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
     # the timed region: exactly `steps` steps between two synchronisations
     t0 = torch.cuda.Event(enable_timing=True)
@@ -409,10 +418,9 @@ def timed_steps(torch, dev, stream, step, args):
     """ms per step of `step(i, hip_stream)` over args.steps steps after
     args.warmup eager ones (preceded by settle_clocks); the steps replayed
     from a captured HIP graph unless args.eager."""
-    args.settled_ms = settle_clocks(torch, args.settle_ms)
-    for i in range(args.warmup):
-        step(i, stream.cuda_stream)
-    torch.cuda.synchronize()
+    if args.warmup > 0:
+        step(0, stream.cuda_stream)  # also loads the kernels before the capture
+        torch.cuda.synchronize()
     graph = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
@@ -420,6 +428,10 @@ def timed_steps(torch, dev, stream, step, args):
             cap = torch.cuda.current_stream(dev).cuda_stream
             for i in range(args.steps):
                 step(i, cap)
+    args.settled_ms = settle_clocks(torch, args.settle_ms)
+    for i in range(1, args.warmup):
+        step(i, stream.cuda_stream)
+    if graph is not None:
         graph.replay()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
