@@ -41,7 +41,7 @@ VALU_PEAK_GOPS = 256 * 64 * 2.4
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("dcn4_kernels.hip", "dcn4_internal.h", "dcn4_api.cpp"):
+    for f in ("dcn4_kernels.hip", "dcn4_tile_part.hip", "dcn4_internal.h", "dcn4_api.cpp"):
         with open(os.path.join(ROOT, "dynamic_sparse_vision_dcn4_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -212,7 +212,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_slices = t.slices;
     info->tile_window = t.whole ? 2 : 1;
     info->tile_passes = t.passes;
-    info->tile_f16_window = dcn4::tile_f16_window(p) ? 1 : 0;
+    info->tile_f16_window = dcn4::tile_f16_window(p);
     info->tile_om_unit = t.om_direct ? 1 : t.omu;
     return DCN4_OK;
   }
@@ -288,8 +288,8 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
       q.tile_om_unit = value;
       break;
     case DCN4_OPT_TILE_F16_WINDOW:
-      if (value != 0 && value != 1)
-        return fail(DCN4_ERR_INVALID_ARG, "tile f16 window must be 0 or 1");
+      if (value < 0 || value > 2)
+        return fail(DCN4_ERR_INVALID_ARG, "tile f16 window must be 0, 1 or 2");
       q.f16_window = value;
       break;
     case DCN4_OPT_BUCKET_CAPACITY:

@@ -100,8 +100,8 @@ struct TileArgs {
   int32_t oppp;          // tile pixels per pass when orpp == 0
   int32_t opasses;       // offset/weight staging passes
   int32_t om_lds;        // byte offset of the offset/weight area in LDS
-  int32_t f16_window;    // bf16: stage the window as fp16 when it converts exactly
-                         // (set only when wpasses fits the register staging)
+  int32_t f16_window;    // bf16: the window as fp16 when it converts exactly, re-encoded
+                         // through registers (1: wpasses fits them) or in LDS (2); 0 never
   int32_t flag_lds;      // byte offset of 16 bytes of LDS for the workgroup's
                          // agreement on the window encoding
   int32_t tiles_x, tiles_y, chunks, nblocks;
@@ -156,7 +156,8 @@ struct Plan {
   int32_t tile_passes;   // whole-image window: tile rows per workgroup (0: automatic)
   int32_t dp_user;       // 1: channels per lane set by the caller
   int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
-  int32_t f16_window;    // bf16 tiled forward: 1 = fp16 window when exact, 0 = never
+  int32_t f16_window;    // bf16 tiled forward: 1 = fp16 window when exact (automatic
+                         // method), 2 = always re-encoded in LDS, 0 = never
   int32_t tile_om_unit;  // tiled kernels' offset/weight copy unit: 0 automatic, 4, 16
   TileShape tile;
 };
@@ -165,7 +166,9 @@ struct Plan {
 void resolve_tile(Plan& p);
 // Whether the plan's tiled forward stages a bf16 window through registers
 // and re-encodes it as fp16 when every value converts exactly.
-bool tile_f16_window(const Plan& p);
+// bf16 tiled forward's window encoding: 0 bf16 only, 1 re-encoded as fp16
+// through registers, 2 re-encoded in LDS after the copies (when exact)
+int32_t tile_f16_window(const Plan& p);
 
 // Kernel-side entry points (dcn4_kernels.hip).  Arguments are validated by
 // the caller; these only shape and enqueue the launches.

@@ -859,6 +859,58 @@ __device__ __forceinline__ bool stage_window_f16(const TileArgs& a, const TileOr
   return f16;
 }
 
+// The same re-encoding for a bf16 window already copied to LDS by
+// stage_window, for windows of more staging passes than the registers hold:
+// every thread reads back the 16-byte chunks it copied, the workgroup agrees
+// (as in stage_window_f16) whether every value converts exactly, and if so
+// each thread rewrites its chunks as fp16.  Called after a barrier that
+// follows the copies; returns true when LDS holds fp16.  The rewrites are
+// issued but not waited for: the caller's barrier orders them before the
+// first read.
+__device__ __forceinline__ bool convert_window_f16(const TileArgs& a, char* lds, char* flags) {
+  const uint32_t t = threadIdx.x, lane = t & 63u;
+  const uint32_t rp = fastdiv(t, a.div_cpr);  // row within the pass
+  const bool copies = rp < (uint32_t)a.wrpp;
+  const uint32_t pass_lds = (uint32_t)(a.wrpp * a.cpr) * 16u;
+  const uint32_t dst0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds + t * 16u;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4_w;
+  u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
+  for (int p = 0; p < a.wpasses; ++p) {
+    if (copies && (int)rp + p * a.wrpp < a.WH) {
+      const u32x4 v = *reinterpret_cast<lds_u32x4_w*>((uintptr_t)(dst0 + (uint32_t)p * pass_lds));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u16x2 m = __builtin_bit_cast(u16x2, v[e] & 0x7fff7fffu);
+        mx = __builtin_elementwise_max(mx, m);
+        mn = __builtin_elementwise_min(mn, m + (u16x2){0xffff, 0xffff});
+      }
+    }
+  }
+  const bool ok = (uint32_t)__builtin_elementwise_max(mx.x, mx.y) <= kF16MagMax &&
+                  (uint32_t)__builtin_elementwise_min(mn.x, mn.y) >= kF16MagMin1;
+  const uint64_t bad = __builtin_amdgcn_ballot_w64(!ok);
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  if (lane == 0)
+    *reinterpret_cast<lds_u32*>((uintptr_t)(__attribute__((address_space(3))) char*)(flags + (t >> 6) * 4u)) =
+        bad == 0 ? 1u : 0u;
+  __syncthreads();
+  const u32x4 f = *reinterpret_cast<lds_u32x4*>(
+      (uintptr_t)(__attribute__((address_space(3))) char*)flags);
+  const bool f16 = __builtin_amdgcn_readfirstlane((int)(f[0] & f[1] & f[2] & f[3])) != 0;
+  if (f16) {
+    for (int p = 0; p < a.wpasses; ++p) {
+      if (copies && (int)rp + p * a.wrpp < a.WH) {
+        lds_u32x4_w* q = reinterpret_cast<lds_u32x4_w*>((uintptr_t)(dst0 + (uint32_t)p * pass_lds));
+        u32x4 v = *q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+        *q = v;
+      }
+    }
+  }
+  return f16;
+}
+
 // Stage the tile's offset/weight values at `lds_om`.  Per tile pixel the
 // chunk's GB*3K values are OSU units of OMU bytes (4 or 16: fewer copy
 // instructions for the larger unit) from the 4-byte boundary at or below their
@@ -1104,11 +1156,15 @@ void dcn4_tile_kernel(TileArgs a) {
   bool f16w = false;
   rsrc_t xr;
   if constexpr (DT == DCN4_BF16) {
-    if (a.f16_window) {
+    if (a.f16_window == 1) {
       xr = make_rsrc(a.x + (uint64_t)org.n * a.img_bytes, a.img_bytes);
       f16w = stage_window_f16(a, org, lds, xr, lds + a.flag_lds);
     } else {
       xr = stage_window<es>(a, org, lds);
+      if (a.f16_window == 2) {  // re-encoded in LDS after the copies land
+        __syncthreads();
+        f16w = convert_window_f16(a, lds, lds + a.flag_lds);
+      }
     }
   } else {
     xr = stage_window<es>(a, org, lds);
@@ -2796,12 +2852,17 @@ void resolve_tile(Plan& p) {
   else p.tile = tm;
 }
 
-bool tile_f16_window(const Plan& p) {
+int32_t tile_f16_window(const Plan& p) {
   const TileShape& ts = p.tile;
-  if (!ts.ok || p.desc.dtype != DCN4_BF16 || !p.f16_window) return false;
+  if (!ts.ok || p.desc.dtype != DCN4_BF16 || !p.f16_window) return 0;
+  if (p.f16_window == 2) return 2;
   const int32_t cpr = ts.ww * (ts.ps / 16);
   const int32_t wrpp = kBlock / cpr;
-  return (ts.wh + wrpp - 1) / wrpp <= kF16WinPasses;
+  // automatic: through registers when the window fits them; a larger window
+  // stays bf16 (re-encoding it in LDS measured slower: FlowDCN tokens 97.0 ->
+  // 109.5 us at margin 5, the U-Net block 119.8 -> 121.4 us against the
+  // register path)
+  return (ts.wh + wrpp - 1) / wrpp <= kF16WinPasses ? 1 : 0;
 }
 
 void fill_tile_args(const Plan& p, TileArgs& a) {
@@ -2840,7 +2901,7 @@ void fill_tile_args(const Plan& p, TileArgs& a) {
   a.om_lds = (int32_t)((((int64_t)ts.wh * ts.ww * ts.ps) + 15) & ~int64_t(15));
   a.om_direct = 0;  // set by the forward launch
   a.flag_lds = a.om_lds + ts.th * ts.tw * ts.osu * ts.omu;
-  a.f16_window = tile_f16_window(p) ? 1 : 0;
+  a.f16_window = tile_f16_window(p);
   a.tiles_x = (p.Wo + ts.tw - 1) / ts.tw;
   a.tiles_y = (p.Ho + ts.th * a.passes - 1) / (ts.th * a.passes);
   a.chunks = d.group / ts.gb * ts.slices;

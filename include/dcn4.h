@@ -172,12 +172,13 @@ typedef struct {
                                 footprint plus the margin, 2 the whole image
                                 plus a one-pixel zero border (0: no tile)   */
   int32_t tile_passes;       /* tiled forward: tile rows a workgroup takes
-                                under one staging of its window (1 for the
-                                margin window)                               */
-  int32_t tile_f16_window;   /* tiled bf16 forward: 1 when a workgroup
-                                re-encodes its window as fp16 whenever every
-                                value of it converts exactly (the fma then
-                                widens the value; other windows stay bf16)  */
+                                under one staging of its window             */
+  int32_t tile_f16_window;   /* tiled bf16 forward: a workgroup re-encodes
+                                its window as fp16 whenever every value of
+                                it converts exactly (the fma then widens the
+                                value; other windows stay bf16): 1 through
+                                registers while staging, 2 in LDS after the
+                                copies; 0 never                             */
   int32_t tile_om_unit;      /* tiled forward: bytes per lane of an
                                 offset/weight copy instruction (4 or 16),
                                 or 1: rows read into registers, not staged */
@@ -216,14 +217,18 @@ typedef enum {
    * leaves it; only where it fits LDS), 0 = automatic (the whole image when
    * it fits and stages at most 1.25 times the bytes of the margin window) */
   DCN4_OPT_TILE_WINDOW = 7,
-  /* tiled forward under the whole-image window: tile rows each workgroup
-   * computes from one staging of the image, 1-64 (at most the image's tile
-   * rows); 0 = automatic (as many as keep four workgroups per CU) */
+  /* tiled forward: tile rows each workgroup computes from one staging of
+   * its window, 1-64 (at most the output's tile rows; fewer when the joint
+   * window does not fit LDS).  Whole-image window: 0 = automatic (as many as
+   * keep four workgroups per CU).  Margin window: the window covers the
+   * rows' joint footprint plus the margin; 0 = one row. */
   DCN4_OPT_TILE_PASSES = 8,
-  /* tiled bf16 forward: 1 = a workgroup whose window values are all zero or
-   * of magnitude in [2^-17, 65280] (exactly representable in fp16) stages
-   * them as fp16, which its fp32 fmas widen for free; other windows stay
-   * bf16.  0 = always bf16.  Default 1. */
+  /* tiled bf16 forward: a workgroup whose window values are all zero or of
+   * magnitude in [2^-17, 65280] (exactly representable in fp16) stages them
+   * as fp16, which its fp32 fmas widen for free; other windows stay bf16.
+   * 1 = re-encoded through registers while staging when the window takes
+   * at most 10 staging passes (larger windows stay bf16); 2 = re-encoded in
+   * LDS after the copies land, any window size; 0 = always bf16.  Default 1. */
   DCN4_OPT_TILE_F16_WINDOW = 9,
   /* tiled kernels: how a workgroup's offset/weight rows reach its lanes.
    * 4 or 16: staged in LDS by copy instructions of that many bytes per lane

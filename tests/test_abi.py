@@ -238,17 +238,22 @@ def test_f16_window_option():
     assert unet.info()["tile_f16_window"] == 0
     unet.set_option("tile_f16_window", 1)
     assert unet.info()["tile_f16_window"] == 1
-    for bad in (-1, 2):
+    unet.set_option("tile_f16_window", 2)   # re-encoded in LDS
+    assert unet.info()["tile_f16_window"] == 2
+    unet.set_option("tile_f16_window", 1)
+    for bad in (-1, 3):
         with pytest.raises(d4.DCN4Error) as e:
             unet.set_option("tile_f16_window", bad)
         assert e.value.status == d4.DCN4_ERR_INVALID_ARG
     # FlowDCN's 24-channel slices: 48-byte window pixels; at margin 4 nine
-    # staging passes (fp16 window), at the group-scale default margin of 5
-    # fifteen, more than the registers hold (bf16 window)
+    # staging passes (through registers), at the group-scale default margin
+    # of 5 fifteen, more than the registers hold (bf16, or in LDS on request)
     fl = d4.Plan(desc_of(Shape(2, 32, 32, 1152, 16, multiscale=True), "bf16"), tile_margin=4)
     assert fl.info()["tile_f16_window"] == 1
     fl.set_option("tile_margin", 5)
     assert fl.info()["tile_f16_window"] == 0
+    fl.set_option("tile_f16_window", 2)
+    assert fl.info()["tile_f16_window"] == 2
     for dt in ("f16", "f32"):
         p = d4.Plan(desc_of(Shape(2, 40, 40, 64, 4), dt), channels_per_lane=8 if dt == "f32" else 0)
         assert p.info()["kernel"] == 2 and p.info()["tile_f16_window"] == 0
@@ -256,7 +261,8 @@ def test_f16_window_option():
     assert direct.info()["tile_f16_window"] == 0
     # a window of more staging passes than the registers hold stays bf16
     # (margin 14 and two tile rows per workgroup: 63 x 47 window pixels of 16
-    # bytes, five rows per pass: 13 passes; one tile row: 47 rows, 10 passes)
+    # bytes, five rows per pass: 13 passes; one tile row: 47 rows, 10
+    # passes, through registers)
     wide = d4.Plan(desc_of(Shape(1, 96, 96, 64, 4), "bf16"), tile_window=1, tile_margin=14,
                    tile_passes=2)
     i = wide.info()

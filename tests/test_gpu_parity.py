@@ -643,21 +643,26 @@ def test_nonfinite_values_propagate_like_the_oracle():
 # above 65280, bf16 subnormals, inf, NaN)
 F16_OK = [0x3700, 0xB700, 0x477F, 0xC77F, 0x8000, 0x0000, 0x3701, 0x387F, 0x3880]
 F16_NOT = [0x36FF, 0xB6FF, 0x4780, 0xC780, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC0]
-# (shape, plan options): the margin window with whole groups, the whole-image
-# window, and FlowDCN's 24-channel slices in group-scale mode
-F16_CASES = [(Shape(2, 40, 36, 64, 4), {"tile_window": 1}),
-             (Shape(2, 20, 22, 64, 4), {"tile_window": 2}),
-             (Shape(1, 33, 35, 144, 2, multiscale=True), {"tile_window": 1, "tile_margin": 4})]
+# (shape, plan options, method of option 1): the margin window with whole
+# groups, the whole-image window, FlowDCN's 24-channel slices in group-scale
+# mode at margin 4 (re-encoded through registers) and at its default margin
+# of 5 (fifteen staging passes: bf16 unless re-encoded in LDS), and two tile
+# rows per workgroup
+F16_CASES = [(Shape(2, 40, 36, 64, 4), {"tile_window": 1}, 1),
+             (Shape(2, 20, 22, 64, 4), {"tile_window": 2}, 1),
+             (Shape(1, 33, 35, 144, 2, multiscale=True), {"tile_window": 1, "tile_margin": 4}, 1),
+             (Shape(1, 33, 35, 144, 2, multiscale=True), {"tile_window": 1}, 0),
+             (Shape(1, 70, 40, 64, 4), {"tile_window": 1, "tile_margin": 12, "tile_passes": 2}, 0)]
 
 
 @pytest.mark.parametrize("case", range(len(F16_CASES)))
 def test_f16_window_boundaries(case):
-    """bf16 windows whose values all convert exactly are staged as fp16; any
-    other window stays bf16.  Values at both sides of the boundaries
+    """bf16 windows whose values all convert exactly are staged as fp16
+    (re-encoded through registers or in LDS); any other window stays bf16.  Values at both sides of the boundaries
     (2^-17, 65280, subnormals, inf, NaN) are planted in some tiles' windows
     and not in others, so both encodings run in one launch; the output
     equals the oracle's and the plan without the re-encoding bit for bit."""
-    s, opts = F16_CASES[case]
+    s, opts, auto = F16_CASES[case]
     dt = "bf16"
     o = oracle.get()
     Ho, Wo = o.out_size(s)
@@ -674,15 +679,15 @@ def test_f16_window_boundaries(case):
         x[0, yy, xx, rng.integers(0, s.C)] = v
     y_or = o.forward_f32(s, dt, inp.x, inp.om, inp.scales, nthreads=NTHREADS)
     outs = []
-    for f16w in (1, 0):
+    for f16w in (1, 2, 0):
         plan = d4.Plan(desc_of(s, dt), kernel=2, tile_f16_window=f16w, **opts)
         info = plan.info()
         say(f"f16 window case {case} ({f16w}): {s} {info}")
-        assert info["tile_f16_window"] == f16w
+        assert info["tile_f16_window"] == (auto if f16w == 1 else f16w)
         y = gpu_forward(plan, inp, dt)
         check_against_oracle(y, y_or, dt, f"f16 window case {case} option {f16w}")
         outs.append(y)
-    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
 def test_repeatable_and_stream_independent():
