@@ -1119,6 +1119,9 @@ __device__ __forceinline__ void tile_points(const TileArgs& a, const FwdArgs& fa
   }
 }
 
+// Occupancy hint of the tiled forward for lanes of at most two vectors
+// (a build-time knob): 4 waves per SIMD fit its registers without spills;
+// 5 and 6 measured 28-100% slower on the U-Net block, 2 and 3 the same.
 #ifndef DCN4_TILE_WAVES_NV2
 #define DCN4_TILE_WAVES_NV2 4
 #endif
@@ -2683,6 +2686,13 @@ namespace {
 // false when it does not fit (lanes, staging passes or LDS).
 // slices > 1: chunks of one group's dp channels (one lane per pixel, the
 // window holds the slice only); slices == 1: chunks of gb whole groups.
+// Tile height and width for tp tile pixels (a power of two up to 256).
+void tile_dims(int32_t tp, int32_t& th, int32_t& tw) {
+  tw = tp >= 16 ? 16 : tp;
+  th = tp / tw;
+  if (tp == 64) { th = 8; tw = 8; }
+}
+
 bool tile_shape_mp(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whole,
                    int32_t mp, TileShape& t) {
   const dcn4_desc& d = p.desc;
@@ -2691,8 +2701,8 @@ bool tile_shape_mp(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool w
   const int32_t lanes_px = gb * L;
   if (gb < 1 || d.group % gb || lanes_px > kBlock || kBlock % lanes_px) return false;
   const int32_t tp = kBlock / lanes_px;  // tile pixels
-  int32_t tw = tp >= 16 ? 16 : tp, th = tp / tw;
-  if (tp == 64) { th = 8; tw = 8; }
+  int32_t th, tw;
+  tile_dims(tp, th, tw);
   const int32_t M = p.tile_margin;
   // margin window: mp consecutive tile rows per workgroup under one staging
   if (whole) mp = 1;
@@ -2782,8 +2792,8 @@ bool tile_shape(const Plan& p, int32_t dp, int32_t gb, int32_t slices, bool whol
   if (whole) return tile_shape_mp(p, dp, gb, slices, true, 1, t);
   const int32_t lanes_px = gb * (slices > 1 ? 1 : p.D / (dp > 0 ? dp : 1));
   const int32_t tp = lanes_px > 0 && lanes_px <= kBlock ? kBlock / lanes_px : 1;
-  int32_t th = (tp >= 16 ? 16 : tp);
-  th = tp == 64 ? 8 : tp / th;
+  int32_t th, tw;
+  tile_dims(tp, th, tw);
   const int32_t rows = (p.Ho + th - 1) / th;
   int32_t mp = p.tile_passes > 0 ? p.tile_passes : kDefaultMarginPasses;
   if (mp > rows) mp = rows;
