@@ -74,7 +74,8 @@ class dcn4_launch_info(ctypes.Structure):
                 ("tile_window", ctypes.c_int32),
                 ("tile_passes", ctypes.c_int32),
                 ("tile_f16_window", ctypes.c_int32),
-                ("tile_om_unit", ctypes.c_int32)]
+                ("tile_om_unit", ctypes.c_int32),
+                ("tile_passes_x", ctypes.c_int32)]
 
 # dcn4_option
 DCN4_OPT_CHANNELS_PER_LANE = 0
@@ -88,12 +89,13 @@ DCN4_OPT_TILE_WINDOW = 7
 DCN4_OPT_TILE_PASSES = 8
 DCN4_OPT_TILE_F16_WINDOW = 9
 DCN4_OPT_TILE_OM_UNIT = 10
+DCN4_OPT_TILE_PASSES_X = 11
 OPTIONS = {"channels_per_lane": DCN4_OPT_CHANNELS_PER_LANE, "kernel": DCN4_OPT_KERNEL,
            "tile_margin": DCN4_OPT_TILE_MARGIN, "tile_groups": DCN4_OPT_TILE_GROUPS,
            "tile_pad": DCN4_OPT_TILE_PAD, "tile_swizzle": DCN4_OPT_TILE_SWIZZLE,
            "bucket_capacity": DCN4_OPT_BUCKET_CAPACITY, "tile_window": DCN4_OPT_TILE_WINDOW,
            "tile_passes": DCN4_OPT_TILE_PASSES, "tile_f16_window": DCN4_OPT_TILE_F16_WINDOW,
-           "tile_om_unit": DCN4_OPT_TILE_OM_UNIT}
+           "tile_om_unit": DCN4_OPT_TILE_OM_UNIT, "tile_passes_x": DCN4_OPT_TILE_PASSES_X}
 
 
 _P = ctypes.c_void_p
@@ -370,7 +372,7 @@ class Plan:
 
     def __init__(self, desc: Desc, channels_per_lane: int = 0, **options):
         """options: kernel, tile_margin, tile_groups, tile_pad, tile_swizzle,
-        tile_window, tile_passes, tile_f16_window, bucket_capacity (dcn4_option).  The
+        tile_window, tile_passes, tile_passes_x, tile_f16_window, bucket_capacity (dcn4_option).  The
         kernel choice is applied last, so a forced tiled
         kernel is checked against the tile options given with it."""
         self.desc = desc

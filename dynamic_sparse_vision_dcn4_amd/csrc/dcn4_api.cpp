@@ -127,6 +127,7 @@ dcn4_status dcn4_create(const dcn4_desc* desc, dcn4_plan** plan) {
   p.tile_swizzle = kDefaultTileSwizzle;
   p.tile_window = 0;
   p.tile_passes = 0;
+  p.tile_passes_x = 0;
   p.f16_window = 1;
   p.tile_om_unit = 0;
   dcn4::resolve_tile(p);
@@ -197,7 +198,8 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->channels_per_lane = t.dp;
     info->lanes_per_group = p.D / t.dp;
     const int64_t rows = t.th * (t.passes > 0 ? t.passes : 1);  // output rows per workgroup
-    const int64_t tiles = int64_t((p.Ho + rows - 1) / rows) * ((p.Wo + t.tw - 1) / t.tw);
+    const int64_t cols = t.tw * (t.passes_x > 0 ? t.passes_x : 1);  // and columns
+    const int64_t tiles = int64_t((p.Ho + rows - 1) / rows) * ((p.Wo + cols - 1) / cols);
     const int64_t per_image = tiles * (p.desc.group / t.gb) * t.slices;
     const int64_t imgs = (int64_t(1) << 30) / per_image;
     info->kernel = 2;
@@ -212,6 +214,7 @@ dcn4_status dcn4_plan_info(const dcn4_plan* plan, dcn4_launch_info* info) {
     info->tile_slices = t.slices;
     info->tile_window = t.whole ? 2 : 1;
     info->tile_passes = t.passes;
+    info->tile_passes_x = t.passes_x;
     info->tile_f16_window = dcn4::tile_f16_window(p);
     info->tile_om_unit = t.om_direct ? 1 : t.omu;
     return DCN4_OK;
@@ -281,6 +284,10 @@ dcn4_status dcn4_plan_set_option(dcn4_plan* plan, int32_t option, int32_t value)
     case DCN4_OPT_TILE_PASSES:
       if (value < 0 || value > 64) return fail(DCN4_ERR_INVALID_ARG, "tile passes must be 0-64");
       q.tile_passes = value;
+      break;
+    case DCN4_OPT_TILE_PASSES_X:
+      if (value < 0 || value > 64) return fail(DCN4_ERR_INVALID_ARG, "tile passes x must be 0-64");
+      q.tile_passes_x = value;
       break;
     case DCN4_OPT_TILE_OM_UNIT:
       if (value != 0 && value != 1 && value != 4 && value != 16)

@@ -88,6 +88,7 @@ struct TileArgs {
   int32_t slices;        // channel slices per group (1: whole groups)
   int32_t whole;         // 1: the window is the whole image plus a 1-pixel zero border
   int32_t passes;        // tile rows per workgroup under one window staging
+  int32_t passes_x;      // and tile columns (whole-image window; 1 otherwise)
   int32_t DSL;           // channels per slice (D when not sliced)
   int32_t cpr;           // 16-byte chunks per window row, WW*PS/16 (<= 256)
   int32_t wrpp, wpasses; // window rows per staging pass, passes
@@ -135,6 +136,7 @@ struct TileShape {
   int32_t slices;  // channel slices per group (one lane per pixel when > 1)
   int32_t whole;   // window = the whole image plus a 1-pixel zero border
   int32_t passes;  // forward: tile rows a workgroup takes under one staging
+  int32_t passes_x;  // forward, whole-image window: and tile columns
   int32_t om_direct;      // forward: offset/weight rows read into registers
   int32_t fwd_lds_bytes;  // forward's LDS (lds_bytes less the offset/weight
                           // area when om_direct; the backward stages it)
@@ -154,6 +156,7 @@ struct Plan {
   int32_t kernel_choice, tile_margin, tile_groups, tile_pad, tile_swizzle;
   int32_t tile_window;   // 0 automatic, 1 tile footprint plus margin, 2 whole image
   int32_t tile_passes;   // whole-image window: tile rows per workgroup (0: automatic)
+  int32_t tile_passes_x; // whole-image window: tile columns per workgroup (0: automatic)
   int32_t dp_user;       // 1: channels per lane set by the caller
   int32_t bucket_cap;    // records per bucket of the gathered grad_x (0: automatic)
   int32_t f16_window;    // bf16 tiled forward: 1 = fp16 window when exact (automatic

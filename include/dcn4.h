@@ -182,6 +182,9 @@ typedef struct {
   int32_t tile_om_unit;      /* tiled forward: bytes per lane of an
                                 offset/weight copy instruction (4 or 16),
                                 or 1: rows read into registers, not staged */
+  int32_t tile_passes_x;     /* tiled forward, whole-image window: tile
+                                columns a workgroup takes under one staging
+                                (1 otherwise)                               */
 } dcn4_launch_info;
 
 /* Fills *info for the plan as it would run with 16-byte aligned pointers.
@@ -238,7 +241,12 @@ typedef enum {
    * per workgroup; other plans, and the backward, stage 4-byte units).
    * 0 = automatic: 1 where it applies, else 16 when it keeps the
    * workgroups per compute unit, else 4.  Same results. */
-  DCN4_OPT_TILE_OM_UNIT = 10
+  DCN4_OPT_TILE_OM_UNIT = 10,
+  /* tiled forward under the whole-image window: tile columns each
+   * workgroup computes from one staging of the image (with the rows of
+   * DCN4_OPT_TILE_PASSES), 1-64, at most the output's tile columns;
+   * 0 = automatic (one column).  No effect on the margin window. */
+  DCN4_OPT_TILE_PASSES_X = 11
 } dcn4_option;
 
 /* Sets one option (see dcn4_option).  Errors: DCN4_ERR_NULL,

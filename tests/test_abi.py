@@ -210,11 +210,21 @@ def test_tile_window_choice():
     assert i["tile_slices"] == 2 and (i["tile_h"], i["tile_w"]) == (16, 16)
     # images x tile columns x groups x slices: a workgroup walks both tile
     # rows of its column under one staging (four workgroups per CU remain)
-    assert i["tile_passes"] == 2 and i["blocks"] == 16 * 2 * 40 * 2
+    assert i["tile_passes"] == 2 and i["tile_passes_x"] == 1
+    assert i["blocks"] == 16 * 2 * 40 * 2
     wide.set_option("tile_passes", 1)
     assert wide.info()["tile_passes"] == 1 and wide.info()["blocks"] == 16 * 4 * 40 * 2
     wide.set_option("tile_passes", 9)   # at most the image's tile rows
     assert wide.info()["tile_passes"] == 2
+    # both tile columns too: one workgroup per (image, group, slice)
+    wide.set_option("tile_passes_x", 2)
+    assert wide.info()["tile_passes_x"] == 2 and wide.info()["blocks"] == 16 * 40 * 2
+    wide.set_option("tile_passes_x", 5)  # at most the image's tile columns
+    assert wide.info()["tile_passes_x"] == 2
+    with pytest.raises(d4.DCN4Error):
+        wide.set_option("tile_passes_x", 65)
+    wide.set_option("tile_passes_x", 0)
+    assert wide.info()["tile_passes_x"] == 1
     with pytest.raises(d4.DCN4Error):
         wide.set_option("tile_passes", 65)
     wide.set_option("tile_window", 1)

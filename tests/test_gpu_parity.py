@@ -504,12 +504,13 @@ def test_tiled_whole_image_window(case):
     assert margin.info()["tile_window"] == 1
     assert np.array_equal(bits_equal(gpu_forward(margin, inp, dt), y, dt),
                           np.ones(y.shape, bool))
-    # several tile rows per workgroup under one staging (the last one ragged
-    # or past the image for some shapes): the same bits
-    for passes in (2, 3):
+    # a block of several tile rows and columns per workgroup under one
+    # staging (the last ones ragged or past the image for some shapes): the
+    # same bits
+    for passes, passes_x in ((1, 1), (2, 1), (3, 1), (1, 2), (2, 2), (3, 3)):
         pp = d4.Plan(desc_of(s, dt), channels_per_lane=dp, kernel=2, tile_window=2,
-                     tile_passes=passes)
-        say(f"  passes {passes}: {pp.info()}")
+                     tile_passes=passes, tile_passes_x=passes_x)
+        say(f"  passes {passes} x {passes_x}: {pp.info()}")
         assert np.array_equal(bits_equal(gpu_forward(pp, inp, dt), y, dt),
                               np.ones(y.shape, bool))
 
