@@ -1734,9 +1734,29 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
   const int ty0 = org.ty0, tx0 = org.tx0, wy0 = org.wy0, wx0 = org.wx0;
   const uint32_t t = threadIdx.x;
   const uint32_t pix_bytes = (uint32_t)(a.C * es);
+  // 16-bit offset/weight rows, one group per workgroup: each lane reads its
+  // row from global memory into registers (as the forward does), else the
+  // rows are staged in LDS
+  constexpr bool OMD_OK = es == 2;
+  const bool omd = OMD_OK && a.om_direct != 0;
+  uint32_t omw[kOmWords<es>];
+  uint32_t mis;
+  if (OMD_OK && omd) {
+    mis = (g0 * (uint32_t)(27 * es)) & 3u;
+    load_om_row<es>(a, n, g0, ty0, tx0, omw);
+  } else {
+    mis = stage_om<es>(a, org, K, lds + a.om_lds);
+  }
   const rsrc_t xr = stage_window<es>(a, org, lds);
-  const uint32_t mis = stage_om<es>(a, org, K, lds + a.om_lds);
   __syncthreads();
+  if (OMD_OK && omd && mis) {
+    // the row starts at the odd 16-bit position: move it down by 16 bits so
+    // that value j is half j of the words
+#pragma unroll
+    for (int q = 0; q + 1 < kOmWords<es>; ++q)
+      omw[q] = __builtin_amdgcn_alignbit(omw[q + 1], omw[q], 16u);
+    omw[kOmWords<es> - 1] >>= 16;
+  }
 
   // ---- lane -> (tile pixel, group in chunk, channel slice)
   const uint32_t tp = fastdiv(t, a.div_gbl);
@@ -1797,8 +1817,16 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int i = k / KS, j = k - (k / KS) * KS;
-    const float dx = io::dec(om[2 * k]), dy = io::dec(om[2 * k + 1]);
-    const float m = io::dec(om[2 * K + k]);
+    float dx, dy, m;
+    if (OMD_OK && omd) {
+      dx = om_packed<DT, 0>(omw, 2 * k);
+      dy = om_packed<DT, 0>(omw, 2 * k + 1);
+      m = om_packed<DT, 0>(omw, 2 * K + k);
+    } else {
+      dx = io::dec(om[2 * k]);
+      dy = io::dec(om[2 * k + 1]);
+      m = io::dec(om[2 * K + k]);
+    }
     const float gyy = GS ? (float)(i - hy) : 0.0f, gxx = GS ? (float)(j - hx) : 0.0f;
     const Loc lc = sample_location<MODE>(GS ? ry0 : ry0 + (float)(i * a.dh),
                                          GS ? rx0 : rx0 + (float)(j * a.dw), gyy, gxx, dy, dx,
@@ -1884,7 +1912,8 @@ __global__ __launch_bounds__(kBlock) void dcn4_tile_bwd_kernel(TileArgs a, BwdTi
   if constexpr (SL) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const float mf = io::dec(om[2 * K + k]) * f;
+      const float mk = (OMD_OK && omd) ? om_packed<DT, 0>(omw, 2 * K + k) : io::dec(om[2 * K + k]);
+      const float mf = mk * f;
       res[2 * k] = mf * res[2 * k];
       res[2 * k + 1] = mf * res[2 * k + 1];
     }
@@ -3051,6 +3080,7 @@ dcn4_status launch_tiled_backward(const Plan& p, const void* x, const void* om,
   TileArgs a{};
   fill_tile_args(p, a);
   a.scales = scales;
+  a.om_direct = ts.om_direct;  // 16-bit rows of one group: read into registers
   BwdTileArgs b{};
   // one tile row per workgroup (the forward's passes are not used here); a
   // margin window covers that row alone

@@ -207,6 +207,14 @@ def test_tiled_backward(case, margin):
     ref = oracle.get().backward(s, dt, inp.x, inp.om, gy, inp.scales, inp.pscales)
     _, gom = run_backward(plan, inp, gy, dt, want_x=False)
     check_bound(gom, ref["gom"], ref["gom_abs"], ref["max_terms"], f"tiled grad_om {case} m{margin}")
+    if info["tile_om_unit"] == 1:
+        # the rows read into registers (16-bit rows of one group) and staged
+        # in LDS give the same bits
+        staged = d4.Plan(desc_of(s, dt), channels_per_lane=dp, tile_margin=margin,
+                         tile_om_unit=4, **rest)
+        assert staged.info()["tile_om_unit"] == 4
+        _, gom_s = run_backward(staged, inp, gy, dt, want_x=False)
+        assert np.array_equal(gom.view(np.uint32), gom_s.view(np.uint32))
     gxg, gom_g = run_backward(plan, inp, gy, dt)
     assert np.array_equal(gom.view(np.uint32), gom_g.view(np.uint32))
     check_bound(gxg, ref["gx"], ref["gx_abs"], ref["max_terms"], f"gathered grad_x {case} m{margin}")
